@@ -1,0 +1,381 @@
+"""Float64 CPU oracle for the fused LM-head + cross-entropy + KL distillation loss.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or link
+this module: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` use it. It shares no code with the HIP library and does not
+import it.
+
+The oracle reaches every result by its plain definition. It materialises the
+full-vocabulary logits of each row block in float64, computes log-sum-exp over
+all V columns at once, and forms the gradients of the logits in closed form
+before contracting them with the inputs. It never streams over vocabulary
+chunks: the flash_kd page (module description) states that the online-softmax
+stream is numerically identical to the full computation, so the full
+computation is the reference.
+
+Inputs are the *stored* values (bf16 or fp32 tensors converted to float64,
+which is exact). Arrays are NumPy; callers convert torch tensors first.
+
+Sources (page title, then section):
+  * orda-kernel (PyPI page): Quickstart, Teacher descriptors, Parameters.
+  * flash_kd (Model-Optimizer API page): flash_ce_kd_loss, Parameters/Returns.
+  * CompactifAI/Full-Chunked-KL-Loss (README): Methods, objective; Full Dense
+    KL; Full Chunked KL.
+  * nemo_automodel.components.loss.kd_loss (NeMo AutoModel API page): KDLoss
+    parameters (temperature) and KDLoss.forward (num_batch_labels).
+
+Readings of points the pages leave open (each is also listed in the design doc):
+  R1  cross-entropy is always at temperature 1; T applies to the KL term only.
+  R2  the per-token KL output includes the T**2 factor.
+  R3  the per-token KL is reported for every row; loss and gradients exclude
+      rows whose label is ignored; per-token CE is 0 on ignored rows.
+  R4  an all-ignored batch divides by max(n_valid, 1): loss 0, gradients 0.
+  R6  a frozen teacher's CE enters the loss value but gives no gradient.
+  R7  top-K indices are int32, probabilities fp32; M is the sum of the stored p.
+  R8  0 * log 0 = 0 in the teacher-entropy term.
+  R10 top-K mode has no labels: every row is valid, there is no CE.
+  --  a label outside [0, V) that is not ignore_index is treated as ignored.
+
+Parity pins for every function live in tests/test_oracle.py (closed forms,
+library cross-checks, invariants, finite differences). No function here is
+parity unpinned.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+F64 = np.float64
+
+# Rows per block when materialising (rows, V) float64 logits.
+ROW_BLOCK = 256
+
+
+@dataclass
+class Params:
+    """Loss configuration.
+
+    Term weights and temperature follow orda-kernel, Parameters
+    (student_ce_weight / teacher_ce_weight / kl_weight, kl_temperature);
+    reduction and num_batch_labels follow nemo kd_loss, KDLoss.forward.
+    ``normalizer > 0`` plays the role of num_batch_labels.
+    """
+
+    student_ce_weight: float = 1.0
+    teacher_ce_weight: float = 0.0
+    kl_weight: float = 0.0
+    temperature: float = 1.0
+    ignore_index: int = -100
+    reduction: str = "mean"  # "mean" | "sum"
+    normalizer: float = 0.0
+
+
+# ---------------------------------------------------------------------------
+# Elementary definitions
+# ---------------------------------------------------------------------------
+
+def as_f64(x) -> np.ndarray:
+    """Exact conversion of stored values to float64."""
+    return np.asarray(x, dtype=F64)
+
+
+def project(hidden, weight) -> np.ndarray:
+    """Logits of an LM head with no bias: hidden @ weight.T.
+
+    orda-kernel, Quickstart: weight has shape (vocab, hidden); flash_kd,
+    flash_ce_kd_loss: teacher logits are teacher_hidden @ weight[chunk].T.
+    """
+    return as_f64(hidden) @ as_f64(weight).T
+
+
+def logsumexp(x: np.ndarray) -> np.ndarray:
+    """log sum_v exp(x_v) over the last axis, shifted by the row maximum."""
+    m = x.max(axis=-1)
+    return m + np.log(np.exp(x - m[..., None]).sum(axis=-1))
+
+
+def log_softmax(x: np.ndarray) -> np.ndarray:
+    return x - logsumexp(x)[..., None]
+
+
+def softmax(x: np.ndarray) -> np.ndarray:
+    return np.exp(log_softmax(x))
+
+
+def valid_mask(labels, vocab: int, ignore_index: int) -> np.ndarray:
+    """Rows that carry a usable label.
+
+    orda-kernel, Parameters (ignore_index): the ignored value is excluded from
+    CE and KL and is never used as a memory index. A value outside [0, vocab)
+    is treated like ignore_index (the library also raises a status flag).
+    """
+    y = np.asarray(labels, dtype=np.int64)
+    return (y != ignore_index) & (y >= 0) & (y < vocab)
+
+
+# ---------------------------------------------------------------------------
+# Per-token terms
+# ---------------------------------------------------------------------------
+
+def cross_entropy(logits: np.ndarray, labels, valid: np.ndarray) -> np.ndarray:
+    """Per-token CE at temperature 1: lse(x) - x[y]; 0 on ignored rows.
+
+    flash_kd, flash_ce_kd_loss Parameters (labels): ignored entries get CE 0,
+    as F.cross_entropy(reduction="none") does; Returns: standard CE.
+    """
+    y = np.where(valid, np.asarray(labels, dtype=np.int64), 0)
+    picked = np.take_along_axis(logits, y[:, None], axis=1)[:, 0]
+    return np.where(valid, logsumexp(logits) - picked, 0.0)
+
+
+def forward_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
+    """Per-token T**2 * KL(P_T || P_S) with P = softmax(logits / T).
+
+    nemo kd_loss, KDLoss (temperature): both logits are divided by T and the
+    loss is multiplied by T**2; orda-kernel, KL variants: "forward" is
+    KL(teacher || student). Reported for every row (reading R3).
+    """
+    lp_s = log_softmax(student_logits / T)
+    lp_t = log_softmax(teacher_logits / T)
+    return (T * T) * (np.exp(lp_t) * (lp_t - lp_s)).sum(axis=-1)
+
+
+def topk_kl(student_logits: np.ndarray, idx, prob) -> np.ndarray:
+    """Sparse forward KL against cached top-K teacher probabilities.
+
+    CompactifAI/Full-Chunked-KL-Loss, Methods (objective): with support S,
+    retained mass M = sum_S p (not renormalised) and student logits z,
+        L = sum_S p log p - sum_S p z + M * logsumexp(z).
+    0 * log 0 is taken as 0 (reading R8).
+    """
+    p = as_f64(prob)
+    ix = np.asarray(idx, dtype=np.int64)
+    safe = np.where(p > 0, p, 1.0)
+    entropy_term = np.where(p > 0, p * np.log(safe), 0.0).sum(axis=1)
+    cross_term = (p * np.take_along_axis(student_logits, ix, axis=1)).sum(axis=1)
+    mass = p.sum(axis=1)
+    return entropy_term - cross_term + mass * logsumexp(student_logits)
+
+
+# ---------------------------------------------------------------------------
+# Logit gradients (closed form)
+# ---------------------------------------------------------------------------
+
+def dce_dlogits(logits: np.ndarray, labels, valid: np.ndarray) -> np.ndarray:
+    """d CE / d logits = softmax(x) - onehot(y) on valid rows, 0 elsewhere."""
+    g = softmax(logits)
+    rows = np.nonzero(valid)[0]
+    g[rows, np.asarray(labels, dtype=np.int64)[rows]] -= 1.0
+    g[~valid] = 0.0
+    return g
+
+
+def dkl_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
+    """d (T**2 KL(P_T || P_S)) / d z = T * (softmax(z/T) - softmax(t/T))."""
+    return T * (softmax(student_logits / T) - softmax(teacher_logits / T))
+
+
+def dtopk_dstudent(student_logits: np.ndarray, idx, prob) -> np.ndarray:
+    """Closed-form gradient of the sparse objective: M * softmax(z) - p scattered.
+
+    CompactifAI/Full-Chunked-KL-Loss, Full Chunked KL: the backward applies
+    M softmax(z) - p.
+    """
+    p = as_f64(prob)
+    g = p.sum(axis=1)[:, None] * softmax(student_logits)
+    rows = np.arange(g.shape[0])[:, None]
+    np.subtract.at(g, (np.broadcast_to(rows, p.shape), np.asarray(idx, dtype=np.int64)), p)
+    return g
+
+
+# ---------------------------------------------------------------------------
+# Whole-batch forward / backward
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Teacher:
+    """Teacher descriptor (orda-kernel, Teacher descriptors).
+
+    kind "tied": hidden only, projected with the student weight.
+    kind "separate": hidden (N, D_t) and weight (V, D_t), detached.
+    kind "topk": cached (idx, prob), each (N, K) (Full-Chunked-KL-Loss).
+    """
+
+    kind: str
+    hidden: Optional[np.ndarray] = None
+    weight: Optional[np.ndarray] = None
+    idx: Optional[np.ndarray] = None
+    prob: Optional[np.ndarray] = None
+
+
+@dataclass
+class Student:
+    """Student side: hidden (N, D) and weight (V, D), or given logits (N, V).
+
+    The logits form is the flash_kd scorer (student_logits already
+    materialised, forward only).
+    """
+
+    hidden: Optional[np.ndarray] = None
+    weight: Optional[np.ndarray] = None
+    logits: Optional[np.ndarray] = None
+
+    @property
+    def n(self) -> int:
+        return (self.logits if self.logits is not None else self.hidden).shape[0]
+
+    @property
+    def v(self) -> int:
+        return self.logits.shape[1] if self.logits is not None else self.weight.shape[0]
+
+
+def _student_logits(s: Student, rows: np.ndarray) -> np.ndarray:
+    if s.logits is not None:
+        return as_f64(s.logits[rows])
+    return project(s.hidden[rows], s.weight)
+
+
+def _teacher_logits(t: Teacher, s: Student, rows: np.ndarray) -> Optional[np.ndarray]:
+    if t.kind == "tied":
+        return project(t.hidden[rows], s.weight)
+    if t.kind == "separate":
+        return project(t.hidden[rows], t.weight)
+    return None
+
+
+def per_token(student: Student, teacher: Teacher, p: Params, labels=None,
+              rows: Optional[np.ndarray] = None) -> dict:
+    """Per-token terms for the selected rows (all rows by default).
+
+    Returns float64 arrays: student_ce, teacher_ce, kl (T**2 included), and for
+    top-K mode the sparse objective in ``kl`` as well.
+    """
+    n = student.n
+    v = student.v
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    if labels is None:
+        lab = np.full(n, p.ignore_index, dtype=np.int64)
+        valid_all = np.ones(n, dtype=bool)  # reading R10: top-K rows are all valid
+    else:
+        lab = np.asarray(labels, dtype=np.int64)
+        valid_all = valid_mask(lab, v, p.ignore_index)
+    out = {k: np.zeros(len(rows), F64) for k in ("student_ce", "teacher_ce", "kl")}
+    out["valid"] = valid_all[rows]
+    for b in range(0, len(rows), ROW_BLOCK):
+        r = rows[b:b + ROW_BLOCK]
+        z = _student_logits(student, r)
+        vb = valid_all[r]
+        if labels is not None:
+            out["student_ce"][b:b + len(r)] = cross_entropy(z, lab[r], vb)
+        if teacher.kind == "topk":
+            out["kl"][b:b + len(r)] = topk_kl(z, teacher.idx[r], teacher.prob[r])
+            continue
+        t = _teacher_logits(teacher, student, r)
+        if labels is not None:
+            out["teacher_ce"][b:b + len(r)] = cross_entropy(t, lab[r], vb)
+        out["kl"][b:b + len(r)] = forward_kl(z, t, p.temperature)
+    return out
+
+
+def denominator(p: Params, n_valid: int) -> float:
+    """Loss normaliser.
+
+    nemo kd_loss, KDLoss.forward (num_batch_labels): divide by the given total
+    when provided, else average over the valid tokens; orda-kernel, Parameters
+    (reduction): "mean" or "sum". Reading R4: an all-ignored mean divides by 1.
+    """
+    if p.normalizer > 0:
+        return float(p.normalizer)
+    if p.reduction == "mean":
+        return float(max(n_valid, 1))
+    return 1.0
+
+
+def forward(student: Student, teacher: Teacher, p: Params, labels=None) -> dict:
+    """Per-token outputs plus the reduced loss.
+
+    loss = sum over valid rows of (w_s ce_s + w_t ce_t + w_kl kl) / den
+    (orda-kernel, Quickstart: DistillationLossOutput holds the loss and the
+    unweighted components).
+    """
+    out = per_token(student, teacher, p, labels)
+    valid = out["valid"]
+    contrib = (p.student_ce_weight * out["student_ce"]
+               + p.teacher_ce_weight * out["teacher_ce"]
+               + p.kl_weight * out["kl"])
+    n_valid = int(valid.sum())
+    den = denominator(p, n_valid)
+    out["n_valid"] = n_valid
+    out["den"] = den
+    out["loss"] = float(np.where(valid, contrib, 0.0).sum() / den)
+    return out
+
+
+def logit_grad(student: Student, teacher: Teacher, p: Params, labels, rows: np.ndarray,
+               den: float, grad_loss: float = 1.0) -> np.ndarray:
+    """d loss / d z for the given rows, shape (len(rows), V).
+
+    (g / den) * valid * [w_s (softmax z - e_y) + w_kl T (softmax(z/T) - softmax(t/T))],
+    or w_kl (M softmax z - p) in top-K mode. The teacher is detached (orda-kernel,
+    KL variants: all variants except mutual/cojeffreys detach the teacher), so
+    the teacher CE contributes no gradient (reading R6).
+    """
+    z = _student_logits(student, rows)
+    v = student.v
+    if labels is None:
+        valid = np.ones(len(rows), dtype=bool)
+        lab = None
+    else:
+        lab = np.asarray(labels, dtype=np.int64)[rows]
+        valid = valid_mask(lab, v, p.ignore_index)
+    g = np.zeros_like(z)
+    if teacher.kind == "topk":
+        g += p.kl_weight * dtopk_dstudent(z, teacher.idx[rows], teacher.prob[rows])
+    else:
+        if lab is not None and p.student_ce_weight != 0.0:
+            g += p.student_ce_weight * dce_dlogits(z, lab, valid)
+        if p.kl_weight != 0.0:
+            t = _teacher_logits(teacher, student, rows)
+            g += p.kl_weight * dkl_dstudent(z, t, p.temperature)
+    g[~valid] = 0.0
+    return g * (grad_loss / den)
+
+
+def backward(student: Student, teacher: Teacher, p: Params, labels=None,
+             grad_loss: float = 1.0, den: Optional[float] = None):
+    """Gradients of the reduced loss with respect to student hidden and weight.
+
+    dH = dZ @ W and dW = dZ.T @ H (CompactifAI/Full-Chunked-KL-Loss, Full
+    Chunked KL: gradients of the hidden states and the projection from the
+    closed-form logit gradient). Returns float64 (dH, dW).
+    """
+    n = student.n
+    if den is None:
+        if labels is None:
+            n_valid = n
+        else:
+            n_valid = int(valid_mask(labels, student.v, p.ignore_index).sum())
+        den = denominator(p, n_valid)
+    W = as_f64(student.weight)
+    dH = np.zeros((n, W.shape[1]), F64)
+    dW = np.zeros_like(W)
+    for b in range(0, n, ROW_BLOCK):
+        r = np.arange(b, min(b + ROW_BLOCK, n))
+        g = logit_grad(student, teacher, p, labels, r, den, grad_loss)
+        dH[r] = g @ W
+        dW += g.T @ as_f64(student.hidden[r])
+    return dH, dW
+
+
+def backward_rows(student: Student, teacher: Teacher, p: Params, labels, rows,
+                  den: float, grad_loss: float = 1.0) -> np.ndarray:
+    """dH restricted to the given rows (each row's gradient needs only that row)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    W = as_f64(student.weight)
+    out = np.zeros((len(rows), W.shape[1]), F64)
+    for b in range(0, len(rows), ROW_BLOCK):
+        r = rows[b:b + ROW_BLOCK]
+        out[b:b + len(r)] = logit_grad(student, teacher, p, labels, r, den, grad_loss) @ W
+    return out

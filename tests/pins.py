@@ -1,0 +1,411 @@
+"""Pins that tie the float64 oracle to facts outside itself.
+
+Each ``check_*`` takes an oracle module ``O`` and raises AssertionError when
+the oracle disagrees with something the pages or the mathematics fix:
+closed forms, special cases that reduce to a library routine
+(torch.nn.functional.cross_entropy / kl_div, autograd), invariants, and
+central finite differences. None of them retypes the oracle's own formula.
+
+tests/test_oracle.py runs them against the real oracle; tests/test_oracle_mutants.py
+runs them against copies of the oracle with one planted mistake each and
+requires that some pin fails.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+RNG_SEED = 1234
+
+
+def _rng(k=0):
+    return np.random.default_rng(RNG_SEED + k)
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    ok = np.allclose(a, b, rtol=rtol, atol=atol)
+    assert ok, f"{what}: max abs diff {np.max(np.abs(a - b)):.3e}"
+
+
+def _student_logits_case(O, n=6, v=9, k=0):
+    r = _rng(k)
+    z = r.normal(size=(n, v)) * 2.0
+    return O.Student(logits=z), z
+
+
+# ---------------------------------------------------------------------------
+# Cross-entropy (flash_kd, flash_ce_kd_loss: standard CE, 0 on ignored rows)
+# ---------------------------------------------------------------------------
+
+def check_ce_uniform_logits(O):
+    """W = 0 makes every logit 0: CE = log V exactly, softmax = 1/V, and the
+    logit gradient of the mean CE is (1/V - e_y)/n_valid in closed form."""
+    n, d, v = 5, 4, 11
+    r = _rng(1)
+    H = r.normal(size=(n, d))
+    W = np.zeros((v, d))
+    y = np.array([3, 0, -100, 10, 7])
+    s = O.Student(hidden=H, weight=W)
+    t = O.Teacher("tied", hidden=H)
+    p = O.Params(student_ce_weight=1.0, kl_weight=0.0)
+    out = O.forward(s, t, p, y)
+    valid = y != -100
+    _close(out["student_ce"], np.where(valid, math.log(v), 0.0), what="CE = log V")
+    _close(out["loss"], math.log(v), what="mean CE = log V")
+    g = O.logit_grad(s, t, p, y, np.arange(n), den=float(valid.sum()))
+    expect = np.zeros((n, v))
+    for i in range(n):
+        if valid[i]:
+            expect[i] = 1.0 / v
+            expect[i, y[i]] -= 1.0
+    _close(g, expect / valid.sum(), what="dCE/dz closed form")
+
+
+def check_ce_library(O):
+    """Per-token CE equals torch's cross_entropy(reduction='none') in float64,
+    ignore_index rows included (flash_kd, labels parameter)."""
+    s, z = _student_logits_case(O, n=7, v=13, k=2)
+    y = np.array([0, 12, -100, 5, 5, -100, 9])
+    p = O.Params(student_ce_weight=1.0, kl_weight=0.0)
+    out = O.per_token(s, O.Teacher("topk", idx=np.zeros((7, 1), np.int64),
+                                   prob=np.zeros((7, 1))), p, y)
+    ref = F.cross_entropy(torch.from_numpy(z), torch.from_numpy(y), reduction="none",
+                          ignore_index=-100).numpy()
+    _close(out["student_ce"], ref, what="CE vs F.cross_entropy")
+    mean = F.cross_entropy(torch.from_numpy(z), torch.from_numpy(y), ignore_index=-100).item()
+    w = O.Teacher("topk", idx=np.zeros((7, 1), np.int64), prob=np.zeros((7, 1)))
+    _close(O.forward(s, w, p, y)["loss"], mean, what="mean CE vs F.cross_entropy")
+
+
+def check_ce_two_classes(O):
+    """V = 2: CE = softplus(z_other - z_y)."""
+    s, z = _student_logits_case(O, n=8, v=2, k=3)
+    y = np.array([0, 1, 1, 0, 1, 0, 0, 1])
+    p = O.Params(student_ce_weight=1.0, kl_weight=0.0)
+    w = O.Teacher("topk", idx=np.zeros((8, 1), np.int64), prob=np.zeros((8, 1)))
+    out = O.per_token(s, w, p, y)
+    other = z[np.arange(8), 1 - y]
+    own = z[np.arange(8), y]
+    _close(out["student_ce"], np.log1p(np.exp(other - own)), what="CE softplus")
+
+
+def check_ce_large_logits(O):
+    """A shift of every logit by a constant leaves CE unchanged (lse is
+    shift-equivariant); a shift of 1e4 overflows exp without the max shift."""
+    s, z = _student_logits_case(O, n=4, v=6, k=4)
+    y = np.array([1, 2, 3, 4])
+    p = O.Params(student_ce_weight=1.0, kl_weight=0.0)
+    w = O.Teacher("topk", idx=np.zeros((4, 1), np.int64), prob=np.zeros((4, 1)))
+    a = O.per_token(s, w, p, y)["student_ce"]
+    b = O.per_token(O.Student(logits=z + 1.0e4), w, p, y)["student_ce"]
+    _close(a, b, rtol=1e-9, atol=1e-9, what="CE shift invariance")
+
+
+# ---------------------------------------------------------------------------
+# Forward KL (nemo kd_loss, KDLoss temperature; orda-kernel, KL variants)
+# ---------------------------------------------------------------------------
+
+def _tied_case(O, n=6, d=5, v=10, k=5, same=False):
+    r = _rng(k)
+    Hs = r.normal(size=(n, d))
+    Ht = Hs.copy() if same else r.normal(size=(n, d)) * 1.3
+    W = r.normal(size=(v, d)) * 0.7
+    return O.Student(hidden=Hs, weight=W), O.Teacher("tied", hidden=Ht)
+
+
+def check_kl_zero_for_identical(O):
+    """KL = 0 when the teacher equals the student (tied with H_t = H_s;
+    separate with W_t = W and H_t = H_s), at any temperature."""
+    for T in (1.0, 2.0, 0.5):
+        s, t = _tied_case(O, same=True)
+        p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T)
+        _close(O.per_token(s, t, p)["kl"], 0.0, atol=1e-13, what="KL tied identical")
+        t2 = O.Teacher("separate", hidden=s.hidden.copy(), weight=s.weight.copy())
+        _close(O.per_token(s, t2, p)["kl"], 0.0, atol=1e-13, what="KL separate identical")
+
+
+def check_kl_nonnegative(O):
+    """Gibbs' inequality: KL >= 0, and > 0 for distinct distributions."""
+    s, t = _tied_case(O, k=6)
+    for T in (1.0, 3.0):
+        p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T)
+        kl = O.per_token(s, t, p)["kl"]
+        assert (kl > 0).all(), f"KL not positive: {kl}"
+
+
+def check_kl_library(O):
+    """T^2 * kl_div(log_softmax(z/T), log_softmax(t/T), log_target) summed over
+    the vocabulary equals the oracle's per-token KL (nemo kd_loss: divide by T,
+    multiply by T^2; flash_kd: T = 1 is the plain kl_div metric)."""
+    s, t = _tied_case(O, n=7, d=4, v=12, k=7)
+    z = torch.from_numpy(s.hidden @ s.weight.T)
+    tt = torch.from_numpy(t.hidden @ s.weight.T)
+    for T in (1.0, 2.0, 0.7):
+        p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T)
+        ref = F.kl_div(F.log_softmax(z / T, -1), F.log_softmax(tt / T, -1), log_target=True,
+                       reduction="none").sum(-1) * T * T
+        _close(O.per_token(s, t, p)["kl"], ref.numpy(), rtol=1e-11, atol=1e-12,
+               what=f"KL vs F.kl_div T={T}")
+
+
+def check_kl_two_classes(O):
+    """V = 2: closed-form Bernoulli KL between sigmoid((t1-t0)/T) and
+    sigmoid((z1-z0)/T), times T^2."""
+    r = _rng(8)
+    z = r.normal(size=(6, 2)) * 1.5
+    tl = r.normal(size=(6, 2)) * 1.5
+    T = 1.7
+    qs = 1.0 / (1.0 + np.exp(-(z[:, 1] - z[:, 0]) / T))
+    qt = 1.0 / (1.0 + np.exp(-(tl[:, 1] - tl[:, 0]) / T))
+    ref = T * T * (qt * np.log(qt / qs) + (1 - qt) * np.log((1 - qt) / (1 - qs)))
+    # separate teacher whose head is the identity: logits equal the hidden states
+    s = O.Student(hidden=z, weight=np.eye(2))
+    t = O.Teacher("separate", hidden=tl, weight=np.eye(2))
+    p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T)
+    _close(O.per_token(s, t, p)["kl"], ref, rtol=1e-11, atol=1e-13, what="Bernoulli KL")
+
+
+def check_kl_temperature_identity(O):
+    """KL at temperature T on (z, t) equals T^2 times KL at T = 1 on (z/T, t/T)."""
+    s, t = _tied_case(O, k=9)
+    T = 2.5
+    z = s.hidden @ s.weight.T
+    tl = t.hidden @ s.weight.T
+    pT = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T)
+    p1 = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=1.0)
+    eye = np.eye(z.shape[1])
+    a = O.per_token(s, t, pT)["kl"]
+    b = O.per_token(O.Student(hidden=z / T, weight=eye),
+                    O.Teacher("separate", hidden=tl / T, weight=eye), p1)["kl"]
+    _close(a, T * T * b, rtol=1e-11, atol=1e-13, what="KL temperature identity")
+
+
+# ---------------------------------------------------------------------------
+# Sparse top-K objective (Full-Chunked-KL-Loss, Methods / Full Dense KL)
+# ---------------------------------------------------------------------------
+
+def _topk_case(n=6, v=15, k=4, seed=10, zero_one=True):
+    r = _rng(seed)
+    z = r.normal(size=(n, v)) * 1.5
+    idx = np.stack([r.choice(v, size=k, replace=False) for _ in range(n)])
+    g = r.gamma(0.3, size=(n, k))
+    p = g / g.sum(1, keepdims=True) * r.uniform(0.85, 0.99, size=(n, 1))
+    if zero_one:
+        p[0, 0] = 0.0  # a zero probability exercises 0 log 0 = 0
+    return z, idx, p
+
+
+def check_topk_dense_scatter(O):
+    """The sparse objective equals the dense-scatter form, the pages' correctness
+    baseline: q = p scattered to the vocabulary (0 elsewhere),
+    L = sum_v q log q - sum_v q log_softmax(z), with 0 log 0 = 0."""
+    z, idx, p = _topk_case()
+    n, v = z.shape
+    q = np.zeros((n, v))
+    for i in range(n):
+        q[i, idx[i]] = p[i]
+    lsm = F.log_softmax(torch.from_numpy(z), -1).numpy()
+    qlogq = np.where(q > 0, q * np.log(np.where(q > 0, q, 1.0)), 0.0)
+    ref = qlogq.sum(1) - (q * lsm).sum(1)
+    s = O.Student(logits=z)
+    w = O.Teacher("topk", idx=idx, prob=p)
+    got = O.per_token(s, w, O.Params(student_ce_weight=0.0, kl_weight=1.0))["kl"]
+    _close(got, ref, rtol=1e-11, atol=1e-13, what="sparse = dense scatter")
+
+
+def check_topk_full_support(O):
+    """K = V with M = 1: the sparse objective is the dense forward KL with teacher
+    probabilities p, i.e. kl_div(log_softmax(z), log p, log_target) summed."""
+    r = _rng(11)
+    n, v = 5, 8
+    z = r.normal(size=(n, v))
+    logits_t = r.normal(size=(n, v))
+    p = torch.softmax(torch.from_numpy(logits_t), -1).numpy()
+    idx = np.stack([r.permutation(v) for _ in range(n)])
+    pp = np.take_along_axis(p, idx, 1)
+    ref = F.kl_div(F.log_softmax(torch.from_numpy(z), -1), torch.from_numpy(np.log(p)),
+                   log_target=True, reduction="none").sum(-1).numpy()
+    got = O.per_token(O.Student(logits=z), O.Teacher("topk", idx=idx, prob=pp),
+                      O.Params(student_ce_weight=0.0, kl_weight=1.0))["kl"]
+    _close(got, ref, rtol=1e-11, atol=1e-13, what="full-support top-K = dense KL")
+
+
+def check_topk_ce_bridge(O):
+    """K = 1 with p = 1 on the label (M = 1) reduces the objective to CE(z, y)."""
+    r = _rng(12)
+    n, v = 6, 9
+    z = r.normal(size=(n, v)) * 2
+    y = r.integers(0, v, size=n)
+    got = O.per_token(O.Student(logits=z), O.Teacher("topk", idx=y[:, None], prob=np.ones((n, 1))),
+                      O.Params(student_ce_weight=0.0, kl_weight=1.0))["kl"]
+    ref = F.cross_entropy(torch.from_numpy(z), torch.from_numpy(y), reduction="none").numpy()
+    _close(got, ref, rtol=1e-12, atol=1e-13, what="top-K K=1 is CE")
+
+
+def check_topk_mass_scaling(O):
+    """Scaling every cached p by c changes the objective to
+    c * L + c log c * M (from L = sum p log p - sum p z + M lse z)."""
+    z, idx, p = _topk_case(seed=13, zero_one=False)
+    c = 0.6
+    s = O.Student(logits=z)
+    prm = O.Params(student_ce_weight=0.0, kl_weight=1.0)
+    a = O.per_token(s, O.Teacher("topk", idx=idx, prob=p), prm)["kl"]
+    b = O.per_token(s, O.Teacher("topk", idx=idx, prob=c * p), prm)["kl"]
+    _close(b, c * a + c * math.log(c) * p.sum(1), rtol=1e-11, atol=1e-13, what="mass scaling")
+
+
+# ---------------------------------------------------------------------------
+# Reduction (nemo kd_loss, KDLoss.forward num_batch_labels; orda reduction)
+# ---------------------------------------------------------------------------
+
+def check_reduction_modes(O):
+    """mean divides by the valid count, sum by 1, a normaliser by itself; the
+    mean of CE equals F.cross_entropy(reduction='mean', ignore_index)."""
+    s, t = _tied_case(O, n=8, d=4, v=10, k=14)
+    y = np.array([1, -100, 3, 9, -100, 0, 4, 4])
+    z = torch.from_numpy(s.hidden @ s.weight.T)
+    ce_mean = F.cross_entropy(z, torch.from_numpy(y), ignore_index=-100).item()
+    ce_sum = F.cross_entropy(z, torch.from_numpy(y), ignore_index=-100, reduction="sum").item()
+    base = dict(student_ce_weight=1.0, kl_weight=0.0)
+    _close(O.forward(s, t, O.Params(**base, reduction="mean"), y)["loss"], ce_mean, what="mean")
+    _close(O.forward(s, t, O.Params(**base, reduction="sum"), y)["loss"], ce_sum, what="sum")
+    _close(O.forward(s, t, O.Params(**base, normalizer=40.0), y)["loss"], ce_sum / 40.0,
+           what="normalizer")
+
+
+def check_all_ignored(O):
+    """Every row ignored: loss 0 and zero gradients (reading R4)."""
+    s, t = _tied_case(O, n=4, d=3, v=6, k=15)
+    y = np.full(4, -100)
+    p = O.Params(student_ce_weight=1.0, kl_weight=1.0, temperature=2.0)
+    out = O.forward(s, t, p, y)
+    assert out["loss"] == 0.0 and out["den"] == 1.0
+    dH, dW = O.backward(s, t, p, y)
+    assert not dH.any() and not dW.any()
+
+
+def check_out_of_range_label_is_ignored(O):
+    """A label outside [0, V) behaves exactly like ignore_index."""
+    s, t = _tied_case(O, n=5, d=3, v=7, k=16)
+    p = O.Params(student_ce_weight=1.0, kl_weight=1.0, temperature=1.5)
+    a = O.forward(s, t, p, np.array([1, 7, 2, -5, 0]))
+    b = O.forward(s, t, p, np.array([1, -100, 2, -100, 0]))
+    _close(a["loss"], b["loss"], what="out-of-range label")
+    _close(a["student_ce"], b["student_ce"], what="out-of-range label CE")
+
+
+# ---------------------------------------------------------------------------
+# Gradients
+# ---------------------------------------------------------------------------
+
+def _fd_cases(O):
+    r = _rng(20)
+    n, d, v, dt = 4, 5, 9, 3
+    Hs = r.normal(size=(n, d))
+    W = r.normal(size=(v, d)) * 0.8
+    Ht = r.normal(size=(n, d)) * 1.2
+    Htt = r.normal(size=(n, dt))
+    Wt = r.normal(size=(v, dt))
+    y = np.array([2, -100, 8, 0])
+    idx = np.stack([r.choice(v, size=3, replace=False) for _ in range(n)])
+    g = r.gamma(0.5, size=(n, 3))
+    pk = g / g.sum(1, keepdims=True) * 0.9
+    return [
+        ("tied", O.Teacher("tied", hidden=Ht), y,
+         O.Params(student_ce_weight=0.7, kl_weight=1.3, temperature=2.0)),
+        ("separate", O.Teacher("separate", hidden=Htt, weight=Wt), y,
+         O.Params(student_ce_weight=1.0, teacher_ce_weight=1.0, kl_weight=1.0, temperature=1.0)),
+        ("topk", O.Teacher("topk", idx=idx, prob=pk), None,
+         O.Params(student_ce_weight=0.0, kl_weight=1.0)),
+        ("sum", O.Teacher("tied", hidden=Ht), y,
+         O.Params(student_ce_weight=1.0, kl_weight=0.5, temperature=0.8, reduction="sum")),
+    ], Hs, W
+
+
+def check_grad_finite_differences(O):
+    """Central differences of the reduced loss (float64, h = 1e-6) match the
+    analytic dH and dW to 1e-6 relative, including the upstream gradient."""
+    cases, Hs, W = _fd_cases(O)
+    h = 1e-6
+    for name, t, y, p in cases:
+        g_up = 1.7
+
+        # The teacher is detached: a tied teacher keeps projecting with the
+        # unperturbed W while the student's W moves.
+        t_fixed = O.Teacher("separate", hidden=t.hidden, weight=W.copy()) if t.kind == "tied" else t
+
+        def loss(H_, W_):
+            return O.forward(O.Student(hidden=H_, weight=W_), t_fixed, p, y)["loss"] * g_up
+
+        dH, dW = O.backward(O.Student(hidden=Hs, weight=W), t, p, y, grad_loss=g_up)
+        for X, G, which in ((Hs, dH, "H"), (W, dW, "W")):
+            num = np.zeros_like(X)
+            for ij in np.ndindex(*X.shape):
+                Xp = X.copy()
+                Xm = X.copy()
+                Xp[ij] += h
+                Xm[ij] -= h
+                if which == "H":
+                    num[ij] = (loss(Xp, W) - loss(Xm, W)) / (2 * h)
+                else:
+                    num[ij] = (loss(Hs, Xp) - loss(Hs, Xm)) / (2 * h)
+            err = np.max(np.abs(num - G)) / max(np.max(np.abs(G)), 1e-30)
+            assert err < 1e-6, f"finite differences {name} d{which}: rel err {err:.2e}"
+
+
+def check_grad_autograd_library(O):
+    """dH and dW equal torch autograd through a loss built from library calls
+    (F.cross_entropy with ignore_index, F.kl_div on F.log_softmax)."""
+    cases, Hs, W = _fd_cases(O)
+    for name, t, y, p in cases:
+        if t.kind == "topk":
+            continue
+        H_ = torch.tensor(Hs, requires_grad=True)
+        W_ = torch.tensor(W, requires_grad=True)
+        z = H_ @ W_.T
+        tl = torch.from_numpy(t.hidden @ (s_w := (W if t.kind == "tied" else t.weight)).T)
+        del s_w
+        yt = torch.from_numpy(y)
+        valid = yt != -100
+        T = p.temperature
+        ce = F.cross_entropy(z, yt, ignore_index=-100, reduction="none")
+        kl = F.kl_div(F.log_softmax(z / T, -1), F.log_softmax(tl / T, -1), log_target=True,
+                      reduction="none").sum(-1) * T * T
+        total = (p.student_ce_weight * ce + p.kl_weight * kl)[valid].sum()
+        den = float(valid.sum()) if p.reduction == "mean" else 1.0
+        (total / den).backward()
+        dH, dW = O.backward(O.Student(hidden=Hs, weight=W), t, p, y)
+        _close(dH, H_.grad.numpy(), rtol=1e-10, atol=1e-13, what=f"autograd dH {name}")
+        _close(dW, W_.grad.numpy(), rtol=1e-10, atol=1e-13, what=f"autograd dW {name}")
+
+
+def check_grad_invariants(O):
+    """Every logit-gradient row sums to zero, hence sum_v dW[v, :] = 0; and
+    tr(dH^T H) = tr(dW^T W) (both equal sum dz * z)."""
+    cases, Hs, W = _fd_cases(O)
+    for name, t, y, p in cases:
+        dH, dW = O.backward(O.Student(hidden=Hs, weight=W), t, p, y)
+        scale = np.abs(dW).max()
+        _close(dW.sum(0) / scale, 0.0, atol=1e-12, what=f"sum_v dW {name}")
+        a = (dH * Hs).sum()
+        b = (dW * W).sum()
+        _close(a, b, rtol=1e-10, atol=1e-13, what=f"trace identity {name}")
+
+
+def check_backward_rows_consistent(O):
+    """dH for a subset of rows equals those rows of the full dH."""
+    cases, Hs, W = _fd_cases(O)
+    for name, t, y, p in cases:
+        s = O.Student(hidden=Hs, weight=W)
+        dH, _ = O.backward(s, t, p, y)
+        out = O.forward(s, t, p, y)
+        rows = np.array([3, 1])
+        _close(O.backward_rows(s, t, p, y, rows, out["den"]), dH[rows], what=f"rows {name}")
+
+
+ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

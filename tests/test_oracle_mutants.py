@@ -1,0 +1,72 @@
+"""Each planted mistake in a copy of the oracle must fail at least one pin.
+
+The mistakes are the plausible ones: a dropped factor, a wrong sign, an
+off-by-one index, a transposed or swapped operand, a wrong normaliser. The
+copies are built from the oracle source on the CPU; the real oracle is not
+touched.
+"""
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "oracle.py")
+
+MUTANTS = {
+    "kl_without_T2": ("return (T * T) * (np.exp(lp_t)", "return (np.exp(lp_t)"),
+    "kl_teacher_not_tempered": ("lp_t = log_softmax(teacher_logits / T)",
+                                "lp_t = log_softmax(teacher_logits)"),
+    "kl_reversed": ("(np.exp(lp_t) * (lp_t - lp_s))", "(np.exp(lp_s) * (lp_s - lp_t))"),
+    "ce_label_off_by_one": ("picked = np.take_along_axis(logits, y[:, None], axis=1)",
+                            "picked = np.take_along_axis(logits, (y[:, None] + 1) % logits.shape[1], axis=1)"),
+    "ce_ignored_not_zeroed": ("return np.where(valid, logsumexp(logits) - picked, 0.0)",
+                              "return logsumexp(logits) - picked"),
+    "lse_missing_shift": ("return m + np.log(np.exp(x - m[..., None]).sum(axis=-1))",
+                          "return np.log(np.exp(x - m[..., None]).sum(axis=-1))"),
+    "topk_mass_dropped": ("return entropy_term - cross_term + mass * logsumexp(student_logits)",
+                          "return entropy_term - cross_term + logsumexp(student_logits)"),
+    "topk_entropy_sign": ("return entropy_term - cross_term + mass",
+                          "return -entropy_term - cross_term + mass"),
+    "dkl_missing_T": ("return T * (softmax(student_logits / T) - softmax(teacher_logits / T))",
+                      "return (softmax(student_logits / T) - softmax(teacher_logits / T))"),
+    "dtopk_plus_p": ("np.subtract.at(g,", "np.add.at(g,"),
+    "dce_label_not_subtracted": ("g[rows, np.asarray(labels, dtype=np.int64)[rows]] -= 1.0",
+                                 "pass"),
+    "den_counts_all_rows": ("return float(max(n_valid, 1))", "return float(max(n_valid + 1, 1))"),
+    "grad_not_masked": ("    g[~valid] = 0.0\n    return g * (grad_loss / den)",
+                        "    return g * (grad_loss / den)"),
+    "dW_uses_teacher_hidden": ("dW += g.T @ as_f64(student.hidden[r])",
+                               "dW += g.T @ as_f64((teacher.hidden if teacher.hidden is not None and teacher.hidden.shape == student.hidden.shape else student.hidden)[r])"),
+    "dH_transposed_weight_rows": ("dH[r] = g @ W", "dH[r] = g @ W[::-1]"),
+    "grad_loss_ignored": ("return g * (grad_loss / den)", "return g * (1.0 / den)"),
+    "out_of_range_label_valid": ("return (y != ignore_index) & (y >= 0) & (y < vocab)",
+                                 "return (y != ignore_index)"),
+}
+
+
+def _load_mutant(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutant {name}: anchor not found exactly once"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__file__ = SRC
+    sys.modules[mod.__name__] = mod
+    exec(compile(src.replace(old, new), SRC, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    mod = _load_mutant(name, old, new)
+    failures = []
+    for check in pins.ALL:
+        try:
+            check(mod)
+        except Exception as e:  # AssertionError, or an error the mistake provokes
+            failures.append((check.__name__, type(e).__name__))
+    assert failures, f"planted mistake {name} passed every pin"
