@@ -1,0 +1,214 @@
+/*
+ * kd_loss.h — C ABI of the fused LM-head + cross-entropy + KL distillation loss
+ * for AMD MI355X (gfx950).
+ *
+ * What it computes (sources are the four pages this library follows, cited by
+ * page title and section):
+ *
+ *   z = H_s W^T (student logits, never stored), t = teacher logits:
+ *     TIED      t = H_t W^T      (orda-kernel, Teacher descriptors: TiedTeacher)
+ *     SEPARATE  t = H_t W_t^T    (orda-kernel, Teacher descriptors: SeparateTeacher;
+ *                                 the hidden+weight form of PrecomputedTeacher)
+ *     TOPK      cached (idx, p)  (CompactifAI/Full-Chunked-KL-Loss, Methods)
+ *   per token i, with valid_i = (y_i != ignore_index and 0 <= y_i < V):
+ *     student_ce_i = valid_i * (lse(z_i) - z_i[y_i])              (T = 1)
+ *     teacher_ce_i = valid_i * (lse(t_i) - t_i[y_i])              (T = 1)
+ *     kl_i = T^2 * KL(softmax(t_i/T) || softmax(z_i/T))   for every row
+ *            (nemo kd_loss, KDLoss temperature; orda-kernel, KL variants "forward")
+ *     TOPK: kl_i = sum_k p log p - sum_k p z[idx_k] + M_i lse(z_i), M_i = sum_k p
+ *            (CompactifAI/Full-Chunked-KL-Loss, Methods: objective)
+ *   loss = sum_i valid_i (w_s student_ce_i + w_t teacher_ce_i + w_kl kl_i) / den
+ *     den = normalizer if > 0 (nemo kd_loss, KDLoss.forward num_batch_labels),
+ *           max(n_valid, 1) for MEAN, 1 for SUM (orda-kernel, Parameters: reduction).
+ *   Gradients (teacher detached; CompactifAI/Full-Chunked-KL-Loss, Full Chunked KL):
+ *     dz_i = (g / den) valid_i [w_s (softmax z_i - e_y) + w_kl T (softmax(z_i/T) - softmax(t_i/T))]
+ *     TOPK: dz_i = (g / den) w_kl (M_i softmax z_i - p_i scattered)
+ *     dH = dZ W,  dW = dZ^T H_s.
+ *
+ * The (n, v) logits are never materialised: the forward streams vocabulary
+ * tiles through registers with online (max, rescaled sum) statistics
+ * (flash_kd, module description), and the backward recomputes each vocabulary
+ * chunk and writes only an (n, chunk) gradient slab.
+ *
+ * Conventions.
+ *   - Every pointer in the structs below is a DEVICE pointer, except the
+ *     structs themselves and the host pointers named as such.
+ *   - Row-major everywhere: hidden [n, d], weight [v, d], logits [n, v],
+ *     topk_idx / topk_prob [n, k], labels [n].
+ *   - The caller allocates and owns every buffer (inputs, outputs, saved,
+ *     workspace). The library never allocates, frees or synchronises, except
+ *     kd_read_status, which synchronises the stream it is given.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and returns before it runs. Calls that overlap in time need distinct
+ *     workspaces. Inputs are read only; outputs are overwritten (except dH/dW
+ *     with accumulate = 1).
+ *   - Results are deterministic: no atomics, fixed reduction orders.
+ *   - Errors found on the host return synchronously before anything is
+ *     enqueued. A label outside [0, v) that is not ignore_index, or a top-K
+ *     index outside [0, v), is treated as ignored / skipped and raises a device
+ *     flag read by kd_read_status; such values are never used as addresses
+ *     (orda-kernel, Parameters: ignore_index).
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef KD_LOSS_H
+#define KD_LOSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kd_status;
+enum {
+  KD_OK = 0,
+  KD_ERR_NULL = 1,         /* a required pointer is NULL */
+  KD_ERR_SHAPE = 2,        /* n, d, v, d_t or k out of range, or inconsistent */
+  KD_ERR_DTYPE = 3,        /* unknown dtype, or a mode that does not accept it */
+  KD_ERR_PARAM = 4,        /* temperature/weights not finite or not allowed, bad reduction */
+  KD_ERR_ALIGN = 5,        /* a pointer not 16-byte aligned, or d / d_t not a multiple of 8 */
+  KD_ERR_WORKSPACE = 6,    /* workspace smaller than kd_workspace_bytes, or saved missing */
+  KD_ERR_UNSUPPORTED = 7,  /* valid but not provided (e.g. backward of the logits scorer) */
+  KD_ERR_LABEL_RANGE = 8,  /* device flag: a label or top-K index was out of range */
+  KD_ERR_HIP = 9           /* a HIP launch or runtime call failed */
+};
+
+/* Element type of hidden / weight / logits. Accumulation is always fp32. */
+enum { KD_F32 = 0, KD_BF16 = 1 };
+
+/* Student side. PROJECTION: logits z = hidden @ weight^T (forward + backward).
+ * LOGITS: z is given as `logits` [n, v] (flash_kd, flash_ce_kd_loss:
+ * student_logits); forward only, and the teacher must be SEPARATE. */
+enum { KD_STUDENT_PROJECTION = 0, KD_STUDENT_LOGITS = 1 };
+
+/* Teacher descriptor kinds (orda-kernel, Teacher descriptors). */
+enum { KD_TEACHER_TIED = 1, KD_TEACHER_SEPARATE = 2, KD_TEACHER_TOPK = 3 };
+
+/* Loss reduction (orda-kernel, Parameters: reduction). NONE produces the
+ * per-token outputs and the sum in `loss`; it has no backward. */
+enum { KD_REDUCE_MEAN = 0, KD_REDUCE_SUM = 1, KD_REDUCE_NONE = 2 };
+
+typedef struct {
+  int32_t kind;        /* KD_STUDENT_* */
+  int32_t dtype;       /* KD_F32 | KD_BF16: hidden, weight, logits and the teacher tensors */
+  int64_t n;           /* tokens (flattened batch x sequence), 1 <= n < 2^31 */
+  int64_t d;           /* student hidden size (PROJECTION), multiple of 8 */
+  int64_t v;           /* vocabulary size, 1 <= v < 2^31 */
+  const void* hidden;  /* [n, d]  PROJECTION */
+  const void* weight;  /* [v, d]  PROJECTION */
+  const void* logits;  /* [n, v]  LOGITS */
+} kd_student;
+
+typedef struct {
+  int32_t kind;             /* KD_TEACHER_* */
+  int32_t k;                /* TOPK: entries per row, 1 <= k <= v */
+  int64_t d_t;              /* SEPARATE: teacher hidden size (multiple of 8); TIED: 0 or d */
+  const void* hidden;       /* TIED [n, d], SEPARATE [n, d_t]; student dtype */
+  const void* weight;       /* SEPARATE [v, d_t]; student dtype */
+  const int32_t* topk_idx;  /* TOPK [n, k], distinct per row */
+  const float* topk_prob;   /* TOPK [n, k], not renormalised (sum = retained mass M) */
+} kd_teacher;
+
+typedef struct {
+  float student_ce_weight;   /* w_s >= 0, finite (orda-kernel, Parameters) */
+  float teacher_ce_weight;   /* w_t >= 0; the teacher is detached: no gradient */
+  float kl_weight;           /* w_kl >= 0 */
+  float temperature;         /* T > 0, finite; TOPK requires T == 1 */
+  int64_t ignore_index;      /* label value excluded from CE and from the loss */
+  int32_t reduction;         /* KD_REDUCE_* */
+  float normalizer;          /* > 0: divide the summed loss by it (num_batch_labels) */
+  int64_t vocab_chunk;       /* vocabulary columns per streaming step; 0 = library default */
+  int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
+} kd_params;
+
+/* Forward outputs, all device pointers, each nullable (NULL = not written).
+ * loss: one fp32; student_ce, teacher_ce, kl: fp32 [n]. The per-token kl
+ * includes T^2 and is given for every row, ignored ones too; the CE terms are
+ * 0 on ignored rows (flash_kd, flash_ce_kd_loss: labels and Returns). */
+typedef struct {
+  float* loss;
+  float* student_ce;
+  float* teacher_ce;
+  float* kl;
+} kd_outputs;
+
+/* Optional timing hook for profiling. When non-NULL, the library records
+ * events[count] before and events[count+1] after each launch whose class bit
+ * is set in `mask`, stores the class in kinds[count/2] and adds 2 to count,
+ * while count + 2 <= capacity. Events are hipEvent_t handles made by
+ * kd_events_create; `kinds` is a host array of capacity/2 entries. */
+enum {
+  KD_KERNEL_PREP = 0,      /* label logits, validity, top-K sums */
+  KD_KERNEL_FWD = 1,       /* forward projection tiles + online-softmax epilogue */
+  KD_KERNEL_MERGE = 2,     /* per-token merge of vocabulary-slice records */
+  KD_KERNEL_FINALIZE = 3,  /* loss reduction */
+  KD_KERNEL_BWD_DZ = 4,    /* backward recompute tiles + logit-gradient epilogue */
+  KD_KERNEL_SCATTER = 5,   /* top-K: subtract p at the cached indices */
+  KD_KERNEL_GEMM_DW = 6,   /* dW[chunk] = dZ_chunk^T H */
+  KD_KERNEL_GEMM_DH = 7    /* dH += dZ_chunk W[chunk] */
+};
+typedef struct {
+  void** events;     /* host array of hipEvent_t */
+  int32_t* kinds;    /* host array */
+  int32_t capacity;  /* number of entries in events */
+  int32_t count;     /* events recorded so far (updated by the library) */
+  uint32_t mask;     /* bit KD_KERNEL_x set: bracket launches of that class */
+} kd_trace;
+
+/* Bytes of device workspace one call needs (for_backward = 0: kd_loss_fwd,
+ * 1: kd_loss_bwd). Validates the descriptors like the calls do. */
+kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                             int32_t for_backward, size_t* bytes /* host */);
+
+/* Bytes of the buffer that carries per-row statistics from forward to
+ * backward: 16 per row plus a 64-byte header. One backward per forward
+ * (orda-kernel, Quickstart: each fused forward supports one backward pass). */
+size_t kd_saved_bytes(int64_t n);
+
+/* Forward: per-token outputs, the reduced loss, and `saved` for the backward
+ * (saved may be NULL when no backward follows). labels: int64 [n]; NULL means
+ * every row is valid and no CE is computed (then w_s and w_t must be 0); TOPK
+ * takes no labels. workspace: ws_bytes >= kd_workspace_bytes(..., 0). */
+kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                      const int64_t* labels, const kd_outputs* out, void* saved,
+                      void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
+
+/* Backward of the reduced loss to the student hidden states and weight.
+ * saved: written by the matching kd_loss_fwd with the same inputs and params.
+ * grad_loss: device fp32 scalar (upstream gradient of loss), NULL = 1.
+ * d_hidden: fp32 [n, d], d_weight: fp32 [v, d], each nullable (NULL = skip).
+ * accumulate = 1 adds into d_hidden / d_weight (orda-kernel, Parameters:
+ * KernelConfig weight-gradient accumulation); 0 overwrites.
+ * Not available for LOGITS students or REDUCE_NONE (KD_ERR_UNSUPPORTED). */
+kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                      const int64_t* labels, const void* saved, const float* grad_loss,
+                      float* d_hidden, float* d_weight, int32_t accumulate,
+                      void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
+
+/* Synchronises `stream`, then reads the device flags left in `workspace` by
+ * the last kd_loss_fwd that used it: *flags (host, nullable) receives them;
+ * returns KD_ERR_LABEL_RANGE if a label or top-K index was out of range. */
+kd_status kd_read_status(const void* workspace, void* stream, int32_t* flags);
+
+/* Static description of a status code. */
+const char* kd_status_string(kd_status st);
+
+/* 1 if `device` is a gfx950 GPU this library was built for, else 0
+ * (cf. orda-kernel, Installation: is_available). */
+int32_t kd_device_supported(int32_t device);
+
+/* Timing helpers for kd_trace: create / destroy n timing events, and the
+ * elapsed milliseconds between two recorded events (waits for the second). */
+kd_status kd_events_create(void** events /* host [n] */, int32_t n);
+kd_status kd_events_destroy(void** events, int32_t n);
+kd_status kd_event_elapsed_ms(void* start, void* stop, float* ms /* host */);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* kd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_LOSS_H */

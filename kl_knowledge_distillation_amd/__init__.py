@@ -8,7 +8,7 @@ point raises if it is missing (there is no CPU fallback).
 from __future__ import annotations
 
 __all__ = [
-    "distillation_loss", "flash_ce_kd_loss", "kd_div_loss", "DistillationLossOutput",
+    "distillation_loss", "flash_ce_kd_loss", "DistillationLossOutput", "Runner", "Tracer",
     "TiedTeacher", "SeparateTeacher", "PrecomputedTeacher", "TopKTeacher",
     "DistillationLoss", "is_available", "lib",
 ]

@@ -1,0 +1,356 @@
+"""PyTorch-facing API over the C ABI. Torch provides device memory and streams only.
+
+Every computation runs in libkdloss.so; this module builds the descriptors,
+allocates outputs / saved / workspace with the torch caching allocator and
+passes pointers. If the library is missing, every entry point raises.
+
+User API (orda-kernel, Quickstart / Teacher descriptors / Parameters):
+    distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
+                      teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
+                      kl_divergence="forward", ignore_index=-100, reduction="mean",
+                      num_batch_labels=None, vocab_chunk=0) -> DistillationLossOutput
+    teachers: TiedTeacher(hidden), SeparateTeacher(hidden, weight),
+              PrecomputedTeacher(teacher_hidden=..., teacher_weight=...),
+              TopKTeacher(indices, probs)   (Full-Chunked-KL-Loss cached top-K)
+Scorer (flash_kd, flash_ce_kd_loss):
+    flash_ce_kd_loss(student_logits, teacher_hidden, teacher_lm_head_weight, labels, *,
+                     temperature=1.0, ignore_index=-1, chunk_size=16384) -> (ce, kd)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib as L
+
+
+# ---------------------------------------------------------------------------
+# Teacher descriptors
+# ---------------------------------------------------------------------------
+
+@dataclass
+class TiedTeacher:
+    """Teacher that shares the student's projection weight; hidden: (BT, hidden)."""
+    hidden: torch.Tensor
+    mode: Optional[str] = None
+
+
+@dataclass
+class SeparateTeacher:
+    """Teacher with its own hidden (BT, D_t) and projection (vocab, D_t); detached."""
+    hidden: torch.Tensor
+    weight: torch.Tensor
+
+
+@dataclass
+class PrecomputedTeacher:
+    """Cached teacher given as teacher_hidden + teacher_weight (no gradient)."""
+    teacher_hidden: torch.Tensor
+    teacher_weight: torch.Tensor
+
+
+@dataclass
+class TopKTeacher:
+    """Cached sparse teacher: per row K distinct indices (int32) and probabilities (fp32),
+    not renormalised."""
+    indices: torch.Tensor
+    probs: torch.Tensor
+
+
+class DistillationLossOutput(NamedTuple):
+    loss: torch.Tensor
+    student_ce: torch.Tensor
+    teacher_ce: torch.Tensor
+    kl: torch.Tensor
+
+
+def is_available(device: int = 0) -> bool:
+    """True when the library is built and `device` is a gfx950 GPU."""
+    try:
+        lib = L.load()
+    except Exception:
+        return False
+    if not torch.cuda.is_available():
+        return False
+    return bool(lib.kd_device_supported(device))
+
+
+def lib():
+    return L.load()
+
+
+_DTYPES = {torch.float32: L.KD_F32, torch.bfloat16: L.KD_BF16}
+_REDUCTIONS = {"mean": L.KD_REDUCE_MEAN, "sum": L.KD_REDUCE_SUM, "none": L.KD_REDUCE_NONE}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+class Runner:
+    """One configured loss call with its buffers; reusable across steps.
+
+    Holds the C descriptors, the per-token outputs, the scalar loss, the saved
+    statistics and the forward/backward workspaces. ``forward()`` and
+    ``backward()`` enqueue on the current torch stream and return at once.
+    """
+
+    def __init__(self, *, student_hidden=None, weight=None, student_logits=None, labels=None,
+                 teacher_kind="tied", teacher_hidden=None, teacher_weight=None, topk_idx=None,
+                 topk_prob=None, student_ce_weight=1.0, teacher_ce_weight=0.0, kl_weight=0.0,
+                 temperature=1.0, ignore_index=-100, reduction="mean", normalizer=0.0,
+                 vocab_chunk=0, want_grads=True):
+        self.lib = L.load()
+        ref = student_hidden if student_hidden is not None else student_logits
+        if ref is None:
+            raise ValueError("student_hidden or student_logits is required")
+        if not ref.is_cuda:
+            raise ValueError("inputs must be on a GPU device")
+        self.device = ref.device
+        dtype = _DTYPES.get(ref.dtype)
+        if dtype is None:
+            raise ValueError(f"unsupported dtype {ref.dtype}")
+        # keep the tensors alive for the lifetime of the descriptors
+        self._keep = [student_hidden, weight, student_logits, labels, teacher_hidden,
+                      teacher_weight, topk_idx, topk_prob]
+        self.labels = labels
+        s = L.KdStudent()
+        s.dtype = dtype
+        if student_logits is not None:
+            s.kind = L.KD_STUDENT_LOGITS
+            s.n, s.v = student_logits.shape
+            s.d = 0
+            s.logits = _ptr(student_logits)
+        else:
+            s.kind = L.KD_STUDENT_PROJECTION
+            s.n, s.d = student_hidden.shape
+            s.v = weight.shape[0]
+            if weight.shape[1] != s.d:
+                raise ValueError("weight must be (vocab, hidden)")
+            s.hidden = _ptr(student_hidden)
+            s.weight = _ptr(weight)
+        t = L.KdTeacher()
+        if teacher_kind == "tied":
+            t.kind = L.KD_TEACHER_TIED
+            t.d_t = teacher_hidden.shape[1]
+            t.hidden = _ptr(teacher_hidden)
+        elif teacher_kind == "separate":
+            t.kind = L.KD_TEACHER_SEPARATE
+            t.d_t = teacher_hidden.shape[1]
+            t.hidden = _ptr(teacher_hidden)
+            t.weight = _ptr(teacher_weight)
+        elif teacher_kind == "topk":
+            t.kind = L.KD_TEACHER_TOPK
+            t.k = topk_idx.shape[1]
+            t.topk_idx = _ptr(topk_idx)
+            t.topk_prob = _ptr(topk_prob)
+        else:
+            raise ValueError(f"unknown teacher kind {teacher_kind}")
+        p = L.KdParams()
+        p.student_ce_weight = student_ce_weight
+        p.teacher_ce_weight = teacher_ce_weight
+        p.kl_weight = kl_weight
+        p.temperature = temperature
+        p.ignore_index = ignore_index
+        p.reduction = _REDUCTIONS[reduction]
+        p.normalizer = float(normalizer or 0.0)
+        p.vocab_chunk = int(vocab_chunk)
+        self.s, self.t, self.p = s, t, p
+        self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.loss = torch.zeros((), **f32)
+        self.student_ce = torch.empty(self.n, **f32)
+        self.teacher_ce = torch.empty(self.n, **f32)
+        self.kl = torch.empty(self.n, **f32)
+        self.out = L.KdOutputs(self.loss.data_ptr(), self.student_ce.data_ptr(),
+                               self.teacher_ce.data_ptr(), self.kl.data_ptr())
+        self.saved = torch.empty(self.lib.kd_saved_bytes(self.n), dtype=torch.uint8,
+                                 device=self.device)
+        self.ws_fwd = self._workspace(0)
+        self.ws_bwd = self._workspace(1) if (want_grads and s.kind == L.KD_STUDENT_PROJECTION) \
+            else None
+        self.labels_ptr = _ptr(labels)
+
+    def _workspace(self, backward: int) -> torch.Tensor:
+        nb = ctypes.c_size_t(0)
+        L.check(self.lib.kd_workspace_bytes(ctypes.byref(self.s), ctypes.byref(self.t),
+                                            ctypes.byref(self.p), backward, ctypes.byref(nb)),
+                "kd_workspace_bytes")
+        return torch.empty(max(int(nb.value), 256), dtype=torch.uint8, device=self.device)
+
+    @staticmethod
+    def _stream() -> int:
+        return torch.cuda.current_stream().cuda_stream
+
+    def forward(self, trace: Optional[L.KdTrace] = None) -> None:
+        st = self.lib.kd_loss_fwd(ctypes.byref(self.s), ctypes.byref(self.t), ctypes.byref(self.p),
+                                  self.labels_ptr, ctypes.byref(self.out), self.saved.data_ptr(),
+                                  self.ws_fwd.data_ptr(), self.ws_fwd.numel(), self._stream(),
+                                  ctypes.byref(trace) if trace is not None else None)
+        L.check(st, "kd_loss_fwd")
+
+    def backward(self, d_hidden: Optional[torch.Tensor], d_weight: Optional[torch.Tensor],
+                 grad_loss: Optional[torch.Tensor] = None, accumulate: bool = False,
+                 trace: Optional[L.KdTrace] = None) -> None:
+        for g, shape in ((d_hidden, (self.n, self.d)), (d_weight, (self.v, self.d))):
+            if g is not None and (g.dtype != torch.float32 or tuple(g.shape) != shape
+                                  or not g.is_contiguous()):
+                raise ValueError(f"gradient buffers must be contiguous fp32 {shape}")
+        st = self.lib.kd_loss_bwd(ctypes.byref(self.s), ctypes.byref(self.t), ctypes.byref(self.p),
+                                  self.labels_ptr, self.saved.data_ptr(), _ptr(grad_loss),
+                                  _ptr(d_hidden), _ptr(d_weight), int(accumulate),
+                                  self.ws_bwd.data_ptr(), self.ws_bwd.numel(), self._stream(),
+                                  ctypes.byref(trace) if trace is not None else None)
+        L.check(st, "kd_loss_bwd")
+
+    def read_status(self) -> int:
+        flags = ctypes.c_int32(0)
+        self.lib.kd_read_status(self.ws_fwd.data_ptr(), self._stream(), ctypes.byref(flags))
+        return int(flags.value)
+
+
+class Tracer:
+    """Brackets library launches with HIP events (kd_trace) and reports the
+    mean duration per kernel class."""
+
+    def __init__(self, capacity: int = 4096, kernels=("fwd",)):
+        self.lib = L.load()
+        self.capacity = capacity
+        self.events = (ctypes.c_void_p * capacity)()
+        self.kinds = (ctypes.c_int32 * (capacity // 2))()
+        L.check(self.lib.kd_events_create(self.events, capacity), "kd_events_create")
+        mask = 0
+        for k in kernels:
+            mask |= 1 << L.KERNEL_ID[k]
+        self.trace = L.KdTrace(self.events, self.kinds, capacity, 0, mask)
+
+    def reset(self) -> None:
+        self.trace.count = 0
+
+    def durations_ms(self) -> dict:
+        out = {}
+        ms = ctypes.c_float(0)
+        for j in range(self.trace.count // 2):
+            L.check(self.lib.kd_event_elapsed_ms(self.events[2 * j], self.events[2 * j + 1],
+                                                 ctypes.byref(ms)), "kd_event_elapsed_ms")
+            out.setdefault(L.KERNELS[self.kinds[j]], []).append(ms.value)
+        return out
+
+    def close(self) -> None:
+        if self.events is not None:
+            self.lib.kd_events_destroy(self.events, self.capacity)
+            self.events = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------
+# Autograd function (orda-kernel style API)
+# ---------------------------------------------------------------------------
+
+class _FusedLoss(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, student_hidden, weight, runner: Runner):
+        runner.forward()
+        ctx.runner = runner
+        ctx.used = False
+        return (runner.loss.clone(), runner.student_ce.clone(), runner.teacher_ce.clone(),
+                runner.kl.clone())
+
+    @staticmethod
+    def backward(ctx, g_loss, g_sce, g_tce, g_kl):
+        # Only the reduced loss is differentiated; the components are for logging
+        # (orda-kernel, Quickstart: components are unweighted for logging).
+        if ctx.used:
+            raise RuntimeError("each fused forward supports one backward pass")
+        ctx.used = True
+        r: Runner = ctx.runner
+        need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        dh = torch.empty((r.n, r.d), dtype=torch.float32, device=r.device) if need_h else None
+        dw = torch.empty((r.v, r.d), dtype=torch.float32, device=r.device) if need_w else None
+        g = (g_loss if g_loss is not None else torch.ones((), device=r.device))
+        g = g.detach().to(torch.float32).contiguous()
+        r.backward(dh, dw, grad_loss=g)
+        return dh, dw, None
+
+
+_KL_SUPPORTED = ("forward",)
+
+
+def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
+                      teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
+                      kl_divergence="forward", ignore_index=-100, reduction="mean",
+                      num_batch_labels=None, vocab_chunk=0) -> DistillationLossOutput:
+    """Fused LM-head + CE + KL loss; differentiable in student_hidden and weight.
+
+    The teacher is always detached. Returns the loss and the unweighted per-token
+    components (student_ce, teacher_ce, kl with T^2 included).
+    """
+    if kl_divergence not in _KL_SUPPORTED:
+        raise NotImplementedError(f"kl_divergence={kl_divergence!r}; available: {_KL_SUPPORTED}")
+    kw = dict(student_hidden=student_hidden.detach().contiguous(),
+              weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
+              teacher_ce_weight=teacher_ce_weight, kl_weight=kl_weight,
+              temperature=kl_temperature, ignore_index=ignore_index, reduction=reduction,
+              normalizer=float(num_batch_labels or 0), vocab_chunk=vocab_chunk)
+    if isinstance(teacher, TiedTeacher):
+        kw.update(teacher_kind="tied", teacher_hidden=teacher.hidden.detach().contiguous())
+    elif isinstance(teacher, (SeparateTeacher, PrecomputedTeacher)):
+        h = teacher.hidden if isinstance(teacher, SeparateTeacher) else teacher.teacher_hidden
+        w = teacher.weight if isinstance(teacher, SeparateTeacher) else teacher.teacher_weight
+        kw.update(teacher_kind="separate", teacher_hidden=h.detach().contiguous(),
+                  teacher_weight=w.detach().contiguous())
+    elif isinstance(teacher, TopKTeacher):
+        kw.update(teacher_kind="topk", topk_idx=teacher.indices.to(torch.int32).contiguous(),
+                  topk_prob=teacher.probs.to(torch.float32).contiguous())
+        labels = None
+    else:
+        raise TypeError(f"unknown teacher descriptor {type(teacher).__name__}")
+    if labels is not None:
+        kw["labels"] = labels.to(torch.int64).contiguous()
+    runner = Runner(**kw)
+    loss, sce, tce, kl = _FusedLoss.apply(student_hidden, weight, runner)
+    return DistillationLossOutput(loss, sce, tce, kl)
+
+
+class DistillationLoss(torch.nn.Module):
+    """Module form of distillation_loss with the weights fixed at construction."""
+
+    def __init__(self, **kwargs):
+        super().__init__()
+        self.kwargs = kwargs
+
+    def forward(self, student_hidden, weight, labels, teacher):
+        return distillation_loss(student_hidden, weight, labels, teacher, **self.kwargs)
+
+
+def flash_ce_kd_loss(student_logits, teacher_hidden, teacher_lm_head_weight, labels, *,
+                     temperature=1.0, ignore_index=-1, chunk_size=16384, upcast=True):
+    """Forward-only per-token CE and KL(P_T || P_S) from given student logits.
+
+    flash_kd, flash_ce_kd_loss: teacher logits are recomputed chunk by chunk;
+    ignore_index rows get CE 0; the returned KD is NOT multiplied by T^2.
+    Accumulation is always fp32 (``upcast`` is accepted for compatibility).
+    """
+    del upcast
+    with torch.no_grad():
+        r = Runner(student_logits=student_logits.contiguous(), labels=labels.to(torch.int64)
+                   .contiguous(), teacher_kind="separate",
+                   teacher_hidden=teacher_hidden.contiguous(),
+                   teacher_weight=teacher_lm_head_weight.contiguous(), student_ce_weight=1.0,
+                   kl_weight=1.0, temperature=temperature, ignore_index=ignore_index,
+                   reduction="none", vocab_chunk=chunk_size, want_grads=False)
+        r.forward()
+        kd = r.kl / (temperature * temperature)
+        return r.student_ce.clone(), kd

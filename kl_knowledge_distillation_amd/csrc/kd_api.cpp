@@ -1,0 +1,282 @@
+// C ABI of the distillation-loss library: argument validation, launch
+// planning and workspace sizing. Every check here runs on the host before
+// anything is enqueued, so invalid calls never reach the GPU.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kd_internal.hpp"
+
+namespace {
+
+using kd::Plan;
+
+constexpr int64_t kTile = 128;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kDefaultChunk = 8192;
+constexpr int64_t kTargetFwdBlocks = 4096;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
+
+kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                    const int64_t* labels, bool check_labels_ptr, bool backward, Plan* out) {
+  if (!s || !t || !p || !out) return KD_ERR_NULL;
+  Plan q;
+  if (s->dtype != KD_F32 && s->dtype != KD_BF16) return KD_ERR_DTYPE;
+  q.dtype = s->dtype;
+  if (s->n < 1 || s->n >= kMaxDim || s->v < 1 || s->v >= kMaxDim) return KD_ERR_SHAPE;
+  q.n = s->n;
+  q.v = s->v;
+  const int64_t vec = (s->dtype == KD_BF16) ? 8 : 4;  // elements per 16-byte chunk
+
+  if (s->kind == KD_STUDENT_PROJECTION) {
+    if (!s->hidden || !s->weight) return KD_ERR_NULL;
+    if (s->d < 1 || s->d >= kMaxDim) return KD_ERR_SHAPE;
+    if (s->d % 8 != 0 || !aligned16(s->hidden) || !aligned16(s->weight)) return KD_ERR_ALIGN;
+    q.d = s->d;
+  } else if (s->kind == KD_STUDENT_LOGITS) {
+    if (!s->logits) return KD_ERR_NULL;
+    if (t->kind != KD_TEACHER_SEPARATE) return KD_ERR_UNSUPPORTED;
+    if (backward) return KD_ERR_UNSUPPORTED;  // the scorer is forward only (flash_kd)
+    if (((uintptr_t)s->logits & (s->dtype == KD_BF16 ? 1u : 3u)) != 0) return KD_ERR_ALIGN;
+  } else {
+    return KD_ERR_PARAM;
+  }
+  (void)vec;
+
+  switch (t->kind) {
+    case KD_TEACHER_TIED:
+      if (s->kind != KD_STUDENT_PROJECTION) return KD_ERR_UNSUPPORTED;
+      if (!t->hidden) return KD_ERR_NULL;
+      if (t->d_t != 0 && t->d_t != s->d) return KD_ERR_SHAPE;
+      if (!aligned16(t->hidden)) return KD_ERR_ALIGN;
+      q.mode = kd::MODE_TIED;
+      q.dt = s->d;
+      break;
+    case KD_TEACHER_SEPARATE:
+      if (!t->hidden || !t->weight) return KD_ERR_NULL;
+      if (t->d_t < 1 || t->d_t >= kMaxDim) return KD_ERR_SHAPE;
+      if (t->d_t % 8 != 0 || !aligned16(t->hidden) || !aligned16(t->weight)) return KD_ERR_ALIGN;
+      q.mode = (s->kind == KD_STUDENT_LOGITS) ? kd::MODE_LOGITS : kd::MODE_SEPARATE;
+      q.dt = t->d_t;
+      break;
+    case KD_TEACHER_TOPK:
+      if (s->kind != KD_STUDENT_PROJECTION) return KD_ERR_UNSUPPORTED;
+      if (!t->topk_idx || !t->topk_prob) return KD_ERR_NULL;
+      if (t->k < 1 || (int64_t)t->k > s->v) return KD_ERR_SHAPE;
+      if (((uintptr_t)t->topk_idx & 3u) || ((uintptr_t)t->topk_prob & 3u)) return KD_ERR_ALIGN;
+      q.mode = kd::MODE_TOPK;
+      q.k = t->k;
+      break;
+    default:
+      return KD_ERR_PARAM;
+  }
+
+  if (!isfinite(p->temperature) || p->temperature <= 0.f) return KD_ERR_PARAM;
+  if (!finite_nonneg(p->student_ce_weight) || !finite_nonneg(p->teacher_ce_weight) ||
+      !finite_nonneg(p->kl_weight))
+    return KD_ERR_PARAM;
+  if (p->reduction != KD_REDUCE_MEAN && p->reduction != KD_REDUCE_SUM &&
+      p->reduction != KD_REDUCE_NONE)
+    return KD_ERR_PARAM;
+  if (!isfinite(p->normalizer) || p->normalizer < 0.f) return KD_ERR_PARAM;
+  if (p->vocab_chunk < 0) return KD_ERR_PARAM;
+  if (backward && p->reduction == KD_REDUCE_NONE) return KD_ERR_UNSUPPORTED;
+  if (q.mode == kd::MODE_TOPK) {
+    // The cached teacher has no temperature and no labels (Full-Chunked-KL-Loss, Methods).
+    if (p->temperature != 1.f) return KD_ERR_UNSUPPORTED;
+    if (p->student_ce_weight != 0.f || p->teacher_ce_weight != 0.f) return KD_ERR_PARAM;
+    if (check_labels_ptr && labels) return KD_ERR_PARAM;
+  } else if (check_labels_ptr && !labels &&
+             (p->student_ce_weight != 0.f || p->teacher_ce_weight != 0.f)) {
+    return KD_ERR_NULL;
+  }
+  if (check_labels_ptr && labels && ((uintptr_t)labels & 7u)) return KD_ERR_ALIGN;
+
+  q.ws = p->student_ce_weight;
+  q.wt = p->teacher_ce_weight;
+  q.wkl = p->kl_weight;
+  q.T = p->temperature;
+  q.ignore = p->ignore_index;
+  q.reduction = p->reduction;
+  q.normalizer = p->normalizer;
+  q.need_zT = (q.T != 1.f) ? 1 : 0;
+  q.need_t1 = (q.T != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
+  q.has_labels = labels ? 1 : 0;
+
+  // Forward grid: (vocabulary slice) x (128-token tile).
+  q.n_ttiles = (int)ceil_div(q.n, kTile);
+  q.n_vtiles = (int)ceil_div(q.v, kTile);
+  int64_t tps;
+  if (p->vocab_chunk > 0) {
+    tps = ceil_div(p->vocab_chunk, kTile);
+  } else {
+    tps = ((int64_t)q.n_vtiles * q.n_ttiles) / kTargetFwdBlocks;
+  }
+  tps = std::max<int64_t>(1, std::min<int64_t>(tps, q.n_vtiles));
+  q.tps = (int)tps;
+  q.n_slices = (int)ceil_div(q.n_vtiles, tps);
+  // Backward chunk.
+  int64_t chunk = (p->vocab_chunk > 0) ? ceil_div(p->vocab_chunk, kTile) * kTile : kDefaultChunk;
+  chunk = std::min<int64_t>(chunk, ceil_div(q.v, kTile) * kTile);
+  q.chunk = chunk;
+  q.n_chunks = (int)ceil_div(q.v, chunk);
+  q.merge_blocks = (int)ceil_div(q.n, kd::kMergeThreads);
+
+  size_t off = kd::kStatusBytes;
+  q.off_prep = off;
+  off = align_up(off + 4 * sizeof(float) * (size_t)q.n, 256);
+  q.off_rec = off;
+  off = align_up(off + (size_t)kd::kRecFields * q.n_slices * (size_t)q.n * sizeof(float), 256);
+  q.off_part = off;
+  off = align_up(off + (size_t)q.merge_blocks * 4 * sizeof(double), 256);
+  q.fwd_bytes = off;
+  const size_t elem = (q.dtype == KD_BF16) ? 2 : 4;
+  q.off_dz = kd::kStatusBytes;
+  q.bwd_bytes = align_up(q.off_dz + (size_t)q.n * (size_t)q.chunk * elem, 256);
+  *out = q;
+  return KD_OK;
+}
+
+kd::Tensors tensors_of(const kd_student* s, const kd_teacher* t, const int64_t* labels) {
+  kd::Tensors x;
+  x.hs = s->hidden;
+  x.w = s->weight;
+  x.logits = s->logits;
+  x.labels = labels;
+  if (t->kind == KD_TEACHER_TIED) {
+    x.ht = t->hidden;
+    x.wt = s->weight;
+  } else if (t->kind == KD_TEACHER_SEPARATE) {
+    x.ht = t->hidden;
+    x.wt = t->weight;
+  } else {
+    x.topk_idx = t->topk_idx;
+    x.topk_prob = t->topk_prob;
+  }
+  return x;
+}
+
+}  // namespace
+
+extern "C" {
+
+kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                             int32_t for_backward, size_t* bytes) {
+  if (!bytes) return KD_ERR_NULL;
+  Plan q;
+  const kd_status st = plan_call(s, t, p, nullptr, false, for_backward != 0, &q);
+  if (st != KD_OK) return st;
+  *bytes = for_backward ? q.bwd_bytes : q.fwd_bytes;
+  return KD_OK;
+}
+
+size_t kd_saved_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return 16 * (size_t)n + kd::kSavedHeaderBytes;
+}
+
+kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                      const int64_t* labels, const kd_outputs* out, void* saved, void* workspace,
+                      size_t ws_bytes, void* stream, kd_trace* trace) {
+  Plan q;
+  const kd_status st = plan_call(s, t, p, labels, true, false, &q);
+  if (st != KD_OK) return st;
+  if (!workspace) return KD_ERR_NULL;
+  if (ws_bytes < q.fwd_bytes) return KD_ERR_WORKSPACE;
+  if (!aligned16(workspace) || (saved && !aligned16(saved))) return KD_ERR_ALIGN;
+  if (out) {
+    const void* ptrs[4] = {out->loss, out->student_ce, out->teacher_ce, out->kl};
+    for (const void* ptr : ptrs)
+      if (ptr && ((uintptr_t)ptr & 3u)) return KD_ERR_ALIGN;
+  }
+  return kd::run_forward(q, tensors_of(s, t, labels), out, saved, workspace,
+                         static_cast<hipStream_t>(stream), trace);
+}
+
+kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                      const int64_t* labels, const void* saved, const float* grad_loss,
+                      float* d_hidden, float* d_weight, int32_t accumulate, void* workspace,
+                      size_t ws_bytes, void* stream, kd_trace* trace) {
+  Plan q;
+  const kd_status st = plan_call(s, t, p, labels, true, true, &q);
+  if (st != KD_OK) return st;
+  if (!saved) return KD_ERR_WORKSPACE;
+  if (!workspace) return KD_ERR_NULL;
+  if (ws_bytes < q.bwd_bytes) return KD_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(saved)) return KD_ERR_ALIGN;
+  if ((d_hidden && !aligned16(d_hidden)) || (d_weight && !aligned16(d_weight))) return KD_ERR_ALIGN;
+  if (grad_loss && ((uintptr_t)grad_loss & 3u)) return KD_ERR_ALIGN;
+  if (!d_hidden && !d_weight) return KD_OK;
+  return kd::run_backward(q, tensors_of(s, t, labels), saved, grad_loss, d_hidden, d_weight,
+                          accumulate ? 1 : 0, workspace, static_cast<hipStream_t>(stream), trace);
+}
+
+kd_status kd_read_status(const void* workspace, void* stream, int32_t* flags) {
+  if (!workspace) return KD_ERR_NULL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KD_ERR_HIP;
+  int32_t f = 0;
+  if (hipMemcpy(&f, workspace, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return KD_ERR_HIP;
+  if (flags) *flags = f;
+  return f ? KD_ERR_LABEL_RANGE : KD_OK;
+}
+
+const char* kd_status_string(kd_status st) {
+  switch (st) {
+    case KD_OK: return "ok";
+    case KD_ERR_NULL: return "a required pointer is NULL";
+    case KD_ERR_SHAPE: return "shape out of range or inconsistent";
+    case KD_ERR_DTYPE: return "unsupported dtype";
+    case KD_ERR_PARAM: return "invalid parameter";
+    case KD_ERR_ALIGN: return "misaligned pointer or hidden size not a multiple of 8";
+    case KD_ERR_WORKSPACE: return "workspace too small or saved buffer missing";
+    case KD_ERR_UNSUPPORTED: return "unsupported combination";
+    case KD_ERR_LABEL_RANGE: return "a label or top-K index was out of range";
+    case KD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t kd_device_supported(int32_t device) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return 0;
+  return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+kd_status kd_events_create(void** events, int32_t n) {
+  if (!events || n < 0) return KD_ERR_NULL;
+  for (int32_t i = 0; i < n; ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return KD_ERR_HIP;
+    events[i] = e;
+  }
+  return KD_OK;
+}
+
+kd_status kd_events_destroy(void** events, int32_t n) {
+  if (!events || n < 0) return KD_ERR_NULL;
+  for (int32_t i = 0; i < n; ++i)
+    if (events[i]) {
+      hipEventDestroy(static_cast<hipEvent_t>(events[i]));
+      events[i] = nullptr;
+    }
+  return KD_OK;
+}
+
+kd_status kd_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return KD_ERR_NULL;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return KD_ERR_HIP;
+  if (hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) !=
+      hipSuccess)
+    return KD_ERR_HIP;
+  return KD_OK;
+}
+
+const char* kd_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// Device building blocks for gfx950 (CDNA4): element types, LDS operand
+// staging, and the double-buffered MFMA main loop shared by every tile kernel.
+//
+// Tile shape. A workgroup has 256 threads = 4 wave64s arranged 2 x 2 and
+// computes a 128 x 128 output tile; each wave owns a 64 x 64 sub-tile made of
+// 2 x 2 blocks of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
+// v_mfma_f32_32x32x2_f32 for fp32). One K step moves 64 bytes of every
+// operand row: 32 bf16 or 16 fp32 elements.
+//
+// LDS layout. Each staged operand tile is 128 rows x 80 bytes: the 64 data
+// bytes of a row, K-contiguous, plus 16 pad bytes, which makes the 16-byte
+// fragment reads of 16 consecutive rows land in distinct bank groups. Two
+// stages are kept (double buffering); one barrier per K step.
+//
+// Output layout of the 32x32 MFMA (same for both element types): lane l holds
+// column j = l % 32 and rows i = 8*(r/4) + 4*(l/32) + r%4 of the block, r in
+// [0, 16). The tile kernels put vocabulary on the row axis, so the
+// per-token reductions of the epilogue run over a lane's own registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kd {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 128;
+constexpr int kRowBytes = 80;
+constexpr int kTileBytes = kTile * kRowBytes;  // 10240
+constexpr int kXcds = 8;                       // MI355X: 8 XCDs, each with its own L2
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef uint16_t bf16_t;  // bf16 storage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBK = 16;       // elements per K step
+  static constexpr int kPerChunk = 4;  // elements per 16-byte chunk
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBK = 32;
+  static constexpr int kPerChunk = 8;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The dispatcher hands workgroup b to XCD b % 8. Remap so that each XCD owns a
+// contiguous range of tile indices: neighbouring tiles then share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int per = nblocks / kXcds, rem = nblocks % kXcds;
+  const int x = bid % kXcds, local = bid / kXcds;
+  return x * per + min(x, rem) + local;
+}
+
+// Grouped order over an (na x nb) grid of tiles: runs of `group` consecutive
+// b values for each a, so a window of consecutive tiles covers a near-square
+// block and both operands are re-read from L2 rather than HBM.
+__device__ __forceinline__ void grouped_tile(int t, int na, int nb, int group, int& a, int& b) {
+  const int width = group * na;
+  const int g = t / width;
+  const int first = g * group;
+  const int gsz = min(nb - first, group);
+  const int r = t - g * width;
+  a = r / gsz;
+  b = first + r % gsz;
+}
+
+// An operand of C = A B^T-style contractions, seen as (row, k) elements.
+// KC  (K-contiguous):  element (row, k) at ptr[row * ld + k]; rows < `rows`, k < `kdim`.
+// !KC (row-contiguous): element (row, k) at ptr[k * ld + row]; `rows` a multiple of
+//                       the chunk width, k < `kdim`.
+template <typename T, bool KC>
+struct Operand {
+  const T* ptr;
+  int64_t ld;
+  int64_t rows;
+  int64_t kdim;
+};
+
+// Stages one 128-row x K-step tile of an operand: global -> registers -> LDS.
+// Out-of-range rows / k are zero-filled, so ragged edges contribute nothing.
+template <typename T, bool KC>
+struct Stager {
+  uint4 r[2];
+
+  __device__ __forceinline__ void load(const Operand<T, KC>& op, int64_t row0, int64_t k0, int tid) {
+    constexpr int PC = Elem<T>::kPerChunk;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = tid + kThreads * j;
+      if constexpr (KC) {
+        const int row = q >> 2, c = q & 3;
+        const int64_t grow = row0 + row, k = k0 + (int64_t)c * PC;
+        if (grow < op.rows && k < op.kdim)
+          r[j] = *reinterpret_cast<const uint4*>(op.ptr + grow * op.ld + k);
+        else
+          r[j] = make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        constexpr int CPR = kTile / PC;  // chunks per k-row
+        const int krow = q / CPR, mc = q % CPR;
+        const int64_t k = k0 + krow, m = row0 + (int64_t)mc * PC;
+        if (k < op.kdim && m < op.rows)
+          r[j] = *reinterpret_cast<const uint4*>(op.ptr + k * op.ld + m);
+        else
+          r[j] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+    constexpr int PC = Elem<T>::kPerChunk;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = tid + kThreads * j;
+      if constexpr (KC) {
+        const int row = q >> 2, c = q & 3;
+        *reinterpret_cast<uint4*>(lds + row * kRowBytes + c * 16) = r[j];
+      } else {
+        constexpr int CPR = kTile / PC;
+        const int krow = q / CPR, m = (q % CPR) * PC;
+        const T* e = reinterpret_cast<const T*>(&r[j]);
+#pragma unroll
+        for (int x = 0; x < PC; ++x)
+          *reinterpret_cast<T*>(lds + (m + x) * kRowBytes + krow * (int)sizeof(T)) = e[x];
+      }
+    }
+  }
+};
+
+// One K step of MFMAs: acc[g] += A_tile * B_tile[g]^T for every B operand g.
+// The A fragments are read once and shared by all B operands.
+template <typename T, int NB>
+__device__ __forceinline__ void mma_step(const uint8_t* ldsA, const uint8_t* ldsB0,
+                                         f32x16 (&acc)[NB][2][2], int wm, int wn, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int cb = (2 * kk + h) * 16;
+      bf16x8 a[2], b[NB][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        a[mb] = *reinterpret_cast<const bf16x8*>(ldsA + (wm * 64 + mb * 32 + r) * kRowBytes + cb);
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          b[g][nb] = *reinterpret_cast<const bf16x8*>(ldsB0 + g * kTileBytes +
+                                                      (wn * 64 + nb * 32 + r) * kRowBytes + cb);
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[g][mb][nb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[g][nb], acc[g][mb][nb], 0, 0, 0);
+    }
+  } else {
+    // fp32: lane half h takes elements [8h, 8h+8) of the 16-element K step for
+    // both operands, one per v_mfma_f32_32x32x2_f32; the sum over k is the same.
+    f32x4 a[2][2], b[NB][2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        a[mb][c] = *reinterpret_cast<const f32x4*>(ldsA + (wm * 64 + mb * 32 + r) * kRowBytes +
+                                                   (2 * h + c) * 16);
+#pragma unroll
+    for (int g = 0; g < NB; ++g)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          b[g][nb][c] = *reinterpret_cast<const f32x4*>(
+              ldsB0 + g * kTileBytes + (wn * 64 + nb * 32 + r) * kRowBytes + (2 * h + c) * 16);
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int g = 0; g < NB; ++g)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][c][e], b[g][nb][c][e],
+                                                                   acc[g][mb][nb], 0, 0, 0);
+  }
+}
+
+// acc[g] = A[a_row0 : a_row0+128, 0:K] * B[g][b_row0 : b_row0+128, 0:K]^T.
+// `lds` holds 2 stages of (1 + NB) tiles. Ends with a barrier, so the caller
+// may reuse `lds` right after.
+template <typename T, bool AKC, bool BKC, int NB>
+__device__ __forceinline__ void mainloop(const Operand<T, AKC>& A, const Operand<T, BKC>* B,
+                                         int64_t a_row0, int64_t b_row0, int64_t K, uint8_t* lds,
+                                         f32x16 (&acc)[NB][2][2], int tid) {
+  constexpr int BK = Elem<T>::kBK;
+  constexpr int kStage = (1 + NB) * kTileBytes;
+  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int g = 0; g < NB; ++g)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) acc[g][mb][nb][x] = 0.f;
+
+  const int64_t nk = (K + BK - 1) / BK;
+  Stager<T, AKC> sa;
+  Stager<T, BKC> sb[NB];
+  sa.load(A, a_row0, 0, tid);
+#pragma unroll
+  for (int g = 0; g < NB; ++g) sb[g].load(B[g], b_row0, 0, tid);
+  sa.store(lds, tid);
+#pragma unroll
+  for (int g = 0; g < NB; ++g) sb[g].store(lds + (1 + g) * kTileBytes, tid);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = lds + (kt & 1) * kStage;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * kStage;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      sa.load(A, a_row0, (kt + 1) * BK, tid);
+#pragma unroll
+      for (int g = 0; g < NB; ++g) sb[g].load(B[g], b_row0, (kt + 1) * BK, tid);
+    }
+    mma_step<T, NB>(cur, cur + kTileBytes, acc, wm, wn, lane);
+    if (more) {
+      sa.store(nxt, tid);
+#pragma unroll
+      for (int g = 0; g < NB; ++g) sb[g].store(nxt + (1 + g) * kTileBytes, tid);
+    }
+    __syncthreads();
+  }
+}
+
+// Vocabulary row (within the 128-row tile) of accumulator register x of block mb.
+__device__ __forceinline__ int acc_row(int wm, int mb, int x, int lane) {
+  return wm * 64 + mb * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+}
+// Token column (within the 128-column tile) of block nb.
+__device__ __forceinline__ int acc_col(int wn, int nb, int lane) { return wn * 64 + nb * 32 + (lane & 31); }
+
+}  // namespace kd

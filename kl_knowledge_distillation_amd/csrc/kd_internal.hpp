@@ -1,0 +1,63 @@
+// Internal plan shared by the C ABI (kd_api.cpp) and the launchers
+// (kd_kernels.hip). Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kd_loss.h"
+
+namespace kd {
+
+enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3 };
+
+// Number of fp32 fields of one per-(token, vocabulary slice) record.
+constexpr int kRecFields = 9;
+// Tokens per merge workgroup; also the number of partial sums per block.
+constexpr int kMergeThreads = 256;
+// Bytes reserved at the start of the workspace for device flags.
+constexpr size_t kStatusBytes = 256;
+// Offset of the header inside `saved` is 16 * n; its size is 64 bytes.
+constexpr size_t kSavedHeaderBytes = 64;
+
+struct Plan {
+  int mode = 0;
+  int dtype = 0;  // KD_F32 | KD_BF16
+  int64_t n = 0, d = 0, dt = 0, v = 0;
+  int k = 0;
+  float ws = 0.f, wt = 0.f, wkl = 0.f, T = 1.f;
+  int64_t ignore = -100;
+  int reduction = KD_REDUCE_MEAN;
+  float normalizer = 0.f;
+  int need_zT = 0;    // T != 1: student statistics at z/T are kept apart from z
+  int need_t1 = 0;    // teacher CE wanted at T != 1: teacher statistics at t
+  int has_labels = 0;
+  int n_ttiles = 0, n_vtiles = 0, tps = 1, n_slices = 0;  // forward grid
+  int64_t chunk = 0;  // backward vocabulary chunk (multiple of 128)
+  int n_chunks = 0;
+  int merge_blocks = 0;
+  // forward workspace layout (bytes from the workspace base)
+  size_t off_prep = 0, off_rec = 0, off_part = 0, fwd_bytes = 0;
+  // backward workspace layout
+  size_t off_dz = 0, bwd_bytes = 0;
+};
+
+struct Tensors {
+  const void* hs = nullptr;      // student hidden [n, d]
+  const void* w = nullptr;       // student weight [v, d]
+  const void* logits = nullptr;  // student logits [n, v]
+  const void* ht = nullptr;      // teacher hidden [n, d_t]
+  const void* wt = nullptr;      // teacher weight [v, d_t] (tied: == w)
+  const int32_t* topk_idx = nullptr;
+  const float* topk_prob = nullptr;
+  const int64_t* labels = nullptr;
+};
+
+kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
+                      void* workspace, hipStream_t stream, kd_trace* trace);
+kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
+                       float* d_hidden, float* d_weight, int accumulate, void* workspace,
+                       hipStream_t stream, kd_trace* trace);
+
+}  // namespace kd

@@ -1,0 +1,895 @@
+// HIP kernels of the fused LM-head + CE + KL distillation loss, gfx950.
+//
+// Forward  (kd_loss_fwd):
+//   prep      one wave per token: label logits z[y], t[y] by a D-long dot
+//             product, validity flags; top-K: M = sum p, E = sum p log p and
+//             S = sum p z[idx] from the cached entries.
+//   fwd       grid = (vocabulary slice) x (128-token tile). For each 128-row
+//             vocabulary tile of its slice a workgroup runs the MFMA main loop
+//             (logit tiles z = W H_s^T and t = W H_t^T or W_t H_t^T) and folds
+//             the tile into per-token online statistics held in registers:
+//             running max and rescaled sum of 2^(x log2e / T) for z, z/T, t/T,
+//             t, and the cross term sum 2^(t~ - m) (t - z). The logits never
+//             leave registers (flash_kd, module description: online softmax).
+//   merge     one thread per token combines the slice records into lse values,
+//             per-token CE / KL / top-K objective, the saved statistics and a
+//             per-block partial loss.
+//   finalize  one workgroup sums the partials in a fixed order.
+// Backward (kd_loss_bwd), per vocabulary chunk (CompactifAI/Full-Chunked-KL-
+// Loss, Full Chunked KL: recompute each chunk, apply the closed-form gradient):
+//   bwd_dz    recompute the chunk's logit tiles, form dz in registers from the
+//             saved lse values, round and store the (n x chunk) slab.
+//   scatter   top-K only: subtract (g/den) w_kl p at the cached indices.
+//   gemm_dw   dW[chunk] = dz^T H_s       (K = n)
+//   gemm_dh   dH += dz W[chunk]          (K = chunk)
+#include <math.h>
+
+#include "kd_device.hpp"
+#include "kd_internal.hpp"
+
+namespace kd {
+
+// ---------------------------------------------------------------------------
+// Online statistics
+// ---------------------------------------------------------------------------
+
+struct RowStats {
+  float mz1, sz1;      // z at T = 1 (base-2 units of z log2e)
+  float mzT, szT;      // z / T
+  float mtT, stT, a;   // t / T and the cross term sum 2^(t~ - mtT) (t - z)
+  float mt1, st1;      // t at T = 1 (teacher CE when T != 1)
+};
+
+__device__ __forceinline__ void stats_init(RowStats& s) {
+  s.mz1 = s.mzT = s.mtT = s.mt1 = -INFINITY;
+  s.sz1 = s.szT = s.stT = s.st1 = s.a = 0.f;
+}
+
+// 2^(m_old - m_new), with an empty record (m_new = -inf) scaling to 0.
+__device__ __forceinline__ float rescale(float m_old, float m_new) {
+  return (m_new == -INFINITY) ? 0.f : exp2_fast(m_old - m_new);
+}
+
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  s = s * rescale(m, mn) + s2 * rescale(m2, mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void merge_msa(float& m, float& s, float& a, float m2, float s2, float a2) {
+  const float mn = fmaxf(m, m2);
+  const float f1 = rescale(m, mn), f2 = rescale(m2, mn);
+  s = s * f1 + s2 * f2;
+  a = a * f1 + a2 * f2;
+  m = mn;
+}
+
+__device__ __forceinline__ void stats_merge(RowStats& s, const RowStats& o) {
+  merge_ms(s.mz1, s.sz1, o.mz1, o.sz1);
+  merge_ms(s.mzT, s.szT, o.mzT, o.szT);
+  merge_msa(s.mtT, s.stT, s.a, o.mtT, o.stT, o.a);
+  merge_ms(s.mt1, s.st1, o.mt1, o.st1);
+}
+
+__device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int x) { return (ok >> (mb * 16 + x)) & 1u; }
+
+// Folds the 32 values a lane holds for token block nb into (m, s) at scale c.
+template <bool TAIL>
+__device__ __forceinline__ void online_ms(float& m, float& s, const f32x16 (&x)[2][2], int nb, float c,
+                                          uint32_t ok) {
+  float bm = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!TAIL || ok_bit(ok, mb, r)) bm = fmaxf(bm, x[mb][nb][r]);
+  const float mn = fmaxf(m, bm * c);
+  const float sc = rescale(m, mn);
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e0 = exp2_fast(fmaf(x[0][nb][r], c, -mn));
+    float e1 = exp2_fast(fmaf(x[1][nb][r], c, -mn));
+    if (TAIL) {
+      e0 = ok_bit(ok, 0, r) ? e0 : 0.f;
+      e1 = ok_bit(ok, 1, r) ? e1 : 0.f;
+    }
+    acc0 += e0;
+    acc1 += e1;
+  }
+  s = s * sc + (acc0 + acc1);
+  m = mn;
+}
+
+// Teacher statistics at scale c plus the cross term sum 2^(t c - m) (t - z).
+template <bool TAIL>
+__device__ __forceinline__ void online_msa(float& m, float& s, float& a, const f32x16 (&t)[2][2],
+                                           const f32x16 (&z)[2][2], int nb, float c, uint32_t ok) {
+  float bm = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!TAIL || ok_bit(ok, mb, r)) bm = fmaxf(bm, t[mb][nb][r]);
+  const float mn = fmaxf(m, bm * c);
+  const float sc = rescale(m, mn);
+  float s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float e0 = exp2_fast(fmaf(t[0][nb][r], c, -mn));
+    float e1 = exp2_fast(fmaf(t[1][nb][r], c, -mn));
+    if (TAIL) {
+      e0 = ok_bit(ok, 0, r) ? e0 : 0.f;
+      e1 = ok_bit(ok, 1, r) ? e1 : 0.f;
+    }
+    s0 += e0;
+    s1 += e1;
+    a0 = fmaf(e0, t[0][nb][r] - z[0][nb][r], a0);
+    a1 = fmaf(e1, t[1][nb][r] - z[1][nb][r], a1);
+  }
+  s = s * sc + (s0 + s1);
+  a = a * sc + (a0 + a1);
+  m = mn;
+}
+
+template <int MODE, bool TAIL>
+__device__ __forceinline__ void fwd_update(const f32x16 (&z)[2][2], const f32x16 (&t)[2][2],
+                                           RowStats (&st)[2], float cT, bool need_zT, bool need_t1,
+                                           uint32_t ok) {
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    online_ms<TAIL>(st[nb].mz1, st[nb].sz1, z, nb, kLog2e, ok);
+    if (MODE == MODE_TOPK) continue;
+    if (need_zT) online_ms<TAIL>(st[nb].mzT, st[nb].szT, z, nb, cT, ok);
+    online_msa<TAIL>(st[nb].mtT, st[nb].stT, st[nb].a, t, z, nb, cT, ok);
+    if (need_t1) online_ms<TAIL>(st[nb].mt1, st[nb].st1, t, nb, kLog2e, ok);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward tile kernel
+// ---------------------------------------------------------------------------
+
+struct FwdArgs {
+  const void* hs;
+  const void* w;
+  const void* ht;
+  const void* wt;
+  const void* logits;
+  int64_t n, d, dt, v;
+  int n_ttiles, n_vtiles, tps, n_slices;
+  float cT;
+  int need_zT, need_t1;
+  float* rec;  // [kRecFields][n_slices][n]
+};
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
+  constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (1 + NB) * kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  int slice, tt;
+  grouped_tile(t, a.n_slices, a.n_ttiles, 8, slice, tt);
+  const int64_t t0 = (int64_t)tt * kTile;
+  const int vt_begin = slice * a.tps;
+  const int vt_end = min(a.n_vtiles, vt_begin + a.tps);
+
+  RowStats st[2];
+  stats_init(st[0]);
+  stats_init(st[1]);
+
+  const T* hs = static_cast<const T*>(a.hs);
+  const T* W = static_cast<const T*>(a.w);
+  const T* ht = static_cast<const T*>(a.ht);
+  const T* Wt = static_cast<const T*>(a.wt);
+
+  f32x16 acc[NB][2][2];
+  f32x16 tacc[1][2][2];  // teacher accumulator of the separate / logits modes
+  f32x16 zl[2][2];       // student logits loaded in LOGITS mode
+
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    const int64_t v0 = (int64_t)vt * kTile;
+    if constexpr (MODE == MODE_TIED) {
+      const Operand<T, true> A{W, a.d, a.v, a.d};
+      const Operand<T, true> B[2] = {{hs, a.d, a.n, a.d}, {ht, a.d, a.n, a.d}};
+      mainloop<T, true, true, 2>(A, B, v0, t0, a.d, lds, acc, tid);
+    } else if constexpr (MODE == MODE_SEPARATE) {
+      const Operand<T, true> A{W, a.d, a.v, a.d};
+      const Operand<T, true> B{hs, a.d, a.n, a.d};
+      mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
+      const Operand<T, true> At{Wt, a.dt, a.v, a.dt};
+      const Operand<T, true> Bt{ht, a.dt, a.n, a.dt};
+      mainloop<T, true, true, 1>(At, &Bt, v0, t0, a.dt, lds, tacc, tid);
+    } else if constexpr (MODE == MODE_TOPK) {
+      const Operand<T, true> A{W, a.d, a.v, a.d};
+      const Operand<T, true> B{hs, a.d, a.n, a.d};
+      mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
+    } else {  // MODE_LOGITS
+      const Operand<T, true> At{Wt, a.dt, a.v, a.dt};
+      const Operand<T, true> Bt{ht, a.dt, a.n, a.dt};
+      mainloop<T, true, true, 1>(At, &Bt, v0, t0, a.dt, lds, tacc, tid);
+      const T* L = static_cast<const T*>(a.logits);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int64_t tok = t0 + acc_col(wn, nb, lane);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int64_t vv = v0 + acc_row(wm, mb, x, lane);
+            zl[mb][nb][x] = (tok < a.n && vv < a.v) ? to_f32(L[tok * a.v + vv]) : 0.f;
+          }
+      }
+    }
+
+    uint32_t ok = 0xffffffffu;
+    const bool tail = v0 + kTile > a.v;
+    if (tail) {
+      ok = 0u;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+          if (v0 + acc_row(wm, mb, x, lane) < a.v) ok |= 1u << (mb * 16 + x);
+    }
+    // Pick the (z, t) accumulators of this mode.
+    if constexpr (MODE == MODE_TIED) {
+      if (tail) fwd_update<MODE, true>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
+      else fwd_update<MODE, false>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
+    } else if constexpr (MODE == MODE_SEPARATE) {
+      if (tail) fwd_update<MODE, true>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+      else fwd_update<MODE, false>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+    } else if constexpr (MODE == MODE_TOPK) {
+      if (tail) fwd_update<MODE, true>(acc[0], acc[0], st, a.cT, false, false, ok);
+      else fwd_update<MODE, false>(acc[0], acc[0], st, a.cT, false, false, ok);
+    } else {
+      if (tail) fwd_update<MODE, true>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+      else fwd_update<MODE, false>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+    }
+  }
+
+  // Combine the two lane halves (same tokens, different vocabulary rows).
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    RowStats o;
+    o.mz1 = __shfl_xor(st[nb].mz1, 32);
+    o.sz1 = __shfl_xor(st[nb].sz1, 32);
+    o.mzT = __shfl_xor(st[nb].mzT, 32);
+    o.szT = __shfl_xor(st[nb].szT, 32);
+    o.mtT = __shfl_xor(st[nb].mtT, 32);
+    o.stT = __shfl_xor(st[nb].stT, 32);
+    o.a = __shfl_xor(st[nb].a, 32);
+    o.mt1 = __shfl_xor(st[nb].mt1, 32);
+    o.st1 = __shfl_xor(st[nb].st1, 32);
+    stats_merge(st[nb], o);
+  }
+  // Combine the two waves that share a token block (wm = 0 and wm = 1). The
+  // main loop ended with a barrier, so the operand LDS is free.
+  float* xs = reinterpret_cast<float*>(lds);
+  const int l32 = lane & 31;
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      float* p = xs + ((wn * 2 + nb) * kRecFields) * 32 + l32;
+      const RowStats& s = st[nb];
+      p[0 * 32] = s.mz1; p[1 * 32] = s.sz1; p[2 * 32] = s.mzT; p[3 * 32] = s.szT;
+      p[4 * 32] = s.mtT; p[5 * 32] = s.stT; p[6 * 32] = s.a;   p[7 * 32] = s.mt1;
+      p[8 * 32] = s.st1;
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float* p = xs + ((wn * 2 + nb) * kRecFields) * 32 + l32;
+      RowStats o;
+      o.mz1 = p[0 * 32]; o.sz1 = p[1 * 32]; o.mzT = p[2 * 32]; o.szT = p[3 * 32];
+      o.mtT = p[4 * 32]; o.stT = p[5 * 32]; o.a = p[6 * 32];   o.mt1 = p[7 * 32];
+      o.st1 = p[8 * 32];
+      stats_merge(st[nb], o);
+      const int64_t tok = t0 + acc_col(wn, nb, lane);
+      if (tok < a.n) {
+        const int64_t stride = (int64_t)a.n_slices * a.n;
+        float* r = a.rec + (int64_t)slice * a.n + tok;
+        const RowStats& s = st[nb];
+        r[0 * stride] = s.mz1; r[1 * stride] = s.sz1; r[2 * stride] = s.mzT;
+        r[3 * stride] = s.szT; r[4 * stride] = s.mtT; r[5 * stride] = s.stT;
+        r[6 * stride] = s.a;   r[7 * stride] = s.mt1; r[8 * stride] = s.st1;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prep: label logits, validity, top-K sums (one wave per token)
+// ---------------------------------------------------------------------------
+
+struct PrepArgs {
+  const void* hs;
+  const void* w;
+  const void* ht;
+  const void* wt;
+  const void* logits;
+  const int64_t* labels;
+  const int32_t* idx;
+  const float* prob;
+  int64_t n, d, dt, v, ignore;
+  int k;
+  int want_teacher;  // teacher label logit needed (teacher CE weight or output)
+  float* prep;       // [4][n]: z[y] | S, t[y] | E, M, flag
+};
+
+template <typename T>
+__device__ __forceinline__ float wave_dot(const T* x, const T* y, int64_t len, int lane) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  float s = 0.f;
+  for (int64_t e = (int64_t)lane * PC; e < len; e += 64 * PC) {
+    const uint4 ux = *reinterpret_cast<const uint4*>(x + e);
+    const uint4 uy = *reinterpret_cast<const uint4*>(y + e);
+    const T* px = reinterpret_cast<const T*>(&ux);
+    const T* py = reinterpret_cast<const T*>(&uy);
+#pragma unroll
+    for (int j = 0; j < PC; ++j) s = fmaf(to_f32(px[j]), to_f32(py[j]), s);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  return s;
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (i >= a.n) return;
+  const T* hs = static_cast<const T*>(a.hs);
+  const T* W = static_cast<const T*>(a.w);
+  float f0 = 0.f, f1 = 0.f, f2 = 0.f, flag = 1.f;
+  if constexpr (MODE == MODE_TOPK) {
+    float mass = 0.f, ent = 0.f, cross = 0.f;
+    bool bad = false;
+    for (int j = 0; j < a.k; ++j) {
+      const int32_t ix = a.idx[i * a.k + j];
+      const float p = a.prob[i * a.k + j];
+      mass += p;
+      ent += (p > 0.f) ? p * logf(p) : 0.f;
+      if (ix < 0 || (int64_t)ix >= a.v) {  // never used as an address
+        bad = true;
+        continue;
+      }
+      cross = fmaf(p, wave_dot<T>(hs + i * a.d, W + (int64_t)ix * a.d, a.d, lane), cross);
+    }
+    f0 = cross;
+    f1 = ent;
+    f2 = mass;
+    flag = bad ? 2.f : 1.f;
+  } else {
+    const int64_t y = a.labels ? a.labels[i] : a.ignore;
+    const bool in_range = y >= 0 && y < a.v;
+    const bool valid = a.labels == nullptr || (y != a.ignore && in_range);
+    flag = valid ? 1.f : ((y != a.ignore && !in_range) ? 2.f : 0.f);
+    if (a.labels != nullptr && valid) {
+      if constexpr (MODE == MODE_LOGITS) {
+        f0 = to_f32(static_cast<const T*>(a.logits)[i * a.v + y]);
+      } else {
+        f0 = wave_dot<T>(hs + i * a.d, W + y * a.d, a.d, lane);
+      }
+      if (a.want_teacher) {
+        const T* ht = static_cast<const T*>(a.ht);
+        const T* Wt = static_cast<const T*>(a.wt);
+        f1 = wave_dot<T>(ht + i * a.dt, Wt + y * a.dt, a.dt, lane);
+      }
+    }
+  }
+  if (lane == 0) {
+    a.prep[i] = f0;
+    a.prep[a.n + i] = f1;
+    a.prep[2 * a.n + i] = f2;
+    a.prep[3 * a.n + i] = flag;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: per-token outputs, saved statistics, per-block partial sums
+// ---------------------------------------------------------------------------
+
+struct MergeArgs {
+  const float* rec;
+  const float* prep;
+  int n_slices;
+  int64_t n;
+  int mode;
+  float T;
+  int need_zT, need_t1, teacher_ce;
+  float ws, wt, wkl;
+  float* out_sce;
+  float* out_tce;
+  float* out_kl;
+  float* saved;       // [n][4] or null
+  double* partials;   // [blocks][4]: loss sum, valid count, bad count, 0
+};
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  __shared__ double red[3][kMergeThreads];
+  const int tid = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * kMergeThreads + tid;
+  double contrib = 0.0, cnt = 0.0, bad = 0.0;
+  if (i < a.n) {
+    RowStats s;
+    stats_init(s);
+    const int64_t stride = (int64_t)a.n_slices * a.n;
+    for (int sl = 0; sl < a.n_slices; ++sl) {
+      const float* r = a.rec + (int64_t)sl * a.n + i;
+      RowStats o;
+      o.mz1 = r[0 * stride]; o.sz1 = r[1 * stride]; o.mzT = r[2 * stride];
+      o.szT = r[3 * stride]; o.mtT = r[4 * stride]; o.stT = r[5 * stride];
+      o.a = r[6 * stride];   o.mt1 = r[7 * stride]; o.st1 = r[8 * stride];
+      stats_merge(s, o);
+    }
+    const float lz1 = kLn2 * (s.mz1 + log2f(s.sz1));
+    const float lzT = a.need_zT ? kLn2 * (s.mzT + log2f(s.szT)) : lz1;
+    const float f0 = a.prep[i], f1 = a.prep[a.n + i], f2 = a.prep[2 * a.n + i];
+    const float flag = a.prep[3 * a.n + i];
+    float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f;
+    bool valid;
+    if (a.mode == MODE_TOPK) {
+      // sum p log p - sum p z[idx] + M lse(z)
+      kl = f1 - f0 + f2 * lz1;
+      mass = f2;
+      valid = true;
+    } else {
+      ltT = kLn2 * (s.mtT + log2f(s.stT));
+      const float lt1 = a.need_t1 ? kLn2 * (s.mt1 + log2f(s.st1)) : ltT;
+      const float cross = s.a / (s.stT * a.T);  // E_{P_T}[(t - z) / T]
+      kl = a.T * a.T * (cross - ltT + lzT);
+      valid = flag == 1.f;
+      sce = valid ? lz1 - f0 : 0.f;
+      tce = (valid && a.teacher_ce) ? lt1 - f1 : 0.f;
+    }
+    bad = (flag == 2.f) ? 1.0 : 0.0;
+    cnt = valid ? 1.0 : 0.0;
+    contrib = valid ? ((double)a.ws * sce + (double)a.wt * tce + (double)a.wkl * kl) : 0.0;
+    if (a.out_sce) a.out_sce[i] = sce;
+    if (a.out_tce) a.out_tce[i] = tce;
+    if (a.out_kl) a.out_kl[i] = kl;
+    if (a.saved) {
+      float4 sv = make_float4(lz1, lzT, ltT, mass);
+      reinterpret_cast<float4*>(a.saved)[i] = sv;
+    }
+  }
+  red[0][tid] = contrib;
+  red[1][tid] = cnt;
+  red[2][tid] = bad;
+  __syncthreads();
+  for (int off = kMergeThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      red[0][tid] += red[0][tid + off];
+      red[1][tid] += red[1][tid + off];
+      red[2][tid] += red[2][tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double* p = a.partials + (int64_t)blockIdx.x * 4;
+    p[0] = red[0][0];
+    p[1] = red[1][0];
+    p[2] = red[2][0];
+    p[3] = 0.0;
+  }
+}
+
+struct FinalArgs {
+  const double* partials;
+  int blocks;
+  float normalizer;
+  int reduction;
+  float* loss;       // nullable
+  float* saved_hdr;  // nullable: [den, n_valid, n_bad, 0]
+  int32_t* status;   // workspace flag word
+};
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
+  __shared__ double red[3][kThreads];
+  const int tid = threadIdx.x;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+  for (int b = tid; b < a.blocks; b += kThreads) {
+    s0 += a.partials[b * 4 + 0];
+    s1 += a.partials[b * 4 + 1];
+    s2 += a.partials[b * 4 + 2];
+  }
+  red[0][tid] = s0;
+  red[1][tid] = s1;
+  red[2][tid] = s2;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      red[0][tid] += red[0][tid + off];
+      red[1][tid] += red[1][tid + off];
+      red[2][tid] += red[2][tid + off];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double total = red[0][0], n_valid = red[1][0], n_bad = red[2][0];
+    double den;
+    if (a.normalizer > 0.f) den = a.normalizer;
+    else if (a.reduction == KD_REDUCE_MEAN) den = n_valid > 1.0 ? n_valid : 1.0;
+    else den = 1.0;
+    if (a.loss) *a.loss = (float)(total / den);
+    if (a.saved_hdr) {
+      a.saved_hdr[0] = (float)den;
+      a.saved_hdr[1] = (float)n_valid;
+      a.saved_hdr[2] = (float)n_bad;
+      a.saved_hdr[3] = 0.f;
+    }
+    a.status[0] = n_bad > 0.0 ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward: recompute a chunk and write the logit-gradient slab
+// ---------------------------------------------------------------------------
+
+struct BwdArgs {
+  const void* hs;
+  const void* w;
+  const void* ht;
+  const void* wt;
+  int64_t n, d, dt, v;
+  const int64_t* labels;
+  int64_t ignore;
+  const float* saved;     // [n][4] + header at 16 n bytes
+  const float* grad;      // device scalar or null
+  float ws, wkl, T, cT;
+  int need_zT;
+  int64_t c0;             // first vocabulary row of the chunk
+  int n_vt, n_ttiles;     // tiles of the chunk
+  void* dz;               // [n][ldz]
+  int64_t ldz;
+};
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float x0, float x1, float x2, float x3);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, float x2, float x3) {
+  uint2 u;
+  u.x = (uint32_t)bf16_rne(x0) | ((uint32_t)bf16_rne(x1) << 16);
+  u.y = (uint32_t)bf16_rne(x2) | ((uint32_t)bf16_rne(x3) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
+  constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (1 + NB) * kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  int vt, tt;
+  grouped_tile(t, a.n_vt, a.n_ttiles, 8, vt, tt);
+  const int64_t v0 = a.c0 + (int64_t)vt * kTile;
+  const int64_t t0 = (int64_t)tt * kTile;
+  const T* hs = static_cast<const T*>(a.hs);
+  const T* W = static_cast<const T*>(a.w);
+  const T* ht = static_cast<const T*>(a.ht);
+  const T* Wt = static_cast<const T*>(a.wt);
+
+  f32x16 acc[NB][2][2];
+  f32x16 tacc[1][2][2];
+  if constexpr (MODE == MODE_TIED) {
+    const Operand<T, true> A{W, a.d, a.v, a.d};
+    const Operand<T, true> B[2] = {{hs, a.d, a.n, a.d}, {ht, a.d, a.n, a.d}};
+    mainloop<T, true, true, 2>(A, B, v0, t0, a.d, lds, acc, tid);
+  } else if constexpr (MODE == MODE_SEPARATE) {
+    const Operand<T, true> A{W, a.d, a.v, a.d};
+    const Operand<T, true> B{hs, a.d, a.n, a.d};
+    mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
+    const Operand<T, true> At{Wt, a.dt, a.v, a.dt};
+    const Operand<T, true> Bt{ht, a.dt, a.n, a.dt};
+    mainloop<T, true, true, 1>(At, &Bt, v0, t0, a.dt, lds, tacc, tid);
+  } else {  // MODE_TOPK
+    const Operand<T, true> A{W, a.d, a.v, a.d};
+    const Operand<T, true> B{hs, a.d, a.n, a.d};
+    mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
+  }
+  const f32x16(&z)[2][2] = acc[0];
+  const f32x16(&tl)[2][2] = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+
+  const float* hdr = a.saved + 4 * a.n;
+  const float den = hdr[0];
+  const float g = a.grad ? *a.grad : 1.f;
+  T* dz = static_cast<T*>(a.dz);
+
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t tok = t0 + acc_col(wn, nb, lane);
+    if (tok >= a.n) continue;
+    const float4 sv = reinterpret_cast<const float4*>(a.saved)[tok];
+    const float L1 = sv.x * kLog2e, LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
+    int64_t y = -1;
+    bool valid = true;
+    if (MODE != MODE_TOPK && a.labels) {
+      y = a.labels[tok];
+      valid = y != a.ignore && y >= 0 && y < a.v;
+    }
+    const float coef = valid ? g / den : 0.f;
+    const float cs = coef * a.ws;            // student CE
+    const float ck = coef * a.wkl * a.T;     // T^2 KL -> T (P_S - P_T)
+    const float cm = coef * a.wkl * mass;    // top-K: M softmax(z)
+    T* row = dz + tok * a.ldz + (v0 - a.c0);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = q * 4 + e;
+          const int64_t vv = v0 + acc_row(wm, mb, x, lane);
+          const float zz = z[mb][nb][x];
+          const float p1 = exp2_fast(fmaf(zz, kLog2e, -L1));
+          float dv;
+          if (MODE == MODE_TOPK) {
+            dv = cm * p1;
+          } else {
+            dv = cs * (p1 - (vv == y ? 1.f : 0.f));
+            const float pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
+            const float pt = exp2_fast(fmaf(tl[mb][nb][x], a.cT, -LtT));
+            dv = fmaf(ck, pz - pt, dv);
+          }
+          o[e] = (vv < a.v) ? dv : 0.f;
+        }
+        store4<T>(row + acc_row(wm, mb, q * 4, lane), o[0], o[1], o[2], o[3]);
+      }
+  }
+}
+
+// Top-K: dz[i, idx - c0] -= (g/den) w_kl p for the entries of this chunk.
+// Indices are distinct per row, so every element has a single writer.
+struct ScatterArgs {
+  const int32_t* idx;
+  const float* prob;
+  int k;
+  int64_t n, v, c0, cw;
+  const float* saved;
+  const float* grad;
+  float wkl;
+  void* dz;
+  int64_t ldz;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= a.n * a.k) return;
+  const int32_t ix = a.idx[e];
+  if (ix < 0 || (int64_t)ix >= a.v) return;
+  const int64_t off = (int64_t)ix - a.c0;
+  if (off < 0 || off >= a.cw) return;
+  const int64_t i = e / a.k;
+  const float den = a.saved[4 * a.n];
+  const float g = a.grad ? *a.grad : 1.f;
+  T* p = static_cast<T*>(a.dz) + i * a.ldz + off;
+  const float nv = to_f32(*p) - (g / den) * a.wkl * a.prob[e];
+  if constexpr (sizeof(T) == 2) *p = bf16_rne(nv);
+  else *p = nv;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM for dW and dH: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output
+// ---------------------------------------------------------------------------
+
+template <typename T, bool AKC, bool BKC>
+struct GemmArgs {
+  Operand<T, AKC> A;
+  Operand<T, BKC> B;
+  float* C;
+  int64_t ldc, M, N, K;
+  int accumulate;
+  int n_mt, n_nt;
+};
+
+template <typename T, bool AKC, bool BKC>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC> a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTileBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  int mt, nt;
+  grouped_tile(t, a.n_mt, a.n_nt, 8, mt, nt);
+  const int64_t m0 = (int64_t)mt * kTile, n0 = (int64_t)nt * kTile;
+  f32x16 acc[1][2][2];
+  mainloop<T, AKC, BKC, 1>(a.A, &a.B, m0, n0, a.K, lds, acc, tid);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t col = n0 + acc_col(wn, nb, lane);
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int64_t row = m0 + acc_row(wm, mb, x, lane);
+        if (row < a.M) {
+          float* p = a.C + row * a.ldc + col;
+          const float vv = acc[0][mb][nb][x];
+          *p = a.accumulate ? *p + vv : vv;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct Launch {
+  hipStream_t s;
+  kd_trace* tr;
+  template <class F>
+  kd_status run(int kind, F&& f) {
+    const bool rec = tr && tr->events && ((tr->mask >> kind) & 1u) && tr->count + 2 <= tr->capacity;
+    if (rec && hipEventRecord(static_cast<hipEvent_t>(tr->events[tr->count]), s) != hipSuccess)
+      return KD_ERR_HIP;
+    f();
+    if (hipGetLastError() != hipSuccess) return KD_ERR_HIP;
+    if (rec) {
+      if (hipEventRecord(static_cast<hipEvent_t>(tr->events[tr->count + 1]), s) != hipSuccess)
+        return KD_ERR_HIP;
+      if (tr->kinds) tr->kinds[tr->count / 2] = kind;
+      tr->count += 2;
+    }
+    return KD_OK;
+  }
+};
+
+#define KD_TRY(x)                     \
+  do {                                \
+    const kd_status st_ = (x);        \
+    if (st_ != KD_OK) return st_;     \
+  } while (0)
+
+template <typename T>
+kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved, void* ws,
+                    hipStream_t stream, kd_trace* trace) {
+  Launch L{stream, trace};
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* prep = reinterpret_cast<float*>(base + p.off_prep);
+  float* rec = reinterpret_cast<float*>(base + p.off_rec);
+  double* part = reinterpret_cast<double*>(base + p.off_part);
+  int32_t* status = reinterpret_cast<int32_t*>(base);
+
+  PrepArgs pa{x.hs, x.w, x.ht, x.wt, x.logits, x.labels, x.topk_idx, x.topk_prob,
+              p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, prep};
+  pa.want_teacher = (p.mode == MODE_TIED || p.mode == MODE_SEPARATE || p.mode == MODE_LOGITS) &&
+                    (p.wt > 0.f || (out && out->teacher_ce));
+  const dim3 pgrid((unsigned)((p.n + 3) / 4));
+  KD_TRY(L.run(KD_KERNEL_PREP, [&] {
+    switch (p.mode) {
+      case MODE_TOPK: prep_kernel<T, MODE_TOPK><<<pgrid, kThreads, 0, stream>>>(pa); break;
+      case MODE_LOGITS: prep_kernel<T, MODE_LOGITS><<<pgrid, kThreads, 0, stream>>>(pa); break;
+      default: prep_kernel<T, MODE_TIED><<<pgrid, kThreads, 0, stream>>>(pa); break;
+    }
+  }));
+
+  FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, p.n, p.d, p.dt, p.v,
+             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, p.need_zT, p.need_t1, rec};
+  const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
+  KD_TRY(L.run(KD_KERNEL_FWD, [&] {
+    switch (p.mode) {
+      case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED><<<fgrid, kThreads, 0, stream>>>(fa); break;
+      case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE><<<fgrid, kThreads, 0, stream>>>(fa); break;
+      case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK><<<fgrid, kThreads, 0, stream>>>(fa); break;
+      default: fwd_tiles_kernel<T, MODE_LOGITS><<<fgrid, kThreads, 0, stream>>>(fa); break;
+    }
+  }));
+
+  MergeArgs ma{rec, prep, p.n_slices, p.n, p.mode, p.T, p.need_zT, p.need_t1,
+               (p.mode != MODE_TOPK) ? 1 : 0, p.ws, p.wt, p.wkl,
+               out ? out->student_ce : nullptr, out ? out->teacher_ce : nullptr,
+               out ? out->kl : nullptr, static_cast<float*>(saved), part};
+  ma.teacher_ce = pa.want_teacher;
+  KD_TRY(L.run(KD_KERNEL_MERGE, [&] {
+    merge_kernel<<<dim3((unsigned)p.merge_blocks), kMergeThreads, 0, stream>>>(ma);
+  }));
+
+  FinalArgs fin{part, p.merge_blocks, p.normalizer, p.reduction, out ? out->loss : nullptr,
+                saved ? static_cast<float*>(saved) + 4 * p.n : nullptr, status};
+  KD_TRY(L.run(KD_KERNEL_FINALIZE, [&] { finalize_kernel<<<1, kThreads, 0, stream>>>(fin); }));
+  return KD_OK;
+}
+
+template <typename T>
+kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const float* grad,
+                     float* dh, float* dw, int accumulate, void* ws, hipStream_t stream,
+                     kd_trace* trace) {
+  Launch L{stream, trace};
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  T* dz = reinterpret_cast<T*>(base + p.off_dz);
+  const int64_t ldz = p.chunk;
+  for (int c = 0; c < p.n_chunks; ++c) {
+    const int64_t c0 = (int64_t)c * p.chunk;
+    const int64_t cw = (p.v - c0 < p.chunk) ? (p.v - c0) : p.chunk;  // valid columns
+    const int n_vt = (int)((cw + kTile - 1) / kTile);
+    BwdArgs ba{x.hs, x.w, x.ht, x.wt, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
+               static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T, p.need_zT,
+               c0, n_vt, p.n_ttiles, dz, ldz};
+    const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
+    KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
+      switch (p.mode) {
+        case MODE_TIED: bwd_dz_kernel<T, MODE_TIED><<<grid, kThreads, 0, stream>>>(ba); break;
+        case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE><<<grid, kThreads, 0, stream>>>(ba); break;
+        default: bwd_dz_kernel<T, MODE_TOPK><<<grid, kThreads, 0, stream>>>(ba); break;
+      }
+    }));
+    if (p.mode == MODE_TOPK) {
+      ScatterArgs sa{x.topk_idx, x.topk_prob, p.k, p.n, p.v, c0, cw,
+                     static_cast<const float*>(saved), grad, p.wkl, dz, ldz};
+      const int64_t ne = p.n * p.k;
+      KD_TRY(L.run(KD_KERNEL_SCATTER, [&] {
+        scatter_kernel<T><<<dim3((unsigned)((ne + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(sa);
+      }));
+    }
+    const int64_t cpad = (int64_t)n_vt * kTile;  // columns written by bwd_dz
+    if (dw) {
+      // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]; A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n]
+      GemmArgs<T, false, false> ga;
+      ga.A = Operand<T, false>{dz, ldz, cpad, p.n};
+      ga.B = Operand<T, false>{static_cast<const T*>(x.hs), p.d, p.d, p.n};
+      ga.C = dw + c0 * p.d;
+      ga.ldc = p.d;
+      ga.M = cw;
+      ga.N = p.d;
+      ga.K = p.n;
+      ga.accumulate = accumulate;
+      ga.n_mt = n_vt;
+      ga.n_nt = (int)((p.d + kTile - 1) / kTile);
+      KD_TRY(L.run(KD_KERNEL_GEMM_DW, [&] {
+        gemm_kernel<T, false, false>
+            <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), kThreads, 0, stream>>>(ga);
+      }));
+    }
+    if (dh) {
+      // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]; A(i, m) = dz[i * ldz + m], B(n, m) = W[(c0 + m) * d + n]
+      GemmArgs<T, true, false> gb;
+      gb.A = Operand<T, true>{dz, ldz, p.n, cpad};
+      gb.B = Operand<T, false>{static_cast<const T*>(x.w) + c0 * p.d, p.d, p.d, cw};
+      gb.C = dh;
+      gb.ldc = p.d;
+      gb.M = p.n;
+      gb.N = p.d;
+      gb.K = cw;
+      gb.accumulate = (accumulate || c > 0) ? 1 : 0;
+      gb.n_mt = p.n_ttiles;
+      gb.n_nt = (int)((p.d + kTile - 1) / kTile);
+      KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
+        gemm_kernel<T, true, false>
+            <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), kThreads, 0, stream>>>(gb);
+      }));
+    }
+  }
+  return KD_OK;
+}
+
+}  // namespace
+
+kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
+                      void* workspace, hipStream_t stream, kd_trace* trace) {
+  if (p.dtype == KD_BF16) return forward_t<bf16_t>(p, x, out, saved, workspace, stream, trace);
+  return forward_t<float>(p, x, out, saved, workspace, stream, trace);
+}
+
+kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
+                       float* d_hidden, float* d_weight, int accumulate, void* workspace,
+                       hipStream_t stream, kd_trace* trace) {
+  if (p.dtype == KD_BF16)
+    return backward_t<bf16_t>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace,
+                              stream, trace);
+  return backward_t<float>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace,
+                           stream, trace);
+}
+
+}  // namespace kd

@@ -1,0 +1,212 @@
+"""C ABI: the library loads, exports every function include/kd_loss.h declares,
+and rejects invalid calls on the host before anything is enqueued.
+
+No test here launches a kernel: every call either fails validation or only
+sizes buffers, so the file is safe with or without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kl_knowledge_distillation_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kd_loss.h")
+
+FAKE = 1 << 20  # a 16-byte aligned, never dereferenced address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for must in ("kd_loss_fwd", "kd_loss_bwd", "kd_workspace_bytes", "kd_saved_bytes",
+                 "kd_read_status", "kd_status_string", "kd_device_supported"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+    # and the binding's table covers exactly the declared functions
+    assert sorted(L.EXPORTS) == declared_functions()
+
+
+def _desc(kind="tied", dtype=L.KD_BF16, n=300, d=512, v=3000, d_t=0, k=0):
+    s = L.KdStudent(L.KD_STUDENT_PROJECTION, dtype, n, d, v, FAKE, FAKE, None)
+    t = L.KdTeacher()
+    if kind == "tied":
+        t.kind, t.d_t, t.hidden = L.KD_TEACHER_TIED, d_t, FAKE
+    elif kind == "separate":
+        t.kind, t.d_t, t.hidden, t.weight = L.KD_TEACHER_SEPARATE, d_t or 256, FAKE, FAKE
+    else:
+        t.kind, t.k, t.topk_idx, t.topk_prob = L.KD_TEACHER_TOPK, k or 10, FAKE, FAKE
+    p = L.KdParams(1.0, 0.0, 1.0, 2.0 if kind != "topk" else 1.0, -100, L.KD_REDUCE_MEAN, 0.0, 0, 0)
+    if kind == "topk":
+        p.student_ce_weight = 0.0
+    return s, t, p
+
+
+def _ws(s, t, p, bwd=0):
+    lib = L.load()
+    nb = ctypes.c_size_t(0)
+    st = lib.kd_workspace_bytes(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), bwd,
+                                ctypes.byref(nb))
+    return st, nb.value
+
+
+def _fwd(s, t, p, labels=FAKE, ws_bytes=None, saved=FAKE, workspace=FAKE):
+    lib = L.load()
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    out = L.KdOutputs(FAKE, FAKE, FAKE, FAKE)
+    return lib.kd_loss_fwd(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), labels,
+                           ctypes.byref(out), saved, workspace, ws_bytes, None, None)
+
+
+def _bwd(s, t, p, labels=FAKE, ws_bytes=1 << 40, saved=FAKE):
+    lib = L.load()
+    return lib.kd_loss_bwd(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), labels, saved, None,
+                           FAKE, FAKE, 0, FAKE, ws_bytes, None, None)
+
+
+def test_saved_bytes():
+    lib = L.load()
+    assert lib.kd_saved_bytes(0) == 64
+    assert lib.kd_saved_bytes(4096) == 16 * 4096 + 64
+
+
+def test_status_strings():
+    lib = L.load()
+    for code in range(10):
+        assert lib.kd_status_string(code)
+    assert lib.kd_status_string(L.KD_OK) == b"ok"
+
+
+def test_workspace_sizes_are_valid_and_monotone_in_chunk():
+    s, t, p = _desc()
+    prev_bwd = 0
+    for chunk in (128, 1024, 2048, 8192):
+        p.vocab_chunk = chunk
+        st, fwd = _ws(s, t, p, 0)
+        assert st == L.KD_OK and fwd > 0
+        st, bwd = _ws(s, t, p, 1)
+        assert st == L.KD_OK
+        assert bwd >= prev_bwd  # the dz slab grows with the chunk (until it covers V)
+        prev_bwd = bwd
+    # forward records shrink as the slice widens
+    p.vocab_chunk = 128
+    small = _ws(s, t, p, 0)[1]
+    p.vocab_chunk = 2048
+    assert _ws(s, t, p, 0)[1] < small
+
+
+def test_backward_workspace_is_O_n_chunk_not_n_vocab():
+    # topk-sized problem: the dz slab is n * chunk * 2 bytes, far below n * v * 4
+    s, t, p = _desc("topk", n=32768, d=4096, v=151936, k=100)
+    p.vocab_chunk = 8192
+    st, bwd = _ws(s, t, p, 1)
+    assert st == L.KD_OK
+    assert bwd <= 32768 * 8192 * 2 + (1 << 16)
+    assert bwd < 32768 * 151936 * 4 / 8
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("n0", L.KD_ERR_SHAPE), ("v0", L.KD_ERR_SHAPE), ("d_odd", L.KD_ERR_ALIGN),
+    ("dtype", L.KD_ERR_DTYPE), ("T0", L.KD_ERR_PARAM), ("Tnan", L.KD_ERR_PARAM),
+    ("wneg", L.KD_ERR_PARAM), ("winf", L.KD_ERR_PARAM), ("reduction", L.KD_ERR_PARAM),
+    ("null_hidden", L.KD_ERR_NULL), ("misaligned", L.KD_ERR_ALIGN),
+    ("tied_dt", L.KD_ERR_SHAPE), ("sep_dt0", L.KD_ERR_SHAPE), ("topk_k", L.KD_ERR_SHAPE),
+    ("topk_T", L.KD_ERR_UNSUPPORTED), ("topk_ce", L.KD_ERR_PARAM),
+    ("topk_labels", L.KD_ERR_PARAM), ("labels_missing", L.KD_ERR_NULL),
+    ("ws_small", L.KD_ERR_WORKSPACE), ("ws_null", L.KD_ERR_NULL), ("chunk_neg", L.KD_ERR_PARAM),
+    ("teacher_kind", L.KD_ERR_PARAM), ("labels_misaligned", L.KD_ERR_ALIGN),
+])
+def test_forward_rejects_invalid_arguments(case, expect):
+    kind = "topk" if case.startswith("topk") else ("separate" if case.startswith("sep") else "tied")
+    s, t, p = _desc(kind)
+    kw = {}
+    if case == "n0":
+        s.n = 0
+    elif case == "v0":
+        s.v = 0
+    elif case == "d_odd":
+        s.d = 100
+    elif case == "dtype":
+        s.dtype = 7
+    elif case == "T0":
+        p.temperature = 0.0
+    elif case == "Tnan":
+        p.temperature = float("nan")
+    elif case == "wneg":
+        p.kl_weight = -1.0
+    elif case == "winf":
+        p.student_ce_weight = float("inf")
+    elif case == "reduction":
+        p.reduction = 9
+    elif case == "null_hidden":
+        s.hidden = None
+    elif case == "misaligned":
+        s.weight = FAKE + 2
+    elif case == "tied_dt":
+        t.d_t = 256
+    elif case == "sep_dt0":
+        t.d_t = 0
+    elif case == "topk_k":
+        t.k = 0
+    elif case == "topk_T":
+        p.temperature = 2.0
+    elif case == "topk_ce":
+        p.student_ce_weight = 1.0
+    elif case == "topk_labels":
+        pass
+    elif case == "labels_missing":
+        kw["labels"] = None
+    elif case == "ws_small":
+        kw["ws_bytes"] = 16
+    elif case == "ws_null":
+        kw["workspace"] = None
+    elif case == "chunk_neg":
+        p.vocab_chunk = -1
+    elif case == "teacher_kind":
+        t.kind = 42
+    elif case == "labels_misaligned":
+        kw["labels"] = FAKE + 4
+    if kind == "topk" and case not in ("topk_labels",):
+        kw.setdefault("labels", None)
+    assert _fwd(s, t, p, **kw) == expect
+
+
+def test_backward_rejections():
+    s, t, p = _desc()
+    p.reduction = L.KD_REDUCE_NONE
+    assert _bwd(s, t, p) == L.KD_ERR_UNSUPPORTED
+    s, t, p = _desc()
+    assert _bwd(s, t, p, saved=None) == L.KD_ERR_WORKSPACE
+    assert _bwd(s, t, p, ws_bytes=16) == L.KD_ERR_WORKSPACE
+    # the logits scorer is forward only
+    s2 = L.KdStudent(L.KD_STUDENT_LOGITS, L.KD_BF16, 300, 0, 3000, None, None, FAKE)
+    t2 = L.KdTeacher(L.KD_TEACHER_SEPARATE, 0, 256, FAKE, FAKE, None, None)
+    assert _bwd(s2, t2, p) == L.KD_ERR_UNSUPPORTED
+
+
+def test_logits_student_requires_separate_teacher():
+    s = L.KdStudent(L.KD_STUDENT_LOGITS, L.KD_BF16, 300, 0, 3000, None, None, FAKE)
+    t = L.KdTeacher(L.KD_TEACHER_TIED, 0, 0, FAKE, None, None, None)
+    p = L.KdParams(1.0, 0.0, 1.0, 1.0, -1, L.KD_REDUCE_NONE, 0.0, 0, 0)
+    assert _fwd(s, t, p) == L.KD_ERR_UNSUPPORTED
+
+
+def test_null_descriptors():
+    lib = L.load()
+    assert lib.kd_loss_fwd(None, None, None, None, None, None, None, 0, None, None) == L.KD_ERR_NULL
+    nb = ctypes.c_size_t(0)
+    assert lib.kd_workspace_bytes(None, None, None, 0, ctypes.byref(nb)) == L.KD_ERR_NULL
+    assert lib.kd_read_status(None, None, None) == L.KD_ERR_NULL

@@ -1,0 +1,143 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Sizes are chosen so the oracle finishes in seconds while the problem still
+spans several 128-row tiles, several vocabulary slices / chunks, and ragged
+tails in tokens and vocabulary.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_common import (assert_grad, assert_scalar, assert_tokens, full_parity, make_runner,
+                        oracle_problem, params_of, run_gpu, say, to_np)
+from kl_knowledge_distillation_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+C1 = WORKLOADS["tiny_tied_fp32"]
+C2 = WORKLOADS["quickstart_tied_bf16"]
+C3 = WORKLOADS["separate_bf16"]
+C4 = WORKLOADS["topk_bf16"]
+C5 = WORKLOADS["scorer_bf16"]
+
+SMALL = {
+    "tiny_fp32": C1,
+    "tiny_fp32_ragged": C1.scaled(n=70, v=1000, ignore_frac=0.2),
+    "quickstart_small": C2.scaled(n=300, d=512, v=3000),
+    "quickstart_ragged": C2.scaled(n=130, d=136, v=1029),
+    "separate_small": C3.scaled(n=200, d=256, d_t=512, v=2000),
+    "separate_small_T2": C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=2.0,
+                                   ignore_frac=0.1),
+    "topk_small": C4.scaled(n=300, d=512, v=5000),
+    "topk_ragged": C4.scaled(n=129, d=264, v=1031, k=7),
+    "scorer_small": C5.scaled(n=300, d_t=512, v=5000),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    full_parity(SMALL[name])
+
+
+@pytest.mark.parametrize("chunk", [128, 384, 1024])
+def test_chunk_and_slice_sizes(chunk):
+    full_parity(C2.scaled(n=260, d=256, v=2100, name=f"quickstart_chunk{chunk}"), vocab_chunk=chunk)
+
+
+@pytest.mark.parametrize("chunk", [256, 2048, 16384])
+def test_scorer_chunk_sweep(chunk):
+    full_parity(C5.scaled(n=256, d_t=256, v=9000), vocab_chunk=chunk)
+
+
+def test_reductions_and_normalizer():
+    w = C2.scaled(n=200, d=256, v=1500)
+    x = make_inputs(w, "cuda", seed=3)
+    s, t, labels = oracle_problem(w, x)
+    for red, norm in (("sum", 0.0), ("mean", 0.0), ("mean", 777.0)):
+        say(f"[reduction] {red} normalizer={norm}")
+        r = make_runner(w, x, reduction=red)
+        r.p.normalizer = norm
+        r.forward()
+        dh = torch.empty((r.n, r.d), dtype=torch.float32, device="cuda")
+        dw = torch.empty((r.v, r.d), dtype=torch.float32, device="cuda")
+        g = torch.tensor(0.37, device="cuda")
+        r.backward(dh, dw, grad_loss=g)
+        torch.cuda.synchronize()
+        p = params_of(w)
+        p.reduction, p.normalizer = red, norm
+        ref = O.forward(s, t, p, labels)
+        assert_scalar(float(r.loss), ref["loss"], "bf16", f"loss {red}")
+        dH, dW = O.backward(s, t, p, labels, grad_loss=0.37)
+        assert_grad(to_np(dh), dH, "bf16", f"dH {red}")
+        assert_grad(to_np(dw), dW, "bf16", f"dW {red}")
+
+
+def test_accumulate_adds_into_gradients():
+    w = C1.scaled(n=96, v=700)
+    x = make_inputs(w, "cuda", seed=5)
+    r, dh, dw = run_gpu(w, x)
+    dh2 = torch.full_like(dh, 0.5)
+    dw2 = torch.full_like(dw, -0.25)
+    r.forward()
+    r.backward(dh2, dw2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(dh2, dh + 0.5, rtol=1e-6, atol=1e-6)
+    assert torch.allclose(dw2, dw - 0.25, rtol=1e-6, atol=1e-6)
+
+
+def test_kl_exactly_zero_for_identical_teacher():
+    """Tied teacher with H_t = H_s: the two logit tiles are computed by the same
+    MFMA sequence, so every statistic matches and KL is 0 bit for bit."""
+    w = C2.scaled(n=260, d=256, v=3000)
+    x = make_inputs(w, "cuda", seed=1)
+    x["teacher_hidden"] = x["student_hidden"].clone()
+    r, dh, dw = run_gpu(w, x)
+    assert torch.count_nonzero(r.kl).item() == 0
+
+
+def test_deterministic_bitwise():
+    w = C2.scaled(n=300, d=256, v=2500)
+    x = make_inputs(w, "cuda", seed=2)
+    outs = []
+    for _ in range(2):
+        r, dh, dw = run_gpu(w, x, vocab_chunk=1024)
+        outs.append((r.loss.clone(), r.kl.clone(), r.student_ce.clone(), dh.clone(), dw.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_out_of_range_label_flag():
+    w = C2.scaled(n=150, d=128, v=900)
+    x = make_inputs(w, "cuda", seed=4)
+    lab = x["labels"].clone()
+    lab[7] = w.v + 5
+    lab[11] = -3
+    x["labels"] = lab
+    r, dh, dw = run_gpu(w, x)
+    assert r.read_status() == 1
+    s, t, labels = oracle_problem(w, x)
+    ref = O.forward(s, t, params_of(w), labels)  # the oracle treats them as ignored
+    assert_tokens(to_np(r.student_ce), ref["student_ce"], "bf16", "ce with bad labels")
+    assert_scalar(float(r.loss), ref["loss"], "bf16", "loss with bad labels")
+    dH, dW = O.backward(s, t, params_of(w), labels)
+    assert_grad(to_np(dh), dH, "bf16", "dH with bad labels")
+
+
+def test_all_labels_ignored():
+    w = C2.scaled(n=140, d=128, v=700)
+    x = make_inputs(w, "cuda", seed=6)
+    x["labels"] = torch.full_like(x["labels"], w.ignore_index)
+    r, dh, dw = run_gpu(w, x)
+    assert float(r.loss) == 0.0
+    assert torch.count_nonzero(dh).item() == 0 and torch.count_nonzero(dw).item() == 0
+
+
+def test_full_quickstart_tied_bf16():
+    """Whole quickstart-shaped problem (N=4096, D=2048, V=32000), every output."""
+    full_parity(C2)
+
+
+def test_full_tiny_fp32_default_and_chunked():
+    full_parity(C1)
+    full_parity(C1, vocab_chunk=256)
