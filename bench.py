@@ -1,0 +1,280 @@
+"""Benchmark: fused LM-head + CE + KL distillation loss, forward + backward, one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--vocab-chunk C]
+
+One step is the whole hot path on one batch of synthetic input already
+resident in HBM: prep, forward tiles, merge, finalize, then per vocabulary
+chunk the backward recompute (dz), the dW GEMM and the dH GEMM. The default
+workload is the quickstart-shaped tied teacher (N=4096, D=2048, V=32000,
+bf16, T=2). Prints one JSON line.
+
+Throughput `value` is tokens per second. Besides it the line carries the
+method's MFMA TFLOP/s (including the backward recompute), peak HBM bytes,
+the roofline of the dominant kernel (HIP events around its launches on the
+library's stream, inside the timed region), and the float64 oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def method_flops(w) -> dict:
+    """Algorithmic MFMA flops of one fwd+bwd step and of one launch of each kernel.
+
+    Forward projection tiles: 2 N D V per student GEMM and per teacher GEMM;
+    the backward recomputes them, then dW and dH cost 2 N D V each.
+    """
+    n, d, v, dt = w.n, w.d, w.v, w.teacher_dim
+    if w.teacher == "tied":
+        fwd = 4 * n * d * v
+    elif w.teacher == "separate":
+        fwd = 2 * n * d * v + 2 * n * dt * v
+    else:
+        fwd = 2 * n * d * v
+    total = 2 * fwd + 4 * n * d * v
+    useful = fwd + 4 * n * d * v
+    return {"total": total, "useful": useful, "fwd_per_launch": fwd}
+
+
+def kernel_flops_per_launch(w, kernel: str, chunk: int) -> float:
+    n, d, v = w.n, w.d, w.v
+    fl = method_flops(w)
+    if kernel == "fwd":
+        return fl["fwd_per_launch"]
+    n_chunks = -(-v // chunk)
+    per_chunk_cols = v / n_chunks  # average columns per launch
+    if kernel == "bwd_dz":
+        return fl["fwd_per_launch"] * per_chunk_cols / v
+    if kernel in ("gemm_dw", "gemm_dh"):
+        return 2 * n * d * per_chunk_cols
+    return 0.0
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kl_knowledge_distillation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float = 12.0) -> dict:
+    """The float64 oracle (as it stands) on a bounded row sample of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from kl_knowledge_distillation_amd.inputs import make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+
+    cap = min(w.n, 2048)
+    x = make_inputs(w.scaled(n=cap), "cpu", seed=0)
+    f = lambda t: None if t is None else t.float().numpy().astype(np.float64)  # noqa: E731
+    full = {k: f(v) if k not in ("labels", "topk_idx") else (None if v is None else v.numpy())
+            for k, v in x.items()}
+    p = O.Params(student_ce_weight=w.student_ce_weight, teacher_ce_weight=w.teacher_ce_weight,
+                 kl_weight=w.kl_weight, temperature=w.temperature, ignore_index=w.ignore_index)
+
+    def run(rows: int) -> float:
+        g = lambda k: None if full[k] is None else full[k][:rows]  # noqa: E731
+        s = O.Student(hidden=g("student_hidden"), weight=full["weight"])
+        if w.teacher == "tied":
+            t = O.Teacher("tied", hidden=g("teacher_hidden"))
+        elif w.teacher == "separate":
+            t = O.Teacher("separate", hidden=g("teacher_hidden"), weight=full["teacher_weight"])
+        else:
+            t = O.Teacher("topk", idx=g("topk_idx"), prob=g("topk_prob"))
+        t0 = time.perf_counter()
+        O.forward(s, t, p, g("labels"))
+        O.backward(s, t, p, g("labels"))
+        return time.perf_counter() - t0
+
+    probe = 64
+    dt = run(probe)
+    rows = int(min(cap, max(probe, probe * target_s / max(dt, 1e-3))))
+    rows = max(probe, rows // 64 * 64)
+    dt = run(rows)
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} of {w.n} rows of {w.name}, forward + backward (dH, dW) in float64, "
+                      f"{dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="quickstart_tied_bf16")
+    ap.add_argument("--vocab-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from kl_knowledge_distillation_amd import _lib as L
+    from kl_knowledge_distillation_amd.api import Runner, Tracer
+    from kl_knowledge_distillation_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(w, dev, seed=0)
+    torch.cuda.synchronize()
+    kw = dict(labels=x["labels"], student_ce_weight=w.student_ce_weight,
+              teacher_ce_weight=w.teacher_ce_weight, kl_weight=w.kl_weight,
+              temperature=w.temperature, ignore_index=w.ignore_index,
+              vocab_chunk=args.vocab_chunk, want_grads=not w.forward_only)
+    if w.student == "logits":
+        kw["student_logits"] = x["student_logits"]
+    else:
+        kw.update(student_hidden=x["student_hidden"], weight=x["weight"])
+    if w.teacher == "tied":
+        kw.update(teacher_kind="tied", teacher_hidden=x["teacher_hidden"])
+    elif w.teacher == "separate":
+        kw.update(teacher_kind="separate", teacher_hidden=x["teacher_hidden"],
+                  teacher_weight=x["teacher_weight"])
+    else:
+        kw.update(teacher_kind="topk", topk_idx=x["topk_idx"], topk_prob=x["topk_prob"])
+    input_bytes = sum(t.numel() * t.element_size() for t in x.values() if t is not None)
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
+    r = Runner(**kw)
+    dh = dw = None
+    if not w.forward_only:
+        dh = torch.empty((r.n, r.d), dtype=torch.float32, device=dev)
+        dw = torch.empty((r.v, r.d), dtype=torch.float32, device=dev)
+    output_bytes = sum(t.numel() * t.element_size() for t in (dh, dw) if t is not None)
+    output_bytes += 3 * r.n * 4 + 4
+
+    def step(trace=None):
+        r.forward(trace)
+        if dh is not None:
+            r.backward(dh, dw, trace=trace)
+
+    # Warm-up, with every kernel class traced once to find the dominant one.
+    all_tr = Tracer(capacity=4096, kernels=L.KERNELS)
+    for i in range(max(args.warmup, 1)):
+        all_tr.reset()
+        step(all_tr.trace)
+    torch.cuda.synchronize()
+    last_step = all_tr.durations_ms()
+    per_kernel = {k: sum(v) for k, v in last_step.items()}
+    dominant = max(per_kernel, key=per_kernel.get)
+    n_dom = len(last_step[dominant])
+    all_tr.close()
+
+    tr = Tracer(capacity=2 * n_dom * args.steps + 2, kernels=(dominant,))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(tr.trace)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    durs = tr.durations_ms().get(dominant, [])
+    tr.close()
+    status = r.read_status()
+    peak = torch.cuda.max_memory_allocated(dev)
+
+    ms_per_step = gpu_ms / args.steps
+    tokens_per_s = r.n * args.steps / (gpu_ms / 1e3)
+    fl = method_flops(w)
+    peak_tflops = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
+    tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
+    # the backward chunk the library used (same rule as the C ABI's default)
+    chunk = args.vocab_chunk if args.vocab_chunk > 0 else 8192
+    chunk = min(-(-chunk // 128) * 128, -(-w.v // 128) * 128)
+    launch_ms = sum(durs) / len(durs) if durs else float("nan")
+    kflops = kernel_flops_per_launch(w, dominant, chunk)
+    achieved = kflops / (launch_ms / 1e3) / 1e12 if durs else None
+    rec = {
+        "metric": "fused LM-head+CE+KL fwd+bwd tokens/s" if not w.forward_only
+        else "fused teacher-LM-head+CE+KL forward tokens/s",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "fp32" else "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "n_tokens": w.n, "hidden": w.d, "teacher_hidden": w.teacher_dim,
+                   "vocab": w.v, "teacher": w.teacher, "temperature": w.temperature,
+                   "top_k": w.k or None, "vocab_chunk": chunk, "parallelism": "single GPU"},
+        "mfma_tflops": round(tflops, 1),
+        "mfma_frac_of_peak": round(tflops / peak_tflops, 4),
+        "useful_tflops": round(fl["useful"] / (ms_per_step / 1e3) / 1e12, 1),
+        "peak_hbm_bytes": int(peak),
+        "peak_extra_hbm_bytes": int(peak - base_alloc - output_bytes),
+        "input_bytes": int(input_bytes),
+        "wall_s": round(wall, 3),
+        "device_status": status,
+        "kernel_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": peak_tflops,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak_tflops, 4) if achieved else None,
+            "traffic": traffic_for(dominant, w.name),
+            "launch_ms": round(launch_ms, 4),
+            "launches": len(durs),
+            "flop_per_launch": kflops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -94,50 +94,87 @@ struct Operand {
 
 // Stages one 128-row x K-step tile of an operand: global -> registers -> LDS.
 // Out-of-range rows / k are zero-filled, so ragged edges contribute nothing.
+//
+// K-contiguous operands move 16-byte chunks straight through. Row-contiguous
+// operands are transposed on the way: lane L of wave w owns rows 2L and 2L+1
+// and the 16-byte K chunk w of both (8 bf16 or 4 fp32 k-values). It reads one
+// element pair from each of those k-rows (each load instruction of the wave
+// covers 256 contiguous bytes of one k-row), repacks the pairs in registers,
+// and writes two 16-byte LDS chunks whose addresses fall in distinct banks.
 template <typename T, bool KC>
 struct Stager {
   uint4 r[2];
 
   __device__ __forceinline__ void load(const Operand<T, KC>& op, int64_t row0, int64_t k0, int tid) {
     constexpr int PC = Elem<T>::kPerChunk;
+    if constexpr (KC) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + kThreads * j;
-      if constexpr (KC) {
+      for (int j = 0; j < 2; ++j) {
+        const int q = tid + kThreads * j;
         const int row = q >> 2, c = q & 3;
         const int64_t grow = row0 + row, k = k0 + (int64_t)c * PC;
         if (grow < op.rows && k < op.kdim)
           r[j] = *reinterpret_cast<const uint4*>(op.ptr + grow * op.ld + k);
         else
           r[j] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      const int lane = tid & 63, w = tid >> 6;
+      const int64_t m = row0 + 2 * lane;
+      const bool mok = m < op.rows;  // rows is a multiple of the chunk width, so m+1 too
+      uint32_t* u = reinterpret_cast<uint32_t*>(r);
+      if constexpr (sizeof(T) == 2) {
+        // k-rows k0 + 8w + j, j = 0..7; one 32-bit pair (rows m, m+1) each.
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t k = k0 + 8 * w + j;
+          u[j] = (mok && k < op.kdim)
+                     ? *reinterpret_cast<const uint32_t*>(op.ptr + k * op.ld + m)
+                     : 0u;
+        }
       } else {
-        constexpr int CPR = kTile / PC;  // chunks per k-row
-        const int krow = q / CPR, mc = q % CPR;
-        const int64_t k = k0 + krow, m = row0 + (int64_t)mc * PC;
-        if (k < op.kdim && m < op.rows)
-          r[j] = *reinterpret_cast<const uint4*>(op.ptr + k * op.ld + m);
-        else
-          r[j] = make_uint4(0u, 0u, 0u, 0u);
+        // k-rows k0 + 4w + j, j = 0..3; one 64-bit pair (rows m, m+1) each.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t k = k0 + 4 * w + j;
+          uint2 p = make_uint2(0u, 0u);
+          if (mok && k < op.kdim) p = *reinterpret_cast<const uint2*>(op.ptr + k * op.ld + m);
+          u[2 * j] = p.x;
+          u[2 * j + 1] = p.y;
+        }
       }
     }
   }
 
   __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
-    constexpr int PC = Elem<T>::kPerChunk;
+    if constexpr (KC) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + kThreads * j;
-      if constexpr (KC) {
+      for (int j = 0; j < 2; ++j) {
+        const int q = tid + kThreads * j;
         const int row = q >> 2, c = q & 3;
         *reinterpret_cast<uint4*>(lds + row * kRowBytes + c * 16) = r[j];
-      } else {
-        constexpr int CPR = kTile / PC;
-        const int krow = q / CPR, m = (q % CPR) * PC;
-        const T* e = reinterpret_cast<const T*>(&r[j]);
-#pragma unroll
-        for (int x = 0; x < PC; ++x)
-          *reinterpret_cast<T*>(lds + (m + x) * kRowBytes + krow * (int)sizeof(T)) = e[x];
       }
+    } else {
+      const int lane = tid & 63, w = tid >> 6;
+      const uint32_t* u = reinterpret_cast<const uint32_t*>(r);
+      uint4 lo, hi;  // k-values of row 2L and of row 2L+1
+      if constexpr (sizeof(T) == 2) {
+        // u[j] = (row m at k_j) | (row m+1 at k_j) << 16
+        lo.x = (u[0] & 0xffffu) | (u[1] << 16);
+        lo.y = (u[2] & 0xffffu) | (u[3] << 16);
+        lo.z = (u[4] & 0xffffu) | (u[5] << 16);
+        lo.w = (u[6] & 0xffffu) | (u[7] << 16);
+        hi.x = (u[0] >> 16) | (u[1] & 0xffff0000u);
+        hi.y = (u[2] >> 16) | (u[3] & 0xffff0000u);
+        hi.z = (u[4] >> 16) | (u[5] & 0xffff0000u);
+        hi.w = (u[6] >> 16) | (u[7] & 0xffff0000u);
+      } else {
+        // u[2j] = row m at k_j, u[2j+1] = row m+1 at k_j
+        lo = make_uint4(u[0], u[2], u[4], u[6]);
+        hi = make_uint4(u[1], u[3], u[5], u[7]);
+      }
+      *reinterpret_cast<uint4*>(lds + (2 * lane) * kRowBytes + w * 16) = lo;
+      *reinterpret_cast<uint4*>(lds + (2 * lane + 1) * kRowBytes + w * 16) = hi;
     }
   }
 };
