@@ -140,6 +140,9 @@ def main() -> int:
     ap.add_argument("--workload", default="quickstart_tied_bf16")
     ap.add_argument("--vocab-chunk", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="copy a buffer of this many MiB once before the timed steps, so a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a known transfer")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -202,6 +205,12 @@ def main() -> int:
     n_dom = len(last_step[dominant])
     all_tr.close()
 
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     tr = Tracer(capacity=2 * n_dom * args.steps + 2, kernels=(dominant,))
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()

@@ -5,7 +5,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdloss.so")
+# KD_LIBRARY may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("KD_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libkdloss.so")
 
 # Status codes and enums (values fixed by include/kd_loss.h).
 KD_OK, KD_ERR_NULL, KD_ERR_SHAPE, KD_ERR_DTYPE, KD_ERR_PARAM = 0, 1, 2, 3, 4

@@ -109,21 +109,28 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.need_t1 = (q.T != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
   q.has_labels = labels ? 1 : 0;
 
+  // Tile geometry: bf16 with every contraction length a multiple of 32 runs the
+  // pipelined 256-row tiles; everything else the register-staged 128-row tiles.
+  const bool d_ok = q.mode == kd::MODE_LOGITS || q.d % 32 == 0;
+  const bool dt_ok = (q.mode != kd::MODE_SEPARATE && q.mode != kd::MODE_LOGITS) || q.dt % 32 == 0;
+  q.pipe = (q.dtype == KD_BF16 && d_ok && dt_ok) ? 1 : 0;
+  q.vt_rows = q.pipe ? kd::pipe_vocab_rows() : 128;
+  const int64_t vt = q.vt_rows;
   // Forward grid: (vocabulary slice) x (128-token tile).
   q.n_ttiles = (int)ceil_div(q.n, kTile);
-  q.n_vtiles = (int)ceil_div(q.v, kTile);
+  q.n_vtiles = (int)ceil_div(q.v, vt);
   int64_t tps;
   if (p->vocab_chunk > 0) {
-    tps = ceil_div(p->vocab_chunk, kTile);
+    tps = ceil_div(p->vocab_chunk, vt);
   } else {
     tps = ((int64_t)q.n_vtiles * q.n_ttiles) / kTargetFwdBlocks;
   }
   tps = std::max<int64_t>(1, std::min<int64_t>(tps, q.n_vtiles));
   q.tps = (int)tps;
   q.n_slices = (int)ceil_div(q.n_vtiles, tps);
-  // Backward chunk.
-  int64_t chunk = (p->vocab_chunk > 0) ? ceil_div(p->vocab_chunk, kTile) * kTile : kDefaultChunk;
-  chunk = std::min<int64_t>(chunk, ceil_div(q.v, kTile) * kTile);
+  // Backward chunk: a whole number of fused vocabulary tiles.
+  int64_t chunk = (p->vocab_chunk > 0) ? ceil_div(p->vocab_chunk, vt) * vt : kDefaultChunk;
+  chunk = std::min<int64_t>(chunk, ceil_div(q.v, vt) * vt);
   q.chunk = chunk;
   q.n_chunks = (int)ceil_div(q.v, chunk);
   q.merge_blocks = (int)ceil_div(q.n, kd::kMergeThreads);
@@ -137,8 +144,9 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   off = align_up(off + (size_t)q.merge_blocks * 4 * sizeof(double), 256);
   q.fwd_bytes = off;
   const size_t elem = (q.dtype == KD_BF16) ? 2 : 4;
+  q.dz_rows = (int64_t)q.n_ttiles * kTile;
   q.off_dz = kd::kStatusBytes;
-  q.bwd_bytes = align_up(q.off_dz + (size_t)q.n * (size_t)q.chunk * elem, 256);
+  q.bwd_bytes = align_up(q.off_dz + (size_t)q.dz_rows * (size_t)q.chunk * elem, 256);
   *out = q;
   return KD_OK;
 }

@@ -33,8 +33,11 @@ struct Plan {
   int need_zT = 0;    // T != 1: student statistics at z/T are kept apart from z
   int need_t1 = 0;    // teacher CE wanted at T != 1: teacher statistics at t
   int has_labels = 0;
+  int pipe = 0;       // bf16 with hidden sizes multiple of 32: 256-row pipelined tiles
+  int vt_rows = 128;  // vocabulary rows per fused tile
   int n_ttiles = 0, n_vtiles = 0, tps = 1, n_slices = 0;  // forward grid
-  int64_t chunk = 0;  // backward vocabulary chunk (multiple of 128)
+  int64_t chunk = 0;  // backward vocabulary chunk (multiple of the fused tile rows)
+  int64_t dz_rows = 0;  // rows of the logit-gradient slab: n rounded up to the token tile
   int n_chunks = 0;
   int merge_blocks = 0;
   // forward workspace layout (bytes from the workspace base)
@@ -53,6 +56,9 @@ struct Tensors {
   const float* topk_prob = nullptr;
   const int64_t* labels = nullptr;
 };
+
+// Vocabulary rows per tile of the pipelined bf16 geometry compiled in.
+int pipe_vocab_rows();
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
                       void* workspace, hipStream_t stream, kd_trace* trace);

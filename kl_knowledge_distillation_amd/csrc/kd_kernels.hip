@@ -24,8 +24,11 @@
 //   gemm_dh   dH += dz W[chunk]          (K = chunk)
 #include <math.h>
 
+#include <type_traits>
+
 #include "kd_device.hpp"
 #include "kd_internal.hpp"
+#include "kd_pipe.hpp"
 
 namespace kd {
 
@@ -146,6 +149,60 @@ __device__ __forceinline__ void fwd_update(const f32x16 (&z)[2][2], const f32x16
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Tile geometry of the fused kernels
+// ---------------------------------------------------------------------------
+
+// Staged: 128 vocabulary rows x 128 tokens, 4 waves (2 x 2), registers carry
+// the copies; any element type, any hidden size that is a multiple of 8.
+struct GeoStaged {
+  static constexpr bool kPipe = false;
+  static constexpr int kThreads = 256, kVT = 128, kTT = 128, kWM = 2;
+  template <int NB> static constexpr int lds_bytes() { return 2 * (1 + NB) * kTileBytes; }
+};
+// Pipelined: VT vocabulary rows x 128 tokens, WM x 2 waves, S stages of direct
+// global -> LDS copies; bf16 with hidden sizes that are multiples of 32.
+template <int VT, int WM, int S>
+struct GeoPipe {
+  static constexpr bool kPipe = true;
+  static constexpr int kThreads = 128 * WM, kVT = VT, kTT = 128, kWM = WM, kStages = S;
+  template <int NB> using Cfg = PipeCfg<VT, 128, NB, WM, S>;
+  template <int NB> static constexpr int lds_bytes() { return Cfg<NB>::kLdsBytes; }
+};
+#ifndef KD_PIPE_GEO
+#define KD_PIPE_GEO 0
+#endif
+#if KD_PIPE_GEO == 1
+using GeoFused = GeoPipe<128, 2, 3>;
+#elif KD_PIPE_GEO == 2
+using GeoFused = GeoPipe<256, 4, 3>;
+#else
+using GeoFused = GeoPipe<256, 4, 4>;
+#endif
+
+// acc[g] = A[a_row0 : +VT, 0:K] * B_g[b_row0 : +TT, 0:K]^T for K-contiguous operands.
+template <typename T, class G, int NB>
+__device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t arows,
+                                             const T* const (&b)[NB], int64_t ldb, int64_t brows,
+                                             int64_t a_row0, int64_t b_row0, int64_t K,
+                                             uint8_t* lds, f32x16 (&acc)[NB][2][2], int tid) {
+  if constexpr (G::kPipe) {
+    static_assert(sizeof(T) == 2, "the pipelined geometry is bf16 only");
+    const PipeOperand A{a, lda, arows};
+    PipeOperand B[NB];
+#pragma unroll
+    for (int g = 0; g < NB; ++g) B[g] = PipeOperand{b[g], ldb, brows};
+    pipe_mainloop<typename G::template Cfg<NB>, NB>(A, B, a_row0, b_row0, K, lds, acc, tid);
+  } else {
+    const Operand<T, true> A{a, lda, arows, K};
+    Operand<T, true> B[NB];
+#pragma unroll
+    for (int g = 0; g < NB; ++g) B[g] = Operand<T, true>{b[g], ldb, brows, K};
+    mainloop<T, true, true, NB>(A, B, a_row0, b_row0, K, lds, acc, tid);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward tile kernel
 // ---------------------------------------------------------------------------
@@ -163,15 +220,15 @@ struct FwdArgs {
   float* rec;  // [kRecFields][n_slices][n]
 };
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
+template <typename T, int MODE, class G>
+__global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (1 + NB) * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::template lds_bytes<NB>()];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int slice, tt;
   grouped_tile(t, a.n_slices, a.n_ttiles, 8, slice, tt);
-  const int64_t t0 = (int64_t)tt * kTile;
+  const int64_t t0 = (int64_t)tt * G::kTT;
   const int vt_begin = slice * a.tps;
   const int vt_end = min(a.n_vtiles, vt_begin + a.tps);
 
@@ -189,26 +246,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   f32x16 zl[2][2];       // student logits loaded in LOGITS mode
 
   for (int vt = vt_begin; vt < vt_end; ++vt) {
-    const int64_t v0 = (int64_t)vt * kTile;
+    const int64_t v0 = (int64_t)vt * G::kVT;
     if constexpr (MODE == MODE_TIED) {
-      const Operand<T, true> A{W, a.d, a.v, a.d};
-      const Operand<T, true> B[2] = {{hs, a.d, a.n, a.d}, {ht, a.d, a.n, a.d}};
-      mainloop<T, true, true, 2>(A, B, v0, t0, a.d, lds, acc, tid);
+      const T* const b[2] = {hs, ht};
+      tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     } else if constexpr (MODE == MODE_SEPARATE) {
-      const Operand<T, true> A{W, a.d, a.v, a.d};
-      const Operand<T, true> B{hs, a.d, a.n, a.d};
-      mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
-      const Operand<T, true> At{Wt, a.dt, a.v, a.dt};
-      const Operand<T, true> Bt{ht, a.dt, a.n, a.dt};
-      mainloop<T, true, true, 1>(At, &Bt, v0, t0, a.dt, lds, tacc, tid);
+      const T* const b[1] = {hs};
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+      const T* const bt[1] = {ht};
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
     } else if constexpr (MODE == MODE_TOPK) {
-      const Operand<T, true> A{W, a.d, a.v, a.d};
-      const Operand<T, true> B{hs, a.d, a.n, a.d};
-      mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
+      const T* const b[1] = {hs};
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     } else {  // MODE_LOGITS
-      const Operand<T, true> At{Wt, a.dt, a.v, a.dt};
-      const Operand<T, true> Bt{ht, a.dt, a.n, a.dt};
-      mainloop<T, true, true, 1>(At, &Bt, v0, t0, a.dt, lds, tacc, tid);
+      const T* const bt[1] = {ht};
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
       const T* L = static_cast<const T*>(a.logits);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -224,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     }
 
     uint32_t ok = 0xffffffffu;
-    const bool tail = v0 + kTile > a.v;
+    const bool tail = v0 + G::kVT > a.v;
     if (tail) {
       ok = 0u;
 #pragma unroll
@@ -233,7 +285,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
         for (int x = 0; x < 16; ++x)
           if (v0 + acc_row(wm, mb, x, lane) < a.v) ok |= 1u << (mb * 16 + x);
     }
-    // Pick the (z, t) accumulators of this mode.
     if constexpr (MODE == MODE_TIED) {
       if (tail) fwd_update<MODE, true>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
       else fwd_update<MODE, false>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
@@ -264,14 +315,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     o.st1 = __shfl_xor(st[nb].st1, 32);
     stats_merge(st[nb], o);
   }
-  // Combine the two waves that share a token block (wm = 0 and wm = 1). The
-  // main loop ended with a barrier, so the operand LDS is free.
+  // Combine the kWM waves that share a token block (same wn, different vocabulary
+  // rows), in the fixed order wm = 1, 2, ... The main loop ended with a barrier,
+  // so its LDS is free.
   float* xs = reinterpret_cast<float*>(lds);
   const int l32 = lane & 31;
-  if (wm == 1 && lane < 32) {
+  if (wm > 0 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      float* p = xs + ((wn * 2 + nb) * kRecFields) * 32 + l32;
+      float* p = xs + ((((wm - 1) * 2 + wn) * 2 + nb) * kRecFields) * 32 + l32;
       const RowStats& s = st[nb];
       p[0 * 32] = s.mz1; p[1 * 32] = s.sz1; p[2 * 32] = s.mzT; p[3 * 32] = s.szT;
       p[4 * 32] = s.mtT; p[5 * 32] = s.stT; p[6 * 32] = s.a;   p[7 * 32] = s.mt1;
@@ -282,12 +334,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   if (wm == 0 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const float* p = xs + ((wn * 2 + nb) * kRecFields) * 32 + l32;
-      RowStats o;
-      o.mz1 = p[0 * 32]; o.sz1 = p[1 * 32]; o.mzT = p[2 * 32]; o.szT = p[3 * 32];
-      o.mtT = p[4 * 32]; o.stT = p[5 * 32]; o.a = p[6 * 32];   o.mt1 = p[7 * 32];
-      o.st1 = p[8 * 32];
-      stats_merge(st[nb], o);
+#pragma unroll
+      for (int src = 1; src < G::kWM; ++src) {
+        const float* p = xs + ((((src - 1) * 2 + wn) * 2 + nb) * kRecFields) * 32 + l32;
+        RowStats o;
+        o.mz1 = p[0 * 32]; o.sz1 = p[1 * 32]; o.mzT = p[2 * 32]; o.szT = p[3 * 32];
+        o.mtT = p[4 * 32]; o.stT = p[5 * 32]; o.a = p[6 * 32];   o.mt1 = p[7 * 32];
+        o.st1 = p[8 * 32];
+        stats_merge(st[nb], o);
+      }
       const int64_t tok = t0 + acc_col(wn, nb, lane);
       if (tok < a.n) {
         const int64_t stride = (int64_t)a.n_slices * a.n;
@@ -544,8 +599,9 @@ struct BwdArgs {
   int need_zT;
   int64_t c0;             // first vocabulary row of the chunk
   int n_vt, n_ttiles;     // tiles of the chunk
-  void* dz;               // [n][ldz]
+  void* dz;               // [dz_rows][ldz]
   int64_t ldz;
+  int64_t dz_rows;        // n rounded up to the token tile; rows past n are written as 0
 };
 
 template <typename T>
@@ -562,16 +618,16 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, fl
   *reinterpret_cast<uint2*>(p) = u;
 }
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
+template <typename T, int MODE, class G>
+__global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (1 + NB) * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::template lds_bytes<NB>()];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int vt, tt;
   grouped_tile(t, a.n_vt, a.n_ttiles, 8, vt, tt);
-  const int64_t v0 = a.c0 + (int64_t)vt * kTile;
-  const int64_t t0 = (int64_t)tt * kTile;
+  const int64_t v0 = a.c0 + (int64_t)vt * G::kVT;
+  const int64_t t0 = (int64_t)tt * G::kTT;
   const T* hs = static_cast<const T*>(a.hs);
   const T* W = static_cast<const T*>(a.w);
   const T* ht = static_cast<const T*>(a.ht);
@@ -580,20 +636,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   f32x16 acc[NB][2][2];
   f32x16 tacc[1][2][2];
   if constexpr (MODE == MODE_TIED) {
-    const Operand<T, true> A{W, a.d, a.v, a.d};
-    const Operand<T, true> B[2] = {{hs, a.d, a.n, a.d}, {ht, a.d, a.n, a.d}};
-    mainloop<T, true, true, 2>(A, B, v0, t0, a.d, lds, acc, tid);
+    const T* const b[2] = {hs, ht};
+    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   } else if constexpr (MODE == MODE_SEPARATE) {
-    const Operand<T, true> A{W, a.d, a.v, a.d};
-    const Operand<T, true> B{hs, a.d, a.n, a.d};
-    mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
-    const Operand<T, true> At{Wt, a.dt, a.v, a.dt};
-    const Operand<T, true> Bt{ht, a.dt, a.n, a.dt};
-    mainloop<T, true, true, 1>(At, &Bt, v0, t0, a.dt, lds, tacc, tid);
+    const T* const b[1] = {hs};
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    const T* const bt[1] = {ht};
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
   } else {  // MODE_TOPK
-    const Operand<T, true> A{W, a.d, a.v, a.d};
-    const Operand<T, true> B{hs, a.d, a.n, a.d};
-    mainloop<T, true, true, 1>(A, &B, v0, t0, a.d, lds, acc, tid);
+    const T* const b[1] = {hs};
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   }
   const f32x16(&z)[2][2] = acc[0];
   const f32x16(&tl)[2][2] = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
@@ -606,12 +658,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int64_t tok = t0 + acc_col(wn, nb, lane);
-    if (tok >= a.n) continue;
-    const float4 sv = reinterpret_cast<const float4*>(a.saved)[tok];
+    if (tok >= a.dz_rows) continue;
+    const bool live = tok < a.n;  // rows past n are zero padding of the slab
+    const float4 sv = live ? reinterpret_cast<const float4*>(a.saved)[tok] : make_float4(0.f, 0.f, 0.f, 0.f);
     const float L1 = sv.x * kLog2e, LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
     int64_t y = -1;
-    bool valid = true;
-    if (MODE != MODE_TOPK && a.labels) {
+    bool valid = live;
+    if (live && MODE != MODE_TOPK && a.labels) {
       y = a.labels[tok];
       valid = y != a.ignore && y >= 0 && y < a.v;
     }
@@ -640,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
             const float pt = exp2_fast(fmaf(tl[mb][nb][x], a.cT, -LtT));
             dv = fmaf(ck, pz - pt, dv);
           }
-          o[e] = (vv < a.v) ? dv : 0.f;
+          o[e] = (vv < a.v && valid) ? dv : 0.f;
         }
         store4<T>(row + acc_row(wm, mb, q * 4, lane), o[0], o[1], o[2], o[3]);
       }
@@ -720,6 +773,47 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
     }
 }
 
+// Pipelined bf16 GEMM: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output, tile
+// 256 x BN, 8 waves, 4 stages. A / B are K-contiguous or row-contiguous.
+template <bool AKC, bool BKC, int BN>
+struct GemmPipeArgs {
+  std::conditional_t<AKC, PipeOperand, PipeOperandMN> A;
+  std::conditional_t<BKC, PipeOperand, PipeOperandMN> B;
+  float* C;
+  int64_t ldc, M, N, K;
+  int accumulate;
+  int n_mt, n_nt;
+};
+
+template <bool AKC, bool BKC, int BN>
+__global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC, BN> a) {
+  using C = PipeCfg<256, BN, 1, 4, 4, AKC, BKC>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  int mt, nt;
+  grouped_tile(t, a.n_mt, a.n_nt, 8, mt, nt);
+  const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
+  f32x16 acc[1][C::MBLK][C::NBLK];
+  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, a.K, lds, acc, tid);
+#pragma unroll
+  for (int mb = 0; mb < C::MBLK; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NBLK; ++nb) {
+      const int64_t col = n0 + wn * C::TN + nb * 32 + (lane & 31);
+      if (col >= a.N) continue;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int64_t row = m0 + wm * C::TM + mb * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+        if (row < a.M) {
+          float* p = a.C + row * a.ldc + col;
+          const float vv = acc[0][mb][nb][x];
+          *p = a.accumulate ? *p + vv : vv;
+        }
+      }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -752,7 +846,7 @@ struct Launch {
     if (st_ != KD_OK) return st_;     \
   } while (0)
 
-template <typename T>
+template <typename T, class G>
 kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved, void* ws,
                     hipStream_t stream, kd_trace* trace) {
   Launch L{stream, trace};
@@ -780,10 +874,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
-      case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED><<<fgrid, kThreads, 0, stream>>>(fa); break;
-      case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE><<<fgrid, kThreads, 0, stream>>>(fa); break;
-      case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK><<<fgrid, kThreads, 0, stream>>>(fa); break;
-      default: fwd_tiles_kernel<T, MODE_LOGITS><<<fgrid, kThreads, 0, stream>>>(fa); break;
+      case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+      case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+      case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+      default: fwd_tiles_kernel<T, MODE_LOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
     }
   }));
 
@@ -802,7 +896,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   return KD_OK;
 }
 
-template <typename T>
+template <typename T, class G>
 kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const float* grad,
                      float* dh, float* dw, int accumulate, void* ws, hipStream_t stream,
                      kd_trace* trace) {
@@ -813,16 +907,16 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
   for (int c = 0; c < p.n_chunks; ++c) {
     const int64_t c0 = (int64_t)c * p.chunk;
     const int64_t cw = (p.v - c0 < p.chunk) ? (p.v - c0) : p.chunk;  // valid columns
-    const int n_vt = (int)((cw + kTile - 1) / kTile);
+    const int n_vt = (int)((cw + G::kVT - 1) / G::kVT);  // fused tiles of the chunk
     BwdArgs ba{x.hs, x.w, x.ht, x.wt, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
                static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T, p.need_zT,
-               c0, n_vt, p.n_ttiles, dz, ldz};
+               c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
       switch (p.mode) {
-        case MODE_TIED: bwd_dz_kernel<T, MODE_TIED><<<grid, kThreads, 0, stream>>>(ba); break;
-        case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE><<<grid, kThreads, 0, stream>>>(ba); break;
-        default: bwd_dz_kernel<T, MODE_TOPK><<<grid, kThreads, 0, stream>>>(ba); break;
+        case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        default: bwd_dz_kernel<T, MODE_TOPK, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
       }
     }));
     if (p.mode == MODE_TOPK) {
@@ -833,7 +927,55 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         scatter_kernel<T><<<dim3((unsigned)((ne + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(sa);
       }));
     }
-    const int64_t cpad = (int64_t)n_vt * kTile;  // columns written by bwd_dz
+    const int64_t cpad = (int64_t)n_vt * G::kVT;  // columns written by bwd_dz
+    const int n_gemm_mt = (int)((cw + kTile - 1) / kTile);
+    if constexpr (G::kPipe) {
+      if (dw) {
+        // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]: A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n],
+        // both row-contiguous; the slab's zero rows past n pad K to a multiple of 32.
+        GemmPipeArgs<false, false, 256> ga;
+        ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
+        ga.B = PipeOperandMN{static_cast<const T*>(x.hs), p.d, p.d, p.n};
+        ga.C = dw + c0 * p.d;
+        ga.ldc = p.d;
+        ga.M = cw;
+        ga.N = p.d;
+        ga.K = p.dz_rows;
+        ga.accumulate = accumulate;
+        ga.n_mt = (int)((cw + 255) / 256);
+        ga.n_nt = (int)((p.d + 255) / 256);
+        KD_TRY(L.run(KD_KERNEL_GEMM_DW, [&] {
+          gemm_pipe_kernel<false, false, 256>
+              <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), 512, 0, stream>>>(ga);
+        }));
+      }
+      if (dh) {
+        // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]: A(i, m) = dz[i * ldz + m] (K-contiguous),
+        // B(n, m) = W[(c0 + m) * d + n] (row-contiguous); slab columns past cw are zero.
+        const int mt = (int)((p.n + 255) / 256);
+        const bool wide = (int64_t)mt * ((p.d + 255) / 256) >= 256;
+        auto launch = [&](auto bn_tag) {
+          constexpr int BN = decltype(bn_tag)::value;
+          GemmPipeArgs<true, false, BN> gb;
+          gb.A = PipeOperand{dz, ldz, p.n};
+          gb.B = PipeOperandMN{static_cast<const T*>(x.w) + c0 * p.d, p.d, p.d, cw};
+          gb.C = dh;
+          gb.ldc = p.d;
+          gb.M = p.n;
+          gb.N = p.d;
+          gb.K = cpad;
+          gb.accumulate = (accumulate || c > 0) ? 1 : 0;
+          gb.n_mt = mt;
+          gb.n_nt = (int)((p.d + BN - 1) / BN);
+          return L.run(KD_KERNEL_GEMM_DH, [&] {
+            gemm_pipe_kernel<true, false, BN>
+                <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), 512, 0, stream>>>(gb);
+          });
+        };
+        KD_TRY(wide ? launch(std::integral_constant<int, 256>{})
+                    : launch(std::integral_constant<int, 128>{}));
+      }
+    } else {
     if (dw) {
       // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]; A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n]
       GemmArgs<T, false, false> ga;
@@ -845,7 +987,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       ga.N = p.d;
       ga.K = p.n;
       ga.accumulate = accumulate;
-      ga.n_mt = n_vt;
+      ga.n_mt = n_gemm_mt;
       ga.n_nt = (int)((p.d + kTile - 1) / kTile);
       KD_TRY(L.run(KD_KERNEL_GEMM_DW, [&] {
         gemm_kernel<T, false, false>
@@ -870,26 +1012,36 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
             <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), kThreads, 0, stream>>>(gb);
       }));
     }
+    }
   }
   return KD_OK;
 }
 
 }  // namespace
 
+int pipe_vocab_rows() { return GeoFused::kVT; }
+
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
                       void* workspace, hipStream_t stream, kd_trace* trace) {
-  if (p.dtype == KD_BF16) return forward_t<bf16_t>(p, x, out, saved, workspace, stream, trace);
-  return forward_t<float>(p, x, out, saved, workspace, stream, trace);
+  if (p.dtype == KD_BF16) {
+    if (p.pipe) return forward_t<bf16_t, GeoFused>(p, x, out, saved, workspace, stream, trace);
+    return forward_t<bf16_t, GeoStaged>(p, x, out, saved, workspace, stream, trace);
+  }
+  return forward_t<float, GeoStaged>(p, x, out, saved, workspace, stream, trace);
 }
 
 kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
                        float* d_hidden, float* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace) {
-  if (p.dtype == KD_BF16)
-    return backward_t<bf16_t>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace,
-                              stream, trace);
-  return backward_t<float>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace,
-                           stream, trace);
+  if (p.dtype == KD_BF16) {
+    if (p.pipe)
+      return backward_t<bf16_t, GeoFused>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate,
+                                         workspace, stream, trace);
+    return backward_t<bf16_t, GeoStaged>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate,
+                                         workspace, stream, trace);
+  }
+  return backward_t<float, GeoStaged>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate,
+                                      workspace, stream, trace);
 }
 
 }  // namespace kd
