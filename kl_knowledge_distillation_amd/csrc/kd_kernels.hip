@@ -161,8 +161,8 @@ struct GeoStaged {
   static constexpr int kThreads = 256, kVT = 128, kTT = 128, kWM = 2;
   template <int NB> static constexpr int lds_bytes() { return 2 * (1 + NB) * kTileBytes; }
 };
-// Pipelined: VT vocabulary rows x 128 tokens, WM x 2 waves, S stages of direct
-// global -> LDS copies; bf16 with hidden sizes that are multiples of 32.
+// Pipelined: VT vocabulary rows x 128 tokens, WM x 2 waves (two ping-pong groups),
+// S slots of direct global -> LDS copies; bf16 with hidden sizes multiple of 32.
 template <int VT, int WM, int S>
 struct GeoPipe {
   static constexpr bool kPipe = true;
@@ -170,16 +170,7 @@ struct GeoPipe {
   template <int NB> using Cfg = PipeCfg<VT, 128, NB, WM, S>;
   template <int NB> static constexpr int lds_bytes() { return Cfg<NB>::kLdsBytes; }
 };
-#ifndef KD_PIPE_GEO
-#define KD_PIPE_GEO 0
-#endif
-#if KD_PIPE_GEO == 1
-using GeoFused = GeoPipe<128, 2, 3>;
-#elif KD_PIPE_GEO == 2
-using GeoFused = GeoPipe<256, 4, 3>;
-#else
 using GeoFused = GeoPipe<256, 4, 4>;
-#endif
 
 // acc[g] = A[a_row0 : +VT, 0:K] * B_g[b_row0 : +TT, 0:K]^T for K-contiguous operands.
 template <typename T, class G, int NB>

@@ -84,8 +84,7 @@ struct PipeCfg {
 // Issue the copies of one R-row operand tile for K step k0 into `dst`.
 template <int R, int NWAVES>
 __device__ __forceinline__ void pipe_copy(const PipeOperand& op, int64_t row0, int64_t k0,
-                                          uint8_t* dst, int tid) {
-  const int lane = tid & 63, w = tid >> 6;
+                                          uint8_t* dst, int lane, int w) {
   constexpr int kPerWave = R / (16 * NWAVES);
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
@@ -123,9 +122,8 @@ __device__ __forceinline__ int mn_offset(int k, int m) {
 
 template <int R, int NWAVES>
 __device__ __forceinline__ void pipe_copy_mn(const PipeOperandMN& op, int64_t row0, int64_t k0,
-                                             uint8_t* dst, int tid) {
+                                             uint8_t* dst, int lane, int w) {
   static_assert(R >= 128 && R % 128 == 0, "row-contiguous tiles are 128 or 256 wide");
-  const int lane = tid & 63, w = tid >> 6;
   constexpr int kCpr = R / 8;               // 16-byte chunks per k-row
   constexpr int kRowsPerInst = 64 / kCpr;   // k-rows per copy instruction
   constexpr int kPerWave = R / (16 * NWAVES);
@@ -146,18 +144,27 @@ __device__ __forceinline__ void pipe_copy_mn(const PipeOperandMN& op, int64_t ro
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// ds_read_b64_tr_b16 through inline asm: issued this way the compiler does not
+// add a wait for every in-flight LDS copy in front of it (it cannot tell the
+// intrinsic form apart from the slots those copies fill). Its results are only
+// ready after an lgkmcnt wait, which the main loop issues explicitly before the
+// fragments are used.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
+  uint2 v;
+  const uint32_t addr = (uint32_t)(uintptr_t)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+  return v;
+}
+
 // Fragment of rows [m0, m0 + 32) at k16 step kk from a row-contiguous tile.
 template <int R>
 __device__ __forceinline__ bf16x8 mn_frag(const uint8_t* tile, int m0, int kk, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int m = m0 + 16 * (g & 1) + 4 * (i & 3);
   const int kb = 16 * kk + 8 * (g >> 1) + (i >> 2);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(tile + mn_offset<R>(kb, m)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(tile + mn_offset<R>(kb + 4, m)));
-  const short __attribute__((ext_vector_type(8))) v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  return __builtin_bit_cast(bf16x8, v);
+  const uint2 lo = lds_read_tr16(tile + mn_offset<R>(kb, m));
+  const uint2 hi = lds_read_tr16(tile + mn_offset<R>(kb + 4, m));
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 // K-contiguous fragment of rows [row0, row0 + 32) at k16 step kk.
@@ -167,34 +174,41 @@ __device__ __forceinline__ bf16x8 kc_frag(const uint8_t* tile, int row0, int kk,
   return *reinterpret_cast<const bf16x8*>(tile + row * 64 + ((c ^ pipe_swz(row)) << 4));
 }
 
-template <class C, int NB, class OA, class OB>
-__device__ __forceinline__ void pipe_issue(const OA& A, const OB* B, int64_t a_row0, int64_t b_row0,
-                                           int64_t k0, uint8_t* stage, int tid) {
-  if constexpr (C::kAKC) pipe_copy<C::kABytes / 64, C::kWaves>(A, a_row0, k0, stage, tid);
-  else pipe_copy_mn<C::kABytes / 64, C::kWaves>(A, a_row0, k0, stage, tid);
+// The A-group (waves 0..3) copies the A tile, the B-group (waves 4..7) the B tiles.
+template <class C, class OA>
+__device__ __forceinline__ void pipe_issue_a(const OA& A, int64_t a_row0, int64_t k0, uint8_t* stage,
+                                             int lane, int gw) {
+  if constexpr (C::kAKC) pipe_copy<C::kABytes / 64, 4>(A, a_row0, k0, stage, lane, gw);
+  else pipe_copy_mn<C::kABytes / 64, 4>(A, a_row0, k0, stage, lane, gw);
+}
+template <class C, int NB, class OB>
+__device__ __forceinline__ void pipe_issue_b(const OB* B, int64_t b_row0, int64_t k0, uint8_t* stage,
+                                             int lane, int gw) {
 #pragma unroll
   for (int g = 0; g < NB; ++g) {
     uint8_t* dst = stage + C::kABytes + g * C::kBBytes;
-    if constexpr (C::kBKC) pipe_copy<C::kBBytes / 64, C::kWaves>(B[g], b_row0, k0, dst, tid);
-    else pipe_copy_mn<C::kBBytes / 64, C::kWaves>(B[g], b_row0, k0, dst, tid);
+    if constexpr (C::kBKC) pipe_copy<C::kBBytes / 64, 4>(B[g], b_row0, k0, dst, lane, gw);
+    else pipe_copy_mn<C::kBBytes / 64, 4>(B[g], b_row0, k0, dst, lane, gw);
   }
 }
 
-// One K step of MFMAs. All fragments of the step (both 16-wide halves) are
-// read first into distinct registers, then the MFMAs run; the scheduling
-// barriers keep the compiler from interleaving reads into registers that
-// in-flight MFMAs still read, which would expose the LDS latency per half-step.
+// Fragments of one K step (both 16-wide halves) for this wave's sub-tile.
 template <class C, int NB>
-__device__ __forceinline__ void pipe_mma(const uint8_t* stage, f32x16 (&acc)[NB][C::MBLK][C::NBLK],
-                                         int wm, int wn, int lane) {
-  bf16x8 a[2][C::MBLK], b[2][NB][C::NBLK];
+struct PipeFrags {
+  bf16x8 a[2][C::MBLK];
+  bf16x8 b[2][NB][C::NBLK];
+};
+
+template <class C, int NB>
+__device__ __forceinline__ void pipe_read(const uint8_t* stage, PipeFrags<C, NB>& f, int wm, int wn,
+                                          int lane) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < C::MBLK; ++mb) {
       const int row0 = wm * C::TM + mb * 32;
-      if constexpr (C::kAKC) a[kk][mb] = kc_frag(stage, row0, kk, lane);
-      else a[kk][mb] = mn_frag<C::kABytes / 64>(stage, row0, kk, lane);
+      if constexpr (C::kAKC) f.a[kk][mb] = kc_frag(stage, row0, kk, lane);
+      else f.a[kk][mb] = mn_frag<C::kABytes / 64>(stage, row0, kk, lane);
     }
 #pragma unroll
     for (int g = 0; g < NB; ++g)
@@ -202,10 +216,14 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* stage, f32x16 (&acc)[NB]
       for (int nb = 0; nb < C::NBLK; ++nb) {
         const uint8_t* tile = stage + C::kABytes + g * C::kBBytes;
         const int row0 = wn * C::TN + nb * 32;
-        if constexpr (C::kBKC) b[kk][g][nb] = kc_frag(tile, row0, kk, lane);
-        else b[kk][g][nb] = mn_frag<C::kBBytes / 64>(tile, row0, kk, lane);
+        if constexpr (C::kBKC) f.b[kk][g][nb] = kc_frag(tile, row0, kk, lane);
+        else f.b[kk][g][nb] = mn_frag<C::kBBytes / 64>(tile, row0, kk, lane);
       }
   }
+}
+
+template <class C, int NB>
+__device__ __forceinline__ void pipe_mma(const PipeFrags<C, NB>& f, f32x16 (&acc)[NB][C::MBLK][C::NBLK]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -214,12 +232,8 @@ __device__ __forceinline__ void pipe_mma(const uint8_t* stage, f32x16 (&acc)[NB]
       for (int mb = 0; mb < C::MBLK; ++mb)
 #pragma unroll
         for (int nb = 0; nb < C::NBLK; ++nb)
-          acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][mb], b[kk][g][nb],
+          acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][mb], f.b[kk][g][nb],
                                                                    acc[g][mb][nb], 0, 0, 0);
-  constexpr int kReads = 2 * ((C::kAKC ? 1 : 2) * C::MBLK + (C::kBKC ? 1 : 2) * NB * C::NBLK);
-  constexpr int kMfma = 2 * NB * C::MBLK * C::NBLK;
-  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // DS reads
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);   // then MFMAs
 }
 
 // Wait until at most `n` copy instructions of this thread are still in flight.
@@ -232,13 +246,39 @@ __device__ __forceinline__ void wait_stages(int n) {
 }
 
 // acc[g] = A[a_row0 : +BM, 0:K] * B[g][b_row0 : +BN, 0:K]^T, K a multiple of 32.
-// Ends with a barrier, so the caller may reuse `lds` right after.
+//
+// Ping-pong schedule. Waves 0..3 (group A, one per SIMD) and waves 4..7
+// (group B) run half an iteration apart, with two barriers per K step:
+//
+//   part 1:  A: MFMAs of step i           B: read fragments of step i,
+//                                            copy B tiles of step i+S-1
+//   barrier 1 (step i+1 visible: every wave first waits for its own copies)
+//   part 2:  A: read fragments of step i+1 B: MFMAs of step i
+//               copy A tile of step i+S-1
+//   barrier 2
+//
+// While one group's wave issues MFMAs, the other group's wave on the same SIMD
+// does its LDS reads and copies, so the matrix pipe does not drain at the
+// barriers. Slot reuse: step i+S-1 goes into the slot of step i-1, whose reads
+// finished before barrier 1 of step i-1 (group B waits for its reads before
+// that barrier; group A's were consumed by its MFMAs of step i-1).
+// Ends with a full barrier, so the caller may reuse `lds` right after.
 template <class C, int NB, class OA, class OB>
 __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t a_row0, int64_t b_row0,
                                               int64_t K, uint8_t* lds,
                                               f32x16 (&acc)[NB][C::MBLK][C::NBLK], int tid) {
   constexpr int S = C::kStages;
-  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  static_assert(S >= 3, "the ping-pong schedule needs at least 3 slots");
+  static_assert(C::kWaves == 8, "two groups of four waves");
+  constexpr int kCopiesA = C::kABytes / 1024 / 4;        // per A-group wave per step
+  constexpr int kCopiesB = NB * C::kBBytes / 1024 / 4;   // per B-group wave per step
+  // The wave index is the same for all lanes of a wave; readfirstlane makes that
+  // visible to the compiler, so the group branches below are scalar branches.
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const bool grp_b = w >= 4;
+  const int gw = w & 3;
 #pragma unroll
   for (int g = 0; g < NB; ++g)
 #pragma unroll
@@ -249,23 +289,63 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
         for (int x = 0; x < 16; ++x) acc[g][mb][nb][x] = 0.f;
 
   const int nk = (int)(K / kPipeBK);
+  // Prologue: steps 0 .. S-2, each group its own operand.
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
-    if (st < nk) pipe_issue<C, NB, OA, OB>(A, B, a_row0, b_row0, (int64_t)st * kPipeBK, lds + st * C::kStageBytes, tid);
-  int cur = 0;  // buffer of stage kt
-  for (int kt = 0; kt < nk; ++kt) {
-    // stages kt+1 .. min(kt+S-2, nk-1) may stay in flight
-    const int later = min(S - 2, nk - 1 - kt);
-    wait_stages<C::kCopies, S - 2>(later);
-    pipe_barrier();
-    if (kt + S - 1 < nk) {
-      int nxt = cur + S - 1;
-      nxt = nxt >= S ? nxt - S : nxt;
-      pipe_issue<C, NB, OA, OB>(A, B, a_row0, b_row0, (int64_t)(kt + S - 1) * kPipeBK,
-                        lds + nxt * C::kStageBytes, tid);
+    if (st < nk) {
+      uint8_t* slot = lds + st * C::kStageBytes;
+      if (grp_b) pipe_issue_b<C, NB, OB>(B, b_row0, (int64_t)st * kPipeBK, slot, lane, gw);
+      else pipe_issue_a<C, OA>(A, a_row0, (int64_t)st * kPipeBK, slot, lane, gw);
     }
-    pipe_mma<C, NB>(lds + cur * C::kStageBytes, acc, wm, wn, lane);
-    cur = (cur + 1 == S) ? 0 : cur + 1;
+  // Step 0 visible: at most steps 1 .. min(S-2, nk-1) still in flight.
+  {
+    const int later = min(S - 2, nk - 1);
+    if (grp_b) wait_stages<kCopiesB, S - 2>(later);
+    else wait_stages<kCopiesA, S - 2>(later);
+  }
+  pipe_barrier();
+  PipeFrags<C, NB> f;
+  if (!grp_b) {
+    // Group A: MFMAs in part 1, reads and A-tile copies in part 2.
+    pipe_read<C, NB>(lds, f, wm, wn, lane);
+    int cur = 0;  // slot of step i
+    for (int i = 0; i < nk; ++i) {
+      const int nxt = (cur + 1 == S) ? 0 : cur + 1;     // slot of step i+1
+      const int fill = (cur == 0) ? S - 1 : cur - 1;    // slot of step i+S-1
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments of step i ready
+      __builtin_amdgcn_s_setprio(1);
+      pipe_mma<C, NB>(f, acc);
+      __builtin_amdgcn_s_setprio(0);
+      // step i+1 must have landed; steps i+2 .. i+S-2 may stay in flight
+      wait_stages<kCopiesA, S - 2>(max(0, min(S - 3, nk - 2 - i)));
+      pipe_barrier();
+      if (i + 1 < nk) pipe_read<C, NB>(lds + nxt * C::kStageBytes, f, wm, wn, lane);
+      if (i + S - 1 < nk)
+        pipe_issue_a<C, OA>(A, a_row0, (int64_t)(i + S - 1) * kPipeBK, lds + fill * C::kStageBytes,
+                            lane, gw);
+      pipe_barrier();
+      cur = nxt;
+    }
+  } else {
+    // Group B: reads and B-tile copies in part 1, MFMAs in part 2.
+    int cur = 0;
+    for (int i = 0; i < nk; ++i) {
+      const int nxt = (cur + 1 == S) ? 0 : cur + 1;
+      const int fill = (cur == 0) ? S - 1 : cur - 1;
+      pipe_read<C, NB>(lds + cur * C::kStageBytes, f, wm, wn, lane);
+      if (i + S - 1 < nk)
+        pipe_issue_b<C, NB, OB>(B, b_row0, (int64_t)(i + S - 1) * kPipeBK, lds + fill * C::kStageBytes,
+                                lane, gw);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of slot `cur` done
+      // step i+1 must have landed; steps i+2 .. i+S-1 may stay in flight
+      wait_stages<kCopiesB, S - 2>(max(0, min(S - 2, nk - 2 - i)));
+      pipe_barrier();
+      __builtin_amdgcn_s_setprio(1);
+      pipe_mma<C, NB>(f, acc);
+      __builtin_amdgcn_s_setprio(0);
+      pipe_barrier();
+      cur = nxt;
+    }
   }
   __syncthreads();
 }
