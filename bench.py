@@ -139,6 +139,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="quickstart_tied_bf16")
     ap.add_argument("--vocab-chunk", type=int, default=0)
+    ap.add_argument("--n", type=int, default=0, help="override the token count")
+    ap.add_argument("--d", type=int, default=0, help="override the student hidden size")
+    ap.add_argument("--v", type=int, default=0, help="override the vocabulary size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="copy a buffer of this many MiB once before the timed steps, so a "
@@ -158,6 +161,9 @@ def main() -> int:
     from kl_knowledge_distillation_amd.inputs import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    over = {k: getattr(args, k) for k in ("n", "d", "v") if getattr(args, k)}
+    if over:
+        w = w.scaled(name=w.name + "_" + "_".join(f"{k}{v}" for k, v in over.items()), **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = make_inputs(w, dev, seed=0)

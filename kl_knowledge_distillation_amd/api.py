@@ -106,7 +106,7 @@ class Runner:
                  teacher_kind="tied", teacher_hidden=None, teacher_weight=None, topk_idx=None,
                  topk_prob=None, student_ce_weight=1.0, teacher_ce_weight=0.0, kl_weight=0.0,
                  temperature=1.0, ignore_index=-100, reduction="mean", normalizer=0.0,
-                 vocab_chunk=0, want_grads=True):
+                 vocab_chunk=0, want_grads=True, want_teacher_ce=None):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -169,8 +169,13 @@ class Runner:
         self.student_ce = torch.empty(self.n, **f32)
         self.teacher_ce = torch.empty(self.n, **f32)
         self.kl = torch.empty(self.n, **f32)
+        if want_teacher_ce is None:
+            want_teacher_ce = teacher_ce_weight > 0
+        self.teacher_ce.zero_()
+        # The teacher CE is computed only when it is weighted or asked for.
         self.out = L.KdOutputs(self.loss.data_ptr(), self.student_ce.data_ptr(),
-                               self.teacher_ce.data_ptr(), self.kl.data_ptr())
+                               self.teacher_ce.data_ptr() if want_teacher_ce else None,
+                               self.kl.data_ptr())
         self.saved = torch.empty(self.lib.kd_saved_bytes(self.n), dtype=torch.uint8,
                                  device=self.device)
         self.ws_fwd = self._workspace(0)
@@ -291,11 +296,15 @@ _KL_SUPPORTED = ("forward",)
 def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
                       teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
                       kl_divergence="forward", ignore_index=-100, reduction="mean",
-                      num_batch_labels=None, vocab_chunk=0) -> DistillationLossOutput:
+                      num_batch_labels=None, vocab_chunk=0,
+                      return_teacher_ce=True) -> DistillationLossOutput:
     """Fused LM-head + CE + KL loss; differentiable in student_hidden and weight.
 
     The teacher is always detached. Returns the loss and the unweighted per-token
-    components (student_ce, teacher_ce, kl with T^2 included).
+    components (student_ce, teacher_ce, kl with T^2 included). With
+    return_teacher_ce=False and teacher_ce_weight=0 the teacher CE is skipped
+    (one exponential pass fewer per tile when the temperature is not 1) and
+    reported as zeros.
     """
     if kl_divergence not in _KL_SUPPORTED:
         raise NotImplementedError(f"kl_divergence={kl_divergence!r}; available: {_KL_SUPPORTED}")
@@ -303,7 +312,8 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
               weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
               teacher_ce_weight=teacher_ce_weight, kl_weight=kl_weight,
               temperature=kl_temperature, ignore_index=ignore_index, reduction=reduction,
-              normalizer=float(num_batch_labels or 0), vocab_chunk=vocab_chunk)
+              normalizer=float(num_batch_labels or 0), vocab_chunk=vocab_chunk,
+              want_teacher_ce=bool(return_teacher_ce or teacher_ce_weight > 0))
     if isinstance(teacher, TiedTeacher):
         kw.update(teacher_kind="tied", teacher_hidden=teacher.hidden.detach().contiguous())
     elif isinstance(teacher, (SeparateTeacher, PrecomputedTeacher)):

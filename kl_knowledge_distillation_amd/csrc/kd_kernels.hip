@@ -860,8 +860,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
     }
   }));
 
+  // Teacher statistics at T = 1 only feed the teacher CE.
+  const int need_t1 = (p.need_t1 && pa.want_teacher) ? 1 : 0;
   FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, p.n, p.d, p.dt, p.v,
-             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, p.need_zT, p.need_t1, rec};
+             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, p.need_zT, need_t1, rec};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
@@ -872,7 +874,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
     }
   }));
 
-  MergeArgs ma{rec, prep, p.n_slices, p.n, p.mode, p.T, p.need_zT, p.need_t1,
+  MergeArgs ma{rec, prep, p.n_slices, p.n, p.mode, p.T, p.need_zT, need_t1,
                (p.mode != MODE_TOPK) ? 1 : 0, p.ws, p.wt, p.wkl,
                out ? out->student_ce : nullptr, out ? out->teacher_ce : nullptr,
                out ? out->kl : nullptr, static_cast<float*>(saved), part};

@@ -141,3 +141,22 @@ def test_full_quickstart_tied_bf16():
 def test_full_tiny_fp32_default_and_chunked():
     full_parity(C1)
     full_parity(C1, vocab_chunk=256)
+
+
+@pytest.mark.parametrize("want", [True, False])
+def test_teacher_ce_on_request_at_temperature_2(want):
+    """Teacher CE weight 0 at T = 2: the per-token teacher CE (taken at T = 1) is
+    computed when asked for and left at zero otherwise; the loss is the same."""
+    w = C2.scaled(n=260, d=256, v=2100)
+    x = make_inputs(w, "cuda", seed=8)
+    r = make_runner(w, x, want_teacher_ce=want)
+    r.forward()
+    torch.cuda.synchronize()
+    s, t, labels = oracle_problem(w, x)
+    ref = O.forward(s, t, params_of(w), labels)
+    assert_scalar(float(r.loss), ref["loss"], "bf16", "loss")
+    assert_tokens(to_np(r.kl), ref["kl"], "bf16", "kl")
+    if want:
+        assert_tokens(to_np(r.teacher_ce), ref["teacher_ce"], "bf16", "teacher_ce")
+    else:
+        assert torch.count_nonzero(r.teacher_ce).item() == 0
