@@ -16,7 +16,6 @@ using kd::Plan;
 constexpr int64_t kTile = 128;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kDefaultChunk = 8192;
-constexpr int64_t kTargetFwdBlocks = 4096;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -109,25 +108,20 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.need_t1 = (q.T != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
   q.has_labels = labels ? 1 : 0;
 
-  // Tile geometry: bf16 with every contraction length a multiple of 32 runs the
+  // Tile geometry: bf16 with every contraction length a multiple of 64 runs the
   // pipelined 256-row tiles; everything else the register-staged 128-row tiles.
-  const bool d_ok = q.mode == kd::MODE_LOGITS || q.d % 32 == 0;
-  const bool dt_ok = (q.mode != kd::MODE_SEPARATE && q.mode != kd::MODE_LOGITS) || q.dt % 32 == 0;
+  const bool d_ok = q.mode == kd::MODE_LOGITS || q.d % kd::kPipeK == 0;
+  const bool dt_ok = (q.mode != kd::MODE_SEPARATE && q.mode != kd::MODE_LOGITS) || q.dt % kd::kPipeK == 0;
   q.pipe = (q.dtype == KD_BF16 && d_ok && dt_ok) ? 1 : 0;
   q.vt_rows = q.pipe ? kd::pipe_vocab_rows() : 128;
   const int64_t vt = q.vt_rows;
-  // Forward grid: (vocabulary slice) x (128-token tile).
+  // Forward grid: (vocabulary tile) x (128-token tile), one tile per workgroup,
+  // so the per-token statistics are only live after the main loop; each
+  // vocabulary tile leaves one record per token for the merge.
   q.n_ttiles = (int)ceil_div(q.n, kTile);
   q.n_vtiles = (int)ceil_div(q.v, vt);
-  int64_t tps;
-  if (p->vocab_chunk > 0) {
-    tps = ceil_div(p->vocab_chunk, vt);
-  } else {
-    tps = ((int64_t)q.n_vtiles * q.n_ttiles) / kTargetFwdBlocks;
-  }
-  tps = std::max<int64_t>(1, std::min<int64_t>(tps, q.n_vtiles));
-  q.tps = (int)tps;
-  q.n_slices = (int)ceil_div(q.n_vtiles, tps);
+  q.tps = 1;
+  q.n_slices = q.n_vtiles;
   // Backward chunk: a whole number of fused vocabulary tiles.
   int64_t chunk = (p->vocab_chunk > 0) ? ceil_div(p->vocab_chunk, vt) * vt : kDefaultChunk;
   chunk = std::min<int64_t>(chunk, ceil_div(q.v, vt) * vt);

@@ -1,10 +1,11 @@
 // Device building blocks for gfx950 (CDNA4): element types, LDS operand
-// staging, and the double-buffered MFMA main loop shared by every tile kernel.
+// staging, and the double-buffered MFMA main loop of the register-staged path
+// (fp32, and bf16 hidden sizes that are not a multiple of 64).
 //
 // Tile shape. A workgroup has 256 threads = 4 wave64s arranged 2 x 2 and
 // computes a 128 x 128 output tile; each wave owns a 64 x 64 sub-tile made of
-// 2 x 2 blocks of the 32x32 MFMA (v_mfma_f32_32x32x16_bf16 for bf16,
-// v_mfma_f32_32x32x2_f32 for fp32). One K step moves 64 bytes of every
+// 4 x 4 blocks of the 16x16 MFMA (v_mfma_f32_16x16x32_bf16 for bf16,
+// v_mfma_f32_16x16x4_f32 for fp32). One K step moves 64 bytes of every
 // operand row: 32 bf16 or 16 fp32 elements.
 //
 // LDS layout. Each staged operand tile is 128 rows x 80 bytes: the 64 data
@@ -12,10 +13,11 @@
 // fragment reads of 16 consecutive rows land in distinct bank groups. Two
 // stages are kept (double buffering); one barrier per K step.
 //
-// Output layout of the 32x32 MFMA (same for both element types): lane l holds
-// column j = l % 32 and rows i = 8*(r/4) + 4*(l/32) + r%4 of the block, r in
-// [0, 16). The tile kernels put vocabulary on the row axis, so the
-// per-token reductions of the epilogue run over a lane's own registers.
+// Output layout of the 16x16 MFMA (both element types, and the pipelined bf16
+// path): lane l holds column l % 16 and rows 4 (l / 16) + r, r in [0, 4), of
+// its block. The tile kernels put vocabulary on the row axis, so the per-token
+// reductions of the epilogue run over a lane's own registers and then over the
+// four lanes l % 16 + 16 q.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -180,64 +182,54 @@ struct Stager {
 };
 
 // One K step of MFMAs: acc[g] += A_tile * B_tile[g]^T for every B operand g.
-// The A fragments are read once and shared by all B operands.
+// Lane l reads 16-byte chunk l / 16 of rows l % 16 of each 16-row block. For
+// bf16 that is the 8 k values of one 16x16x32 MFMA; for fp32 the 4 k values
+// feed 4 MFMAs of 16x16x4, MFMA e taking element e (k = 4 (l / 16) + e), the
+// same order for both operands, so the sum over k is unchanged.
 template <typename T, int NB>
 __device__ __forceinline__ void mma_step(const uint8_t* ldsA, const uint8_t* ldsB0,
-                                         f32x16 (&acc)[NB][2][2], int wm, int wn, int lane) {
-  const int r = lane & 31, h = lane >> 5;
+                                         f32x4 (&acc)[NB][4][4], int wm, int wn, int lane) {
+  const int r = lane & 15, cb = (lane >> 4) * 16;
   if constexpr (sizeof(T) == 2) {
+    bf16x8 a[4], b[NB][4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int cb = (2 * kk + h) * 16;
-      bf16x8 a[2], b[NB][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        a[mb] = *reinterpret_cast<const bf16x8*>(ldsA + (wm * 64 + mb * 32 + r) * kRowBytes + cb);
-#pragma unroll
-      for (int g = 0; g < NB; ++g)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          b[g][nb] = *reinterpret_cast<const bf16x8*>(ldsB0 + g * kTileBytes +
-                                                      (wn * 64 + nb * 32 + r) * kRowBytes + cb);
-#pragma unroll
-      for (int g = 0; g < NB; ++g)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            acc[g][mb][nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[g][nb], acc[g][mb][nb], 0, 0, 0);
-    }
-  } else {
-    // fp32: lane half h takes elements [8h, 8h+8) of the 16-element K step for
-    // both operands, one per v_mfma_f32_32x32x2_f32; the sum over k is the same.
-    f32x4 a[2][2], b[NB][2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        a[mb][c] = *reinterpret_cast<const f32x4*>(ldsA + (wm * 64 + mb * 32 + r) * kRowBytes +
-                                                   (2 * h + c) * 16);
+    for (int mb = 0; mb < 4; ++mb)
+      a[mb] = *reinterpret_cast<const bf16x8*>(ldsA + (wm * 64 + mb * 16 + r) * kRowBytes + cb);
 #pragma unroll
     for (int g = 0; g < NB; ++g)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
+        b[g][nb] = *reinterpret_cast<const bf16x8*>(ldsB0 + g * kTileBytes +
+                                                    (wn * 64 + nb * 16 + r) * kRowBytes + cb);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          b[g][nb][c] = *reinterpret_cast<const f32x4*>(
-              ldsB0 + g * kTileBytes + (wn * 64 + nb * 32 + r) * kRowBytes + (2 * h + c) * 16);
+    for (int g = 0; g < NB; ++g)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+        for (int nb = 0; nb < 4; ++nb)
+          acc[g][mb][nb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], b[g][nb], acc[g][mb][nb], 0, 0, 0);
+  } else {
+    f32x4 a[4], b[NB][4];
 #pragma unroll
-        for (int g = 0; g < NB; ++g)
+    for (int mb = 0; mb < 4; ++mb)
+      a[mb] = *reinterpret_cast<const f32x4*>(ldsA + (wm * 64 + mb * 16 + r) * kRowBytes + cb);
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+    for (int g = 0; g < NB; ++g)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][c][e], b[g][nb][c][e],
-                                                                   acc[g][mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < 4; ++nb)
+        b[g][nb] = *reinterpret_cast<const f32x4*>(ldsB0 + g * kTileBytes +
+                                                   (wn * 64 + nb * 16 + r) * kRowBytes + cb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mb][e], b[g][nb][e],
+                                                                 acc[g][mb][nb], 0, 0, 0);
   }
 }
 
@@ -247,18 +239,18 @@ __device__ __forceinline__ void mma_step(const uint8_t* ldsA, const uint8_t* lds
 template <typename T, bool AKC, bool BKC, int NB>
 __device__ __forceinline__ void mainloop(const Operand<T, AKC>& A, const Operand<T, BKC>* B,
                                          int64_t a_row0, int64_t b_row0, int64_t K, uint8_t* lds,
-                                         f32x16 (&acc)[NB][2][2], int tid) {
+                                         f32x4 (&acc)[NB][4][4], int tid) {
   constexpr int BK = Elem<T>::kBK;
   constexpr int kStage = (1 + NB) * kTileBytes;
   const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
   for (int g = 0; g < NB; ++g)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[g][mb][nb][x] = 0.f;
+        for (int x = 0; x < 4; ++x) acc[g][mb][nb][x] = 0.f;
 
   const int64_t nk = (K + BK - 1) / BK;
   Stager<T, AKC> sa;
@@ -289,11 +281,15 @@ __device__ __forceinline__ void mainloop(const Operand<T, AKC>& A, const Operand
   }
 }
 
-// Vocabulary row (within the 128-row tile) of accumulator register x of block mb.
-__device__ __forceinline__ int acc_row(int wm, int mb, int x, int lane) {
-  return wm * 64 + mb * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+// Both tile geometries give each wave a 64 x 64 sub-tile of 4 x 4 blocks.
+constexpr int kMB = 4, kNB = 4;
+typedef f32x4 WaveAcc[kMB][kNB];
+
+// Vocabulary row (within the tile) of accumulator register r of block mb.
+__device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
+  return wm * 64 + mb * 16 + 4 * (lane >> 4) + r;
 }
-// Token column (within the 128-column tile) of block nb.
-__device__ __forceinline__ int acc_col(int wn, int nb, int lane) { return wn * 64 + nb * 32 + (lane & 31); }
+// Token column (within the tile) of block nb.
+__device__ __forceinline__ int acc_col(int wn, int nb, int lane) { return wn * 64 + nb * 16 + (lane & 15); }
 
 }  // namespace kd

@@ -59,6 +59,8 @@ struct Tensors {
 
 // Vocabulary rows per tile of the pipelined bf16 geometry compiled in.
 int pipe_vocab_rows();
+// Contraction lengths of the pipelined path are multiples of this (one K step).
+constexpr int kPipeK = 64;
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
                       void* workspace, hipStream_t stream, kd_trace* trace);

@@ -74,73 +74,77 @@ __device__ __forceinline__ void stats_merge(RowStats& s, const RowStats& o) {
   merge_ms(s.mt1, s.st1, o.mt1, o.st1);
 }
 
-__device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int x) { return (ok >> (mb * 16 + x)) & 1u; }
+// Bit 4 mb + r of `ok`: register r of row block mb is a real vocabulary row.
+__device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int r) { return (ok >> (mb * 4 + r)) & 1u; }
 
-// Folds the 32 values a lane holds for token block nb into (m, s) at scale c.
+// Folds the 16 values a lane holds for token block nb into (m, s) at scale c.
 template <bool TAIL>
-__device__ __forceinline__ void online_ms(float& m, float& s, const f32x16 (&x)[2][2], int nb, float c,
+__device__ __forceinline__ void online_ms(float& m, float& s, const WaveAcc& x, int nb, float c,
                                           uint32_t ok) {
   float bm = -INFINITY;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < 4; ++r)
       if (!TAIL || ok_bit(ok, mb, r)) bm = fmaxf(bm, x[mb][nb][r]);
   const float mn = fmaxf(m, bm * c);
   const float sc = rescale(m, mn);
   float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float e0 = exp2_fast(fmaf(x[0][nb][r], c, -mn));
-    float e1 = exp2_fast(fmaf(x[1][nb][r], c, -mn));
-    if (TAIL) {
-      e0 = ok_bit(ok, 0, r) ? e0 : 0.f;
-      e1 = ok_bit(ok, 1, r) ? e1 : 0.f;
+  for (int mb = 0; mb < kMB; mb += 2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mn));
+      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mn));
+      if (TAIL) {
+        e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
+        e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
+      }
+      acc0 += e0;
+      acc1 += e1;
     }
-    acc0 += e0;
-    acc1 += e1;
-  }
   s = s * sc + (acc0 + acc1);
   m = mn;
 }
 
 // Teacher statistics at scale c plus the cross term sum 2^(t c - m) (t - z).
 template <bool TAIL>
-__device__ __forceinline__ void online_msa(float& m, float& s, float& a, const f32x16 (&t)[2][2],
-                                           const f32x16 (&z)[2][2], int nb, float c, uint32_t ok) {
+__device__ __forceinline__ void online_msa(float& m, float& s, float& a, const WaveAcc& t,
+                                           const WaveAcc& z, int nb, float c, uint32_t ok) {
   float bm = -INFINITY;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < 4; ++r)
       if (!TAIL || ok_bit(ok, mb, r)) bm = fmaxf(bm, t[mb][nb][r]);
   const float mn = fmaxf(m, bm * c);
   const float sc = rescale(m, mn);
   float s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float e0 = exp2_fast(fmaf(t[0][nb][r], c, -mn));
-    float e1 = exp2_fast(fmaf(t[1][nb][r], c, -mn));
-    if (TAIL) {
-      e0 = ok_bit(ok, 0, r) ? e0 : 0.f;
-      e1 = ok_bit(ok, 1, r) ? e1 : 0.f;
+  for (int mb = 0; mb < kMB; mb += 2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e0 = exp2_fast(fmaf(t[mb][nb][r], c, -mn));
+      float e1 = exp2_fast(fmaf(t[mb + 1][nb][r], c, -mn));
+      if (TAIL) {
+        e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
+        e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
+      }
+      s0 += e0;
+      s1 += e1;
+      a0 = fmaf(e0, t[mb][nb][r] - z[mb][nb][r], a0);
+      a1 = fmaf(e1, t[mb + 1][nb][r] - z[mb + 1][nb][r], a1);
     }
-    s0 += e0;
-    s1 += e1;
-    a0 = fmaf(e0, t[0][nb][r] - z[0][nb][r], a0);
-    a1 = fmaf(e1, t[1][nb][r] - z[1][nb][r], a1);
-  }
   s = s * sc + (s0 + s1);
   a = a * sc + (a0 + a1);
   m = mn;
 }
 
 template <int MODE, bool TAIL>
-__device__ __forceinline__ void fwd_update(const f32x16 (&z)[2][2], const f32x16 (&t)[2][2],
-                                           RowStats (&st)[2], float cT, bool need_zT, bool need_t1,
-                                           uint32_t ok) {
+__device__ __forceinline__ void fwd_update(const WaveAcc& z, const WaveAcc& t, RowStats (&st)[kNB],
+                                           float cT, bool need_zT, bool need_t1, uint32_t ok) {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     online_ms<TAIL>(st[nb].mz1, st[nb].sz1, z, nb, kLog2e, ok);
     if (MODE == MODE_TOPK) continue;
     if (need_zT) online_ms<TAIL>(st[nb].mzT, st[nb].szT, z, nb, cT, ok);
@@ -148,7 +152,6 @@ __device__ __forceinline__ void fwd_update(const f32x16 (&z)[2][2], const f32x16
     if (need_t1) online_ms<TAIL>(st[nb].mt1, st[nb].st1, t, nb, kLog2e, ok);
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Tile geometry of the fused kernels
@@ -161,23 +164,22 @@ struct GeoStaged {
   static constexpr int kThreads = 256, kVT = 128, kTT = 128, kWM = 2;
   template <int NB> static constexpr int lds_bytes() { return 2 * (1 + NB) * kTileBytes; }
 };
-// Pipelined: VT vocabulary rows x 128 tokens, WM x 2 waves (two ping-pong groups),
-// S slots of direct global -> LDS copies; bf16 with hidden sizes multiple of 32.
-template <int VT, int WM, int S>
+// Pipelined: 256 vocabulary rows x 128 tokens, 8 waves (4 x 2, two ping-pong
+// groups), two slots of buffer-load copies; bf16 with hidden sizes multiple of 64.
 struct GeoPipe {
   static constexpr bool kPipe = true;
-  static constexpr int kThreads = 128 * WM, kVT = VT, kTT = 128, kWM = WM, kStages = S;
-  template <int NB> using Cfg = PipeCfg<VT, 128, NB, WM, S>;
+  static constexpr int kThreads = 512, kVT = 256, kTT = 128, kWM = 4;
+  template <int NB> using Cfg = PipeCfg<256, 128, NB>;
   template <int NB> static constexpr int lds_bytes() { return Cfg<NB>::kLdsBytes; }
 };
-using GeoFused = GeoPipe<256, 4, 4>;
+using GeoFused = GeoPipe;
 
 // acc[g] = A[a_row0 : +VT, 0:K] * B_g[b_row0 : +TT, 0:K]^T for K-contiguous operands.
 template <typename T, class G, int NB>
 __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t arows,
                                              const T* const (&b)[NB], int64_t ldb, int64_t brows,
                                              int64_t a_row0, int64_t b_row0, int64_t K,
-                                             uint8_t* lds, f32x16 (&acc)[NB][2][2], int tid) {
+                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][kNB], int tid) {
   if constexpr (G::kPipe) {
     static_assert(sizeof(T) == 2, "the pipelined geometry is bf16 only");
     const PipeOperand A{a, lda, arows};
@@ -217,121 +219,119 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::template lds_bytes<NB>()];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  int slice, tt;
+  int slice, tt;  // slice = the vocabulary tile of this workgroup
   grouped_tile(t, a.n_slices, a.n_ttiles, 8, slice, tt);
   const int64_t t0 = (int64_t)tt * G::kTT;
-  const int vt_begin = slice * a.tps;
-  const int vt_end = min(a.n_vtiles, vt_begin + a.tps);
-
-  RowStats st[2];
-  stats_init(st[0]);
-  stats_init(st[1]);
+  const int64_t v0 = (int64_t)slice * G::kVT;
 
   const T* hs = static_cast<const T*>(a.hs);
   const T* W = static_cast<const T*>(a.w);
   const T* ht = static_cast<const T*>(a.ht);
   const T* Wt = static_cast<const T*>(a.wt);
 
-  f32x16 acc[NB][2][2];
-  f32x16 tacc[1][2][2];  // teacher accumulator of the separate / logits modes
-  f32x16 zl[2][2];       // student logits loaded in LOGITS mode
+  f32x4 acc[NB][kMB][kNB];
+  f32x4 tacc[1][kMB][kNB];  // teacher accumulator of the separate / logits modes
+  WaveAcc zl;               // student logits loaded in LOGITS mode
 
-  for (int vt = vt_begin; vt < vt_end; ++vt) {
-    const int64_t v0 = (int64_t)vt * G::kVT;
-    if constexpr (MODE == MODE_TIED) {
-      const T* const b[2] = {hs, ht};
-      tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    } else if constexpr (MODE == MODE_SEPARATE) {
-      const T* const b[1] = {hs};
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-      const T* const bt[1] = {ht};
-      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-    } else if constexpr (MODE == MODE_TOPK) {
-      const T* const b[1] = {hs};
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    } else {  // MODE_LOGITS
-      const T* const bt[1] = {ht};
-      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-      const T* L = static_cast<const T*>(a.logits);
+  if constexpr (MODE == MODE_TIED) {
+    const T* const b[2] = {hs, ht};
+    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+  } else if constexpr (MODE == MODE_SEPARATE) {
+    const T* const b[1] = {hs};
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    const T* const bt[1] = {ht};
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
+  } else if constexpr (MODE == MODE_TOPK) {
+    const T* const b[1] = {hs};
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+  } else {  // MODE_LOGITS
+    const T* const bt[1] = {ht};
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
+    const T* L = static_cast<const T*>(a.logits);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int64_t tok = t0 + acc_col(wn, nb, lane);
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int64_t tok = t0 + acc_col(wn, nb, lane);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int64_t vv = v0 + acc_row(wm, mb, x, lane);
-            zl[mb][nb][x] = (tok < a.n && vv < a.v) ? to_f32(L[tok * a.v + vv]) : 0.f;
-          }
-      }
-    }
-
-    uint32_t ok = 0xffffffffu;
-    const bool tail = v0 + G::kVT > a.v;
-    if (tail) {
-      ok = 0u;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int x = 0; x < 16; ++x)
-          if (v0 + acc_row(wm, mb, x, lane) < a.v) ok |= 1u << (mb * 16 + x);
-    }
-    if constexpr (MODE == MODE_TIED) {
-      if (tail) fwd_update<MODE, true>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
-      else fwd_update<MODE, false>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
-    } else if constexpr (MODE == MODE_SEPARATE) {
-      if (tail) fwd_update<MODE, true>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-      else fwd_update<MODE, false>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-    } else if constexpr (MODE == MODE_TOPK) {
-      if (tail) fwd_update<MODE, true>(acc[0], acc[0], st, a.cT, false, false, ok);
-      else fwd_update<MODE, false>(acc[0], acc[0], st, a.cT, false, false, ok);
-    } else {
-      if (tail) fwd_update<MODE, true>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-      else fwd_update<MODE, false>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+        for (int r = 0; r < 4; ++r) {
+          const int64_t vv = v0 + acc_row(wm, mb, r, lane);
+          zl[mb][nb][r] = (tok < a.n && vv < a.v) ? to_f32(L[tok * a.v + vv]) : 0.f;
+        }
     }
   }
 
-  // Combine the two lane halves (same tokens, different vocabulary rows).
+  RowStats st[kNB];  // one per token block nb of this lane
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    RowStats o;
-    o.mz1 = __shfl_xor(st[nb].mz1, 32);
-    o.sz1 = __shfl_xor(st[nb].sz1, 32);
-    o.mzT = __shfl_xor(st[nb].mzT, 32);
-    o.szT = __shfl_xor(st[nb].szT, 32);
-    o.mtT = __shfl_xor(st[nb].mtT, 32);
-    o.stT = __shfl_xor(st[nb].stT, 32);
-    o.a = __shfl_xor(st[nb].a, 32);
-    o.mt1 = __shfl_xor(st[nb].mt1, 32);
-    o.st1 = __shfl_xor(st[nb].st1, 32);
-    stats_merge(st[nb], o);
+  for (int nb = 0; nb < kNB; ++nb) stats_init(st[nb]);
+  uint32_t ok = 0xffffu;
+  const bool tail = v0 + G::kVT > a.v;
+  if (tail) {
+    ok = 0u;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (v0 + acc_row(wm, mb, r, lane) < a.v) ok |= 1u << (mb * 4 + r);
+  }
+  if constexpr (MODE == MODE_TIED) {
+    if (tail) fwd_update<MODE, true>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
+    else fwd_update<MODE, false>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
+  } else if constexpr (MODE == MODE_SEPARATE) {
+    if (tail) fwd_update<MODE, true>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+    else fwd_update<MODE, false>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+  } else if constexpr (MODE == MODE_TOPK) {
+    if (tail) fwd_update<MODE, true>(acc[0], acc[0], st, a.cT, false, false, ok);
+    else fwd_update<MODE, false>(acc[0], acc[0], st, a.cT, false, false, ok);
+  } else {
+    if (tail) fwd_update<MODE, true>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+    else fwd_update<MODE, false>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
+  }
+
+  // Combine the four lanes l % 16 + 16 q (same token, different vocabulary rows).
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+#pragma unroll
+    for (int off = 16; off <= 32; off *= 2) {
+      RowStats o;
+      o.mz1 = __shfl_xor(st[nb].mz1, off);
+      o.sz1 = __shfl_xor(st[nb].sz1, off);
+      o.mzT = __shfl_xor(st[nb].mzT, off);
+      o.szT = __shfl_xor(st[nb].szT, off);
+      o.mtT = __shfl_xor(st[nb].mtT, off);
+      o.stT = __shfl_xor(st[nb].stT, off);
+      o.a = __shfl_xor(st[nb].a, off);
+      o.mt1 = __shfl_xor(st[nb].mt1, off);
+      o.st1 = __shfl_xor(st[nb].st1, off);
+      stats_merge(st[nb], o);
+    }
   }
   // Combine the kWM waves that share a token block (same wn, different vocabulary
   // rows), in the fixed order wm = 1, 2, ... The main loop ended with a barrier,
   // so its LDS is free.
   float* xs = reinterpret_cast<float*>(lds);
-  const int l32 = lane & 31;
-  if (wm > 0 && lane < 32) {
+  const int l16 = lane & 15;
+  if (wm > 0 && lane < 16) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float* p = xs + ((((wm - 1) * 2 + wn) * 2 + nb) * kRecFields) * 32 + l32;
+    for (int nb = 0; nb < kNB; ++nb) {
+      float* p = xs + ((((wm - 1) * 2 + wn) * kNB + nb) * kRecFields) * 16 + l16;
       const RowStats& s = st[nb];
-      p[0 * 32] = s.mz1; p[1 * 32] = s.sz1; p[2 * 32] = s.mzT; p[3 * 32] = s.szT;
-      p[4 * 32] = s.mtT; p[5 * 32] = s.stT; p[6 * 32] = s.a;   p[7 * 32] = s.mt1;
-      p[8 * 32] = s.st1;
+      p[0 * 16] = s.mz1; p[1 * 16] = s.sz1; p[2 * 16] = s.mzT; p[3 * 16] = s.szT;
+      p[4 * 16] = s.mtT; p[5 * 16] = s.stT; p[6 * 16] = s.a;   p[7 * 16] = s.mt1;
+      p[8 * 16] = s.st1;
     }
   }
   __syncthreads();
-  if (wm == 0 && lane < 32) {
+  if (wm == 0 && lane < 16) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
 #pragma unroll
       for (int src = 1; src < G::kWM; ++src) {
-        const float* p = xs + ((((src - 1) * 2 + wn) * 2 + nb) * kRecFields) * 32 + l32;
+        const float* p = xs + ((((src - 1) * 2 + wn) * kNB + nb) * kRecFields) * 16 + l16;
         RowStats o;
-        o.mz1 = p[0 * 32]; o.sz1 = p[1 * 32]; o.mzT = p[2 * 32]; o.szT = p[3 * 32];
-        o.mtT = p[4 * 32]; o.stT = p[5 * 32]; o.a = p[6 * 32];   o.mt1 = p[7 * 32];
-        o.st1 = p[8 * 32];
+        o.mz1 = p[0 * 16]; o.sz1 = p[1 * 16]; o.mzT = p[2 * 16]; o.szT = p[3 * 16];
+        o.mtT = p[4 * 16]; o.stT = p[5 * 16]; o.a = p[6 * 16];   o.mt1 = p[7 * 16];
+        o.st1 = p[8 * 16];
         stats_merge(st[nb], o);
       }
       const int64_t tok = t0 + acc_col(wn, nb, lane);
@@ -624,8 +624,8 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   const T* ht = static_cast<const T*>(a.ht);
   const T* Wt = static_cast<const T*>(a.wt);
 
-  f32x16 acc[NB][2][2];
-  f32x16 tacc[1][2][2];
+  f32x4 acc[NB][kMB][kNB];
+  f32x4 tacc[1][kMB][kNB];
   if constexpr (MODE == MODE_TIED) {
     const T* const b[2] = {hs, ht};
     tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
@@ -638,8 +638,8 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   }
-  const f32x16(&z)[2][2] = acc[0];
-  const f32x16(&tl)[2][2] = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const WaveAcc& z = acc[0];
+  const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
 
   const float* hdr = a.saved + 4 * a.n;
   const float den = hdr[0];
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   T* dz = static_cast<T*>(a.dz);
 
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     const int64_t tok = t0 + acc_col(wn, nb, lane);
     if (tok >= a.dz_rows) continue;
     const bool live = tok < a.n;  // rows past n are zero padding of the slab
@@ -665,29 +665,27 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const float cm = coef * a.wkl * mass;    // top-K: M softmax(z)
     T* row = dz + tok * a.ldz + (v0 - a.c0);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kMB; ++mb) {
+      // registers r = 0..3 are four consecutive vocabulary rows
+      float o[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = q * 4 + e;
-          const int64_t vv = v0 + acc_row(wm, mb, x, lane);
-          const float zz = z[mb][nb][x];
-          const float p1 = exp2_fast(fmaf(zz, kLog2e, -L1));
-          float dv;
-          if (MODE == MODE_TOPK) {
-            dv = cm * p1;
-          } else {
-            dv = cs * (p1 - (vv == y ? 1.f : 0.f));
-            const float pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
-            const float pt = exp2_fast(fmaf(tl[mb][nb][x], a.cT, -LtT));
-            dv = fmaf(ck, pz - pt, dv);
-          }
-          o[e] = (vv < a.v && valid) ? dv : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int64_t vv = v0 + acc_row(wm, mb, r, lane);
+        const float zz = z[mb][nb][r];
+        const float p1 = exp2_fast(fmaf(zz, kLog2e, -L1));
+        float dv;
+        if (MODE == MODE_TOPK) {
+          dv = cm * p1;
+        } else {
+          dv = cs * (p1 - (vv == y ? 1.f : 0.f));
+          const float pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
+          const float pt = exp2_fast(fmaf(tl[mb][nb][r], a.cT, -LtT));
+          dv = fmaf(ck, pz - pt, dv);
         }
-        store4<T>(row + acc_row(wm, mb, q * 4, lane), o[0], o[1], o[2], o[3]);
+        o[r] = (vv < a.v && valid) ? dv : 0.f;
       }
+      store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
@@ -744,20 +742,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
   int mt, nt;
   grouped_tile(t, a.n_mt, a.n_nt, 8, mt, nt);
   const int64_t m0 = (int64_t)mt * kTile, n0 = (int64_t)nt * kTile;
-  f32x16 acc[1][2][2];
+  f32x4 acc[1][kMB][kNB];
   mainloop<T, AKC, BKC, 1>(a.A, &a.B, m0, n0, a.K, lds, acc, tid);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
       const int64_t col = n0 + acc_col(wn, nb, lane);
       if (col >= a.N) continue;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int64_t row = m0 + acc_row(wm, mb, x, lane);
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + acc_row(wm, mb, r, lane);
         if (row < a.M) {
           float* p = a.C + row * a.ldc + col;
-          const float vv = acc[0][mb][nb][x];
+          const float vv = acc[0][mb][nb][r];
           *p = a.accumulate ? *p + vv : vv;
         }
       }
@@ -765,7 +763,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
 }
 
 // Pipelined bf16 GEMM: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output, tile
-// 256 x BN, 8 waves, 4 stages. A / B are K-contiguous or row-contiguous.
+// 256 x BN, 8 waves, two slots. A / B are K-contiguous or row-contiguous; K is
+// a multiple of 64 and both operands are zero (or read as zero) past their
+// own K extent.
 template <bool AKC, bool BKC, int BN>
 struct GemmPipeArgs {
   std::conditional_t<AKC, PipeOperand, PipeOperandMN> A;
@@ -778,27 +778,27 @@ struct GemmPipeArgs {
 
 template <bool AKC, bool BKC, int BN>
 __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC, BN> a) {
-  using C = PipeCfg<256, BN, 1, 4, 4, AKC, BKC>;
+  using C = PipeCfg<256, BN, 1, AKC, BKC>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int mt, nt;
   grouped_tile(t, a.n_mt, a.n_nt, 8, mt, nt);
   const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
-  f32x16 acc[1][C::MBLK][C::NBLK];
+  f32x4 acc[1][C::MB][C::NBK];
   pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, a.K, lds, acc, tid);
 #pragma unroll
-  for (int mb = 0; mb < C::MBLK; ++mb)
+  for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < C::NBLK; ++nb) {
-      const int64_t col = n0 + wn * C::TN + nb * 32 + (lane & 31);
+    for (int nb = 0; nb < C::NBK; ++nb) {
+      const int64_t col = n0 + pipe_col<C>(wn, nb, lane);
       if (col >= a.N) continue;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int64_t row = m0 + wm * C::TM + mb * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + pipe_row<C>(wm, mb, r, lane);
         if (row < a.M) {
           float* p = a.C + row * a.ldc + col;
-          const float vv = acc[0][mb][nb][x];
+          const float vv = acc[0][mb][nb][r];
           *p = a.accumulate ? *p + vv : vv;
         }
       }
@@ -925,8 +925,8 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     if constexpr (G::kPipe) {
       if (dw) {
         // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]: A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n],
-        // both row-contiguous; the slab's zero rows past n pad K to a multiple of 32.
-        GemmPipeArgs<false, false, 256> ga;
+        // both row-contiguous; the slab's zero rows past n pad K to a multiple of 64.
+        GemmPipeArgs<false, false, 128> ga;
         ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
         ga.B = PipeOperandMN{static_cast<const T*>(x.hs), p.d, p.d, p.n};
         ga.C = dw + c0 * p.d;
@@ -936,9 +936,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         ga.K = p.dz_rows;
         ga.accumulate = accumulate;
         ga.n_mt = (int)((cw + 255) / 256);
-        ga.n_nt = (int)((p.d + 255) / 256);
+        ga.n_nt = (int)((p.d + 127) / 128);
         KD_TRY(L.run(KD_KERNEL_GEMM_DW, [&] {
-          gemm_pipe_kernel<false, false, 256>
+          gemm_pipe_kernel<false, false, 128>
               <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), 512, 0, stream>>>(ga);
         }));
       }
@@ -946,7 +946,6 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]: A(i, m) = dz[i * ldz + m] (K-contiguous),
         // B(n, m) = W[(c0 + m) * d + n] (row-contiguous); slab columns past cw are zero.
         const int mt = (int)((p.n + 255) / 256);
-        const bool wide = (int64_t)mt * ((p.d + 255) / 256) >= 256;
         auto launch = [&](auto bn_tag) {
           constexpr int BN = decltype(bn_tag)::value;
           GemmPipeArgs<true, false, BN> gb;
@@ -965,8 +964,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
                 <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), 512, 0, stream>>>(gb);
           });
         };
-        KD_TRY(wide ? launch(std::integral_constant<int, 256>{})
-                    : launch(std::integral_constant<int, 128>{}));
+        KD_TRY(launch(std::integral_constant<int, 128>{}));
       }
     } else {
     if (dw) {
@@ -1012,6 +1010,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
 
 }  // namespace
 
+static_assert(kPipeK == kPipeBK, "K step of the pipelined path");
 int pipe_vocab_rows() { return GeoFused::kVT; }
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,

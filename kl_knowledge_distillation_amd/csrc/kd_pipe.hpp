@@ -1,40 +1,57 @@
-// bf16 main loop with direct global -> LDS copies and a 3-stage pipeline (gfx950).
+// bf16 main loop with buffer loads straight into LDS, two slots, ping-pong
+// scheduling and v_mfma_f32_16x16x32_bf16 (gfx950).
 //
 // Workgroup: 512 threads = 8 wave64 as 4 (A rows) x 2 (B rows). Output tile
-// BM x BN (A rows x B rows), each wave TM x TN = (BM/4) x (BN/2), made of 32x32
-// blocks of v_mfma_f32_32x32x16_bf16. One K step moves 32 bf16 (64 bytes) of
-// every operand row.
+// BM x BN (A rows x B rows); each wave owns TM x TN = (BM/4) x (BN/2), made of
+// 16x16 blocks. One K step moves 64 bf16 (128 bytes, one cache line) of every
+// operand row.
 //
-// Copies. global_load_lds_dwordx4 writes lane l's 16 bytes at LDS base + 16 l,
-// whatever the source address, so a wave fills 1 KB of LDS per instruction and
-// never touches a VGPR. An operand tile is stored as rows of 64 bytes (4 chunks
-// of 16 bytes); one copy instruction fills 16 whole rows, so each row's 64
-// bytes come from one contiguous global segment. The chunk index is XOR-
-// swizzled by swz(r) = (r >> 2) & 3: the lane that owns LDS slot (row, p)
-// fetches logical chunk p ^ swz(row). On gfx950 the fragment reads (32 rows,
-// one 16-byte chunk each, ds_read_b128) are then free of bank conflicts; the
-// swizzles measured for this were 4-way (r & 3), 2-way (several others) or
-// conflict-free (this one among them). A fragment-native layout (32 rows x 32
-// bytes per copy) is conflict-free too but doubles the cache lines each copy
-// touches, and measured slower.
-
-// Ragged edges. A row past the operand's end is clamped to its last row: the
-// duplicated values feed only output rows/columns the callers mask out. The K
-// extent must be a multiple of 32 (checked on the host).
+// Output layout of the 16x16x32 MFMA: lane l holds column l % 16 and rows
+// 4 (l / 16) + r, r in [0, 4), of its block. The A fragment of lane l is row
+// l % 16 with 8 k values; the B fragment is column l % 16 with the same 8 k
+// values (any k order shared by both operands gives the same sum).
 //
-// Pipeline. Stages s = 0, 1 are issued up front; iteration kt waits until its
-// own stage has landed (vmcnt counts this thread's copies, a barrier makes all
-// threads' copies visible), issues stage kt + 2 into the buffer iteration
-// kt - 1 just finished with, and runs the MFMAs of stage kt.
+// Why this shape. With random bf16 operands the chip is power limited well
+// below its nominal MFMA peak, and the 16x16x32 form sustains a higher clock
+// than 32x32x16 for the same work. Moving a full 128-byte line per row and step
+// halves the cache-line traffic per byte against 64-byte row segments.
+//
+// Copies. buffer_load_dwordx4 ... lds writes lane l's 16 bytes at LDS base +
+// 16 l and never touches a VGPR; a wave fills 1 KB per instruction. The buffer
+// descriptor bounds every copy: a lane past the end of the operand reads zero,
+// so ragged tiles need no clamping and padded rows / k-rows hold zeros. The
+// wave-uniform part of each address (row block, K offset) goes into soffset,
+// so all copies of an operand share one or two offset VGPRs.
+//
+// K-contiguous tiles are rows of 128 bytes (8 chunks of 16 bytes); one copy
+// fills 8 whole rows, each from one cache line. Chunk c of row r sits at
+// position c ^ swz(r), swz(r) = (r >> 1) & 7: the 16 rows a fragment read
+// touches at one chunk then fall in 16 distinct 16-byte bank groups.
+//
+// Row-contiguous tiles (the dW / dH operands) are 64 k-rows of R bf16; their
+// fragments are read with ds_read_b64_tr_b16 (see mn_offset).
+//
+// Schedule (two slots). Waves 0..3 (group A) and 4..7 (group B), one of each
+// per SIMD, run half a step apart:
+//   part 1:  A: MFMAs of step i            B: read fragments of step i
+//   barrier 1 (step i+1 has landed: group B waited for its copies)
+//   part 2:  A: read fragments of step i+1 B: MFMAs of step i, issuing the
+//                                             copies of step i+2 into the slot
+//                                             of step i between them
+//   barrier 2
+// While one wave of a SIMD issues MFMAs the other does its LDS reads, so the
+// matrix pipe keeps running across the barriers. The slot of step i is free at
+// barrier 1: group B read it in part 1, group A in part 2 of step i-1. Copies
+// of step i+2 have the rest of part 2 and part 1 of step i+1 to land.
 #pragma once
 
 #include "kd_device.hpp"
 
 namespace kd {
 
-constexpr int kPipeBK = 32;  // bf16 elements per K step
+constexpr int kPipeBK = 64;  // bf16 elements per K step
 
-__device__ __forceinline__ int pipe_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int pipe_swz(int r) { return (r >> 1) & 7; }
 
 // Workgroup barrier without the implicit wait for every outstanding memory
 // operation that __syncthreads() carries: the pipeline has already waited for
@@ -53,6 +70,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes); sizes of 4 GiB and more are
+// cut to 4 GiB - 1 (every offset a tile uses stays far below it).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffll ? 0xffffffffu : (uint32_t)bytes);
+  // dword 3: 32-bit data format, the setting raw buffer loads use on gfx9.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// 16 bytes per lane from descriptor r at voff + soff into dst + 16 lane; lanes
+// whose offset falls outside the descriptor write zeros.
+__device__ __forceinline__ void buffer_copy(rsrc_t r, uint8_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           soff, 0, 0);
+}
+
 // A K-contiguous bf16 operand: element (row, k) at ptr[row * ld + k], rows < `rows`.
 struct PipeOperand {
   const bf16_t* ptr;
@@ -60,48 +94,9 @@ struct PipeOperand {
   int64_t rows;
 };
 
-// Tile configuration: BM x BN output tile, NB B operands sharing the A tile,
-// WM x 2 waves, S pipeline stages; AKC / BKC: whether A / B are K-contiguous
-// (else row-contiguous, see pipe_copy_mn).
-template <int BM, int BN, int NB, int WM = 4, int S = 3, bool AKC = true, bool BKC = true>
-struct PipeCfg {
-  static constexpr int WN = 2;
-  static constexpr bool kAKC = AKC, kBKC = BKC;
-  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves, kStages = S;
-  static constexpr int TM = BM / WM, TN = BN / WN;
-  static constexpr int MBLK = TM / 32, NBLK = TN / 32;
-  static constexpr int kABytes = BM * 64, kBBytes = BN * 64;
-  static constexpr int kStageBytes = kABytes + NB * kBBytes;
-  static constexpr int kLdsBytes = S * kStageBytes;
-  // copy instructions per thread per stage: R rows / 16 rows per instruction / waves
-  static constexpr int kCopiesA = BM / (16 * kWaves), kCopiesB = BN / (16 * kWaves);
-  static constexpr int kCopies = kCopiesA + NB * kCopiesB;
-  static_assert(BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "copies must split evenly");
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
-  static_assert(S >= 2 && kCopies * (S - 2) < 64, "pipeline depth");
-};
-
-// Issue the copies of one R-row operand tile for K step k0 into `dst`.
-template <int R, int NWAVES>
-__device__ __forceinline__ void pipe_copy(const PipeOperand& op, int64_t row0, int64_t k0,
-                                          uint8_t* dst, int lane, int w) {
-  constexpr int kPerWave = R / (16 * NWAVES);
-#pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int inst = w * kPerWave + j;           // 16 rows per instruction
-    const int row = inst * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ pipe_swz(row);
-    int64_t grow = row0 + row;
-    grow = grow < op.rows ? grow : op.rows - 1;
-    const bf16_t* src = op.ptr + grow * op.ld + k0 + chunk * 8;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)src, (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
-  }
-}
-
-// A row-contiguous bf16 operand: element (row, k) at ptr[k * ld + row]; rows < `rows`
-// (a multiple of 8), k-rows < `kdim`. A k-row past `kdim` is clamped to the last
-// one, so the other operand must be zero there (callers guarantee it).
+// A row-contiguous bf16 operand: element (row, k) at ptr[k * ld + row], k < `kdim`.
+// Rows past `rows` read neighbouring (finite) data or zeros; they only feed
+// outputs the callers drop.
 struct PipeOperandMN {
   const bf16_t* ptr;
   int64_t ld;
@@ -109,40 +104,102 @@ struct PipeOperandMN {
   int64_t kdim;
 };
 
-// Row-contiguous tile image: 32 k-rows of R bf16 each (2R bytes per k-row), the
-// 16-byte chunk index XOR-ed with (k & 3) << 2. Copies move whole k-row segments
-// (R/8 lanes per k-row, fully coalesced); fragments are read with
-// ds_read_b64_tr_b16, which returns lane i of each 16-lane group the 4 values
-// (k0 + e, m0 + i), e = 0..3, when lane 4e + q reads 8 bytes at (k0 + e, m0 + 4q).
-// With the swizzle, the 4 k-rows a half-wave reads land in distinct bank quarters.
+// Row-contiguous tile image: 64 k-rows of R bf16 each (2R bytes per k-row), the
+// 16-byte chunk index XOR-ed with (k & 3) << 2. Fragments are read with
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4e + q reads 8 bytes at
+// (k0 + e, m0 + 4q) and lane i receives the 4 values (k0 + e, m0 + i), e = 0..3.
 template <int R>
 __device__ __forceinline__ int mn_offset(int k, int m) {
   return k * (2 * R) + (((m >> 3) ^ ((k & 3) << 2)) << 4) + 2 * (m & 7);
 }
 
-template <int R, int NWAVES>
-__device__ __forceinline__ void pipe_copy_mn(const PipeOperandMN& op, int64_t row0, int64_t k0,
-                                             uint8_t* dst, int lane, int w) {
-  static_assert(R >= 128 && R % 128 == 0, "row-contiguous tiles are 128 or 256 wide");
-  constexpr int kCpr = R / 8;               // 16-byte chunks per k-row
-  constexpr int kRowsPerInst = 64 / kCpr;   // k-rows per copy instruction
-  constexpr int kPerWave = R / (16 * NWAVES);
-#pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int inst = w * kPerWave + j;
-    const int krow = inst * kRowsPerInst + lane / kCpr;
-    const int chunk = (lane % kCpr) ^ ((krow & 3) << 2);
-    int64_t k = k0 + krow;
-    k = k < op.kdim ? k : op.kdim - 1;
-    int64_t m = row0 + chunk * 8;
-    m = m < op.rows ? m : op.rows - 8;
-    const bf16_t* src = op.ptr + k * op.ld + m;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)src, (__attribute__((address_space(3))) void*)(dst + inst * 1024), 16, 0, 0);
-  }
-}
+// Copy source of one operand tile. issue(k0, dst, local) moves 1 KB block
+// `local` of the tile for the K step starting at k0 into dst + 1024 local.
+template <bool KC, int R>
+struct TileSrc;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// K-contiguous: block `local` is rows 8 local .. 8 local + 7.
+template <int R>
+struct TileSrc<true, R> {
+  rsrc_t rsrc;
+  uint32_t voff[2];  // lane offset for even / odd blocks (the swizzle depends on row bit 3)
+  uint32_t stride;   // bytes per row
+
+  __device__ __forceinline__ void init(const PipeOperand& op, int64_t row0, int lane) {
+    rsrc = make_rsrc(op.ptr + row0 * op.ld, (op.rows - row0) * op.ld * 2);
+    stride = (uint32_t)(op.ld * 2);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int row = p * 8 + (lane >> 3);  // row within a pair of blocks
+      const int chunk = (lane & 7) ^ pipe_swz(row);
+      voff[p] = (uint32_t)(lane >> 3) * stride + (uint32_t)chunk * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* dst, int local) const {
+    const uint32_t soff = (uint32_t)local * 8u * stride + (uint32_t)(k0 * 2);
+    buffer_copy(rsrc, dst + local * 1024, voff[local & 1], soff);
+  }
+};
+
+// Row-contiguous: block `local` is k-rows kKpi local .. kKpi (local + 1) - 1.
+template <int R>
+struct TileSrc<false, R> {
+  static_assert(R == 128 || R == 256, "row-contiguous tiles are 128 or 256 wide");
+  static constexpr int kCpr = R / 8;      // 16-byte chunks per k-row
+  static constexpr int kKpi = 64 / kCpr;  // k-rows per block (4 or 2)
+  const bf16_t* base;                     // element (row0, k = 0)
+  int64_t ld, kdim, row0;
+  uint32_t voff[2];  // by bit 1 of the block's first k-row (the swizzle uses k & 3)
+
+  __device__ __forceinline__ void init(const PipeOperandMN& op, int64_t r0, int lane) {
+    base = op.ptr + r0;
+    ld = op.ld;
+    kdim = op.kdim;
+    row0 = r0;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int kr = lane / kCpr;  // k-row within the block
+      const int chunk = (lane % kCpr) ^ (((2 * p + kr) & 3) << 2);
+      voff[p] = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)chunk * 16u;
+    }
+  }
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* dst, int local) const {
+    // descriptor from k-row k0 on, so offsets stay small whatever K * ld is
+    const rsrc_t r = make_rsrc(base + k0 * ld, ((kdim - k0) * ld - row0) * 2);
+    const uint32_t soff = (uint32_t)(local * kKpi) * (uint32_t)(ld * 2);
+    buffer_copy(r, dst + local * 1024, voff[((local * kKpi) >> 1) & 1], soff);
+  }
+};
+
+// Tile configuration: BM x BN output tile, NB B operands sharing the A tile;
+// AKC / BKC: whether A / B are K-contiguous.
+template <int BM, int BN, int NB, bool AKC = true, bool BKC = true>
+struct PipeCfg {
+  static constexpr int WM = 4, WN = 2;
+  static constexpr bool kAKC = AKC, kBKC = BKC;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int MB = TM / 16, NBK = TN / 16;
+  static constexpr int kABytes = BM * 128, kBBytes = BN * 128;
+  static constexpr int kStageBytes = kABytes + NB * kBBytes;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  // copy instructions per group-B wave per step: A blocks first, then each B
+  static constexpr int kAPer = kABytes / 1024 / 4, kBPer = kBBytes / 1024 / 4;
+  static constexpr int kCopies = kAPer + NB * kBPer;
+  static constexpr int kMfma = 2 * NB * MB * NBK;  // per wave per step
+  static constexpr int kIL = (kMfma / 2) / kCopies > 0 ? (kMfma / 2) / kCopies : 1;
+  static_assert(BM % 256 == 0 && BN % 128 == 0, "copies must split evenly over 4 waves");
+  static_assert(kCopies * kIL <= kMfma, "copies must fit between the MFMAs");
+  static_assert(kCopies < 64, "vmcnt range");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+};
+
+// K-contiguous fragment of rows [row0, row0 + 16) at k32 step kk.
+__device__ __forceinline__ bf16x8 kc_frag(const uint8_t* tile, int row0, int kk, int lane) {
+  const int row = row0 + (lane & 15);
+  const int c = 4 * kk + (lane >> 4);
+  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + ((c ^ pipe_swz(row)) << 4));
+}
 
 // ds_read_b64_tr_b16 through inline asm: issued this way the compiler does not
 // add a wait for every in-flight LDS copy in front of it (it cannot tell the
@@ -156,47 +213,23 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
   return v;
 }
 
-// Fragment of rows [m0, m0 + 32) at k16 step kk from a row-contiguous tile.
+// Row-contiguous fragment of rows [m0, m0 + 16) at k32 step kk: lane l gets
+// row l % 16 at k = 32 kk + 8 (l / 16) + e, e = 0..7 (the K-contiguous order).
 template <int R>
 __device__ __forceinline__ bf16x8 mn_frag(const uint8_t* tile, int m0, int kk, int lane) {
-  const int g = lane >> 4, i = lane & 15;
-  const int m = m0 + 16 * (g & 1) + 4 * (i & 3);
-  const int kb = 16 * kk + 8 * (g >> 1) + (i >> 2);
-  const uint2 lo = lds_read_tr16(tile + mn_offset<R>(kb, m));
-  const uint2 hi = lds_read_tr16(tile + mn_offset<R>(kb + 4, m));
+  const int g = lane >> 4, j = lane & 15;
+  const int k = 32 * kk + 8 * g + (j >> 2);
+  const int m = m0 + 4 * (j & 3);
+  const uint2 lo = lds_read_tr16(tile + mn_offset<R>(k, m));
+  const uint2 hi = lds_read_tr16(tile + mn_offset<R>(k + 4, m));
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// K-contiguous fragment of rows [row0, row0 + 32) at k16 step kk.
-__device__ __forceinline__ bf16x8 kc_frag(const uint8_t* tile, int row0, int kk, int lane) {
-  const int row = row0 + (lane & 31);
-  const int c = 2 * kk + (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(tile + row * 64 + ((c ^ pipe_swz(row)) << 4));
-}
-
-// The A-group (waves 0..3) copies the A tile, the B-group (waves 4..7) the B tiles.
-template <class C, class OA>
-__device__ __forceinline__ void pipe_issue_a(const OA& A, int64_t a_row0, int64_t k0, uint8_t* stage,
-                                             int lane, int gw) {
-  if constexpr (C::kAKC) pipe_copy<C::kABytes / 64, 4>(A, a_row0, k0, stage, lane, gw);
-  else pipe_copy_mn<C::kABytes / 64, 4>(A, a_row0, k0, stage, lane, gw);
-}
-template <class C, int NB, class OB>
-__device__ __forceinline__ void pipe_issue_b(const OB* B, int64_t b_row0, int64_t k0, uint8_t* stage,
-                                             int lane, int gw) {
-#pragma unroll
-  for (int g = 0; g < NB; ++g) {
-    uint8_t* dst = stage + C::kABytes + g * C::kBBytes;
-    if constexpr (C::kBKC) pipe_copy<C::kBBytes / 64, 4>(B[g], b_row0, k0, dst, lane, gw);
-    else pipe_copy_mn<C::kBBytes / 64, 4>(B[g], b_row0, k0, dst, lane, gw);
-  }
-}
-
-// Fragments of one K step (both 16-wide halves) for this wave's sub-tile.
+// Fragments of one K step (two k32 halves) for this wave's sub-tile.
 template <class C, int NB>
 struct PipeFrags {
-  bf16x8 a[2][C::MBLK];
-  bf16x8 b[2][NB][C::NBLK];
+  bf16x8 a[2][C::MB];
+  bf16x8 b[2][NB][C::NBK];
 };
 
 template <class C, int NB>
@@ -205,73 +238,84 @@ __device__ __forceinline__ void pipe_read(const uint8_t* stage, PipeFrags<C, NB>
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-    for (int mb = 0; mb < C::MBLK; ++mb) {
-      const int row0 = wm * C::TM + mb * 32;
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int row0 = wm * C::TM + mb * 16;
       if constexpr (C::kAKC) f.a[kk][mb] = kc_frag(stage, row0, kk, lane);
-      else f.a[kk][mb] = mn_frag<C::kABytes / 64>(stage, row0, kk, lane);
+      else f.a[kk][mb] = mn_frag<C::kABytes / 128>(stage, row0, kk, lane);
     }
 #pragma unroll
     for (int g = 0; g < NB; ++g)
 #pragma unroll
-      for (int nb = 0; nb < C::NBLK; ++nb) {
+      for (int nb = 0; nb < C::NBK; ++nb) {
         const uint8_t* tile = stage + C::kABytes + g * C::kBBytes;
-        const int row0 = wn * C::TN + nb * 32;
+        const int row0 = wn * C::TN + nb * 16;
         if constexpr (C::kBKC) f.b[kk][g][nb] = kc_frag(tile, row0, kk, lane);
-        else f.b[kk][g][nb] = mn_frag<C::kBBytes / 64>(tile, row0, kk, lane);
+        else f.b[kk][g][nb] = mn_frag<C::kBBytes / 128>(tile, row0, kk, lane);
       }
   }
 }
 
 template <class C, int NB>
-__device__ __forceinline__ void pipe_mma(const PipeFrags<C, NB>& f, f32x16 (&acc)[NB][C::MBLK][C::NBLK]) {
+__device__ __forceinline__ void pipe_mma(const PipeFrags<C, NB>& f, f32x4 (&acc)[NB][C::MB][C::NBK]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int g = 0; g < NB; ++g)
 #pragma unroll
-      for (int mb = 0; mb < C::MBLK; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < C::NBLK; ++nb)
-          acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][mb], f.b[kk][g][nb],
+        for (int nb = 0; nb < C::NBK; ++nb)
+          acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[kk][mb], f.b[kk][g][nb],
                                                                    acc[g][mb][nb], 0, 0, 0);
 }
 
-// Wait until at most `n` copy instructions of this thread are still in flight.
-template <int PER, int MAXN>
-__device__ __forceinline__ void wait_stages(int n) {
-  if constexpr (MAXN >= 3) { if (n >= 3) { wait_vmcnt<3 * PER>(); return; } }
-  if constexpr (MAXN >= 2) { if (n == 2) { wait_vmcnt<2 * PER>(); return; } }
-  if constexpr (MAXN >= 1) { if (n == 1) { wait_vmcnt<PER>(); return; } }
-  wait_vmcnt<0>();
+// The same MFMAs with copy(j), j = 0 .. C::kCopies-1, issued after MFMA
+// kIL (j + 1) - 1, in that order (sched_group_barrier keeps the interleave).
+template <class C, int NB, class F>
+__device__ __forceinline__ void pipe_mma_copies(const PipeFrags<C, NB>& f,
+                                                f32x4 (&acc)[NB][C::MB][C::NBK], F&& copy) {
+  int m = 0;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int g = 0; g < NB; ++g)
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < C::NBK; ++nb) {
+          acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[kk][mb], f.b[kk][g][nb],
+                                                                   acc[g][mb][nb], 0, 0, 0);
+          if (m % C::kIL == C::kIL - 1 && m / C::kIL < C::kCopies) copy(m / C::kIL);
+          ++m;
+        }
+#pragma unroll
+  for (int j = 0; j < C::kCopies; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, C::kIL, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // VMEM read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, C::kMfma - C::kCopies * C::kIL, 0);
 }
 
-// acc[g] = A[a_row0 : +BM, 0:K] * B[g][b_row0 : +BN, 0:K]^T, K a multiple of 32.
-//
-// Ping-pong schedule. Waves 0..3 (group A, one per SIMD) and waves 4..7
-// (group B) run half an iteration apart, with two barriers per K step:
-//
-//   part 1:  A: MFMAs of step i           B: read fragments of step i,
-//                                            copy B tiles of step i+S-1
-//   barrier 1 (step i+1 visible: every wave first waits for its own copies)
-//   part 2:  A: read fragments of step i+1 B: MFMAs of step i
-//               copy A tile of step i+S-1
-//   barrier 2
-//
-// While one group's wave issues MFMAs, the other group's wave on the same SIMD
-// does its LDS reads and copies, so the matrix pipe does not drain at the
-// barriers. Slot reuse: step i+S-1 goes into the slot of step i-1, whose reads
-// finished before barrier 1 of step i-1 (group B waits for its reads before
-// that barrier; group A's were consumed by its MFMAs of step i-1).
+// Copy j of group-B wave gw for the K step at k0 into `stage`: the wave takes a
+// quarter of the A blocks, then a quarter of each B operand's blocks.
+template <class C, int NB, class SA, class SB>
+__device__ __forceinline__ void pipe_copy(const SA& sa, const SB (&sb)[NB], int64_t k0, uint8_t* stage,
+                                          int gw, int j) {
+  if (j < C::kAPer) {
+    sa.issue(k0, stage, gw * C::kAPer + j);
+  } else {
+    const int g = (j - C::kAPer) / C::kBPer, jj = (j - C::kAPer) % C::kBPer;
+    sb[g].issue(k0, stage + C::kABytes + g * C::kBBytes, gw * C::kBPer + jj);
+  }
+}
+
+// acc[g] = A[a_row0 : +BM, 0:K] * B[g][b_row0 : +BN, 0:K]^T, K a multiple of 64.
 // Ends with a full barrier, so the caller may reuse `lds` right after.
 template <class C, int NB, class OA, class OB>
 __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t a_row0, int64_t b_row0,
                                               int64_t K, uint8_t* lds,
-                                              f32x16 (&acc)[NB][C::MBLK][C::NBLK], int tid) {
-  constexpr int S = C::kStages;
-  static_assert(S >= 3, "the ping-pong schedule needs at least 3 slots");
+                                              f32x4 (&acc)[NB][C::MB][C::NBK], int tid) {
   static_assert(C::kWaves == 8, "two groups of four waves");
-  constexpr int kCopiesA = C::kABytes / 1024 / 4;        // per A-group wave per step
-  constexpr int kCopiesB = NB * C::kBBytes / 1024 / 4;   // per B-group wave per step
   // The wave index is the same for all lanes of a wave; readfirstlane makes that
   // visible to the compiler, so the group branches below are scalar branches.
   const int lane = tid & 63;
@@ -282,80 +326,82 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
 #pragma unroll
   for (int g = 0; g < NB; ++g)
 #pragma unroll
-    for (int mb = 0; mb < C::MBLK; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < C::NBLK; ++nb)
+      for (int nb = 0; nb < C::NBK; ++nb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) acc[g][mb][nb][x] = 0.f;
+        for (int x = 0; x < 4; ++x) acc[g][mb][nb][x] = 0.f;
 
   const int nk = (int)(K / kPipeBK);
-  // Prologue: steps 0 .. S-2, each group its own operand.
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (st < nk) {
-      uint8_t* slot = lds + st * C::kStageBytes;
-      if (grp_b) pipe_issue_b<C, NB, OB>(B, b_row0, (int64_t)st * kPipeBK, slot, lane, gw);
-      else pipe_issue_a<C, OA>(A, a_row0, (int64_t)st * kPipeBK, slot, lane, gw);
-    }
-  // Step 0 visible: at most steps 1 .. min(S-2, nk-1) still in flight.
-  {
-    const int later = min(S - 2, nk - 1);
-    if (grp_b) wait_stages<kCopiesB, S - 2>(later);
-    else wait_stages<kCopiesA, S - 2>(later);
-  }
-  pipe_barrier();
   PipeFrags<C, NB> f;
   if (!grp_b) {
-    // Group A: MFMAs in part 1, reads and A-tile copies in part 2.
+    pipe_barrier();  // pairs with the prologue barrier of group B: step 0 visible
     pipe_read<C, NB>(lds, f, wm, wn, lane);
-    int cur = 0;  // slot of step i
     for (int i = 0; i < nk; ++i) {
-      const int nxt = (cur + 1 == S) ? 0 : cur + 1;     // slot of step i+1
-      const int fill = (cur == 0) ? S - 1 : cur - 1;    // slot of step i+S-1
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments of step i ready
       __builtin_amdgcn_s_setprio(1);
       pipe_mma<C, NB>(f, acc);
       __builtin_amdgcn_s_setprio(0);
-      // step i+1 must have landed; steps i+2 .. i+S-2 may stay in flight
-      wait_stages<kCopiesA, S - 2>(max(0, min(S - 3, nk - 2 - i)));
-      pipe_barrier();
-      if (i + 1 < nk) pipe_read<C, NB>(lds + nxt * C::kStageBytes, f, wm, wn, lane);
-      if (i + S - 1 < nk)
-        pipe_issue_a<C, OA>(A, a_row0, (int64_t)(i + S - 1) * kPipeBK, lds + fill * C::kStageBytes,
-                            lane, gw);
-      pipe_barrier();
-      cur = nxt;
+      pipe_barrier();  // 1: step i+1 has landed
+      if (i + 1 < nk) pipe_read<C, NB>(lds + ((i + 1) & 1) * C::kStageBytes, f, wm, wn, lane);
+      pipe_barrier();  // 2
     }
   } else {
-    // Group B: reads and B-tile copies in part 1, MFMAs in part 2.
-    int cur = 0;
-    for (int i = 0; i < nk; ++i) {
-      const int nxt = (cur + 1 == S) ? 0 : cur + 1;
-      const int fill = (cur == 0) ? S - 1 : cur - 1;
-      pipe_read<C, NB>(lds + cur * C::kStageBytes, f, wm, wn, lane);
-      if (i + S - 1 < nk)
-        pipe_issue_b<C, NB, OB>(B, b_row0, (int64_t)(i + S - 1) * kPipeBK, lds + fill * C::kStageBytes,
-                                lane, gw);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of slot `cur` done
-      // step i+1 must have landed; steps i+2 .. i+S-1 may stay in flight
-      wait_stages<kCopiesB, S - 2>(max(0, min(S - 2, nk - 2 - i)));
-      pipe_barrier();
+    TileSrc<C::kAKC, C::kABytes / 128> sa;
+    TileSrc<C::kBKC, C::kBBytes / 128> sb[NB];
+    sa.init(A, a_row0, lane);
+#pragma unroll
+    for (int g = 0; g < NB; ++g) sb[g].init(B[g], b_row0, lane);
+    // Prologue: steps 0 and 1; step 0 visible at the first barrier.
+#pragma unroll
+    for (int j = 0; j < C::kCopies; ++j) pipe_copy<C, NB>(sa, sb, 0, lds, gw, j);
+    if (nk > 1) {
+#pragma unroll
+      for (int j = 0; j < C::kCopies; ++j)
+        pipe_copy<C, NB>(sa, sb, kPipeBK, lds + C::kStageBytes, gw, j);
+      wait_vmcnt<C::kCopies>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    pipe_barrier();
+    // Steps that still copy step i+2, then the last two without copies: two
+    // branch-free loop bodies.
+    int i = 0;
+    for (; i + 2 < nk; ++i) {
+      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, wm, wn, lane);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step i done
+      wait_vmcnt<0>();                                       // step i+1 has landed
+      pipe_barrier();  // 1
+      __builtin_amdgcn_s_setprio(1);
+      uint8_t* stage = lds + (i & 1) * C::kStageBytes;
+      const int64_t k0 = (int64_t)(i + 2) * kPipeBK;
+      pipe_mma_copies<C, NB>(f, acc, [&](int j) { pipe_copy<C, NB>(sa, sb, k0, stage, gw, j); });
+      __builtin_amdgcn_s_setprio(0);
+      pipe_barrier();  // 2
+    }
+    for (; i < nk; ++i) {
+      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, wm, wn, lane);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wait_vmcnt<0>();
+      pipe_barrier();  // 1
       __builtin_amdgcn_s_setprio(1);
       pipe_mma<C, NB>(f, acc);
       __builtin_amdgcn_s_setprio(0);
-      pipe_barrier();
-      cur = nxt;
+      pipe_barrier();  // 2
     }
   }
   __syncthreads();
 }
 
-// Row of the BM-row tile held by accumulator register x of block mb (wave row wm).
-template <int TM>
-__device__ __forceinline__ int pipe_row(int wm, int mb, int x, int lane) {
-  return wm * TM + mb * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+// Row (A side) and column (B side) within the BM x BN tile of accumulator
+// register r of block (mb, nb).
+template <class C>
+__device__ __forceinline__ int pipe_row(int wm, int mb, int r, int lane) {
+  return wm * C::TM + mb * 16 + 4 * (lane >> 4) + r;
 }
-template <int TN>
-__device__ __forceinline__ int pipe_col(int wn, int nb, int lane) { return wn * TN + nb * 32 + (lane & 31); }
+template <class C>
+__device__ __forceinline__ int pipe_col(int wn, int nb, int lane) {
+  return wn * C::TN + nb * 16 + (lane & 15);
+}
 
 }  // namespace kd
