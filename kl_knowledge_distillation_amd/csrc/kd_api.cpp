@@ -127,7 +127,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   chunk = std::min<int64_t>(chunk, ceil_div(q.v, vt) * vt);
   q.chunk = chunk;
   q.n_chunks = (int)ceil_div(q.v, chunk);
-  q.merge_blocks = (int)ceil_div(q.n, kd::kMergeThreads);
+  q.merge_blocks = (int)ceil_div(q.n, kd::kMergeTok);
 
   size_t off = kd::kStatusBytes;
   q.off_prep = off;

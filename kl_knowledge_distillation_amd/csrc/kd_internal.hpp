@@ -16,6 +16,7 @@ enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3 };
 constexpr int kRecFields = 9;
 // Tokens per merge workgroup; also the number of partial sums per block.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeTok = 16;  // tokens per merge workgroup
 // Bytes reserved at the start of the workspace for device flags.
 constexpr size_t kStatusBytes = 256;
 // Offset of the header inside `saved` is 16 * n; its size is 64 bytes.

@@ -455,16 +455,21 @@ struct MergeArgs {
   double* partials;   // [blocks][4]: loss sum, valid count, bad count, 0
 };
 
+// A workgroup takes kMergeTok tokens; thread (token tl, group sg) folds the
+// records of tiles sg, sg + kMergeGroups, ... in order, then the group
+// partials are folded in the order sg = 0, 1, ... (deterministic).
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
-  __shared__ double red[3][kMergeThreads];
-  const int tid = threadIdx.x;
-  const int64_t i = (int64_t)blockIdx.x * kMergeThreads + tid;
-  double contrib = 0.0, cnt = 0.0, bad = 0.0;
-  if (i < a.n) {
-    RowStats s;
-    stats_init(s);
+  constexpr int kGroups = kMergeThreads / kMergeTok;
+  __shared__ float part[kRecFields][kGroups][kMergeTok];
+  __shared__ double red[3][kMergeTok];
+  const int tid = threadIdx.x, tl = tid % kMergeTok, sg = tid / kMergeTok;
+  const int64_t i = (int64_t)blockIdx.x * kMergeTok + tl;
+  const bool live = i < a.n;
+  RowStats s;
+  stats_init(s);
+  if (live) {
     const int64_t stride = (int64_t)a.n_slices * a.n;
-    for (int sl = 0; sl < a.n_slices; ++sl) {
+    for (int sl = sg; sl < a.n_slices; sl += kGroups) {
       const float* r = a.rec + (int64_t)sl * a.n + i;
       RowStats o;
       o.mz1 = r[0 * stride]; o.sz1 = r[1 * stride]; o.mzT = r[2 * stride];
@@ -472,54 +477,68 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       o.a = r[6 * stride];   o.mt1 = r[7 * stride]; o.st1 = r[8 * stride];
       stats_merge(s, o);
     }
-    const float lz1 = kLn2 * (s.mz1 + log2f(s.sz1));
-    const float lzT = a.need_zT ? kLn2 * (s.mzT + log2f(s.szT)) : lz1;
-    const float f0 = a.prep[i], f1 = a.prep[a.n + i], f2 = a.prep[2 * a.n + i];
-    const float flag = a.prep[3 * a.n + i];
-    float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f;
-    bool valid;
-    if (a.mode == MODE_TOPK) {
-      // sum p log p - sum p z[idx] + M lse(z)
-      kl = f1 - f0 + f2 * lz1;
-      mass = f2;
-      valid = true;
-    } else {
-      ltT = kLn2 * (s.mtT + log2f(s.stT));
-      const float lt1 = a.need_t1 ? kLn2 * (s.mt1 + log2f(s.st1)) : ltT;
-      const float cross = s.a / (s.stT * a.T);  // E_{P_T}[(t - z) / T]
-      kl = a.T * a.T * (cross - ltT + lzT);
-      valid = flag == 1.f;
-      sce = valid ? lz1 - f0 : 0.f;
-      tce = (valid && a.teacher_ce) ? lt1 - f1 : 0.f;
-    }
-    bad = (flag == 2.f) ? 1.0 : 0.0;
-    cnt = valid ? 1.0 : 0.0;
-    contrib = valid ? ((double)a.ws * sce + (double)a.wt * tce + (double)a.wkl * kl) : 0.0;
-    if (a.out_sce) a.out_sce[i] = sce;
-    if (a.out_tce) a.out_tce[i] = tce;
-    if (a.out_kl) a.out_kl[i] = kl;
-    if (a.saved) {
-      float4 sv = make_float4(lz1, lzT, ltT, mass);
-      reinterpret_cast<float4*>(a.saved)[i] = sv;
-    }
   }
-  red[0][tid] = contrib;
-  red[1][tid] = cnt;
-  red[2][tid] = bad;
+  part[0][sg][tl] = s.mz1; part[1][sg][tl] = s.sz1; part[2][sg][tl] = s.mzT;
+  part[3][sg][tl] = s.szT; part[4][sg][tl] = s.mtT; part[5][sg][tl] = s.stT;
+  part[6][sg][tl] = s.a;   part[7][sg][tl] = s.mt1; part[8][sg][tl] = s.st1;
   __syncthreads();
-  for (int off = kMergeThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) {
-      red[0][tid] += red[0][tid + off];
-      red[1][tid] += red[1][tid + off];
-      red[2][tid] += red[2][tid + off];
+  if (sg == 0) {
+    for (int q = 1; q < kGroups; ++q) {
+      RowStats o;
+      o.mz1 = part[0][q][tl]; o.sz1 = part[1][q][tl]; o.mzT = part[2][q][tl];
+      o.szT = part[3][q][tl]; o.mtT = part[4][q][tl]; o.stT = part[5][q][tl];
+      o.a = part[6][q][tl];   o.mt1 = part[7][q][tl]; o.st1 = part[8][q][tl];
+      stats_merge(s, o);
     }
-    __syncthreads();
+    double contrib = 0.0, cnt = 0.0, bad = 0.0;
+    if (live) {
+      const float lz1 = kLn2 * (s.mz1 + log2f(s.sz1));
+      const float lzT = a.need_zT ? kLn2 * (s.mzT + log2f(s.szT)) : lz1;
+      const float f0 = a.prep[i], f1 = a.prep[a.n + i], f2 = a.prep[2 * a.n + i];
+      const float flag = a.prep[3 * a.n + i];
+      float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f;
+      bool valid;
+      if (a.mode == MODE_TOPK) {
+        // sum p log p - sum p z[idx] + M lse(z)
+        kl = f1 - f0 + f2 * lz1;
+        mass = f2;
+        valid = true;
+      } else {
+        ltT = kLn2 * (s.mtT + log2f(s.stT));
+        const float lt1 = a.need_t1 ? kLn2 * (s.mt1 + log2f(s.st1)) : ltT;
+        const float cross = s.a / (s.stT * a.T);  // E_{P_T}[(t - z) / T]
+        kl = a.T * a.T * (cross - ltT + lzT);
+        valid = flag == 1.f;
+        sce = valid ? lz1 - f0 : 0.f;
+        tce = (valid && a.teacher_ce) ? lt1 - f1 : 0.f;
+      }
+      bad = (flag == 2.f) ? 1.0 : 0.0;
+      cnt = valid ? 1.0 : 0.0;
+      contrib = valid ? ((double)a.ws * sce + (double)a.wt * tce + (double)a.wkl * kl) : 0.0;
+      if (a.out_sce) a.out_sce[i] = sce;
+      if (a.out_tce) a.out_tce[i] = tce;
+      if (a.out_kl) a.out_kl[i] = kl;
+      if (a.saved) {
+        float4 sv = make_float4(lz1, lzT, ltT, mass);
+        reinterpret_cast<float4*>(a.saved)[i] = sv;
+      }
+    }
+    red[0][tl] = contrib;
+    red[1][tl] = cnt;
+    red[2][tl] = bad;
   }
+  __syncthreads();
   if (tid == 0) {
+    double t0 = 0.0, t1 = 0.0, t2 = 0.0;
+    for (int q = 0; q < kMergeTok; ++q) {
+      t0 += red[0][q];
+      t1 += red[1][q];
+      t2 += red[2][q];
+    }
     double* p = a.partials + (int64_t)blockIdx.x * 4;
-    p[0] = red[0][0];
-    p[1] = red[1][0];
-    p[2] = red[2][0];
+    p[0] = t0;
+    p[1] = t1;
+    p[2] = t2;
     p[3] = 0.0;
   }
 }

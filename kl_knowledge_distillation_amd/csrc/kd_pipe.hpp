@@ -105,12 +105,16 @@ struct PipeOperandMN {
 };
 
 // Row-contiguous tile image: 64 k-rows of R bf16 each (2R bytes per k-row), the
-// 16-byte chunk index XOR-ed with (k & 3) << 2. Fragments are read with
+// 16-byte chunk index XOR-ed with mn_swz(k). Fragments are read with
 // ds_read_b64_tr_b16: in each 16-lane group, lane 4e + q reads 8 bytes at
 // (k0 + e, m0 + 4q) and lane i receives the 4 values (k0 + e, m0 + i), e = 0..3.
+// Lane groups 0 and 1 (served together) read k-rows k0 + e and k0 + 8 + e: bits
+// 2-3 of the swizzle spread the four k-rows of a group over distinct banks, bit
+// 1 (from k-row bit 3) separates the two groups.
+__device__ __forceinline__ int mn_swz(int k) { return ((k & 3) << 2) | (((k >> 3) & 1) << 1); }
 template <int R>
 __device__ __forceinline__ int mn_offset(int k, int m) {
-  return k * (2 * R) + (((m >> 3) ^ ((k & 3) << 2)) << 4) + 2 * (m & 7);
+  return k * (2 * R) + (((m >> 3) ^ mn_swz(k)) << 4) + 2 * (m & 7);
 }
 
 // Copy source of one operand tile. issue(k0, dst, local) moves 1 KB block
@@ -149,25 +153,32 @@ struct TileSrc<false, R> {
   static constexpr int kKpi = 64 / kCpr;  // k-rows per block (4 or 2)
   const bf16_t* base;                     // element (row0, k = 0)
   int64_t ld, kdim, row0;
-  uint32_t voff[2];  // by bit 1 of the block's first k-row (the swizzle uses k & 3)
+  // lane offsets by the swizzle-relevant bits of the block's first k-row
+  // (bit 1 and bit 3; k-rows within a block only differ below those)
+  uint32_t voff[4];
 
+  __device__ __forceinline__ static int variant(int local) {
+    const int k = local * kKpi;
+    return ((k >> 1) & 1) | (((k >> 3) & 1) << 1);
+  }
   __device__ __forceinline__ void init(const PipeOperandMN& op, int64_t r0, int lane) {
     base = op.ptr + r0;
     ld = op.ld;
     kdim = op.kdim;
     row0 = r0;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int kr = lane / kCpr;  // k-row within the block
-      const int chunk = (lane % kCpr) ^ (((2 * p + kr) & 3) << 2);
-      voff[p] = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)chunk * 16u;
+    for (int v = 0; v < 4; ++v) {
+      const int kr = lane / kCpr;                      // k-row within the block
+      const int k = ((v & 1) << 1) + ((v >> 1) << 3) + kr;
+      const int chunk = (lane % kCpr) ^ mn_swz(k);
+      voff[v] = (uint32_t)kr * (uint32_t)(ld * 2) + (uint32_t)chunk * 16u;
     }
   }
   __device__ __forceinline__ void issue(int64_t k0, uint8_t* dst, int local) const {
     // descriptor from k-row k0 on, so offsets stay small whatever K * ld is
     const rsrc_t r = make_rsrc(base + k0 * ld, ((kdim - k0) * ld - row0) * 2);
     const uint32_t soff = (uint32_t)(local * kKpi) * (uint32_t)(ld * 2);
-    buffer_copy(r, dst + local * 1024, voff[((local * kKpi) >> 1) & 1], soff);
+    buffer_copy(r, dst + local * 1024, voff[variant(local)], soff);
   }
 };
 
