@@ -942,29 +942,35 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     const int64_t cpad = (int64_t)n_vt * G::kVT;  // columns written by bwd_dz
     const int n_gemm_mt = (int)((cw + kTile - 1) / kTile);
     if constexpr (G::kPipe) {
+      // 256-wide tiles when they still give every CU a tile, else 128-wide.
+      auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((p.d + 255) / 256) >= 256; };
       if (dw) {
         // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]: A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n],
         // both row-contiguous; the slab's zero rows past n pad K to a multiple of 64.
-        GemmPipeArgs<false, false, 128> ga;
-        ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
-        ga.B = PipeOperandMN{static_cast<const T*>(x.hs), p.d, p.d, p.n};
-        ga.C = dw + c0 * p.d;
-        ga.ldc = p.d;
-        ga.M = cw;
-        ga.N = p.d;
-        ga.K = p.dz_rows;
-        ga.accumulate = accumulate;
-        ga.n_mt = (int)((cw + 255) / 256);
-        ga.n_nt = (int)((p.d + 127) / 128);
-        KD_TRY(L.run(KD_KERNEL_GEMM_DW, [&] {
-          gemm_pipe_kernel<false, false, 128>
-              <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), 512, 0, stream>>>(ga);
-        }));
+        auto launch = [&](auto bn_tag) {
+          constexpr int BN = decltype(bn_tag)::value;
+          GemmPipeArgs<false, false, BN> ga;
+          ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
+          ga.B = PipeOperandMN{static_cast<const T*>(x.hs), p.d, p.d, p.n};
+          ga.C = dw + c0 * p.d;
+          ga.ldc = p.d;
+          ga.M = cw;
+          ga.N = p.d;
+          ga.K = p.dz_rows;
+          ga.accumulate = accumulate;
+          ga.n_mt = (int)((cw + 255) / 256);
+          ga.n_nt = (int)((p.d + BN - 1) / BN);
+          return L.run(KD_KERNEL_GEMM_DW, [&] {
+            gemm_pipe_kernel<false, false, BN>
+                <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), 512, 0, stream>>>(ga);
+          });
+        };
+        KD_TRY(wide(cw) ? launch(std::integral_constant<int, 256>{})
+                        : launch(std::integral_constant<int, 128>{}));
       }
       if (dh) {
         // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]: A(i, m) = dz[i * ldz + m] (K-contiguous),
         // B(n, m) = W[(c0 + m) * d + n] (row-contiguous); slab columns past cw are zero.
-        const int mt = (int)((p.n + 255) / 256);
         auto launch = [&](auto bn_tag) {
           constexpr int BN = decltype(bn_tag)::value;
           GemmPipeArgs<true, false, BN> gb;
@@ -976,14 +982,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
           gb.N = p.d;
           gb.K = cpad;
           gb.accumulate = (accumulate || c > 0) ? 1 : 0;
-          gb.n_mt = mt;
+          gb.n_mt = (int)((p.n + 255) / 256);
           gb.n_nt = (int)((p.d + BN - 1) / BN);
           return L.run(KD_KERNEL_GEMM_DH, [&] {
             gemm_pipe_kernel<true, false, BN>
                 <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), 512, 0, stream>>>(gb);
           });
         };
-        KD_TRY(launch(std::integral_constant<int, 128>{}));
+        KD_TRY(wide(p.n) ? launch(std::integral_constant<int, 256>{})
+                         : launch(std::integral_constant<int, 128>{}));
       }
     } else {
     if (dw) {

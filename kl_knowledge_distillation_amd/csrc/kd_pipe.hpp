@@ -224,15 +224,30 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
   return v;
 }
 
-// Row-contiguous fragment of rows [m0, m0 + 16) at k32 step kk: lane l gets
-// row l % 16 at k = 32 kk + 8 (l / 16) + e, e = 0..7 (the K-contiguous order).
-template <int R>
-__device__ __forceinline__ bf16x8 mn_frag(const uint8_t* tile, int m0, int kk, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int k = 32 * kk + 8 * g + (j >> 2);
-  const int m = m0 + 4 * (j & 3);
-  const uint2 lo = lds_read_tr16(tile + mn_offset<R>(k, m));
-  const uint2 hi = lds_read_tr16(tile + mn_offset<R>(k + 4, m));
+// Per-lane part of the transposed-read addresses of NF fragments of rows
+// [m_first + 16 f, m_first + 16 f + 16), f = 0 .. NF-1, at k32 step 0 of a
+// tile. Lane l = 16 g + 4 e + q reads k-row 8 g + e and rows m + 4 q; its
+// swizzle mn_swz(8 g + e) does not change with the k32 step (32 kk) or the
+// second half (+4), which only add a constant. Keeping one base per fragment
+// (instead of every final address) keeps the register count down.
+template <int R, int NF>
+struct MnLane {
+  uint32_t base[NF];
+  __device__ __forceinline__ void init(int m_first, int lane) {
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const int k = 8 * g + e;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) base[f] = (uint32_t)mn_offset<R>(k, m_first + 16 * f + 4 * q);
+  }
+};
+
+// Row-contiguous fragment f at k32 step kk: lane l gets row l % 16 at
+// k = 32 kk + 8 (l / 16) + e, e = 0..7 (the K-contiguous order).
+template <int R, int NF>
+__device__ __forceinline__ bf16x8 mn_frag(const uint8_t* tile, const MnLane<R, NF>& ml, int f, int kk) {
+  const uint8_t* p = tile + ml.base[f] + kk * 32 * (2 * R);
+  const uint2 lo = lds_read_tr16(p);
+  const uint2 hi = lds_read_tr16(p + 4 * (2 * R));
   return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
@@ -243,25 +258,35 @@ struct PipeFrags {
   bf16x8 b[2][NB][C::NBK];
 };
 
+// Transposed-read lane bases of this wave's A and B fragments (unused for
+// K-contiguous operands).
+template <class C>
+struct PipeLanes {
+  MnLane<C::kABytes / 128, C::MB> a;
+  MnLane<C::kBBytes / 128, C::NBK> b;
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    if constexpr (!C::kAKC) a.init(wm * C::TM, lane);
+    if constexpr (!C::kBKC) b.init(wn * C::TN, lane);
+  }
+};
+
 template <class C, int NB>
-__device__ __forceinline__ void pipe_read(const uint8_t* stage, PipeFrags<C, NB>& f, int wm, int wn,
-                                          int lane) {
+__device__ __forceinline__ void pipe_read(const uint8_t* stage, PipeFrags<C, NB>& f, const PipeLanes<C>& pl,
+                                          int wm, int wn, int lane) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
-      const int row0 = wm * C::TM + mb * 16;
-      if constexpr (C::kAKC) f.a[kk][mb] = kc_frag(stage, row0, kk, lane);
-      else f.a[kk][mb] = mn_frag<C::kABytes / 128>(stage, row0, kk, lane);
+      if constexpr (C::kAKC) f.a[kk][mb] = kc_frag(stage, wm * C::TM + mb * 16, kk, lane);
+      else f.a[kk][mb] = mn_frag(stage, pl.a, mb, kk);
     }
 #pragma unroll
     for (int g = 0; g < NB; ++g)
 #pragma unroll
       for (int nb = 0; nb < C::NBK; ++nb) {
         const uint8_t* tile = stage + C::kABytes + g * C::kBBytes;
-        const int row0 = wn * C::TN + nb * 16;
-        if constexpr (C::kBKC) f.b[kk][g][nb] = kc_frag(tile, row0, kk, lane);
-        else f.b[kk][g][nb] = mn_frag<C::kBBytes / 128>(tile, row0, kk, lane);
+        if constexpr (C::kBKC) f.b[kk][g][nb] = kc_frag(tile, wn * C::TN + nb * 16, kk, lane);
+        else f.b[kk][g][nb] = mn_frag(tile, pl.b, nb, kk);
       }
   }
 }
@@ -345,16 +370,18 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
 
   const int nk = (int)(K / kPipeBK);
   PipeFrags<C, NB> f;
+  PipeLanes<C> pl;
+  pl.init(wm, wn, lane);
   if (!grp_b) {
     pipe_barrier();  // pairs with the prologue barrier of group B: step 0 visible
-    pipe_read<C, NB>(lds, f, wm, wn, lane);
+    pipe_read<C, NB>(lds, f, pl, wm, wn, lane);
     for (int i = 0; i < nk; ++i) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments of step i ready
       __builtin_amdgcn_s_setprio(1);
       pipe_mma<C, NB>(f, acc);
       __builtin_amdgcn_s_setprio(0);
       pipe_barrier();  // 1: step i+1 has landed
-      if (i + 1 < nk) pipe_read<C, NB>(lds + ((i + 1) & 1) * C::kStageBytes, f, wm, wn, lane);
+      if (i + 1 < nk) pipe_read<C, NB>(lds + ((i + 1) & 1) * C::kStageBytes, f, pl, wm, wn, lane);
       pipe_barrier();  // 2
     }
   } else {
@@ -379,7 +406,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     // branch-free loop bodies.
     int i = 0;
     for (; i + 2 < nk; ++i) {
-      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, wm, wn, lane);
+      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, pl, wm, wn, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step i done
       wait_vmcnt<0>();                                       // step i+1 has landed
       pipe_barrier();  // 1
@@ -391,7 +418,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
       pipe_barrier();  // 2
     }
     for (; i < nk; ++i) {
-      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, wm, wn, lane);
+      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, pl, wm, wn, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       wait_vmcnt<0>();
       pipe_barrier();  // 1

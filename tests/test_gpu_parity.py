@@ -160,3 +160,11 @@ def test_teacher_ce_on_request_at_temperature_2(want):
         assert_tokens(to_np(r.teacher_ce), ref["teacher_ce"], "bf16", "teacher_ce")
     else:
         assert torch.count_nonzero(r.teacher_ce).item() == 0
+
+
+@pytest.mark.parametrize("shape", [dict(n=8192, d=2048, v=1000), dict(n=256, d=8192, v=8192)],
+                         ids=["wide_dh", "wide_dw"])
+def test_wide_gemm_tiles(shape):
+    """Shapes where the dH (first) or dW (second) GEMM has enough 256x256 tiles to
+    use them, so both GEMM tile widths are checked against the oracle."""
+    full_parity(C2.scaled(name="quickstart_" + "_".join(f"{k}{v}" for k, v in shape.items()), **shape))
