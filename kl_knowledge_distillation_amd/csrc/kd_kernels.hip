@@ -77,55 +77,50 @@ __device__ __forceinline__ void stats_merge(RowStats& s, const RowStats& o) {
 // Bit 4 mb + r of `ok`: register r of row block mb is a real vocabulary row.
 __device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int r) { return (ok >> (mb * 4 + r)) & 1u; }
 
-// Folds the 16 values a lane holds for token block nb into (m, s) at scale c.
+// Largest of the 16 values a lane holds for token block nb (masked rows skipped).
 template <bool TAIL>
-__device__ __forceinline__ void online_ms(float& m, float& s, const WaveAcc& x, int nb, float c,
-                                          uint32_t ok) {
-  float bm = -INFINITY;
+__device__ __forceinline__ float tile_max(const WaveAcc& x, int nb, uint32_t ok) {
+  float m = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (!TAIL || ok_bit(ok, mb, r)) bm = fmaxf(bm, x[mb][nb][r]);
-  const float mn = fmaxf(m, bm * c);
-  const float sc = rescale(m, mn);
-  float acc0 = 0.f, acc1 = 0.f;
+      if (!TAIL || ok_bit(ok, mb, r)) m = fmaxf(m, x[mb][nb][r]);
+  return m;
+}
+
+// sum over the lane's 16 values of 2^(x c - mc); mc = c * (token max), so every
+// term is at most 1 and all partial sums of a token share one reference.
+template <bool TAIL>
+__device__ __forceinline__ float tile_sum(const WaveAcc& x, int nb, float c, float mc, uint32_t ok) {
+  float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mn));
-      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mn));
+      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mc));
+      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mc));
       if (TAIL) {
         e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
         e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
       }
-      acc0 += e0;
-      acc1 += e1;
+      s0 += e0;
+      s1 += e1;
     }
-  s = s * sc + (acc0 + acc1);
-  m = mn;
+  return s0 + s1;
 }
 
-// Teacher statistics at scale c plus the cross term sum 2^(t c - m) (t - z).
+// Teacher sum at scale c and the cross term sum 2^(t c - mc) (t - z).
 template <bool TAIL>
-__device__ __forceinline__ void online_msa(float& m, float& s, float& a, const WaveAcc& t,
-                                           const WaveAcc& z, int nb, float c, uint32_t ok) {
-  float bm = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (!TAIL || ok_bit(ok, mb, r)) bm = fmaxf(bm, t[mb][nb][r]);
-  const float mn = fmaxf(m, bm * c);
-  const float sc = rescale(m, mn);
+__device__ __forceinline__ void tile_sum_cross(const WaveAcc& t, const WaveAcc& z, int nb, float c, float mc,
+                                               uint32_t ok, float& s, float& a) {
   float s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e0 = exp2_fast(fmaf(t[mb][nb][r], c, -mn));
-      float e1 = exp2_fast(fmaf(t[mb + 1][nb][r], c, -mn));
+      float e0 = exp2_fast(fmaf(t[mb][nb][r], c, -mc));
+      float e1 = exp2_fast(fmaf(t[mb + 1][nb][r], c, -mc));
       if (TAIL) {
         e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
         e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
@@ -135,22 +130,8 @@ __device__ __forceinline__ void online_msa(float& m, float& s, float& a, const W
       a0 = fmaf(e0, t[mb][nb][r] - z[mb][nb][r], a0);
       a1 = fmaf(e1, t[mb + 1][nb][r] - z[mb + 1][nb][r], a1);
     }
-  s = s * sc + (s0 + s1);
-  a = a * sc + (a0 + a1);
-  m = mn;
-}
-
-template <int MODE, bool TAIL>
-__device__ __forceinline__ void fwd_update(const WaveAcc& z, const WaveAcc& t, RowStats (&st)[kNB],
-                                           float cT, bool need_zT, bool need_t1, uint32_t ok) {
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    online_ms<TAIL>(st[nb].mz1, st[nb].sz1, z, nb, kLog2e, ok);
-    if (MODE == MODE_TOPK) continue;
-    if (need_zT) online_ms<TAIL>(st[nb].mzT, st[nb].szT, z, nb, cT, ok);
-    online_msa<TAIL>(st[nb].mtT, st[nb].stT, st[nb].a, t, z, nb, cT, ok);
-    if (need_t1) online_ms<TAIL>(st[nb].mt1, st[nb].st1, t, nb, kLog2e, ok);
-  }
+  s = s0 + s1;
+  a = a0 + a1;
 }
 
 // ---------------------------------------------------------------------------
@@ -261,9 +242,12 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     }
   }
 
-  RowStats st[kNB];  // one per token block nb of this lane
-#pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) stats_init(st[nb]);
+  // Epilogue: this tile's statistics of every token, in two passes over the
+  // registers. (1) Token maxima of z and t over the tile's vocabulary rows:
+  // lane maxima, then the four lanes l % 16 + 16 q, then the kWM waves of the
+  // token block (LDS). (2) Sums of 2^(x c - c max) against those maxima, so the
+  // partial sums of lanes and waves simply add. The main loop ended with a
+  // barrier, so its LDS is free.
   uint32_t ok = 0xffffu;
   const bool tail = v0 + G::kVT > a.v;
   if (tail) {
@@ -274,74 +258,95 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       for (int r = 0; r < 4; ++r)
         if (v0 + acc_row(wm, mb, r, lane) < a.v) ok |= 1u << (mb * 4 + r);
   }
-  if constexpr (MODE == MODE_TIED) {
-    if (tail) fwd_update<MODE, true>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
-    else fwd_update<MODE, false>(acc[0], acc[1], st, a.cT, a.need_zT, a.need_t1, ok);
-  } else if constexpr (MODE == MODE_SEPARATE) {
-    if (tail) fwd_update<MODE, true>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-    else fwd_update<MODE, false>(acc[0], tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-  } else if constexpr (MODE == MODE_TOPK) {
-    if (tail) fwd_update<MODE, true>(acc[0], acc[0], st, a.cT, false, false, ok);
-    else fwd_update<MODE, false>(acc[0], acc[0], st, a.cT, false, false, ok);
-  } else {
-    if (tail) fwd_update<MODE, true>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-    else fwd_update<MODE, false>(zl, tacc[0], st, a.cT, a.need_zT, a.need_t1, ok);
-  }
+  const WaveAcc& z = (MODE == MODE_LOGITS) ? zl : acc[0];
+  const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  constexpr bool kTeacher = MODE != MODE_TOPK;
+  constexpr int kSums = 5;  // sz1, szT, stT, a, st1
+  float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNB][2][16]
+  float* xsum = xmax + G::kWM * 2 * kNB * 2 * 16;                 // [kWM][2][kNB][kSums][16]
+  const int l16 = lane & 15;
 
-  // Combine the four lanes l % 16 + 16 q (same token, different vocabulary rows).
+  float mz[kNB], mt[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
+    mz[nb] = tail ? tile_max<true>(z, nb, ok) : tile_max<false>(z, nb, ok);
+    mt[nb] = !kTeacher ? 0.f : (tail ? tile_max<true>(tl, nb, ok) : tile_max<false>(tl, nb, ok));
 #pragma unroll
     for (int off = 16; off <= 32; off *= 2) {
-      RowStats o;
-      o.mz1 = __shfl_xor(st[nb].mz1, off);
-      o.sz1 = __shfl_xor(st[nb].sz1, off);
-      o.mzT = __shfl_xor(st[nb].mzT, off);
-      o.szT = __shfl_xor(st[nb].szT, off);
-      o.mtT = __shfl_xor(st[nb].mtT, off);
-      o.stT = __shfl_xor(st[nb].stT, off);
-      o.a = __shfl_xor(st[nb].a, off);
-      o.mt1 = __shfl_xor(st[nb].mt1, off);
-      o.st1 = __shfl_xor(st[nb].st1, off);
-      stats_merge(st[nb], o);
+      mz[nb] = fmaxf(mz[nb], __shfl_xor(mz[nb], off));
+      if (kTeacher) mt[nb] = fmaxf(mt[nb], __shfl_xor(mt[nb], off));
+    }
+    if (lane < 16) {
+      float* p = xmax + (((wm * 2 + wn) * kNB + nb) * 2) * 16 + l16;
+      p[0] = mz[nb];
+      p[16] = mt[nb];
     }
   }
-  // Combine the kWM waves that share a token block (same wn, different vocabulary
-  // rows), in the fixed order wm = 1, 2, ... The main loop ended with a barrier,
-  // so its LDS is free.
-  float* xs = reinterpret_cast<float*>(lds);
-  const int l16 = lane & 15;
-  if (wm > 0 && lane < 16) {
+  __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      float* p = xs + ((((wm - 1) * 2 + wn) * kNB + nb) * kRecFields) * 16 + l16;
-      const RowStats& s = st[nb];
-      p[0 * 16] = s.mz1; p[1 * 16] = s.sz1; p[2 * 16] = s.mzT; p[3 * 16] = s.szT;
-      p[4 * 16] = s.mtT; p[5 * 16] = s.stT; p[6 * 16] = s.a;   p[7 * 16] = s.mt1;
-      p[8 * 16] = s.st1;
+  for (int nb = 0; nb < kNB; ++nb) {
+    // every wave reads the same kWM values (fmax is exact, so the order is free)
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int src = 0; src < G::kWM; ++src) {
+      const float* p = xmax + (((src * 2 + wn) * kNB + nb) * 2) * 16 + l16;
+      m0 = fmaxf(m0, p[0]);
+      m1 = fmaxf(m1, p[16]);
+    }
+    mz[nb] = m0;
+    mt[nb] = m1;
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    const float mz1 = mz[nb] * kLog2e, mzT = mz[nb] * a.cT;
+    const float mtT = mt[nb] * a.cT, mt1 = mt[nb] * kLog2e;
+    if (tail) {
+      v[0] = tile_sum<true>(z, nb, kLog2e, mz1, ok);
+      if (kTeacher) {
+        if (a.need_zT) v[1] = tile_sum<true>(z, nb, a.cT, mzT, ok);
+        tile_sum_cross<true>(tl, z, nb, a.cT, mtT, ok, v[2], v[3]);
+        if (a.need_t1) v[4] = tile_sum<true>(tl, nb, kLog2e, mt1, ok);
+      }
+    } else {
+      v[0] = tile_sum<false>(z, nb, kLog2e, mz1, ok);
+      if (kTeacher) {
+        if (a.need_zT) v[1] = tile_sum<false>(z, nb, a.cT, mzT, ok);
+        tile_sum_cross<false>(tl, z, nb, a.cT, mtT, ok, v[2], v[3]);
+        if (a.need_t1) v[4] = tile_sum<false>(tl, nb, kLog2e, mt1, ok);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSums; ++j) {
+      v[j] += __shfl_xor(v[j], 16);
+      v[j] += __shfl_xor(v[j], 32);
+    }
+    if (lane < 16) {
+      float* p = xsum + (((wm * 2 + wn) * kNB + nb) * kSums) * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < kSums; ++j) p[j * 16] = v[j];
     }
   }
   __syncthreads();
   if (wm == 0 && lane < 16) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
+      float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int src = 1; src < G::kWM; ++src) {
-        const float* p = xs + ((((src - 1) * 2 + wn) * kNB + nb) * kRecFields) * 16 + l16;
-        RowStats o;
-        o.mz1 = p[0 * 16]; o.sz1 = p[1 * 16]; o.mzT = p[2 * 16]; o.szT = p[3 * 16];
-        o.mtT = p[4 * 16]; o.stT = p[5 * 16]; o.a = p[6 * 16];   o.mt1 = p[7 * 16];
-        o.st1 = p[8 * 16];
-        stats_merge(st[nb], o);
+      for (int src = 0; src < G::kWM; ++src) {  // fixed order
+        const float* p = xsum + (((src * 2 + wn) * kNB + nb) * kSums) * 16 + l16;
+#pragma unroll
+        for (int j = 0; j < kSums; ++j) v[j] += p[j * 16];
       }
       const int64_t tok = t0 + acc_col(wn, nb, lane);
       if (tok < a.n) {
         const int64_t stride = (int64_t)a.n_slices * a.n;
         float* r = a.rec + (int64_t)slice * a.n + tok;
-        const RowStats& s = st[nb];
-        r[0 * stride] = s.mz1; r[1 * stride] = s.sz1; r[2 * stride] = s.mzT;
-        r[3 * stride] = s.szT; r[4 * stride] = s.mtT; r[5 * stride] = s.stT;
-        r[6 * stride] = s.a;   r[7 * stride] = s.mt1; r[8 * stride] = s.st1;
+        r[0 * stride] = mz[nb] * kLog2e; r[1 * stride] = v[0];
+        r[2 * stride] = mz[nb] * a.cT;   r[3 * stride] = v[1];
+        r[4 * stride] = mt[nb] * a.cT;   r[5 * stride] = v[2];
+        r[6 * stride] = v[3];
+        r[7 * stride] = mt[nb] * kLog2e; r[8 * stride] = v[4];
       }
     }
   }
