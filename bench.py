@@ -64,12 +64,19 @@ def kernel_flops_per_launch(w, kernel: str, chunk: int) -> float:
 
 
 def source_digest() -> str:
+    """Hash of the kernel sources with comments and blank lines removed, so a
+    counter summary stays valid across edits that do not change the code."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kl_knowledge_distillation_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode())
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(f.encode())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 
@@ -86,6 +93,70 @@ def traffic_for(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+_KERNEL_CLASS = (("prep_kernel", "prep"), ("fwd_tiles_kernel", "fwd"), ("merge_kernel", "merge"),
+                 ("finalize_kernel", "finalize"), ("bwd_dz_kernel", "bwd_dz"),
+                 ("scatter_kernel", "scatter"), ("gemm_pipe_kernel<false, false", "gemm_dw"),
+                 ("gemm_pipe_kernel<true, false", "gemm_dh"), ("gemm_kernel<float, false, false", "gemm_dw"),
+                 ("gemm_kernel<unsigned short, false, false", "gemm_dw"),
+                 ("gemm_kernel<float, true, false", "gemm_dh"),
+                 ("gemm_kernel<unsigned short, true, false", "gemm_dh"))
+
+
+def _counter_per_dispatch(path: str, counter: str):
+    """{dispatch id: (kernel name, counter summed over its instances)} from a
+    rocprofv3 --pmc CSV (run_counter_collection.csv)."""
+    import csv
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, val = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, val + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_from(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, commands) -> dict:
+    """HBM bytes per launch of each kernel class from FETCH_SIZE / WRITE_SIZE runs.
+
+    Both counters read KiB per dispatch. Each is scaled by calib / reading of the
+    largest buffer-copy dispatch, the calib_mib device-to-device copy the
+    profiled bench run makes before its timed steps (a plain copy reads and
+    writes exactly that many bytes)."""
+    res = {}
+    for key, path, ctr in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        per = _counter_per_dispatch(path, ctr)
+        copies = [v for name, v in per.values() if "copyBuffer" in name]
+        if not copies:
+            raise SystemExit(f"no buffer-copy dispatch in {path}")
+        factor = (calib_mib * 1024.0) / max(copies)
+        cls = {}
+        for name, v in per.values():
+            for pat, c in _KERNEL_CLASS:
+                if pat in name:
+                    cls.setdefault(c, []).append(v * factor * 1024.0)
+                    break
+        res[key] = (factor, cls)
+    digest = source_digest()
+    written = {}
+    for c in res["fetch"][1]:
+        f = res["fetch"][1][c]
+        wv = res["write"][1].get(c, [0.0])
+        fb, wb = sum(f) / len(f), sum(wv) / len(wv)
+        rec = {"kernel": c, "workload": workload, "source_digest": digest,
+               "hbm_bytes_per_launch": round(fb + wb), "fetch_bytes_per_launch": round(fb),
+               "write_bytes_per_launch": round(wb), "dispatches": len(f),
+               "fetch_factor": round(res["fetch"][0], 4), "write_factor": round(res["write"][0], 4),
+               "calib_copy_mib": calib_mib, "commands": list(commands)}
+        path = os.path.join(ROOT, "profiles", f"traffic_{c}_{workload}.json")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        written[c] = rec
+    return written
+
+
 def cpu_baseline(w, target_s: float = 12.0) -> dict:
     """The float64 oracle (as it stands) on a bounded row sample of the workload."""
     import numpy as np
@@ -100,7 +171,7 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
 
-    cap = min(w.n, 2048)
+    cap = w.n
     x = make_inputs(w.scaled(n=cap), "cpu", seed=0)
     f = lambda t: None if t is None else t.float().numpy().astype(np.float64)  # noqa: E731
     full = {k: f(v) if k not in ("labels", "topk_idx") else (None if v is None else v.numpy())
@@ -146,7 +217,25 @@ def main() -> int:
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="copy a buffer of this many MiB once before the timed steps, so a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known transfer")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 counter CSVs of this bench (FETCH_SIZE, "
+                         "WRITE_SIZE, both with --calib-copy-mib) into profiles/traffic_*.json")
+    ap.add_argument("--traffic-commands", nargs="*", default=[],
+                    help="the commands that produced the CSVs, recorded with the numbers")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        name = args.workload
+        over = [f"{k}{getattr(args, k)}" for k in ("n", "d", "v") if getattr(args, k)]
+        if over:
+            name = name + "_" + "_".join(over)
+        out = traffic_from(args.traffic_from[0], args.traffic_from[1], args.calib_copy_mib or 1024,
+                           name, args.traffic_commands)
+        for c, rec in sorted(out.items()):
+            print(f"{c:10s} {rec['hbm_bytes_per_launch'] / 1e6:10.1f} MB/launch "
+                  f"(fetch {rec['fetch_bytes_per_launch'] / 1e6:.1f}, write "
+                  f"{rec['write_bytes_per_launch'] / 1e6:.1f}, {rec['dispatches']} dispatches)")
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -118,7 +118,8 @@ typedef struct {
   int64_t ignore_index;      /* label value excluded from CE and from the loss */
   int32_t reduction;         /* KD_REDUCE_* */
   float normalizer;          /* > 0: divide the summed loss by it (num_batch_labels) */
-  int64_t vocab_chunk;       /* vocabulary columns per streaming step; 0 = library default */
+  int64_t vocab_chunk;       /* vocabulary columns per backward chunk, rounded up to whole tiles;
+                                the dz slab holds n x chunk; 0 = library default (8192) */
   int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
 } kd_params;
 
@@ -141,7 +142,7 @@ typedef struct {
 enum {
   KD_KERNEL_PREP = 0,      /* label logits, validity, top-K sums */
   KD_KERNEL_FWD = 1,       /* forward projection tiles + online-softmax epilogue */
-  KD_KERNEL_MERGE = 2,     /* per-token merge of vocabulary-slice records */
+  KD_KERNEL_MERGE = 2,     /* per-token merge of the vocabulary-tile records */
   KD_KERNEL_FINALIZE = 3,  /* loss reduction */
   KD_KERNEL_BWD_DZ = 4,    /* backward recompute tiles + logit-gradient epilogue */
   KD_KERNEL_SCATTER = 5,   /* top-K: subtract p at the cached indices */

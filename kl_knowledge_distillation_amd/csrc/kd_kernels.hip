@@ -4,16 +4,16 @@
 //   prep      one wave per token: label logits z[y], t[y] by a D-long dot
 //             product, validity flags; top-K: M = sum p, E = sum p log p and
 //             S = sum p z[idx] from the cached entries.
-//   fwd       grid = (vocabulary slice) x (128-token tile). For each 128-row
-//             vocabulary tile of its slice a workgroup runs the MFMA main loop
-//             (logit tiles z = W H_s^T and t = W H_t^T or W_t H_t^T) and folds
-//             the tile into per-token online statistics held in registers:
-//             running max and rescaled sum of 2^(x log2e / T) for z, z/T, t/T,
-//             t, and the cross term sum 2^(t~ - m) (t - z). The logits never
-//             leave registers (flash_kd, module description: online softmax).
-//   merge     one thread per token combines the slice records into lse values,
-//             per-token CE / KL / top-K objective, the saved statistics and a
-//             per-block partial loss.
+//   fwd       grid = (vocabulary tile) x (128-token tile). A workgroup runs the
+//             MFMA main loop (logit tiles z = W H_s^T and t = W H_t^T or
+//             W_t H_t^T) and reduces its tile to per-token statistics: the
+//             tile maxima of z and t, the sums of 2^(x log2e / T - max) for z,
+//             z/T, t/T, t, and the cross term sum 2^(t~ - m) (t - z). The
+//             logits never leave registers (flash_kd, module description:
+//             online softmax over vocabulary chunks is exact).
+//   merge     combines the per-tile records of each token (the online-softmax
+//             merge) into lse values, per-token CE / KL / top-K objective, the
+//             saved statistics and a per-block partial loss.
 //   finalize  one workgroup sums the partials in a fixed order.
 // Backward (kd_loss_bwd), per vocabulary chunk (CompactifAI/Full-Chunked-KL-
 // Loss, Full Chunked KL: recompute each chunk, apply the closed-form gradient):
