@@ -34,6 +34,10 @@ Readings of points the pages leave open (each is also listed in the design doc):
   R7  top-K indices are int32, probabilities fp32; M is the sum of the stored p.
   R8  0 * log 0 = 0 in the teacher-entropy term.
   R10 top-K mode has no labels: every row is valid, there is no CE.
+  R17 "reverse" KL(P_S || P_T) and "jeffreys" KL(P_T || P_S) + KL(P_S || P_T)
+      take the same 1/T on both logits and the same T**2 factor as "forward".
+  R18 the cached top-K teacher supports "forward" only (its distribution is
+      zero off the support, so KL(P_S || P_T) is not finite).
   --  a label outside [0, V) that is not ignore_index is treated as ignored.
 
 Parity pins for every function live in tests/test_oracle.py (closed forms,
@@ -70,6 +74,7 @@ class Params:
     ignore_index: int = -100
     reduction: str = "mean"  # "mean" | "sum"
     normalizer: float = 0.0
+    kl_divergence: str = "forward"  # "forward" | "reverse" | "jeffreys"
 
 
 # ---------------------------------------------------------------------------
@@ -142,6 +147,31 @@ def forward_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float)
     return (T * T) * (np.exp(lp_t) * (lp_t - lp_s)).sum(axis=-1)
 
 
+def reverse_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
+    """Per-token T**2 * KL(P_S || P_T) with P = softmax(logits / T).
+
+    orda-kernel, KL variants: p = student, q = teacher, "reverse" is KL(p || q);
+    the temperature convention is the forward one (reading R17).
+    """
+    lp_s = log_softmax(student_logits / T)
+    lp_t = log_softmax(teacher_logits / T)
+    return (T * T) * (np.exp(lp_s) * (lp_s - lp_t)).sum(axis=-1)
+
+
+def kl_term(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
+            variant: str = "forward") -> np.ndarray:
+    """The per-token KL of the selected variant (orda-kernel, KL variants):
+    forward KL(q || p), reverse KL(p || q), jeffreys KL(q || p) + KL(p || q)."""
+    if variant == "forward":
+        return forward_kl(student_logits, teacher_logits, T)
+    if variant == "reverse":
+        return reverse_kl(student_logits, teacher_logits, T)
+    if variant == "jeffreys":
+        return (forward_kl(student_logits, teacher_logits, T)
+                + reverse_kl(student_logits, teacher_logits, T))
+    raise ValueError(f"unknown kl_divergence {variant!r}")
+
+
 def topk_kl(student_logits: np.ndarray, idx, prob) -> np.ndarray:
     """Sparse forward KL against cached top-K teacher probabilities.
 
@@ -175,6 +205,32 @@ def dce_dlogits(logits: np.ndarray, labels, valid: np.ndarray) -> np.ndarray:
 def dkl_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
     """d (T**2 KL(P_T || P_S)) / d z = T * (softmax(z/T) - softmax(t/T))."""
     return T * (softmax(student_logits / T) - softmax(teacher_logits / T))
+
+
+def dreverse_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
+    """d (T**2 KL(P_S || P_T)) / d z = T * P_S * (log P_S - log P_T - KL(P_S || P_T)).
+
+    From d log P_S,v / d z_j = (delta_vj - P_S,j) / T: the T**2 and the 1/T of
+    the softmax leave T, and the terms from differentiating log P_S sum to zero.
+    """
+    lp_s = log_softmax(student_logits / T)
+    lp_t = log_softmax(teacher_logits / T)
+    p = np.exp(lp_s)
+    kl = (p * (lp_s - lp_t)).sum(axis=-1, keepdims=True)
+    return T * p * (lp_s - lp_t - kl)
+
+
+def dkl_term(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
+             variant: str = "forward") -> np.ndarray:
+    """Gradient of kl_term with respect to the student logits."""
+    if variant == "forward":
+        return dkl_dstudent(student_logits, teacher_logits, T)
+    if variant == "reverse":
+        return dreverse_dstudent(student_logits, teacher_logits, T)
+    if variant == "jeffreys":
+        return (dkl_dstudent(student_logits, teacher_logits, T)
+                + dreverse_dstudent(student_logits, teacher_logits, T))
+    raise ValueError(f"unknown kl_divergence {variant!r}")
 
 
 def dtopk_dstudent(student_logits: np.ndarray, idx, prob) -> np.ndarray:
@@ -270,12 +326,14 @@ def per_token(student: Student, teacher: Teacher, p: Params, labels=None,
         if labels is not None:
             out["student_ce"][b:b + len(r)] = cross_entropy(z, lab[r], vb)
         if teacher.kind == "topk":
+            if p.kl_divergence != "forward":
+                raise ValueError("the cached top-K teacher supports forward KL only (reading R18)")
             out["kl"][b:b + len(r)] = topk_kl(z, teacher.idx[r], teacher.prob[r])
             continue
         t = _teacher_logits(teacher, student, r)
         if labels is not None:
             out["teacher_ce"][b:b + len(r)] = cross_entropy(t, lab[r], vb)
-        out["kl"][b:b + len(r)] = forward_kl(z, t, p.temperature)
+        out["kl"][b:b + len(r)] = kl_term(z, t, p.temperature, p.kl_divergence)
     return out
 
 
@@ -332,13 +390,15 @@ def logit_grad(student: Student, teacher: Teacher, p: Params, labels, rows: np.n
         valid = valid_mask(lab, v, p.ignore_index)
     g = np.zeros_like(z)
     if teacher.kind == "topk":
+        if p.kl_divergence != "forward":
+            raise ValueError("the cached top-K teacher supports forward KL only (reading R18)")
         g += p.kl_weight * dtopk_dstudent(z, teacher.idx[rows], teacher.prob[rows])
     else:
         if lab is not None and p.student_ce_weight != 0.0:
             g += p.student_ce_weight * dce_dlogits(z, lab, valid)
         if p.kl_weight != 0.0:
             t = _teacher_logits(teacher, student, rows)
-            g += p.kl_weight * dkl_dstudent(z, t, p.temperature)
+            g += p.kl_weight * dkl_term(z, t, p.temperature, p.kl_divergence)
     g[~valid] = 0.0
     return g * (grad_loss / den)
 

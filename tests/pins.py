@@ -189,6 +189,66 @@ def check_kl_temperature_identity(O):
 # Sparse top-K objective (Full-Chunked-KL-Loss, Methods / Full Dense KL)
 # ---------------------------------------------------------------------------
 
+def check_reverse_kl_library(O):
+    """Reverse KL: T^2 * kl_div with the operands swapped (target = student),
+    summed over the vocabulary (orda-kernel, KL variants: reverse = KL(p || q),
+    p = student)."""
+    s, t = _tied_case(O, n=7, d=4, v=12, k=3)
+    z = torch.from_numpy(s.hidden @ s.weight.T)
+    tt = torch.from_numpy(t.hidden @ s.weight.T)
+    for T in (1.0, 2.0, 0.7):
+        p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T, kl_divergence="reverse")
+        ref = F.kl_div(F.log_softmax(tt / T, -1), F.log_softmax(z / T, -1), log_target=True,
+                       reduction="none").sum(-1) * T * T
+        _close(O.per_token(s, t, p)["kl"], ref.numpy(), rtol=1e-11, atol=1e-12,
+               what=f"reverse KL vs F.kl_div T={T}")
+
+
+def check_reverse_kl_two_classes(O):
+    """V = 2: closed-form Bernoulli KL(P_S || P_T) times T^2."""
+    r = _rng(9)
+    z = r.normal(size=(6, 2)) * 1.5
+    tl = r.normal(size=(6, 2)) * 1.5
+    T = 1.3
+    qs = 1.0 / (1.0 + np.exp(-(z[:, 1] - z[:, 0]) / T))
+    qt = 1.0 / (1.0 + np.exp(-(tl[:, 1] - tl[:, 0]) / T))
+    ref = T * T * (qs * np.log(qs / qt) + (1 - qs) * np.log((1 - qs) / (1 - qt)))
+    s = O.Student(hidden=z, weight=np.eye(2))
+    t = O.Teacher("separate", hidden=tl, weight=np.eye(2))
+    p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T, kl_divergence="reverse")
+    _close(O.per_token(s, t, p)["kl"], ref, rtol=1e-11, atol=1e-13, what="reverse Bernoulli")
+
+
+def check_jeffreys_symmetric(O):
+    """Jeffreys is symmetric: swapping the student and teacher logits leaves it
+    unchanged, while forward and reverse trade places; forward + reverse = it."""
+    r = _rng(11)
+    z = r.normal(size=(5, 9)) * 2.0
+    tl = r.normal(size=(5, 9)) * 2.0
+    eye = np.eye(9)
+    T = 1.6
+
+    def kl(a, b, variant):
+        p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=T, kl_divergence=variant)
+        return O.per_token(O.Student(hidden=a, weight=eye), O.Teacher("separate", hidden=b, weight=eye),
+                           p)["kl"]
+
+    _close(kl(z, tl, "jeffreys"), kl(tl, z, "jeffreys"), rtol=1e-12, what="jeffreys symmetric")
+    _close(kl(z, tl, "forward"), kl(tl, z, "reverse"), rtol=1e-12, what="forward/reverse swap")
+    _close(kl(z, tl, "jeffreys"), kl(z, tl, "forward") + kl(z, tl, "reverse"), rtol=1e-12,
+           what="jeffreys = forward + reverse")
+
+
+def check_reverse_zero_and_nonnegative(O):
+    """Reverse and Jeffreys KL are 0 for identical logits and > 0 otherwise (Gibbs)."""
+    for variant in ("reverse", "jeffreys"):
+        p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=1.9, kl_divergence=variant)
+        s, t = _tied_case(O, n=5, d=4, v=11, k=4, same=True)
+        _close(O.per_token(s, t, p)["kl"], 0.0, atol=1e-14, what=f"{variant} zero")
+        s, t = _tied_case(O, n=5, d=4, v=11, k=4)
+        assert (O.per_token(s, t, p)["kl"] > 0).all(), f"{variant} not positive"
+
+
 def _topk_case(n=6, v=15, k=4, seed=10, zero_one=True):
     r = _rng(seed)
     z = r.normal(size=(n, v)) * 1.5
@@ -324,6 +384,10 @@ def _fd_cases(O):
          O.Params(student_ce_weight=0.0, kl_weight=1.0)),
         ("sum", O.Teacher("tied", hidden=Ht), y,
          O.Params(student_ce_weight=1.0, kl_weight=0.5, temperature=0.8, reduction="sum")),
+        ("reverse", O.Teacher("tied", hidden=Ht), y,
+         O.Params(student_ce_weight=0.4, kl_weight=1.1, temperature=2.0, kl_divergence="reverse")),
+        ("jeffreys", O.Teacher("separate", hidden=Htt, weight=Wt), y,
+         O.Params(student_ce_weight=1.0, kl_weight=0.9, temperature=1.3, kl_divergence="jeffreys")),
     ], Hs, W
 
 
@@ -374,8 +438,10 @@ def check_grad_autograd_library(O):
         valid = yt != -100
         T = p.temperature
         ce = F.cross_entropy(z, yt, ignore_index=-100, reduction="none")
-        kl = F.kl_div(F.log_softmax(z / T, -1), F.log_softmax(tl / T, -1), log_target=True,
-                      reduction="none").sum(-1) * T * T
+        lp_s, lp_t = F.log_softmax(z / T, -1), F.log_softmax(tl / T, -1)
+        fwd = F.kl_div(lp_s, lp_t, log_target=True, reduction="none").sum(-1) * T * T
+        rev = F.kl_div(lp_t, lp_s, log_target=True, reduction="none").sum(-1) * T * T
+        kl = {"forward": fwd, "reverse": rev, "jeffreys": fwd + rev}[p.kl_divergence]
         total = (p.student_ce_weight * ce + p.kl_weight * kl)[valid].sum()
         den = float(valid.sum()) if p.reduction == "mean" else 1.0
         (total / den).backward()

@@ -18,9 +18,17 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
                    "oracle.py")
 
 MUTANTS = {
+    "reverse_as_forward": ("return (T * T) * (np.exp(lp_s) * (lp_s - lp_t)).sum(axis=-1)",
+                           "return (T * T) * (np.exp(lp_t) * (lp_t - lp_s)).sum(axis=-1)"),
+    "reverse_grad_missing_kl": ("return T * p * (lp_s - lp_t - kl)", "return T * p * (lp_s - lp_t)"),
+    "reverse_grad_missing_T": ("return T * p * (lp_s - lp_t - kl)", "return p * (lp_s - lp_t - kl)"),
+    "jeffreys_twice_forward": ("""        return (forward_kl(student_logits, teacher_logits, T)
+                + reverse_kl(student_logits, teacher_logits, T))""",
+                               """        return (forward_kl(student_logits, teacher_logits, T)
+                + forward_kl(student_logits, teacher_logits, T))"""),
     "kl_without_T2": ("return (T * T) * (np.exp(lp_t)", "return (np.exp(lp_t)"),
-    "kl_teacher_not_tempered": ("lp_t = log_softmax(teacher_logits / T)",
-                                "lp_t = log_softmax(teacher_logits)"),
+    "kl_teacher_not_tempered": ("lp_t = log_softmax(teacher_logits / T)\n    return (T * T) * (np.exp(lp_t)",
+                                "lp_t = log_softmax(teacher_logits)\n    return (T * T) * (np.exp(lp_t)"),
     "kl_reversed": ("(np.exp(lp_t) * (lp_t - lp_s))", "(np.exp(lp_s) * (lp_s - lp_t))"),
     "ce_label_off_by_one": ("picked = np.take_along_axis(logits, y[:, None], axis=1)",
                             "picked = np.take_along_axis(logits, (y[:, None] + 1) % logits.shape[1], axis=1)"),
