@@ -66,10 +66,10 @@ enum {
   KD_ERR_NULL = 1,         /* a required pointer is NULL */
   KD_ERR_SHAPE = 2,        /* n, d, v, d_t or k out of range, or inconsistent */
   KD_ERR_DTYPE = 3,        /* unknown dtype, or a mode that does not accept it */
-  KD_ERR_PARAM = 4,        /* temperature/weights not finite or not allowed, bad reduction */
+  KD_ERR_PARAM = 4,        /* temperature/weights not finite or not allowed, bad reduction or KL variant */
   KD_ERR_ALIGN = 5,        /* a pointer not 16-byte aligned, or d / d_t not a multiple of 8 */
   KD_ERR_WORKSPACE = 6,    /* workspace smaller than kd_workspace_bytes, or saved missing */
-  KD_ERR_UNSUPPORTED = 7,  /* valid but not provided (e.g. backward of the logits scorer) */
+  KD_ERR_UNSUPPORTED = 7,  /* valid but not provided (backward of the logits scorer, a non-forward KL with a TOPK teacher) */
   KD_ERR_LABEL_RANGE = 8,  /* device flag: a label or top-K index was out of range */
   KD_ERR_HIP = 9           /* a HIP launch or runtime call failed */
 };
@@ -88,6 +88,13 @@ enum { KD_TEACHER_TIED = 1, KD_TEACHER_SEPARATE = 2, KD_TEACHER_TOPK = 3 };
 /* Loss reduction (orda-kernel, Parameters: reduction). NONE produces the
  * per-token outputs and the sum in `loss`; it has no backward. */
 enum { KD_REDUCE_MEAN = 0, KD_REDUCE_SUM = 1, KD_REDUCE_NONE = 2 };
+
+/* KL variant of the distillation term (orda-kernel, KL variants; p = student,
+ * q = teacher, both softmax(logits / T)). FORWARD is KL(q || p), REVERSE
+ * KL(p || q), JEFFREYS their sum; the per-token value and the loss carry T^2,
+ * and the teacher is always detached. A TOPK teacher allows FORWARD only (its
+ * distribution is zero off the support). */
+enum { KD_KL_FORWARD = 0, KD_KL_REVERSE = 1, KD_KL_JEFFREYS = 2 };
 
 typedef struct {
   int32_t kind;        /* KD_STUDENT_* */
@@ -121,6 +128,7 @@ typedef struct {
   int64_t vocab_chunk;       /* vocabulary columns per backward chunk, rounded up to whole tiles;
                                 the dz slab holds n x chunk; 0 = library default (8192) */
   int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
+  int32_t kl_divergence;     /* KD_KL_* */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).

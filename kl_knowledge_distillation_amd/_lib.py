@@ -16,6 +16,7 @@ KD_F32, KD_BF16 = 0, 1
 KD_STUDENT_PROJECTION, KD_STUDENT_LOGITS = 0, 1
 KD_TEACHER_TIED, KD_TEACHER_SEPARATE, KD_TEACHER_TOPK = 1, 2, 3
 KD_REDUCE_MEAN, KD_REDUCE_SUM, KD_REDUCE_NONE = 0, 1, 2
+KD_KL_FORWARD, KD_KL_REVERSE, KD_KL_JEFFREYS = 0, 1, 2
 KERNELS = ["prep", "fwd", "merge", "finalize", "bwd_dz", "scatter", "gemm_dw", "gemm_dh"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
@@ -34,7 +35,7 @@ class KdParams(ctypes.Structure):
     _fields_ = [("student_ce_weight", c_float), ("teacher_ce_weight", c_float),
                 ("kl_weight", c_float), ("temperature", c_float), ("ignore_index", c_int64),
                 ("reduction", c_int32), ("normalizer", c_float), ("vocab_chunk", c_int64),
-                ("assume_valid_labels", c_int32)]
+                ("assume_valid_labels", c_int32), ("kl_divergence", c_int32)]
 
 
 class KdOutputs(ctypes.Structure):

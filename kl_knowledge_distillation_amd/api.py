@@ -84,6 +84,9 @@ def lib():
 
 _DTYPES = {torch.float32: L.KD_F32, torch.bfloat16: L.KD_BF16}
 _REDUCTIONS = {"mean": L.KD_REDUCE_MEAN, "sum": L.KD_REDUCE_SUM, "none": L.KD_REDUCE_NONE}
+# orda-kernel, KL variants: KL(P_T || P_S), KL(P_S || P_T) and their sum.
+_KL_DIVERGENCES = {"forward": L.KD_KL_FORWARD, "reverse": L.KD_KL_REVERSE,
+                   "jeffreys": L.KD_KL_JEFFREYS}
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -106,7 +109,7 @@ class Runner:
                  teacher_kind="tied", teacher_hidden=None, teacher_weight=None, topk_idx=None,
                  topk_prob=None, student_ce_weight=1.0, teacher_ce_weight=0.0, kl_weight=0.0,
                  temperature=1.0, ignore_index=-100, reduction="mean", normalizer=0.0,
-                 vocab_chunk=0, want_grads=True, want_teacher_ce=None):
+                 vocab_chunk=0, want_grads=True, want_teacher_ce=None, kl_divergence="forward"):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -162,6 +165,9 @@ class Runner:
         p.reduction = _REDUCTIONS[reduction]
         p.normalizer = float(normalizer or 0.0)
         p.vocab_chunk = int(vocab_chunk)
+        if kl_divergence not in _KL_DIVERGENCES:
+            raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
+        p.kl_divergence = _KL_DIVERGENCES[kl_divergence]
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
         f32 = dict(dtype=torch.float32, device=self.device)
@@ -290,9 +296,6 @@ class _FusedLoss(torch.autograd.Function):
         return dh, dw, None
 
 
-_KL_SUPPORTED = ("forward",)
-
-
 def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
                       teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
                       kl_divergence="forward", ignore_index=-100, reduction="mean",
@@ -306,9 +309,11 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
     (one exponential pass fewer per tile when the temperature is not 1) and
     reported as zeros.
     """
-    if kl_divergence not in _KL_SUPPORTED:
-        raise NotImplementedError(f"kl_divergence={kl_divergence!r}; available: {_KL_SUPPORTED}")
-    kw = dict(student_hidden=student_hidden.detach().contiguous(),
+    if kl_divergence not in _KL_DIVERGENCES:
+        raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
+    if isinstance(teacher, TopKTeacher) and kl_divergence != "forward":
+        raise NotImplementedError("the top-K teacher supports kl_divergence='forward' only")
+    kw = dict(kl_divergence=kl_divergence, student_hidden=student_hidden.detach().contiguous(),
               weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
               teacher_ce_weight=teacher_ce_weight, kl_weight=kl_weight,
               temperature=kl_temperature, ignore_index=ignore_index, reduction=reduction,

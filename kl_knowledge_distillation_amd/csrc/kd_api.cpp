@@ -85,10 +85,15 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
     return KD_ERR_PARAM;
   if (!isfinite(p->normalizer) || p->normalizer < 0.f) return KD_ERR_PARAM;
   if (p->vocab_chunk < 0) return KD_ERR_PARAM;
+  if (p->kl_divergence != KD_KL_FORWARD && p->kl_divergence != KD_KL_REVERSE &&
+      p->kl_divergence != KD_KL_JEFFREYS)
+    return KD_ERR_PARAM;
   if (backward && p->reduction == KD_REDUCE_NONE) return KD_ERR_UNSUPPORTED;
   if (q.mode == kd::MODE_TOPK) {
     // The cached teacher has no temperature and no labels (Full-Chunked-KL-Loss, Methods).
     if (p->temperature != 1.f) return KD_ERR_UNSUPPORTED;
+    // Its distribution is zero off the support: only KL(teacher || student) is finite.
+    if (p->kl_divergence != KD_KL_FORWARD) return KD_ERR_UNSUPPORTED;
     if (p->student_ce_weight != 0.f || p->teacher_ce_weight != 0.f) return KD_ERR_PARAM;
     if (check_labels_ptr && labels) return KD_ERR_PARAM;
   } else if (check_labels_ptr && !labels &&
@@ -104,7 +109,10 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.ignore = p->ignore_index;
   q.reduction = p->reduction;
   q.normalizer = p->normalizer;
-  q.need_zT = (q.T != 1.f) ? 1 : 0;
+  q.kl = p->kl_divergence;
+  // Student statistics at z/T: needed for the KL at T != 1, and always for the
+  // reverse direction, whose weights are the student's softmax(z/T).
+  q.need_zT = (q.T != 1.f || q.kl != KD_KL_FORWARD) ? 1 : 0;
   q.need_t1 = (q.T != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
   q.has_labels = labels ? 1 : 0;
 

@@ -12,8 +12,8 @@ namespace kd {
 
 enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3 };
 
-// Number of fp32 fields of one per-(token, vocabulary slice) record.
-constexpr int kRecFields = 9;
+// Number of fp32 fields of one per-(token, vocabulary tile) record.
+constexpr int kRecFields = 10;
 // Tokens per merge workgroup; also the number of partial sums per block.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTok = 16;  // tokens per merge workgroup
@@ -31,7 +31,8 @@ struct Plan {
   int64_t ignore = -100;
   int reduction = KD_REDUCE_MEAN;
   float normalizer = 0.f;
-  int need_zT = 0;    // T != 1: student statistics at z/T are kept apart from z
+  int kl = KD_KL_FORWARD;  // KD_KL_*
+  int need_zT = 0;    // statistics at z/T kept apart from z (T != 1, or a reverse-direction KL)
   int need_t1 = 0;    // teacher CE wanted at T != 1: teacher statistics at t
   int has_labels = 0;
   int pipe = 0;       // bf16 with hidden sizes multiple of 32: 256-row pipelined tiles

@@ -38,14 +38,14 @@ namespace kd {
 
 struct RowStats {
   float mz1, sz1;      // z at T = 1 (base-2 units of z log2e)
-  float mzT, szT;      // z / T
+  float mzT, szT, ar;  // z / T and the cross term sum 2^(z~ - mzT) (z - t) (reverse KL)
   float mtT, stT, a;   // t / T and the cross term sum 2^(t~ - mtT) (t - z)
   float mt1, st1;      // t at T = 1 (teacher CE when T != 1)
 };
 
 __device__ __forceinline__ void stats_init(RowStats& s) {
   s.mz1 = s.mzT = s.mtT = s.mt1 = -INFINITY;
-  s.sz1 = s.szT = s.stT = s.st1 = s.a = 0.f;
+  s.sz1 = s.szT = s.stT = s.st1 = s.a = s.ar = 0.f;
 }
 
 // 2^(m_old - m_new), with an empty record (m_new = -inf) scaling to 0.
@@ -69,7 +69,7 @@ __device__ __forceinline__ void merge_msa(float& m, float& s, float& a, float m2
 
 __device__ __forceinline__ void stats_merge(RowStats& s, const RowStats& o) {
   merge_ms(s.mz1, s.sz1, o.mz1, o.sz1);
-  merge_ms(s.mzT, s.szT, o.mzT, o.szT);
+  merge_msa(s.mzT, s.szT, s.ar, o.mzT, o.szT, o.ar);
   merge_msa(s.mtT, s.stT, s.a, o.mtT, o.stT, o.a);
   merge_ms(s.mt1, s.st1, o.mt1, o.st1);
 }
@@ -191,6 +191,7 @@ struct FwdArgs {
   int n_ttiles, n_vtiles, tps, n_slices;
   float cT;
   int need_zT, need_t1;
+  int kl;      // KD_KL_*: the reverse direction also needs sum 2^(z~ - m) (z - t)
   float* rec;  // [kRecFields][n_slices][n]
 };
 
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   const WaveAcc& z = (MODE == MODE_LOGITS) ? zl : acc[0];
   const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
   constexpr bool kTeacher = MODE != MODE_TOPK;
-  constexpr int kSums = 5;  // sz1, szT, stT, a, st1
+  constexpr int kSums = 6;  // sz1, szT, stT, a, st1, ar
   float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNB][2][16]
   float* xsum = xmax + G::kWM * 2 * kNB * 2 * 16;                 // [kWM][2][kNB][kSums][16]
   const int l16 = lane & 15;
@@ -298,20 +299,23 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   }
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
-    float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const bool rev = a.kl != KD_KL_FORWARD;
     const float mz1 = mz[nb] * kLog2e, mzT = mz[nb] * a.cT;
     const float mtT = mt[nb] * a.cT, mt1 = mt[nb] * kLog2e;
     if (tail) {
       v[0] = tile_sum<true>(z, nb, kLog2e, mz1, ok);
       if (kTeacher) {
-        if (a.need_zT) v[1] = tile_sum<true>(z, nb, a.cT, mzT, ok);
+        if (rev) tile_sum_cross<true>(z, tl, nb, a.cT, mzT, ok, v[1], v[5]);
+        else if (a.need_zT) v[1] = tile_sum<true>(z, nb, a.cT, mzT, ok);
         tile_sum_cross<true>(tl, z, nb, a.cT, mtT, ok, v[2], v[3]);
         if (a.need_t1) v[4] = tile_sum<true>(tl, nb, kLog2e, mt1, ok);
       }
     } else {
       v[0] = tile_sum<false>(z, nb, kLog2e, mz1, ok);
       if (kTeacher) {
-        if (a.need_zT) v[1] = tile_sum<false>(z, nb, a.cT, mzT, ok);
+        if (rev) tile_sum_cross<false>(z, tl, nb, a.cT, mzT, ok, v[1], v[5]);
+        else if (a.need_zT) v[1] = tile_sum<false>(z, nb, a.cT, mzT, ok);
         tile_sum_cross<false>(tl, z, nb, a.cT, mtT, ok, v[2], v[3]);
         if (a.need_t1) v[4] = tile_sum<false>(tl, nb, kLog2e, mt1, ok);
       }
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   if (wm == 0 && lane < 16) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f};
+      float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int src = 0; src < G::kWM; ++src) {  // fixed order
         const float* p = xsum + (((src * 2 + wn) * kNB + nb) * kSums) * 16 + l16;
@@ -347,6 +351,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
         r[4 * stride] = mt[nb] * a.cT;   r[5 * stride] = v[2];
         r[6 * stride] = v[3];
         r[7 * stride] = mt[nb] * kLog2e; r[8 * stride] = v[4];
+        r[9 * stride] = v[5];
       }
     }
   }
@@ -452,11 +457,12 @@ struct MergeArgs {
   int mode;
   float T;
   int need_zT, need_t1, teacher_ce;
+  int kl;             // KD_KL_*
   float ws, wt, wkl;
   float* out_sce;
   float* out_tce;
   float* out_kl;
-  float* saved;       // [n][4] or null
+  float* saved;       // [n][4] or null: lse(z), lse(z/T), lse(t/T), M (top-K) or KL(P_S||P_T)
   double* partials;   // [blocks][4]: loss sum, valid count, bad count, 0
 };
 
@@ -480,12 +486,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       o.mz1 = r[0 * stride]; o.sz1 = r[1 * stride]; o.mzT = r[2 * stride];
       o.szT = r[3 * stride]; o.mtT = r[4 * stride]; o.stT = r[5 * stride];
       o.a = r[6 * stride];   o.mt1 = r[7 * stride]; o.st1 = r[8 * stride];
+      o.ar = r[9 * stride];
       stats_merge(s, o);
     }
   }
   part[0][sg][tl] = s.mz1; part[1][sg][tl] = s.sz1; part[2][sg][tl] = s.mzT;
   part[3][sg][tl] = s.szT; part[4][sg][tl] = s.mtT; part[5][sg][tl] = s.stT;
   part[6][sg][tl] = s.a;   part[7][sg][tl] = s.mt1; part[8][sg][tl] = s.st1;
+  part[9][sg][tl] = s.ar;
   __syncthreads();
   if (sg == 0) {
     for (int q = 1; q < kGroups; ++q) {
@@ -493,6 +501,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       o.mz1 = part[0][q][tl]; o.sz1 = part[1][q][tl]; o.mzT = part[2][q][tl];
       o.szT = part[3][q][tl]; o.mtT = part[4][q][tl]; o.stT = part[5][q][tl];
       o.a = part[6][q][tl];   o.mt1 = part[7][q][tl]; o.st1 = part[8][q][tl];
+      o.ar = part[9][q][tl];
       stats_merge(s, o);
     }
     double contrib = 0.0, cnt = 0.0, bad = 0.0;
@@ -511,8 +520,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       } else {
         ltT = kLn2 * (s.mtT + log2f(s.stT));
         const float lt1 = a.need_t1 ? kLn2 * (s.mt1 + log2f(s.st1)) : ltT;
-        const float cross = s.a / (s.stT * a.T);  // E_{P_T}[(t - z) / T]
-        kl = a.T * a.T * (cross - ltT + lzT);
+        // KL(P_T || P_S) = E_{P_T}[(t - z) / T] - lse(t/T) + lse(z/T), and
+        // KL(P_S || P_T) = E_{P_S}[(z - t) / T] - lse(z/T) + lse(t/T)
+        // (orda-kernel, KL variants: forward, reverse, jeffreys = their sum).
+        const float kl_f = s.a / (s.stT * a.T) - ltT + lzT;
+        const float kl_r = (a.kl != KD_KL_FORWARD) ? s.ar / (s.szT * a.T) - lzT + ltT : 0.f;
+        kl = a.T * a.T * ((a.kl != KD_KL_REVERSE ? kl_f : 0.f) + kl_r);
+        mass = kl_r;  // the reverse-direction gradient needs this row's KL(P_S || P_T)
         valid = flag == 1.f;
         sce = valid ? lz1 - f0 : 0.f;
         tce = (valid && a.teacher_ce) ? lt1 - f1 : 0.f;
@@ -612,6 +626,7 @@ struct BwdArgs {
   const float* grad;      // device scalar or null
   float ws, wkl, T, cT;
   int need_zT;
+  int kl;                 // KD_KL_*
   int64_t c0;             // first vocabulary row of the chunk
   int n_vt, n_ttiles;     // tiles of the chunk
   void* dz;               // [dz_rows][ldz]
@@ -670,6 +685,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   const float g = a.grad ? *a.grad : 1.f;
   T* dz = static_cast<T*>(a.dz);
 
+  // The reverse-direction term is compiled only into the variant that uses it,
+  // so the forward-KL epilogue carries no extra arithmetic.
+  auto epilogue = [&](auto rev_tag) {
+  constexpr bool kRev = decltype(rev_tag)::value;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int64_t tok = t0 + acc_col(wn, nb, lane);
@@ -687,6 +706,12 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const float cs = coef * a.ws;            // student CE
     const float ck = coef * a.wkl * a.T;     // T^2 KL -> T (P_S - P_T)
     const float cm = coef * a.wkl * mass;    // top-K: M softmax(z)
+    // T^2 KL(P_S || P_T) -> T P_S (log P_S - log P_T - KL(P_S || P_T)); with
+    // log P_S - log P_T = (z - t) / T - lse(z/T) + lse(t/T) (natural logs).
+    const float ckf = (a.kl != KD_KL_REVERSE) ? ck : 0.f;
+    const float ckr = ck;
+    const float rev0 = sv.z - sv.y - mass;   // lse(t/T) - lse(z/T) - KL(P_S || P_T)
+    const float invT = 1.f / a.T;
     T* row = dz + tok * a.ldz + (v0 - a.c0);
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
@@ -702,15 +727,20 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
           dv = cm * p1;
         } else {
           dv = cs * (p1 - (vv == y ? 1.f : 0.f));
+          const float tt = tl[mb][nb][r];
           const float pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
-          const float pt = exp2_fast(fmaf(tl[mb][nb][r], a.cT, -LtT));
-          dv = fmaf(ck, pz - pt, dv);
+          const float pt = exp2_fast(fmaf(tt, a.cT, -LtT));
+          dv = fmaf(ckf, pz - pt, dv);
+          if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(zz - tt, invT, rev0), dv);
         }
         o[r] = (vv < a.v && valid) ? dv : 0.f;
       }
       store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
     }
   }
+  };
+  if (MODE != MODE_TOPK && a.kl != KD_KL_FORWARD) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // Top-K: dz[i, idx - c0] -= (g/den) w_kl p for the entries of this chunk.
@@ -887,7 +917,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   // Teacher statistics at T = 1 only feed the teacher CE.
   const int need_t1 = (p.need_t1 && pa.want_teacher) ? 1 : 0;
   FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, p.n, p.d, p.dt, p.v,
-             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, p.need_zT, need_t1, rec};
+             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, p.need_zT, need_t1, p.kl, rec};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
@@ -899,7 +929,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   }));
 
   MergeArgs ma{rec, prep, p.n_slices, p.n, p.mode, p.T, p.need_zT, need_t1,
-               (p.mode != MODE_TOPK) ? 1 : 0, p.ws, p.wt, p.wkl,
+               (p.mode != MODE_TOPK) ? 1 : 0, p.kl, p.ws, p.wt, p.wkl,
                out ? out->student_ce : nullptr, out ? out->teacher_ce : nullptr,
                out ? out->kl : nullptr, static_cast<float*>(saved), part};
   ma.teacher_ce = pa.want_teacher;
@@ -927,7 +957,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     const int n_vt = (int)((cw + G::kVT - 1) / G::kVT);  // fused tiles of the chunk
     BwdArgs ba{x.hs, x.w, x.ht, x.wt, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
                static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T, p.need_zT,
-               c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
+               p.kl, c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
       switch (p.mode) {

@@ -43,6 +43,7 @@ class Workload:
     student_ce_weight: float = 1.0
     teacher_ce_weight: float = 0.0
     kl_weight: float = 1.0
+    kl_divergence: str = "forward"  # "forward" | "reverse" | "jeffreys"
     ignore_index: int = -100
     ignore_frac: float = 0.0
     k: int = 0

@@ -128,6 +128,8 @@ def test_backward_workspace_is_O_n_chunk_not_n_vocab():
     ("topk_labels", L.KD_ERR_PARAM), ("labels_missing", L.KD_ERR_NULL),
     ("ws_small", L.KD_ERR_WORKSPACE), ("ws_null", L.KD_ERR_NULL), ("chunk_neg", L.KD_ERR_PARAM),
     ("teacher_kind", L.KD_ERR_PARAM), ("labels_misaligned", L.KD_ERR_ALIGN),
+    ("kl_bad", L.KD_ERR_PARAM), ("kl_neg", L.KD_ERR_PARAM),
+    ("topk_reverse", L.KD_ERR_UNSUPPORTED), ("topk_jeffreys", L.KD_ERR_UNSUPPORTED),
 ])
 def test_forward_rejects_invalid_arguments(case, expect):
     kind = "topk" if case.startswith("topk") else ("separate" if case.startswith("sep") else "tied")
@@ -179,6 +181,14 @@ def test_forward_rejects_invalid_arguments(case, expect):
         t.kind = 42
     elif case == "labels_misaligned":
         kw["labels"] = FAKE + 4
+    elif case == "kl_bad":
+        p.kl_divergence = 3
+    elif case == "kl_neg":
+        p.kl_divergence = -1
+    elif case == "topk_reverse":
+        p.kl_divergence = L.KD_KL_REVERSE
+    elif case == "topk_jeffreys":
+        p.kl_divergence = L.KD_KL_JEFFREYS
     if kind == "topk" and case not in ("topk_labels",):
         kw.setdefault("labels", None)
     assert _fwd(s, t, p, **kw) == expect

@@ -1,0 +1,32 @@
+"""Host-side argument checks of the torch API (no GPU and no library call needed)."""
+import pytest
+import torch
+
+from kl_knowledge_distillation_amd import api
+
+
+def _cpu_problem():
+    h = torch.zeros(4, 8)
+    w = torch.zeros(16, 8)
+    return h, w, torch.zeros(4, dtype=torch.int64)
+
+
+def test_unknown_kl_divergence_is_rejected():
+    h, w, y = _cpu_problem()
+    with pytest.raises(ValueError, match="kl_divergence"):
+        api.distillation_loss(h, w, y, api.TiedTeacher(h), kl_divergence="js")
+
+
+@pytest.mark.parametrize("kl", ["reverse", "jeffreys"])
+def test_topk_teacher_allows_forward_kl_only(kl):
+    h, w, _ = _cpu_problem()
+    t = api.TopKTeacher(torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
+    with pytest.raises(NotImplementedError, match="top-K"):
+        api.distillation_loss(h, w, None, t, kl_weight=1.0, kl_divergence=kl)
+
+
+def test_kl_divergence_table_matches_the_header():
+    from kl_knowledge_distillation_amd import _lib as L
+    assert api._KL_DIVERGENCES == {"forward": L.KD_KL_FORWARD, "reverse": L.KD_KL_REVERSE,
+                                   "jeffreys": L.KD_KL_JEFFREYS}
+    assert (L.KD_KL_FORWARD, L.KD_KL_REVERSE, L.KD_KL_JEFFREYS) == (0, 1, 2)

@@ -86,10 +86,12 @@ def test_accumulate_adds_into_gradients():
     assert torch.allclose(dw2, dw - 0.25, rtol=1e-6, atol=1e-6)
 
 
-def test_kl_exactly_zero_for_identical_teacher():
+@pytest.mark.parametrize("kl", ["forward", "reverse", "jeffreys"])
+def test_kl_exactly_zero_for_identical_teacher(kl):
     """Tied teacher with H_t = H_s: the two logit tiles are computed by the same
-    MFMA sequence, so every statistic matches and KL is 0 bit for bit."""
-    w = C2.scaled(n=260, d=256, v=3000)
+    MFMA sequence, so every statistic matches and KL is 0 bit for bit in every
+    direction."""
+    w = C2.scaled(n=260, d=256, v=3000, kl_divergence=kl)
     x = make_inputs(w, "cuda", seed=1)
     x["teacher_hidden"] = x["student_hidden"].clone()
     r, dh, dw = run_gpu(w, x)
@@ -141,6 +143,29 @@ def test_full_quickstart_tied_bf16():
 def test_full_tiny_fp32_default_and_chunked():
     full_parity(C1)
     full_parity(C1, vocab_chunk=256)
+
+
+KL_VARIANTS = {
+    "tied_T2_reverse": C2.scaled(n=300, d=512, v=3000, kl_divergence="reverse"),
+    "tied_T2_jeffreys_ragged": C2.scaled(n=130, d=136, v=1029, kl_divergence="jeffreys",
+                                         ignore_frac=0.2),
+    "separate_T1.3_jeffreys_tce": C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=1.3,
+                                            kl_divergence="jeffreys", teacher_ce_weight=0.5),
+    "separate_T1_reverse": C3.scaled(n=200, d=256, d_t=512, v=2000, kl_divergence="reverse"),
+    "fp32_T2_reverse": C1.scaled(n=70, v=1000, kl_divergence="reverse"),
+    "fp32_T2_jeffreys": C1.scaled(kl_divergence="jeffreys"),
+    "scorer_reverse": C5.scaled(n=300, d_t=512, v=5000, kl_divergence="reverse"),
+}
+
+
+@pytest.mark.parametrize("name", list(KL_VARIANTS))
+def test_kl_variants(name):
+    """Reverse KL(P_S || P_T) and the Jeffreys sum, forward and backward, against
+    the oracle, on the tied, separate, fp32 and logits-input paths."""
+    w = KL_VARIANTS[name]
+    full_parity(w)
+    if w.dtype == "fp32":
+        full_parity(w, vocab_chunk=256)
 
 
 @pytest.mark.parametrize("want", [True, False])
