@@ -38,6 +38,12 @@ Readings of points the pages leave open (each is also listed in the design doc):
       take the same 1/T on both logits and the same T**2 factor as "forward".
   R18 the cached top-K teacher supports "forward" only (its distribution is
       zero off the support, so KL(P_S || P_T) is not finite).
+  R19 with a teacher temperature T_t apart from the student's T_s, the teacher
+      distribution is softmax(t / T_t), the student's softmax(z / T_s), and
+      every KL direction is scaled by T_s**2.
+  R20 a teacher logit of -inf (a cached or projected teacher with no mass on a
+      column) is a zero teacher probability: its forward-KL term is 0, its
+      reverse-KL term (with a nonzero student probability) is +inf.
   --  a label outside [0, V) that is not ignore_index is treated as ignored.
 
 Parity pins for every function live in tests/test_oracle.py (closed forms,
@@ -75,6 +81,13 @@ class Params:
     reduction: str = "mean"  # "mean" | "sum"
     normalizer: float = 0.0
     kl_divergence: str = "forward"  # "forward" | "reverse" | "jeffreys"
+    # orda-kernel, Parameters (kl_teacher_temperature): None means T_s.
+    teacher_temperature: Optional[float] = None
+
+
+def teacher_temperature(p: Params) -> float:
+    """T_t: the teacher's own temperature, or the student's when unset."""
+    return p.temperature if p.teacher_temperature is None else p.teacher_temperature
 
 
 # ---------------------------------------------------------------------------
@@ -135,40 +148,48 @@ def cross_entropy(logits: np.ndarray, labels, valid: np.ndarray) -> np.ndarray:
     return np.where(valid, logsumexp(logits) - picked, 0.0)
 
 
-def forward_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
-    """Per-token T**2 * KL(P_T || P_S) with P = softmax(logits / T).
+def forward_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
+               Tt: Optional[float] = None) -> np.ndarray:
+    """Per-token T**2 * KL(P_T || P_S), P_S = softmax(z / T), P_T = softmax(t / Tt).
 
     nemo kd_loss, KDLoss (temperature): both logits are divided by T and the
     loss is multiplied by T**2; orda-kernel, KL variants: "forward" is
-    KL(teacher || student). Reported for every row (reading R3).
+    KL(teacher || student); orda-kernel, Parameters: the teacher temperature
+    defaults to the student's and each row scales by T_s**2 (reading R19).
+    Reported for every row (reading R3). A zero teacher probability adds 0
+    (reading R20).
     """
+    Tt = T if Tt is None else Tt
     lp_s = log_softmax(student_logits / T)
-    lp_t = log_softmax(teacher_logits / T)
-    return (T * T) * (np.exp(lp_t) * (lp_t - lp_s)).sum(axis=-1)
+    lp_t = log_softmax(teacher_logits / Tt)
+    q = np.exp(lp_t)
+    return (T * T) * (q * np.where(q > 0, lp_t - lp_s, 0.0)).sum(axis=-1)
 
 
-def reverse_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
-    """Per-token T**2 * KL(P_S || P_T) with P = softmax(logits / T).
+def reverse_kl(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
+               Tt: Optional[float] = None) -> np.ndarray:
+    """Per-token T**2 * KL(P_S || P_T), P_S = softmax(z / T), P_T = softmax(t / Tt).
 
     orda-kernel, KL variants: p = student, q = teacher, "reverse" is KL(p || q);
-    the temperature convention is the forward one (reading R17).
+    the temperature convention is the forward one (readings R17, R19).
     """
+    Tt = T if Tt is None else Tt
     lp_s = log_softmax(student_logits / T)
-    lp_t = log_softmax(teacher_logits / T)
+    lp_t = log_softmax(teacher_logits / Tt)
     return (T * T) * (np.exp(lp_s) * (lp_s - lp_t)).sum(axis=-1)
 
 
 def kl_term(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
-            variant: str = "forward") -> np.ndarray:
+            variant: str = "forward", Tt: Optional[float] = None) -> np.ndarray:
     """The per-token KL of the selected variant (orda-kernel, KL variants):
     forward KL(q || p), reverse KL(p || q), jeffreys KL(q || p) + KL(p || q)."""
     if variant == "forward":
-        return forward_kl(student_logits, teacher_logits, T)
+        return forward_kl(student_logits, teacher_logits, T, Tt)
     if variant == "reverse":
-        return reverse_kl(student_logits, teacher_logits, T)
+        return reverse_kl(student_logits, teacher_logits, T, Tt)
     if variant == "jeffreys":
-        return (forward_kl(student_logits, teacher_logits, T)
-                + reverse_kl(student_logits, teacher_logits, T))
+        return (forward_kl(student_logits, teacher_logits, T, Tt)
+                + reverse_kl(student_logits, teacher_logits, T, Tt))
     raise ValueError(f"unknown kl_divergence {variant!r}")
 
 
@@ -202,34 +223,42 @@ def dce_dlogits(logits: np.ndarray, labels, valid: np.ndarray) -> np.ndarray:
     return g
 
 
-def dkl_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
-    """d (T**2 KL(P_T || P_S)) / d z = T * (softmax(z/T) - softmax(t/T))."""
-    return T * (softmax(student_logits / T) - softmax(teacher_logits / T))
+def dkl_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
+                 Tt: Optional[float] = None) -> np.ndarray:
+    """d (T**2 KL(P_T || P_S)) / d z = T * (softmax(z/T) - softmax(t/Tt)).
+
+    Only P_S depends on z, through z / T, so the teacher temperature enters
+    through P_T alone.
+    """
+    Tt = T if Tt is None else Tt
+    return T * (softmax(student_logits / T) - softmax(teacher_logits / Tt))
 
 
-def dreverse_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float) -> np.ndarray:
+def dreverse_dstudent(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
+                      Tt: Optional[float] = None) -> np.ndarray:
     """d (T**2 KL(P_S || P_T)) / d z = T * P_S * (log P_S - log P_T - KL(P_S || P_T)).
 
     From d log P_S,v / d z_j = (delta_vj - P_S,j) / T: the T**2 and the 1/T of
     the softmax leave T, and the terms from differentiating log P_S sum to zero.
     """
+    Tt = T if Tt is None else Tt
     lp_s = log_softmax(student_logits / T)
-    lp_t = log_softmax(teacher_logits / T)
+    lp_t = log_softmax(teacher_logits / Tt)
     p = np.exp(lp_s)
     kl = (p * (lp_s - lp_t)).sum(axis=-1, keepdims=True)
     return T * p * (lp_s - lp_t - kl)
 
 
 def dkl_term(student_logits: np.ndarray, teacher_logits: np.ndarray, T: float,
-             variant: str = "forward") -> np.ndarray:
+             variant: str = "forward", Tt: Optional[float] = None) -> np.ndarray:
     """Gradient of kl_term with respect to the student logits."""
     if variant == "forward":
-        return dkl_dstudent(student_logits, teacher_logits, T)
+        return dkl_dstudent(student_logits, teacher_logits, T, Tt)
     if variant == "reverse":
-        return dreverse_dstudent(student_logits, teacher_logits, T)
+        return dreverse_dstudent(student_logits, teacher_logits, T, Tt)
     if variant == "jeffreys":
-        return (dkl_dstudent(student_logits, teacher_logits, T)
-                + dreverse_dstudent(student_logits, teacher_logits, T))
+        return (dkl_dstudent(student_logits, teacher_logits, T, Tt)
+                + dreverse_dstudent(student_logits, teacher_logits, T, Tt))
     raise ValueError(f"unknown kl_divergence {variant!r}")
 
 
@@ -257,6 +286,8 @@ class Teacher:
     kind "tied": hidden only, projected with the student weight.
     kind "separate": hidden (N, D_t) and weight (V, D_t), detached.
     kind "topk": cached (idx, prob), each (N, K) (Full-Chunked-KL-Loss).
+    kind "logits": cached dense logits (N, V), detached (orda-kernel, Teacher
+    descriptors: PrecomputedTeacher(logits=...)).
     """
 
     kind: str
@@ -264,6 +295,7 @@ class Teacher:
     weight: Optional[np.ndarray] = None
     idx: Optional[np.ndarray] = None
     prob: Optional[np.ndarray] = None
+    logits: Optional[np.ndarray] = None
 
 
 @dataclass
@@ -298,6 +330,8 @@ def _teacher_logits(t: Teacher, s: Student, rows: np.ndarray) -> Optional[np.nda
         return project(t.hidden[rows], s.weight)
     if t.kind == "separate":
         return project(t.hidden[rows], t.weight)
+    if t.kind == "logits":
+        return as_f64(t.logits[rows])
     return None
 
 
@@ -333,7 +367,8 @@ def per_token(student: Student, teacher: Teacher, p: Params, labels=None,
         t = _teacher_logits(teacher, student, r)
         if labels is not None:
             out["teacher_ce"][b:b + len(r)] = cross_entropy(t, lab[r], vb)
-        out["kl"][b:b + len(r)] = kl_term(z, t, p.temperature, p.kl_divergence)
+        out["kl"][b:b + len(r)] = kl_term(z, t, p.temperature, p.kl_divergence,
+                                          teacher_temperature(p))
     return out
 
 
@@ -375,7 +410,7 @@ def logit_grad(student: Student, teacher: Teacher, p: Params, labels, rows: np.n
                den: float, grad_loss: float = 1.0) -> np.ndarray:
     """d loss / d z for the given rows, shape (len(rows), V).
 
-    (g / den) * valid * [w_s (softmax z - e_y) + w_kl T (softmax(z/T) - softmax(t/T))],
+    (g / den) * valid * [w_s (softmax z - e_y) + w_kl T (softmax(z/T) - softmax(t/T_t))],
     or w_kl (M softmax z - p) in top-K mode. The teacher is detached (orda-kernel,
     KL variants: all variants except mutual/cojeffreys detach the teacher), so
     the teacher CE contributes no gradient (reading R6).
@@ -398,7 +433,8 @@ def logit_grad(student: Student, teacher: Teacher, p: Params, labels, rows: np.n
             g += p.student_ce_weight * dce_dlogits(z, lab, valid)
         if p.kl_weight != 0.0:
             t = _teacher_logits(teacher, student, rows)
-            g += p.kl_weight * dkl_term(z, t, p.temperature, p.kl_divergence)
+            g += p.kl_weight * dkl_term(z, t, p.temperature, p.kl_divergence,
+                                        teacher_temperature(p))
     g[~valid] = 0.0
     return g * (grad_loss / den)
 

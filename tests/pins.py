@@ -249,6 +249,109 @@ def check_reverse_zero_and_nonnegative(O):
         assert (O.per_token(s, t, p)["kl"] > 0).all(), f"{variant} not positive"
 
 
+# ---------------------------------------------------------------------------
+# Independent teacher temperature and cached dense teacher logits
+# (orda-kernel, Parameters: kl_teacher_temperature; Teacher descriptors:
+# PrecomputedTeacher(logits=...))
+# ---------------------------------------------------------------------------
+
+def _eye_pair(O, z, tl):
+    eye = np.eye(z.shape[1])
+    return O.Student(hidden=z, weight=eye), O.Teacher("separate", hidden=tl, weight=eye)
+
+
+def check_teacher_temperature_library(O):
+    """T_s^2 * kl_div(log_softmax(z/T_s), log_softmax(t/T_t)) summed over the
+    vocabulary, in both directions, for T_t apart from T_s."""
+    r = _rng(30)
+    z = r.normal(size=(6, 11)) * 2.0
+    tl = r.normal(size=(6, 11)) * 2.0
+    s, t = _eye_pair(O, z, tl)
+    zt, tt = torch.from_numpy(z), torch.from_numpy(tl)
+    for Ts, Tt in ((1.0, 2.0), (2.0, 0.7), (1.5, 1.5)):
+        lp_s, lp_t = F.log_softmax(zt / Ts, -1), F.log_softmax(tt / Tt, -1)
+        fwd = F.kl_div(lp_s, lp_t, log_target=True, reduction="none").sum(-1) * Ts * Ts
+        rev = F.kl_div(lp_t, lp_s, log_target=True, reduction="none").sum(-1) * Ts * Ts
+        for variant, ref in (("forward", fwd), ("reverse", rev), ("jeffreys", fwd + rev)):
+            p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=Ts,
+                         teacher_temperature=Tt, kl_divergence=variant)
+            _close(O.per_token(s, t, p)["kl"], ref.numpy(), rtol=1e-11, atol=1e-12,
+                   what=f"{variant} KL T_s={Ts} T_t={Tt}")
+
+
+def check_teacher_temperature_two_classes(O):
+    """V = 2: Bernoulli KL(q || p) with q = sigmoid((t1-t0)/T_t), p = sigmoid((z1-z0)/T_s),
+    times T_s^2."""
+    r = _rng(31)
+    z = r.normal(size=(6, 2)) * 1.5
+    tl = r.normal(size=(6, 2)) * 1.5
+    Ts, Tt = 1.2, 2.9
+    ps = 1.0 / (1.0 + np.exp(-(z[:, 1] - z[:, 0]) / Ts))
+    qt = 1.0 / (1.0 + np.exp(-(tl[:, 1] - tl[:, 0]) / Tt))
+    ref = Ts * Ts * (qt * np.log(qt / ps) + (1 - qt) * np.log((1 - qt) / (1 - ps)))
+    s, t = _eye_pair(O, z, tl)
+    p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=Ts, teacher_temperature=Tt)
+    _close(O.per_token(s, t, p)["kl"], ref, rtol=1e-11, atol=1e-13, what="Bernoulli KL, T_t != T_s")
+
+
+def check_teacher_temperature_unset_is_student(O):
+    """teacher_temperature=None gives the same values and gradients as T_t = T_s."""
+    s, t = _tied_case(O, k=12)
+    y = np.array([1, 3, -100, 0, 9, 4])
+    for variant in ("forward", "reverse"):
+        a = O.Params(student_ce_weight=0.3, kl_weight=1.0, temperature=1.8, kl_divergence=variant)
+        b = O.Params(student_ce_weight=0.3, kl_weight=1.0, temperature=1.8, teacher_temperature=1.8,
+                     kl_divergence=variant)
+        _close(O.forward(s, t, a, y)["loss"], O.forward(s, t, b, y)["loss"], rtol=1e-14)
+        _close(O.backward(s, t, a, y)[0], O.backward(s, t, b, y)[0], rtol=1e-14, atol=1e-15)
+
+
+def check_zero_teacher_probability(O):
+    """Teacher logits of -inf are zero teacher probabilities: forward KL is
+    T_s^2 * sum rel_entr(q, p) (scipy: rel_entr(0, y) = 0), reverse KL is +inf,
+    and the forward-KL gradient stays finite with P_T = 0 on those columns."""
+    from scipy.special import rel_entr, softmax as sp_softmax
+    r = _rng(32)
+    z = r.normal(size=(5, 10)) * 1.5
+    tl = r.normal(size=(5, 10)) * 1.5
+    tl[:, [2, 7]] = -np.inf
+    tl[3, :6] = -np.inf
+    Ts, Tt = 1.3, 0.9
+    q = sp_softmax(tl / Tt, axis=1)
+    pz = sp_softmax(z / Ts, axis=1)
+    ref = Ts * Ts * rel_entr(q, pz).sum(axis=1)
+    s = O.Student(hidden=z, weight=np.eye(10))
+    t = O.Teacher("logits", logits=tl)
+    p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=Ts, teacher_temperature=Tt)
+    _close(O.per_token(s, t, p)["kl"], ref, rtol=1e-11, atol=1e-13, what="KL with -inf teacher logits")
+    g = O.logit_grad(s, t, p, None, np.arange(5), den=1.0)
+    _close(g, Ts * (pz - q), rtol=1e-11, atol=1e-14, what="forward-KL gradient with P_T = 0")
+    pr = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=Ts, teacher_temperature=Tt,
+                  kl_divergence="reverse")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        assert np.isposinf(O.per_token(s, t, pr)["kl"]).all(), "reverse KL with P_T = 0 is +inf"
+
+
+def check_logits_teacher_matches_projection(O):
+    """A dense cached teacher holding H_t W_t^T gives the separate teacher's
+    per-token values and gradients."""
+    r = _rng(33)
+    n, d, dt, v = 6, 5, 4, 13
+    Hs, W = r.normal(size=(n, d)), r.normal(size=(v, d)) * 0.6
+    Ht, Wt = r.normal(size=(n, dt)), r.normal(size=(v, dt))
+    y = np.array([0, 12, -100, 5, 7, 7])
+    s = O.Student(hidden=Hs, weight=W)
+    sep = O.Teacher("separate", hidden=Ht, weight=Wt)
+    lg = O.Teacher("logits", logits=Ht @ Wt.T)
+    p = O.Params(student_ce_weight=0.6, teacher_ce_weight=0.4, kl_weight=1.0, temperature=1.7,
+                 teacher_temperature=1.1, kl_divergence="jeffreys")
+    a, b = O.per_token(s, sep, p, y), O.per_token(s, lg, p, y)
+    for k in ("student_ce", "teacher_ce", "kl"):
+        _close(a[k], b[k], rtol=1e-12, atol=1e-13, what=f"logits teacher {k}")
+    for ga, gb in zip(O.backward(s, sep, p, y), O.backward(s, lg, p, y)):
+        _close(ga, gb, rtol=1e-12, atol=1e-14, what="logits teacher gradient")
+
+
 def _topk_case(n=6, v=15, k=4, seed=10, zero_one=True):
     r = _rng(seed)
     z = r.normal(size=(n, v)) * 1.5
@@ -375,6 +478,8 @@ def _fd_cases(O):
     idx = np.stack([r.choice(v, size=3, replace=False) for _ in range(n)])
     g = r.gamma(0.5, size=(n, 3))
     pk = g / g.sum(1, keepdims=True) * 0.9
+    tl_inf = r.normal(size=(n, v)) * 1.5
+    tl_inf[:, [1, 4]] = -np.inf
     return [
         ("tied", O.Teacher("tied", hidden=Ht), y,
          O.Params(student_ce_weight=0.7, kl_weight=1.3, temperature=2.0)),
@@ -388,6 +493,11 @@ def _fd_cases(O):
          O.Params(student_ce_weight=0.4, kl_weight=1.1, temperature=2.0, kl_divergence="reverse")),
         ("jeffreys", O.Teacher("separate", hidden=Htt, weight=Wt), y,
          O.Params(student_ce_weight=1.0, kl_weight=0.9, temperature=1.3, kl_divergence="jeffreys")),
+        ("teacher_T", O.Teacher("separate", hidden=Htt, weight=Wt), y,
+         O.Params(student_ce_weight=0.8, kl_weight=1.2, temperature=1.4, teacher_temperature=2.3,
+                  kl_divergence="jeffreys")),
+        ("logits_inf", O.Teacher("logits", logits=tl_inf), y,
+         O.Params(student_ce_weight=0.5, kl_weight=1.1, temperature=1.5, teacher_temperature=0.8)),
     ], Hs, W
 
 
@@ -427,7 +537,7 @@ def check_grad_autograd_library(O):
     (F.cross_entropy with ignore_index, F.kl_div on F.log_softmax)."""
     cases, Hs, W = _fd_cases(O)
     for name, t, y, p in cases:
-        if t.kind == "topk":
+        if t.kind in ("topk", "logits"):  # kl_div has no 0 * log 0 = 0 for -inf targets
             continue
         H_ = torch.tensor(Hs, requires_grad=True)
         W_ = torch.tensor(W, requires_grad=True)
@@ -437,8 +547,9 @@ def check_grad_autograd_library(O):
         yt = torch.from_numpy(y)
         valid = yt != -100
         T = p.temperature
+        Tt = T if p.teacher_temperature is None else p.teacher_temperature
         ce = F.cross_entropy(z, yt, ignore_index=-100, reduction="none")
-        lp_s, lp_t = F.log_softmax(z / T, -1), F.log_softmax(tl / T, -1)
+        lp_s, lp_t = F.log_softmax(z / T, -1), F.log_softmax(tl / Tt, -1)
         fwd = F.kl_div(lp_s, lp_t, log_target=True, reduction="none").sum(-1) * T * T
         rev = F.kl_div(lp_t, lp_s, log_target=True, reduction="none").sum(-1) * T * T
         kl = {"forward": fwd, "reverse": rev, "jeffreys": fwd + rev}[p.kl_divergence]

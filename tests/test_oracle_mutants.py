@@ -22,14 +22,30 @@ MUTANTS = {
                            "return (T * T) * (np.exp(lp_t) * (lp_t - lp_s)).sum(axis=-1)"),
     "reverse_grad_missing_kl": ("return T * p * (lp_s - lp_t - kl)", "return T * p * (lp_s - lp_t)"),
     "reverse_grad_missing_T": ("return T * p * (lp_s - lp_t - kl)", "return p * (lp_s - lp_t - kl)"),
-    "jeffreys_twice_forward": ("""        return (forward_kl(student_logits, teacher_logits, T)
-                + reverse_kl(student_logits, teacher_logits, T))""",
-                               """        return (forward_kl(student_logits, teacher_logits, T)
-                + forward_kl(student_logits, teacher_logits, T))"""),
-    "kl_without_T2": ("return (T * T) * (np.exp(lp_t)", "return (np.exp(lp_t)"),
-    "kl_teacher_not_tempered": ("lp_t = log_softmax(teacher_logits / T)\n    return (T * T) * (np.exp(lp_t)",
-                                "lp_t = log_softmax(teacher_logits)\n    return (T * T) * (np.exp(lp_t)"),
-    "kl_reversed": ("(np.exp(lp_t) * (lp_t - lp_s))", "(np.exp(lp_s) * (lp_s - lp_t))"),
+    "jeffreys_twice_forward": ("""        return (forward_kl(student_logits, teacher_logits, T, Tt)
+                + reverse_kl(student_logits, teacher_logits, T, Tt))""",
+                               """        return (forward_kl(student_logits, teacher_logits, T, Tt)
+                + forward_kl(student_logits, teacher_logits, T, Tt))"""),
+    "kl_without_T2": ("return (T * T) * (q * np.where", "return (q * np.where"),
+    "kl_scaled_by_teacher_T": ("return (T * T) * (q * np.where", "return (Tt * Tt) * (q * np.where"),
+    "kl_teacher_not_tempered": ("lp_t = log_softmax(teacher_logits / Tt)\n    q = np.exp(lp_t)",
+                                "lp_t = log_softmax(teacher_logits)\n    q = np.exp(lp_t)"),
+    "kl_teacher_at_student_T": ("lp_t = log_softmax(teacher_logits / Tt)\n    q = np.exp(lp_t)",
+                                "lp_t = log_softmax(teacher_logits / T)\n    q = np.exp(lp_t)"),
+    "reverse_teacher_at_student_T": (
+        "lp_t = log_softmax(teacher_logits / Tt)\n    return (T * T) * (np.exp(lp_s)",
+        "lp_t = log_softmax(teacher_logits / T)\n    return (T * T) * (np.exp(lp_s)"),
+    "dkl_teacher_at_student_T": ("return T * (softmax(student_logits / T) - softmax(teacher_logits / Tt))",
+                                 "return T * (softmax(student_logits / T) - softmax(teacher_logits / T))"),
+    "dreverse_teacher_at_student_T": ("lp_t = log_softmax(teacher_logits / Tt)\n    p = np.exp(lp_s)",
+                                      "lp_t = log_softmax(teacher_logits / T)\n    p = np.exp(lp_s)"),
+    "teacher_temperature_ignored": (
+        "return p.temperature if p.teacher_temperature is None else p.teacher_temperature",
+        "return p.temperature"),
+    "zero_teacher_probability_nan": ("(q * np.where(q > 0, lp_t - lp_s, 0.0))", "(q * (lp_t - lp_s))"),
+    "logits_teacher_columns_reversed": ("return as_f64(t.logits[rows])",
+                                        "return as_f64(t.logits[rows][:, ::-1])"),
+    "kl_reversed": ("(q * np.where(q > 0, lp_t - lp_s, 0.0))", "(np.exp(lp_s) * (lp_s - lp_t))"),
     "ce_label_off_by_one": ("picked = np.take_along_axis(logits, y[:, None], axis=1)",
                             "picked = np.take_along_axis(logits, (y[:, None] + 1) % logits.shape[1], axis=1)"),
     "ce_ignored_not_zeroed": ("return np.where(valid, logsumexp(logits) - picked, 0.0)",
@@ -40,8 +56,8 @@ MUTANTS = {
                           "return entropy_term - cross_term + logsumexp(student_logits)"),
     "topk_entropy_sign": ("return entropy_term - cross_term + mass",
                           "return -entropy_term - cross_term + mass"),
-    "dkl_missing_T": ("return T * (softmax(student_logits / T) - softmax(teacher_logits / T))",
-                      "return (softmax(student_logits / T) - softmax(teacher_logits / T))"),
+    "dkl_missing_T": ("return T * (softmax(student_logits / T) - softmax(teacher_logits / Tt))",
+                      "return (softmax(student_logits / T) - softmax(teacher_logits / Tt))"),
     "dtopk_plus_p": ("np.subtract.at(g,", "np.add.at(g,"),
     "dce_label_not_subtracted": ("g[rows, np.asarray(labels, dtype=np.int64)[rows]] -= 1.0",
                                  "pass"),
