@@ -44,6 +44,8 @@ Readings of points the pages leave open (each is also listed in the design doc):
   R20 a teacher logit of -inf (a cached or projected teacher with no mass on a
       column) is a zero teacher probability: its forward-KL term is 0, its
       reverse-KL term (with a nonzero student probability) is +inf.
+  R21 a loss term whose weight is 0 is absent from the loss, not 0 times its
+      value (which may be infinite, e.g. the teacher CE of R20's columns).
   --  a label outside [0, V) that is not ignore_index is treated as ignored.
 
 Parity pins for every function live in tests/test_oracle.py (closed forms,
@@ -395,9 +397,13 @@ def forward(student: Student, teacher: Teacher, p: Params, labels=None) -> dict:
     """
     out = per_token(student, teacher, p, labels)
     valid = out["valid"]
-    contrib = (p.student_ce_weight * out["student_ce"]
-               + p.teacher_ce_weight * out["teacher_ce"]
-               + p.kl_weight * out["kl"])
+    # A term whose weight is 0 is absent (reading R21), so an infinite teacher
+    # CE at a zero-probability label does not enter an unweighted loss.
+    contrib = np.zeros(len(valid), F64)
+    for w_term, term in ((p.student_ce_weight, out["student_ce"]),
+                         (p.teacher_ce_weight, out["teacher_ce"]), (p.kl_weight, out["kl"])):
+        if w_term != 0.0:
+            contrib = contrib + w_term * term
     n_valid = int(valid.sum())
     den = denominator(p, n_valid)
     out["n_valid"] = n_valid

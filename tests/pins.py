@@ -332,6 +332,25 @@ def check_zero_teacher_probability(O):
         assert np.isposinf(O.per_token(s, t, pr)["kl"]).all(), "reverse KL with P_T = 0 is +inf"
 
 
+def check_zero_weight_term_is_absent(O):
+    """With teacher_ce_weight = 0 the loss ignores the teacher CE, even where it
+    is infinite (a label on a -inf teacher column): the loss equals the weighted
+    mean of the student CE and the KL alone."""
+    r = _rng(34)
+    z = r.normal(size=(4, 6))
+    tl = r.normal(size=(4, 6))
+    tl[:, 5] = -np.inf
+    y = np.array([5, 0, 5, 2])
+    s = O.Student(hidden=z, weight=np.eye(6))
+    t = O.Teacher("logits", logits=tl)
+    p = O.Params(student_ce_weight=0.5, teacher_ce_weight=0.0, kl_weight=1.0, temperature=1.0)
+    from scipy.special import rel_entr, softmax as sp_softmax
+    ce = F.cross_entropy(torch.from_numpy(z), torch.from_numpy(y), reduction="none").numpy()
+    kl = rel_entr(sp_softmax(tl, axis=1), sp_softmax(z, axis=1)).sum(1)
+    _close(O.forward(s, t, p, y)["loss"], np.mean(0.5 * ce + kl), rtol=1e-12,
+           what="zero-weighted infinite teacher CE")
+
+
 def check_logits_teacher_matches_projection(O):
     """A dense cached teacher holding H_t W_t^T gives the separate teacher's
     per-token values and gradients."""
