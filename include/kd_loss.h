@@ -66,7 +66,7 @@ enum {
   KD_ERR_NULL = 1,         /* a required pointer is NULL */
   KD_ERR_SHAPE = 2,        /* n, d, v, d_t or k out of range, or inconsistent */
   KD_ERR_DTYPE = 3,        /* unknown dtype, or a mode that does not accept it */
-  KD_ERR_PARAM = 4,        /* temperature/weights not finite or not allowed, bad reduction or KL variant */
+  KD_ERR_PARAM = 4,        /* temperatures/weights not finite or not allowed, bad reduction or KL variant */
   KD_ERR_ALIGN = 5,        /* a pointer not 16-byte aligned, or d / d_t not a multiple of 8 */
   KD_ERR_WORKSPACE = 6,    /* workspace smaller than kd_workspace_bytes, or saved missing */
   KD_ERR_UNSUPPORTED = 7,  /* valid but not provided (backward of the logits scorer, a non-forward KL with a TOPK teacher) */
@@ -82,18 +82,22 @@ enum { KD_F32 = 0, KD_BF16 = 1 };
  * student_logits); forward only, and the teacher must be SEPARATE. */
 enum { KD_STUDENT_PROJECTION = 0, KD_STUDENT_LOGITS = 1 };
 
-/* Teacher descriptor kinds (orda-kernel, Teacher descriptors). */
-enum { KD_TEACHER_TIED = 1, KD_TEACHER_SEPARATE = 2, KD_TEACHER_TOPK = 3 };
+/* Teacher descriptor kinds (orda-kernel, Teacher descriptors). LOGITS is the
+ * cached dense form of PrecomputedTeacher: teacher logits [n, v] given
+ * directly, read tile by tile in place of the teacher projection; it needs a
+ * PROJECTION student. */
+enum { KD_TEACHER_TIED = 1, KD_TEACHER_SEPARATE = 2, KD_TEACHER_TOPK = 3, KD_TEACHER_LOGITS = 4 };
 
 /* Loss reduction (orda-kernel, Parameters: reduction). NONE produces the
  * per-token outputs and the sum in `loss`; it has no backward. */
 enum { KD_REDUCE_MEAN = 0, KD_REDUCE_SUM = 1, KD_REDUCE_NONE = 2 };
 
-/* KL variant of the distillation term (orda-kernel, KL variants; p = student,
- * q = teacher, both softmax(logits / T)). FORWARD is KL(q || p), REVERSE
- * KL(p || q), JEFFREYS their sum; the per-token value and the loss carry T^2,
- * and the teacher is always detached. A TOPK teacher allows FORWARD only (its
- * distribution is zero off the support). */
+/* KL variant of the distillation term (orda-kernel, KL variants; p = student
+ * softmax(z / T), q = teacher softmax(t / T_t), T_t = teacher_temperature or
+ * T). FORWARD is KL(q || p), REVERSE KL(p || q), JEFFREYS their sum; the
+ * per-token value and the loss carry T^2 (orda-kernel, Parameters: each KL row
+ * scales by T_s^2), and the teacher is always detached. A TOPK teacher allows
+ * FORWARD only (its distribution is zero off the support). */
 enum { KD_KL_FORWARD = 0, KD_KL_REVERSE = 1, KD_KL_JEFFREYS = 2 };
 
 typedef struct {
@@ -115,6 +119,9 @@ typedef struct {
   const void* weight;       /* SEPARATE [v, d_t]; student dtype */
   const int32_t* topk_idx;  /* TOPK [n, k], distinct per row */
   const float* topk_prob;   /* TOPK [n, k], not renormalised (sum = retained mass M) */
+  const void* logits;       /* LOGITS [n, v] row-major, student dtype, element-aligned. A -inf
+                               entry is a zero teacher probability: it adds 0 to the forward KL
+                               and makes the reverse KL +inf. Every row needs a finite entry. */
 } kd_teacher;
 
 typedef struct {
@@ -129,6 +136,8 @@ typedef struct {
                                 the dz slab holds n x chunk; 0 = library default (8192) */
   int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
   int32_t kl_divergence;     /* KD_KL_* */
+  float teacher_temperature; /* T_t > 0, finite: the teacher's own temperature (orda-kernel,
+                                Parameters: kl_teacher_temperature); 0 = T. TOPK: 0 or 1 */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).

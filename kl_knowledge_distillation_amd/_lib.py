@@ -14,7 +14,7 @@ KD_OK, KD_ERR_NULL, KD_ERR_SHAPE, KD_ERR_DTYPE, KD_ERR_PARAM = 0, 1, 2, 3, 4
 KD_ERR_ALIGN, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_LABEL_RANGE, KD_ERR_HIP = 5, 6, 7, 8, 9
 KD_F32, KD_BF16 = 0, 1
 KD_STUDENT_PROJECTION, KD_STUDENT_LOGITS = 0, 1
-KD_TEACHER_TIED, KD_TEACHER_SEPARATE, KD_TEACHER_TOPK = 1, 2, 3
+KD_TEACHER_TIED, KD_TEACHER_SEPARATE, KD_TEACHER_TOPK, KD_TEACHER_LOGITS = 1, 2, 3, 4
 KD_REDUCE_MEAN, KD_REDUCE_SUM, KD_REDUCE_NONE = 0, 1, 2
 KD_KL_FORWARD, KD_KL_REVERSE, KD_KL_JEFFREYS = 0, 1, 2
 KERNELS = ["prep", "fwd", "merge", "finalize", "bwd_dz", "scatter", "gemm_dw", "gemm_dh"]
@@ -28,14 +28,16 @@ class KdStudent(ctypes.Structure):
 
 class KdTeacher(ctypes.Structure):
     _fields_ = [("kind", c_int32), ("k", c_int32), ("d_t", c_int64), ("hidden", c_void_p),
-                ("weight", c_void_p), ("topk_idx", c_void_p), ("topk_prob", c_void_p)]
+                ("weight", c_void_p), ("topk_idx", c_void_p), ("topk_prob", c_void_p),
+                ("logits", c_void_p)]
 
 
 class KdParams(ctypes.Structure):
     _fields_ = [("student_ce_weight", c_float), ("teacher_ce_weight", c_float),
                 ("kl_weight", c_float), ("temperature", c_float), ("ignore_index", c_int64),
                 ("reduction", c_int32), ("normalizer", c_float), ("vocab_chunk", c_int64),
-                ("assume_valid_labels", c_int32), ("kl_divergence", c_int32)]
+                ("assume_valid_labels", c_int32), ("kl_divergence", c_int32),
+                ("teacher_temperature", c_float)]
 
 
 class KdOutputs(ctypes.Structure):

@@ -7,10 +7,12 @@ passes pointers. If the library is missing, every entry point raises.
 User API (orda-kernel, Quickstart / Teacher descriptors / Parameters):
     distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
                       teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
-                      kl_divergence="forward", ignore_index=-100, reduction="mean",
-                      num_batch_labels=None, vocab_chunk=0) -> DistillationLossOutput
+                      kl_teacher_temperature=None, kl_divergence="forward",
+                      ignore_index=-100, reduction="mean", num_batch_labels=None,
+                      vocab_chunk=0) -> DistillationLossOutput
+    kl_divergence: "forward" | "reverse" | "jeffreys"
     teachers: TiedTeacher(hidden), SeparateTeacher(hidden, weight),
-              PrecomputedTeacher(teacher_hidden=..., teacher_weight=...),
+              PrecomputedTeacher(logits=...) or (teacher_hidden=..., teacher_weight=...),
               TopKTeacher(indices, probs)   (Full-Chunked-KL-Loss cached top-K)
 Scorer (flash_kd, flash_ce_kd_loss):
     flash_ce_kd_loss(student_logits, teacher_hidden, teacher_lm_head_weight, labels, *,
@@ -47,9 +49,18 @@ class SeparateTeacher:
 
 @dataclass
 class PrecomputedTeacher:
-    """Cached teacher given as teacher_hidden + teacher_weight (no gradient)."""
-    teacher_hidden: torch.Tensor
-    teacher_weight: torch.Tensor
+    """Cached teacher, no gradient: dense ``logits`` (BT, vocab), or
+    ``teacher_hidden`` (BT, D_t) with ``teacher_weight`` (vocab, D_t).
+    A logit of -inf is a zero teacher probability."""
+    logits: Optional[torch.Tensor] = None
+    teacher_hidden: Optional[torch.Tensor] = None
+    teacher_weight: Optional[torch.Tensor] = None
+
+    def __post_init__(self):
+        has_proj = self.teacher_hidden is not None or self.teacher_weight is not None
+        if (self.logits is None) == (not has_proj) or \
+                (has_proj and (self.teacher_hidden is None or self.teacher_weight is None)):
+            raise ValueError("give either logits, or teacher_hidden and teacher_weight")
 
 
 @dataclass
@@ -107,9 +118,10 @@ class Runner:
 
     def __init__(self, *, student_hidden=None, weight=None, student_logits=None, labels=None,
                  teacher_kind="tied", teacher_hidden=None, teacher_weight=None, topk_idx=None,
-                 topk_prob=None, student_ce_weight=1.0, teacher_ce_weight=0.0, kl_weight=0.0,
-                 temperature=1.0, ignore_index=-100, reduction="mean", normalizer=0.0,
-                 vocab_chunk=0, want_grads=True, want_teacher_ce=None, kl_divergence="forward"):
+                 topk_prob=None, teacher_logits=None, student_ce_weight=1.0,
+                 teacher_ce_weight=0.0, kl_weight=0.0, temperature=1.0, ignore_index=-100,
+                 reduction="mean", normalizer=0.0, vocab_chunk=0, want_grads=True,
+                 want_teacher_ce=None, kl_divergence="forward", teacher_temperature=None):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -122,7 +134,7 @@ class Runner:
             raise ValueError(f"unsupported dtype {ref.dtype}")
         # keep the tensors alive for the lifetime of the descriptors
         self._keep = [student_hidden, weight, student_logits, labels, teacher_hidden,
-                      teacher_weight, topk_idx, topk_prob]
+                      teacher_weight, topk_idx, topk_prob, teacher_logits]
         self.labels = labels
         s = L.KdStudent()
         s.dtype = dtype
@@ -149,6 +161,11 @@ class Runner:
             t.d_t = teacher_hidden.shape[1]
             t.hidden = _ptr(teacher_hidden)
             t.weight = _ptr(teacher_weight)
+        elif teacher_kind == "logits":
+            t.kind = L.KD_TEACHER_LOGITS
+            if tuple(teacher_logits.shape) != (s.n, s.v) or teacher_logits.dtype != ref.dtype:
+                raise ValueError("teacher logits must be (BT, vocab) in the student dtype")
+            t.logits = _ptr(teacher_logits)
         elif teacher_kind == "topk":
             t.kind = L.KD_TEACHER_TOPK
             t.k = topk_idx.shape[1]
@@ -168,6 +185,7 @@ class Runner:
         if kl_divergence not in _KL_DIVERGENCES:
             raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
         p.kl_divergence = _KL_DIVERGENCES[kl_divergence]
+        p.teacher_temperature = 0.0 if teacher_temperature is None else float(teacher_temperature)
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
         f32 = dict(dtype=torch.float32, device=self.device)
@@ -298,8 +316,8 @@ class _FusedLoss(torch.autograd.Function):
 
 def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
                       teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
-                      kl_divergence="forward", ignore_index=-100, reduction="mean",
-                      num_batch_labels=None, vocab_chunk=0,
+                      kl_teacher_temperature=None, kl_divergence="forward", ignore_index=-100,
+                      reduction="mean", num_batch_labels=None, vocab_chunk=0,
                       return_teacher_ce=True) -> DistillationLossOutput:
     """Fused LM-head + CE + KL loss; differentiable in student_hidden and weight.
 
@@ -313,7 +331,9 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
         raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
     if isinstance(teacher, TopKTeacher) and kl_divergence != "forward":
         raise NotImplementedError("the top-K teacher supports kl_divergence='forward' only")
-    kw = dict(kl_divergence=kl_divergence, student_hidden=student_hidden.detach().contiguous(),
+    if kl_teacher_temperature is not None and not kl_teacher_temperature > 0:
+        raise ValueError("kl_teacher_temperature must be positive")
+    kw = dict(kl_divergence=kl_divergence, teacher_temperature=kl_teacher_temperature, student_hidden=student_hidden.detach().contiguous(),
               weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
               teacher_ce_weight=teacher_ce_weight, kl_weight=kl_weight,
               temperature=kl_temperature, ignore_index=ignore_index, reduction=reduction,
@@ -321,6 +341,8 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
               want_teacher_ce=bool(return_teacher_ce or teacher_ce_weight > 0))
     if isinstance(teacher, TiedTeacher):
         kw.update(teacher_kind="tied", teacher_hidden=teacher.hidden.detach().contiguous())
+    elif isinstance(teacher, PrecomputedTeacher) and teacher.logits is not None:
+        kw.update(teacher_kind="logits", teacher_logits=teacher.logits.detach().contiguous())
     elif isinstance(teacher, (SeparateTeacher, PrecomputedTeacher)):
         h = teacher.hidden if isinstance(teacher, SeparateTeacher) else teacher.teacher_hidden
         w = teacher.weight if isinstance(teacher, SeparateTeacher) else teacher.teacher_weight

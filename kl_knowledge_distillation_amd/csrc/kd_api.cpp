@@ -64,6 +64,12 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
       q.mode = (s->kind == KD_STUDENT_LOGITS) ? kd::MODE_LOGITS : kd::MODE_SEPARATE;
       q.dt = t->d_t;
       break;
+    case KD_TEACHER_LOGITS:
+      if (s->kind != KD_STUDENT_PROJECTION) return KD_ERR_UNSUPPORTED;
+      if (!t->logits) return KD_ERR_NULL;
+      if (((uintptr_t)t->logits & (s->dtype == KD_BF16 ? 1u : 3u)) != 0) return KD_ERR_ALIGN;
+      q.mode = kd::MODE_TLOGITS;
+      break;
     case KD_TEACHER_TOPK:
       if (s->kind != KD_STUDENT_PROJECTION) return KD_ERR_UNSUPPORTED;
       if (!t->topk_idx || !t->topk_prob) return KD_ERR_NULL;
@@ -77,6 +83,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   }
 
   if (!isfinite(p->temperature) || p->temperature <= 0.f) return KD_ERR_PARAM;
+  if (!isfinite(p->teacher_temperature) || p->teacher_temperature < 0.f) return KD_ERR_PARAM;
   if (!finite_nonneg(p->student_ce_weight) || !finite_nonneg(p->teacher_ce_weight) ||
       !finite_nonneg(p->kl_weight))
     return KD_ERR_PARAM;
@@ -92,6 +99,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   if (q.mode == kd::MODE_TOPK) {
     // The cached teacher has no temperature and no labels (Full-Chunked-KL-Loss, Methods).
     if (p->temperature != 1.f) return KD_ERR_UNSUPPORTED;
+    if (p->teacher_temperature != 0.f && p->teacher_temperature != 1.f) return KD_ERR_UNSUPPORTED;
     // Its distribution is zero off the support: only KL(teacher || student) is finite.
     if (p->kl_divergence != KD_KL_FORWARD) return KD_ERR_UNSUPPORTED;
     if (p->student_ce_weight != 0.f || p->teacher_ce_weight != 0.f) return KD_ERR_PARAM;
@@ -106,6 +114,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.wt = p->teacher_ce_weight;
   q.wkl = p->kl_weight;
   q.T = p->temperature;
+  q.Tt = (p->teacher_temperature > 0.f) ? p->teacher_temperature : p->temperature;
   q.ignore = p->ignore_index;
   q.reduction = p->reduction;
   q.normalizer = p->normalizer;
@@ -113,7 +122,8 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   // Student statistics at z/T: needed for the KL at T != 1, and always for the
   // reverse direction, whose weights are the student's softmax(z/T).
   q.need_zT = (q.T != 1.f || q.kl != KD_KL_FORWARD) ? 1 : 0;
-  q.need_t1 = (q.T != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
+  // Teacher statistics at t (T = 1) beside those at t/T_t, for the teacher CE.
+  q.need_t1 = (q.Tt != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
   q.has_labels = labels ? 1 : 0;
 
   // Tile geometry: bf16 with every contraction length a multiple of 64 runs the
@@ -165,6 +175,8 @@ kd::Tensors tensors_of(const kd_student* s, const kd_teacher* t, const int64_t* 
   } else if (t->kind == KD_TEACHER_SEPARATE) {
     x.ht = t->hidden;
     x.wt = t->weight;
+  } else if (t->kind == KD_TEACHER_LOGITS) {
+    x.tlogits = t->logits;
   } else {
     x.topk_idx = t->topk_idx;
     x.topk_prob = t->topk_prob;

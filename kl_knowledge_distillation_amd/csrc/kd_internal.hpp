@@ -10,7 +10,10 @@
 
 namespace kd {
 
-enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3 };
+// TIED / SEPARATE / TOPK: projection student with that teacher; LOGITS: given
+// student logits with a separate teacher (forward only); TLOGITS: projection
+// student with given dense teacher logits.
+enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3, MODE_TLOGITS = 4 };
 
 // Number of fp32 fields of one per-(token, vocabulary tile) record.
 constexpr int kRecFields = 10;
@@ -28,12 +31,13 @@ struct Plan {
   int64_t n = 0, d = 0, dt = 0, v = 0;
   int k = 0;
   float ws = 0.f, wt = 0.f, wkl = 0.f, T = 1.f;
+  float Tt = 1.f;     // teacher temperature (T unless set apart)
   int64_t ignore = -100;
   int reduction = KD_REDUCE_MEAN;
   float normalizer = 0.f;
   int kl = KD_KL_FORWARD;  // KD_KL_*
   int need_zT = 0;    // statistics at z/T kept apart from z (T != 1, or a reverse-direction KL)
-  int need_t1 = 0;    // teacher CE wanted at T != 1: teacher statistics at t
+  int need_t1 = 0;    // teacher statistics at t kept apart from t/T_t (T_t != 1)
   int has_labels = 0;
   int pipe = 0;       // bf16 with hidden sizes multiple of 32: 256-row pipelined tiles
   int vt_rows = 128;  // vocabulary rows per fused tile
@@ -54,6 +58,7 @@ struct Tensors {
   const void* logits = nullptr;  // student logits [n, v]
   const void* ht = nullptr;      // teacher hidden [n, d_t]
   const void* wt = nullptr;      // teacher weight [v, d_t] (tied: == w)
+  const void* tlogits = nullptr; // dense teacher logits [n, v]
   const int32_t* topk_idx = nullptr;
   const float* topk_prob = nullptr;
   const int64_t* labels = nullptr;

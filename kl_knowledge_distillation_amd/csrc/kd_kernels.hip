@@ -110,25 +110,41 @@ __device__ __forceinline__ float tile_sum(const WaveAcc& x, int nb, float c, flo
   return s0 + s1;
 }
 
-// Teacher sum at scale c and the cross term sum 2^(t c - mc) (t - z).
-template <bool TAIL>
-__device__ __forceinline__ void tile_sum_cross(const WaveAcc& t, const WaveAcc& z, int nb, float c, float mc,
-                                               uint32_t ok, float& s, float& a) {
+// Sum of x at scale c and the cross term. Teacher-weighted (TEACHER_W):
+// x = t, y = z, e = 2^(t c - mc), a = sum e (t rho - z); student-weighted:
+// x = z, y = t, a = sum e (z - t rho); rho = T_s / T_t, so a / T_s is the
+// weighted sum of t / T_t - z / T_s (or its negative). ZERO_SAFE: an e of 0
+// adds 0 even where the difference is infinite (a teacher logit of -inf).
+template <bool TAIL, bool TEACHER_W, bool ZERO_SAFE = false>
+__device__ __forceinline__ void tile_sum_cross(const WaveAcc& x, const WaveAcc& y, int nb, float c, float mc,
+                                               float rho, uint32_t ok, float& s, float& a) {
   float s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e0 = exp2_fast(fmaf(t[mb][nb][r], c, -mc));
-      float e1 = exp2_fast(fmaf(t[mb + 1][nb][r], c, -mc));
+      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mc));
+      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mc));
       if (TAIL) {
         e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
         e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
       }
       s0 += e0;
       s1 += e1;
-      a0 = fmaf(e0, t[mb][nb][r] - z[mb][nb][r], a0);
-      a1 = fmaf(e1, t[mb + 1][nb][r] - z[mb + 1][nb][r], a1);
+      float d0, d1;
+      if constexpr (TEACHER_W) {
+        d0 = fmaf(x[mb][nb][r], rho, -y[mb][nb][r]);
+        d1 = fmaf(x[mb + 1][nb][r], rho, -y[mb + 1][nb][r]);
+      } else {
+        d0 = fmaf(y[mb][nb][r], -rho, x[mb][nb][r]);
+        d1 = fmaf(y[mb + 1][nb][r], -rho, x[mb + 1][nb][r]);
+      }
+      if constexpr (ZERO_SAFE) {
+        d0 = (e0 > 0.f) ? d0 : 0.f;
+        d1 = (e1 > 0.f) ? d1 : 0.f;
+      }
+      a0 = fmaf(e0, d0, a0);
+      a1 = fmaf(e1, d1, a1);
     }
   s = s0 + s1;
   a = a0 + a1;
@@ -177,6 +193,46 @@ __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t ar
   }
 }
 
+// The [kVT x kTT] tile of a row-major [n x v] logits matrix (tokens are rows)
+// in the accumulator layout: register r of row block mb, token block nb holds
+// vocabulary row v0 + acc_row(wm, mb, r, lane) of token t0 + acc_col(wn, nb, lane).
+// A lane's four rows are consecutive in memory and load as one 8-byte (bf16) or
+// 16-byte (fp32) vector when `vec` (v a multiple of 4, base aligned to the
+// vector). Rows past v and tokens past n read 0; the epilogue masks them.
+template <typename T>
+__device__ __forceinline__ void load_logits_tile(const T* L, int64_t n, int64_t v, int64_t t0, int64_t v0,
+                                                 int wm, int wn, int lane, bool vec, WaveAcc& out) {
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int64_t tok = t0 + acc_col(wn, nb, lane);
+    const bool live = tok < n;
+    const int64_t base = live ? tok * v : 0;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int64_t vv = v0 + acc_row(wm, mb, 0, lane);
+      if (live && vec && vv + 4 <= v) {
+        if constexpr (sizeof(T) == 2) {
+          const uint2 u = *reinterpret_cast<const uint2*>(L + base + vv);
+          out[mb][nb][0] = __uint_as_float(u.x << 16);
+          out[mb][nb][1] = __uint_as_float(u.x & 0xffff0000u);
+          out[mb][nb][2] = __uint_as_float(u.y << 16);
+          out[mb][nb][3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(L + base + vv);
+          out[mb][nb][0] = f.x;
+          out[mb][nb][1] = f.y;
+          out[mb][nb][2] = f.z;
+          out[mb][nb][3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          out[mb][nb][r] = (live && vv + r < v) ? to_f32(L[base + vv + r]) : 0.f;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Forward tile kernel
 // ---------------------------------------------------------------------------
@@ -186,12 +242,14 @@ struct FwdArgs {
   const void* w;
   const void* ht;
   const void* wt;
-  const void* logits;
+  const void* logits;   // student logits (LOGITS)
+  const void* tlogits;  // teacher logits (TLOGITS)
   int64_t n, d, dt, v;
   int n_ttiles, n_vtiles, tps, n_slices;
-  float cT;
+  float cT, cTt, rho;   // log2(e) / T_s, log2(e) / T_t, T_s / T_t
   int need_zT, need_t1;
   int kl;      // KD_KL_*: the reverse direction also needs sum 2^(z~ - m) (z - t)
+  int vec;     // the given logits matrix loads as 4-element vectors
   float* rec;  // [kRecFields][n_slices][n]
 };
 
@@ -226,21 +284,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   } else if constexpr (MODE == MODE_TOPK) {
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+  } else if constexpr (MODE == MODE_TLOGITS) {
+    const T* const b[1] = {hs};
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    load_logits_tile<T>(static_cast<const T*>(a.tlogits), a.n, a.v, t0, v0, wm, wn, lane, a.vec != 0,
+                        tacc[0]);
   } else {  // MODE_LOGITS
     const T* const bt[1] = {ht};
     tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-    const T* L = static_cast<const T*>(a.logits);
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const int64_t tok = t0 + acc_col(wn, nb, lane);
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t vv = v0 + acc_row(wm, mb, r, lane);
-          zl[mb][nb][r] = (tok < a.n && vv < a.v) ? to_f32(L[tok * a.v + vv]) : 0.f;
-        }
-    }
+    load_logits_tile<T>(static_cast<const T*>(a.logits), a.n, a.v, t0, v0, wm, wn, lane, a.vec != 0, zl);
   }
 
   // Epilogue: this tile's statistics of every token, in two passes over the
@@ -262,6 +314,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   const WaveAcc& z = (MODE == MODE_LOGITS) ? zl : acc[0];
   const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
   constexpr bool kTeacher = MODE != MODE_TOPK;
+  constexpr bool kInfT = MODE == MODE_TLOGITS;  // given teacher logits may be -inf
   constexpr int kSums = 6;  // sz1, szT, stT, a, st1, ar
   float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNB][2][16]
   float* xsum = xmax + G::kWM * 2 * kNB * 2 * 16;                 // [kWM][2][kNB][kSums][16]
@@ -302,21 +355,25 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const bool rev = a.kl != KD_KL_FORWARD;
     const float mz1 = mz[nb] * kLog2e, mzT = mz[nb] * a.cT;
-    const float mtT = mt[nb] * a.cT, mt1 = mt[nb] * kLog2e;
+    // A teacher tile with no finite logit (all -inf) sums 2^-inf = 0 against a
+    // finite reference; its record keeps the -inf maximum, which the merge
+    // treats as empty.
+    const float mtb = (kInfT && mt[nb] == -INFINITY) ? 0.f : mt[nb];
+    const float mtT = mtb * a.cTt, mt1 = mtb * kLog2e;
     if (tail) {
       v[0] = tile_sum<true>(z, nb, kLog2e, mz1, ok);
       if (kTeacher) {
-        if (rev) tile_sum_cross<true>(z, tl, nb, a.cT, mzT, ok, v[1], v[5]);
+        if (rev) tile_sum_cross<true, false>(z, tl, nb, a.cT, mzT, a.rho, ok, v[1], v[5]);
         else if (a.need_zT) v[1] = tile_sum<true>(z, nb, a.cT, mzT, ok);
-        tile_sum_cross<true>(tl, z, nb, a.cT, mtT, ok, v[2], v[3]);
+        tile_sum_cross<true, true, kInfT>(tl, z, nb, a.cTt, mtT, a.rho, ok, v[2], v[3]);
         if (a.need_t1) v[4] = tile_sum<true>(tl, nb, kLog2e, mt1, ok);
       }
     } else {
       v[0] = tile_sum<false>(z, nb, kLog2e, mz1, ok);
       if (kTeacher) {
-        if (rev) tile_sum_cross<false>(z, tl, nb, a.cT, mzT, ok, v[1], v[5]);
+        if (rev) tile_sum_cross<false, false>(z, tl, nb, a.cT, mzT, a.rho, ok, v[1], v[5]);
         else if (a.need_zT) v[1] = tile_sum<false>(z, nb, a.cT, mzT, ok);
-        tile_sum_cross<false>(tl, z, nb, a.cT, mtT, ok, v[2], v[3]);
+        tile_sum_cross<false, true, kInfT>(tl, z, nb, a.cTt, mtT, a.rho, ok, v[2], v[3]);
         if (a.need_t1) v[4] = tile_sum<false>(tl, nb, kLog2e, mt1, ok);
       }
     }
@@ -348,7 +405,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
         float* r = a.rec + (int64_t)slice * a.n + tok;
         r[0 * stride] = mz[nb] * kLog2e; r[1 * stride] = v[0];
         r[2 * stride] = mz[nb] * a.cT;   r[3 * stride] = v[1];
-        r[4 * stride] = mt[nb] * a.cT;   r[5 * stride] = v[2];
+        r[4 * stride] = mt[nb] * a.cTt;  r[5 * stride] = v[2];
         r[6 * stride] = v[3];
         r[7 * stride] = mt[nb] * kLog2e; r[8 * stride] = v[4];
         r[9 * stride] = v[5];
@@ -366,7 +423,8 @@ struct PrepArgs {
   const void* w;
   const void* ht;
   const void* wt;
-  const void* logits;
+  const void* logits;   // student logits (LOGITS)
+  const void* tlogits;  // teacher logits (TLOGITS)
   const int64_t* labels;
   const int32_t* idx;
   const float* prob;
@@ -431,9 +489,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
         f0 = wave_dot<T>(hs + i * a.d, W + y * a.d, a.d, lane);
       }
       if (a.want_teacher) {
-        const T* ht = static_cast<const T*>(a.ht);
-        const T* Wt = static_cast<const T*>(a.wt);
-        f1 = wave_dot<T>(ht + i * a.dt, Wt + y * a.dt, a.dt, lane);
+        if constexpr (MODE == MODE_TLOGITS) {
+          f1 = to_f32(static_cast<const T*>(a.tlogits)[i * a.v + y]);
+        } else {
+          const T* ht = static_cast<const T*>(a.ht);
+          const T* Wt = static_cast<const T*>(a.wt);
+          f1 = wave_dot<T>(ht + i * a.dt, Wt + y * a.dt, a.dt, lane);
+        }
       }
     }
   }
@@ -533,7 +595,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       }
       bad = (flag == 2.f) ? 1.0 : 0.0;
       cnt = valid ? 1.0 : 0.0;
-      contrib = valid ? ((double)a.ws * sce + (double)a.wt * tce + (double)a.wkl * kl) : 0.0;
+      // A term of weight 0 is left out, not multiplied: its value may be
+      // infinite (a teacher CE at a label whose teacher logit is -inf).
+      if (valid) {
+        if (a.ws != 0.f) contrib += (double)a.ws * sce;
+        if (a.wt != 0.f) contrib += (double)a.wt * tce;
+        if (a.wkl != 0.f) contrib += (double)a.wkl * kl;
+      }
       if (a.out_sce) a.out_sce[i] = sce;
       if (a.out_tce) a.out_tce[i] = tce;
       if (a.out_kl) a.out_kl[i] = kl;
@@ -619,14 +687,17 @@ struct BwdArgs {
   const void* w;
   const void* ht;
   const void* wt;
+  const void* tlogits;    // teacher logits (TLOGITS)
   int64_t n, d, dt, v;
   const int64_t* labels;
   int64_t ignore;
   const float* saved;     // [n][4] + header at 16 n bytes
   const float* grad;      // device scalar or null
   float ws, wkl, T, cT;
+  float cTt, rho;         // log2(e) / T_t, T_s / T_t
   int need_zT;
   int kl;                 // KD_KL_*
+  int vec;                // teacher logits load as 4-element vectors
   int64_t c0;             // first vocabulary row of the chunk
   int n_vt, n_ttiles;     // tiles of the chunk
   void* dz;               // [dz_rows][ldz]
@@ -673,6 +744,11 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     const T* const bt[1] = {ht};
     tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
+  } else if constexpr (MODE == MODE_TLOGITS) {
+    const T* const b[1] = {hs};
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    load_logits_tile<T>(static_cast<const T*>(a.tlogits), a.n, a.v, t0, v0, wm, wn, lane, a.vec != 0,
+                        tacc[0]);
   } else {  // MODE_TOPK
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
@@ -707,7 +783,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const float ck = coef * a.wkl * a.T;     // T^2 KL -> T (P_S - P_T)
     const float cm = coef * a.wkl * mass;    // top-K: M softmax(z)
     // T^2 KL(P_S || P_T) -> T P_S (log P_S - log P_T - KL(P_S || P_T)); with
-    // log P_S - log P_T = (z - t) / T - lse(z/T) + lse(t/T) (natural logs).
+    // log P_S - log P_T = (z - t rho) / T - lse(z/T) + lse(t/T_t) (natural logs).
     const float ckf = (a.kl != KD_KL_REVERSE) ? ck : 0.f;
     const float ckr = ck;
     const float rev0 = sv.z - sv.y - mass;   // lse(t/T) - lse(z/T) - KL(P_S || P_T)
@@ -729,9 +805,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
           dv = cs * (p1 - (vv == y ? 1.f : 0.f));
           const float tt = tl[mb][nb][r];
           const float pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
-          const float pt = exp2_fast(fmaf(tt, a.cT, -LtT));
+          const float pt = exp2_fast(fmaf(tt, a.cTt, -LtT));
           dv = fmaf(ckf, pz - pt, dv);
-          if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(zz - tt, invT, rev0), dv);
+          if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(fmaf(tt, -a.rho, zz), invT, rev0), dv);
         }
         o[r] = (vv < a.v && valid) ? dv : 0.f;
       }
@@ -891,6 +967,13 @@ struct Launch {
     if (st_ != KD_OK) return st_;     \
   } while (0)
 
+// A given [n x v] logits matrix loads a lane's four consecutive elements as one
+// vector when every row start keeps the vector alignment.
+template <typename T>
+int vector_ok(const void* ptr, int64_t v) {
+  return (ptr != nullptr && v % 4 == 0 && ((uintptr_t)ptr % (4 * sizeof(T))) == 0) ? 1 : 0;
+}
+
 template <typename T, class G>
 kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved, void* ws,
                     hipStream_t stream, kd_trace* trace) {
@@ -901,29 +984,32 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   double* part = reinterpret_cast<double*>(base + p.off_part);
   int32_t* status = reinterpret_cast<int32_t*>(base);
 
-  PrepArgs pa{x.hs, x.w, x.ht, x.wt, x.logits, x.labels, x.topk_idx, x.topk_prob,
+  PrepArgs pa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, x.labels, x.topk_idx, x.topk_prob,
               p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, prep};
-  pa.want_teacher = (p.mode == MODE_TIED || p.mode == MODE_SEPARATE || p.mode == MODE_LOGITS) &&
-                    (p.wt > 0.f || (out && out->teacher_ce));
+  pa.want_teacher = p.mode != MODE_TOPK && (p.wt > 0.f || (out && out->teacher_ce));
   const dim3 pgrid((unsigned)((p.n + 3) / 4));
   KD_TRY(L.run(KD_KERNEL_PREP, [&] {
     switch (p.mode) {
       case MODE_TOPK: prep_kernel<T, MODE_TOPK><<<pgrid, kThreads, 0, stream>>>(pa); break;
       case MODE_LOGITS: prep_kernel<T, MODE_LOGITS><<<pgrid, kThreads, 0, stream>>>(pa); break;
+      case MODE_TLOGITS: prep_kernel<T, MODE_TLOGITS><<<pgrid, kThreads, 0, stream>>>(pa); break;
       default: prep_kernel<T, MODE_TIED><<<pgrid, kThreads, 0, stream>>>(pa); break;
     }
   }));
 
   // Teacher statistics at T = 1 only feed the teacher CE.
   const int need_t1 = (p.need_t1 && pa.want_teacher) ? 1 : 0;
-  FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, p.n, p.d, p.dt, p.v,
-             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, p.need_zT, need_t1, p.kl, rec};
+  const void* given = (p.mode == MODE_TLOGITS) ? x.tlogits : x.logits;
+  FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
+             p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, kLog2e / p.Tt, p.T / p.Tt,
+             p.need_zT, need_t1, p.kl, vector_ok<T>(given, p.v), rec};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
       case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
       case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
       case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+      case MODE_TLOGITS: fwd_tiles_kernel<T, MODE_TLOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
       default: fwd_tiles_kernel<T, MODE_LOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
     }
   }));
@@ -955,14 +1041,16 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     const int64_t c0 = (int64_t)c * p.chunk;
     const int64_t cw = (p.v - c0 < p.chunk) ? (p.v - c0) : p.chunk;  // valid columns
     const int n_vt = (int)((cw + G::kVT - 1) / G::kVT);  // fused tiles of the chunk
-    BwdArgs ba{x.hs, x.w, x.ht, x.wt, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
-               static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T, p.need_zT,
-               p.kl, c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
+    BwdArgs ba{x.hs, x.w, x.ht, x.wt, x.tlogits, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
+               static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T,
+               kLog2e / p.Tt, p.T / p.Tt, p.need_zT, p.kl, vector_ok<T>(x.tlogits, p.v),
+               c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
       switch (p.mode) {
         case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_TLOGITS: bwd_dz_kernel<T, MODE_TLOGITS, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
         default: bwd_dz_kernel<T, MODE_TOPK, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
       }
     }));

@@ -18,6 +18,10 @@ Workloads (shapes from the pages, distributions as stated):
                         --topk 100, batch 1)
   scorer_bf16           N=65536, D_t=4096, V=248320, student logits given,
                         forward only (flash_kd: vocab ~248k)
+  quickstart_logits_bf16  the quickstart shape with a cached dense teacher
+                        (orda-kernel, Teacher descriptors: PrecomputedTeacher
+                        logits) of N(0,1) logits, the per-entry variance of
+                        the projected quickstart teacher, T_s = 2, T_t = 1.5
 """
 from __future__ import annotations
 
@@ -37,19 +41,22 @@ class Workload:
     v: int
     d_t: int = 0
     dtype: str = "bf16"            # "bf16" | "fp32"
-    teacher: str = "tied"          # "tied" | "separate" | "topk"
+    teacher: str = "tied"          # "tied" | "separate" | "topk" | "logits"
     student: str = "projection"    # "projection" | "logits"
     temperature: float = 1.0
     student_ce_weight: float = 1.0
     teacher_ce_weight: float = 0.0
     kl_weight: float = 1.0
     kl_divergence: str = "forward"  # "forward" | "reverse" | "jeffreys"
+    teacher_temperature: Optional[float] = None  # None: the student temperature
     ignore_index: int = -100
     ignore_frac: float = 0.0
     k: int = 0
     student_hidden_std: float = 1.0
     teacher_hidden_std: float = 1.0
     logits_var: float = 0.0
+    teacher_logits_var: float = 1.0   # dense teacher logits ~ N(0, var)
+    teacher_neg_inf_frac: float = 0.0  # vocabulary columns whose teacher logit is -inf
     forward_only: bool = False
     has_labels: bool = True
 
@@ -83,11 +90,16 @@ WORKLOADS: Dict[str, Workload] = {
         "scorer_bf16", n=65536, d=0, d_t=4096, v=248320, teacher="separate",
         student="logits", temperature=1.0, student_ce_weight=1.0, kl_weight=1.0,
         ignore_index=-1, ignore_frac=0.03, logits_var=2.0, forward_only=True),
+    "quickstart_logits_bf16": Workload(
+        "quickstart_logits_bf16", n=4096, d=2048, v=32000, teacher="logits",
+        temperature=2.0, teacher_temperature=1.5, student_ce_weight=1.0, kl_weight=1.0,
+        ignore_frac=0.05),
 }
 
 # One generator stream per named tensor (seed 0 by default).
 _STREAM = {"student_hidden": 1, "weight": 2, "teacher_hidden": 3, "teacher_weight": 4,
-           "labels": 5, "ignore": 6, "topk": 7, "student_logits": 8}
+           "labels": 5, "ignore": 6, "topk": 7, "student_logits": 8, "teacher_logits": 9,
+           "teacher_mask": 10}
 
 _SLICE_ELEMS = 1 << 28  # rows are drawn in slices of at most this many elements
 
@@ -157,13 +169,18 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0) -> Dict[str, Optional[
     """All tensors of one workload instance, on ``device``.
 
     Keys: student_hidden, weight, student_logits, teacher_hidden, teacher_weight,
-    labels, topk_idx, topk_prob (absent ones are None).
+    teacher_logits, labels, topk_idx, topk_prob (absent ones are None).
+
+    Dense teacher logits: N(0, teacher_logits_var); with teacher_neg_inf_frac > 0
+    the first round(frac * v) columns of a seeded permutation are -inf in every
+    row, as a teacher projected from another vocabulary leaves its unmatched
+    columns (orda-kernel, Cross-vocabulary distillation).
     """
     device = torch.device(device)
     dt = w.torch_dtype
     out: Dict[str, Optional[torch.Tensor]] = dict.fromkeys(
         ["student_hidden", "weight", "student_logits", "teacher_hidden", "teacher_weight",
-         "labels", "topk_idx", "topk_prob"])
+         "teacher_logits", "labels", "topk_idx", "topk_prob"])
     if w.student == "projection":
         out["student_hidden"] = _normal((w.n, w.d), w.student_hidden_std, dt, device, seed,
                                         "student_hidden")
@@ -177,6 +194,14 @@ def make_inputs(w: Workload, device="cpu", seed: int = 0) -> Dict[str, Optional[
     if w.teacher == "separate":
         out["teacher_weight"] = _normal((w.v, w.d_t), 1.0 / math.sqrt(w.d_t), dt, device, seed,
                                         "teacher_weight")
+    if w.teacher == "logits":
+        tl = _normal((w.n, w.v), math.sqrt(w.teacher_logits_var), dt, device, seed,
+                     "teacher_logits")
+        k = int(round(w.teacher_neg_inf_frac * w.v))
+        if k:
+            cols = torch.randperm(w.v, generator=_gen(torch.device("cpu"), seed, "teacher_mask"))[:k]
+            tl[:, cols.to(device)] = float("-inf")
+        out["teacher_logits"] = tl
     if w.teacher == "topk":
         idx, prob = make_topk(w.n, w.v, w.k, seed)
         out["topk_idx"] = idx.to(device)

@@ -39,7 +39,7 @@ def to_np(t: Optional[torch.Tensor]):
 def params_of(w: Workload) -> O.Params:
     return O.Params(student_ce_weight=w.student_ce_weight, teacher_ce_weight=w.teacher_ce_weight,
                     kl_weight=w.kl_weight, temperature=w.temperature, ignore_index=w.ignore_index,
-                    kl_divergence=w.kl_divergence)
+                    kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature)
 
 
 def oracle_problem(w: Workload, x: dict, rows=None):
@@ -59,6 +59,8 @@ def oracle_problem(w: Workload, x: dict, rows=None):
     elif w.teacher == "separate":
         t = O.Teacher("separate", hidden=f64(x["teacher_hidden"], rows) if w.student == "logits"
                       else f64(x["teacher_hidden"]), weight=f64(x["teacher_weight"]))
+    elif w.teacher == "logits":
+        t = O.Teacher("logits", logits=f64(x["teacher_logits"]))
     else:
         t = O.Teacher("topk", idx=to_np(x["topk_idx"]).astype(np.int64),
                       prob=to_np(x["topk_prob"]).astype(np.float64))
@@ -76,7 +78,8 @@ def make_runner(w: Workload, x: dict, vocab_chunk: int = 0, reduction: str = "me
               temperature=w.temperature, ignore_index=w.ignore_index, reduction=reduction,
               vocab_chunk=vocab_chunk,
               want_grads=(not w.forward_only) if want_grads is None else want_grads,
-              want_teacher_ce=want_teacher_ce, kl_divergence=w.kl_divergence)
+              want_teacher_ce=want_teacher_ce, kl_divergence=w.kl_divergence,
+              teacher_temperature=w.teacher_temperature)
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:
@@ -87,6 +90,8 @@ def make_runner(w: Workload, x: dict, vocab_chunk: int = 0, reduction: str = "me
     elif w.teacher == "separate":
         kw.update(teacher_kind="separate", teacher_hidden=x["teacher_hidden"],
                   teacher_weight=x["teacher_weight"])
+    elif w.teacher == "logits":
+        kw.update(teacher_kind="logits", teacher_logits=x["teacher_logits"])
     else:
         kw.update(teacher_kind="topk", topk_idx=x["topk_idx"], topk_prob=x["topk_prob"])
     return Runner(**kw)

@@ -130,6 +130,8 @@ def test_backward_workspace_is_O_n_chunk_not_n_vocab():
     ("teacher_kind", L.KD_ERR_PARAM), ("labels_misaligned", L.KD_ERR_ALIGN),
     ("kl_bad", L.KD_ERR_PARAM), ("kl_neg", L.KD_ERR_PARAM),
     ("topk_reverse", L.KD_ERR_UNSUPPORTED), ("topk_jeffreys", L.KD_ERR_UNSUPPORTED),
+    ("tT_neg", L.KD_ERR_PARAM), ("tT_nan", L.KD_ERR_PARAM), ("topk_tT", L.KD_ERR_UNSUPPORTED),
+    ("tlog_null", L.KD_ERR_NULL), ("tlog_misaligned", L.KD_ERR_ALIGN),
 ])
 def test_forward_rejects_invalid_arguments(case, expect):
     kind = "topk" if case.startswith("topk") else ("separate" if case.startswith("sep") else "tied")
@@ -189,6 +191,18 @@ def test_forward_rejects_invalid_arguments(case, expect):
         p.kl_divergence = L.KD_KL_REVERSE
     elif case == "topk_jeffreys":
         p.kl_divergence = L.KD_KL_JEFFREYS
+    elif case == "tT_neg":
+        p.teacher_temperature = -1.0
+    elif case == "tT_nan":
+        p.teacher_temperature = float("nan")
+    elif case == "topk_tT":
+        p.teacher_temperature = 2.0
+    elif case == "tlog_null":
+        t.kind = L.KD_TEACHER_LOGITS
+        t.logits = None
+    elif case == "tlog_misaligned":
+        t.kind = L.KD_TEACHER_LOGITS
+        t.logits = FAKE + 1
     if kind == "topk" and case not in ("topk_labels",):
         kw.setdefault("labels", None)
     assert _fwd(s, t, p, **kw) == expect
@@ -220,3 +234,17 @@ def test_null_descriptors():
     nb = ctypes.c_size_t(0)
     assert lib.kd_workspace_bytes(None, None, None, 0, ctypes.byref(nb)) == L.KD_ERR_NULL
     assert lib.kd_read_status(None, None, None) == L.KD_ERR_NULL
+
+
+def test_teacher_logits_descriptor():
+    """A dense teacher-logits descriptor plans like the others; it needs a
+    projection student, and a teacher temperature of its own is accepted."""
+    s, t, p = _desc()
+    t.kind, t.hidden, t.logits = L.KD_TEACHER_LOGITS, None, FAKE
+    p.teacher_temperature = 1.5
+    st, fwd = _ws(s, t, p, 0)
+    assert st == L.KD_OK and fwd > 0
+    st, bwd = _ws(s, t, p, 1)
+    assert st == L.KD_OK and bwd > 0
+    s2 = L.KdStudent(L.KD_STUDENT_LOGITS, L.KD_BF16, 300, 0, 3000, None, None, FAKE)
+    assert _ws(s2, t, p, 0)[0] == L.KD_ERR_UNSUPPORTED

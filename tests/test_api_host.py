@@ -30,3 +30,19 @@ def test_kl_divergence_table_matches_the_header():
     assert api._KL_DIVERGENCES == {"forward": L.KD_KL_FORWARD, "reverse": L.KD_KL_REVERSE,
                                    "jeffreys": L.KD_KL_JEFFREYS}
     assert (L.KD_KL_FORWARD, L.KD_KL_REVERSE, L.KD_KL_JEFFREYS) == (0, 1, 2)
+
+
+def test_precomputed_teacher_takes_one_form():
+    x = torch.zeros(4, 16)
+    h, w = torch.zeros(4, 8), torch.zeros(16, 8)
+    api.PrecomputedTeacher(logits=x)
+    api.PrecomputedTeacher(teacher_hidden=h, teacher_weight=w)
+    for bad in (dict(), dict(logits=x, teacher_hidden=h, teacher_weight=w), dict(teacher_hidden=h)):
+        with pytest.raises(ValueError):
+            api.PrecomputedTeacher(**bad)
+
+
+def test_teacher_temperature_must_be_positive():
+    h, w, y = _cpu_problem()
+    with pytest.raises(ValueError, match="kl_teacher_temperature"):
+        api.distillation_loss(h, w, y, api.TiedTeacher(h), kl_teacher_temperature=0.0)

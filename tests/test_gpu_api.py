@@ -104,3 +104,24 @@ def test_topk_teacher_through_the_api():
     assert_scalar(float(out.loss.detach()), ref["loss"], "bf16", "top-K loss")
     dH, _ = O.backward(s, t, p, None)
     assert_grad(f64(hs.grad), dH, "bf16", "top-K student_hidden.grad")
+
+
+def test_precomputed_logits_teacher_with_its_own_temperature():
+    w = WORKLOADS["quickstart_logits_bf16"].scaled(n=200, d=256, v=2048, teacher_neg_inf_frac=0.1)
+    x = make_inputs(w, "cuda", seed=15)
+    hs = x["student_hidden"].clone().requires_grad_(True)
+    out = api.distillation_loss(hs, x["weight"], x["labels"],
+                                api.PrecomputedTeacher(logits=x["teacher_logits"]),
+                                kl_weight=1.0, kl_temperature=2.0, kl_teacher_temperature=1.5,
+                                return_teacher_ce=False)
+    out.loss.backward()
+    torch.cuda.synchronize()
+    s = O.Student(hidden=f64(x["student_hidden"]), weight=f64(x["weight"]))
+    t = O.Teacher("logits", logits=f64(x["teacher_logits"]))
+    labels = to_np(x["labels"]).astype(np.int64)
+    p = O.Params(student_ce_weight=1.0, kl_weight=1.0, temperature=2.0, teacher_temperature=1.5)
+    ref = O.forward(s, t, p, labels)
+    assert_scalar(float(out.loss.detach()), ref["loss"], "bf16", "loss")
+    assert_tokens(to_np(out.kl), ref["kl"], "bf16", "kl")
+    dH, _ = O.backward(s, t, p, labels)
+    assert_grad(f64(hs.grad), dH, "bf16", "student_hidden.grad")

@@ -20,6 +20,7 @@ C2 = WORKLOADS["quickstart_tied_bf16"]
 C3 = WORKLOADS["separate_bf16"]
 C4 = WORKLOADS["topk_bf16"]
 C5 = WORKLOADS["scorer_bf16"]
+C6 = WORKLOADS["quickstart_logits_bf16"]
 
 SMALL = {
     "tiny_fp32": C1,
@@ -166,6 +167,62 @@ def test_kl_variants(name):
     full_parity(w)
     if w.dtype == "fp32":
         full_parity(w, vocab_chunk=256)
+
+
+TEACHER_CASES = {
+    # dense cached teacher logits: pipelined bf16 with vector loads (V % 4 == 0)
+    "logits_small": C6.scaled(n=300, d=512, v=3000),
+    # staged bf16 (D % 64 != 0) with element loads (V % 4 != 0), ragged tiles
+    "logits_ragged": C6.scaled(n=130, d=136, v=1029, ignore_frac=0.2),
+    "logits_fp32": C1.scaled(teacher="logits", teacher_temperature=0.7),
+    # 30% of the columns -inf in every row: zero teacher probabilities
+    "logits_neg_inf": C6.scaled(n=260, d=256, v=2100, teacher_neg_inf_frac=0.3),
+    "logits_jeffreys_tce": C6.scaled(n=200, d=256, v=2048, kl_divergence="jeffreys",
+                                     teacher_ce_weight=0.5),
+    # teacher temperature apart from the student's on the projected teachers
+    "tied_Ts2_Tt1": C2.scaled(n=300, d=512, v=3000, teacher_temperature=1.0, teacher_ce_weight=0.3),
+    "separate_Ts1.5_Tt3_reverse_tce": C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=1.5,
+                                                teacher_temperature=3.0, kl_divergence="reverse"),
+    "fp32_Ts2_Tt0.6_jeffreys": C1.scaled(teacher_temperature=0.6, kl_divergence="jeffreys"),
+    "scorer_Tt2": C5.scaled(n=300, d_t=512, v=5000, teacher_temperature=2.0),
+}
+
+
+@pytest.mark.parametrize("name", list(TEACHER_CASES))
+def test_teacher_logits_and_temperature(name):
+    """Dense cached teacher logits (with -inf entries) and a teacher temperature
+    of its own, forward and backward, against the oracle."""
+    w = TEACHER_CASES[name]
+    full_parity(w)
+    if w.dtype == "fp32":
+        full_parity(w, vocab_chunk=256)
+
+
+def test_infinite_teacher_ce_with_zero_weight():
+    """Labels on -inf teacher columns: the requested per-token teacher CE is +inf
+    there, and with teacher_ce_weight = 0 the loss stays finite and equal to the
+    oracle's (a zero-weighted term is left out)."""
+    w = C6.scaled(n=200, d=256, v=2048, teacher_neg_inf_frac=0.5)
+    x = make_inputs(w, "cuda", seed=9)
+    r = make_runner(w, x, want_teacher_ce=True)
+    r.forward()
+    torch.cuda.synchronize()
+    s, t, labels = oracle_problem(w, x)
+    ref = O.forward(s, t, params_of(w), labels)
+    tce = to_np(r.teacher_ce).astype(np.float64)
+    inf_rows = np.isinf(ref["teacher_ce"]) & ref["valid"]
+    assert inf_rows.sum() > 10
+    assert np.isposinf(tce[inf_rows]).all()
+    assert_tokens(tce[~inf_rows], ref["teacher_ce"][~inf_rows], "bf16", "finite teacher CE",
+                  ref["valid"][~inf_rows])
+    assert np.isfinite(float(r.loss))
+    assert_scalar(float(r.loss), ref["loss"], "bf16", "loss")
+
+
+def test_full_quickstart_logits_teacher_bf16():
+    """Quickstart shape with a dense cached teacher (N=4096, D=2048, V=32000,
+    T_s = 2, T_t = 1.5), every output."""
+    full_parity(C6)
 
 
 @pytest.mark.parametrize("want", [True, False])
