@@ -177,7 +177,8 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
     full = {k: f(v) if k not in ("labels", "topk_idx") else (None if v is None else v.numpy())
             for k, v in x.items()}
     p = O.Params(student_ce_weight=w.student_ce_weight, teacher_ce_weight=w.teacher_ce_weight,
-                 kl_weight=w.kl_weight, temperature=w.temperature, ignore_index=w.ignore_index)
+                 kl_weight=w.kl_weight, temperature=w.temperature, ignore_index=w.ignore_index,
+                 kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature)
 
     def run(rows: int) -> float:
         g = lambda k: None if full[k] is None else full[k][:rows]  # noqa: E731
@@ -186,6 +187,8 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
             t = O.Teacher("tied", hidden=g("teacher_hidden"))
         elif w.teacher == "separate":
             t = O.Teacher("separate", hidden=g("teacher_hidden"), weight=full["teacher_weight"])
+        elif w.teacher == "logits":
+            t = O.Teacher("logits", logits=g("teacher_logits"))
         else:
             t = O.Teacher("topk", idx=g("topk_idx"), prob=g("topk_prob"))
         t0 = time.perf_counter()
@@ -260,7 +263,8 @@ def main() -> int:
     kw = dict(labels=x["labels"], student_ce_weight=w.student_ce_weight,
               teacher_ce_weight=w.teacher_ce_weight, kl_weight=w.kl_weight,
               temperature=w.temperature, ignore_index=w.ignore_index,
-              vocab_chunk=args.vocab_chunk, want_grads=not w.forward_only)
+              vocab_chunk=args.vocab_chunk, want_grads=not w.forward_only,
+              kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature)
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:
@@ -270,6 +274,8 @@ def main() -> int:
     elif w.teacher == "separate":
         kw.update(teacher_kind="separate", teacher_hidden=x["teacher_hidden"],
                   teacher_weight=x["teacher_weight"])
+    elif w.teacher == "logits":
+        kw.update(teacher_kind="logits", teacher_logits=x["teacher_logits"])
     else:
         kw.update(teacher_kind="topk", topk_idx=x["topk_idx"], topk_prob=x["topk_prob"])
     input_bytes = sum(t.numel() * t.element_size() for t in x.values() if t is not None)
@@ -351,6 +357,7 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "n_tokens": w.n, "hidden": w.d, "teacher_hidden": w.teacher_dim,
                    "vocab": w.v, "teacher": w.teacher, "temperature": w.temperature,
+                   "teacher_temperature": w.teacher_temperature, "kl_divergence": w.kl_divergence,
                    "top_k": w.k or None, "vocab_chunk": chunk, "parallelism": "single GPU"},
         "mfma_tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / peak_tflops, 4),

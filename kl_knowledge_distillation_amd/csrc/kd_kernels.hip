@@ -233,6 +233,70 @@ __device__ __forceinline__ void load_logits_tile(const T* L, int64_t n, int64_t 
   }
 }
 
+// Given bf16 logits staged through LDS (pipelined geometry). The [128 x 256]
+// tile (128 token rows of 256 vocabulary entries) is copied with buffer loads
+// straight into LDS by the four group-A waves before the main loop: those waves
+// issue no main-loop copies and never wait on them, so these copies land while
+// the MFMAs run. After the main loop every wave reads its registers in the
+// accumulator layout. Image: token row tr is 32 chunks of 16 bytes, chunk c at
+// position c ^ (tr & 15), so the 16 tokens of one ds_read_b64 fall in 16
+// distinct 16-byte bank groups. Needs v a multiple of 8 and a 16-byte aligned
+// matrix (every chunk is then one aligned 16-byte load).
+constexpr int kGivenTokens = 128, kGivenVocab = 256;
+constexpr int kGivenBytes = kGivenTokens * kGivenVocab * 2;  // 64 KB
+
+__device__ __forceinline__ void given_tile_copy(const bf16_t* L, int64_t n, int64_t v, int64_t t0,
+                                                int64_t v0, uint8_t* img, int gw, int lane) {
+  const int64_t rows = (n - t0 < kGivenTokens) ? (n - t0) : kGivenTokens;
+  const rsrc_t r = make_rsrc(L + t0 * v, rows * v * 2);  // token rows past n read zeros
+  const uint32_t row_bytes = (uint32_t)(v * 2);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = gw * 16 + i;  // 1 KB block j: token rows 2 j and 2 j + 1
+    const int tr = 2 * j + h;
+    const int c = (lane & 31) ^ (tr & 15);
+    const uint32_t voff = (uint32_t)h * row_bytes + (uint32_t)c * 16u;
+    const uint32_t soff = (uint32_t)(2 * j) * row_bytes + (uint32_t)(v0 * 2);
+    buffer_copy(r, img + j * 1024, voff, soff);
+  }
+}
+
+__device__ __forceinline__ void given_tile_read(const uint8_t* img, int wm, int wn, int lane, WaveAcc& out) {
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int tr = acc_col(wn, nb, lane);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int vl = acc_row(wm, mb, 0, lane);
+      const uint2 u = *reinterpret_cast<const uint2*>(img + tr * (kGivenVocab * 2) +
+                                                      (((vl >> 3) ^ (tr & 15)) << 4) + (vl & 7) * 2);
+      out[mb][nb][0] = __uint_as_float(u.x << 16);
+      out[mb][nb][1] = __uint_as_float(u.x & 0xffff0000u);
+      out[mb][nb][2] = __uint_as_float(u.y << 16);
+      out[mb][nb][3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+  }
+}
+
+// Given logits of this tile: staged through LDS (flag 2, pipelined geometry;
+// `stage` already issued its copies and the main loop has ended), else loaded
+// from memory (flag 1: 4-element vectors, 0: elements).
+template <typename T, class G>
+__device__ __forceinline__ void given_tile(const T* L, int64_t n, int64_t v, int64_t t0, int64_t v0,
+                                           int flag, const uint8_t* img, int w, int wm, int wn,
+                                           int lane, WaveAcc& out) {
+  if constexpr (G::kPipe) {
+    if (flag == 2) {
+      if (w < 4) wait_vmcnt<0>();  // group A issued the copies
+      pipe_barrier();
+      given_tile_read(img, wm, wn, lane, out);
+      return;
+    }
+  }
+  load_logits_tile<T>(L, n, v, t0, v0, wm, wn, lane, flag != 0, out);
+}
+
 // ---------------------------------------------------------------------------
 // Forward tile kernel
 // ---------------------------------------------------------------------------
@@ -249,14 +313,16 @@ struct FwdArgs {
   float cT, cTt, rho;   // log2(e) / T_s, log2(e) / T_t, T_s / T_t
   int need_zT, need_t1;
   int kl;      // KD_KL_*: the reverse direction also needs sum 2^(z~ - m) (z - t)
-  int vec;     // the given logits matrix loads as 4-element vectors
+  int vec;     // given logits: 2 staged through LDS, 1 vector loads, 0 element loads
   float* rec;  // [kRecFields][n_slices][n]
 };
 
 template <typename T, int MODE, class G>
 __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G::template lds_bytes<NB>()];
+  constexpr bool kGiven = MODE == MODE_TLOGITS || MODE == MODE_LOGITS;  // one logits tile is given
+  constexpr int kMainBytes = G::template lds_bytes<NB>();
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int slice, tt;  // slice = the vocabulary tile of this workgroup
@@ -285,14 +351,21 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   } else if constexpr (MODE == MODE_TLOGITS) {
+    const T* L = static_cast<const T*>(a.tlogits);
+    if constexpr (G::kPipe)
+      if (a.vec == 2 && w < 4)
+        given_tile_copy(L, a.n, a.v, t0, v0, lds + kMainBytes, __builtin_amdgcn_readfirstlane(w), lane);
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    load_logits_tile<T>(static_cast<const T*>(a.tlogits), a.n, a.v, t0, v0, wm, wn, lane, a.vec != 0,
-                        tacc[0]);
+    given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, tacc[0]);
   } else {  // MODE_LOGITS
+    const T* L = static_cast<const T*>(a.logits);
+    if constexpr (G::kPipe)
+      if (a.vec == 2 && w < 4)
+        given_tile_copy(L, a.n, a.v, t0, v0, lds + kMainBytes, __builtin_amdgcn_readfirstlane(w), lane);
     const T* const bt[1] = {ht};
     tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-    load_logits_tile<T>(static_cast<const T*>(a.logits), a.n, a.v, t0, v0, wm, wn, lane, a.vec != 0, zl);
+    given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, zl);
   }
 
   // Epilogue: this tile's statistics of every token, in two passes over the
@@ -697,7 +770,7 @@ struct BwdArgs {
   float cTt, rho;         // log2(e) / T_t, T_s / T_t
   int need_zT;
   int kl;                 // KD_KL_*
-  int vec;                // teacher logits load as 4-element vectors
+  int vec;                // teacher logits: 2 staged through LDS, 1 vector loads, 0 element loads
   int64_t c0;             // first vocabulary row of the chunk
   int n_vt, n_ttiles;     // tiles of the chunk
   void* dz;               // [dz_rows][ldz]
@@ -722,7 +795,9 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, fl
 template <typename T, int MODE, class G>
 __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G::template lds_bytes<NB>()];
+  constexpr bool kGiven = MODE == MODE_TLOGITS;
+  constexpr int kMainBytes = G::template lds_bytes<NB>();
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   int vt, tt;
@@ -745,10 +820,13 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const T* const bt[1] = {ht};
     tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
   } else if constexpr (MODE == MODE_TLOGITS) {
+    const T* L = static_cast<const T*>(a.tlogits);
+    if constexpr (G::kPipe)
+      if (a.vec == 2 && w < 4)
+        given_tile_copy(L, a.n, a.v, t0, v0, lds + kMainBytes, __builtin_amdgcn_readfirstlane(w), lane);
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    load_logits_tile<T>(static_cast<const T*>(a.tlogits), a.n, a.v, t0, v0, wm, wn, lane, a.vec != 0,
-                        tacc[0]);
+    given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, tacc[0]);
   } else {  // MODE_TOPK
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
@@ -967,11 +1045,16 @@ struct Launch {
     if (st_ != KD_OK) return st_;     \
   } while (0)
 
-// A given [n x v] logits matrix loads a lane's four consecutive elements as one
-// vector when every row start keeps the vector alignment.
-template <typename T>
-int vector_ok(const void* ptr, int64_t v) {
-  return (ptr != nullptr && v % 4 == 0 && ((uintptr_t)ptr % (4 * sizeof(T))) == 0) ? 1 : 0;
+// How a given [n x v] logits matrix is read: 2 = staged through LDS with
+// 16-byte buffer loads (pipelined bf16 tiles: v a multiple of 8, 16-byte
+// aligned, v up to 2^23), 1 = a lane's four consecutive elements as one vector (v a multiple
+// of 4, vector-aligned), 0 = element by element.
+template <typename T, class G>
+int given_mode(const void* ptr, int64_t v) {
+  if (ptr == nullptr) return 0;
+  // (the copy offsets of a 128-row tile are 32-bit: 128 rows of 2 v bytes)
+  if (G::kPipe && sizeof(T) == 2 && v % 8 == 0 && v <= (1 << 23) && (uintptr_t)ptr % 16 == 0) return 2;
+  return (v % 4 == 0 && ((uintptr_t)ptr % (4 * sizeof(T))) == 0) ? 1 : 0;
 }
 
 template <typename T, class G>
@@ -1002,7 +1085,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   const void* given = (p.mode == MODE_TLOGITS) ? x.tlogits : x.logits;
   FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
              p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, kLog2e / p.Tt, p.T / p.Tt,
-             p.need_zT, need_t1, p.kl, vector_ok<T>(given, p.v), rec};
+             p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v), rec};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
@@ -1043,7 +1126,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     const int n_vt = (int)((cw + G::kVT - 1) / G::kVT);  // fused tiles of the chunk
     BwdArgs ba{x.hs, x.w, x.ht, x.wt, x.tlogits, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
                static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T,
-               kLog2e / p.Tt, p.T / p.Tt, p.need_zT, p.kl, vector_ok<T>(x.tlogits, p.v),
+               kLog2e / p.Tt, p.T / p.Tt, p.need_zT, p.kl, given_mode<T, G>(x.tlogits, p.v),
                c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
