@@ -46,6 +46,10 @@ Readings of points the pages leave open (each is also listed in the design doc):
       reverse-KL term (with a nonzero student probability) is +inf.
   R21 a loss term whose weight is 0 is absent from the loss, not 0 times its
       value (which may be infinite, e.g. the teacher CE of R20's columns).
+  R22 with compact_valid the rows whose label is ignored are excluded from the
+      KL too (orda-kernel, Parameters: ignore_index is excluded from CE and
+      KL; nemo kd_loss: only valid tokens are processed): their per-token KL
+      is 0. Without it the KL is reported for every row (R3).
   --  a label outside [0, V) that is not ignore_index is treated as ignored.
 
 Parity pins for every function live in tests/test_oracle.py (closed forms,
@@ -85,6 +89,9 @@ class Params:
     kl_divergence: str = "forward"  # "forward" | "reverse" | "jeffreys"
     # orda-kernel, Parameters (kl_teacher_temperature): None means T_s.
     teacher_temperature: Optional[float] = None
+    # Rows whose label is ignored are left out of the per-token KL as well
+    # (reading R22); the loss and the gradients do not change.
+    compact_valid: bool = False
 
 
 def teacher_temperature(p: Params) -> float:
@@ -369,8 +376,8 @@ def per_token(student: Student, teacher: Teacher, p: Params, labels=None,
         t = _teacher_logits(teacher, student, r)
         if labels is not None:
             out["teacher_ce"][b:b + len(r)] = cross_entropy(t, lab[r], vb)
-        out["kl"][b:b + len(r)] = kl_term(z, t, p.temperature, p.kl_divergence,
-                                          teacher_temperature(p))
+        kl = kl_term(z, t, p.temperature, p.kl_divergence, teacher_temperature(p))
+        out["kl"][b:b + len(r)] = np.where(vb, kl, 0.0) if p.compact_valid else kl
     return out
 
 

@@ -351,6 +351,23 @@ def check_zero_weight_term_is_absent(O):
            what="zero-weighted infinite teacher CE")
 
 
+def check_compact_valid_changes_only_ignored_kl(O):
+    """compact_valid zeroes the per-token KL of ignored rows and leaves the
+    loss, the valid rows' KL and the gradients exactly as they were (the
+    ignored rows never entered them)."""
+    s, t = _tied_case(O, n=6, d=5, v=10, k=13)
+    y = np.array([3, -100, 9, -100, 0, 4])
+    a = O.Params(student_ce_weight=0.7, kl_weight=1.0, temperature=2.0)
+    b = O.Params(student_ce_weight=0.7, kl_weight=1.0, temperature=2.0, compact_valid=True)
+    fa, fb = O.forward(s, t, a, y), O.forward(s, t, b, y)
+    assert fa["loss"] == fb["loss"]
+    valid = y != -100
+    assert (fb["kl"][~valid] == 0).all() and (fa["kl"][~valid] > 0).all()
+    assert np.array_equal(fa["kl"][valid], fb["kl"][valid])
+    for ga, gb in zip(O.backward(s, t, a, y), O.backward(s, t, b, y)):
+        assert np.array_equal(ga, gb)
+
+
 def check_logits_teacher_matches_projection(O):
     """A dense cached teacher holding H_t W_t^T gives the separate teacher's
     per-token values and gradients."""

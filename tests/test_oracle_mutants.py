@@ -47,6 +47,8 @@ MUTANTS = {
                                         "return as_f64(t.logits[rows][:, ::-1])"),
     "zero_weight_term_multiplied": ("        if w_term != 0.0:\n            contrib = contrib + w_term * term",
                                     "        contrib = contrib + w_term * term"),
+    "compact_keeps_ignored_kl": ("np.where(vb, kl, 0.0) if p.compact_valid else kl",
+                                 "kl if p.compact_valid else kl"),
     "kl_reversed": ("(q * np.where(q > 0, lp_t - lp_s, 0.0))", "(np.exp(lp_s) * (lp_s - lp_t))"),
     "ce_label_off_by_one": ("picked = np.take_along_axis(logits, y[:, None], axis=1)",
                             "picked = np.take_along_axis(logits, (y[:, None] + 1) % logits.shape[1], axis=1)"),
