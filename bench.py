@@ -178,7 +178,8 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
             for k, v in x.items()}
     p = O.Params(student_ce_weight=w.student_ce_weight, teacher_ce_weight=w.teacher_ce_weight,
                  kl_weight=w.kl_weight, temperature=w.temperature, ignore_index=w.ignore_index,
-                 kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature)
+                 kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature,
+                 compact_valid=w.compact_valid)
 
     def run(rows: int) -> float:
         g = lambda k: None if full[k] is None else full[k][:rows]  # noqa: E731
@@ -217,6 +218,12 @@ def main() -> int:
     ap.add_argument("--d", type=int, default=0, help="override the student hidden size")
     ap.add_argument("--v", type=int, default=0, help="override the vocabulary size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--compact", action="store_true",
+                    help="leave rows with an ignored label out of the projections (compact_valid)")
+    ap.add_argument("--kl", choices=("forward", "reverse", "jeffreys"), default=None,
+                    help="override the workload's KL direction")
+    ap.add_argument("--ignore-frac", type=float, default=None,
+                    help="override the fraction of rows whose label is ignored")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="copy a buffer of this many MiB once before the timed steps, so a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known transfer")
@@ -254,8 +261,17 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     over = {k: getattr(args, k) for k in ("n", "d", "v") if getattr(args, k)}
+    if args.kl:
+        over["kl_divergence"] = args.kl
+    if args.compact:
+        over["compact_valid"] = True
+    if args.ignore_frac is not None:
+        over["ignore_frac"] = args.ignore_frac
     if over:
-        w = w.scaled(name=w.name + "_" + "_".join(f"{k}{v}" for k, v in over.items()), **over)
+        tag = {"kl_divergence": lambda v: v, "compact_valid": lambda v: "compact",
+               "ignore_frac": lambda v: f"ignore{v:g}"}
+        w = w.scaled(name=w.name + "_" + "_".join(tag[k](v) if k in tag else f"{k}{v}"
+                                                  for k, v in over.items()), **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = make_inputs(w, dev, seed=0)
@@ -264,7 +280,8 @@ def main() -> int:
               teacher_ce_weight=w.teacher_ce_weight, kl_weight=w.kl_weight,
               temperature=w.temperature, ignore_index=w.ignore_index,
               vocab_chunk=args.vocab_chunk, want_grads=not w.forward_only,
-              kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature)
+              kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature,
+              compact_valid=w.compact_valid)
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:
@@ -358,6 +375,7 @@ def main() -> int:
         "config": {"workload": w.name, "n_tokens": w.n, "hidden": w.d, "teacher_hidden": w.teacher_dim,
                    "vocab": w.v, "teacher": w.teacher, "temperature": w.temperature,
                    "teacher_temperature": w.teacher_temperature, "kl_divergence": w.kl_divergence,
+                   "compact_valid": w.compact_valid, "ignored_rows": w.ignore_frac,
                    "top_k": w.k or None, "vocab_chunk": chunk, "parallelism": "single GPU"},
         "mfma_tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / peak_tflops, 4),

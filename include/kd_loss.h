@@ -138,6 +138,13 @@ typedef struct {
   int32_t kl_divergence;     /* KD_KL_* */
   float teacher_temperature; /* T_t > 0, finite: the teacher's own temperature (orda-kernel,
                                 Parameters: kl_teacher_temperature); 0 = T. TOPK: 0 or 1 */
+  int32_t compact_valid;     /* 1: rows whose label is ignored (or out of range) are left out of
+                                every projection and GEMM (orda-kernel, Parameters: ignore_index is
+                                excluded from CE and KL); their per-token outputs are 0, the loss
+                                and gradients are unchanged. TIED and SEPARATE teachers with labels
+                                only (else KD_ERR_UNSUPPORTED); workspaces grow by
+                                8 n + 16 ceil(n/128) (d + d_t) bytes (bf16). 0: every row is
+                                projected and its KL reported. */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).

@@ -37,7 +37,7 @@ class KdParams(ctypes.Structure):
                 ("kl_weight", c_float), ("temperature", c_float), ("ignore_index", c_int64),
                 ("reduction", c_int32), ("normalizer", c_float), ("vocab_chunk", c_int64),
                 ("assume_valid_labels", c_int32), ("kl_divergence", c_int32),
-                ("teacher_temperature", c_float)]
+                ("teacher_temperature", c_float), ("compact_valid", c_int32)]
 
 
 class KdOutputs(ctypes.Structure):

@@ -121,7 +121,8 @@ class Runner:
                  topk_prob=None, teacher_logits=None, student_ce_weight=1.0,
                  teacher_ce_weight=0.0, kl_weight=0.0, temperature=1.0, ignore_index=-100,
                  reduction="mean", normalizer=0.0, vocab_chunk=0, want_grads=True,
-                 want_teacher_ce=None, kl_divergence="forward", teacher_temperature=None):
+                 want_teacher_ce=None, kl_divergence="forward", teacher_temperature=None,
+                 compact_valid=False):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -186,6 +187,7 @@ class Runner:
             raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
         p.kl_divergence = _KL_DIVERGENCES[kl_divergence]
         p.teacher_temperature = 0.0 if teacher_temperature is None else float(teacher_temperature)
+        p.compact_valid = 1 if compact_valid else 0
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
         f32 = dict(dtype=torch.float32, device=self.device)
@@ -318,14 +320,16 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
                       teacher_ce_weight=0.0, kl_weight=0.0, kl_temperature=1.0,
                       kl_teacher_temperature=None, kl_divergence="forward", ignore_index=-100,
                       reduction="mean", num_batch_labels=None, vocab_chunk=0,
-                      return_teacher_ce=True) -> DistillationLossOutput:
+                      return_teacher_ce=True, compact_valid=False) -> DistillationLossOutput:
     """Fused LM-head + CE + KL loss; differentiable in student_hidden and weight.
 
     The teacher is always detached. Returns the loss and the unweighted per-token
     components (student_ce, teacher_ce, kl with T^2 included). With
     return_teacher_ce=False and teacher_ce_weight=0 the teacher CE is skipped
     (one exponential pass fewer per tile when the temperature is not 1) and
-    reported as zeros.
+    reported as zeros. compact_valid=True leaves the rows whose label is
+    ignored out of every projection (tied and projected teachers): their
+    per-token terms are reported as 0, the loss and gradients are unchanged.
     """
     if kl_divergence not in _KL_DIVERGENCES:
         raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
@@ -333,7 +337,8 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
         raise NotImplementedError("the top-K teacher supports kl_divergence='forward' only")
     if kl_teacher_temperature is not None and not kl_teacher_temperature > 0:
         raise ValueError("kl_teacher_temperature must be positive")
-    kw = dict(kl_divergence=kl_divergence, teacher_temperature=kl_teacher_temperature, student_hidden=student_hidden.detach().contiguous(),
+    kw = dict(kl_divergence=kl_divergence, teacher_temperature=kl_teacher_temperature,
+              student_hidden=student_hidden.detach().contiguous(),
               weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
               teacher_ce_weight=teacher_ce_weight, kl_weight=kl_weight,
               temperature=kl_temperature, ignore_index=ignore_index, reduction=reduction,
@@ -354,6 +359,9 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
         labels = None
     else:
         raise TypeError(f"unknown teacher descriptor {type(teacher).__name__}")
+    if compact_valid and (labels is None or kw["teacher_kind"] not in ("tied", "separate")):
+        raise NotImplementedError("compact_valid needs labels and a tied or projected teacher")
+    kw["compact_valid"] = bool(compact_valid)
     if labels is not None:
         kw["labels"] = labels.to(torch.int64).contiguous()
     runner = Runner(**kw)

@@ -109,6 +109,9 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
     return KD_ERR_NULL;
   }
   if (check_labels_ptr && labels && ((uintptr_t)labels & 7u)) return KD_ERR_ALIGN;
+  if (p->compact_valid != 0 && p->compact_valid != 1) return KD_ERR_PARAM;
+  if (p->compact_valid && q.mode != kd::MODE_TIED && q.mode != kd::MODE_SEPARATE)
+    return KD_ERR_UNSUPPORTED;
 
   q.ws = p->student_ce_weight;
   q.wt = p->teacher_ce_weight;
@@ -125,6 +128,9 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   // Teacher statistics at t (T = 1) beside those at t/T_t, for the teacher CE.
   q.need_t1 = (q.Tt != 1.f && q.mode != kd::MODE_TOPK) ? 1 : 0;
   q.has_labels = labels ? 1 : 0;
+  // Without labels no row is ignored; the workspace query (labels unknown)
+  // still reserves the compaction buffers.
+  q.compact = (p->compact_valid && (labels || !check_labels_ptr)) ? 1 : 0;
 
   // Tile geometry: bf16 with every contraction length a multiple of 64 runs the
   // pipelined 256-row tiles; everything else the register-staged 128-row tiles.
@@ -147,7 +153,21 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.n_chunks = (int)ceil_div(q.v, chunk);
   q.merge_blocks = (int)ceil_div(q.n, kd::kMergeTok);
 
+  const size_t elem = (q.dtype == KD_BF16) ? 2 : 4;
+  q.dz_rows = (int64_t)q.n_ttiles * kTile;
+  // Compaction buffers first, at the same offsets in both workspaces.
   size_t off = kd::kStatusBytes;
+  if (q.compact) {
+    q.off_cidx = off;
+    off = align_up(off + 4 * (size_t)q.n, 256);
+    q.off_cpos = off;
+    off = align_up(off + 4 * (size_t)q.n, 256);
+    q.off_hc = off;
+    off = align_up(off + (size_t)q.dz_rows * (size_t)q.d * elem, 256);
+    q.off_htc = off;
+    off = align_up(off + (size_t)q.dz_rows * (size_t)q.dt * elem, 256);
+  }
+  const size_t off_common = off;
   q.off_prep = off;
   off = align_up(off + 4 * sizeof(float) * (size_t)q.n, 256);
   q.off_rec = off;
@@ -155,9 +175,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.off_part = off;
   off = align_up(off + (size_t)q.merge_blocks * 4 * sizeof(double), 256);
   q.fwd_bytes = off;
-  const size_t elem = (q.dtype == KD_BF16) ? 2 : 4;
-  q.dz_rows = (int64_t)q.n_ttiles * kTile;
-  q.off_dz = kd::kStatusBytes;
+  q.off_dz = off_common;
   q.bwd_bytes = align_up(q.off_dz + (size_t)q.dz_rows * (size_t)q.chunk * elem, 256);
   *out = q;
   return KD_OK;

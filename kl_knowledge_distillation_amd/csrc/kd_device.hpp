@@ -69,6 +69,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return x * per + min(x, rem) + local;
 }
 
+// The same split for a grid sized for more tiles than have work: only the
+// first `live` tiles (in tile order) do, and they are spread evenly over the
+// XCDs. Returns false for a block past its XCD's share (it has nothing to do).
+// With live == nblocks this is xcd_remap.
+__device__ __forceinline__ bool xcd_live_tile(int bid, int live, int& t) {
+  const int per = live / kXcds, rem = live % kXcds;
+  const int x = bid % kXcds, local = bid / kXcds;
+  if (local >= per + (x < rem ? 1 : 0)) return false;
+  t = x * per + min(x, rem) + local;
+  return true;
+}
+
 // Grouped order over an (na x nb) grid of tiles: runs of `group` consecutive
 // b values for each a, so a window of consecutive tiles covers a near-square
 // block and both operands are re-read from L2 rather than HBM.

@@ -20,8 +20,10 @@ constexpr int kRecFields = 10;
 // Tokens per merge workgroup; also the number of partial sums per block.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeTok = 16;  // tokens per merge workgroup
-// Bytes reserved at the start of the workspace for device flags.
+// Bytes reserved at the start of the workspace for device flags (int32 at 0)
+// and the compacted row count (int32 at kNvOffset).
 constexpr size_t kStatusBytes = 256;
+constexpr size_t kNvOffset = 8;
 // Offset of the header inside `saved` is 16 * n; its size is 64 bytes.
 constexpr size_t kSavedHeaderBytes = 64;
 
@@ -39,6 +41,7 @@ struct Plan {
   int need_zT = 0;    // statistics at z/T kept apart from z (T != 1, or a reverse-direction KL)
   int need_t1 = 0;    // teacher statistics at t kept apart from t/T_t (T_t != 1)
   int has_labels = 0;
+  int compact = 0;    // rows with an ignored label left out of the tiles and GEMMs
   int pipe = 0;       // bf16 with hidden sizes multiple of 32: 256-row pipelined tiles
   int vt_rows = 128;  // vocabulary rows per fused tile
   int n_ttiles = 0, n_vtiles = 0, tps = 1, n_slices = 0;  // forward grid
@@ -50,6 +53,9 @@ struct Plan {
   size_t off_prep = 0, off_rec = 0, off_part = 0, fwd_bytes = 0;
   // backward workspace layout
   size_t off_dz = 0, bwd_bytes = 0;
+  // compaction buffers (same offsets in both workspaces): idx, pos [n] int32,
+  // compacted H_s [dz_rows x d] and H_t [dz_rows x dt] in the input dtype
+  size_t off_cidx = 0, off_cpos = 0, off_hc = 0, off_htc = 0;
 };
 
 struct Tensors {

@@ -315,6 +315,7 @@ struct FwdArgs {
   int kl;      // KD_KL_*: the reverse direction also needs sum 2^(z~ - m) (z - t)
   int vec;     // given logits: 2 staged through LDS, 1 vector loads, 0 element loads
   float* rec;  // [kRecFields][n_slices][n]
+  const int32_t* nv;  // compacted rows: their number (tiles past it exit); null = n
 };
 
 template <typename T, int MODE, class G>
@@ -324,9 +325,13 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int kMainBytes = G::template lds_bytes<NB>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // Compacted rows: only the token tiles below nv have work; they are mapped
+  // onto the first blocks of every XCD and the rest of the grid exits.
+  const int n_tt = a.nv ? (int)((*a.nv + G::kTT - 1) / G::kTT) : a.n_ttiles;
+  int t;
+  if (!xcd_live_tile(blockIdx.x, a.n_slices * n_tt, t)) return;
   int slice, tt;  // slice = the vocabulary tile of this workgroup
-  grouped_tile(t, a.n_slices, a.n_ttiles, 8, slice, tt);
+  grouped_tile(t, a.n_slices, n_tt, 8, slice, tt);
   const int64_t t0 = (int64_t)tt * G::kTT;
   const int64_t v0 = (int64_t)slice * G::kVT;
 
@@ -599,6 +604,7 @@ struct MergeArgs {
   float* out_kl;
   float* saved;       // [n][4] or null: lse(z), lse(z/T), lse(t/T), M (top-K) or KL(P_S||P_T)
   double* partials;   // [blocks][4]: loss sum, valid count, bad count, 0
+  const int32_t* pos; // compacted rows: record column of row i, -1 = left out; null = i
 };
 
 // A workgroup takes kMergeTok tokens; thread (token tl, group sg) folds the
@@ -611,12 +617,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int tid = threadIdx.x, tl = tid % kMergeTok, sg = tid / kMergeTok;
   const int64_t i = (int64_t)blockIdx.x * kMergeTok + tl;
   const bool live = i < a.n;
+  // record column of this row: its compacted position, or -1 for a row the
+  // compacted tiles left out (its label is ignored)
+  const int64_t col = (live && a.pos) ? a.pos[i] : i;
+  const bool has = live && col >= 0;
   RowStats s;
   stats_init(s);
-  if (live) {
+  if (has) {
     const int64_t stride = (int64_t)a.n_slices * a.n;
     for (int sl = sg; sl < a.n_slices; sl += kGroups) {
-      const float* r = a.rec + (int64_t)sl * a.n + i;
+      const float* r = a.rec + (int64_t)sl * a.n + col;
       RowStats o;
       o.mz1 = r[0 * stride]; o.sz1 = r[1 * stride]; o.mzT = r[2 * stride];
       o.szT = r[3 * stride]; o.mtT = r[4 * stride]; o.stT = r[5 * stride];
@@ -640,7 +650,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       stats_merge(s, o);
     }
     double contrib = 0.0, cnt = 0.0, bad = 0.0;
-    if (live) {
+    if (live && !has) {
+      // left out by the compaction: an ignored label, excluded from CE and KL
+      bad = (a.prep[3 * a.n + i] == 2.f) ? 1.0 : 0.0;
+      if (a.out_sce) a.out_sce[i] = 0.f;
+      if (a.out_tce) a.out_tce[i] = 0.f;
+      if (a.out_kl) a.out_kl[i] = 0.f;
+      if (a.saved) reinterpret_cast<float4*>(a.saved)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (live) {
       const float lz1 = kLn2 * (s.mz1 + log2f(s.sz1));
       const float lzT = a.need_zT ? kLn2 * (s.mzT + log2f(s.szT)) : lz1;
       const float f0 = a.prep[i], f1 = a.prep[a.n + i], f2 = a.prep[2 * a.n + i];
@@ -771,6 +788,8 @@ struct BwdArgs {
   int need_zT;
   int kl;                 // KD_KL_*
   int vec;                // teacher logits: 2 staged through LDS, 1 vector loads, 0 element loads
+  const int32_t* idx;     // compacted rows: original row of each (null: rows are original)
+  const int32_t* nv;      // compacted rows: their number
   int64_t c0;             // first vocabulary row of the chunk
   int n_vt, n_ttiles;     // tiles of the chunk
   void* dz;               // [dz_rows][ldz]
@@ -799,9 +818,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int kMainBytes = G::template lds_bytes<NB>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  // Compacted rows: token tiles from round_up(nv, 128) on would hold only zero
+  // rows, which no GEMM reads (their K and M stop at nv); only the tiles below
+  // are mapped, onto the first blocks of every XCD.
+  const int64_t n_live = a.nv ? *a.nv : a.n;
+  const int n_tt = a.nv ? (int)((n_live + G::kTT - 1) / G::kTT) : a.n_ttiles;
+  int t;
+  if (!xcd_live_tile(blockIdx.x, a.n_vt * n_tt, t)) return;
   int vt, tt;
-  grouped_tile(t, a.n_vt, a.n_ttiles, 8, vt, tt);
+  grouped_tile(t, a.n_vt, n_tt, 8, vt, tt);
   const int64_t v0 = a.c0 + (int64_t)vt * G::kVT;
   const int64_t t0 = (int64_t)tt * G::kTT;
   const T* hs = static_cast<const T*>(a.hs);
@@ -847,13 +872,14 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   for (int nb = 0; nb < kNB; ++nb) {
     const int64_t tok = t0 + acc_col(wn, nb, lane);
     if (tok >= a.dz_rows) continue;
-    const bool live = tok < a.n;  // rows past n are zero padding of the slab
-    const float4 sv = live ? reinterpret_cast<const float4*>(a.saved)[tok] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool live = tok < n_live;  // rows past n (or nv) are zero padding of the slab
+    const int64_t orig = (live && a.idx) ? a.idx[tok] : tok;  // original row
+    const float4 sv = live ? reinterpret_cast<const float4*>(a.saved)[orig] : make_float4(0.f, 0.f, 0.f, 0.f);
     const float L1 = sv.x * kLog2e, LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
     int64_t y = -1;
     bool valid = live;
     if (live && MODE != MODE_TOPK && a.labels) {
-      y = a.labels[tok];
+      y = a.labels[orig];
       valid = y != a.ignore && y >= 0 && y < a.v;
     }
     const float coef = valid ? g / den : 0.f;
@@ -929,6 +955,92 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Compaction of the rows with a usable label (the others never enter the loss)
+// ---------------------------------------------------------------------------
+
+// idx[c] = the c-th row (in row order) whose label is usable, pos[i] = the
+// compacted position of row i or -1, *nv = the number of such rows. One
+// workgroup: thread t counts the rows of its segment, a workgroup scan of the
+// counts gives each segment its first position, then the segment is written.
+constexpr int kCompactThreads = 1024;
+struct CompactArgs {
+  const int64_t* labels;
+  int64_t n, v, ignore;
+  int32_t* idx;
+  int32_t* pos;
+  int32_t* nv;
+};
+
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(CompactArgs a) {
+  __shared__ int32_t sc[kCompactThreads];
+  const int t = threadIdx.x;
+  const int64_t seg = (a.n + kCompactThreads - 1) / kCompactThreads;
+  const int64_t r0 = min(a.n, (int64_t)t * seg), r1 = min(a.n, r0 + seg);
+  auto usable = [&](int64_t i) {
+    const int64_t y = a.labels[i];
+    return y != a.ignore && y >= 0 && y < a.v;
+  };
+  int cnt = 0;
+  for (int64_t i = r0; i < r1; ++i) cnt += usable(i) ? 1 : 0;
+  sc[t] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kCompactThreads; off <<= 1) {  // inclusive scan
+    const int x = (t >= off) ? sc[t - off] : 0;
+    __syncthreads();
+    sc[t] += x;
+    __syncthreads();
+  }
+  int c = sc[t] - cnt;
+  for (int64_t i = r0; i < r1; ++i) {
+    if (usable(i)) {
+      a.idx[c] = (int32_t)i;
+      a.pos[i] = c++;
+    } else {
+      a.pos[i] = -1;
+    }
+  }
+  if (t == kCompactThreads - 1) *a.nv = sc[t];
+}
+
+// out[c, :] = in[idx[c], :] for c < nv and 0 for nv <= c < rows, in 16-byte
+// pieces (row_bytes is a multiple of 16); one wave per row.
+// Two matrices per launch (blockIdx.y selects one: student, teacher hidden).
+struct GatherArgs {
+  const uint8_t* in[2];
+  uint8_t* out[2];
+  int64_t row_bytes[2];
+  const int32_t* idx;
+  const int32_t* nv;
+  int64_t rows;
+};
+
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.y;
+  const int64_t c = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (c >= a.rows) return;
+  const int64_t rb = a.row_bytes[m];
+  uint4* dst = reinterpret_cast<uint4*>(a.out[m] + c * rb);
+  const int64_t pieces = rb / 16;
+  if (c < *a.nv) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.in[m] + (int64_t)a.idx[c] * rb);
+    for (int64_t j = lane; j < pieces; j += 64) dst[j] = src[j];
+  } else {
+    for (int64_t j = lane; j < pieces; j += 64) dst[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// Rows i with pos[i] < 0 (left out by the compaction) of an fp32 [n x d] matrix
+// set to zero; one wave per row.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(float* m, const int32_t* pos, int64_t n,
+                                                              int64_t d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (i >= n || pos[i] >= 0) return;
+  for (int64_t j = lane; j < d; j += 64) m[i * d + j] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
 // GEMM for dW and dH: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output
 // ---------------------------------------------------------------------------
 
@@ -940,18 +1052,25 @@ struct GemmArgs {
   int64_t ldc, M, N, K;
   int accumulate;
   int n_mt, n_nt;
+  const int32_t* kdev;    // non-null: K = min(K, *kdev) (compacted token rows)
+  const int32_t* mdev;    // non-null: M = min(M, *mdev)
+  const int32_t* rowmap;  // non-null: C row m is stored at row rowmap[m]
 };
 
 template <typename T, bool AKC, bool BKC>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC> a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 2 * kTileBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t M = a.mdev ? min(a.M, (int64_t)*a.mdev) : a.M;
+  const int64_t K = a.kdev ? min(a.K, (int64_t)*a.kdev) : a.K;
+  const int n_mt = a.mdev ? (int)((M + kTile - 1) / kTile) : a.n_mt;  // row tiles with work
+  int t;
+  if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
   int mt, nt;
-  grouped_tile(t, a.n_mt, a.n_nt, 8, mt, nt);
+  grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
   const int64_t m0 = (int64_t)mt * kTile, n0 = (int64_t)nt * kTile;
   f32x4 acc[1][kMB][kNB];
-  mainloop<T, AKC, BKC, 1>(a.A, &a.B, m0, n0, a.K, lds, acc, tid);
+  mainloop<T, AKC, BKC, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -961,8 +1080,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + acc_row(wm, mb, r, lane);
-        if (row < a.M) {
-          float* p = a.C + row * a.ldc + col;
+        if (row < M) {
+          float* p = a.C + (a.rowmap ? (int64_t)a.rowmap[row] : row) * a.ldc + col;
           const float vv = acc[0][mb][nb][r];
           *p = a.accumulate ? *p + vv : vv;
         }
@@ -982,6 +1101,9 @@ struct GemmPipeArgs {
   int64_t ldc, M, N, K;
   int accumulate;
   int n_mt, n_nt;
+  const int32_t* kdev;    // non-null: K = min(K, round_up(*kdev, 64)) (compacted token rows)
+  const int32_t* mdev;    // non-null: M = min(M, *mdev)
+  const int32_t* rowmap;  // non-null: C row m is stored at row rowmap[m]
 };
 
 template <bool AKC, bool BKC, int BN>
@@ -989,12 +1111,25 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
   using C = PipeCfg<256, BN, 1, AKC, BKC>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t M = a.mdev ? min(a.M, (int64_t)*a.mdev) : a.M;
+  const int64_t K = a.kdev ? min(a.K, ((int64_t)*a.kdev + kPipeBK - 1) / kPipeBK * kPipeBK) : a.K;
+  const int n_mt = a.mdev ? (int)((M + 255) / 256) : a.n_mt;  // row tiles with work
+  int t;
+  if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
   int mt, nt;
-  grouped_tile(t, a.n_mt, a.n_nt, 8, mt, nt);
+  grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
   const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
   f32x4 acc[1][C::MB][C::NBK];
-  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, a.K, lds, acc, tid);
+  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid);
+  // output row of each of this lane's MB x 4 accumulator rows
+  int64_t orow[C::MB][4];
+#pragma unroll
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + pipe_row<C>(wm, mb, r, lane);
+      orow[mb][r] = (row >= M) ? -1 : (a.rowmap ? (int64_t)a.rowmap[row] : row);
+    }
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
@@ -1003,9 +1138,8 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
       if (col >= a.N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + pipe_row<C>(wm, mb, r, lane);
-        if (row < a.M) {
-          float* p = a.C + row * a.ldc + col;
+        if (orow[mb][r] >= 0) {
+          float* p = a.C + orow[mb][r] * a.ldc + col;
           const float vv = acc[0][mb][nb][r];
           *p = a.accumulate ? *p + vv : vv;
         }
@@ -1057,6 +1191,33 @@ int given_mode(const void* ptr, int64_t v) {
   return (v % 4 == 0 && ((uintptr_t)ptr % (4 * sizeof(T))) == 0) ? 1 : 0;
 }
 
+// Compaction of the usable-label rows into workspace copies of the token-side
+// operands: idx / pos / nv, then H_s (and H_t) gathered into hc / htc.
+struct Compacted {
+  const int32_t* idx;
+  const int32_t* pos;
+  const int32_t* nv;
+  const void* hs;
+  const void* ht;
+};
+
+template <typename T>
+kd_status compact_rows(const Plan& p, const Tensors& x, uint8_t* base, Launch& L, hipStream_t stream,
+                       Compacted* out) {
+  int32_t* idx = reinterpret_cast<int32_t*>(base + p.off_cidx);
+  int32_t* pos = reinterpret_cast<int32_t*>(base + p.off_cpos);
+  int32_t* nv = reinterpret_cast<int32_t*>(base + kNvOffset);
+  CompactArgs ca{x.labels, p.n, p.v, p.ignore, idx, pos, nv};
+  KD_TRY(L.run(KD_KERNEL_PREP, [&] { compact_kernel<<<1, kCompactThreads, 0, stream>>>(ca); }));
+  const dim3 grid((unsigned)((p.dz_rows + kThreads / 64 - 1) / (kThreads / 64)), 2);
+  GatherArgs ga{{static_cast<const uint8_t*>(x.hs), static_cast<const uint8_t*>(x.ht)},
+                {base + p.off_hc, base + p.off_htc},
+                {p.d * (int64_t)sizeof(T), p.dt * (int64_t)sizeof(T)}, idx, nv, p.dz_rows};
+  KD_TRY(L.run(KD_KERNEL_PREP, [&] { gather_rows_kernel<<<grid, kThreads, 0, stream>>>(ga); }));
+  *out = Compacted{idx, pos, nv, base + p.off_hc, base + p.off_htc};
+  return KD_OK;
+}
+
 template <typename T, class G>
 kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved, void* ws,
                     hipStream_t stream, kd_trace* trace) {
@@ -1080,12 +1241,16 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
     }
   }));
 
+  // Rows with an ignored label left out: the tiles run on compacted copies.
+  Compacted cp{nullptr, nullptr, nullptr, x.hs, x.ht};
+  if (p.compact) KD_TRY(compact_rows<T>(p, x, base, L, stream, &cp));
+
   // Teacher statistics at T = 1 only feed the teacher CE.
   const int need_t1 = (p.need_t1 && pa.want_teacher) ? 1 : 0;
   const void* given = (p.mode == MODE_TLOGITS) ? x.tlogits : x.logits;
-  FwdArgs fa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
+  FwdArgs fa{cp.hs, x.w, cp.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
              p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, kLog2e / p.Tt, p.T / p.Tt,
-             p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v), rec};
+             p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v), rec, cp.nv};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
@@ -1100,7 +1265,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   MergeArgs ma{rec, prep, p.n_slices, p.n, p.mode, p.T, p.need_zT, need_t1,
                (p.mode != MODE_TOPK) ? 1 : 0, p.kl, p.ws, p.wt, p.wkl,
                out ? out->student_ce : nullptr, out ? out->teacher_ce : nullptr,
-               out ? out->kl : nullptr, static_cast<float*>(saved), part};
+               out ? out->kl : nullptr, static_cast<float*>(saved), part, cp.pos};
   ma.teacher_ce = pa.want_teacher;
   KD_TRY(L.run(KD_KERNEL_MERGE, [&] {
     merge_kernel<<<dim3((unsigned)p.merge_blocks), kMergeThreads, 0, stream>>>(ma);
@@ -1120,14 +1285,26 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
   uint8_t* base = static_cast<uint8_t*>(ws);
   T* dz = reinterpret_cast<T*>(base + p.off_dz);
   const int64_t ldz = p.chunk;
+  Compacted cp{nullptr, nullptr, nullptr, x.hs, x.ht};
+  if (p.compact) {
+    KD_TRY(compact_rows<T>(p, x, base, L, stream, &cp));
+    // dH rows of left-out tokens: the compacted GEMMs never write them
+    if (dh && !accumulate) {
+      KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
+        zero_rows_kernel<<<dim3((unsigned)((p.n + kThreads / 64 - 1) / (kThreads / 64))), kThreads, 0,
+                           stream>>>(dh, cp.pos, p.n, p.d);
+      }));
+    }
+  }
+  const T* hs = static_cast<const T*>(cp.hs);
   for (int c = 0; c < p.n_chunks; ++c) {
     const int64_t c0 = (int64_t)c * p.chunk;
     const int64_t cw = (p.v - c0 < p.chunk) ? (p.v - c0) : p.chunk;  // valid columns
     const int n_vt = (int)((cw + G::kVT - 1) / G::kVT);  // fused tiles of the chunk
-    BwdArgs ba{x.hs, x.w, x.ht, x.wt, x.tlogits, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
+    BwdArgs ba{cp.hs, x.w, cp.ht, x.wt, x.tlogits, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
                static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T,
                kLog2e / p.Tt, p.T / p.Tt, p.need_zT, p.kl, given_mode<T, G>(x.tlogits, p.v),
-               c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
+               cp.idx, cp.nv, c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
       switch (p.mode) {
@@ -1157,7 +1334,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
           constexpr int BN = decltype(bn_tag)::value;
           GemmPipeArgs<false, false, BN> ga;
           ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
-          ga.B = PipeOperandMN{static_cast<const T*>(x.hs), p.d, p.d, p.n};
+          ga.B = PipeOperandMN{hs, p.d, p.d, p.n};
           ga.C = dw + c0 * p.d;
           ga.ldc = p.d;
           ga.M = cw;
@@ -1166,6 +1343,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
           ga.accumulate = accumulate;
           ga.n_mt = (int)((cw + 255) / 256);
           ga.n_nt = (int)((p.d + BN - 1) / BN);
+          ga.kdev = cp.nv;  // compacted: the token rows stop at nv
+          ga.mdev = nullptr;
+          ga.rowmap = nullptr;
           return L.run(KD_KERNEL_GEMM_DW, [&] {
             gemm_pipe_kernel<false, false, BN>
                 <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), 512, 0, stream>>>(ga);
@@ -1190,6 +1370,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
           gb.accumulate = (accumulate || c > 0) ? 1 : 0;
           gb.n_mt = (int)((p.n + 255) / 256);
           gb.n_nt = (int)((p.d + BN - 1) / BN);
+          gb.kdev = nullptr;
+          gb.mdev = cp.nv;      // compacted: rows past nv are not tokens
+          gb.rowmap = cp.idx;   // compacted row m is token idx[m]
           return L.run(KD_KERNEL_GEMM_DH, [&] {
             gemm_pipe_kernel<true, false, BN>
                 <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), 512, 0, stream>>>(gb);
@@ -1203,7 +1386,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]; A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n]
       GemmArgs<T, false, false> ga;
       ga.A = Operand<T, false>{dz, ldz, cpad, p.n};
-      ga.B = Operand<T, false>{static_cast<const T*>(x.hs), p.d, p.d, p.n};
+      ga.B = Operand<T, false>{hs, p.d, p.d, p.n};
       ga.C = dw + c0 * p.d;
       ga.ldc = p.d;
       ga.M = cw;
@@ -1212,6 +1395,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       ga.accumulate = accumulate;
       ga.n_mt = n_gemm_mt;
       ga.n_nt = (int)((p.d + kTile - 1) / kTile);
+      ga.kdev = cp.nv;
+      ga.mdev = nullptr;
+      ga.rowmap = nullptr;
       KD_TRY(L.run(KD_KERNEL_GEMM_DW, [&] {
         gemm_kernel<T, false, false>
             <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), kThreads, 0, stream>>>(ga);
@@ -1230,6 +1416,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       gb.accumulate = (accumulate || c > 0) ? 1 : 0;
       gb.n_mt = p.n_ttiles;
       gb.n_nt = (int)((p.d + kTile - 1) / kTile);
+      gb.kdev = nullptr;
+      gb.mdev = cp.nv;
+      gb.rowmap = cp.idx;
       KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
         gemm_kernel<T, true, false>
             <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), kThreads, 0, stream>>>(gb);

@@ -49,6 +49,7 @@ class Workload:
     kl_weight: float = 1.0
     kl_divergence: str = "forward"  # "forward" | "reverse" | "jeffreys"
     teacher_temperature: Optional[float] = None  # None: the student temperature
+    compact_valid: bool = False    # rows with an ignored label left out of the projections
     ignore_index: int = -100
     ignore_frac: float = 0.0
     k: int = 0

@@ -39,7 +39,8 @@ def to_np(t: Optional[torch.Tensor]):
 def params_of(w: Workload) -> O.Params:
     return O.Params(student_ce_weight=w.student_ce_weight, teacher_ce_weight=w.teacher_ce_weight,
                     kl_weight=w.kl_weight, temperature=w.temperature, ignore_index=w.ignore_index,
-                    kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature)
+                    kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature,
+                    compact_valid=w.compact_valid)
 
 
 def oracle_problem(w: Workload, x: dict, rows=None):
@@ -79,7 +80,7 @@ def make_runner(w: Workload, x: dict, vocab_chunk: int = 0, reduction: str = "me
               vocab_chunk=vocab_chunk,
               want_grads=(not w.forward_only) if want_grads is None else want_grads,
               want_teacher_ce=want_teacher_ce, kl_divergence=w.kl_divergence,
-              teacher_temperature=w.teacher_temperature)
+              teacher_temperature=w.teacher_temperature, compact_valid=w.compact_valid)
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:

@@ -132,6 +132,7 @@ def test_backward_workspace_is_O_n_chunk_not_n_vocab():
     ("topk_reverse", L.KD_ERR_UNSUPPORTED), ("topk_jeffreys", L.KD_ERR_UNSUPPORTED),
     ("tT_neg", L.KD_ERR_PARAM), ("tT_nan", L.KD_ERR_PARAM), ("topk_tT", L.KD_ERR_UNSUPPORTED),
     ("tlog_null", L.KD_ERR_NULL), ("tlog_misaligned", L.KD_ERR_ALIGN),
+    ("topk_compact", L.KD_ERR_UNSUPPORTED), ("compact_bad", L.KD_ERR_PARAM),
 ])
 def test_forward_rejects_invalid_arguments(case, expect):
     kind = "topk" if case.startswith("topk") else ("separate" if case.startswith("sep") else "tied")
@@ -197,6 +198,10 @@ def test_forward_rejects_invalid_arguments(case, expect):
         p.teacher_temperature = float("nan")
     elif case == "topk_tT":
         p.teacher_temperature = 2.0
+    elif case == "topk_compact":
+        p.compact_valid = 1
+    elif case == "compact_bad":
+        p.compact_valid = 2
     elif case == "tlog_null":
         t.kind = L.KD_TEACHER_LOGITS
         t.logits = None
@@ -248,3 +253,15 @@ def test_teacher_logits_descriptor():
     assert st == L.KD_OK and bwd > 0
     s2 = L.KdStudent(L.KD_STUDENT_LOGITS, L.KD_BF16, 300, 0, 3000, None, None, FAKE)
     assert _ws(s2, t, p, 0)[0] == L.KD_ERR_UNSUPPORTED
+
+
+def test_compaction_workspace():
+    """compact_valid reserves idx / pos and the compacted hidden copies in both
+    workspaces (bf16: 8 n + 2 * 128 ceil(n/128) * (d + d_t) bytes, rounded)."""
+    s, t, p = _desc()
+    base_f, base_b = _ws(s, t, p, 0)[1], _ws(s, t, p, 1)[1]
+    p.compact_valid = 1
+    f, b = _ws(s, t, p, 0)[1], _ws(s, t, p, 1)[1]
+    extra = 8 * 300 + 2 * 384 * (512 + 512)
+    assert extra <= f - base_f <= extra + 4 * 256
+    assert extra <= b - base_b <= extra + 4 * 256

@@ -46,3 +46,13 @@ def test_teacher_temperature_must_be_positive():
     h, w, y = _cpu_problem()
     with pytest.raises(ValueError, match="kl_teacher_temperature"):
         api.distillation_loss(h, w, y, api.TiedTeacher(h), kl_teacher_temperature=0.0)
+
+
+def test_compact_valid_needs_labels_and_a_projected_teacher():
+    h, w, y = _cpu_problem()
+    t = api.TopKTeacher(torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2))
+    with pytest.raises(NotImplementedError, match="compact_valid"):
+        api.distillation_loss(h, w, None, t, kl_weight=1.0, student_ce_weight=0.0, compact_valid=True)
+    with pytest.raises(NotImplementedError, match="compact_valid"):
+        api.distillation_loss(h, w, y, api.PrecomputedTeacher(logits=torch.zeros(4, 16)),
+                              compact_valid=True)

@@ -125,3 +125,26 @@ def test_precomputed_logits_teacher_with_its_own_temperature():
     assert_tokens(to_np(out.kl), ref["kl"], "bf16", "kl")
     dH, _ = O.backward(s, t, p, labels)
     assert_grad(f64(hs.grad), dH, "bf16", "student_hidden.grad")
+
+
+def test_distillation_loss_compacted_matches_uncompacted():
+    """compact_valid=True: same loss and gradients (to the rounding of a
+    different summation grouping), per-token terms of ignored rows 0."""
+    w = WORKLOADS["quickstart_tied_bf16"].scaled(n=384, d=256, v=2100, ignore_frac=0.3)
+    x = make_inputs(w, "cuda", seed=16)
+    outs = []
+    for compact in (False, True):
+        hs = x["student_hidden"].clone().requires_grad_(True)
+        W = x["weight"].clone().requires_grad_(True)
+        o = api.distillation_loss(hs, W, x["labels"], api.TiedTeacher(x["teacher_hidden"]),
+                                  kl_weight=1.0, kl_temperature=2.0, compact_valid=compact)
+        o.loss.backward()
+        outs.append((o, hs.grad.float(), W.grad.float()))
+    torch.cuda.synchronize()
+    (a, ha, wa), (b, hb, wb) = outs
+    assert_scalar(float(b.loss.detach()), float(a.loss.detach()), "bf16", "compacted loss")
+    ign = x["labels"] == w.ignore_index
+    assert torch.count_nonzero(b.kl[ign]).item() == 0
+    assert torch.allclose(b.kl[~ign], a.kl[~ign], rtol=1e-5, atol=1e-6)
+    assert_grad(to_np(hb), to_np(ha).astype(np.float64), "bf16", "compacted dH")
+    assert_grad(to_np(wb), to_np(wa).astype(np.float64), "bf16", "compacted dW")

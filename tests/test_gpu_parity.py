@@ -219,6 +219,50 @@ def test_infinite_teacher_ce_with_zero_weight():
     assert_scalar(float(r.loss), ref["loss"], "bf16", "loss")
 
 
+COMPACT_CASES = {
+    "tied_pipe": C2.scaled(n=300, d=512, v=3000, ignore_frac=0.3, compact_valid=True),
+    "tied_reverse_pipe": C2.scaled(n=520, d=256, v=2100, ignore_frac=0.4, kl_divergence="reverse",
+                                   compact_valid=True),
+    "separate_T2_tce": C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=2.0, ignore_frac=0.25,
+                                 compact_valid=True),
+    "ragged_staged": C2.scaled(n=130, d=136, v=1029, ignore_frac=0.5, compact_valid=True),
+    "fp32": C1.scaled(compact_valid=True),
+}
+
+
+@pytest.mark.parametrize("name", list(COMPACT_CASES))
+def test_compacted_valid_rows(name):
+    """Rows with an ignored label left out of every projection: loss, gradients
+    and the valid rows' terms as the oracle gives them, zeros on the others."""
+    w = COMPACT_CASES[name]
+    full_parity(w)
+    if w.dtype == "fp32":
+        full_parity(w, vocab_chunk=256)
+
+
+def test_compacted_all_ignored_and_accumulate():
+    """No usable label: nothing is projected, loss 0, dH and dW 0; with
+    accumulate the gradients keep their values (the left-out rows of dH too)."""
+    w = C2.scaled(n=200, d=256, v=1500, compact_valid=True)
+    x = make_inputs(w, "cuda", seed=7)
+    x["labels"] = torch.full_like(x["labels"], w.ignore_index)
+    r, dh, dw = run_gpu(w, x)
+    assert float(r.loss) == 0.0 and torch.count_nonzero(r.kl).item() == 0
+    assert torch.count_nonzero(dh).item() == 0 and torch.count_nonzero(dw).item() == 0
+    w = C2.scaled(n=300, d=256, v=1500, ignore_frac=0.3, compact_valid=True)
+    x = make_inputs(w, "cuda", seed=8)
+    r, dh, dw = run_gpu(w, x)
+    dh2 = torch.full_like(dh, 0.5)
+    dw2 = torch.full_like(dw, -0.25)
+    r.forward()
+    r.backward(dh2, dw2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(dh2, dh + 0.5, rtol=1e-6, atol=1e-6)
+    assert torch.allclose(dw2, dw - 0.25, rtol=1e-6, atol=1e-6)
+    ignored = (x["labels"] == w.ignore_index)
+    assert torch.count_nonzero(dh[ignored]).item() == 0
+
+
 def test_full_quickstart_logits_teacher_bf16():
     """Quickstart shape with a dense cached teacher (N=4096, D=2048, V=32000,
     T_s = 2, T_t = 1.5), every output."""
