@@ -30,7 +30,12 @@ Readings of points the pages leave open (each is also listed in the design doc):
   R3  the per-token KL is reported for every row; loss and gradients exclude
       rows whose label is ignored; per-token CE is 0 on ignored rows.
   R4  an all-ignored batch divides by max(n_valid, 1): loss 0, gradients 0.
-  R6  a frozen teacher's CE enters the loss value but gives no gradient.
+  R6  a frozen teacher's CE enters the loss value but gives no gradient. A
+      teacher trained through its CE (orda-kernel, Teacher descriptors: the
+      role follows the weights; teacher_ce_weight > 0 trains via CE) gets the
+      gradient of w_t * CE(t) only: every KL variant here detaches the teacher
+      (orda-kernel, KL variants), so the KL gives the teacher nothing. With a
+      tied teacher the shared weight receives both halves.
   R7  top-K indices are int32, probabilities fp32; M is the sum of the stored p.
   R8  0 * log 0 = 0 in the teacher-entropy term.
   R10 top-K mode has no labels: every row is valid, there is no CE.
@@ -488,3 +493,39 @@ def backward_rows(student: Student, teacher: Teacher, p: Params, labels, rows,
         r = rows[b:b + ROW_BLOCK]
         out[b:b + len(r)] = logit_grad(student, teacher, p, labels, r, den, grad_loss) @ W
     return out
+
+
+def teacher_logit_grad(student: Student, teacher: Teacher, p: Params, labels, rows: np.ndarray,
+                       den: float, grad_loss: float = 1.0) -> np.ndarray:
+    """d loss / d t for the given rows of a teacher trained through its CE.
+
+    (g / den) * valid * w_t (softmax(t) - e_y): the teacher CE is taken at
+    temperature 1 (reading R1) and the KL detaches the teacher (reading R6).
+    """
+    if teacher.kind not in ("tied", "separate"):
+        raise ValueError("only a projected teacher (tied or separate) can be trained")
+    lab = np.asarray(labels, dtype=np.int64)[rows]
+    valid = valid_mask(lab, student.v, p.ignore_index)
+    t = _teacher_logits(teacher, student, rows)
+    g = p.teacher_ce_weight * dce_dlogits(t, lab, valid)  # 0 on invalid rows
+    return g * (grad_loss / den)
+
+
+def backward_teacher(student: Student, teacher: Teacher, p: Params, labels,
+                     grad_loss: float = 1.0, den: Optional[float] = None):
+    """Gradients of the reduced loss with respect to the teacher's hidden
+    states and projection: dH_t = dT W_t and dW_t = dT^T H_t, dT from
+    teacher_logit_grad (a tied teacher projects with the student weight, so
+    its dW_t is the teacher half of that weight's gradient). float64."""
+    n = student.n
+    if den is None:
+        den = denominator(p, int(valid_mask(labels, student.v, p.ignore_index).sum()))
+    Wt = as_f64(student.weight if teacher.kind == "tied" else teacher.weight)
+    dHt = np.zeros((n, Wt.shape[1]), F64)
+    dWt = np.zeros_like(Wt)
+    for b in range(0, n, ROW_BLOCK):
+        r = np.arange(b, min(b + ROW_BLOCK, n))
+        g = teacher_logit_grad(student, teacher, p, labels, r, den, grad_loss)
+        dHt[r] = g @ Wt
+        dWt += g.T @ as_f64(teacher.hidden[r])
+    return dHt, dWt

@@ -368,6 +368,80 @@ def check_compact_valid_changes_only_ignored_kl(O):
         assert np.array_equal(ga, gb)
 
 
+def check_teacher_grad_autograd_library(O):
+    """A teacher trained through its CE: autograd through w_s CE(z) + w_t CE(t)
+    + w_kl KL(t.detach(), z) gives dH_t, dW_t (separate) and, tied, the
+    shared weight's gradient as the student half plus the teacher half."""
+    r = _rng(35)
+    n, d, dt, v = 5, 4, 3, 11
+    Hs, Ht = r.normal(size=(n, d)), r.normal(size=(n, d)) * 1.2
+    Htt, Wt, W = r.normal(size=(n, dt)), r.normal(size=(v, dt)), r.normal(size=(v, d)) * 0.7
+    y = np.array([3, -100, 10, 0, 7])
+    yt = torch.from_numpy(y)
+    valid = yt != -100
+    for kind in ("tied", "separate"):
+        for T, variant in ((1.0, "forward"), (1.7, "reverse")):
+            p = O.Params(student_ce_weight=0.6, teacher_ce_weight=1.3, kl_weight=0.9,
+                         temperature=T, kl_divergence=variant)
+            W_ = torch.tensor(W, requires_grad=True)
+            Hs_ = torch.tensor(Hs, requires_grad=True)
+            if kind == "tied":
+                Ht_ = torch.tensor(Ht, requires_grad=True)
+                Wt_ = W_
+            else:
+                Ht_ = torch.tensor(Htt, requires_grad=True)
+                Wt_ = torch.tensor(Wt, requires_grad=True)
+            z, t = Hs_ @ W_.T, Ht_ @ Wt_.T
+            ce_s = F.cross_entropy(z, yt, ignore_index=-100, reduction="none")
+            ce_t = F.cross_entropy(t, yt, ignore_index=-100, reduction="none")
+            lp_s, lp_t = F.log_softmax(z / T, -1), F.log_softmax(t.detach() / T, -1)
+            if variant == "forward":
+                kl = F.kl_div(lp_s, lp_t, log_target=True, reduction="none").sum(-1) * T * T
+            else:
+                kl = F.kl_div(lp_t, lp_s, log_target=True, reduction="none").sum(-1) * T * T
+            loss = (0.6 * ce_s + 1.3 * ce_t + 0.9 * kl)[valid].sum() / float(valid.sum())
+            loss.backward()
+            s = O.Student(hidden=Hs, weight=W)
+            te = O.Teacher("tied", hidden=Ht) if kind == "tied" else O.Teacher("separate", hidden=Htt, weight=Wt)
+            dHs, dWs = O.backward(s, te, p, y)
+            dHt, dWt = O.backward_teacher(s, te, p, y)
+            _close(dHs, Hs_.grad.numpy(), rtol=1e-10, atol=1e-13, what=f"{kind} student dH")
+            _close(dHt, Ht_.grad.numpy(), rtol=1e-10, atol=1e-13, what=f"{kind} teacher dH")
+            if kind == "tied":
+                _close(dWs + dWt, W_.grad.numpy(), rtol=1e-10, atol=1e-13, what="tied shared dW")
+            else:
+                _close(dWs, W_.grad.numpy(), rtol=1e-10, atol=1e-13, what="student dW")
+                _close(dWt, Wt_.grad.numpy(), rtol=1e-10, atol=1e-13, what="teacher dW")
+
+
+def check_teacher_grad_finite_differences(O):
+    """Central differences of the teacher-CE part of the loss in H_t and W_t
+    match backward_teacher (the KL part does not depend on a detached teacher)."""
+    r = _rng(36)
+    n, d, dt, v = 4, 3, 3, 7
+    Hs, W = r.normal(size=(n, d)), r.normal(size=(v, d))
+    Ht, Wt = r.normal(size=(n, dt)), r.normal(size=(v, dt))
+    y = np.array([1, 6, -100, 2])
+    p = O.Params(student_ce_weight=0.0, teacher_ce_weight=1.4, kl_weight=0.0, temperature=2.0)
+    s = O.Student(hidden=Hs, weight=W)
+
+    def loss(Ht_, Wt_):
+        return O.forward(s, O.Teacher("separate", hidden=Ht_, weight=Wt_), p, y)["loss"] * 0.8
+
+    dHt, dWt = O.backward_teacher(s, O.Teacher("separate", hidden=Ht, weight=Wt), p, y, grad_loss=0.8)
+    h = 1e-6
+    for X, G, which in ((Ht, dHt, "H_t"), (Wt, dWt, "W_t")):
+        num = np.zeros_like(X)
+        for ij in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[ij] += h
+            Xm[ij] -= h
+            num[ij] = ((loss(Xp, Wt) - loss(Xm, Wt)) if which == "H_t" else
+                       (loss(Ht, Xp) - loss(Ht, Xm))) / (2 * h)
+        err = np.max(np.abs(num - G)) / np.max(np.abs(G))
+        assert err < 1e-6, f"teacher finite differences d{which}: {err:.2e}"
+
+
 def check_logits_teacher_matches_projection(O):
     """A dense cached teacher holding H_t W_t^T gives the separate teacher's
     per-token values and gradients."""

@@ -49,6 +49,15 @@ MUTANTS = {
                                     "        contrib = contrib + w_term * term"),
     "compact_keeps_ignored_kl": ("np.where(vb, kl, 0.0) if p.compact_valid else kl",
                                  "kl if p.compact_valid else kl"),
+    "teacher_grad_missing_weight": ("g = p.teacher_ce_weight * dce_dlogits(t, lab, valid)",
+                                    "g = dce_dlogits(t, lab, valid)"),
+    "teacher_grad_loss_ignored": ("# 0 on invalid rows\n    return g * (grad_loss / den)",
+                                  "# 0 on invalid rows\n    return g * (1.0 / den)"),
+    "teacher_dW_uses_student_hidden": ("dWt += g.T @ as_f64(teacher.hidden[r])",
+                                       "dWt += g.T @ as_f64(student.hidden[r])"),
+    "teacher_dH_uses_teacher_weight_when_tied": (
+        "Wt = as_f64(student.weight if teacher.kind == \"tied\" else teacher.weight)",
+        "Wt = as_f64(teacher.weight if teacher.weight is not None else student.weight[::-1])"),
     "kl_reversed": ("(q * np.where(q > 0, lp_t - lp_s, 0.0))", "(np.exp(lp_s) * (lp_s - lp_t))"),
     "ce_label_off_by_one": ("picked = np.take_along_axis(logits, y[:, None], axis=1)",
                             "picked = np.take_along_axis(logits, (y[:, None] + 1) % logits.shape[1], axis=1)"),
@@ -71,7 +80,8 @@ MUTANTS = {
     "dW_uses_teacher_hidden": ("dW += g.T @ as_f64(student.hidden[r])",
                                "dW += g.T @ as_f64((teacher.hidden if teacher.hidden is not None and teacher.hidden.shape == student.hidden.shape else student.hidden)[r])"),
     "dH_transposed_weight_rows": ("dH[r] = g @ W", "dH[r] = g @ W[::-1]"),
-    "grad_loss_ignored": ("return g * (grad_loss / den)", "return g * (1.0 / den)"),
+    "grad_loss_ignored": ("    g[~valid] = 0.0\n    return g * (grad_loss / den)",
+                          "    g[~valid] = 0.0\n    return g * (1.0 / den)"),
     "out_of_range_label_valid": ("return (y != ignore_index) & (y >= 0) & (y < vocab)",
                                  "return (y != ignore_index)"),
 }
