@@ -187,7 +187,7 @@ kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_
                              int32_t for_backward, size_t* bytes /* host */);
 
 /* Bytes of the buffer that carries per-row statistics from forward to
- * backward: 16 per row plus a 64-byte header. One backward per forward
+ * backward: 20 per row plus a 64-byte header. One backward per forward
  * (orda-kernel, Quickstart: each fused forward supports one backward pass). */
 size_t kd_saved_bytes(int64_t n);
 
@@ -210,6 +210,20 @@ kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params*
                       const int64_t* labels, const void* saved, const float* grad_loss,
                       float* d_hidden, float* d_weight, int32_t accumulate,
                       void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
+
+/* Backward to a teacher trained through its CE (orda-kernel, Teacher
+ * descriptors: with teacher_ce_weight > 0 the teacher trains via CE; the KL
+ * variants here detach the teacher, so only w_t CE(t) at T = 1 reaches it).
+ * TIED or SEPARATE teacher, PROJECTION student, same arguments as kd_loss_bwd
+ * (the same workspace size serves). d_teacher_hidden: fp32 [n, d_t];
+ * d_teacher_weight: fp32 [v, d_t] (TIED: d_t = d and this is the teacher
+ * half of the shared weight's gradient: pass d_weight with accumulate = 1
+ * after kd_loss_bwd to sum the halves). Each nullable; accumulate as above.
+ * With teacher_ce_weight = 0 the gradients are 0. */
+kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                              const int64_t* labels, const void* saved, const float* grad_loss,
+                              float* d_teacher_hidden, float* d_teacher_weight, int32_t accumulate,
+                              void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
 
 /* Synchronises `stream`, then reads the device flags left in `workspace` by
  * the last kd_loss_fwd that used it: *flags (host, nullable) receives them;

@@ -60,6 +60,9 @@ EXPORTS = {
     "kd_loss_bwd": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                               c_void_p, c_size_t, c_void_p, POINTER(KdTrace)]),
+    "kd_loss_bwd_teacher": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                      c_void_p, c_size_t, c_void_p, POINTER(KdTrace)]),
     "kd_read_status": (c_int32, [c_void_p, c_void_p, POINTER(c_int32)]),
     "kd_status_string": (c_char_p, [c_int32]),
     "kd_device_supported": (c_int32, [c_int32]),

@@ -190,6 +190,8 @@ class Runner:
         p.compact_valid = 1 if compact_valid else 0
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
+        self.teacher_kind = teacher_kind
+        self.dt = int(t.d_t) if teacher_kind == "separate" else self.d
         f32 = dict(dtype=torch.float32, device=self.device)
         self.loss = torch.zeros((), **f32)
         self.student_ce = torch.empty(self.n, **f32)
@@ -240,6 +242,23 @@ class Runner:
                                   self.ws_bwd.data_ptr(), self.ws_bwd.numel(), self._stream(),
                                   ctypes.byref(trace) if trace is not None else None)
         L.check(st, "kd_loss_bwd")
+
+    def backward_teacher(self, d_teacher_hidden: Optional[torch.Tensor],
+                         d_teacher_weight: Optional[torch.Tensor],
+                         grad_loss: Optional[torch.Tensor] = None, accumulate: bool = False,
+                         trace: Optional[L.KdTrace] = None) -> None:
+        """Gradient of w_t CE(t) to a tied or separate teacher (the KL detaches it).
+        Tied: d_teacher_weight is the teacher half of the shared weight's gradient."""
+        for g, shape in ((d_teacher_hidden, (self.n, self.dt)), (d_teacher_weight, (self.v, self.dt))):
+            if g is not None and (g.dtype != torch.float32 or tuple(g.shape) != shape
+                                  or not g.is_contiguous()):
+                raise ValueError(f"gradient buffers must be contiguous fp32 {shape}")
+        st = self.lib.kd_loss_bwd_teacher(
+            ctypes.byref(self.s), ctypes.byref(self.t), ctypes.byref(self.p), self.labels_ptr,
+            self.saved.data_ptr(), _ptr(grad_loss), _ptr(d_teacher_hidden), _ptr(d_teacher_weight),
+            int(accumulate), self.ws_bwd.data_ptr(), self.ws_bwd.numel(), self._stream(),
+            ctypes.byref(trace) if trace is not None else None)
+        L.check(st, "kd_loss_bwd_teacher")
 
     def read_status(self) -> int:
         flags = ctypes.c_int32(0)
@@ -292,9 +311,12 @@ class Tracer:
 
 class _FusedLoss(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, student_hidden, weight, runner: Runner):
+    def forward(ctx, student_hidden, weight, teacher_hidden, teacher_weight, runner: Runner):
+        # teacher_hidden / teacher_weight are given only for a teacher trained
+        # through its CE; otherwise None (the teacher is detached).
         runner.forward()
         ctx.runner = runner
+        ctx.train_teacher = getattr(runner, "train_teacher", False)
         ctx.used = False
         return (runner.loss.clone(), runner.student_ce.clone(), runner.teacher_ce.clone(),
                 runner.kl.clone())
@@ -308,12 +330,25 @@ class _FusedLoss(torch.autograd.Function):
         ctx.used = True
         r: Runner = ctx.runner
         need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
-        dh = torch.empty((r.n, r.d), dtype=torch.float32, device=r.device) if need_h else None
-        dw = torch.empty((r.v, r.d), dtype=torch.float32, device=r.device) if need_w else None
+        need_ht, need_wt = ctx.needs_input_grad[2], ctx.needs_input_grad[3]
+        f32 = dict(dtype=torch.float32, device=r.device)
+        dh = torch.empty((r.n, r.d), **f32) if need_h else None
+        dw = torch.empty((r.v, r.d), **f32) if need_w else None
         g = (g_loss if g_loss is not None else torch.ones((), device=r.device))
         g = g.detach().to(torch.float32).contiguous()
-        r.backward(dh, dw, grad_loss=g)
-        return dh, dw, None
+        if dh is not None or dw is not None:
+            r.backward(dh, dw, grad_loss=g)
+        dht = dwt = None
+        if need_ht or need_wt or (r.teacher_kind == "tied" and need_w and ctx.train_teacher):
+            # accumulate: the tied weight's teacher half adds to dw; dht starts at 0
+            dht = torch.zeros((r.n, r.dt), **f32) if need_ht else None
+            if r.teacher_kind == "tied":
+                dwt_buf = dw
+            else:
+                dwt_buf = torch.zeros((r.v, r.dt), **f32) if need_wt else None
+            r.backward_teacher(dht, dwt_buf, grad_loss=g, accumulate=True)
+            dwt = dwt_buf if r.teacher_kind != "tied" else None
+        return dh, dw, dht, dwt, None
 
 
 def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_weight=1.0,
@@ -337,6 +372,28 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
         raise NotImplementedError("the top-K teacher supports kl_divergence='forward' only")
     if kl_teacher_temperature is not None and not kl_teacher_temperature > 0:
         raise ValueError("kl_teacher_temperature must be positive")
+    # A tied or separate teacher whose tensors require grad trains through its
+    # CE when teacher_ce_weight > 0 (orda-kernel, Teacher descriptors); the KL
+    # always detaches it. Cached (precomputed) teachers never receive gradients.
+    if isinstance(teacher, PrecomputedTeacher) and any(
+            x is not None and x.requires_grad
+            for x in (teacher.logits, teacher.teacher_hidden, teacher.teacher_weight)):
+        raise ValueError("PrecomputedTeacher tensors must not require grad")
+    t_hidden = t_weight = None
+    if teacher_ce_weight > 0 and isinstance(teacher, (TiedTeacher, SeparateTeacher)):
+        if teacher.hidden.requires_grad:
+            t_hidden = teacher.hidden
+        if isinstance(teacher, SeparateTeacher) and teacher.weight.requires_grad:
+            t_weight = teacher.weight
+    train_teacher = t_hidden is not None or t_weight is not None or (
+        teacher_ce_weight > 0 and isinstance(teacher, TiedTeacher))
+    if isinstance(teacher, TiedTeacher) and teacher.mode is not None:
+        # the mode asserts the role the weights give; it does not route
+        role = "trained" if teacher_ce_weight > 0 else "frozen"
+        if teacher.mode == "cotrained":
+            raise NotImplementedError("co-trained teachers (mutual / cojeffreys) are not provided")
+        if teacher.mode != role:
+            raise ValueError(f"TiedTeacher(mode={teacher.mode!r}) but the weights make it {role}")
     kw = dict(kl_divergence=kl_divergence, teacher_temperature=kl_teacher_temperature,
               student_hidden=student_hidden.detach().contiguous(),
               weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
@@ -365,7 +422,8 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
     if labels is not None:
         kw["labels"] = labels.to(torch.int64).contiguous()
     runner = Runner(**kw)
-    loss, sce, tce, kl = _FusedLoss.apply(student_hidden, weight, runner)
+    runner.train_teacher = train_teacher
+    loss, sce, tce, kl = _FusedLoss.apply(student_hidden, weight, t_hidden, t_weight, runner)
     return DistillationLossOutput(loss, sce, tce, kl)
 
 

@@ -218,7 +218,7 @@ kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_
 
 size_t kd_saved_bytes(int64_t n) {
   if (n < 0) return 0;
-  return 16 * (size_t)n + kd::kSavedHeaderBytes;
+  return 20 * (size_t)n + kd::kSavedHeaderBytes;
 }
 
 kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
@@ -255,6 +255,29 @@ kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params*
   if (!d_hidden && !d_weight) return KD_OK;
   return kd::run_backward(q, tensors_of(s, t, labels), saved, grad_loss, d_hidden, d_weight,
                           accumulate ? 1 : 0, workspace, static_cast<hipStream_t>(stream), trace);
+}
+
+kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                              const int64_t* labels, const void* saved, const float* grad_loss,
+                              float* d_teacher_hidden, float* d_teacher_weight, int32_t accumulate,
+                              void* workspace, size_t ws_bytes, void* stream, kd_trace* trace) {
+  Plan q;
+  const kd_status st = plan_call(s, t, p, labels, true, true, &q);
+  if (st != KD_OK) return st;
+  if (q.mode != kd::MODE_TIED && q.mode != kd::MODE_SEPARATE) return KD_ERR_UNSUPPORTED;
+  if (!labels && p->teacher_ce_weight != 0.f) return KD_ERR_NULL;
+  if (!saved) return KD_ERR_WORKSPACE;
+  if (!workspace) return KD_ERR_NULL;
+  if (ws_bytes < q.bwd_bytes) return KD_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(saved)) return KD_ERR_ALIGN;
+  if ((d_teacher_hidden && !aligned16(d_teacher_hidden)) ||
+      (d_teacher_weight && !aligned16(d_teacher_weight)))
+    return KD_ERR_ALIGN;
+  if (grad_loss && ((uintptr_t)grad_loss & 3u)) return KD_ERR_ALIGN;
+  if (!d_teacher_hidden && !d_teacher_weight) return KD_OK;
+  return kd::run_backward_teacher(q, tensors_of(s, t, labels), saved, grad_loss, d_teacher_hidden,
+                                  d_teacher_weight, accumulate ? 1 : 0, workspace,
+                                  static_cast<hipStream_t>(stream), trace);
 }
 
 kd_status kd_read_status(const void* workspace, void* stream, int32_t* flags) {

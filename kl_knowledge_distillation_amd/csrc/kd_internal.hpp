@@ -13,7 +13,8 @@ namespace kd {
 // TIED / SEPARATE / TOPK: projection student with that teacher; LOGITS: given
 // student logits with a separate teacher (forward only); TLOGITS: projection
 // student with given dense teacher logits.
-enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3, MODE_TLOGITS = 4 };
+enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3, MODE_TLOGITS = 4,
+            MODE_TCE = 5 /* backward only: the teacher tile and its CE gradient */ };
 
 // Number of fp32 fields of one per-(token, vocabulary tile) record.
 constexpr int kRecFields = 10;
@@ -24,7 +25,8 @@ constexpr int kMergeTok = 16;  // tokens per merge workgroup
 // and the compacted row count (int32 at kNvOffset).
 constexpr size_t kStatusBytes = 256;
 constexpr size_t kNvOffset = 8;
-// Offset of the header inside `saved` is 16 * n; its size is 64 bytes.
+// `saved`: [n] x 16 bytes of row statistics, a 64-byte header at 16 n, then
+// [n] fp32 lse(t) at T = 1 (the teacher-CE backward) at 16 n + 64.
 constexpr size_t kSavedHeaderBytes = 64;
 
 struct Plan {
@@ -80,5 +82,9 @@ kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, vo
 kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
                        float* d_hidden, float* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace);
+// The teacher-CE backward: d_hidden / d_weight are the teacher's.
+kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,
+                               const float* grad_loss, float* d_hidden, float* d_weight,
+                               int accumulate, void* workspace, hipStream_t stream, kd_trace* trace);
 
 }  // namespace kd

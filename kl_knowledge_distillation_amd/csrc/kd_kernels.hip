@@ -656,13 +656,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       if (a.out_sce) a.out_sce[i] = 0.f;
       if (a.out_tce) a.out_tce[i] = 0.f;
       if (a.out_kl) a.out_kl[i] = 0.f;
-      if (a.saved) reinterpret_cast<float4*>(a.saved)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.saved) {
+        reinterpret_cast<float4*>(a.saved)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        a.saved[4 * a.n + kSavedHeaderBytes / 4 + i] = 0.f;
+      }
     } else if (live) {
       const float lz1 = kLn2 * (s.mz1 + log2f(s.sz1));
       const float lzT = a.need_zT ? kLn2 * (s.mzT + log2f(s.szT)) : lz1;
       const float f0 = a.prep[i], f1 = a.prep[a.n + i], f2 = a.prep[2 * a.n + i];
       const float flag = a.prep[3 * a.n + i];
-      float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f;
+      float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f, lt1 = 0.f;
       bool valid;
       if (a.mode == MODE_TOPK) {
         // sum p log p - sum p z[idx] + M lse(z)
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
         valid = true;
       } else {
         ltT = kLn2 * (s.mtT + log2f(s.stT));
-        const float lt1 = a.need_t1 ? kLn2 * (s.mt1 + log2f(s.st1)) : ltT;
+        lt1 = a.need_t1 ? kLn2 * (s.mt1 + log2f(s.st1)) : ltT;
         // KL(P_T || P_S) = E_{P_T}[(t - z) / T] - lse(t/T) + lse(z/T), and
         // KL(P_S || P_T) = E_{P_S}[(z - t) / T] - lse(z/T) + lse(t/T)
         // (orda-kernel, KL variants: forward, reverse, jeffreys = their sum).
@@ -698,6 +701,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       if (a.saved) {
         float4 sv = make_float4(lz1, lzT, ltT, mass);
         reinterpret_cast<float4*>(a.saved)[i] = sv;
+        a.saved[4 * a.n + kSavedHeaderBytes / 4 + i] = lt1;  // lse(t) at T = 1
       }
     }
     red[0][tl] = contrib;
@@ -785,6 +789,7 @@ struct BwdArgs {
   const float* grad;      // device scalar or null
   float ws, wkl, T, cT;
   float cTt, rho;         // log2(e) / T_t, T_s / T_t
+  float wtce;             // teacher-CE weight (MODE_TCE)
   int need_zT;
   int kl;                 // KD_KL_*
   int vec;                // teacher logits: 2 staged through LDS, 1 vector loads, 0 element loads
@@ -852,11 +857,14 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, tacc[0]);
+  } else if constexpr (MODE == MODE_TCE) {  // the teacher tile alone
+    const T* const bt[1] = {ht};
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, acc, tid);
   } else {  // MODE_TOPK
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   }
-  const WaveAcc& z = acc[0];
+  const WaveAcc& z = acc[0];  // MODE_TCE: the teacher logits
   const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
 
   const float* hdr = a.saved + 4 * a.n;
@@ -875,7 +883,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const bool live = tok < n_live;  // rows past n (or nv) are zero padding of the slab
     const int64_t orig = (live && a.idx) ? a.idx[tok] : tok;  // original row
     const float4 sv = live ? reinterpret_cast<const float4*>(a.saved)[orig] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float L1 = sv.x * kLog2e, LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
+    // MODE_TCE: the softmax at T = 1 is the teacher's
+    const float L1 = (MODE == MODE_TCE ? (live ? a.saved[4 * a.n + kSavedHeaderBytes / 4 + orig] : 0.f)
+                                       : sv.x) * kLog2e;
+    const float LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
     int64_t y = -1;
     bool valid = live;
     if (live && MODE != MODE_TOPK && a.labels) {
@@ -883,7 +894,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
       valid = y != a.ignore && y >= 0 && y < a.v;
     }
     const float coef = valid ? g / den : 0.f;
-    const float cs = coef * a.ws;            // student CE
+    const float cs = coef * (MODE == MODE_TCE ? a.wtce : a.ws);  // student (teacher) CE
     const float ck = coef * a.wkl * a.T;     // T^2 KL -> T (P_S - P_T)
     const float cm = coef * a.wkl * mass;    // top-K: M softmax(z)
     // T^2 KL(P_S || P_T) -> T P_S (log P_S - log P_T - KL(P_S || P_T)); with
@@ -905,6 +916,8 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
         float dv;
         if (MODE == MODE_TOPK) {
           dv = cm * p1;
+        } else if (MODE == MODE_TCE) {
+          dv = cs * (p1 - (vv == y ? 1.f : 0.f));
         } else {
           dv = cs * (p1 - (vv == y ? 1.f : 0.f));
           const float tt = tl[mb][nb][r];
@@ -919,7 +932,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     }
   }
   };
-  if (MODE != MODE_TOPK && a.kl != KD_KL_FORWARD) epilogue(std::true_type{});
+  if (MODE != MODE_TOPK && MODE != MODE_TCE && a.kl != KD_KL_FORWARD) epilogue(std::true_type{});
   else epilogue(std::false_type{});
 }
 
@@ -1028,6 +1041,13 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(GatherArgs a) {
   } else {
     for (int64_t j = lane; j < pieces; j += 64) dst[j] = make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+// m[0 .. cnt) = 0 (a fill kernel rather than a memset, so that a captured
+// graph replays it like any other launch).
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* m, int64_t cnt) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < cnt) m[i] = 0.f;
 }
 
 // Rows i with pos[i] < 0 (left out by the compaction) of an fp32 [n x d] matrix
@@ -1278,13 +1298,29 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
 }
 
 template <typename T, class G>
+// teacher = false: the student's dH / dW from the loss's logit gradient;
+// teacher = true: the teacher's from its CE gradient (dh / dw are then the
+// teacher's hidden and weight gradients, of width d_t).
 kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const float* grad,
                      float* dh, float* dw, int accumulate, void* ws, hipStream_t stream,
-                     kd_trace* trace) {
+                     kd_trace* trace, bool teacher) {
   Launch L{stream, trace};
   uint8_t* base = static_cast<uint8_t*>(ws);
   T* dz = reinterpret_cast<T*>(base + p.off_dz);
   const int64_t ldz = p.chunk;
+  const int64_t gd = teacher ? p.dt : p.d;  // width of the gradients
+  if (teacher && p.wt == 0.f) {  // no teacher CE: nothing reaches the teacher
+    if (!accumulate) {
+      for (float* m : {dh, dw}) {
+        if (!m) continue;
+        const int64_t cnt = (m == dh ? p.n : p.v) * gd;
+        KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
+          fill_zero_kernel<<<dim3((unsigned)((cnt + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(m, cnt);
+        }));
+      }
+    }
+    return KD_OK;
+  }
   Compacted cp{nullptr, nullptr, nullptr, x.hs, x.ht};
   if (p.compact) {
     KD_TRY(compact_rows<T>(p, x, base, L, stream, &cp));
@@ -1292,29 +1328,33 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     if (dh && !accumulate) {
       KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
         zero_rows_kernel<<<dim3((unsigned)((p.n + kThreads / 64 - 1) / (kThreads / 64))), kThreads, 0,
-                           stream>>>(dh, cp.pos, p.n, p.d);
+                           stream>>>(dh, cp.pos, p.n, gd);
       }));
     }
   }
-  const T* hs = static_cast<const T*>(cp.hs);
+  // the token-side operand and the weight of the GEMMs
+  const T* hs = static_cast<const T*>(teacher ? cp.ht : cp.hs);
+  const T* wmat = static_cast<const T*>(teacher ? x.wt : x.w);
+  const int mode = teacher ? (int)MODE_TCE : p.mode;
   for (int c = 0; c < p.n_chunks; ++c) {
     const int64_t c0 = (int64_t)c * p.chunk;
     const int64_t cw = (p.v - c0 < p.chunk) ? (p.v - c0) : p.chunk;  // valid columns
     const int n_vt = (int)((cw + G::kVT - 1) / G::kVT);  // fused tiles of the chunk
     BwdArgs ba{cp.hs, x.w, cp.ht, x.wt, x.tlogits, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
                static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T,
-               kLog2e / p.Tt, p.T / p.Tt, p.need_zT, p.kl, given_mode<T, G>(x.tlogits, p.v),
+               kLog2e / p.Tt, p.T / p.Tt, p.wt, p.need_zT, p.kl, given_mode<T, G>(x.tlogits, p.v),
                cp.idx, cp.nv, c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
-      switch (p.mode) {
+      switch (mode) {
+        case MODE_TCE: bwd_dz_kernel<T, MODE_TCE, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_TLOGITS: bwd_dz_kernel<T, MODE_TLOGITS, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
         default: bwd_dz_kernel<T, MODE_TOPK, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
       }
     }));
-    if (p.mode == MODE_TOPK) {
+    if (mode == MODE_TOPK) {
       ScatterArgs sa{x.topk_idx, x.topk_prob, p.k, p.n, p.v, c0, cw,
                      static_cast<const float*>(saved), grad, p.wkl, dz, ldz};
       const int64_t ne = p.n * p.k;
@@ -1326,7 +1366,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     const int n_gemm_mt = (int)((cw + kTile - 1) / kTile);
     if constexpr (G::kPipe) {
       // 256-wide tiles when they still give every CU a tile, else 128-wide.
-      auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((p.d + 255) / 256) >= 256; };
+      auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((gd + 255) / 256) >= 256; };
       if (dw) {
         // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]: A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n],
         // both row-contiguous; the slab's zero rows past n pad K to a multiple of 64.
@@ -1334,15 +1374,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
           constexpr int BN = decltype(bn_tag)::value;
           GemmPipeArgs<false, false, BN> ga;
           ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
-          ga.B = PipeOperandMN{hs, p.d, p.d, p.n};
-          ga.C = dw + c0 * p.d;
-          ga.ldc = p.d;
+          ga.B = PipeOperandMN{hs, gd, gd, p.n};
+          ga.C = dw + c0 * gd;
+          ga.ldc = gd;
           ga.M = cw;
-          ga.N = p.d;
+          ga.N = gd;
           ga.K = p.dz_rows;
           ga.accumulate = accumulate;
           ga.n_mt = (int)((cw + 255) / 256);
-          ga.n_nt = (int)((p.d + BN - 1) / BN);
+          ga.n_nt = (int)((gd + BN - 1) / BN);
           ga.kdev = cp.nv;  // compacted: the token rows stop at nv
           ga.mdev = nullptr;
           ga.rowmap = nullptr;
@@ -1361,15 +1401,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
           constexpr int BN = decltype(bn_tag)::value;
           GemmPipeArgs<true, false, BN> gb;
           gb.A = PipeOperand{dz, ldz, p.n};
-          gb.B = PipeOperandMN{static_cast<const T*>(x.w) + c0 * p.d, p.d, p.d, cw};
+          gb.B = PipeOperandMN{wmat + c0 * gd, gd, gd, cw};
           gb.C = dh;
-          gb.ldc = p.d;
+          gb.ldc = gd;
           gb.M = p.n;
-          gb.N = p.d;
+          gb.N = gd;
           gb.K = cpad;
           gb.accumulate = (accumulate || c > 0) ? 1 : 0;
           gb.n_mt = (int)((p.n + 255) / 256);
-          gb.n_nt = (int)((p.d + BN - 1) / BN);
+          gb.n_nt = (int)((gd + BN - 1) / BN);
           gb.kdev = nullptr;
           gb.mdev = cp.nv;      // compacted: rows past nv are not tokens
           gb.rowmap = cp.idx;   // compacted row m is token idx[m]
@@ -1386,15 +1426,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]; A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n]
       GemmArgs<T, false, false> ga;
       ga.A = Operand<T, false>{dz, ldz, cpad, p.n};
-      ga.B = Operand<T, false>{hs, p.d, p.d, p.n};
-      ga.C = dw + c0 * p.d;
-      ga.ldc = p.d;
+      ga.B = Operand<T, false>{hs, gd, gd, p.n};
+      ga.C = dw + c0 * gd;
+      ga.ldc = gd;
       ga.M = cw;
-      ga.N = p.d;
+      ga.N = gd;
       ga.K = p.n;
       ga.accumulate = accumulate;
       ga.n_mt = n_gemm_mt;
-      ga.n_nt = (int)((p.d + kTile - 1) / kTile);
+      ga.n_nt = (int)((gd + kTile - 1) / kTile);
       ga.kdev = cp.nv;
       ga.mdev = nullptr;
       ga.rowmap = nullptr;
@@ -1407,15 +1447,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]; A(i, m) = dz[i * ldz + m], B(n, m) = W[(c0 + m) * d + n]
       GemmArgs<T, true, false> gb;
       gb.A = Operand<T, true>{dz, ldz, p.n, cpad};
-      gb.B = Operand<T, false>{static_cast<const T*>(x.w) + c0 * p.d, p.d, p.d, cw};
+      gb.B = Operand<T, false>{wmat + c0 * gd, gd, gd, cw};
       gb.C = dh;
-      gb.ldc = p.d;
+      gb.ldc = gd;
       gb.M = p.n;
-      gb.N = p.d;
+      gb.N = gd;
       gb.K = cw;
       gb.accumulate = (accumulate || c > 0) ? 1 : 0;
       gb.n_mt = p.n_ttiles;
-      gb.n_nt = (int)((p.d + kTile - 1) / kTile);
+      gb.n_nt = (int)((gd + kTile - 1) / kTile);
       gb.kdev = nullptr;
       gb.mdev = cp.nv;
       gb.rowmap = cp.idx;
@@ -1443,18 +1483,34 @@ kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, vo
   return forward_t<float, GeoStaged>(p, x, out, saved, workspace, stream, trace);
 }
 
-kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
+namespace {
+kd_status backward_any(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
                        float* d_hidden, float* d_weight, int accumulate, void* workspace,
-                       hipStream_t stream, kd_trace* trace) {
+                       hipStream_t stream, kd_trace* trace, bool teacher) {
   if (p.dtype == KD_BF16) {
     if (p.pipe)
       return backward_t<bf16_t, GeoFused>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate,
-                                         workspace, stream, trace);
+                                         workspace, stream, trace, teacher);
     return backward_t<bf16_t, GeoStaged>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate,
-                                         workspace, stream, trace);
+                                         workspace, stream, trace, teacher);
   }
   return backward_t<float, GeoStaged>(p, x, saved, grad_loss, d_hidden, d_weight, accumulate,
-                                      workspace, stream, trace);
+                                      workspace, stream, trace, teacher);
+}
+}  // namespace
+
+kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
+                       float* d_hidden, float* d_weight, int accumulate, void* workspace,
+                       hipStream_t stream, kd_trace* trace) {
+  return backward_any(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace, stream,
+                      trace, false);
+}
+
+kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,
+                               const float* grad_loss, float* d_hidden, float* d_weight,
+                               int accumulate, void* workspace, hipStream_t stream, kd_trace* trace) {
+  return backward_any(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace, stream,
+                      trace, true);
 }
 
 }  // namespace kd

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    for must in ("kd_loss_fwd", "kd_loss_bwd", "kd_workspace_bytes", "kd_saved_bytes",
+    for must in ("kd_loss_fwd", "kd_loss_bwd", "kd_loss_bwd_teacher", "kd_workspace_bytes", "kd_saved_bytes",
                  "kd_read_status", "kd_status_string", "kd_device_supported"):
         assert must in names
 
@@ -80,7 +80,7 @@ def _bwd(s, t, p, labels=FAKE, ws_bytes=1 << 40, saved=FAKE):
 def test_saved_bytes():
     lib = L.load()
     assert lib.kd_saved_bytes(0) == 64
-    assert lib.kd_saved_bytes(4096) == 16 * 4096 + 64
+    assert lib.kd_saved_bytes(4096) == 20 * 4096 + 64
 
 
 def test_status_strings():
@@ -265,3 +265,19 @@ def test_compaction_workspace():
     extra = 8 * 300 + 2 * 384 * (512 + 512)
     assert extra <= f - base_f <= extra + 4 * 256
     assert extra <= b - base_b <= extra + 4 * 256
+
+
+def test_teacher_backward_rejections():
+    s, t, p = _desc(kind="topk")
+    lib = L.load()
+    st = lib.kd_loss_bwd_teacher(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), None, FAKE, None,
+                                 FAKE, FAKE, 0, FAKE, 1 << 30, None, None)
+    assert st == L.KD_ERR_UNSUPPORTED
+    s, t, p = _desc()
+    p.teacher_ce_weight = 1.0
+    st = lib.kd_loss_bwd_teacher(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), None, FAKE, None,
+                                 FAKE, FAKE, 0, FAKE, 1 << 30, None, None)
+    assert st == L.KD_ERR_NULL  # the teacher CE needs labels
+    st = lib.kd_loss_bwd_teacher(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), FAKE, FAKE, None,
+                                 FAKE + 4, None, 0, FAKE, 1 << 30, None, None)
+    assert st == L.KD_ERR_ALIGN

@@ -56,3 +56,20 @@ def test_compact_valid_needs_labels_and_a_projected_teacher():
     with pytest.raises(NotImplementedError, match="compact_valid"):
         api.distillation_loss(h, w, y, api.PrecomputedTeacher(logits=torch.zeros(4, 16)),
                               compact_valid=True)
+
+
+def test_tied_teacher_mode_asserts_the_role():
+    h, w, y = _cpu_problem()
+    with pytest.raises(ValueError, match="frozen"):
+        api.distillation_loss(h, w, y, api.TiedTeacher(h, mode="trained"), teacher_ce_weight=0.0)
+    with pytest.raises(ValueError, match="trained"):
+        api.distillation_loss(h, w, y, api.TiedTeacher(h, mode="frozen"), teacher_ce_weight=1.0)
+    with pytest.raises(NotImplementedError):
+        api.distillation_loss(h, w, y, api.TiedTeacher(h, mode="cotrained"))
+
+
+def test_precomputed_teacher_must_not_require_grad():
+    h, w, y = _cpu_problem()
+    t = api.PrecomputedTeacher(logits=torch.zeros(4, 16, requires_grad=True))
+    with pytest.raises(ValueError, match="require grad"):
+        api.distillation_loss(h, w, y, t)

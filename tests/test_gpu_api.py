@@ -148,3 +148,43 @@ def test_distillation_loss_compacted_matches_uncompacted():
     assert torch.allclose(b.kl[~ign], a.kl[~ign], rtol=1e-5, atol=1e-6)
     assert_grad(to_np(hb), to_np(ha).astype(np.float64), "bf16", "compacted dH")
     assert_grad(to_np(wb), to_np(wa).astype(np.float64), "bf16", "compacted dW")
+
+
+@pytest.mark.parametrize("kind", ["tied", "separate"])
+def test_teacher_trained_through_autograd(kind):
+    """teacher_ce_weight > 0 with teacher tensors that require grad: the teacher
+    gets the gradient of its CE (the KL detaches it); a tied weight gets both
+    halves."""
+    base = WORKLOADS["quickstart_tied_bf16"] if kind == "tied" else WORKLOADS["separate_bf16"]
+    w = base.scaled(n=260, d=256, d_t=512, v=2100, ignore_frac=0.1)
+    x = make_inputs(w, "cuda", seed=17)
+    hs = x["student_hidden"].clone().requires_grad_(True)
+    W = x["weight"].clone().requires_grad_(True)
+    ht = x["teacher_hidden"].clone().requires_grad_(True)
+    if kind == "tied":
+        teacher = api.TiedTeacher(ht, mode="trained")
+    else:
+        wt = x["teacher_weight"].clone().requires_grad_(True)
+        teacher = api.SeparateTeacher(ht, wt)
+    out = api.distillation_loss(hs, W, x["labels"], teacher, student_ce_weight=0.8,
+                                teacher_ce_weight=0.6, kl_weight=1.0, kl_temperature=2.0,
+                                ignore_index=w.ignore_index)
+    (out.loss * 1.5).backward()
+    torch.cuda.synchronize()
+    s = O.Student(hidden=f64(x["student_hidden"]), weight=f64(x["weight"]))
+    if kind == "tied":
+        t = O.Teacher("tied", hidden=f64(x["teacher_hidden"]))
+    else:
+        t = O.Teacher("separate", hidden=f64(x["teacher_hidden"]), weight=f64(x["teacher_weight"]))
+    labels = to_np(x["labels"]).astype(np.int64)
+    p = O.Params(student_ce_weight=0.8, teacher_ce_weight=0.6, kl_weight=1.0, temperature=2.0,
+                 ignore_index=w.ignore_index)
+    dHs, dWs = O.backward(s, t, p, labels, grad_loss=1.5)
+    dHt, dWt = O.backward_teacher(s, t, p, labels, grad_loss=1.5)
+    assert_grad(f64(hs.grad), dHs, "bf16", "student dH")
+    assert_grad(f64(ht.grad), dHt, "bf16", "teacher dH")
+    if kind == "tied":
+        assert_grad(f64(W.grad), dWs + dWt, "bf16", "shared weight: both halves")
+    else:
+        assert_grad(f64(W.grad), dWs, "bf16", "student dW")
+        assert_grad(f64(wt.grad), dWt, "bf16", "teacher dW")

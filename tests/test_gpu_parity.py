@@ -263,6 +263,53 @@ def test_compacted_all_ignored_and_accumulate():
     assert torch.count_nonzero(dh[ignored]).item() == 0
 
 
+TEACHER_TRAIN_CASES = {
+    "tied_pipe": C2.scaled(n=300, d=512, v=3000, teacher_ce_weight=0.7),
+    "tied_compact": C2.scaled(n=300, d=256, v=2100, teacher_ce_weight=1.0, ignore_frac=0.3,
+                              compact_valid=True),
+    "separate_Ts1.5_Tt2.5": C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=1.5,
+                                      teacher_temperature=2.5, teacher_ce_weight=0.5),
+    "ragged_staged": C2.scaled(n=130, d=136, v=1029, teacher_ce_weight=1.0, ignore_frac=0.2),
+    "fp32": C1.scaled(teacher_ce_weight=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(TEACHER_TRAIN_CASES))
+def test_teacher_trained_through_its_ce(name):
+    """kd_loss_bwd_teacher: dH_t and dW_t of w_t CE(t) against the oracle; with
+    accumulate the second call adds the same gradients again."""
+    w = TEACHER_TRAIN_CASES[name]
+    say(f"[teacher ce] {name}")
+    x = make_inputs(w, "cuda", seed=3)
+    r = make_runner(w, x)
+    r.forward()
+    dht = torch.empty((r.n, r.dt), dtype=torch.float32, device="cuda")
+    dwt = torch.empty((r.v, r.dt), dtype=torch.float32, device="cuda")
+    r.backward_teacher(dht, dwt)
+    torch.cuda.synchronize()
+    s, t, labels = oracle_problem(w, x)
+    dHt, dWt = O.backward_teacher(s, t, params_of(w), labels)
+    assert_grad(to_np(dht), dHt, w.dtype, f"{name} teacher dH")
+    assert_grad(to_np(dwt), dWt, w.dtype, f"{name} teacher dW")
+    dht2, dwt2 = dht.clone(), dwt.clone()
+    r.backward_teacher(dht2, dwt2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(dht2, 2 * dht, rtol=1e-6, atol=1e-7)
+    assert torch.allclose(dwt2, 2 * dwt, rtol=1e-6, atol=1e-7)
+
+
+def test_teacher_gradient_zero_without_teacher_ce():
+    w = C2.scaled(n=200, d=256, v=1500)
+    x = make_inputs(w, "cuda", seed=4)
+    r = make_runner(w, x)
+    r.forward()
+    dht = torch.full((r.n, r.dt), 3.0, dtype=torch.float32, device="cuda")
+    dwt = torch.full((r.v, r.dt), 3.0, dtype=torch.float32, device="cuda")
+    r.backward_teacher(dht, dwt)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dht).item() == 0 and torch.count_nonzero(dwt).item() == 0
+
+
 def test_full_quickstart_logits_teacher_bf16():
     """Quickstart shape with a dense cached teacher (N=4096, D=2048, V=32000,
     T_s = 2, T_t = 1.5), every output."""
