@@ -31,13 +31,15 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
-def method_flops(w) -> dict:
+def method_flops(w, train_teacher: bool = False, n_rows: int = 0) -> dict:
     """Algorithmic MFMA flops of one fwd+bwd step and of one launch of each kernel.
 
     Forward projection tiles: 2 N D V per student GEMM and per teacher GEMM;
-    the backward recomputes them, then dW and dH cost 2 N D V each.
+    the backward recomputes them, then dW and dH cost 2 N D V each. A teacher
+    trained through its CE adds its recompute, dW_t and dH_t: 6 N D_t V.
+    n_rows: the rows projected (the usable-label rows when they are compacted).
     """
-    n, d, v, dt = w.n, w.d, w.v, w.teacher_dim
+    n, d, v, dt = (n_rows or w.n), w.d, w.v, w.teacher_dim
     if w.teacher == "tied":
         fwd = 4 * n * d * v
     elif w.teacher == "separate":
@@ -46,20 +48,28 @@ def method_flops(w) -> dict:
         fwd = 2 * n * d * v
     total = 2 * fwd + 4 * n * d * v
     useful = fwd + 4 * n * d * v
+    if train_teacher:
+        total += 6 * n * dt * v
+        useful += 4 * n * dt * v
     return {"total": total, "useful": useful, "fwd_per_launch": fwd}
 
 
-def kernel_flops_per_launch(w, kernel: str, chunk: int) -> float:
-    n, d, v = w.n, w.d, w.v
-    fl = method_flops(w)
+def kernel_flops_per_launch(w, kernel: str, chunk: int, n_rows: int = 0,
+                            train_teacher: bool = False) -> float:
+    """Flops of one launch of `kernel`; with a trained teacher the launches of a
+    class alternate between the student's and the teacher's, so the mean."""
+    n, d, v, dt = (n_rows or w.n), w.d, w.v, w.teacher_dim
+    fl = method_flops(w, n_rows=n)
     if kernel == "fwd":
         return fl["fwd_per_launch"]
     n_chunks = -(-v // chunk)
     per_chunk_cols = v / n_chunks  # average columns per launch
     if kernel == "bwd_dz":
-        return fl["fwd_per_launch"] * per_chunk_cols / v
+        f = fl["fwd_per_launch"] * per_chunk_cols / v
+        return (f + 2 * n * dt * per_chunk_cols) / 2 if train_teacher else f
     if kernel in ("gemm_dw", "gemm_dh"):
-        return 2 * n * d * per_chunk_cols
+        f = 2 * n * d * per_chunk_cols
+        return (f + 2 * n * dt * per_chunk_cols) / 2 if train_teacher else f
     return 0.0
 
 
@@ -222,6 +232,8 @@ def main() -> int:
                     help="leave rows with an ignored label out of the projections (compact_valid)")
     ap.add_argument("--kl", choices=("forward", "reverse", "jeffreys"), default=None,
                     help="override the workload's KL direction")
+    ap.add_argument("--train-teacher", action="store_true",
+                    help="teacher trained through its CE (weight 1): the step adds its backward")
     ap.add_argument("--ignore-frac", type=float, default=None,
                     help="override the fraction of rows whose label is ignored")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -267,8 +279,11 @@ def main() -> int:
         over["compact_valid"] = True
     if args.ignore_frac is not None:
         over["ignore_frac"] = args.ignore_frac
+    if args.train_teacher:
+        over["teacher_ce_weight"] = 1.0
     if over:
         tag = {"kl_divergence": lambda v: v, "compact_valid": lambda v: "compact",
+               "teacher_ce_weight": lambda v: "train_teacher",
                "ignore_frac": lambda v: f"ignore{v:g}"}
         w = w.scaled(name=w.name + "_" + "_".join(tag[k](v) if k in tag else f"{k}{v}"
                                                   for k, v in over.items()), **over)
@@ -303,13 +318,19 @@ def main() -> int:
     if not w.forward_only:
         dh = torch.empty((r.n, r.d), dtype=torch.float32, device=dev)
         dw = torch.empty((r.v, r.d), dtype=torch.float32, device=dev)
-    output_bytes = sum(t.numel() * t.element_size() for t in (dh, dw) if t is not None)
+    dht = dwt = None
+    if args.train_teacher:
+        dht = torch.empty((r.n, r.dt), dtype=torch.float32, device=dev)
+        dwt = torch.empty((r.v, r.dt), dtype=torch.float32, device=dev)
+    output_bytes = sum(t.numel() * t.element_size() for t in (dh, dw, dht, dwt) if t is not None)
     output_bytes += 3 * r.n * 4 + 4
 
     def step(trace=None):
         r.forward(trace)
         if dh is not None:
             r.backward(dh, dw, trace=trace)
+        if dht is not None:
+            r.backward_teacher(dht, dwt, trace=trace)
 
     # Warm-up, with every kernel class traced once to find the dominant one.
     all_tr = Tracer(capacity=4096, kernels=L.KERNELS)
@@ -349,14 +370,19 @@ def main() -> int:
 
     ms_per_step = gpu_ms / args.steps
     tokens_per_s = r.n * args.steps / (gpu_ms / 1e3)
-    fl = method_flops(w)
+    # rows the kernels project: all, or the usable-label rows when compacted
+    n_rows = w.n
+    if w.compact_valid and x["labels"] is not None:
+        y = x["labels"]
+        n_rows = int(((y != w.ignore_index) & (y >= 0) & (y < w.v)).sum().item())
+    fl = method_flops(w, args.train_teacher, n_rows)
     peak_tflops = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     # the backward chunk the library used (same rule as the C ABI's default)
     chunk = args.vocab_chunk if args.vocab_chunk > 0 else 8192
     chunk = min(-(-chunk // 128) * 128, -(-w.v // 128) * 128)
     launch_ms = sum(durs) / len(durs) if durs else float("nan")
-    kflops = kernel_flops_per_launch(w, dominant, chunk)
+    kflops = kernel_flops_per_launch(w, dominant, chunk, n_rows, args.train_teacher)
     achieved = kflops / (launch_ms / 1e3) / 1e12 if durs else None
     rec = {
         "metric": "fused LM-head+CE+KL fwd+bwd tokens/s" if not w.forward_only
@@ -376,6 +402,7 @@ def main() -> int:
                    "vocab": w.v, "teacher": w.teacher, "temperature": w.temperature,
                    "teacher_temperature": w.teacher_temperature, "kl_divergence": w.kl_divergence,
                    "compact_valid": w.compact_valid, "ignored_rows": w.ignore_frac,
+                   "train_teacher": bool(args.train_teacher), "projected_rows": n_rows,
                    "top_k": w.k or None, "vocab_chunk": chunk, "parallelism": "single GPU"},
         "mfma_tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / peak_tflops, 4),
