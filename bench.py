@@ -67,9 +67,11 @@ def kernel_flops_per_launch(w, kernel: str, chunk: int, n_rows: int = 0,
     if kernel == "bwd_dz":
         f = fl["fwd_per_launch"] * per_chunk_cols / v
         return (f + 2 * n * dt * per_chunk_cols) / 2 if train_teacher else f
-    if kernel in ("gemm_dw", "gemm_dh"):
+    if kernel in ("gemm_dw", "gemm_dh", "gemm_dwdh"):
         f = 2 * n * d * per_chunk_cols
-        return (f + 2 * n * dt * per_chunk_cols) / 2 if train_teacher else f
+        if train_teacher:
+            f = (f + 2 * n * dt * per_chunk_cols) / 2
+        return 2 * f if kernel == "gemm_dwdh" else f
     return 0.0
 
 
@@ -109,7 +111,10 @@ _KERNEL_CLASS = (("prep_kernel", "prep"), ("fwd_tiles_kernel", "fwd"), ("merge_k
                  ("gemm_pipe_kernel<true, false", "gemm_dh"), ("gemm_kernel<float, false, false", "gemm_dw"),
                  ("gemm_kernel<unsigned short, false, false", "gemm_dw"),
                  ("gemm_kernel<float, true, false", "gemm_dh"),
-                 ("gemm_kernel<unsigned short, true, false", "gemm_dh"))
+                 ("gemm_kernel<unsigned short, true, false", "gemm_dh"),
+                 ("gemm_dual_kernel", "gemm_dwdh"), ("compact_kernel", "prep"),
+                 ("gather_rows_kernel", "prep"), ("zero_rows_kernel", "gemm_dh"),
+                 ("fill_zero_kernel", "gemm_dh"))
 
 
 def _counter_per_dispatch(path: str, counter: str):

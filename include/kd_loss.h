@@ -171,7 +171,8 @@ enum {
   KD_KERNEL_BWD_DZ = 4,    /* backward recompute tiles + logit-gradient epilogue */
   KD_KERNEL_SCATTER = 5,   /* top-K: subtract p at the cached indices */
   KD_KERNEL_GEMM_DW = 6,   /* dW[chunk] = dZ_chunk^T H */
-  KD_KERNEL_GEMM_DH = 7    /* dH += dZ_chunk W[chunk] */
+  KD_KERNEL_GEMM_DH = 7,   /* dH += dZ_chunk W[chunk] */
+  KD_KERNEL_GEMM_DWDH = 8  /* both GEMMs of a chunk in one launch */
 };
 typedef struct {
   void** events;     /* host array of hipEvent_t */

@@ -17,7 +17,8 @@ KD_STUDENT_PROJECTION, KD_STUDENT_LOGITS = 0, 1
 KD_TEACHER_TIED, KD_TEACHER_SEPARATE, KD_TEACHER_TOPK, KD_TEACHER_LOGITS = 1, 2, 3, 4
 KD_REDUCE_MEAN, KD_REDUCE_SUM, KD_REDUCE_NONE = 0, 1, 2
 KD_KL_FORWARD, KD_KL_REVERSE, KD_KL_JEFFREYS = 0, 1, 2
-KERNELS = ["prep", "fwd", "merge", "finalize", "bwd_dz", "scatter", "gemm_dw", "gemm_dh"]
+KERNELS = ["prep", "fwd", "merge", "finalize", "bwd_dz", "scatter", "gemm_dw", "gemm_dh",
+           "gemm_dwdh"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
 

@@ -1126,18 +1126,22 @@ struct GemmPipeArgs {
   const int32_t* rowmap;  // non-null: C row m is stored at row rowmap[m]
 };
 
+// M and K of a launch (compacted rows bound them from device memory) and the
+// number of row tiles that have work.
 template <bool AKC, bool BKC, int BN>
-__global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC, BN> a) {
+__device__ __forceinline__ void gemm_pipe_bounds(const GemmPipeArgs<AKC, BKC, BN>& a, int64_t& M,
+                                                 int64_t& K, int& n_mt) {
+  M = a.mdev ? min(a.M, (int64_t)*a.mdev) : a.M;
+  K = a.kdev ? min(a.K, ((int64_t)*a.kdev + kPipeBK - 1) / kPipeBK * kPipeBK) : a.K;
+  n_mt = a.mdev ? (int)((M + 255) / 256) : a.n_mt;
+}
+
+// Output tile (mt, nt) of the pipelined GEMM.
+template <bool AKC, bool BKC, int BN>
+__device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>& a, int mt, int nt,
+                                               int64_t M, int64_t K, uint8_t* lds, int tid) {
   using C = PipeCfg<256, BN, 1, AKC, BKC>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int64_t M = a.mdev ? min(a.M, (int64_t)*a.mdev) : a.M;
-  const int64_t K = a.kdev ? min(a.K, ((int64_t)*a.kdev + kPipeBK - 1) / kPipeBK * kPipeBK) : a.K;
-  const int n_mt = a.mdev ? (int)((M + 255) / 256) : a.n_mt;  // row tiles with work
-  int t;
-  if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
-  int mt, nt;
-  grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
+  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
   f32x4 acc[1][C::MB][C::NBK];
   pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid);
@@ -1165,6 +1169,51 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
         }
       }
     }
+}
+
+template <bool AKC, bool BKC, int BN>
+__global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC, BN> a) {
+  using C = PipeCfg<256, BN, 1, AKC, BKC>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  int64_t M, K;
+  int n_mt;
+  gemm_pipe_bounds(a, M, K, n_mt);
+  int t;
+  if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
+  int mt, nt;
+  grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
+  gemm_pipe_tile(a, mt, nt, M, K, lds, threadIdx.x);
+}
+
+// dH and dW of one chunk in one launch, both from the dz slab with 256 x 256
+// tiles. dH alone has too few 256 x 256 tiles to fill the chip (N/256 x D/256)
+// and its 256 x 128 form moves twice the operand bytes per MFMA; next to the dW
+// tiles it needs no second wave: each XCD takes its share of dH tiles first
+// (the longer ones, K = chunk) and then its share of dW tiles (K = N), so while
+// half of an XCD's CUs run one dH tile the other half run two dW tiles.
+template <int BN>
+__global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, false, BN> h,
+                                                           GemmPipeArgs<false, false, BN> g) {
+  using CH = PipeCfg<256, BN, 1, true, false>;
+  using CW = PipeCfg<256, BN, 1, false, false>;
+  static_assert(CH::kLdsBytes == CW::kLdsBytes, "one LDS image serves both");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CH::kLdsBytes];
+  int64_t mh, kh, mw, kw;
+  int nmt_h, nmt_w;
+  gemm_pipe_bounds(h, mh, kh, nmt_h);
+  gemm_pipe_bounds(g, mw, kw, nmt_w);
+  const int na = nmt_h * h.n_nt, nb = nmt_w * g.n_nt;
+  const int x = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int qa = na / kXcds + (x < na % kXcds ? 1 : 0);
+  const int qb = nb / kXcds + (x < nb % kXcds ? 1 : 0);
+  int mt, nt;
+  if (local < qa) {
+    grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + local, nmt_h, h.n_nt, 8, mt, nt);
+    gemm_pipe_tile(h, mt, nt, mh, kh, lds, threadIdx.x);
+  } else if (local - qa < qb) {
+    grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + (local - qa), nmt_w, g.n_nt, 8, mt, nt);
+    gemm_pipe_tile(g, mt, nt, mw, kw, lds, threadIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1365,61 +1414,74 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     const int64_t cpad = (int64_t)n_vt * G::kVT;  // columns written by bwd_dz
     const int n_gemm_mt = (int)((cw + kTile - 1) / kTile);
     if constexpr (G::kPipe) {
-      // 256-wide tiles when they still give every CU a tile, else 128-wide.
-      auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((gd + 255) / 256) >= 256; };
-      if (dw) {
-        // dW[c0 + m, :] = sum_i dz[i, m] H_s[i, :]: A(m, i) = dz[i * ldz + m], B(n, i) = H_s[i * d + n],
-        // both row-contiguous; the slab's zero rows past n pad K to a multiple of 64.
-        auto launch = [&](auto bn_tag) {
-          constexpr int BN = decltype(bn_tag)::value;
-          GemmPipeArgs<false, false, BN> ga;
-          ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
-          ga.B = PipeOperandMN{hs, gd, gd, p.n};
-          ga.C = dw + c0 * gd;
-          ga.ldc = gd;
-          ga.M = cw;
-          ga.N = gd;
-          ga.K = p.dz_rows;
-          ga.accumulate = accumulate;
-          ga.n_mt = (int)((cw + 255) / 256);
-          ga.n_nt = (int)((gd + BN - 1) / BN);
-          ga.kdev = cp.nv;  // compacted: the token rows stop at nv
-          ga.mdev = nullptr;
-          ga.rowmap = nullptr;
-          return L.run(KD_KERNEL_GEMM_DW, [&] {
-            gemm_pipe_kernel<false, false, BN>
-                <<<dim3((unsigned)(ga.n_mt * ga.n_nt)), 512, 0, stream>>>(ga);
-          });
+      // dW[c0 + m, :] = sum_i dz[i, m] H[i, :]: A(m, i) = dz[i * ldz + m], B(n, i) = H[i * d + n],
+      // both row-contiguous; the slab's zero rows past n pad K to a multiple of 64.
+      auto dw_args = [&](auto bn_tag) {
+        constexpr int BN = decltype(bn_tag)::value;
+        GemmPipeArgs<false, false, BN> ga;
+        ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
+        ga.B = PipeOperandMN{hs, gd, gd, p.n};
+        ga.C = dw + c0 * gd;
+        ga.ldc = gd;
+        ga.M = cw;
+        ga.N = gd;
+        ga.K = p.dz_rows;
+        ga.accumulate = accumulate;
+        ga.n_mt = (int)((cw + 255) / 256);
+        ga.n_nt = (int)((gd + BN - 1) / BN);
+        ga.kdev = cp.nv;  // compacted: the token rows stop at nv
+        ga.mdev = nullptr;
+        ga.rowmap = nullptr;
+        return ga;
+      };
+      // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]: A(i, m) = dz[i * ldz + m] (K-contiguous),
+      // B(n, m) = W[(c0 + m) * d + n] (row-contiguous); slab columns past cw are zero.
+      auto dh_args = [&](auto bn_tag) {
+        constexpr int BN = decltype(bn_tag)::value;
+        GemmPipeArgs<true, false, BN> gb;
+        gb.A = PipeOperand{dz, ldz, p.n};
+        gb.B = PipeOperandMN{wmat + c0 * gd, gd, gd, cw};
+        gb.C = dh;
+        gb.ldc = gd;
+        gb.M = p.n;
+        gb.N = gd;
+        gb.K = cpad;
+        gb.accumulate = (accumulate || c > 0) ? 1 : 0;
+        gb.n_mt = (int)((p.n + 255) / 256);
+        gb.n_nt = (int)((gd + BN - 1) / BN);
+        gb.kdev = nullptr;
+        gb.mdev = cp.nv;      // compacted: rows past nv are not tokens
+        gb.rowmap = cp.idx;   // compacted row m is token idx[m]
+        return gb;
+      };
+      using W256 = std::integral_constant<int, 256>;
+      using W128 = std::integral_constant<int, 128>;
+      if (dw && dh) {
+        // one launch, 256 x 256 tiles for both; the grid covers the largest
+        // per-XCD share of dH plus dW tiles
+        const auto gb = dh_args(W256{});
+        const auto ga = dw_args(W256{});
+        const int na = gb.n_mt * gb.n_nt, nb = ga.n_mt * ga.n_nt;
+        int most = 0;
+        for (int xc = 0; xc < kXcds; ++xc)
+          most = std::max(most, na / kXcds + (xc < na % kXcds) + nb / kXcds + (xc < nb % kXcds));
+        KD_TRY(L.run(KD_KERNEL_GEMM_DWDH, [&] {
+          gemm_dual_kernel<256><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
+        }));
+      } else {
+        // 256-wide tiles when they still give every CU a tile, else 128-wide.
+        auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((gd + 255) / 256) >= 256; };
+        auto run = [&](int kind, auto args, auto kern) {
+          return L.run(kind, [&] { kern<<<dim3((unsigned)(args.n_mt * args.n_nt)), 512, 0, stream>>>(args); });
         };
-        KD_TRY(wide(cw) ? launch(std::integral_constant<int, 256>{})
-                        : launch(std::integral_constant<int, 128>{}));
-      }
-      if (dh) {
-        // dH[i, :] += sum_m dz[i, m] W[c0 + m, :]: A(i, m) = dz[i * ldz + m] (K-contiguous),
-        // B(n, m) = W[(c0 + m) * d + n] (row-contiguous); slab columns past cw are zero.
-        auto launch = [&](auto bn_tag) {
-          constexpr int BN = decltype(bn_tag)::value;
-          GemmPipeArgs<true, false, BN> gb;
-          gb.A = PipeOperand{dz, ldz, p.n};
-          gb.B = PipeOperandMN{wmat + c0 * gd, gd, gd, cw};
-          gb.C = dh;
-          gb.ldc = gd;
-          gb.M = p.n;
-          gb.N = gd;
-          gb.K = cpad;
-          gb.accumulate = (accumulate || c > 0) ? 1 : 0;
-          gb.n_mt = (int)((p.n + 255) / 256);
-          gb.n_nt = (int)((gd + BN - 1) / BN);
-          gb.kdev = nullptr;
-          gb.mdev = cp.nv;      // compacted: rows past nv are not tokens
-          gb.rowmap = cp.idx;   // compacted row m is token idx[m]
-          return L.run(KD_KERNEL_GEMM_DH, [&] {
-            gemm_pipe_kernel<true, false, BN>
-                <<<dim3((unsigned)(gb.n_mt * gb.n_nt)), 512, 0, stream>>>(gb);
-          });
-        };
-        KD_TRY(wide(p.n) ? launch(std::integral_constant<int, 256>{})
-                         : launch(std::integral_constant<int, 128>{}));
+        if (dw) {
+          KD_TRY(wide(cw) ? run(KD_KERNEL_GEMM_DW, dw_args(W256{}), gemm_pipe_kernel<false, false, 256>)
+                          : run(KD_KERNEL_GEMM_DW, dw_args(W128{}), gemm_pipe_kernel<false, false, 128>));
+        }
+        if (dh) {
+          KD_TRY(wide(p.n) ? run(KD_KERNEL_GEMM_DH, dh_args(W256{}), gemm_pipe_kernel<true, false, 256>)
+                           : run(KD_KERNEL_GEMM_DH, dh_args(W128{}), gemm_pipe_kernel<true, false, 128>));
+        }
       }
     } else {
     if (dw) {

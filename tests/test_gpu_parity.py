@@ -87,6 +87,26 @@ def test_accumulate_adds_into_gradients():
     assert torch.allclose(dw2, dw - 0.25, rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("which", ["dh", "dw"])
+def test_one_gradient_at_a_time(which):
+    """Asking for dH or dW alone takes the single-GEMM launches (both together
+    share one); each matches the oracle, and dW alone equals the joint launch's
+    dW bit for bit (same tiles, same order)."""
+    w = C2.scaled(n=600, d=512, v=3000)
+    x = make_inputs(w, "cuda", seed=12)
+    r, dh, dw = run_gpu(w, x)
+    s, t, labels = oracle_problem(w, x)
+    dH, dW = O.backward(s, t, params_of(w), labels)
+    g = torch.empty_like(dh if which == "dh" else dw)
+    r.forward()
+    r.backward(g if which == "dh" else None, g if which == "dw" else None)
+    torch.cuda.synchronize()
+    if which == "dh":
+        assert_grad(to_np(g), dH, "bf16", "dH alone")
+    else:
+        assert_grad(to_np(g), dW, "bf16", "dW alone")
+
+
 @pytest.mark.parametrize("kl", ["forward", "reverse", "jeffreys"])
 def test_kl_exactly_zero_for_identical_teacher(kl):
     """Tied teacher with H_t = H_s: the two logit tiles are computed by the same
