@@ -150,6 +150,51 @@ __device__ __forceinline__ void tile_sum_cross(const WaveAcc& x, const WaveAcc& 
   a = a0 + a1;
 }
 
+// tile_sum_cross with q = sum e^2 besides: the sum at twice the scale against
+// twice the reference. At T = 2 that is the T = 1 sum, so one exponential per
+// element serves both temperatures (the square rounds once more, well inside
+// fp32). STUDENT_W: the student-weighted cross term (e of z, d = z - t rho);
+// CROSS = false: no cross term (a is left alone).
+template <bool TAIL, bool CROSS, bool TEACHER_W, bool ZERO_SAFE = false>
+__device__ __forceinline__ void tile_sums_sq(const WaveAcc& x, const WaveAcc& y, int nb, float c, float mc,
+                                             float rho, uint32_t ok, float& s, float& q, float& a) {
+  float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < kMB; mb += 2)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mc));
+      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mc));
+      if (TAIL) {
+        e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
+        e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
+      }
+      s0 += e0;
+      s1 += e1;
+      q0 = fmaf(e0, e0, q0);
+      q1 = fmaf(e1, e1, q1);
+      if constexpr (CROSS) {
+        float d0, d1;
+        if constexpr (TEACHER_W) {
+          d0 = fmaf(x[mb][nb][r], rho, -y[mb][nb][r]);
+          d1 = fmaf(x[mb + 1][nb][r], rho, -y[mb + 1][nb][r]);
+        } else {
+          d0 = fmaf(y[mb][nb][r], -rho, x[mb][nb][r]);
+          d1 = fmaf(y[mb + 1][nb][r], -rho, x[mb + 1][nb][r]);
+        }
+        if constexpr (ZERO_SAFE) {
+          d0 = (e0 > 0.f) ? d0 : 0.f;
+          d1 = (e1 > 0.f) ? d1 : 0.f;
+        }
+        a0 = fmaf(e0, d0, a0);
+        a1 = fmaf(e1, d1, a1);
+      }
+    }
+  s = s0 + s1;
+  q = q0 + q1;
+  if constexpr (CROSS) a = a0 + a1;
+}
+
 // ---------------------------------------------------------------------------
 // Tile geometry of the fused kernels
 // ---------------------------------------------------------------------------
@@ -314,6 +359,7 @@ struct FwdArgs {
   int need_zT, need_t1;
   int kl;      // KD_KL_*: the reverse direction also needs sum 2^(z~ - m) (z - t)
   int vec;     // given logits: 2 staged through LDS, 1 vector loads, 0 element loads
+  int sqz;     // T_s == 2: the T = 1 student sums are the squares of those at T
   float* rec;  // [kRecFields][n_slices][n]
   const int32_t* nv;  // compacted rows: their number (tiles past it exit); null = n
 };
@@ -438,23 +484,26 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     // treats as empty.
     const float mtb = (kInfT && mt[nb] == -INFINITY) ? 0.f : mt[nb];
     const float mtT = mtb * a.cTt, mt1 = mtb * kLog2e;
-    if (tail) {
-      v[0] = tile_sum<true>(z, nb, kLog2e, mz1, ok);
-      if (kTeacher) {
-        if (rev) tile_sum_cross<true, false>(z, tl, nb, a.cT, mzT, a.rho, ok, v[1], v[5]);
-        else if (a.need_zT) v[1] = tile_sum<true>(z, nb, a.cT, mzT, ok);
-        tile_sum_cross<true, true, kInfT>(tl, z, nb, a.cTt, mtT, a.rho, ok, v[2], v[3]);
-        if (a.need_t1) v[4] = tile_sum<true>(tl, nb, kLog2e, mt1, ok);
+    auto sums = [&](auto tail_tag) {
+      constexpr bool TL = decltype(tail_tag)::value;
+      if (kTeacher && a.sqz) {
+        // T_s = 2: the sums at z/T and at z from one exponential per element
+        if (rev) tile_sums_sq<TL, true, false>(z, tl, nb, a.cT, mzT, a.rho, ok, v[1], v[0], v[5]);
+        else tile_sums_sq<TL, false, false>(z, z, nb, a.cT, mzT, 0.f, ok, v[1], v[0], v[5]);
+      } else {
+        v[0] = tile_sum<TL>(z, nb, kLog2e, mz1, ok);
+        if (kTeacher) {
+          if (rev) tile_sum_cross<TL, false>(z, tl, nb, a.cT, mzT, a.rho, ok, v[1], v[5]);
+          else if (a.need_zT) v[1] = tile_sum<TL>(z, nb, a.cT, mzT, ok);
+        }
       }
-    } else {
-      v[0] = tile_sum<false>(z, nb, kLog2e, mz1, ok);
       if (kTeacher) {
-        if (rev) tile_sum_cross<false, false>(z, tl, nb, a.cT, mzT, a.rho, ok, v[1], v[5]);
-        else if (a.need_zT) v[1] = tile_sum<false>(z, nb, a.cT, mzT, ok);
-        tile_sum_cross<false, true, kInfT>(tl, z, nb, a.cTt, mtT, a.rho, ok, v[2], v[3]);
-        if (a.need_t1) v[4] = tile_sum<false>(tl, nb, kLog2e, mt1, ok);
+        tile_sum_cross<TL, true, kInfT>(tl, z, nb, a.cTt, mtT, a.rho, ok, v[2], v[3]);
+        if (a.need_t1) v[4] = tile_sum<TL>(tl, nb, kLog2e, mt1, ok);
       }
-    }
+    };
+    if (tail) sums(std::true_type{});
+    else sums(std::false_type{});
 #pragma unroll
     for (int j = 0; j < kSums; ++j) {
       v[j] += __shfl_xor(v[j], 16);
@@ -793,6 +842,7 @@ struct BwdArgs {
   int need_zT;
   int kl;                 // KD_KL_*
   int vec;                // teacher logits: 2 staged through LDS, 1 vector loads, 0 element loads
+  int sqz;                // T_s == 2: softmax(z) is the square of one exponential of z/T
   const int32_t* idx;     // compacted rows: original row of each (null: rows are original)
   const int32_t* nv;      // compacted rows: their number
   int64_t c0;             // first vocabulary row of the chunk
@@ -874,8 +924,11 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
 
   // The reverse-direction term is compiled only into the variant that uses it,
   // so the forward-KL epilogue carries no extra arithmetic.
-  auto epilogue = [&](auto rev_tag) {
+  // kSq (T_s = 2): e = 2^(z log2(e)/2 - L1/2) gives softmax(z) = e^2 and
+  // softmax(z/2) = e 2^(L1/2 - LzT): one exponential of z per element, not two.
+  auto epilogue = [&](auto rev_tag, auto sq_tag) {
   constexpr bool kRev = decltype(rev_tag)::value;
+  constexpr bool kSq = decltype(sq_tag)::value;
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const int64_t tok = t0 + acc_col(wn, nb, lane);
@@ -887,6 +940,8 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const float L1 = (MODE == MODE_TCE ? (live ? a.saved[4 * a.n + kSavedHeaderBytes / 4 + orig] : 0.f)
                                        : sv.x) * kLog2e;
     const float LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
+    const float L1h = 0.5f * L1;
+    const float kz = kSq ? exp2_fast(L1h - LzT) : 0.f;
     int64_t y = -1;
     bool valid = live;
     if (live && MODE != MODE_TOPK && a.labels) {
@@ -912,7 +967,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int64_t vv = v0 + acc_row(wm, mb, r, lane);
         const float zz = z[mb][nb][r];
-        const float p1 = exp2_fast(fmaf(zz, kLog2e, -L1));
+        float p1, pz;
+        if constexpr (kSq) {
+          const float e = exp2_fast(fmaf(zz, a.cT, -L1h));
+          p1 = e * e;
+          pz = e * kz;
+        } else {
+          p1 = exp2_fast(fmaf(zz, kLog2e, -L1));
+          pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
+        }
         float dv;
         if (MODE == MODE_TOPK) {
           dv = cm * p1;
@@ -921,7 +984,6 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
         } else {
           dv = cs * (p1 - (vv == y ? 1.f : 0.f));
           const float tt = tl[mb][nb][r];
-          const float pz = a.need_zT ? exp2_fast(fmaf(zz, a.cT, -LzT)) : p1;
           const float pt = exp2_fast(fmaf(tt, a.cTt, -LtT));
           dv = fmaf(ckf, pz - pt, dv);
           if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(fmaf(tt, -a.rho, zz), invT, rev0), dv);
@@ -932,8 +994,14 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     }
   }
   };
-  if (MODE != MODE_TOPK && MODE != MODE_TCE && a.kl != KD_KL_FORWARD) epilogue(std::true_type{});
-  else epilogue(std::false_type{});
+  constexpr bool kStudentKl = MODE != MODE_TOPK && MODE != MODE_TCE;
+  if (kStudentKl && a.sqz) {
+    if (a.kl != KD_KL_FORWARD) epilogue(std::true_type{}, std::true_type{});
+    else epilogue(std::false_type{}, std::true_type{});
+  } else {
+    if (kStudentKl && a.kl != KD_KL_FORWARD) epilogue(std::true_type{}, std::false_type{});
+    else epilogue(std::false_type{}, std::false_type{});
+  }
 }
 
 // Top-K: dz[i, idx - c0] -= (g/den) w_kl p for the entries of this chunk.
@@ -1319,7 +1387,8 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   const void* given = (p.mode == MODE_TLOGITS) ? x.tlogits : x.logits;
   FwdArgs fa{cp.hs, x.w, cp.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
              p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, kLog2e / p.Tt, p.T / p.Tt,
-             p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v), rec, cp.nv};
+             p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v),
+             (p.T == 2.f && p.need_zT) ? 1 : 0, rec, cp.nv};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
@@ -1392,7 +1461,8 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     BwdArgs ba{cp.hs, x.w, cp.ht, x.wt, x.tlogits, p.n, p.d, p.dt, p.v, x.labels, p.ignore,
                static_cast<const float*>(saved), grad, p.ws, p.wkl, p.T, kLog2e / p.T,
                kLog2e / p.Tt, p.T / p.Tt, p.wt, p.need_zT, p.kl, given_mode<T, G>(x.tlogits, p.v),
-               cp.idx, cp.nv, c0, n_vt, p.n_ttiles, dz, ldz, p.dz_rows};
+               (!teacher && p.T == 2.f && p.need_zT) ? 1 : 0, cp.idx, cp.nv, c0, n_vt, p.n_ttiles,
+               dz, ldz, p.dz_rows};
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
       switch (mode) {
