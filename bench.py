@@ -384,7 +384,7 @@ def main() -> int:
     peak_tflops = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     # the backward chunk the library used (same rule as the C ABI's default)
-    chunk = args.vocab_chunk if args.vocab_chunk > 0 else 8192
+    chunk = args.vocab_chunk if args.vocab_chunk > 0 else 16384
     chunk = min(-(-chunk // 128) * 128, -(-w.v // 128) * 128)
     launch_ms = sum(durs) / len(durs) if durs else float("nan")
     kflops = kernel_flops_per_launch(w, dominant, chunk, n_rows, args.train_teacher)

@@ -133,7 +133,8 @@ typedef struct {
   int32_t reduction;         /* KD_REDUCE_* */
   float normalizer;          /* > 0: divide the summed loss by it (num_batch_labels) */
   int64_t vocab_chunk;       /* vocabulary columns per backward chunk, rounded up to whole tiles;
-                                the dz slab holds n x chunk; 0 = library default (8192) */
+                                the dz slab holds n x chunk; 0 = library default (16384,
+                                flash_kd's chunk_size default) */
   int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
   int32_t kl_divergence;     /* KD_KL_* */
   float teacher_temperature; /* T_t > 0, finite: the teacher's own temperature (orda-kernel,

@@ -442,6 +442,36 @@ def check_teacher_grad_finite_differences(O):
         assert err < 1e-6, f"teacher finite differences d{which}: {err:.2e}"
 
 
+def check_logit_grad_finite_differences(O):
+    """Both sides given as logits (nemo KDLoss: student and teacher logits):
+    central differences of the loss in the student logits match logit_grad for
+    forward and reverse KL, with CE, a teacher temperature and an upstream
+    gradient."""
+    r = _rng(37)
+    n, v = 5, 7
+    z = r.normal(size=(n, v)) * 1.5
+    tl = r.normal(size=(n, v)) * 1.5
+    y = np.array([1, -100, 6, 0, 3])
+    for variant, Tt in (("forward", None), ("reverse", 0.9), ("jeffreys", 1.6)):
+        p = O.Params(student_ce_weight=0.4, kl_weight=1.1, temperature=2.0, teacher_temperature=Tt,
+                     kl_divergence=variant, normalizer=3.0)
+        t = O.Teacher("logits", logits=tl)
+
+        def loss(z_):
+            return O.forward(O.Student(logits=z_), t, p, y)["loss"] * 0.7
+
+        g = O.logit_grad(O.Student(logits=z), t, p, y, np.arange(n), den=3.0, grad_loss=0.7)
+        h = 1e-6
+        num = np.zeros_like(z)
+        for ij in np.ndindex(*z.shape):
+            zp, zm = z.copy(), z.copy()
+            zp[ij] += h
+            zm[ij] -= h
+            num[ij] = (loss(zp) - loss(zm)) / (2 * h)
+        err = np.max(np.abs(num - g)) / np.max(np.abs(g))
+        assert err < 1e-6, f"logit-gradient finite differences ({variant}): {err:.2e}"
+
+
 def check_logits_teacher_matches_projection(O):
     """A dense cached teacher holding H_t W_t^T gives the separate teacher's
     per-token values and gradients."""

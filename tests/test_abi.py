@@ -116,6 +116,9 @@ def test_backward_workspace_is_O_n_chunk_not_n_vocab():
     assert st == L.KD_OK
     assert bwd <= 32768 * 8192 * 2 + (1 << 16)
     assert bwd < 32768 * 151936 * 4 / 8
+    p.vocab_chunk = 0  # the default chunk: 16384 columns
+    st, bwd = _ws(s, t, p, 1)
+    assert st == L.KD_OK and 32768 * 16384 * 2 <= bwd <= 32768 * 16384 * 2 + (1 << 16)
 
 
 @pytest.mark.parametrize("case,expect", [
