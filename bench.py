@@ -198,7 +198,10 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
 
     def run(rows: int) -> float:
         g = lambda k: None if full[k] is None else full[k][:rows]  # noqa: E731
-        s = O.Student(hidden=g("student_hidden"), weight=full["weight"])
+        if w.student == "logits":
+            s = O.Student(logits=g("student_logits"))
+        else:
+            s = O.Student(hidden=g("student_hidden"), weight=full["weight"])
         if w.teacher == "tied":
             t = O.Teacher("tied", hidden=g("teacher_hidden"))
         elif w.teacher == "separate":
@@ -208,8 +211,11 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
         else:
             t = O.Teacher("topk", idx=g("topk_idx"), prob=g("topk_prob"))
         t0 = time.perf_counter()
-        O.forward(s, t, p, g("labels"))
-        O.backward(s, t, p, g("labels"))
+        out = O.forward(s, t, p, g("labels"))
+        if w.student == "logits" and w.teacher == "logits":  # the gradient to the given logits
+            O.logit_grad(s, t, p, g("labels"), np.arange(rows), out["den"])
+        elif not w.forward_only:
+            O.backward(s, t, p, g("labels"))
         return time.perf_counter() - t0
 
     probe = 64
@@ -218,8 +224,8 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
     rows = max(probe, rows // 64 * 64)
     dt = run(rows)
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} of {w.n} rows of {w.name}, forward + backward (dH, dW) in float64, "
-                      f"{dt:.1f} s"}
+            "sample": f"{rows} of {w.n} rows of {w.name}, forward + backward "
+                      f"({'d logits' if w.student == 'logits' else 'dH, dW'}) in float64, {dt:.1f} s"}
 
 
 def main() -> int:
@@ -323,11 +329,13 @@ def main() -> int:
     if not w.forward_only:
         dh = torch.empty((r.n, r.d), dtype=torch.float32, device=dev)
         dw = torch.empty((r.v, r.d), dtype=torch.float32, device=dev)
+    both_logits = w.student == "logits" and w.teacher == "logits"
+    dlog = torch.empty((r.n, r.v), dtype=w.torch_dtype, device=dev) if both_logits else None
     dht = dwt = None
     if args.train_teacher:
         dht = torch.empty((r.n, r.dt), dtype=torch.float32, device=dev)
         dwt = torch.empty((r.v, r.dt), dtype=torch.float32, device=dev)
-    output_bytes = sum(t.numel() * t.element_size() for t in (dh, dw, dht, dwt) if t is not None)
+    output_bytes = sum(t.numel() * t.element_size() for t in (dh, dw, dht, dwt, dlog) if t is not None)
     output_bytes += 3 * r.n * 4 + 4
 
     def step(trace=None):
@@ -336,6 +344,8 @@ def main() -> int:
             r.backward(dh, dw, trace=trace)
         if dht is not None:
             r.backward_teacher(dht, dwt, trace=trace)
+        if dlog is not None:
+            r.backward_logits(dlog, trace=trace)
 
     # Warm-up, with every kernel class traced once to find the dominant one.
     all_tr = Tracer(capacity=4096, kernels=L.KERNELS)
@@ -431,6 +441,21 @@ def main() -> int:
             "flop_per_launch": kflops,
         },
     }
+    if both_logits:
+        # No projection: the row kernels stream the logits, HBM-bound. Bytes per
+        # launch: the forward reads both matrices; the backward reads both and
+        # writes the gradient.
+        e = 2 if w.dtype == "bf16" else 4
+        nbytes = {"fwd": 2 * w.n * w.v * e, "bwd_dz": 3 * w.n * w.v * e}.get(dominant, 0)
+        gbs = nbytes / (launch_ms / 1e3) / 1e9 if durs and nbytes else None
+        rec["metric"] = "KL from given logits fwd+bwd tokens/s"
+        rec["mfma_tflops"] = rec["mfma_frac_of_peak"] = rec["useful_tflops"] = None
+        rec["roofline"] = {
+            "kernel": dominant, "bound": "hbm",
+            "achieved": round(gbs, 1) if gbs else None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4) if gbs else None,
+            "traffic": traffic_for(dominant, w.name), "launch_ms": round(launch_ms, 4),
+            "launches": len(durs), "bytes_per_launch": nbytes}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -78,8 +78,10 @@ enum {
 enum { KD_F32 = 0, KD_BF16 = 1 };
 
 /* Student side. PROJECTION: logits z = hidden @ weight^T (forward + backward).
- * LOGITS: z is given as `logits` [n, v] (flash_kd, flash_ce_kd_loss:
- * student_logits); forward only, and the teacher must be SEPARATE. */
+ * LOGITS: z is given as `logits` [n, v], with a SEPARATE teacher (flash_kd,
+ * flash_ce_kd_loss: student_logits; forward only) or a LOGITS teacher (nemo
+ * kd_loss, KDLoss.forward: student_logits and teacher_logits; the gradient to
+ * the student logits comes from kd_loss_bwd_logits). */
 enum { KD_STUDENT_PROJECTION = 0, KD_STUDENT_LOGITS = 1 };
 
 /* Teacher descriptor kinds (orda-kernel, Teacher descriptors). LOGITS is the
@@ -121,7 +123,10 @@ typedef struct {
   const float* topk_prob;   /* TOPK [n, k], not renormalised (sum = retained mass M) */
   const void* logits;       /* LOGITS [n, v] row-major, student dtype, element-aligned. A -inf
                                entry is a zero teacher probability: it adds 0 to the forward KL
-                               and makes the reverse KL +inf. Every row needs a finite entry. */
+                               and makes the reverse KL +inf. Every row needs a finite entry.
+                               With a PROJECTION student the tiles read it in place of the
+                               teacher projection; with a LOGITS student (both given) row
+                               kernels stream the two matrices (no GEMM). */
 } kd_teacher;
 
 typedef struct {
@@ -212,6 +217,16 @@ kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params*
                       const int64_t* labels, const void* saved, const float* grad_loss,
                       float* d_hidden, float* d_weight, int32_t accumulate,
                       void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
+
+/* Backward to given student logits (nemo kd_loss, KDLoss: the loss is
+ * differentiated in student_logits): LOGITS student with a LOGITS teacher.
+ * d_logits: [n, v] in the student dtype (bf16 rounded to nearest even),
+ * row-major, overwritten (accumulate = 0) or added to (1); NULL = nothing.
+ * saved and grad_loss as for kd_loss_bwd; no workspace is needed. Not for
+ * REDUCE_NONE (KD_ERR_UNSUPPORTED). */
+kd_status kd_loss_bwd_logits(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                             const int64_t* labels, const void* saved, const float* grad_loss,
+                             void* d_logits, int32_t accumulate, void* stream, kd_trace* trace);
 
 /* Backward to a teacher trained through its CE (orda-kernel, Teacher
  * descriptors: with teacher_ce_weight > 0 the teacher trains via CE; the KL

@@ -61,6 +61,9 @@ EXPORTS = {
     "kd_loss_bwd": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                               c_void_p, c_size_t, c_void_p, POINTER(KdTrace)]),
+    "kd_loss_bwd_logits": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                     POINTER(KdTrace)]),
     "kd_loss_bwd_teacher": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                       c_void_p, c_size_t, c_void_p, POINTER(KdTrace)]),

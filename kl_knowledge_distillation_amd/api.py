@@ -14,6 +14,9 @@ User API (orda-kernel, Quickstart / Teacher descriptors / Parameters):
     teachers: TiedTeacher(hidden), SeparateTeacher(hidden, weight),
               PrecomputedTeacher(logits=...) or (teacher_hidden=..., teacher_weight=...),
               TopKTeacher(indices, probs)   (Full-Chunked-KL-Loss cached top-K)
+Logits given on both sides (nemo kd_loss, KDLoss):
+    KDLoss(ignore_index=-100, temperature=1.0).forward(student_logits, teacher_logits, labels,
+                                                       num_batch_labels=None) -> scalar
 Scorer (flash_kd, flash_ce_kd_loss):
     flash_ce_kd_loss(student_logits, teacher_hidden, teacher_lm_head_weight, labels, *,
                      temperature=1.0, ignore_index=-1, chunk_size=16384) -> (ce, kd)
@@ -162,7 +165,7 @@ class Runner:
             t.d_t = teacher_hidden.shape[1]
             t.hidden = _ptr(teacher_hidden)
             t.weight = _ptr(teacher_weight)
-        elif teacher_kind == "logits":
+        elif teacher_kind == "logits":  # with student_logits: both given (nemo KDLoss)
             t.kind = L.KD_TEACHER_LOGITS
             if tuple(teacher_logits.shape) != (s.n, s.v) or teacher_logits.dtype != ref.dtype:
                 raise ValueError("teacher logits must be (BT, vocab) in the student dtype")
@@ -209,6 +212,7 @@ class Runner:
         self.ws_fwd = self._workspace(0)
         self.ws_bwd = self._workspace(1) if (want_grads and s.kind == L.KD_STUDENT_PROJECTION) \
             else None
+        self.dtype = ref.dtype
         self.labels_ptr = _ptr(labels)
 
     def _workspace(self, backward: int) -> torch.Tensor:
@@ -242,6 +246,20 @@ class Runner:
                                   self.ws_bwd.data_ptr(), self.ws_bwd.numel(), self._stream(),
                                   ctypes.byref(trace) if trace is not None else None)
         L.check(st, "kd_loss_bwd")
+
+    def backward_logits(self, d_logits: Optional[torch.Tensor], grad_loss: Optional[torch.Tensor] = None,
+                        accumulate: bool = False, trace: Optional[L.KdTrace] = None) -> None:
+        """Gradient to given student logits (student and teacher logits both
+        given): d_logits (BT, vocab) in the logits dtype."""
+        if d_logits is not None and (d_logits.dtype != self.dtype or
+                                     tuple(d_logits.shape) != (self.n, self.v) or
+                                     not d_logits.is_contiguous()):
+            raise ValueError(f"d_logits must be contiguous {self.dtype} {(self.n, self.v)}")
+        st = self.lib.kd_loss_bwd_logits(
+            ctypes.byref(self.s), ctypes.byref(self.t), ctypes.byref(self.p), self.labels_ptr,
+            self.saved.data_ptr(), _ptr(grad_loss), _ptr(d_logits), int(accumulate), self._stream(),
+            ctypes.byref(trace) if trace is not None else None)
+        L.check(st, "kd_loss_bwd_logits")
 
     def backward_teacher(self, d_teacher_hidden: Optional[torch.Tensor],
                          d_teacher_weight: Optional[torch.Tensor],
@@ -436,6 +454,61 @@ class DistillationLoss(torch.nn.Module):
 
     def forward(self, student_hidden, weight, labels, teacher):
         return distillation_loss(student_hidden, weight, labels, teacher, **self.kwargs)
+
+
+class _LogitsKD(torch.autograd.Function):
+    """Loss from given student and teacher logits; differentiable in the student's."""
+
+    @staticmethod
+    def forward(ctx, student_logits, runner: Runner):
+        runner.forward()
+        ctx.runner = runner
+        return runner.loss.clone()
+
+    @staticmethod
+    def backward(ctx, g_loss):
+        r: Runner = ctx.runner
+        if not ctx.needs_input_grad[0]:
+            return None, None
+        d = torch.empty((r.n, r.v), dtype=r.dtype, device=r.device)
+        g = (g_loss if g_loss is not None else torch.ones((), device=r.device))
+        r.backward_logits(d, grad_loss=g.detach().to(torch.float32).contiguous())
+        return d, None
+
+
+class KDLoss(torch.nn.Module):
+    """Forward KL(P_T || P_S) x T^2 over the valid tokens, from student and
+    teacher logits both given (nemo kd_loss, KDLoss and KDLoss.forward).
+
+    Logits are [..., vocab] with labels [...]; rows whose label equals
+    ignore_index are excluded. With num_batch_labels the summed KL is divided
+    by it, else averaged over this batch's valid tokens. Differentiable in
+    student_logits; the teacher is detached. Arithmetic is always fp32
+    (``fp32_upcast`` is accepted for compatibility) and the whole vocabulary is
+    streamed once per pass, so ``chunk_size`` changes nothing here.
+    """
+
+    def __init__(self, ignore_index: int = -100, temperature: float = 1.0, fp32_upcast: bool = True,
+                 tp_group=None, chunk_size: int = 0):
+        super().__init__()
+        if tp_group is not None:
+            raise NotImplementedError("tensor-parallel vocabulary shards are not provided (one GPU)")
+        del fp32_upcast, chunk_size
+        self.ignore_index = ignore_index
+        self.temperature = temperature
+
+    def forward(self, student_logits, teacher_logits, labels, num_batch_labels=None):
+        v = student_logits.shape[-1]
+        if teacher_logits.shape != student_logits.shape:
+            raise ValueError("teacher_logits must have the student logits' shape")
+        z = student_logits.reshape(-1, v)
+        runner = Runner(student_logits=z.detach().contiguous(), teacher_kind="logits",
+                        teacher_logits=teacher_logits.detach().reshape(-1, v).to(z.dtype).contiguous(),
+                        labels=labels.reshape(-1).to(torch.int64).contiguous(),
+                        student_ce_weight=0.0, teacher_ce_weight=0.0, kl_weight=1.0,
+                        temperature=self.temperature, ignore_index=self.ignore_index,
+                        normalizer=float(num_batch_labels or 0), want_grads=False)
+        return _LogitsKD.apply(z, runner)
 
 
 def flash_ce_kd_loss(student_logits, teacher_hidden, teacher_lm_head_weight, labels, *,

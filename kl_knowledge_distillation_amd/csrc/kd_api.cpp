@@ -43,8 +43,10 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
     q.d = s->d;
   } else if (s->kind == KD_STUDENT_LOGITS) {
     if (!s->logits) return KD_ERR_NULL;
-    if (t->kind != KD_TEACHER_SEPARATE) return KD_ERR_UNSUPPORTED;
-    if (backward) return KD_ERR_UNSUPPORTED;  // the scorer is forward only (flash_kd)
+    if (t->kind != KD_TEACHER_SEPARATE && t->kind != KD_TEACHER_LOGITS) return KD_ERR_UNSUPPORTED;
+    // no hidden states or weight to differentiate (the scorer is forward only,
+    // flash_kd; given student logits take kd_loss_bwd_logits)
+    if (backward) return KD_ERR_UNSUPPORTED;
     if (((uintptr_t)s->logits & (s->dtype == KD_BF16 ? 1u : 3u)) != 0) return KD_ERR_ALIGN;
   } else {
     return KD_ERR_PARAM;
@@ -68,10 +70,9 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
       q.dt = t->d_t;
       break;
     case KD_TEACHER_LOGITS:
-      if (s->kind != KD_STUDENT_PROJECTION) return KD_ERR_UNSUPPORTED;
       if (!t->logits) return KD_ERR_NULL;
       if (((uintptr_t)t->logits & (s->dtype == KD_BF16 ? 1u : 3u)) != 0) return KD_ERR_ALIGN;
-      q.mode = kd::MODE_TLOGITS;
+      q.mode = (s->kind == KD_STUDENT_LOGITS) ? kd::MODE_BOTH : kd::MODE_TLOGITS;
       break;
     case KD_TEACHER_TOPK:
       if (s->kind != KD_STUDENT_PROJECTION) return KD_ERR_UNSUPPORTED;
@@ -146,7 +147,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   // so the per-token statistics are only live after the main loop; each
   // vocabulary tile leaves one record per token for the merge.
   q.n_ttiles = (int)ceil_div(q.n, kTile);
-  q.n_vtiles = (int)ceil_div(q.v, vt);
+  q.n_vtiles = (q.mode == kd::MODE_BOTH) ? 1 : (int)ceil_div(q.v, vt);  // row kernels: one record
   q.tps = 1;
   q.n_slices = q.n_vtiles;
   // Backward chunk: a whole number of fused vocabulary tiles.
@@ -260,6 +261,22 @@ kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params*
                           accumulate ? 1 : 0, workspace, static_cast<hipStream_t>(stream), trace);
 }
 
+kd_status kd_loss_bwd_logits(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                             const int64_t* labels, const void* saved, const float* grad_loss,
+                             void* d_logits, int32_t accumulate, void* stream, kd_trace* trace) {
+  Plan q;
+  const kd_status st = plan_call(s, t, p, labels, true, false, &q);
+  if (st != KD_OK) return st;
+  if (q.mode != kd::MODE_BOTH || p->reduction == KD_REDUCE_NONE) return KD_ERR_UNSUPPORTED;
+  if (!saved) return KD_ERR_WORKSPACE;
+  if (!aligned16(saved)) return KD_ERR_ALIGN;
+  if (grad_loss && ((uintptr_t)grad_loss & 3u)) return KD_ERR_ALIGN;
+  if (!d_logits) return KD_OK;
+  if (((uintptr_t)d_logits & (s->dtype == KD_BF16 ? 1u : 3u)) != 0) return KD_ERR_ALIGN;
+  return kd::run_backward_logits(q, tensors_of(s, t, labels), saved, grad_loss, d_logits,
+                                 accumulate ? 1 : 0, static_cast<hipStream_t>(stream), trace);
+}
+
 kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd_params* p,
                               const int64_t* labels, const void* saved, const float* grad_loss,
                               float* d_teacher_hidden, float* d_teacher_weight, int32_t accumulate,
@@ -326,12 +343,13 @@ kd_status kd_events_create(void** events, int32_t n) {
 
 kd_status kd_events_destroy(void** events, int32_t n) {
   if (!events || n < 0) return KD_ERR_NULL;
+  kd_status st = KD_OK;
   for (int32_t i = 0; i < n; ++i)
     if (events[i]) {
-      hipEventDestroy(static_cast<hipEvent_t>(events[i]));
+      if (hipEventDestroy(static_cast<hipEvent_t>(events[i])) != hipSuccess) st = KD_ERR_HIP;
       events[i] = nullptr;
     }
-  return KD_OK;
+  return st;
 }
 
 kd_status kd_event_elapsed_ms(void* start, void* stop, float* ms) {

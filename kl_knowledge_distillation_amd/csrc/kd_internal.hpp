@@ -14,7 +14,8 @@ namespace kd {
 // student logits with a separate teacher (forward only); TLOGITS: projection
 // student with given dense teacher logits.
 enum Mode { MODE_TIED = 0, MODE_SEPARATE = 1, MODE_TOPK = 2, MODE_LOGITS = 3, MODE_TLOGITS = 4,
-            MODE_TCE = 5 /* backward only: the teacher tile and its CE gradient */ };
+            MODE_TCE = 5 /* backward only: the teacher tile and its CE gradient */,
+            MODE_BOTH = 6 /* student and teacher logits both given: row kernels, no GEMM */ };
 
 // Number of fp32 fields of one per-(token, vocabulary tile) record.
 constexpr int kRecFields = 10;
@@ -82,6 +83,10 @@ kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, vo
 kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
                        float* d_hidden, float* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace);
+// The backward to given student logits (student and teacher logits given).
+kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved,
+                              const float* grad_loss, void* d_logits, int accumulate,
+                              hipStream_t stream, kd_trace* trace);
 // The teacher-CE backward: d_hidden / d_weight are the teacher's.
 kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,
                                const float* grad_loss, float* d_hidden, float* d_weight,

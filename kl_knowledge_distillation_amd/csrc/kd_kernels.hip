@@ -610,13 +610,13 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     const bool valid = a.labels == nullptr || (y != a.ignore && in_range);
     flag = valid ? 1.f : ((y != a.ignore && !in_range) ? 2.f : 0.f);
     if (a.labels != nullptr && valid) {
-      if constexpr (MODE == MODE_LOGITS) {
+      if constexpr (MODE == MODE_LOGITS || MODE == MODE_BOTH) {
         f0 = to_f32(static_cast<const T*>(a.logits)[i * a.v + y]);
       } else {
         f0 = wave_dot<T>(hs + i * a.d, W + y * a.d, a.d, lane);
       }
       if (a.want_teacher) {
-        if constexpr (MODE == MODE_TLOGITS) {
+        if constexpr (MODE == MODE_TLOGITS || MODE == MODE_BOTH) {
           f1 = to_f32(static_cast<const T*>(a.tlogits)[i * a.v + y]);
         } else {
           const T* ht = static_cast<const T*>(a.ht);
@@ -631,6 +631,214 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     a.prep[a.n + i] = f1;
     a.prep[2 * a.n + i] = f2;
     a.prep[3 * a.n + i] = flag;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Student and teacher logits both given (nemo kd_loss, KDLoss.forward): no
+// projection, so the path is HBM-bound and runs as row kernels, one wave per
+// token row streaming both [n x v] matrices once, with 16-byte loads.
+// ---------------------------------------------------------------------------
+
+constexpr int kRowUnroll = 4;  // 16-byte chunks per lane in flight per matrix
+
+struct RowArgs {
+  const void* zl;       // student logits [n, v]
+  const void* tl;       // teacher logits [n, v]
+  int64_t n, v;
+  float cT, cTt, rho;   // log2(e) / T_s, log2(e) / T_t, T_s / T_t
+  int need_zT, need_t1, rev;
+  int sqz;              // T_s == 2: the T = 1 student sum from the square of the T one
+  int vec;              // rows are 16-byte aligned: chunk loads, else element loads
+  float* rec;           // [kRecFields][1][n] (forward)
+  // backward
+  const int64_t* labels;
+  int64_t ignore;
+  const float* saved;
+  const float* grad;
+  float ws, wkl, T;
+  int kl, accumulate;
+  void* dz;             // [n, v] student dtype
+};
+
+// Elements [e0, e0 + PC) of a row into x (past v: -inf, so that they weigh 0).
+template <typename T>
+__device__ __forceinline__ void row_chunk(const T* row, int64_t e0, int64_t v, bool vec,
+                                          float (&x)[Elem<T>::kPerChunk]) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  if (vec && e0 + PC <= v) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + e0);
+    const T* p = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int j = 0; j < PC; ++j) x[j] = to_f32(p[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < PC; ++j) x[j] = (e0 + j < v) ? to_f32(row[e0 + j]) : -INFINITY;
+  }
+}
+
+// Running statistics of one lane: maxima of z and t (raw units) and the sums
+// of record fields 1, 3, 5, 6, 8, 9 against them.
+struct RowRun {
+  float mz, mt;
+  float sz1, szT, ar, stT, at, st1;
+};
+
+__device__ __forceinline__ float run_scale(float m_old, float m_new, float c) {
+  // the sums against m_old re-expressed against m_new >= m_old (0 while empty)
+  return (m_old == m_new) ? 1.f : ((m_old == -INFINITY) ? 0.f : exp2_fast((m_old - m_new) * c));
+}
+
+__device__ __forceinline__ void row_fold(RowRun& r, const RowRun& o, float cT, float cTt) {
+  const float mz = fmaxf(r.mz, o.mz), mt = fmaxf(r.mt, o.mt);
+  const float a1 = run_scale(r.mz, mz, kLog2e), b1 = run_scale(o.mz, mz, kLog2e);
+  const float aT = run_scale(r.mz, mz, cT), bT = run_scale(o.mz, mz, cT);
+  const float c1 = run_scale(r.mt, mt, kLog2e), d1 = run_scale(o.mt, mt, kLog2e);
+  const float cTs = run_scale(r.mt, mt, cTt), dTs = run_scale(o.mt, mt, cTt);
+  r.sz1 = r.sz1 * a1 + o.sz1 * b1;
+  r.szT = r.szT * aT + o.szT * bT;
+  r.ar = r.ar * aT + o.ar * bT;
+  r.stT = r.stT * cTs + o.stT * dTs;
+  r.at = r.at * cTs + o.at * dTs;
+  r.st1 = r.st1 * c1 + o.st1 * d1;
+  r.mz = mz;
+  r.mt = mt;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rowstats_kernel(RowArgs a) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (i >= a.n) return;
+  const T* zr = static_cast<const T*>(a.zl) + i * a.v;
+  const T* tr = static_cast<const T*>(a.tl) + i * a.v;
+  RowRun r{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // kRowUnroll chunks per lane per step, all loads issued before any use
+  for (int64_t s0 = (int64_t)lane * PC; s0 < a.v; s0 += kRowUnroll * 64 * PC) {
+    float z[kRowUnroll][PC], t[kRowUnroll][PC];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      row_chunk<T>(zr, s0 + u * 64 * PC, a.v, a.vec != 0, z[u]);
+      row_chunk<T>(tr, s0 + u * 64 * PC, a.v, a.vec != 0, t[u]);
+    }
+    RowRun c{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+      for (int j = 0; j < PC; ++j) {
+        c.mz = fmaxf(c.mz, z[u][j]);
+        c.mt = fmaxf(c.mt, t[u][j]);
+      }
+    // this step's sums against its own maxima, then folded into the run
+    const float bz = (c.mz == -INFINITY) ? 0.f : c.mz, bt = (c.mt == -INFINITY) ? 0.f : c.mt;
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+      for (int j = 0; j < PC; ++j) {
+        const float zz = z[u][j], tt = t[u][j];
+        const float ezT = exp2_fast((zz - bz) * a.cT);
+        const float ez1 = a.sqz ? ezT * ezT : exp2_fast((zz - bz) * kLog2e);
+        const float etT = exp2_fast((tt - bt) * a.cTt);
+        c.sz1 += ez1;
+        c.szT += ezT;
+        c.stT += etT;
+        c.at = (etT > 0.f) ? fmaf(etT, fmaf(tt, a.rho, -zz), c.at) : c.at;
+        if (a.rev) c.ar = (ezT > 0.f) ? fmaf(ezT, fmaf(tt, -a.rho, zz), c.ar) : c.ar;
+        if (a.need_t1) c.st1 += exp2_fast((tt - bt) * kLog2e);
+      }
+    row_fold(r, c, a.cT, a.cTt);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    RowRun o;
+    o.mz = __shfl_xor(r.mz, off);
+    o.mt = __shfl_xor(r.mt, off);
+    o.sz1 = __shfl_xor(r.sz1, off);
+    o.szT = __shfl_xor(r.szT, off);
+    o.ar = __shfl_xor(r.ar, off);
+    o.stT = __shfl_xor(r.stT, off);
+    o.at = __shfl_xor(r.at, off);
+    o.st1 = __shfl_xor(r.st1, off);
+    row_fold(r, o, a.cT, a.cTt);
+  }
+  if (lane == 0) {
+    float* p = a.rec + i;
+    const int64_t n = a.n;
+    p[0 * n] = r.mz * kLog2e;  p[1 * n] = r.sz1;
+    p[2 * n] = r.mz * a.cT;    p[3 * n] = r.szT;
+    p[4 * n] = r.mt * a.cTt;   p[5 * n] = r.stT;
+    p[6 * n] = r.at;
+    p[7 * n] = r.mt * kLog2e;  p[8 * n] = r.st1;
+    p[9 * n] = r.ar;
+  }
+}
+
+// d loss / d z for given student logits: the dz formula of bwd_dz, row by row,
+// stored in the logits dtype (or added to it).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void logits_bwd_kernel(RowArgs a) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (i >= a.n) return;
+  const T* zr = static_cast<const T*>(a.zl) + i * a.v;
+  const T* tr = static_cast<const T*>(a.tl) + i * a.v;
+  T* out = static_cast<T*>(a.dz) + i * a.v;
+  const float4 sv = reinterpret_cast<const float4*>(a.saved)[i];
+  const float den = a.saved[4 * a.n];
+  const float g = a.grad ? *a.grad : 1.f;
+  const int64_t y = a.labels ? a.labels[i] : a.ignore;
+  const bool valid = a.labels == nullptr || (y != a.ignore && y >= 0 && y < a.v);
+  const float coef = valid ? g / den : 0.f;
+  const float cs = coef * a.ws, ck = coef * a.wkl * a.T;
+  const float ckf = (a.kl != KD_KL_REVERSE) ? ck : 0.f, ckr = (a.kl != KD_KL_FORWARD) ? ck : 0.f;
+  const float L1 = sv.x * kLog2e, LzT = sv.y * kLog2e, LtT = sv.z * kLog2e;
+  const float rev0 = sv.z - sv.y - sv.w, invT = 1.f / a.T;
+  for (int64_t s0 = (int64_t)lane * PC; s0 < a.v; s0 += kRowUnroll * 64 * PC) {
+    float zs[kRowUnroll][PC], ts[kRowUnroll][PC];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      row_chunk<T>(zr, s0 + u * 64 * PC, a.v, a.vec != 0, zs[u]);
+      row_chunk<T>(tr, s0 + u * 64 * PC, a.v, a.vec != 0, ts[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t e0 = s0 + u * 64 * PC;
+    const float* z = zs[u];
+    const float* t = ts[u];
+    float o[PC];
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+      const float p1 = exp2_fast(fmaf(z[j], kLog2e, -L1));
+      const float pz = a.need_zT ? exp2_fast(fmaf(z[j], a.cT, -LzT)) : p1;
+      const float pt = exp2_fast(fmaf(t[j], a.cTt, -LtT));
+      float dv = cs * (p1 - (e0 + j == y ? 1.f : 0.f));
+      dv = fmaf(ckf, pz - pt, dv);
+      if (ckr != 0.f) dv = fmaf(ckr * pz, fmaf(fmaf(t[j], -a.rho, z[j]), invT, rev0), dv);
+      o[j] = dv;
+    }
+    if (a.vec && e0 + PC <= a.v) {  // one 16-byte store (and load, to accumulate)
+      uint4 u = a.accumulate ? *reinterpret_cast<const uint4*>(out + e0) : make_uint4(0u, 0u, 0u, 0u);
+      T* q = reinterpret_cast<T*>(&u);
+#pragma unroll
+      for (int j = 0; j < PC; ++j) {
+        const float prev = a.accumulate ? to_f32(q[j]) : 0.f;
+        if constexpr (sizeof(T) == 2) q[j] = bf16_rne(prev + o[j]);
+        else q[j] = prev + o[j];
+      }
+      *reinterpret_cast<uint4*>(out + e0) = u;
+    } else {
+#pragma unroll
+      for (int j = 0; j < PC; ++j) {
+        if (e0 + j < a.v) {
+          const float prev = a.accumulate ? to_f32(out[e0 + j]) : 0.f;
+          if constexpr (sizeof(T) == 2) out[e0 + j] = bf16_rne(prev + o[j]);
+          else out[e0 + j] = prev + o[j];
+        }
+      }
+    }
+    }
   }
 }
 
@@ -1316,6 +1524,13 @@ struct Launch {
     if (st_ != KD_OK) return st_;     \
   } while (0)
 
+// Row kernels load 16-byte chunks when every row start of both matrices is
+// 16-byte aligned.
+template <typename T>
+int row_vec(const void* a, const void* b, int64_t v) {
+  return ((v * (int64_t)sizeof(T)) % 16 == 0 && (uintptr_t)a % 16 == 0 && (uintptr_t)b % 16 == 0) ? 1 : 0;
+}
+
 // How a given [n x v] logits matrix is read: 2 = staged through LDS with
 // 16-byte buffer loads (pipelined bf16 tiles: v a multiple of 8, 16-byte
 // aligned, v up to 2^23), 1 = a lane's four consecutive elements as one vector (v a multiple
@@ -1374,6 +1589,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
       case MODE_TOPK: prep_kernel<T, MODE_TOPK><<<pgrid, kThreads, 0, stream>>>(pa); break;
       case MODE_LOGITS: prep_kernel<T, MODE_LOGITS><<<pgrid, kThreads, 0, stream>>>(pa); break;
       case MODE_TLOGITS: prep_kernel<T, MODE_TLOGITS><<<pgrid, kThreads, 0, stream>>>(pa); break;
+      case MODE_BOTH: prep_kernel<T, MODE_BOTH><<<pgrid, kThreads, 0, stream>>>(pa); break;
       default: prep_kernel<T, MODE_TIED><<<pgrid, kThreads, 0, stream>>>(pa); break;
     }
   }));
@@ -1390,6 +1606,25 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
              p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v),
              (p.T == 2.f && p.need_zT) ? 1 : 0, rec, cp.nv};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
+  if (p.mode == MODE_BOTH) {
+    RowArgs ra{};
+    ra.zl = x.logits;
+    ra.tl = x.tlogits;
+    ra.n = p.n;
+    ra.v = p.v;
+    ra.cT = kLog2e / p.T;
+    ra.cTt = kLog2e / p.Tt;
+    ra.rho = p.T / p.Tt;
+    ra.need_zT = p.need_zT;
+    ra.need_t1 = need_t1;
+    ra.rev = p.kl != KD_KL_FORWARD;
+    ra.sqz = (p.T == 2.f && p.need_zT) ? 1 : 0;
+    ra.vec = row_vec<T>(x.logits, x.tlogits, p.v);
+    ra.rec = rec;
+    KD_TRY(L.run(KD_KERNEL_FWD, [&] {
+      rowstats_kernel<T><<<dim3((unsigned)((p.n + 3) / 4)), kThreads, 0, stream>>>(ra);
+    }));
+  } else
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
     switch (p.mode) {
       case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
@@ -1636,6 +1871,38 @@ kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const
                        hipStream_t stream, kd_trace* trace) {
   return backward_any(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace, stream,
                       trace, false);
+}
+
+kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved,
+                              const float* grad_loss, void* d_logits, int accumulate,
+                              hipStream_t stream, kd_trace* trace) {
+  Launch L{stream, trace};
+  RowArgs ra{};
+  ra.zl = x.logits;
+  ra.tl = x.tlogits;
+  ra.n = p.n;
+  ra.v = p.v;
+  ra.cT = kLog2e / p.T;
+  ra.cTt = kLog2e / p.Tt;
+  ra.rho = p.T / p.Tt;
+  ra.need_zT = p.need_zT;
+  ra.labels = x.labels;
+  ra.ignore = p.ignore;
+  ra.saved = static_cast<const float*>(saved);
+  ra.grad = grad_loss;
+  ra.ws = p.ws;
+  ra.wkl = p.wkl;
+  ra.T = p.T;
+  ra.kl = p.kl;
+  ra.accumulate = accumulate;
+  ra.dz = d_logits;
+  const dim3 grid((unsigned)((p.n + 3) / 4));
+  if (p.dtype == KD_BF16) {
+    ra.vec = row_vec<bf16_t>(x.logits, x.tlogits, p.v) && row_vec<bf16_t>(d_logits, d_logits, p.v);
+    return L.run(KD_KERNEL_BWD_DZ, [&] { logits_bwd_kernel<bf16_t><<<grid, kThreads, 0, stream>>>(ra); });
+  }
+  ra.vec = row_vec<float>(x.logits, x.tlogits, p.v) && row_vec<float>(d_logits, d_logits, p.v);
+  return L.run(KD_KERNEL_BWD_DZ, [&] { logits_bwd_kernel<float><<<grid, kThreads, 0, stream>>>(ra); });
 }
 
 kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,

@@ -18,6 +18,8 @@ Workloads (shapes from the pages, distributions as stated):
                         --topk 100, batch 1)
   scorer_bf16           N=65536, D_t=4096, V=248320, student logits given,
                         forward only (flash_kd: vocab ~248k)
+  kdloss_logits_bf16    N=4096, V=32000, student and teacher logits both given,
+                        N(0, 4) each, T=2, KL only (nemo kd_loss, KDLoss.forward)
   quickstart_logits_bf16  the quickstart shape with a cached dense teacher
                         (orda-kernel, Teacher descriptors: PrecomputedTeacher
                         logits) of N(0,1) logits, the per-entry variance of
@@ -91,6 +93,10 @@ WORKLOADS: Dict[str, Workload] = {
         "scorer_bf16", n=65536, d=0, d_t=4096, v=248320, teacher="separate",
         student="logits", temperature=1.0, student_ce_weight=1.0, kl_weight=1.0,
         ignore_index=-1, ignore_frac=0.03, logits_var=2.0, forward_only=True),
+    "kdloss_logits_bf16": Workload(
+        "kdloss_logits_bf16", n=4096, d=0, v=32000, teacher="logits", student="logits",
+        temperature=2.0, student_ce_weight=0.0, kl_weight=1.0, ignore_frac=0.05,
+        logits_var=4.0, teacher_logits_var=4.0, forward_only=True),
     "quickstart_logits_bf16": Workload(
         "quickstart_logits_bf16", n=4096, d=2048, v=32000, teacher="logits",
         temperature=2.0, teacher_temperature=1.5, student_ce_weight=1.0, kl_weight=1.0,

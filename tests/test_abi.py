@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    for must in ("kd_loss_fwd", "kd_loss_bwd", "kd_loss_bwd_teacher", "kd_workspace_bytes", "kd_saved_bytes",
+    for must in ("kd_loss_fwd", "kd_loss_bwd", "kd_loss_bwd_teacher", "kd_loss_bwd_logits",
+                 "kd_workspace_bytes", "kd_saved_bytes",
                  "kd_read_status", "kd_status_string", "kd_device_supported"):
         assert must in names
 
@@ -244,6 +245,32 @@ def test_null_descriptors():
     assert lib.kd_read_status(None, None, None) == L.KD_ERR_NULL
 
 
+def test_both_logits_descriptors():
+    """Student and teacher logits both given: forward planned (one record per
+    row); the hidden/weight backward is not available, kd_loss_bwd_logits is."""
+    s = L.KdStudent(L.KD_STUDENT_LOGITS, L.KD_BF16, 300, 0, 3000, None, None, FAKE)
+    t = L.KdTeacher()
+    t.kind, t.logits = L.KD_TEACHER_LOGITS, FAKE
+    _, _, p = _desc()
+    p.student_ce_weight = 0.0
+    st, fwd = _ws(s, t, p, 0)
+    assert st == L.KD_OK and fwd > 0
+    assert _ws(s, t, p, 1)[0] == L.KD_ERR_UNSUPPORTED
+    lib = L.load()
+    p.reduction = L.KD_REDUCE_NONE
+    st = lib.kd_loss_bwd_logits(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), FAKE, FAKE, None,
+                                FAKE, 0, None, None)
+    assert st == L.KD_ERR_UNSUPPORTED
+    s2, t2, p2 = _desc()
+    st = lib.kd_loss_bwd_logits(ctypes.byref(s2), ctypes.byref(t2), ctypes.byref(p2), FAKE, FAKE,
+                                None, FAKE, 0, None, None)
+    assert st == L.KD_ERR_UNSUPPORTED  # needs both logits
+    p.reduction = L.KD_REDUCE_MEAN
+    st = lib.kd_loss_bwd_logits(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), FAKE, FAKE, None,
+                                FAKE + 1, 0, None, None)
+    assert st == L.KD_ERR_ALIGN
+
+
 def test_teacher_logits_descriptor():
     """A dense teacher-logits descriptor plans like the others; it needs a
     projection student, and a teacher temperature of its own is accepted."""
@@ -255,7 +282,7 @@ def test_teacher_logits_descriptor():
     st, bwd = _ws(s, t, p, 1)
     assert st == L.KD_OK and bwd > 0
     s2 = L.KdStudent(L.KD_STUDENT_LOGITS, L.KD_BF16, 300, 0, 3000, None, None, FAKE)
-    assert _ws(s2, t, p, 0)[0] == L.KD_ERR_UNSUPPORTED
+    assert _ws(s2, t, p, 1)[0] == L.KD_ERR_UNSUPPORTED  # no hidden / weight backward
 
 
 def test_compaction_workspace():

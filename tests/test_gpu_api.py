@@ -188,3 +188,27 @@ def test_teacher_trained_through_autograd(kind):
     else:
         assert_grad(f64(W.grad), dWs, "bf16", "student dW")
         assert_grad(f64(wt.grad), dWt, "bf16", "teacher dW")
+
+
+def test_kdloss_given_logits_autograd():
+    """nemo-style KDLoss on [B, S, V] logits with num_batch_labels: the scalar
+    and the student-logit gradient against the oracle."""
+    w = WORKLOADS["kdloss_logits_bf16"].scaled(n=2 * 150, v=2048, ignore_frac=0.1)
+    x = make_inputs(w, "cuda", seed=18)
+    zl = x["student_logits"].reshape(2, 150, w.v).clone().requires_grad_(True)
+    tl = x["teacher_logits"].reshape(2, 150, w.v)
+    y = x["labels"].reshape(2, 150)
+    crit = api.KDLoss(ignore_index=w.ignore_index, temperature=2.0)
+    loss = crit(zl, tl, y, num_batch_labels=400)
+    (loss * 0.5).backward()
+    torch.cuda.synchronize()
+    s = O.Student(logits=f64(x["student_logits"]))
+    t = O.Teacher("logits", logits=f64(x["teacher_logits"]))
+    labels = to_np(x["labels"]).astype(np.int64)
+    p = O.Params(student_ce_weight=0.0, kl_weight=1.0, temperature=2.0, ignore_index=w.ignore_index,
+                 normalizer=400.0)
+    ref = O.forward(s, t, p, labels)
+    assert_scalar(float(loss.detach()), ref["loss"], "bf16", "KDLoss")
+    g = O.logit_grad(s, t, p, labels, np.arange(w.n), 400.0, grad_loss=0.5)
+    assert zl.grad.dtype == zl.dtype and zl.grad.shape == zl.shape
+    assert_grad(f64(zl.grad.reshape(w.n, w.v)), g, "bf16", "KDLoss d student logits")

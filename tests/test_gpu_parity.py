@@ -21,6 +21,7 @@ C3 = WORKLOADS["separate_bf16"]
 C4 = WORKLOADS["topk_bf16"]
 C5 = WORKLOADS["scorer_bf16"]
 C6 = WORKLOADS["quickstart_logits_bf16"]
+C7 = WORKLOADS["kdloss_logits_bf16"]
 
 SMALL = {
     "tiny_fp32": C1,
@@ -328,6 +329,40 @@ def test_teacher_gradient_zero_without_teacher_ce():
     r.backward_teacher(dht, dwt)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dht).item() == 0 and torch.count_nonzero(dwt).item() == 0
+
+
+BOTH_LOGITS_CASES = {
+    "bf16_vec": C7.scaled(n=300, v=3000),
+    "bf16_ragged_rows": C7.scaled(n=130, v=1029, ignore_frac=0.2),
+    "fp32": C7.scaled(n=64, v=1024, dtype="fp32"),
+    "reverse_Tt": C7.scaled(n=200, v=2048, kl_divergence="reverse", teacher_temperature=1.3),
+    "jeffreys_ce": C7.scaled(n=200, v=2048, kl_divergence="jeffreys", student_ce_weight=0.5,
+                             teacher_ce_weight=0.25),
+    "neg_inf_T1": C7.scaled(n=260, v=2100, temperature=1.0, teacher_neg_inf_frac=0.3),
+}
+
+
+@pytest.mark.parametrize("name", list(BOTH_LOGITS_CASES))
+def test_both_logits_given(name):
+    """Student and teacher logits both given (row kernels): per-token terms and
+    loss, then the gradient to the student logits, against the oracle."""
+    w = BOTH_LOGITS_CASES[name]
+    full_parity(w, grads=False)
+    x = make_inputs(w, "cuda", seed=0)
+    r = make_runner(w, x, want_grads=False)
+    r.forward()
+    d = torch.empty((r.n, r.v), dtype=w.torch_dtype, device="cuda")
+    r.backward_logits(d)
+    torch.cuda.synchronize()
+    s, t, labels = oracle_problem(w, x)
+    p = params_of(w)
+    ref = O.forward(s, t, p, labels)
+    g = O.logit_grad(s, t, p, labels, np.arange(w.n), ref["den"])
+    assert_grad(to_np(d), g, w.dtype, f"{name} d student logits")
+    d2 = d.clone()
+    r.backward_logits(d2, accumulate=True)
+    torch.cuda.synchronize()
+    assert_grad(to_np(d2), 2 * g, w.dtype, f"{name} accumulated")
 
 
 def test_full_quickstart_logits_teacher_bf16():
