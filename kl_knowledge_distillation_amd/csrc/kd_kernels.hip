@@ -732,20 +732,25 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowArgs a) {
       }
     // this step's sums against its own maxima, then folded into the run
     const float bz = (c.mz == -INFINITY) ? 0.f : c.mz, bt = (c.mt == -INFINITY) ? 0.f : c.mt;
+    const float bzT = bz * a.cT, bz1 = bz * kLog2e, btT = bt * a.cTt, bt1 = bt * kLog2e;
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u)
 #pragma unroll
       for (int j = 0; j < PC; ++j) {
+        // a -inf logit (a zero probability, or past the row) has e = 0; in the
+        // forward cross difference it stands as -1e30, so that 0 times it stays 0
         const float zz = z[u][j], tt = t[u][j];
-        const float ezT = exp2_fast((zz - bz) * a.cT);
-        const float ez1 = a.sqz ? ezT * ezT : exp2_fast((zz - bz) * kLog2e);
-        const float etT = exp2_fast((tt - bt) * a.cTt);
+        const float zc = fmaxf(zz, -1e30f), tc = fmaxf(tt, -1e30f);
+        const float ezT = exp2_fast(fmaf(zz, a.cT, -bzT));
+        const float ez1 = a.sqz ? ezT * ezT : exp2_fast(fmaf(zz, kLog2e, -bz1));
+        const float etT = exp2_fast(fmaf(tt, a.cTt, -btT));
         c.sz1 += ez1;
         c.szT += ezT;
         c.stT += etT;
-        c.at = (etT > 0.f) ? fmaf(etT, fmaf(tt, a.rho, -zz), c.at) : c.at;
+        c.at = fmaf(etT, fmaf(tc, a.rho, -zc), c.at);
+        // reverse: a -inf teacher logit under student mass makes the KL +inf
         if (a.rev) c.ar = (ezT > 0.f) ? fmaf(ezT, fmaf(tt, -a.rho, zz), c.ar) : c.ar;
-        if (a.need_t1) c.st1 += exp2_fast((tt - bt) * kLog2e);
+        if (a.need_t1) c.st1 += exp2_fast(fmaf(tt, kLog2e, -bt1));
       }
     row_fold(r, c, a.cT, a.cTt);
   }

@@ -365,6 +365,18 @@ def test_both_logits_given(name):
     assert_grad(to_np(d2), 2 * g, w.dtype, f"{name} accumulated")
 
 
+def test_reverse_kl_infinite_for_zero_teacher_probability():
+    """Reverse KL with -inf teacher columns (reading R20): +inf on every row,
+    given logits and dense-teacher paths alike."""
+    for w in (C7.scaled(n=130, v=1024, kl_divergence="reverse", teacher_neg_inf_frac=0.2),
+              C6.scaled(n=130, d=256, v=1024, kl_divergence="reverse", teacher_neg_inf_frac=0.2)):
+        x = make_inputs(w, "cuda", seed=5)
+        r = make_runner(w, x, want_grads=False)
+        r.forward()
+        torch.cuda.synchronize()
+        assert torch.isposinf(r.kl).all(), w.name
+
+
 def test_full_quickstart_logits_teacher_bf16():
     """Quickstart shape with a dense cached teacher (N=4096, D=2048, V=32000,
     T_s = 2, T_t = 1.5), every output."""
