@@ -826,11 +826,16 @@ __global__ __launch_bounds__(kThreads) void logits_bwd_kernel(RowArgs a) {
     if (a.vec && e0 + PC <= a.v) {  // one 16-byte store (and load, to accumulate)
       uint4 u = a.accumulate ? *reinterpret_cast<const uint4*>(out + e0) : make_uint4(0u, 0u, 0u, 0u);
       T* q = reinterpret_cast<T*>(&u);
+      float sum[PC];
 #pragma unroll
-      for (int j = 0; j < PC; ++j) {
-        const float prev = a.accumulate ? to_f32(q[j]) : 0.f;
-        if constexpr (sizeof(T) == 2) q[j] = bf16_rne(prev + o[j]);
-        else q[j] = prev + o[j];
+      for (int j = 0; j < PC; ++j) sum[j] = (a.accumulate ? to_f32(q[j]) : 0.f) + o[j];
+      if constexpr (sizeof(T) == 2) {
+        uint32_t* w32 = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+        for (int j = 0; j < PC / 2; ++j) w32[j] = bf16x2_rne(sum[2 * j], sum[2 * j + 1]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < PC; ++j) q[j] = sum[j];
       }
       *reinterpret_cast<uint4*>(out + e0) = u;
     } else {
@@ -1074,8 +1079,8 @@ __device__ __forceinline__ void store4<float>(float* p, float x0, float x1, floa
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, float x2, float x3) {
   uint2 u;
-  u.x = (uint32_t)bf16_rne(x0) | ((uint32_t)bf16_rne(x1) << 16);
-  u.y = (uint32_t)bf16_rne(x2) | ((uint32_t)bf16_rne(x3) << 16);
+  u.x = bf16x2_rne(x0, x1);
+  u.y = bf16x2_rne(x2, x3);
   *reinterpret_cast<uint2*>(p) = u;
 }
 
