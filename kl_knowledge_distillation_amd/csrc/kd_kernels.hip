@@ -22,6 +22,7 @@
 //   scatter   top-K only: subtract (g/den) w_kl p at the cached indices.
 //   gemm_dw   dW[chunk] = dz^T H_s       (K = n)
 //   gemm_dh   dH += dz W[chunk]          (K = chunk)
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -1144,6 +1145,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   // so the forward-KL epilogue carries no extra arithmetic.
   // kSq (T_s = 2): e = 2^(z log2(e)/2 - L1/2) gives softmax(z) = e^2 and
   // softmax(z/2) = e 2^(L1/2 - LzT): one exponential of z per element, not two.
+  // Vocabulary row of register (mb, r) is v0 + rb + 16 mb + r: the label test
+  // and the vocabulary bound become 32-bit compares against constants.
+  const int rb = acc_row(wm, 0, 0, lane);
+  const int lim = (int)min(a.v - v0 - rb, (int64_t)1 << 30);  // rows k >= lim are past v
   auto epilogue = [&](auto rev_tag, auto sq_tag) {
   constexpr bool kRev = decltype(rev_tag)::value;
   constexpr bool kSq = decltype(sq_tag)::value;
@@ -1166,7 +1171,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
       y = a.labels[orig];
       valid = y != a.ignore && y >= 0 && y < a.v;
     }
+    // coef = 0 zeroes every term of a row that is not valid (all are finite)
     const float coef = valid ? g / den : 0.f;
+    const int yl = valid ? (int)(y - v0 - rb) : INT_MIN;  // the label's register index
     const float cs = coef * (MODE == MODE_TCE ? a.wtce : a.ws);  // student (teacher) CE
     const float ck = coef * a.wkl * a.T;     // T^2 KL -> T (P_S - P_T)
     const float cm = coef * a.wkl * mass;    // top-K: M softmax(z)
@@ -1183,7 +1190,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
       float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t vv = v0 + acc_row(wm, mb, r, lane);
+        const int k = mb * 16 + r;
         const float zz = z[mb][nb][r];
         float p1, pz;
         if constexpr (kSq) {
@@ -1198,15 +1205,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
         if (MODE == MODE_TOPK) {
           dv = cm * p1;
         } else if (MODE == MODE_TCE) {
-          dv = cs * (p1 - (vv == y ? 1.f : 0.f));
+          dv = cs * (p1 - (yl == k ? 1.f : 0.f));
         } else {
-          dv = cs * (p1 - (vv == y ? 1.f : 0.f));
+          dv = cs * (p1 - (yl == k ? 1.f : 0.f));
           const float tt = tl[mb][nb][r];
           const float pt = exp2_fast(fmaf(tt, a.cTt, -LtT));
           dv = fmaf(ckf, pz - pt, dv);
           if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(fmaf(tt, -a.rho, zz), invT, rev0), dv);
         }
-        o[r] = (vv < a.v && valid) ? dv : 0.f;
+        o[r] = (k < lim) ? dv : 0.f;
       }
       store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
     }
