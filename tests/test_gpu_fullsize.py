@@ -168,3 +168,58 @@ def test_fullsize_quickstart_dw_identities():
     r.backward(dh, dw)
     torch.cuda.synchronize()
     check_dw_identities(r, x, dh, dw, w.dtype)
+
+
+def test_fullsize_given_logits_kdloss():
+    """Student and teacher logits both given at the quickstart size (N=4096,
+    V=32000): every per-token KL, the loss and the whole gradient to the student
+    logits against the oracle (it fits: 4096 x 32000 float64 per side)."""
+    w = WORKLOADS["kdloss_logits_bf16"]
+    say(f"[fullsize] {w.name}")
+    x = make_inputs(w, "cuda", seed=0)
+    r = make_runner(w, x, want_grads=False)
+    r.forward()
+    d = torch.empty((r.n, r.v), dtype=w.torch_dtype, device="cuda")
+    r.backward_logits(d)
+    torch.cuda.synchronize()
+    s = O.Student(logits=f64_all(x["student_logits"]))
+    t = O.Teacher("logits", logits=f64_all(x["teacher_logits"]))
+    labels = to_np(x["labels"]).astype(np.int64)
+    p = params_of(w)
+    ref = O.forward(s, t, p, labels)
+    assert_tokens(to_np(r.kl), ref["kl"], w.dtype, "given-logits kl")
+    assert_scalar(float(r.loss), ref["loss"], w.dtype, "given-logits loss")
+    g = O.logit_grad(s, t, p, labels, np.arange(w.n), ref["den"])
+    assert_grad(to_np(d), g, w.dtype, "given-logits d student logits")
+
+
+def test_fullsize_compacted_quickstart():
+    """The quickstart problem with 40% ignored labels and compaction: loss,
+    valid rows' terms and dH against the oracle on sampled rows, dW through
+    the identities."""
+    w = WORKLOADS["quickstart_tied_bf16"].scaled(ignore_frac=0.4, compact_valid=True)
+    run_fullsize_compact(w)
+
+
+def run_fullsize_compact(w):
+    say(f"[fullsize] {w.name} compacted, ignored {w.ignore_frac}")
+    x = make_inputs(w, "cuda", seed=0)
+    r = make_runner(w, x)
+    r.forward()
+    dh = torch.empty((r.n, r.d), dtype=torch.float32, device="cuda")
+    dw = torch.empty((r.v, r.d), dtype=torch.float32, device="cuda")
+    r.backward(dh, dw)
+    torch.cuda.synchronize()
+    labels_np = to_np(x["labels"]).astype(np.int64)
+    kl = to_np(r.kl).astype(np.float64)
+    sce = to_np(r.student_ce).astype(np.float64)
+    check_loss_consistency(r, w, labels_np, sce, np.zeros_like(sce), kl)
+    rows = sample_rows(w.n, labels_np, w.ignore_index)
+    s, t = oracle_subset(w, x, rows)
+    p = params_of(w)
+    ref = O.per_token(s, t, p, labels_np[rows])
+    assert_tokens(kl[rows], ref["kl"], w.dtype, "compacted kl (sampled rows)")
+    den = O.denominator(p, int(O.valid_mask(labels_np, w.v, w.ignore_index).sum()))
+    ref_dh = O.backward_rows(s, t, p, labels_np[rows], np.arange(len(rows)), den)
+    assert_grad(f64_rows(dh, rows), ref_dh, w.dtype, "compacted dH (sampled rows)")
+    check_dw_identities(r, x, dh, dw, w.dtype)
