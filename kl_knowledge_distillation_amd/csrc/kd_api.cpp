@@ -147,7 +147,16 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   // so the per-token statistics are only live after the main loop; each
   // vocabulary tile leaves one record per token for the merge.
   q.n_ttiles = (int)ceil_div(q.n, kTile);
-  q.n_vtiles = (q.mode == kd::MODE_BOTH) ? 1 : (int)ceil_div(q.v, vt);  // row kernels: one record
+  q.n_vtiles = (int)ceil_div(q.v, vt);
+  if (q.mode == kd::MODE_BOTH) {
+    // Row kernels: each row split into slices of whole steps, enough of them
+    // that the launch has about kRowWaves waves; one record per slice.
+    const int64_t step = kd::row_step_elems(q.dtype);
+    const int64_t steps = ceil_div(q.v, step);
+    const int64_t want = std::min<int64_t>(steps, std::max<int64_t>(1, ceil_div(kd::kRowWaves, q.n)));
+    q.row_slice = ceil_div(steps, want) * step;
+    q.n_vtiles = (int)ceil_div(q.v, q.row_slice);
+  }
   q.tps = 1;
   q.n_slices = q.n_vtiles;
   // Backward chunk: a whole number of fused vocabulary tiles.

@@ -63,6 +63,15 @@ __device__ __forceinline__ bf16_t bf16_rne(float f) { return (bf16_t)(bf16x2_rne
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte load of data streamed once, marked nontemporal so the caches do
+// not keep it in place of data that is reused. (Nontemporal stores of the
+// given-logits gradient measured slower than plain ones, so stores stay plain.)
+typedef uint32_t u32x4_hw __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const u32x4_hw v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_hw*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // The dispatcher hands workgroup b to XCD b % 8. Remap so that each XCD owns a
 // contiguous range of tile indices: neighbouring tiles then share its L2.
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {

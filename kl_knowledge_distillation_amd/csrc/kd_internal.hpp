@@ -29,6 +29,19 @@ constexpr size_t kNvOffset = 8;
 // `saved`: [n] x 16 bytes of row statistics, a 64-byte header at 16 n, then
 // [n] fp32 lse(t) at T = 1 (the teacher-CE backward) at 16 n + 64.
 constexpr size_t kSavedHeaderBytes = 64;
+// Given-logits row kernels: one wave per (row, slice of the row); each lane
+// takes kRowUnroll 16-byte chunks of each matrix per step, and a launch aims
+// at about kRowWaves waves (8 per SIMD over 256 CUs, twice over).
+#ifndef KD_ROW_UNROLL
+#define KD_ROW_UNROLL 2
+#endif
+#ifndef KD_ROW_WAVES
+#define KD_ROW_WAVES 16384
+#endif
+constexpr int kRowUnroll = KD_ROW_UNROLL;
+constexpr int64_t kRowWaves = KD_ROW_WAVES;
+// Elements of one row kernel step of a wave (64 lanes x kRowUnroll chunks).
+constexpr int64_t row_step_elems(int dtype) { return kRowUnroll * 64 * (dtype == KD_BF16 ? 8 : 4); }
 
 struct Plan {
   int mode = 0;
@@ -48,6 +61,7 @@ struct Plan {
   int pipe = 0;       // bf16 with hidden sizes multiple of 32: 256-row pipelined tiles
   int vt_rows = 128;  // vocabulary rows per fused tile
   int n_ttiles = 0, n_vtiles = 0, tps = 1, n_slices = 0;  // forward grid
+  int64_t row_slice = 0;  // row kernels: elements per slice (a whole number of steps)
   int64_t chunk = 0;  // backward vocabulary chunk (multiple of the fused tile rows)
   int64_t dz_rows = 0;  // rows of the logit-gradient slab: n rounded up to the token tile
   int n_chunks = 0;

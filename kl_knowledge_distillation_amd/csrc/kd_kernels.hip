@@ -304,7 +304,7 @@ __device__ __forceinline__ void given_tile_copy(const bf16_t* L, int64_t n, int6
     const int c = (lane & 31) ^ (tr & 15);
     const uint32_t voff = (uint32_t)h * row_bytes + (uint32_t)c * 16u;
     const uint32_t soff = (uint32_t)(2 * j) * row_bytes + (uint32_t)(v0 * 2);
-    buffer_copy(r, img + j * 1024, voff, soff);
+    buffer_copy_stream(r, img + j * 1024, voff, soff);
   }
 }
 
@@ -637,21 +637,20 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
 
 // ---------------------------------------------------------------------------
 // Student and teacher logits both given (nemo kd_loss, KDLoss.forward): no
-// projection, so the path is HBM-bound and runs as row kernels, one wave per
-// token row streaming both [n x v] matrices once, with 16-byte loads.
+// projection, so the path is HBM-bound and runs as row kernels: one wave per
+// slice of a token row streams that part of both [n x v] matrices once, with
+// 16-byte loads; each slice leaves one record for the merge.
 // ---------------------------------------------------------------------------
-
-constexpr int kRowUnroll = 4;  // 16-byte chunks per lane in flight per matrix
 
 struct RowArgs {
   const void* zl;       // student logits [n, v]
   const void* tl;       // teacher logits [n, v]
   int64_t n, v;
+  int64_t slice;        // elements per slice of a row, a whole number of steps
+  int n_slices;         // slices per row (one wave each)
   float cT, cTt, rho;   // log2(e) / T_s, log2(e) / T_t, T_s / T_t
-  int need_zT, need_t1, rev;
-  int sqz;              // T_s == 2: the T = 1 student sum from the square of the T one
-  int vec;              // rows are 16-byte aligned: chunk loads, else element loads
-  float* rec;           // [kRecFields][1][n] (forward)
+  int vec;              // rows (and the output) 16-byte aligned: chunk loads and stores
+  float* rec;           // [kRecFields][n_slices][n] (forward)
   // backward
   const int64_t* labels;
   int64_t ignore;
@@ -662,20 +661,44 @@ struct RowArgs {
   void* dz;             // [n, v] student dtype
 };
 
-// Elements [e0, e0 + PC) of a row into x (past v: -inf, so that they weigh 0).
+// The (row, slice) of this wave and the slice's element range [b0, b1);
+// false for a wave past the last row.
+__device__ __forceinline__ bool row_wave(const RowArgs& a, int64_t& i, int& sl, int64_t& b0,
+                                         int64_t& b1) {
+  const int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  i = w / a.n_slices;
+  sl = (int)(w - i * a.n_slices);
+  b0 = (int64_t)sl * a.slice;
+  b1 = min(a.v, b0 + a.slice);
+  return i < a.n;
+}
+
+// The 16 bytes of elements [e0, e0 + PC) of a row, still packed, for a step
+// that may cross `end`: elements at or past it read as -inf (weight 0).
 template <typename T>
-__device__ __forceinline__ void row_chunk(const T* row, int64_t e0, int64_t v, bool vec,
-                                          float (&x)[Elem<T>::kPerChunk]) {
+__device__ __forceinline__ uint4 row_fetch(const T* row, int64_t e0, int64_t end, bool vec) {
   constexpr int PC = Elem<T>::kPerChunk;
-  if (vec && e0 + PC <= v) {
-    const uint4 u = *reinterpret_cast<const uint4*>(row + e0);
-    const T* p = reinterpret_cast<const T*>(&u);
+  if (vec && e0 + PC <= end) return load_stream(row + e0);
+  uint4 u;
+  T* p = reinterpret_cast<T*>(&u);
 #pragma unroll
-    for (int j = 0; j < PC; ++j) x[j] = to_f32(p[j]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < PC; ++j) x[j] = (e0 + j < v) ? to_f32(row[e0 + j]) : -INFINITY;
+  for (int j = 0; j < PC; ++j) {
+    if (e0 + j < end) {
+      p[j] = row[e0 + j];
+    } else if constexpr (sizeof(T) == 2) {
+      p[j] = (T)0xff80u;  // bf16 -inf
+    } else {
+      p[j] = -INFINITY;
+    }
   }
+  return u;
+}
+
+template <typename T>
+__device__ __forceinline__ void row_unpack(const uint4& u, float (&x)[Elem<T>::kPerChunk]) {
+  const T* p = reinterpret_cast<const T*>(&u);
+#pragma unroll
+  for (int j = 0; j < Elem<T>::kPerChunk; ++j) x[j] = to_f32(p[j]);
 }
 
 // Running statistics of one lane: maxima of z and t (raw units) and the sums
@@ -706,54 +729,105 @@ __device__ __forceinline__ void row_fold(RowRun& r, const RowRun& o, float cT, f
   r.mt = mt;
 }
 
-template <typename T>
+// How the row kernels get the T = 1 student terms: from squares of the ones at
+// T_s = 2, as those very terms (T_s = 1), or from their own exponentials.
+enum RowZ1 { kZ1Square = 0, kZ1Same = 1, kZ1Own = 2 };
+
+// max(x, -1e30) in one instruction: a -inf logit as a huge finite one
+__device__ __forceinline__ float clamp_ninf(float x) {
+  return __builtin_amdgcn_fmed3f(x, -1e30f, 3.0e38f);
+}
+
+// One step of a lane: raise the running maxima to cover the step's elements
+// (rescaling the sums once), then add the elements' terms against them. Z1,
+// REV (a reverse-direction KL) and T1 (teacher sums at T = 1 kept apart) are
+// template arguments so that the step holds only the terms it needs.
+template <typename T, int Z1, bool REV, bool T1>
+__device__ __forceinline__ void rowstats_step(RowRun& r, const uint4 (&rz)[kRowUnroll],
+                                              const uint4 (&rt)[kRowUnroll], const RowArgs& a) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  float z[kRowUnroll][PC], t[kRowUnroll][PC];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    row_unpack<T>(rz[u], z[u]);
+    row_unpack<T>(rt[u], t[u]);
+  }
+  float mz = r.mz, mt = r.mt;
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+      mz = fmaxf(mz, z[u][j]);
+      mt = fmaxf(mt, t[u][j]);
+    }
+  const float aT = run_scale(r.mz, mz, a.cT), cTs = run_scale(r.mt, mt, a.cTt);
+  r.szT *= aT;
+  r.ar *= aT;
+  if constexpr (Z1 == kZ1Square) r.sz1 *= aT * aT;
+  else if constexpr (Z1 == kZ1Own) r.sz1 *= run_scale(r.mz, mz, kLog2e);
+  r.stT *= cTs;
+  r.at *= cTs;
+  if constexpr (T1) r.st1 *= run_scale(r.mt, mt, kLog2e);
+  r.mz = mz;
+  r.mt = mt;
+  // an all -inf prefix keeps a finite base, so that its terms stay 0
+  const float bz = (mz == -INFINITY) ? 0.f : mz, bt = (mt == -INFINITY) ? 0.f : mt;
+  const float bzT = bz * a.cT, bz1 = bz * kLog2e, btT = bt * a.cTt, bt1 = bt * kLog2e;
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+      // a -inf logit (a zero probability, or past the row) has e = 0; in the
+      // forward cross difference it stands as -1e30, so that 0 times it stays 0
+      const float zz = z[u][j], tt = t[u][j];
+      const float ezT = exp2_fast(fmaf(zz, a.cT, -bzT));
+      const float etT = exp2_fast(fmaf(tt, a.cTt, -btT));
+      if constexpr (Z1 == kZ1Square) r.sz1 = fmaf(ezT, ezT, r.sz1);
+      else if constexpr (Z1 == kZ1Own) r.sz1 += exp2_fast(fmaf(zz, kLog2e, -bz1));
+      r.szT += ezT;
+      r.stT += etT;
+      r.at = fmaf(etT, fmaf(clamp_ninf(tt), a.rho, -clamp_ninf(zz)), r.at);
+      // reverse: a -inf teacher logit under student mass makes the KL +inf
+      if constexpr (REV) r.ar = (ezT > 0.f) ? fmaf(ezT, fmaf(tt, -a.rho, zz), r.ar) : r.ar;
+      if constexpr (T1) r.st1 += exp2_fast(fmaf(tt, kLog2e, -bt1));
+    }
+  if constexpr (Z1 == kZ1Same) r.sz1 = r.szT;
+}
+
+// Forward statistics of one slice of a row: one record, as a vocabulary tile
+// of the projected paths leaves, for the merge.
+template <typename T, int Z1, bool REV, bool T1>
 __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowArgs a) {
   constexpr int PC = Elem<T>::kPerChunk;
+  constexpr int64_t kStep = kRowUnroll * 64 * PC;
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (i >= a.n) return;
+  int64_t i, b0, b1;
+  int sl;
+  if (!row_wave(a, i, sl, b0, b1)) return;
   const T* zr = static_cast<const T*>(a.zl) + i * a.v;
   const T* tr = static_cast<const T*>(a.tl) + i * a.v;
   RowRun r{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  // kRowUnroll chunks per lane per step, all loads issued before any use
-  for (int64_t s0 = (int64_t)lane * PC; s0 < a.v; s0 += kRowUnroll * 64 * PC) {
-    float z[kRowUnroll][PC], t[kRowUnroll][PC];
+  int64_t b = b0;
+  uint4 rz[kRowUnroll], rt[kRowUnroll];
+  if (a.vec) {  // whole steps: plain 16-byte loads
+    for (; b + kStep <= b1; b += kStep) {
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int64_t e0 = b + (u * 64 + lane) * PC;
+        rz[u] = load_stream(zr + e0);
+        rt[u] = load_stream(tr + e0);
+      }
+      rowstats_step<T, Z1, REV, T1>(r, rz, rt, a);
+    }
+  }
+  for (; b < b1; b += kStep) {  // the ragged end (every step when rows are unaligned)
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-      row_chunk<T>(zr, s0 + u * 64 * PC, a.v, a.vec != 0, z[u]);
-      row_chunk<T>(tr, s0 + u * 64 * PC, a.v, a.vec != 0, t[u]);
+      const int64_t e0 = b + (u * 64 + lane) * PC;
+      rz[u] = row_fetch<T>(zr, e0, b1, a.vec != 0);
+      rt[u] = row_fetch<T>(tr, e0, b1, a.vec != 0);
     }
-    RowRun c{-INFINITY, -INFINITY, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-#pragma unroll
-      for (int j = 0; j < PC; ++j) {
-        c.mz = fmaxf(c.mz, z[u][j]);
-        c.mt = fmaxf(c.mt, t[u][j]);
-      }
-    // this step's sums against its own maxima, then folded into the run
-    const float bz = (c.mz == -INFINITY) ? 0.f : c.mz, bt = (c.mt == -INFINITY) ? 0.f : c.mt;
-    const float bzT = bz * a.cT, bz1 = bz * kLog2e, btT = bt * a.cTt, bt1 = bt * kLog2e;
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-#pragma unroll
-      for (int j = 0; j < PC; ++j) {
-        // a -inf logit (a zero probability, or past the row) has e = 0; in the
-        // forward cross difference it stands as -1e30, so that 0 times it stays 0
-        const float zz = z[u][j], tt = t[u][j];
-        const float zc = fmaxf(zz, -1e30f), tc = fmaxf(tt, -1e30f);
-        const float ezT = exp2_fast(fmaf(zz, a.cT, -bzT));
-        const float ez1 = a.sqz ? ezT * ezT : exp2_fast(fmaf(zz, kLog2e, -bz1));
-        const float etT = exp2_fast(fmaf(tt, a.cTt, -btT));
-        c.sz1 += ez1;
-        c.szT += ezT;
-        c.stT += etT;
-        c.at = fmaf(etT, fmaf(tc, a.rho, -zc), c.at);
-        // reverse: a -inf teacher logit under student mass makes the KL +inf
-        if (a.rev) c.ar = (ezT > 0.f) ? fmaf(ezT, fmaf(tt, -a.rho, zz), c.ar) : c.ar;
-        if (a.need_t1) c.st1 += exp2_fast(fmaf(tt, kLog2e, -bt1));
-      }
-    row_fold(r, c, a.cT, a.cTt);
+    rowstats_step<T, Z1, REV, T1>(r, rz, rt, a);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -769,8 +843,8 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowArgs a) {
     row_fold(r, o, a.cT, a.cTt);
   }
   if (lane == 0) {
-    float* p = a.rec + i;
-    const int64_t n = a.n;
+    const int64_t n = (int64_t)a.n_slices * a.n;  // field stride
+    float* p = a.rec + (int64_t)sl * a.n + i;
     p[0 * n] = r.mz * kLog2e;  p[1 * n] = r.sz1;
     p[2 * n] = r.mz * a.cT;    p[3 * n] = r.szT;
     p[4 * n] = r.mt * a.cTt;   p[5 * n] = r.stT;
@@ -780,75 +854,148 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(RowArgs a) {
   }
 }
 
-// d loss / d z for given student logits: the dz formula of bwd_dz, row by row,
-// stored in the logits dtype (or added to it).
+// Per-row constants of the logit gradient.
+struct RowGrad {
+  float cs, ckf, ckr;         // CE, forward-KL and reverse-KL coefficients
+  float L1, LzT, LtT;         // log2-unit lse of z, z/T_s, t/T_t
+  float k1;                   // T_s == 2: P(z) = P_T(z)^2 * k1
+  float rev0, invT;
+  int64_t y;                  // label (or out of range)
+};
+
+// d loss / d z of chunk elements [e0, e0 + PC): the dz formula of bwd_dz.
+// CE says whether the student CE term is present (Z1 as for the forward
+// step: how its P(z) comes), REV whether a reverse-direction KL term is.
+template <typename T, bool CE, int Z1, bool REV>
+__device__ __forceinline__ void logits_grad_chunk(const uint4& rz, const uint4& rt, int64_t e0,
+                                                  const RowGrad& g, const RowArgs& a,
+                                                  float (&o)[Elem<T>::kPerChunk]) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  float z[PC], t[PC];
+  row_unpack<T>(rz, z);
+  row_unpack<T>(rt, t);
+  const int64_t yl = g.y - e0;  // the label's place in the chunk (if in it)
+#pragma unroll
+  for (int j = 0; j < PC; ++j) {
+    const float pz = exp2_fast(fmaf(z[j], a.cT, -g.LzT));  // P_T(z)
+    const float pt = exp2_fast(fmaf(t[j], a.cTt, -g.LtT));
+    float dv = fmaf(g.ckf, pz - pt, 0.f);
+    if constexpr (CE) {
+      float p1;
+      if constexpr (Z1 == kZ1Square) p1 = pz * pz * g.k1;
+      else if constexpr (Z1 == kZ1Same) p1 = pz;
+      else p1 = exp2_fast(fmaf(z[j], kLog2e, -g.L1));
+      dv = fmaf(g.cs, p1 - (yl == j ? 1.f : 0.f), dv);
+    }
+    // (a row of weight 0 skips it: its factor may be infinite)
+    if constexpr (REV) {
+      if (g.ckr != 0.f) dv = fmaf(g.ckr * pz, fmaf(fmaf(t[j], -a.rho, z[j]), g.invT, g.rev0), dv);
+    }
+    o[j] = dv;
+  }
+}
+
 template <typename T>
+__device__ __forceinline__ uint4 row_pack(const float (&x)[Elem<T>::kPerChunk]) {
+  constexpr int PC = Elem<T>::kPerChunk;
+  uint4 u;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t* w32 = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+    for (int j = 0; j < PC / 2; ++j) w32[j] = bf16x2_rne(x[2 * j], x[2 * j + 1]);
+  } else {
+    float* q = reinterpret_cast<float*>(&u);
+#pragma unroll
+    for (int j = 0; j < PC; ++j) q[j] = x[j];
+  }
+  return u;
+}
+
+// d loss / d z for given student logits, one slice of a row per wave, stored
+// in the logits dtype (or added to what the output holds).
+template <typename T, bool CE, int Z1, bool REV>
 __global__ __launch_bounds__(kThreads) void logits_bwd_kernel(RowArgs a) {
   constexpr int PC = Elem<T>::kPerChunk;
+  constexpr int64_t kStep = kRowUnroll * 64 * PC;
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (i >= a.n) return;
+  int64_t i, b0, b1;
+  int sl;
+  if (!row_wave(a, i, sl, b0, b1)) return;
   const T* zr = static_cast<const T*>(a.zl) + i * a.v;
   const T* tr = static_cast<const T*>(a.tl) + i * a.v;
   T* out = static_cast<T*>(a.dz) + i * a.v;
   const float4 sv = reinterpret_cast<const float4*>(a.saved)[i];
   const float den = a.saved[4 * a.n];
-  const float g = a.grad ? *a.grad : 1.f;
-  const int64_t y = a.labels ? a.labels[i] : a.ignore;
-  const bool valid = a.labels == nullptr || (y != a.ignore && y >= 0 && y < a.v);
-  const float coef = valid ? g / den : 0.f;
-  const float cs = coef * a.ws, ck = coef * a.wkl * a.T;
-  const float ckf = (a.kl != KD_KL_REVERSE) ? ck : 0.f, ckr = (a.kl != KD_KL_FORWARD) ? ck : 0.f;
-  const float L1 = sv.x * kLog2e, LzT = sv.y * kLog2e, LtT = sv.z * kLog2e;
-  const float rev0 = sv.z - sv.y - sv.w, invT = 1.f / a.T;
-  for (int64_t s0 = (int64_t)lane * PC; s0 < a.v; s0 += kRowUnroll * 64 * PC) {
-    float zs[kRowUnroll][PC], ts[kRowUnroll][PC];
+  const float gl = a.grad ? *a.grad : 1.f;
+  RowGrad g;
+  g.y = a.labels ? a.labels[i] : a.ignore;
+  const bool valid = a.labels == nullptr || (g.y != a.ignore && g.y >= 0 && g.y < a.v);
+  const float coef = valid ? gl / den : 0.f;
+  const float ck = coef * a.wkl * a.T;
+  g.cs = coef * a.ws;
+  g.ckf = (a.kl != KD_KL_REVERSE) ? ck : 0.f;
+  g.ckr = (a.kl != KD_KL_FORWARD) ? ck : 0.f;
+  g.L1 = sv.x * kLog2e;
+  g.LzT = sv.y * kLog2e;
+  g.LtT = sv.z * kLog2e;
+  g.k1 = exp2_fast(2.f * g.LzT - g.L1);
+  g.rev0 = sv.z - sv.y - sv.w;
+  g.invT = 1.f / a.T;
+  int64_t b = b0;
+  uint4 rz[kRowUnroll], rt[kRowUnroll];
+  if (a.vec) {  // whole steps: plain 16-byte loads and stores
+    for (; b + kStep <= b1; b += kStep) {
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int64_t e0 = b + (u * 64 + lane) * PC;
+        rz[u] = load_stream(zr + e0);
+        rt[u] = load_stream(tr + e0);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int64_t e0 = b + (u * 64 + lane) * PC;
+        float o[PC];
+        logits_grad_chunk<T, CE, Z1, REV>(rz[u], rt[u], e0, g, a, o);
+        if (a.accumulate) {
+          float prev[PC];
+          row_unpack<T>(load_stream(out + e0), prev);
+#pragma unroll
+          for (int j = 0; j < PC; ++j) o[j] += prev[j];
+        }
+        *reinterpret_cast<uint4*>(out + e0) = row_pack<T>(o);
+      }
+    }
+  }
+  for (; b < b1; b += kStep) {  // the ragged end (every step when rows are unaligned)
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-      row_chunk<T>(zr, s0 + u * 64 * PC, a.v, a.vec != 0, zs[u]);
-      row_chunk<T>(tr, s0 + u * 64 * PC, a.v, a.vec != 0, ts[u]);
+      const int64_t e0 = b + (u * 64 + lane) * PC;
+      rz[u] = row_fetch<T>(zr, e0, b1, a.vec != 0);
+      rt[u] = row_fetch<T>(tr, e0, b1, a.vec != 0);
     }
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-    const int64_t e0 = s0 + u * 64 * PC;
-    const float* z = zs[u];
-    const float* t = ts[u];
-    float o[PC];
+      const int64_t e0 = b + (u * 64 + lane) * PC;
+      float o[PC];
+      logits_grad_chunk<T, CE, Z1, REV>(rz[u], rt[u], e0, g, a, o);
+      if (a.vec && e0 + PC <= b1) {
+        if (a.accumulate) {
+          float prev[PC];
+          row_unpack<T>(load_stream(out + e0), prev);
 #pragma unroll
-    for (int j = 0; j < PC; ++j) {
-      const float p1 = exp2_fast(fmaf(z[j], kLog2e, -L1));
-      const float pz = a.need_zT ? exp2_fast(fmaf(z[j], a.cT, -LzT)) : p1;
-      const float pt = exp2_fast(fmaf(t[j], a.cTt, -LtT));
-      float dv = cs * (p1 - (e0 + j == y ? 1.f : 0.f));
-      dv = fmaf(ckf, pz - pt, dv);
-      if (ckr != 0.f) dv = fmaf(ckr * pz, fmaf(fmaf(t[j], -a.rho, z[j]), invT, rev0), dv);
-      o[j] = dv;
-    }
-    if (a.vec && e0 + PC <= a.v) {  // one 16-byte store (and load, to accumulate)
-      uint4 u = a.accumulate ? *reinterpret_cast<const uint4*>(out + e0) : make_uint4(0u, 0u, 0u, 0u);
-      T* q = reinterpret_cast<T*>(&u);
-      float sum[PC];
-#pragma unroll
-      for (int j = 0; j < PC; ++j) sum[j] = (a.accumulate ? to_f32(q[j]) : 0.f) + o[j];
-      if constexpr (sizeof(T) == 2) {
-        uint32_t* w32 = reinterpret_cast<uint32_t*>(&u);
-#pragma unroll
-        for (int j = 0; j < PC / 2; ++j) w32[j] = bf16x2_rne(sum[2 * j], sum[2 * j + 1]);
+          for (int j = 0; j < PC; ++j) o[j] += prev[j];
+        }
+        *reinterpret_cast<uint4*>(out + e0) = row_pack<T>(o);
       } else {
 #pragma unroll
-        for (int j = 0; j < PC; ++j) q[j] = sum[j];
-      }
-      *reinterpret_cast<uint4*>(out + e0) = u;
-    } else {
-#pragma unroll
-      for (int j = 0; j < PC; ++j) {
-        if (e0 + j < a.v) {
-          const float prev = a.accumulate ? to_f32(out[e0 + j]) : 0.f;
-          if constexpr (sizeof(T) == 2) out[e0 + j] = bf16_rne(prev + o[j]);
-          else out[e0 + j] = prev + o[j];
+        for (int j = 0; j < PC; ++j) {
+          if (e0 + j < b1) {
+            const float prev = a.accumulate ? to_f32(out[e0 + j]) : 0.f;
+            if constexpr (sizeof(T) == 2) out[e0 + j] = bf16_rne(prev + o[j]);
+            else out[e0 + j] = prev + o[j];
+          }
         }
       }
-    }
     }
   }
 }
@@ -1548,6 +1695,48 @@ int row_vec(const void* a, const void* b, int64_t v) {
   return ((v * (int64_t)sizeof(T)) % 16 == 0 && (uintptr_t)a % 16 == 0 && (uintptr_t)b % 16 == 0) ? 1 : 0;
 }
 
+// The row kernels' way to the T = 1 student terms for student temperature T.
+inline int row_z1(float T) { return (T == 1.f) ? kZ1Same : ((T == 2.f) ? kZ1Square : kZ1Own); }
+
+// Forward row kernel instantiated for one launch's choices.
+template <typename T, int Z1>
+void rowstats_launch(bool rev, bool t1, dim3 grid, hipStream_t stream, const RowArgs& ra) {
+  if (rev) {
+    if (t1) rowstats_kernel<T, Z1, true, true><<<grid, kThreads, 0, stream>>>(ra);
+    else rowstats_kernel<T, Z1, true, false><<<grid, kThreads, 0, stream>>>(ra);
+  } else {
+    if (t1) rowstats_kernel<T, Z1, false, true><<<grid, kThreads, 0, stream>>>(ra);
+    else rowstats_kernel<T, Z1, false, false><<<grid, kThreads, 0, stream>>>(ra);
+  }
+}
+
+template <typename T>
+void rowstats_launch(int z1, bool rev, bool t1, dim3 grid, hipStream_t stream, const RowArgs& ra) {
+  if (z1 == kZ1Same) rowstats_launch<T, kZ1Same>(rev, t1, grid, stream, ra);
+  else if (z1 == kZ1Square) rowstats_launch<T, kZ1Square>(rev, t1, grid, stream, ra);
+  else rowstats_launch<T, kZ1Own>(rev, t1, grid, stream, ra);
+}
+
+// Logit-gradient row kernel instantiated for one launch's choices.
+template <typename T, int Z1>
+void logits_bwd_launch(bool ce, bool rev, dim3 grid, hipStream_t stream, const RowArgs& ra) {
+  if (ce) {
+    if (rev) logits_bwd_kernel<T, true, Z1, true><<<grid, kThreads, 0, stream>>>(ra);
+    else logits_bwd_kernel<T, true, Z1, false><<<grid, kThreads, 0, stream>>>(ra);
+  } else {
+    if (rev) logits_bwd_kernel<T, false, Z1, true><<<grid, kThreads, 0, stream>>>(ra);
+    else logits_bwd_kernel<T, false, Z1, false><<<grid, kThreads, 0, stream>>>(ra);
+  }
+}
+
+template <typename T>
+void logits_bwd_launch(int z1, bool ce, bool rev, dim3 grid, hipStream_t stream, const RowArgs& ra) {
+  if (!ce) logits_bwd_launch<T, kZ1Same>(false, rev, grid, stream, ra);  // Z1 unused
+  else if (z1 == kZ1Same) logits_bwd_launch<T, kZ1Same>(true, rev, grid, stream, ra);
+  else if (z1 == kZ1Square) logits_bwd_launch<T, kZ1Square>(true, rev, grid, stream, ra);
+  else logits_bwd_launch<T, kZ1Own>(true, rev, grid, stream, ra);
+}
+
 // How a given [n x v] logits matrix is read: 2 = staged through LDS with
 // 16-byte buffer loads (pipelined bf16 tiles: v a multiple of 8, 16-byte
 // aligned, v up to 2^23), 1 = a lane's four consecutive elements as one vector (v a multiple
@@ -1632,14 +1821,13 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
     ra.cT = kLog2e / p.T;
     ra.cTt = kLog2e / p.Tt;
     ra.rho = p.T / p.Tt;
-    ra.need_zT = p.need_zT;
-    ra.need_t1 = need_t1;
-    ra.rev = p.kl != KD_KL_FORWARD;
-    ra.sqz = (p.T == 2.f && p.need_zT) ? 1 : 0;
     ra.vec = row_vec<T>(x.logits, x.tlogits, p.v);
     ra.rec = rec;
+    ra.slice = p.row_slice;
+    ra.n_slices = p.n_slices;
+    const dim3 grid((unsigned)((p.n * (int64_t)p.n_slices + 3) / 4));
     KD_TRY(L.run(KD_KERNEL_FWD, [&] {
-      rowstats_kernel<T><<<dim3((unsigned)((p.n + 3) / 4)), kThreads, 0, stream>>>(ra);
+      rowstats_launch<T>(row_z1(p.T), p.kl != KD_KL_FORWARD, need_t1 != 0, grid, stream, ra);
     }));
   } else
   KD_TRY(L.run(KD_KERNEL_FWD, [&] {
@@ -1902,7 +2090,6 @@ kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved
   ra.cT = kLog2e / p.T;
   ra.cTt = kLog2e / p.Tt;
   ra.rho = p.T / p.Tt;
-  ra.need_zT = p.need_zT;
   ra.labels = x.labels;
   ra.ignore = p.ignore;
   ra.saved = static_cast<const float*>(saved);
@@ -1913,13 +2100,17 @@ kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved
   ra.kl = p.kl;
   ra.accumulate = accumulate;
   ra.dz = d_logits;
-  const dim3 grid((unsigned)((p.n + 3) / 4));
+  ra.slice = p.row_slice;
+  ra.n_slices = p.n_slices;
+  const dim3 grid((unsigned)((p.n * (int64_t)p.n_slices + 3) / 4));
+  const int z1 = row_z1(p.T);
+  const bool ce = p.ws != 0.f, rev = p.kl != KD_KL_FORWARD;
   if (p.dtype == KD_BF16) {
     ra.vec = row_vec<bf16_t>(x.logits, x.tlogits, p.v) && row_vec<bf16_t>(d_logits, d_logits, p.v);
-    return L.run(KD_KERNEL_BWD_DZ, [&] { logits_bwd_kernel<bf16_t><<<grid, kThreads, 0, stream>>>(ra); });
+    return L.run(KD_KERNEL_BWD_DZ, [&] { logits_bwd_launch<bf16_t>(z1, ce, rev, grid, stream, ra); });
   }
   ra.vec = row_vec<float>(x.logits, x.tlogits, p.v) && row_vec<float>(d_logits, d_logits, p.v);
-  return L.run(KD_KERNEL_BWD_DZ, [&] { logits_bwd_kernel<float><<<grid, kThreads, 0, stream>>>(ra); });
+  return L.run(KD_KERNEL_BWD_DZ, [&] { logits_bwd_launch<float>(z1, ce, rev, grid, stream, ra); });
 }
 
 kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,

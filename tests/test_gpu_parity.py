@@ -339,6 +339,13 @@ BOTH_LOGITS_CASES = {
     "jeffreys_ce": C7.scaled(n=200, v=2048, kl_divergence="jeffreys", student_ce_weight=0.5,
                              teacher_ce_weight=0.25),
     "neg_inf_T1": C7.scaled(n=260, v=2100, temperature=1.0, teacher_neg_inf_frac=0.3),
+    # T_s neither 1 nor 2: the T = 1 student terms from exponentials of their own
+    "T1.5_jeffreys_ce": C7.scaled(n=150, v=2500, temperature=1.5, kl_divergence="jeffreys",
+                                  student_ce_weight=0.7),
+    # rows split into slices of two steps each, the last one ragged
+    "multi_step_slices": C7.scaled(n=1000, v=20000, student_ce_weight=0.3),
+    # a row shorter than one step: one slice per row
+    "one_slice": C7.scaled(n=100, v=700),
 }
 
 
