@@ -46,6 +46,8 @@ def method_flops(w, train_teacher: bool = False, n_rows: int = 0) -> dict:
         fwd = 2 * n * d * v + 2 * n * dt * v
     else:
         fwd = 2 * n * d * v
+    if w.forward_only:  # a scorer: the forward tiles are the whole step
+        return {"total": fwd, "useful": fwd, "fwd_per_launch": fwd}
     total = 2 * fwd + 4 * n * d * v
     useful = fwd + 4 * n * d * v
     if train_teacher:

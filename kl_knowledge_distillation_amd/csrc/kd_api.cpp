@@ -187,6 +187,12 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   off = align_up(off + (size_t)kd::kRecFields * q.n_slices * (size_t)q.n * sizeof(float), 256);
   q.off_part = off;
   off = align_up(off + (size_t)q.merge_blocks * 4 * sizeof(double), 256);
+  if (q.mode == kd::MODE_TOPK) {
+    q.off_tks = off;
+    off = align_up(off + 8 * (size_t)q.n * (size_t)q.k, 256);
+    q.off_tko = off;
+    off = align_up(off + 4 * (size_t)q.n * (size_t)(q.n_vtiles + 1), 256);
+  }
   q.fwd_bytes = off;
   q.off_dz = off_common;
   q.bwd_bytes = align_up(q.off_dz + (size_t)q.dz_rows * (size_t)q.chunk * elem, 256);

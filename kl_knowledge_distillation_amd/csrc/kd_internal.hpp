@@ -68,6 +68,10 @@ struct Plan {
   int merge_blocks = 0;
   // forward workspace layout (bytes from the workspace base)
   size_t off_prep = 0, off_rec = 0, off_part = 0, fwd_bytes = 0;
+  // top-K: each row's entries sorted by vocabulary index (int32 idx [n][k], then
+  // fp32 prob [n][k]) and where each vocabulary tile's entries start (int32
+  // [n][n_vtiles + 1])
+  size_t off_tks = 0, off_tko = 0;
   // backward workspace layout
   size_t off_dz = 0, bwd_bytes = 0;
   // compaction buffers (same offsets in both workspaces): idx, pos [n] int32,

@@ -363,14 +363,29 @@ struct FwdArgs {
   int sqz;     // T_s == 2: the T = 1 student sums are the squares of those at T
   float* rec;  // [kRecFields][n_slices][n]
   const int32_t* nv;  // compacted rows: their number (tiles past it exit); null = n
+  // top-K teacher: each row's k entries sorted by index and where each
+  // vocabulary tile's entries start (prep_kernel)
+  const int32_t* topk_sidx;  // [n, k]
+  const float* topk_sprob;   // [n, k]
+  const int32_t* topk_off;   // [n, n_slices + 1]
+  int k;
 };
+
+// Top-K: floats per token row of the z tile staged in LDS (the padding spreads
+// the rows of a 16-token block over the banks).
+template <class G>
+constexpr int topk_zstride() { return G::kVT + 4; }
 
 template <typename T, int MODE, class G>
 __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
   constexpr bool kGiven = MODE == MODE_TLOGITS || MODE == MODE_LOGITS;  // one logits tile is given
   constexpr int kMainBytes = G::template lds_bytes<NB>();
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0)];
+  // top-K: the fp32 z tile [kTT][zstride] after the main loop, then the tile's
+  // cross terms [kTT] past the epilogue's exchange area
+  constexpr int kTopkBytes = (MODE == MODE_TOPK) ? G::kTT * topk_zstride<G>() * 4 : 0;
+  constexpr int kLdsMain = kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsMain > kTopkBytes ? kLdsMain : kTopkBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: only the token tiles below nv have work; they are mapped
   // onto the first blocks of every XCD and the rest of the grid exits.
@@ -443,6 +458,37 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int kSums = 6;  // sz1, szT, stT, a, st1, ar
   float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNB][2][16]
   float* xsum = xmax + G::kWM * 2 * kNB * 2 * 16;                 // [kWM][2][kNB][kSums][16]
+  float* xcross = xsum + G::kWM * 2 * kNB * kSums * 16;           // [kTT] (top-K)
+  if constexpr (MODE == MODE_TOPK) {
+    // Sum over a token's entries whose index falls in this tile of p z[idx]
+    // (orda-kernel, Teacher descriptors: TopKTeacher), z read back from the
+    // tile itself, so the cross term and the statistics share every value.
+    // The tile goes through LDS ([token][vocabulary row], free after the main
+    // loop); the token's entries of this tile are a run of its sorted entries,
+    // added in index order by the first of its kTpt threads.
+    constexpr int kZs = topk_zstride<G>();
+    float* zt = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+        *reinterpret_cast<f32x4*>(zt + acc_col(wn, nb, lane) * kZs + acc_row(wm, mb, 0, lane)) = z[mb][nb];
+    __syncthreads();
+    constexpr int kTpt = G::kThreads / G::kTT;  // threads per token (adjacent lanes)
+    static_assert(kTpt >= 1 && (kTpt & (kTpt - 1)) == 0 && kTpt <= 64, "threads per token");
+    const int tq = tid / kTpt, part = tid % kTpt;
+    const int64_t tok = t0 + tq;
+    float cross = 0.f;
+    if (tok < a.n && part == 0) {
+      const int32_t* off = a.topk_off + tok * (a.n_slices + 1) + slice;
+      const int j0 = off[0], j1 = off[1];  // sorted entries with index in [v0, v0 + kVT) and < v
+      const int32_t* ix = a.topk_sidx + tok * a.k;
+      const float* pr = a.topk_sprob + tok * a.k;
+      for (int j = j0; j < j1; ++j) cross = fmaf(pr[j], zt[tq * kZs + (ix[j] - v0)], cross);
+    }
+    __syncthreads();  // every read of the z tile done: the epilogue reuses the LDS
+    if (part == 0) xcross[tq] = cross;
+  }
   const int l16 = lane & 15;
 
   float mz[kNB], mt[kNB];
@@ -534,7 +580,8 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
         r[0 * stride] = mz[nb] * kLog2e; r[1 * stride] = v[0];
         r[2 * stride] = mz[nb] * a.cT;   r[3 * stride] = v[1];
         r[4 * stride] = mt[nb] * a.cTt;  r[5 * stride] = v[2];
-        r[6 * stride] = v[3];
+        // top-K: field 6 carries the tile's cross term sum p z[idx]
+        r[6 * stride] = (MODE == MODE_TOPK) ? xcross[acc_col(wn, nb, lane)] : v[3];
         r[7 * stride] = mt[nb] * kLog2e; r[8 * stride] = v[4];
         r[9 * stride] = v[5];
       }
@@ -560,6 +607,13 @@ struct PrepArgs {
   int k;
   int want_teacher;  // teacher label logit needed (teacher CE weight or output)
   float* prep;       // [4][n]: z[y] | S, t[y] | E, M, flag
+  // top-K: the row's entries sorted by index (an index outside [0, v) as v,
+  // last), and per vocabulary tile of vt_rows rows the first sorted entry at
+  // or past it ([n_vtiles + 1] per row, the last one past the valid entries)
+  int32_t* sidx;
+  float* sprob;
+  int32_t* toff;
+  int vt_rows, n_vtiles;
 };
 
 template <typename T>
@@ -579,8 +633,13 @@ __device__ __forceinline__ float wave_dot(const T* x, const T* y, int64_t len, i
   return s;
 }
 
+// Top-K rows of up to this many entries keep their sorted indices in LDS, where
+// the vocabulary tiles' first entries are found by binary search.
+constexpr int kTopkLdsK = 1024;
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
+  __shared__ int32_t skeys[(MODE == MODE_TOPK) ? (kThreads / 64) * kTopkLdsK : 1];
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (i >= a.n) return;
@@ -588,20 +647,62 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
   const T* W = static_cast<const T*>(a.w);
   float f0 = 0.f, f1 = 0.f, f2 = 0.f, flag = 1.f;
   if constexpr (MODE == MODE_TOPK) {
-    float mass = 0.f, ent = 0.f, cross = 0.f;
+    // the mass and sum p log p of the row (its cross term comes from the
+    // tiles), and its entries sorted by index for them: entry j goes to its
+    // rank (ties in entry order), O(k^2) compares per row
+    const int32_t* ix = a.idx + i * a.k;
+    const float* pr = a.prob + i * a.k;
+    auto key = [&](int j) -> int64_t {
+      const int64_t x = ix[j];
+      return (x < 0 || x >= a.v) ? a.v : x;  // never used as an address
+    };
+    float mass = 0.f, ent = 0.f;
     bool bad = false;
-    for (int j = 0; j < a.k; ++j) {
-      const int32_t ix = a.idx[i * a.k + j];
-      const float p = a.prob[i * a.k + j];
+    for (int j = lane; j < a.k; j += 64) {
+      const float p = pr[j];
       mass += p;
       ent += (p > 0.f) ? p * logf(p) : 0.f;
-      if (ix < 0 || (int64_t)ix >= a.v) {  // never used as an address
-        bad = true;
-        continue;
+      const int64_t kj = key(j);
+      bad = bad || kj == a.v;
+      int rank = 0;
+      for (int jj = 0; jj < a.k; ++jj) {
+        const int64_t kk = key(jj);
+        rank += (kk < kj || (kk == kj && jj < j)) ? 1 : 0;
       }
-      cross = fmaf(p, wave_dot<T>(hs + i * a.d, W + (int64_t)ix * a.d, a.d, lane), cross);
+      a.sidx[i * a.k + rank] = (int32_t)kj;
+      a.sprob[i * a.k + rank] = p;
+      if (a.k <= kTopkLdsK) skeys[(threadIdx.x >> 6) * kTopkLdsK + rank] = (int32_t)kj;
     }
-    f0 = cross;
+    // tile vt's entries start at the number of keys below min(vt vt_rows, v)
+    if (a.k <= kTopkLdsK) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int32_t* sk = skeys + (threadIdx.x >> 6) * kTopkLdsK;
+      for (int vt = lane; vt <= a.n_vtiles; vt += 64) {
+        const int64_t lo = min((int64_t)vt * a.vt_rows, a.v);
+        int l = 0, h = a.k;  // first position with key >= lo
+        while (l < h) {
+          const int m = (l + h) >> 1;
+          if ((int64_t)sk[m] < lo) l = m + 1;
+          else h = m;
+        }
+        a.toff[i * (a.n_vtiles + 1) + vt] = l;
+      }
+    } else {
+      for (int vt = lane; vt <= a.n_vtiles; vt += 64) {
+        const int64_t lo = min((int64_t)vt * a.vt_rows, a.v);
+        int c = 0;
+        for (int jj = 0; jj < a.k; ++jj) c += (key(jj) < lo) ? 1 : 0;
+        a.toff[i * (a.n_vtiles + 1) + vt] = c;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      mass += __shfl_xor(mass, off);
+      ent += __shfl_xor(ent, off);
+    }
+    bad = __any(bad);
     f1 = ent;
     f2 = mass;
     flag = bad ? 2.f : 1.f;
@@ -1083,8 +1184,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f, lt1 = 0.f;
       bool valid;
       if (a.mode == MODE_TOPK) {
-        // sum p log p - sum p z[idx] + M lse(z)
-        kl = f1 - f0 + f2 * lz1;
+        // sum p log p - sum p z[idx] + M lse(z); the cross term is the sum of
+        // the tiles' record field 6
+        kl = f1 - s.a + f2 * lz1;
         mass = f2;
         valid = true;
       } else {
@@ -1786,8 +1888,12 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   double* part = reinterpret_cast<double*>(base + p.off_part);
   int32_t* status = reinterpret_cast<int32_t*>(base);
 
+  int32_t* tk_idx = reinterpret_cast<int32_t*>(base + p.off_tks);
+  float* tk_prob = reinterpret_cast<float*>(base + p.off_tks + 4 * (size_t)p.n * (size_t)p.k);
+  int32_t* tk_off = reinterpret_cast<int32_t*>(base + p.off_tko);
   PrepArgs pa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, x.labels, x.topk_idx, x.topk_prob,
-              p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, prep};
+              p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, prep, tk_idx, tk_prob, tk_off, p.vt_rows,
+              p.n_vtiles};
   pa.want_teacher = p.mode != MODE_TOPK && (p.wt > 0.f || (out && out->teacher_ce));
   const dim3 pgrid((unsigned)((p.n + 3) / 4));
   KD_TRY(L.run(KD_KERNEL_PREP, [&] {
@@ -1810,7 +1916,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   FwdArgs fa{cp.hs, x.w, cp.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
              p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, kLog2e / p.Tt, p.T / p.Tt,
              p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v),
-             (p.T == 2.f && p.need_zT) ? 1 : 0, rec, cp.nv};
+             (p.T == 2.f && p.need_zT) ? 1 : 0, rec, cp.nv, tk_idx, tk_prob, tk_off, p.k};
   const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
   if (p.mode == MODE_BOTH) {
     RowArgs ra{};

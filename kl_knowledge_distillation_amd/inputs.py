@@ -153,17 +153,22 @@ def make_topk(n: int, v: int, k: int, seed: int = 0):
 
     Indices are uniform without replacement over [0, v) (int32). Probabilities
     are M * Dirichlet(0.1 * 1_k) with M ~ U(0.85, 0.99), stored in fp32 and not
-    renormalised after rounding. Rows with a repeated index are redrawn.
+    renormalised after rounding. With k^2 <= v rows with a repeated index are
+    redrawn; beyond that (where a row without repeats is rare) each row is the
+    first k of a random permutation of [0, v).
     """
     rng = np.random.Generator(np.random.PCG64(seed * 1000 + _STREAM["topk"]))
-    idx = rng.integers(0, v, size=(n, k), dtype=np.int64)
-    while True:
-        s = np.sort(idx, axis=1)
-        dup = (s[:, 1:] == s[:, :-1]).any(axis=1) if k > 1 else np.zeros(n, bool)
-        bad = np.nonzero(dup)[0]
-        if bad.size == 0:
-            break
-        idx[bad] = rng.integers(0, v, size=(bad.size, k), dtype=np.int64)
+    if k * k > v:
+        idx = np.argsort(rng.random((n, v)), axis=1)[:, :k].astype(np.int64)
+    else:
+        idx = rng.integers(0, v, size=(n, k), dtype=np.int64)
+        while True:
+            s = np.sort(idx, axis=1)
+            dup = (s[:, 1:] == s[:, :-1]).any(axis=1) if k > 1 else np.zeros(n, bool)
+            bad = np.nonzero(dup)[0]
+            if bad.size == 0:
+                break
+            idx[bad] = rng.integers(0, v, size=(bad.size, k), dtype=np.int64)
     gam = rng.gamma(0.1, 1.0, size=(n, k))
     tot = gam.sum(axis=1, keepdims=True)
     tot[tot == 0] = 1.0

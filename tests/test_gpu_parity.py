@@ -33,6 +33,8 @@ SMALL = {
                                    ignore_frac=0.1),
     "topk_small": C4.scaled(n=300, d=512, v=5000),
     "topk_ragged": C4.scaled(n=129, d=264, v=1031, k=7),
+    # more entries per row than the prep sorts in LDS (the counting path)
+    "topk_many": C4.scaled(n=40, d=256, v=3000, k=1100),
     "scorer_small": C5.scaled(n=300, d_t=512, v=5000),
 }
 
@@ -146,6 +148,26 @@ def test_out_of_range_label_flag():
     assert_scalar(float(r.loss), ref["loss"], "bf16", "loss with bad labels")
     dH, dW = O.backward(s, t, params_of(w), labels)
     assert_grad(to_np(dh), dH, "bf16", "dH with bad labels")
+
+
+def test_topk_out_of_range_index_flag():
+    """Top-K indices outside [0, V) are never used as addresses: the device
+    status flags them, and every other row keeps its value."""
+    w = C4.scaled(n=64, d=256, v=2000, k=10)
+    x = make_inputs(w, "cuda", seed=8)
+    idx = x["topk_idx"].clone()
+    idx[5, 3] = w.v + 7
+    idx[9, 0] = -2
+    x["topk_idx"] = idx
+    r, dh, dw = run_gpu(w, x)
+    assert r.read_status() == 1
+    good = np.array([i for i in range(w.n) if i not in (5, 9)])
+    s = O.Student(hidden=to_np(x["student_hidden"]).astype(np.float64)[good],
+                  weight=to_np(x["weight"]).astype(np.float64))
+    t = O.Teacher("topk", idx=to_np(idx).astype(np.int64)[good],
+                  prob=to_np(x["topk_prob"]).astype(np.float64)[good])
+    ref = O.forward(s, t, params_of(w), None)
+    assert_tokens(to_np(r.kl)[good], ref["kl"], "bf16", "top-K kl beside bad indices")
 
 
 def test_all_labels_ignored():

@@ -34,6 +34,16 @@ def test_topk_structure():
     assert torch.equal(idx, i2) and torch.equal(p, p2)
 
 
+def test_topk_structure_many_entries():
+    # k^2 > v: rows are drawn as permutation prefixes (distinct, in range)
+    idx, p = make_topk(40, 3000, 1100, seed=0)
+    s = np.sort(idx.numpy(), axis=1)
+    assert idx.shape == (40, 1100) and (s[:, 1:] != s[:, :-1]).all()
+    assert s.min() >= 0 and s.max() < 3000
+    m = p.double().sum(dim=1).numpy()
+    assert (m > 0.85 - 1e-5).all() and (m < 0.99 + 1e-5).all()
+
+
 def test_tiny_inputs_shapes_and_stats():
     w = WORKLOADS["tiny_tied_fp32"]
     x = make_inputs(w, "cpu", seed=0)
