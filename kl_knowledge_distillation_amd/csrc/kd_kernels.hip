@@ -218,18 +218,20 @@ struct GeoPipe {
 using GeoFused = GeoPipe;
 
 // acc[g] = A[a_row0 : +VT, 0:K] * B_g[b_row0 : +TT, 0:K]^T for K-contiguous operands.
+// pf: the cooperative prefetch share of this tile (pipelined, two B operands).
 template <typename T, class G, int NB>
 __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t arows,
                                              const T* const (&b)[NB], int64_t ldb, int64_t brows,
                                              int64_t a_row0, int64_t b_row0, int64_t K,
-                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][kNB], int tid) {
+                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][kNB], int tid,
+                                             PipePrefetch pf = PipePrefetch{0, 0, 0, nullptr}) {
   if constexpr (G::kPipe) {
     static_assert(sizeof(T) == 2, "the pipelined geometry is bf16 only");
     const PipeOperand A{a, lda, arows};
     PipeOperand B[NB];
 #pragma unroll
     for (int g = 0; g < NB; ++g) B[g] = PipeOperand{b[g], ldb, brows};
-    pipe_mainloop<typename G::template Cfg<NB>, NB>(A, B, a_row0, b_row0, K, lds, acc, tid);
+    pipe_mainloop<typename G::template Cfg<NB>, NB>(A, B, a_row0, b_row0, K, lds, acc, tid, pf);
   } else {
     const Operand<T, true> A{a, lda, arows, K};
     Operand<T, true> B[NB];
@@ -384,7 +386,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   // top-K: the fp32 z tile [kTT][zstride] after the main loop, then the tile's
   // cross terms [kTT] past the epilogue's exchange area
   constexpr int kTopkBytes = (MODE == MODE_TOPK) ? G::kTT * topk_zstride<G>() * 4 : 0;
-  constexpr int kLdsMain = kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0);
+  // pipelined tiles with no given logits tile (which fills the LDS): 1 KB past
+  // the slots where the prefetch reads land
+  constexpr bool kPf = G::kPipe && !kGiven && kPipeAhead > 0;
+  constexpr int kLdsMain = kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0) + (kPf ? 1024 : 0);
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsMain > kTopkBytes ? kLdsMain : kTopkBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: only the token tiles below nv have work; they are mapped
@@ -406,17 +411,20 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   f32x4 tacc[1][kMB][kNB];  // teacher accumulator of the separate / logits modes
   WaveAcc zl;               // student logits loaded in LOGITS mode
 
+  // the tile's share of the cooperative prefetch (grouped order: token tiles
+  // tt % 8 and vocabulary tiles slice % 4 run side by side)
+  const PipePrefetch pf{kPf ? 1 : 0, tt % 8, slice % 4, lds + kMainBytes};
   if constexpr (MODE == MODE_TIED) {
     const T* const b[2] = {hs, ht};
-    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   } else if constexpr (MODE == MODE_SEPARATE) {
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
   } else if constexpr (MODE == MODE_TOPK) {
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
     if constexpr (G::kPipe)
@@ -1339,7 +1347,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
   constexpr bool kGiven = MODE == MODE_TLOGITS;
   constexpr int kMainBytes = G::template lds_bytes<NB>();
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0)];
+  constexpr bool kPf = G::kPipe && !kGiven && kPipeAhead > 0;  // prefetch reads: 1 KB
+  __shared__ __attribute__((aligned(16))) uint8_t
+      lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0) + (kPf ? 1024 : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: token tiles from round_up(nv, 128) on would hold only zero
   // rows, which no GEMM reads (their K and M stop at nv); only the tiles below
@@ -1359,14 +1369,16 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
 
   f32x4 acc[NB][kMB][kNB];
   f32x4 tacc[1][kMB][kNB];
+  // the tile's share of the cooperative prefetch (grouped order)
+  const PipePrefetch pf{kPf ? 1 : 0, tt % 8, vt % 4, lds + kMainBytes};
   if constexpr (MODE == MODE_TIED) {
     const T* const b[2] = {hs, ht};
-    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   } else if constexpr (MODE == MODE_SEPARATE) {
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
     if constexpr (G::kPipe)
@@ -1377,10 +1389,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, tacc[0]);
   } else if constexpr (MODE == MODE_TCE) {  // the teacher tile alone
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, acc, tid);
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, acc, tid, pf);
   } else {  // MODE_TOPK
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   }
   const WaveAcc& z = acc[0];  // MODE_TCE: the teacher logits
   const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
