@@ -47,13 +47,13 @@ def method_flops(w, train_teacher: bool = False, n_rows: int = 0) -> dict:
     else:
         fwd = 2 * n * d * v
     if w.forward_only:  # a scorer: the forward tiles are the whole step
-        return {"total": fwd, "useful": fwd, "fwd_per_launch": fwd}
+        return {"total": fwd, "useful": fwd, "fwd": fwd}
     total = 2 * fwd + 4 * n * d * v
     useful = fwd + 4 * n * d * v
     if train_teacher:
         total += 6 * n * dt * v
         useful += 4 * n * dt * v
-    return {"total": total, "useful": useful, "fwd_per_launch": fwd}
+    return {"total": total, "useful": useful, "fwd": fwd}
 
 
 def kernel_flops_per_launch(w, kernel: str, chunk: int, n_rows: int = 0,
@@ -62,12 +62,12 @@ def kernel_flops_per_launch(w, kernel: str, chunk: int, n_rows: int = 0,
     class alternate between the student's and the teacher's, so the mean."""
     n, d, v, dt = (n_rows or w.n), w.d, w.v, w.teacher_dim
     fl = method_flops(w, n_rows=n)
-    if kernel == "fwd":
-        return fl["fwd_per_launch"]
     n_chunks = -(-v // chunk)
+    if kernel == "fwd":  # the forward tiles run one launch per vocabulary chunk
+        return fl["fwd"] / n_chunks
     per_chunk_cols = v / n_chunks  # average columns per launch
     if kernel == "bwd_dz":
-        f = fl["fwd_per_launch"] * per_chunk_cols / v
+        f = fl["fwd"] * per_chunk_cols / v
         return (f + 2 * n * dt * per_chunk_cols) / 2 if train_teacher else f
     if kernel in ("gemm_dw", "gemm_dh", "gemm_dwdh"):
         f = 2 * n * d * per_chunk_cols
@@ -108,6 +108,7 @@ def traffic_for(kernel: str, workload: str):
 
 
 _KERNEL_CLASS = (("prep_kernel", "prep"), ("fwd_tiles_kernel", "fwd"), ("merge_kernel", "merge"),
+                 ("fold_kernel", "merge"),
                  ("finalize_kernel", "finalize"), ("bwd_dz_kernel", "bwd_dz"),
                  ("scatter_kernel", "scatter"), ("gemm_pipe_kernel<false, false", "gemm_dw"),
                  ("gemm_pipe_kernel<true, false", "gemm_dh"), ("gemm_kernel<float, false, false", "gemm_dw"),

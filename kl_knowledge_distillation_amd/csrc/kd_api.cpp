@@ -164,6 +164,9 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   chunk = std::min<int64_t>(chunk, ceil_div(q.v, vt) * vt);
   q.chunk = chunk;
   q.n_chunks = (int)ceil_div(q.v, chunk);
+  // The forward runs the same vocabulary chunks, one launch each, so its
+  // records take O(N * chunk / vt_rows), not O(N * V / vt_rows).
+  q.fwd_slices = (q.mode == kd::MODE_BOTH) ? q.n_slices : (int)std::min<int64_t>(q.n_vtiles, chunk / vt);
   q.merge_blocks = (int)ceil_div(q.n, kd::kMergeTok);
 
   const size_t elem = (q.dtype == KD_BF16) ? 2 : 4;
@@ -184,14 +187,18 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.off_prep = off;
   off = align_up(off + 4 * sizeof(float) * (size_t)q.n, 256);
   q.off_rec = off;
-  off = align_up(off + (size_t)kd::kRecFields * q.n_slices * (size_t)q.n * sizeof(float), 256);
+  off = align_up(off + (size_t)kd::kRecFields * q.fwd_slices * (size_t)q.n * sizeof(float), 256);
+  if (q.fwd_slices < q.n_slices) {
+    q.off_run = off;
+    off = align_up(off + (size_t)kd::kRecFields * (size_t)q.n * sizeof(float), 256);
+  }
   q.off_part = off;
   off = align_up(off + (size_t)q.merge_blocks * 4 * sizeof(double), 256);
   if (q.mode == kd::MODE_TOPK) {
     q.off_tks = off;
     off = align_up(off + 8 * (size_t)q.n * (size_t)q.k, 256);
     q.off_tko = off;
-    off = align_up(off + 4 * (size_t)q.n * (size_t)(q.n_vtiles + 1), 256);
+    off = align_up(off + 4 * (size_t)q.n * (size_t)(q.fwd_slices + 1), 256);
   }
   q.fwd_bytes = off;
   q.off_dz = off_common;

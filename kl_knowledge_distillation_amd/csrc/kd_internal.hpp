@@ -62,15 +62,19 @@ struct Plan {
   int vt_rows = 128;  // vocabulary rows per fused tile
   int n_ttiles = 0, n_vtiles = 0, tps = 1, n_slices = 0;  // forward grid
   int64_t row_slice = 0;  // row kernels: elements per slice (a whole number of steps)
+  // forward tiles: vocabulary tiles per launch (one chunk of `chunk` columns);
+  // with several launches each chunk's records are folded into a running record
+  int fwd_slices = 0;
   int64_t chunk = 0;  // backward vocabulary chunk (multiple of the fused tile rows)
   int64_t dz_rows = 0;  // rows of the logit-gradient slab: n rounded up to the token tile
   int n_chunks = 0;
   int merge_blocks = 0;
   // forward workspace layout (bytes from the workspace base)
   size_t off_prep = 0, off_rec = 0, off_part = 0, fwd_bytes = 0;
+  size_t off_run = 0;  // running record [kRecFields][n] (several forward launches)
   // top-K: each row's entries sorted by vocabulary index (int32 idx [n][k], then
-  // fp32 prob [n][k]) and where each vocabulary tile's entries start (int32
-  // [n][n_vtiles + 1])
+  // fp32 prob [n][k]) and where each vocabulary tile of one forward launch
+  // starts its run of them (int32 [n][fwd_slices + 1])
   size_t off_tks = 0, off_tko = 0;
   // backward workspace layout
   size_t off_dz = 0, bwd_bytes = 0;

@@ -75,6 +75,20 @@ __device__ __forceinline__ void stats_merge(RowStats& s, const RowStats& o) {
   merge_ms(s.mt1, s.st1, o.mt1, o.st1);
 }
 
+// A record's ten fields, `stride` floats apart (SoA records).
+__device__ __forceinline__ void rec_load(const float* r, int64_t stride, RowStats& o) {
+  o.mz1 = r[0 * stride]; o.sz1 = r[1 * stride]; o.mzT = r[2 * stride];
+  o.szT = r[3 * stride]; o.mtT = r[4 * stride]; o.stT = r[5 * stride];
+  o.a = r[6 * stride];   o.mt1 = r[7 * stride]; o.st1 = r[8 * stride];
+  o.ar = r[9 * stride];
+}
+__device__ __forceinline__ void rec_store(float* r, int64_t stride, const RowStats& o) {
+  r[0 * stride] = o.mz1; r[1 * stride] = o.sz1; r[2 * stride] = o.mzT;
+  r[3 * stride] = o.szT; r[4 * stride] = o.mtT; r[5 * stride] = o.stT;
+  r[6 * stride] = o.a;   r[7 * stride] = o.mt1; r[8 * stride] = o.st1;
+  r[9 * stride] = o.ar;
+}
+
 // Bit 4 mb + r of `ok`: register r of row block mb is a real vocabulary row.
 __device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int r) { return (ok >> (mb * 4 + r)) & 1u; }
 
@@ -369,8 +383,9 @@ struct FwdArgs {
   // vocabulary tile's entries start (prep_kernel)
   const int32_t* topk_sidx;  // [n, k]
   const float* topk_sprob;   // [n, k]
-  const int32_t* topk_off;   // [n, n_slices + 1]
+  const int32_t* topk_off;   // [n, n_slices + 1]: this launch's tiles
   int k;
+  int slice0;                // first vocabulary tile of this launch (n_slices tiles from it)
 };
 
 // Top-K: floats per token row of the z tile staged in LDS (the padding spreads
@@ -400,7 +415,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   int slice, tt;  // slice = the vocabulary tile of this workgroup
   grouped_tile(t, a.n_slices, n_tt, 8, slice, tt);
   const int64_t t0 = (int64_t)tt * G::kTT;
-  const int64_t v0 = (int64_t)slice * G::kVT;
+  const int64_t v0 = (int64_t)(a.slice0 + slice) * G::kVT;
 
   const T* hs = static_cast<const T*>(a.hs);
   const T* W = static_cast<const T*>(a.w);
@@ -616,12 +631,9 @@ struct PrepArgs {
   int want_teacher;  // teacher label logit needed (teacher CE weight or output)
   float* prep;       // [4][n]: z[y] | S, t[y] | E, M, flag
   // top-K: the row's entries sorted by index (an index outside [0, v) as v,
-  // last), and per vocabulary tile of vt_rows rows the first sorted entry at
-  // or past it ([n_vtiles + 1] per row, the last one past the valid entries)
+  // last)
   int32_t* sidx;
   float* sprob;
-  int32_t* toff;
-  int vt_rows, n_vtiles;
 };
 
 template <typename T>
@@ -641,13 +653,8 @@ __device__ __forceinline__ float wave_dot(const T* x, const T* y, int64_t len, i
   return s;
 }
 
-// Top-K rows of up to this many entries keep their sorted indices in LDS, where
-// the vocabulary tiles' first entries are found by binary search.
-constexpr int kTopkLdsK = 1024;
-
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
-  __shared__ int32_t skeys[(MODE == MODE_TOPK) ? (kThreads / 64) * kTopkLdsK : 1];
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (i >= a.n) return;
@@ -679,31 +686,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
       }
       a.sidx[i * a.k + rank] = (int32_t)kj;
       a.sprob[i * a.k + rank] = p;
-      if (a.k <= kTopkLdsK) skeys[(threadIdx.x >> 6) * kTopkLdsK + rank] = (int32_t)kj;
-    }
-    // tile vt's entries start at the number of keys below min(vt vt_rows, v)
-    if (a.k <= kTopkLdsK) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int32_t* sk = skeys + (threadIdx.x >> 6) * kTopkLdsK;
-      for (int vt = lane; vt <= a.n_vtiles; vt += 64) {
-        const int64_t lo = min((int64_t)vt * a.vt_rows, a.v);
-        int l = 0, h = a.k;  // first position with key >= lo
-        while (l < h) {
-          const int m = (l + h) >> 1;
-          if ((int64_t)sk[m] < lo) l = m + 1;
-          else h = m;
-        }
-        a.toff[i * (a.n_vtiles + 1) + vt] = l;
-      }
-    } else {
-      for (int vt = lane; vt <= a.n_vtiles; vt += 64) {
-        const int64_t lo = min((int64_t)vt * a.vt_rows, a.v);
-        int c = 0;
-        for (int jj = 0; jj < a.k; ++jj) c += (key(jj) < lo) ? 1 : 0;
-        a.toff[i * (a.n_vtiles + 1) + vt] = c;
-      }
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -742,6 +724,34 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
     a.prep[2 * a.n + i] = f2;
     a.prep[3 * a.n + i] = flag;
   }
+}
+
+// Top-K, one forward launch (vocabulary tiles slice0 .. slice0 + n_slices):
+// where each tile's run of a row's index-sorted entries starts, by binary
+// search, off[i][j] = #{entries of row i with index < min((slice0 + j) vt, v)},
+// j = 0 .. n_slices (the last one closes the last tile's run).
+struct TileStartArgs {
+  const int32_t* sidx;  // [n, k] sorted; an index outside [0, v) stored as v
+  int64_t n, v;
+  int k, vt_rows, slice0, n_slices;
+  int32_t* off;         // [n, n_slices + 1]
+};
+
+__global__ __launch_bounds__(kThreads) void topk_tile_starts_kernel(TileStartArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t per = a.n_slices + 1;
+  if (e >= a.n * per) return;
+  const int64_t i = e / per;
+  const int j = (int)(e - i * per);
+  const int64_t lo = min((int64_t)(a.slice0 + j) * a.vt_rows, a.v);
+  const int32_t* sk = a.sidx + i * a.k;
+  int l = 0, h = a.k;  // the first position with index >= lo
+  while (l < h) {
+    const int m = (l + h) >> 1;
+    if ((int64_t)sk[m] < lo) l = m + 1;
+    else h = m;
+  }
+  a.off[e] = l;
 }
 
 // ---------------------------------------------------------------------------
@@ -1117,6 +1127,7 @@ struct MergeArgs {
   const float* rec;
   const float* prep;
   int n_slices;
+  const float* prior;  // non-null: the running record of the earlier chunks ([kRecFields][n])
   int64_t n;
   int mode;
   float T;
@@ -1148,14 +1159,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   RowStats s;
   stats_init(s);
   if (has) {
+    if (sg == 0 && a.prior) rec_load(a.prior + col, a.n, s);
     const int64_t stride = (int64_t)a.n_slices * a.n;
     for (int sl = sg; sl < a.n_slices; sl += kGroups) {
-      const float* r = a.rec + (int64_t)sl * a.n + col;
       RowStats o;
-      o.mz1 = r[0 * stride]; o.sz1 = r[1 * stride]; o.mzT = r[2 * stride];
-      o.szT = r[3 * stride]; o.mtT = r[4 * stride]; o.stT = r[5 * stride];
-      o.a = r[6 * stride];   o.mt1 = r[7 * stride]; o.st1 = r[8 * stride];
-      o.ar = r[9 * stride];
+      rec_load(a.rec + (int64_t)sl * a.n + col, stride, o);
       stats_merge(s, o);
     }
   }
@@ -1246,6 +1254,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     p[1] = t1;
     p[2] = t2;
     p[3] = 0.0;
+  }
+}
+
+// One vocabulary chunk's records folded into the running record (the first
+// chunk starts it). Laid out like the merge: 16 tokens per workgroup, 16
+// groups of slices; group 0 starts from the running record, each group adds
+// its slices in order, then the groups in order.
+struct FoldArgs {
+  const float* rec;  // [kRecFields][n_slices][n]
+  int n_slices;
+  float* run;        // [kRecFields][n]
+  int64_t n;
+  int first;
+};
+
+__global__ __launch_bounds__(kMergeThreads) void fold_kernel(FoldArgs a) {
+  constexpr int kGroups = kMergeThreads / kMergeTok;
+  __shared__ RowStats part[kGroups][kMergeTok];
+  const int tid = threadIdx.x, tl = tid % kMergeTok, sg = tid / kMergeTok;
+  const int64_t i = (int64_t)blockIdx.x * kMergeTok + tl;
+  RowStats s;
+  stats_init(s);
+  if (i < a.n) {
+    if (sg == 0 && !a.first) rec_load(a.run + i, a.n, s);
+    const int64_t stride = (int64_t)a.n_slices * a.n;
+    for (int sl = sg; sl < a.n_slices; sl += kGroups) {
+      RowStats o;
+      rec_load(a.rec + (int64_t)sl * a.n + i, stride, o);
+      stats_merge(s, o);
+    }
+  }
+  part[sg][tl] = s;
+  __syncthreads();
+  if (sg == 0 && i < a.n) {
+    for (int q = 1; q < kGroups; ++q) stats_merge(s, part[q][tl]);
+    rec_store(a.run + i, a.n, s);
   }
 }
 
@@ -1904,8 +1948,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   float* tk_prob = reinterpret_cast<float*>(base + p.off_tks + 4 * (size_t)p.n * (size_t)p.k);
   int32_t* tk_off = reinterpret_cast<int32_t*>(base + p.off_tko);
   PrepArgs pa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, x.labels, x.topk_idx, x.topk_prob,
-              p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, prep, tk_idx, tk_prob, tk_off, p.vt_rows,
-              p.n_vtiles};
+              p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, prep, tk_idx, tk_prob};
   pa.want_teacher = p.mode != MODE_TOPK && (p.wt > 0.f || (out && out->teacher_ce));
   const dim3 pgrid((unsigned)((p.n + 3) / 4));
   KD_TRY(L.run(KD_KERNEL_PREP, [&] {
@@ -1928,8 +1971,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   FwdArgs fa{cp.hs, x.w, cp.ht, x.wt, x.logits, x.tlogits, p.n, p.d, p.dt, p.v,
              p.n_ttiles, p.n_vtiles, p.tps, p.n_slices, kLog2e / p.T, kLog2e / p.Tt, p.T / p.Tt,
              p.need_zT, need_t1, p.kl, given_mode<T, G>(given, p.v),
-             (p.T == 2.f && p.need_zT) ? 1 : 0, rec, cp.nv, tk_idx, tk_prob, tk_off, p.k};
-  const dim3 fgrid((unsigned)((int64_t)p.n_slices * p.n_ttiles));
+             (p.T == 2.f && p.need_zT) ? 1 : 0, rec, cp.nv, tk_idx, tk_prob, tk_off, p.k, 0};
+  float* run = reinterpret_cast<float*>(base + p.off_run);
+  const bool folded = p.fwd_slices < p.n_slices;  // several forward launches
+  int last_slices = p.fwd_slices;                 // records of the last launch
   if (p.mode == MODE_BOTH) {
     RowArgs ra{};
     ra.zl = x.logits;
@@ -1947,18 +1992,40 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
     KD_TRY(L.run(KD_KERNEL_FWD, [&] {
       rowstats_launch<T>(row_z1(p.T), p.kl != KD_KL_FORWARD, need_t1 != 0, grid, stream, ra);
     }));
-  } else
-  KD_TRY(L.run(KD_KERNEL_FWD, [&] {
-    switch (p.mode) {
-      case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
-      case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
-      case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
-      case MODE_TLOGITS: fwd_tiles_kernel<T, MODE_TLOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
-      default: fwd_tiles_kernel<T, MODE_LOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+  } else {
+    // one launch per vocabulary chunk of fwd_slices tiles
+    for (int s0 = 0; s0 < p.n_vtiles; s0 += p.fwd_slices) {
+      fa.slice0 = s0;
+      fa.n_slices = std::min(p.fwd_slices, p.n_vtiles - s0);
+      const dim3 fgrid((unsigned)((int64_t)fa.n_slices * p.n_ttiles));
+      if (p.mode == MODE_TOPK) {
+        const TileStartArgs ts{tk_idx, p.n, p.v, p.k, p.vt_rows, s0, fa.n_slices, tk_off};
+        const int64_t cnt = p.n * (int64_t)(fa.n_slices + 1);
+        KD_TRY(L.run(KD_KERNEL_PREP, [&] {
+          topk_tile_starts_kernel<<<dim3((unsigned)((cnt + kThreads - 1) / kThreads)), kThreads, 0,
+                                    stream>>>(ts);
+        }));
+      }
+      KD_TRY(L.run(KD_KERNEL_FWD, [&] {
+        switch (p.mode) {
+          case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          case MODE_TLOGITS: fwd_tiles_kernel<T, MODE_TLOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          default: fwd_tiles_kernel<T, MODE_LOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+        }
+      }));
+      last_slices = fa.n_slices;
+      if (s0 + fa.n_slices < p.n_vtiles) {  // the last chunk goes to the merge itself
+        const FoldArgs fo{rec, fa.n_slices, run, p.n, s0 == 0 ? 1 : 0};
+        KD_TRY(L.run(KD_KERNEL_MERGE, [&] {
+          fold_kernel<<<dim3((unsigned)p.merge_blocks), kMergeThreads, 0, stream>>>(fo);
+        }));
+      }
     }
-  }));
+  }
 
-  MergeArgs ma{rec, prep, p.n_slices, p.n, p.mode, p.T, p.need_zT, need_t1,
+  MergeArgs ma{rec, prep, last_slices, folded ? run : nullptr, p.n, p.mode, p.T, p.need_zT, need_t1,
                (p.mode != MODE_TOPK) ? 1 : 0, p.kl, p.ws, p.wt, p.wkl,
                out ? out->student_ce : nullptr, out ? out->teacher_ce : nullptr,
                out ? out->kl : nullptr, static_cast<float*>(saved), part, cp.pos};

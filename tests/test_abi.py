@@ -93,20 +93,31 @@ def test_status_strings():
 
 def test_workspace_sizes_are_valid_and_monotone_in_chunk():
     s, t, p = _desc()
-    prev_bwd = 0
+    prev_fwd = prev_bwd = 0
     for chunk in (128, 1024, 2048, 8192):
         p.vocab_chunk = chunk
         st, fwd = _ws(s, t, p, 0)
         assert st == L.KD_OK and fwd > 0
         st, bwd = _ws(s, t, p, 1)
         assert st == L.KD_OK
-        assert bwd >= prev_bwd  # the dz slab grows with the chunk (until it covers V)
-        prev_bwd = bwd
-    # forward records: one per (vocabulary tile, token), whatever the chunk
-    p.vocab_chunk = 128
-    small = _ws(s, t, p, 0)[1]
-    p.vocab_chunk = 2048
-    assert _ws(s, t, p, 0)[1] == small
+        # the dz slab and the forward's records of one chunk grow with the
+        # chunk (until it covers V)
+        assert bwd >= prev_bwd and fwd >= prev_fwd
+        prev_fwd, prev_bwd = fwd, bwd
+
+
+def test_forward_workspace_is_O_n_chunk_not_n_vocab():
+    # top-K shape: records of one chunk's vocabulary tiles (10 fp32 per token
+    # and tile) plus the sorted top-K entries, far below n * v * 4
+    s, t, p = _desc("topk", n=32768, d=4096, v=151936, k=100)
+    p.vocab_chunk = 8192
+    st, fwd = _ws(s, t, p, 0)
+    assert st == L.KD_OK
+    n, k, tiles = 32768, 100, 8192 // 256
+    records = 10 * 4 * n * (tiles + 1)
+    assert fwd <= records + 8 * n * k + 4 * n * (tiles + 1) + 16 * n + (1 << 20)
+    p.vocab_chunk = 16384
+    assert _ws(s, t, p, 0)[1] > fwd
 
 
 def test_backward_workspace_is_O_n_chunk_not_n_vocab():

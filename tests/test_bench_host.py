@@ -11,7 +11,7 @@ def test_method_flops_tied_quickstart():
     w = WORKLOADS["quickstart_tied_bf16"]
     n, d, v = w.n, w.d, w.v
     f = bench.method_flops(w)
-    assert f["fwd_per_launch"] == 4 * n * d * v
+    assert f["fwd"] == 4 * n * d * v
     assert f["total"] == 12 * n * d * v
     assert f["useful"] == 8 * n * d * v
 
@@ -28,15 +28,15 @@ def test_method_flops_scorer_is_forward_only():
     # given student logits, teacher projection only, no backward
     w = WORKLOADS["scorer_bf16"]
     f = bench.method_flops(w)
-    assert f["total"] == f["useful"] == f["fwd_per_launch"] == 2 * w.n * w.d_t * w.v
+    assert f["total"] == f["useful"] == f["fwd"] == 2 * w.n * w.d_t * w.v
 
 
-@pytest.mark.parametrize("kernel", ["bwd_dz", "gemm_dwdh"])
+@pytest.mark.parametrize("kernel", ["fwd", "bwd_dz", "gemm_dwdh"])
 def test_chunk_launch_flops_add_up(kernel):
     # the per-launch flops of a chunked kernel, summed over the chunks of a step
     w = WORKLOADS["quickstart_tied_bf16"]
     chunk = 16384
     n_chunks = -(-w.v // chunk)
     per = bench.kernel_flops_per_launch(w, kernel, chunk)
-    want = 4 * w.n * w.d * w.v  # recompute of both projections, or dW + dH
+    want = 4 * w.n * w.d * w.v  # both projections (fwd, or their recompute), or dW + dH
     assert abs(per * n_chunks - want) <= 1e-9 * want
