@@ -54,6 +54,24 @@ def test_scorer_chunk_sweep(chunk):
     full_parity(C5.scaled(n=256, d_t=256, v=9000), vocab_chunk=chunk)
 
 
+# Vocabulary spread over several forward launches (their records folded into a
+# running record between launches), for every tile mode.
+CHUNKED_FORWARD = {
+    "topk": (C4.scaled(n=300, d=512, v=5000), 1024),
+    "topk_staged": (C4.scaled(n=129, d=264, v=1031, k=7), 256),
+    "separate_T2": (C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=2.0), 512),
+    "tied_compact": (C2.scaled(n=300, d=512, v=3000, ignore_frac=0.3, compact_valid=True), 768),
+    "tied_jeffreys": (C2.scaled(n=260, d=256, v=2100, kl_divergence="jeffreys"), 512),
+    "dense_teacher_logits": (C6.scaled(n=200, d=256, v=2000), 512),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNKED_FORWARD))
+def test_chunked_forward(name):
+    w, chunk = CHUNKED_FORWARD[name]
+    full_parity(w.scaled(name=f"{w.name}_{name}"), vocab_chunk=chunk)
+
+
 def test_reductions_and_normalizer():
     w = C2.scaled(n=200, d=256, v=1500)
     x = make_inputs(w, "cuda", seed=3)
