@@ -137,9 +137,11 @@ typedef struct {
   int64_t ignore_index;      /* label value excluded from CE and from the loss */
   int32_t reduction;         /* KD_REDUCE_* */
   float normalizer;          /* > 0: divide the summed loss by it (num_batch_labels) */
-  int64_t vocab_chunk;       /* vocabulary columns per backward chunk, rounded up to whole tiles;
-                                the dz slab holds n x chunk; 0 = library default (16384,
-                                flash_kd's chunk_size default) */
+  int64_t vocab_chunk;       /* vocabulary columns per chunk, rounded up to whole tiles; 0 =
+                                library default (16384, flash_kd's chunk_size default). The
+                                backward's dz slab holds n x chunk; the forward runs one tile
+                                launch per chunk and keeps one chunk's tile records (40 bytes
+                                per token and 256 columns). */
   int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
   int32_t kl_divergence;     /* KD_KL_* */
   float teacher_temperature; /* T_t > 0, finite: the teacher's own temperature (orda-kernel,
