@@ -295,67 +295,56 @@ __device__ __forceinline__ void load_logits_tile(const T* L, int64_t n, int64_t 
   }
 }
 
-// Given bf16 logits staged through LDS (pipelined geometry). The [128 x 256]
-// tile (128 token rows of 256 vocabulary entries) is copied with buffer loads
-// straight into LDS by the four group-A waves before the main loop: those waves
-// issue no main-loop copies and never wait on them, so these copies land while
-// the MFMAs run. After the main loop every wave reads its registers in the
-// accumulator layout. Image: token row tr is 32 chunks of 16 bytes, chunk c at
-// position c ^ (tr & 15), so the 16 tokens of one ds_read_b64 fall in 16
-// distinct 16-byte bank groups. Needs v a multiple of 8 and a 16-byte aligned
-// matrix (every chunk is then one aligned 16-byte load).
-constexpr int kGivenTokens = 128, kGivenVocab = 256;
-constexpr int kGivenBytes = kGivenTokens * kGivenVocab * 2;  // 64 KB
-
-__device__ __forceinline__ void given_tile_copy(const bf16_t* L, int64_t n, int64_t v, int64_t t0,
-                                                int64_t v0, uint8_t* img, int gw, int lane) {
-  const int64_t rows = (n - t0 < kGivenTokens) ? (n - t0) : kGivenTokens;
-  const rsrc_t r = make_rsrc(L + t0 * v, rows * v * 2);  // token rows past n read zeros
-  const uint32_t row_bytes = (uint32_t)(v * 2);
-  const int h = lane >> 5;
+// Given bf16 logits kept in registers across the main loop (pipelined
+// geometry): every wave loads its own part of the tile, still packed (two
+// bf16 per register), before the main loop, so the loads land under the
+// MFMAs and the LDS stays free for the copy slots and the prefetch. `vec`: v a
+// multiple of 4 and the matrix 8-byte aligned (one 8-byte load per lane and
+// block); otherwise element loads. Tokens past n and rows past v read 0.
+// (Staging the tile through LDS with buffer loads instead left no LDS for the
+// cooperative prefetch and measured 2-4% slower.)
+typedef uint2 GivenRaw[kMB][kNB];
+__device__ __forceinline__ void given_raw_load(const bf16_t* L, int64_t n, int64_t v, int64_t t0,
+                                               int64_t v0, int wm, int wn, int lane, bool vec,
+                                               GivenRaw& raw) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int j = gw * 16 + i;  // 1 KB block j: token rows 2 j and 2 j + 1
-    const int tr = 2 * j + h;
-    const int c = (lane & 31) ^ (tr & 15);
-    const uint32_t voff = (uint32_t)h * row_bytes + (uint32_t)c * 16u;
-    const uint32_t soff = (uint32_t)(2 * j) * row_bytes + (uint32_t)(v0 * 2);
-    buffer_copy_stream(r, img + j * 1024, voff, soff);
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int64_t tok = t0 + acc_col(wn, nb, lane);
+    const bool live = tok < n;
+    const int64_t base = live ? tok * v : 0;
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      const int64_t vv = v0 + acc_row(wm, mb, 0, lane);
+      if (live && vec && vv + 4 <= v) {
+        raw[mb][nb] = *reinterpret_cast<const uint2*>(L + base + vv);
+      } else {
+        uint32_t e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = (live && vv + r < v) ? (uint32_t)L[base + vv + r] : 0u;
+        raw[mb][nb] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+      }
+    }
   }
 }
 
-__device__ __forceinline__ void given_tile_read(const uint8_t* img, int wm, int wn, int lane, WaveAcc& out) {
+__device__ __forceinline__ void given_raw_unpack(const GivenRaw& raw, WaveAcc& out) {
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int tr = acc_col(wn, nb, lane);
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      const int vl = acc_row(wm, mb, 0, lane);
-      const uint2 u = *reinterpret_cast<const uint2*>(img + tr * (kGivenVocab * 2) +
-                                                      (((vl >> 3) ^ (tr & 15)) << 4) + (vl & 7) * 2);
+    for (int nb = 0; nb < kNB; ++nb) {
+      const uint2 u = raw[mb][nb];
       out[mb][nb][0] = __uint_as_float(u.x << 16);
       out[mb][nb][1] = __uint_as_float(u.x & 0xffff0000u);
       out[mb][nb][2] = __uint_as_float(u.y << 16);
       out[mb][nb][3] = __uint_as_float(u.y & 0xffff0000u);
     }
-  }
 }
 
-// Given logits of this tile: staged through LDS (flag 2, pipelined geometry;
-// `stage` already issued its copies and the main loop has ended), else loaded
-// from memory (flag 1: 4-element vectors, 0: elements).
-template <typename T, class G>
+// Given logits of this tile in the staged geometry, loaded after the main
+// loop (flag 1: 4-element vectors, 0: elements).
+template <typename T>
 __device__ __forceinline__ void given_tile(const T* L, int64_t n, int64_t v, int64_t t0, int64_t v0,
-                                           int flag, const uint8_t* img, int w, int wm, int wn,
-                                           int lane, WaveAcc& out) {
-  if constexpr (G::kPipe) {
-    if (flag == 2) {
-      if (w < 4) wait_vmcnt<0>();  // group A issued the copies
-      pipe_barrier();
-      given_tile_read(img, wm, wn, lane, out);
-      return;
-    }
-  }
+                                           int flag, int wm, int wn, int lane, WaveAcc& out) {
   load_logits_tile<T>(L, n, v, t0, v0, wm, wn, lane, flag != 0, out);
 }
 
@@ -375,7 +364,7 @@ struct FwdArgs {
   float cT, cTt, rho;   // log2(e) / T_s, log2(e) / T_t, T_s / T_t
   int need_zT, need_t1;
   int kl;      // KD_KL_*: the reverse direction also needs sum 2^(z~ - m) (z - t)
-  int vec;     // given logits: 2 staged through LDS, 1 vector loads, 0 element loads
+  int vec;     // given logits: given_mode (3 / 4 registers, 1 vector loads, 0 element loads)
   int sqz;     // T_s == 2: the T = 1 student sums are the squares of those at T
   float* rec;  // [kRecFields][n_slices][n]
   const int32_t* nv;  // compacted rows: their number (tiles past it exit); null = n
@@ -401,10 +390,11 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   // top-K: the fp32 z tile [kTT][zstride] after the main loop, then the tile's
   // cross terms [kTT] past the epilogue's exchange area
   constexpr int kTopkBytes = (MODE == MODE_TOPK) ? G::kTT * topk_zstride<G>() * 4 : 0;
-  // pipelined tiles with no given logits tile (which fills the LDS): 1 KB past
-  // the slots where the prefetch reads land
-  constexpr bool kPf = G::kPipe && !kGiven && kPipeAhead > 0;
-  constexpr int kLdsMain = kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0) + (kPf ? 1024 : 0);
+  // pipelined tiles: 1 KB past the slots where the prefetch reads land; a
+  // given logits tile is held in registers
+  constexpr bool kGivenRegs = kGiven && G::kPipe;
+  constexpr bool kPf = G::kPipe && kPipeAhead > 0;
+  constexpr int kLdsMain = kMainBytes + (kPf ? 1024 : 0);
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsMain > kTopkBytes ? kLdsMain : kTopkBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: only the token tiles below nv have work; they are mapped
@@ -442,20 +432,28 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
-    if constexpr (G::kPipe)
-      if (a.vec == 2 && w < 4)
-        given_tile_copy(L, a.n, a.v, t0, v0, lds + kMainBytes, __builtin_amdgcn_readfirstlane(w), lane);
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, tacc[0]);
+    if constexpr (kGivenRegs) {
+      GivenRaw raw;
+      given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      given_raw_unpack(raw, tacc[0]);
+    } else {
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+      given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
+    }
   } else {  // MODE_LOGITS
     const T* L = static_cast<const T*>(a.logits);
-    if constexpr (G::kPipe)
-      if (a.vec == 2 && w < 4)
-        given_tile_copy(L, a.n, a.v, t0, v0, lds + kMainBytes, __builtin_amdgcn_readfirstlane(w), lane);
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-    given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, zl);
+    if constexpr (kGivenRegs) {
+      GivenRaw raw;
+      given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
+      given_raw_unpack(raw, zl);
+    } else {
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
+      given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, zl);
+    }
   }
 
   // Epilogue: this tile's statistics of every token, in two passes over the
@@ -1361,7 +1359,7 @@ struct BwdArgs {
   float wtce;             // teacher-CE weight (MODE_TCE)
   int need_zT;
   int kl;                 // KD_KL_*
-  int vec;                // teacher logits: 2 staged through LDS, 1 vector loads, 0 element loads
+  int vec;                // teacher logits: given_mode (3 / 4 registers, 1 / 0 after the loop)
   int sqz;                // T_s == 2: softmax(z) is the square of one exponential of z/T
   const int32_t* idx;     // compacted rows: original row of each (null: rows are original)
   const int32_t* nv;      // compacted rows: their number
@@ -1391,9 +1389,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
   constexpr bool kGiven = MODE == MODE_TLOGITS;
   constexpr int kMainBytes = G::template lds_bytes<NB>();
-  constexpr bool kPf = G::kPipe && !kGiven && kPipeAhead > 0;  // prefetch reads: 1 KB
-  __shared__ __attribute__((aligned(16))) uint8_t
-      lds[kMainBytes + ((kGiven && G::kPipe) ? kGivenBytes : 0) + (kPf ? 1024 : 0)];
+  constexpr bool kGivenRegs = kGiven && G::kPipe;  // a given logits tile in registers
+  constexpr bool kPf = G::kPipe && kPipeAhead > 0;  // prefetch reads: 1 KB
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + (kPf ? 1024 : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: token tiles from round_up(nv, 128) on would hold only zero
   // rows, which no GEMM reads (their K and M stop at nv); only the tiles below
@@ -1425,12 +1423,16 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
-    if constexpr (G::kPipe)
-      if (a.vec == 2 && w < 4)
-        given_tile_copy(L, a.n, a.v, t0, v0, lds + kMainBytes, __builtin_amdgcn_readfirstlane(w), lane);
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    given_tile<T, G>(L, a.n, a.v, t0, v0, a.vec, lds + kMainBytes, w, wm, wn, lane, tacc[0]);
+    if constexpr (kGivenRegs) {
+      GivenRaw raw;
+      given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      given_raw_unpack(raw, tacc[0]);
+    } else {
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
+      given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
+    }
   } else if constexpr (MODE == MODE_TCE) {  // the teacher tile alone
     const T* const bt[1] = {ht};
     tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, acc, tid, pf);
@@ -1895,15 +1897,15 @@ void logits_bwd_launch(int z1, bool ce, bool rev, dim3 grid, hipStream_t stream,
   else logits_bwd_launch<T, kZ1Own>(true, rev, grid, stream, ra);
 }
 
-// How a given [n x v] logits matrix is read: 2 = staged through LDS with
-// 16-byte buffer loads (pipelined bf16 tiles: v a multiple of 8, 16-byte
-// aligned, v up to 2^23), 1 = a lane's four consecutive elements as one vector (v a multiple
-// of 4, vector-aligned), 0 = element by element.
+// How a given [n x v] logits matrix is read: pipelined bf16 tiles hold it in
+// registers from before the main loop (3: 8-byte vector loads, v a multiple of
+// 4 and the matrix 8-byte aligned; 4: element loads); staged tiles load it
+// after the main loop (1: a lane's four consecutive elements as one vector, v
+// a multiple of 4 and vector-aligned; 0: element by element).
 template <typename T, class G>
 int given_mode(const void* ptr, int64_t v) {
   if (ptr == nullptr) return 0;
-  // (the copy offsets of a 128-row tile are 32-bit: 128 rows of 2 v bytes)
-  if (G::kPipe && sizeof(T) == 2 && v % 8 == 0 && v <= (1 << 23) && (uintptr_t)ptr % 16 == 0) return 2;
+  if (G::kPipe && sizeof(T) == 2) return (v % 4 == 0 && (uintptr_t)ptr % 8 == 0) ? 3 : 4;
   return (v % 4 == 0 && ((uintptr_t)ptr % (4 * sizeof(T))) == 0) ? 1 : 0;
 }
 

@@ -87,13 +87,6 @@ __device__ __forceinline__ void buffer_copy(rsrc_t r, uint8_t* dst, uint32_t vof
                                            soff, 0, 0);
 }
 
-// The same for data read once: nontemporal (cache policy bit 1, "nt" on gfx950).
-__device__ __forceinline__ void buffer_copy_stream(rsrc_t r, uint8_t* dst, uint32_t voff,
-                                                   uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
-                                           soff, 0, 2);
-}
-
 // A K-contiguous bf16 operand: element (row, k) at ptr[row * ld + k], rows < `rows`.
 struct PipeOperand {
   const bf16_t* ptr;
