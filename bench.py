@@ -31,13 +31,15 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
-def method_flops(w, train_teacher: bool = False, n_rows: int = 0) -> dict:
+def method_flops(w, train_teacher: bool = False, n_rows: int = 0, kept_cols: int = 0) -> dict:
     """Algorithmic MFMA flops of one fwd+bwd step and of one launch of each kernel.
 
     Forward projection tiles: 2 N D V per student GEMM and per teacher GEMM;
     the backward recomputes them, then dW and dH cost 2 N D V each. A teacher
     trained through its CE adds its recompute, dW_t and dH_t: 6 N D_t V.
     n_rows: the rows projected (the usable-label rows when they are compacted).
+    kept_cols: columns of the last chunk whose products the forward kept; the
+    backward recomputes the other V - kept_cols (the teacher's too when trained).
     """
     n, d, v, dt = (n_rows or w.n), w.d, w.v, w.teacher_dim
     if w.teacher == "tied":
@@ -48,18 +50,29 @@ def method_flops(w, train_teacher: bool = False, n_rows: int = 0) -> dict:
         fwd = 2 * n * d * v
     if w.forward_only:  # a scorer: the forward tiles are the whole step
         return {"total": fwd, "useful": fwd, "fwd": fwd}
-    total = 2 * fwd + 4 * n * d * v
+    recomputed = (v - kept_cols) / v
+    total = fwd + fwd * recomputed + 4 * n * d * v
     useful = fwd + 4 * n * d * v
     if train_teacher:
-        total += 6 * n * dt * v
+        total += 2 * n * dt * v * recomputed + 4 * n * dt * v
         useful += 4 * n * dt * v
     return {"total": total, "useful": useful, "fwd": fwd}
 
 
+def kept_columns(w, chunk: int, keep: bool) -> int:
+    """Columns of the last vocabulary chunk when the forward keeps its products
+    for the backward (projection students with a backward), else 0."""
+    if not keep or w.forward_only or w.student == "logits":
+        return 0
+    return w.v - (-(-w.v // chunk) - 1) * chunk
+
+
 def kernel_flops_per_launch(w, kernel: str, chunk: int, n_rows: int = 0,
-                            train_teacher: bool = False) -> float:
+                            train_teacher: bool = False, kept_cols: int = 0) -> float:
     """Flops of one launch of `kernel`; with a trained teacher the launches of a
-    class alternate between the student's and the teacher's, so the mean."""
+    class alternate between the student's and the teacher's, so the mean.
+    With a kept last chunk the recomputing bwd_dz launches are the full chunks
+    before it."""
     n, d, v, dt = (n_rows or w.n), w.d, w.v, w.teacher_dim
     fl = method_flops(w, n_rows=n)
     n_chunks = -(-v // chunk)
@@ -67,8 +80,9 @@ def kernel_flops_per_launch(w, kernel: str, chunk: int, n_rows: int = 0,
         return fl["fwd"] / n_chunks
     per_chunk_cols = v / n_chunks  # average columns per launch
     if kernel == "bwd_dz":
-        f = fl["fwd"] * per_chunk_cols / v
-        return (f + 2 * n * dt * per_chunk_cols) / 2 if train_teacher else f
+        cols = chunk if kept_cols else per_chunk_cols
+        f = fl["fwd"] * cols / v
+        return (f + 2 * n * dt * cols) / 2 if train_teacher else f
     if kernel in ("gemm_dw", "gemm_dh", "gemm_dwdh"):
         f = 2 * n * d * per_chunk_cols
         if train_teacher:
@@ -109,7 +123,8 @@ def traffic_for(kernel: str, workload: str):
 
 _KERNEL_CLASS = (("prep_kernel", "prep"), ("fwd_tiles_kernel", "fwd"), ("merge_kernel", "merge"),
                  ("fold_kernel", "merge"),
-                 ("finalize_kernel", "finalize"), ("bwd_dz_kernel", "bwd_dz"),
+                 ("finalize_kernel", "finalize"), ("GeoPipe, true>", "bwd_kept"),
+                 ("GeoStaged, true>", "bwd_kept"), ("bwd_dz_kernel", "bwd_dz"),
                  ("scatter_kernel", "scatter"), ("gemm_pipe_kernel<false, false", "gemm_dw"),
                  ("gemm_pipe_kernel<true, false", "gemm_dh"), ("gemm_kernel<float, false, false", "gemm_dw"),
                  ("gemm_kernel<unsigned short, false, false", "gemm_dw"),
@@ -246,6 +261,8 @@ def main() -> int:
                     help="leave rows with an ignored label out of the projections (compact_valid)")
     ap.add_argument("--kl", choices=("forward", "reverse", "jeffreys"), default=None,
                     help="override the workload's KL direction")
+    ap.add_argument("--recompute-last-chunk", action="store_true",
+                    help="keep_last_chunk off: the backward recomputes every chunk's products")
     ap.add_argument("--train-teacher", action="store_true",
                     help="teacher trained through its CE (weight 1): the step adds its backward")
     ap.add_argument("--ignore-frac", type=float, default=None,
@@ -310,7 +327,8 @@ def main() -> int:
               temperature=w.temperature, ignore_index=w.ignore_index,
               vocab_chunk=args.vocab_chunk, want_grads=not w.forward_only,
               kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature,
-              compact_valid=w.compact_valid)
+              compact_valid=w.compact_valid,
+              keep_last_chunk=False if args.recompute_last_chunk else None)
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:
@@ -393,14 +411,15 @@ def main() -> int:
     if w.compact_valid and x["labels"] is not None:
         y = x["labels"]
         n_rows = int(((y != w.ignore_index) & (y >= 0) & (y < w.v)).sum().item())
-    fl = method_flops(w, args.train_teacher, n_rows)
-    peak_tflops = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
-    tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     # the backward chunk the library used (same rule as the C ABI's default)
     chunk = args.vocab_chunk if args.vocab_chunk > 0 else 16384
     chunk = min(-(-chunk // 128) * 128, -(-w.v // 128) * 128)
+    kept = kept_columns(w, chunk, not args.recompute_last_chunk)
+    fl = method_flops(w, args.train_teacher, n_rows, kept)
+    peak_tflops = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
+    tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     launch_ms = sum(durs) / len(durs) if durs else float("nan")
-    kflops = kernel_flops_per_launch(w, dominant, chunk, n_rows, args.train_teacher)
+    kflops = kernel_flops_per_launch(w, dominant, chunk, n_rows, args.train_teacher, kept)
     achieved = kflops / (launch_ms / 1e3) / 1e12 if durs else None
     rec = {
         "metric": "fused LM-head+CE+KL fwd+bwd tokens/s" if not w.forward_only
@@ -421,7 +440,8 @@ def main() -> int:
                    "teacher_temperature": w.teacher_temperature, "kl_divergence": w.kl_divergence,
                    "compact_valid": w.compact_valid, "ignored_rows": w.ignore_frac,
                    "train_teacher": bool(args.train_teacher), "projected_rows": n_rows,
-                   "top_k": w.k or None, "vocab_chunk": chunk, "parallelism": "single GPU"},
+                   "top_k": w.k or None, "vocab_chunk": chunk, "keep_last_chunk": kept > 0,
+                   "parallelism": "single GPU"},
         "mfma_tflops": round(tflops, 1),
         "mfma_frac_of_peak": round(tflops / peak_tflops, 4),
         "useful_tflops": round(fl["useful"] / (ms_per_step / 1e3) / 1e12, 1),

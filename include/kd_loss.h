@@ -153,6 +153,19 @@ typedef struct {
                                 only (else KD_ERR_UNSUPPORTED); workspaces grow by
                                 8 n + 16 ceil(n/128) (d + d_t) bytes (bf16). 0: every row is
                                 projected and its KL reported. */
+  int32_t keep_last_chunk;   /* 1: kd_loss_fwd also writes the fp32 products of its last
+                                vocabulary chunk (student, and the teacher's for TIED and
+                                SEPARATE teachers) into `saved`, and the backward calls read
+                                them there instead of recomputing that chunk's products. The
+                                chunk runs last in the forward and its products are the same
+                                accumulators either way, so every result is bit-identical to
+                                keep_last_chunk = 0; saved grows to kd_saved_bytes_for (4 bytes
+                                per token row, rounded up to 128 rows, per column of the last
+                                chunk rounded up to whole tiles, per product). Takes effect for
+                                PROJECTION students when `saved` is given; no effect otherwise.
+                                0: saved is kd_saved_bytes(n) and the backward recomputes every
+                                chunk (CompactifAI/Full-Chunked-KL-Loss, Full Chunked KL:
+                                logits are recomputed chunk by chunk in the backward). */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).
@@ -180,7 +193,8 @@ enum {
   KD_KERNEL_SCATTER = 5,   /* top-K: subtract p at the cached indices */
   KD_KERNEL_GEMM_DW = 6,   /* dW[chunk] = dZ_chunk^T H */
   KD_KERNEL_GEMM_DH = 7,   /* dH += dZ_chunk W[chunk] */
-  KD_KERNEL_GEMM_DWDH = 8  /* both GEMMs of a chunk in one launch */
+  KD_KERNEL_GEMM_DWDH = 8, /* both GEMMs of a chunk in one launch */
+  KD_KERNEL_BWD_KEPT = 9   /* logit-gradient epilogue on the kept last chunk (keep_last_chunk) */
 };
 typedef struct {
   void** events;     /* host array of hipEvent_t */
@@ -199,6 +213,12 @@ kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_
  * backward: 20 per row plus a 64-byte header. One backward per forward
  * (orda-kernel, Quickstart: each fused forward supports one backward pass). */
 size_t kd_saved_bytes(int64_t n);
+
+/* Bytes of `saved` for these descriptors and params: kd_saved_bytes(n), plus
+ * the kept products of the last chunk when keep_last_chunk takes effect.
+ * Validates the descriptors like the calls do; *bytes is host memory. */
+kd_status kd_saved_bytes_for(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                             size_t* bytes /* host */);
 
 /* Forward: per-token outputs, the reduced loss, and `saved` for the backward
  * (saved may be NULL when no backward follows). labels: int64 [n]; NULL means

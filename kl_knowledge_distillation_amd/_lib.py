@@ -18,7 +18,7 @@ KD_TEACHER_TIED, KD_TEACHER_SEPARATE, KD_TEACHER_TOPK, KD_TEACHER_LOGITS = 1, 2,
 KD_REDUCE_MEAN, KD_REDUCE_SUM, KD_REDUCE_NONE = 0, 1, 2
 KD_KL_FORWARD, KD_KL_REVERSE, KD_KL_JEFFREYS = 0, 1, 2
 KERNELS = ["prep", "fwd", "merge", "finalize", "bwd_dz", "scatter", "gemm_dw", "gemm_dh",
-           "gemm_dwdh"]
+           "gemm_dwdh", "bwd_kept"]
 KERNEL_ID = {k: i for i, k in enumerate(KERNELS)}
 
 
@@ -38,7 +38,8 @@ class KdParams(ctypes.Structure):
                 ("kl_weight", c_float), ("temperature", c_float), ("ignore_index", c_int64),
                 ("reduction", c_int32), ("normalizer", c_float), ("vocab_chunk", c_int64),
                 ("assume_valid_labels", c_int32), ("kl_divergence", c_int32),
-                ("teacher_temperature", c_float), ("compact_valid", c_int32)]
+                ("teacher_temperature", c_float), ("compact_valid", c_int32),
+                ("keep_last_chunk", c_int32)]
 
 
 class KdOutputs(ctypes.Structure):
@@ -55,6 +56,8 @@ EXPORTS = {
     "kd_workspace_bytes": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                                      c_int32, POINTER(c_size_t)]),
     "kd_saved_bytes": (c_size_t, [c_int64]),
+    "kd_saved_bytes_for": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
+                                     POINTER(c_size_t)]),
     "kd_loss_fwd": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                               c_void_p, POINTER(KdOutputs), c_void_p, c_void_p, c_size_t,
                               c_void_p, POINTER(KdTrace)]),

@@ -125,7 +125,7 @@ class Runner:
                  teacher_ce_weight=0.0, kl_weight=0.0, temperature=1.0, ignore_index=-100,
                  reduction="mean", normalizer=0.0, vocab_chunk=0, want_grads=True,
                  want_teacher_ce=None, kl_divergence="forward", teacher_temperature=None,
-                 compact_valid=False):
+                 compact_valid=False, keep_last_chunk=None):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -191,6 +191,12 @@ class Runner:
         p.kl_divergence = _KL_DIVERGENCES[kl_divergence]
         p.teacher_temperature = 0.0 if teacher_temperature is None else float(teacher_temperature)
         p.compact_valid = 1 if compact_valid else 0
+        # By default the forward keeps its last chunk's products when a
+        # backward through the projections follows (identical results, one
+        # chunk's products fewer to recompute).
+        if keep_last_chunk is None:
+            keep_last_chunk = want_grads and s.kind == L.KD_STUDENT_PROJECTION
+        p.keep_last_chunk = 1 if keep_last_chunk else 0
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
         self.teacher_kind = teacher_kind
@@ -207,8 +213,10 @@ class Runner:
         self.out = L.KdOutputs(self.loss.data_ptr(), self.student_ce.data_ptr(),
                                self.teacher_ce.data_ptr() if want_teacher_ce else None,
                                self.kl.data_ptr())
-        self.saved = torch.empty(self.lib.kd_saved_bytes(self.n), dtype=torch.uint8,
-                                 device=self.device)
+        nb = ctypes.c_size_t(0)
+        L.check(self.lib.kd_saved_bytes_for(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p),
+                                            ctypes.byref(nb)), "kd_saved_bytes_for")
+        self.saved = torch.empty(int(nb.value), dtype=torch.uint8, device=self.device)
         self.ws_fwd = self._workspace(0)
         self.ws_bwd = self._workspace(1) if (want_grads and s.kind == L.KD_STUDENT_PROJECTION) \
             else None

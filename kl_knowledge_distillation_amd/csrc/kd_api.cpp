@@ -114,6 +114,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   }
   if (check_labels_ptr && labels && ((uintptr_t)labels & 7u)) return KD_ERR_ALIGN;
   if (p->compact_valid != 0 && p->compact_valid != 1) return KD_ERR_PARAM;
+  if (p->keep_last_chunk != 0 && p->keep_last_chunk != 1) return KD_ERR_PARAM;
   if (p->compact_valid && q.mode != kd::MODE_TIED && q.mode != kd::MODE_SEPARATE)
     return KD_ERR_UNSUPPORTED;
 
@@ -203,6 +204,17 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.fwd_bytes = off;
   q.off_dz = off_common;
   q.bwd_bytes = align_up(q.off_dz + (size_t)q.dz_rows * (size_t)q.chunk * elem, 256);
+  // The last chunk's products, kept in `saved` for the backward: columns of
+  // that chunk rounded up to whole tiles, every row of the token tiles.
+  q.saved_bytes = 20 * (size_t)q.n + kd::kSavedHeaderBytes;
+  if (p->keep_last_chunk && (q.mode == kd::MODE_TIED || q.mode == kd::MODE_SEPARATE ||
+                             q.mode == kd::MODE_TLOGITS || q.mode == kd::MODE_TOPK)) {
+    q.keep = 1;
+    q.keep_ops = (q.mode == kd::MODE_TIED || q.mode == kd::MODE_SEPARATE) ? 2 : 1;
+    q.keep_ld = ceil_div(q.v - (int64_t)(q.n_chunks - 1) * q.chunk, vt) * vt;
+    q.keep_off = align_up(q.saved_bytes, 256);
+    q.saved_bytes = q.keep_off + (size_t)q.keep_ops * (size_t)q.dz_rows * (size_t)q.keep_ld * sizeof(float);
+  }
   *out = q;
   return KD_OK;
 }
@@ -245,6 +257,16 @@ kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_
 size_t kd_saved_bytes(int64_t n) {
   if (n < 0) return 0;
   return 20 * (size_t)n + kd::kSavedHeaderBytes;
+}
+
+kd_status kd_saved_bytes_for(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                             size_t* bytes) {
+  if (!bytes) return KD_ERR_NULL;
+  Plan q;
+  const kd_status st = plan_call(s, t, p, nullptr, false, false, &q);
+  if (st != KD_OK) return st;
+  *bytes = q.saved_bytes;
+  return KD_OK;
 }
 
 kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params* p,

@@ -78,6 +78,11 @@ struct Plan {
   size_t off_tks = 0, off_tko = 0;
   // backward workspace layout
   size_t off_dz = 0, bwd_bytes = 0;
+  // Kept products of the last chunk in `saved` (keep_last_chunk): keep_ops
+  // fp32 [dz_rows][keep_ld] matrices (student, then teacher) from byte keep_off.
+  int keep = 0, keep_ops = 0;
+  int64_t keep_ld = 0;
+  size_t keep_off = 0, saved_bytes = 0;
   // compaction buffers (same offsets in both workspaces): idx, pos [n] int32,
   // compacted H_s [dz_rows x d] and H_t [dz_rows x dt] in the input dtype
   size_t off_cidx = 0, off_cpos = 0, off_hc = 0, off_htc = 0;

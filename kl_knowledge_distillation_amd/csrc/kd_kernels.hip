@@ -255,6 +255,36 @@ __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t ar
   }
 }
 
+// Kept products of the last chunk, in register order: tile `tile` (token
+// tile x tiles of the chunk + vocabulary tile) holds its waves' accumulators
+// one after another, block (mb, nb) of wave w as 64 lanes x 16 bytes, so every
+// store and load of a wave is one contiguous 1 KB and a tile one contiguous
+// [kVT x kTT] block. Only the library reads the layout back, with the same
+// tile geometry.
+__device__ __forceinline__ int64_t kept_block(int64_t tile, int waves, int w, int lane) {
+  return ((tile * waves + w) * (kMB * kNB)) * 256 + lane * 4;
+}
+__device__ __forceinline__ void kept_store(float* m, int64_t tile, int waves, int w, int lane,
+                                           const WaveAcc& x) {
+  float* p = m + kept_block(tile, waves, w, lane);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) *reinterpret_cast<f32x4*>(p + (mb * kNB + nb) * 256) = x[mb][nb];
+}
+// Token block nb of that part read back (streaming loads: each byte is read
+// once); a token that is not live reads as zero.
+__device__ __forceinline__ void kept_load(const float* m, int64_t tile, int waves, int w, int lane, int nb,
+                                          bool live, f32x4 (&x)[kMB]) {
+  const float* p = m + kept_block(tile, waves, w, lane);
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) {
+    const uint4 u = load_stream(p + (mb * kNB + nb) * 256);
+    x[mb] = live ? f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)}
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // The [kVT x kTT] tile of a row-major [n x v] logits matrix (tokens are rows)
 // in the accumulator layout: register r of row block mb, token block nb holds
 // vocabulary row v0 + acc_row(wm, mb, r, lane) of token t0 + acc_col(wn, nb, lane).
@@ -375,6 +405,10 @@ struct FwdArgs {
   const int32_t* topk_off;   // [n, n_slices + 1]: this launch's tiles
   int k;
   int slice0;                // first vocabulary tile of this launch (n_slices tiles from it)
+  // non-null: this launch's products kept for the backward in register order
+  // (student, then the teacher's keep_t elements later)
+  float* keep;
+  int64_t keep_t;
 };
 
 // Top-K: floats per token row of the z tile staged in LDS (the padding spreads
@@ -453,6 +487,17 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     } else {
       tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, zl);
+    }
+  }
+  // The products of the last chunk, stored for the backward before the
+  // epilogue so that the stores drain under its arithmetic.
+  if constexpr (MODE != MODE_LOGITS) {
+    if (a.keep) {
+      const int64_t tile = (int64_t)tt * a.n_slices + slice;
+      constexpr int kWaves = G::kThreads / 64;
+      kept_store(a.keep, tile, kWaves, w, lane, acc[0]);
+      if constexpr (MODE == MODE_TIED || MODE == MODE_SEPARATE)
+        kept_store(a.keep + a.keep_t, tile, kWaves, w, lane, MODE == MODE_TIED ? acc[NB - 1] : tacc[0]);
     }
   }
 
@@ -1368,6 +1413,10 @@ struct BwdArgs {
   void* dz;               // [dz_rows][ldz]
   int64_t ldz;
   int64_t dz_rows;        // n rounded up to the token tile; rows past n are written as 0
+  // kept products of this chunk (the forward's last) in register order, the
+  // teacher's keep_t elements after the student's
+  const float* keep;
+  int64_t keep_t;
 };
 
 template <typename T>
@@ -1384,14 +1433,17 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, fl
   *reinterpret_cast<uint2*>(p) = u;
 }
 
-template <typename T, int MODE, class G>
-__global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
+// kKept: the products are the forward's kept ones (a.keep), read instead of
+// recomputed; the tile runs no main loop and needs no LDS.
+template <typename T, int MODE, class G, bool kKept>
+__global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
   constexpr bool kGiven = MODE == MODE_TLOGITS;
   constexpr int kMainBytes = G::template lds_bytes<NB>();
   constexpr bool kGivenRegs = kGiven && G::kPipe;  // a given logits tile in registers
-  constexpr bool kPf = G::kPipe && kPipeAhead > 0;  // prefetch reads: 1 KB
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kMainBytes + (kPf ? 1024 : 0)];
+  constexpr bool kPf = G::kPipe && kPipeAhead > 0 && !kKept;  // prefetch reads: 1 KB
+  constexpr bool kKeptT = kKept && (MODE == MODE_TIED || MODE == MODE_SEPARATE);  // teacher's kept too
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kKept ? 16 : kMainBytes + (kPf ? 1024 : 0)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: token tiles from round_up(nv, 128) on would hold only zero
   // rows, which no GEMM reads (their K and M stop at nv); only the tiles below
@@ -1412,8 +1464,21 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
   f32x4 acc[NB][kMB][kNB];
   f32x4 tacc[1][kMB][kNB];
   // the tile's share of the cooperative prefetch (grouped order)
-  const PipePrefetch pf{kPf ? 1 : 0, tt % 8, vt % 4, lds + kMainBytes};
-  if constexpr (MODE == MODE_TIED) {
+  const PipePrefetch pf{kPf ? 1 : 0, tt % 8, vt % 4, lds + (kKept ? 0 : kMainBytes)};
+  if constexpr (kKept) {
+    // the kept products are read per token block in the epilogue; a given
+    // teacher tile is loaded here as in the recomputing tiles
+    if constexpr (MODE == MODE_TLOGITS) {
+      const T* L = static_cast<const T*>(a.tlogits);
+      if constexpr (kGivenRegs) {
+        GivenRaw raw;
+        given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+        given_raw_unpack(raw, tacc[0]);
+      } else {
+        given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
+      }
+    }
+  } else if constexpr (MODE == MODE_TIED) {
     const T* const b[2] = {hs, ht};
     tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   } else if constexpr (MODE == MODE_SEPARATE) {
@@ -1491,6 +1556,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
     const float rev0 = sv.z - sv.y - mass;   // lse(t/T) - lse(z/T) - KL(P_S || P_T)
     const float invT = 1.f / a.T;
     T* row = dz + tok * a.ldz + (v0 - a.c0);
+    // kept products of this token block: the student's (MODE_TCE: the
+    // teacher's) and, for a TIED or SEPARATE teacher, the teacher's
+    f32x4 zk[kMB], tk[kMB];
+    if constexpr (kKept) {
+      const int64_t tile = (int64_t)tt * a.n_vt + vt;
+      constexpr int kWaves = G::kThreads / 64;
+      kept_load(a.keep + (MODE == MODE_TCE ? a.keep_t : 0), tile, kWaves, w, lane, nb, live, zk);
+      if constexpr (kKeptT) kept_load(a.keep + a.keep_t, tile, kWaves, w, lane, nb, live, tk);
+    }
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       // registers r = 0..3 are four consecutive vocabulary rows
@@ -1498,7 +1572,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int k = mb * 16 + r;
-        const float zz = z[mb][nb][r];
+        float zz;
+        if constexpr (kKept) zz = zk[mb][r];
+        else zz = z[mb][nb][r];
         float p1, pz;
         if constexpr (kSq) {
           const float e = exp2_fast(fmaf(zz, a.cT, -L1h));
@@ -1515,7 +1591,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void bwd_dz_kernel(BwdArgs a) {
           dv = cs * (p1 - (yl == k ? 1.f : 0.f));
         } else {
           dv = cs * (p1 - (yl == k ? 1.f : 0.f));
-          const float tt = tl[mb][nb][r];
+          float tt;
+          if constexpr (kKeptT) tt = tk[mb][r];
+          else tt = tl[mb][nb][r];
           const float pt = exp2_fast(fmaf(tt, a.cTt, -LtT));
           dv = fmaf(ckf, pz - pt, dv);
           if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(fmaf(tt, -a.rho, zz), invT, rev0), dv);
@@ -1999,6 +2077,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
     for (int s0 = 0; s0 < p.n_vtiles; s0 += p.fwd_slices) {
       fa.slice0 = s0;
       fa.n_slices = std::min(p.fwd_slices, p.n_vtiles - s0);
+      // the last chunk's products are kept in `saved` for the backward
+      const bool keep = p.keep && saved && s0 + fa.n_slices >= p.n_vtiles;
+      fa.keep = keep ? reinterpret_cast<float*>(static_cast<uint8_t*>(saved) + p.keep_off) : nullptr;
+      fa.keep_t = (p.keep_ops == 2) ? p.dz_rows * p.keep_ld : 0;
       const dim3 fgrid((unsigned)((int64_t)fa.n_slices * p.n_ttiles));
       if (p.mode == MODE_TOPK) {
         const TileStartArgs ts{tk_idx, p.n, p.v, p.k, p.vt_rows, s0, fa.n_slices, tk_off};
@@ -2090,15 +2172,27 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
                kLog2e / p.Tt, p.T / p.Tt, p.wt, p.need_zT, p.kl, given_mode<T, G>(x.tlogits, p.v),
                (!teacher && p.T == 2.f && p.need_zT) ? 1 : 0, cp.idx, cp.nv, c0, n_vt, p.n_ttiles,
                dz, ldz, p.dz_rows};
+    // The forward's last chunk: its products were kept in `saved` (the
+    // teacher's as well for a TIED or SEPARATE teacher).
+    const bool kept = p.keep && c == p.n_chunks - 1 && (!teacher || p.keep_ops == 2);
+    if (kept) {
+      ba.keep = reinterpret_cast<const float*>(static_cast<const uint8_t*>(saved) + p.keep_off);
+      ba.keep_t = (p.keep_ops == 2) ? p.dz_rows * p.keep_ld : 0;
+    }
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
-    KD_TRY(L.run(KD_KERNEL_BWD_DZ, [&] {
+    auto launch = [&](auto kept_tag) {
+      constexpr bool K = decltype(kept_tag)::value;
       switch (mode) {
-        case MODE_TCE: bwd_dz_kernel<T, MODE_TCE, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
-        case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
-        case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
-        case MODE_TLOGITS: bwd_dz_kernel<T, MODE_TLOGITS, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
-        default: bwd_dz_kernel<T, MODE_TOPK, G><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_TCE: bwd_dz_kernel<T, MODE_TCE, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_TLOGITS: bwd_dz_kernel<T, MODE_TLOGITS, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        default: bwd_dz_kernel<T, MODE_TOPK, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
       }
+    };
+    KD_TRY(L.run(kept ? KD_KERNEL_BWD_KEPT : KD_KERNEL_BWD_DZ, [&] {
+      if (kept) launch(std::true_type{});
+      else launch(std::false_type{});
     }));
     if (mode == MODE_TOPK) {
       ScatterArgs sa{x.topk_idx, x.topk_prob, p.k, p.n, p.v, c0, cw,

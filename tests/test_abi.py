@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for must in ("kd_loss_fwd", "kd_loss_bwd", "kd_loss_bwd_teacher", "kd_loss_bwd_logits",
-                 "kd_workspace_bytes", "kd_saved_bytes",
+                 "kd_workspace_bytes", "kd_saved_bytes", "kd_saved_bytes_for",
                  "kd_read_status", "kd_status_string", "kd_device_supported"):
         assert must in names
 
@@ -82,6 +82,44 @@ def test_saved_bytes():
     lib = L.load()
     assert lib.kd_saved_bytes(0) == 64
     assert lib.kd_saved_bytes(4096) == 20 * 4096 + 64
+
+
+def _saved_for(s, t, p):
+    lib = L.load()
+    nb = ctypes.c_size_t(0)
+    st = lib.kd_saved_bytes_for(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), ctypes.byref(nb))
+    return st, nb.value
+
+
+def test_saved_bytes_for_keep_last_chunk():
+    lib = L.load()
+    align = lambda x: -(-x // 256) * 256  # noqa: E731
+    # bf16, hidden sizes multiple of 32: 256-column tiles; n = 300 -> 384 token rows
+    for kind, ops in (("tied", 2), ("separate", 2), ("topk", 1)):
+        s, t, p = _desc(kind)
+        assert _saved_for(s, t, p) == (L.KD_OK, lib.kd_saved_bytes(300))
+        p.keep_last_chunk = 1
+        p.vocab_chunk = 1024  # chunks of 1024 columns: the last one holds 3000 - 2048 = 952
+        st, nb = _saved_for(s, t, p)
+        assert st == L.KD_OK
+        assert nb == align(lib.kd_saved_bytes(300)) + ops * 384 * 1024 * 4, kind
+        p.vocab_chunk = 0  # one chunk covers the vocabulary: 3000 -> 3072 columns
+        assert _saved_for(s, t, p)[1] == align(lib.kd_saved_bytes(300)) + ops * 384 * 3072 * 4
+    # fp32 inputs run 128-column tiles: the last of the 1024-column chunks rounds 952 up to 1024
+    s, t, p = _desc("tied", dtype=L.KD_F32)
+    p.keep_last_chunk, p.vocab_chunk = 1, 1000
+    assert _saved_for(s, t, p)[1] == align(lib.kd_saved_bytes(300)) + 2 * 384 * 1024 * 4
+    # given student logits: no backward through projections, nothing kept
+    s, t, p = _desc("tied")
+    s.kind, s.logits, s.d = L.KD_STUDENT_LOGITS, FAKE, 0
+    t.kind, t.d_t, t.hidden, t.weight = L.KD_TEACHER_SEPARATE, 256, FAKE, FAKE
+    p.keep_last_chunk = 1
+    assert _saved_for(s, t, p) == (L.KD_OK, lib.kd_saved_bytes(300))
+    # only 0 and 1
+    s, t, p = _desc("tied")
+    p.keep_last_chunk = 2
+    assert _saved_for(s, t, p)[0] == L.KD_ERR_PARAM
+    assert _fwd(s, t, p) == L.KD_ERR_PARAM
 
 
 def test_status_strings():

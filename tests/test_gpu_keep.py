@@ -1,0 +1,71 @@
+"""keep_last_chunk: the forward keeps the fp32 products of its last vocabulary
+chunk in `saved` and the backward reads them instead of recomputing that
+chunk. The products are the same accumulators either way, so every output
+and gradient must be bit-identical to the path that recomputes every chunk
+(whose agreement with the oracle the parity tests check)."""
+import pytest
+import torch
+
+from gpu_common import make_runner, say
+from kl_knowledge_distillation_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+C1 = WORKLOADS["tiny_tied_fp32"]
+C2 = WORKLOADS["quickstart_tied_bf16"]
+C3 = WORKLOADS["separate_bf16"]
+C4 = WORKLOADS["topk_bf16"]
+C6 = WORKLOADS["quickstart_logits_bf16"]
+
+# (workload, vocab chunk): several chunks with a ragged last one unless noted
+CASES = {
+    "tied_pipe": (C2.scaled(n=300, d=512, v=3000), 1024),
+    "tied_one_chunk": (C2.scaled(n=300, d=512, v=3000), 0),
+    "tied_staged_ragged": (C2.scaled(n=130, d=136, v=1029, ignore_frac=0.2), 256),
+    "tied_fp32": (C1.scaled(n=70, v=1000, ignore_frac=0.2), 256),
+    "tied_reverse": (C2.scaled(n=260, d=256, v=2100, kl_divergence="reverse"), 512),
+    "tied_jeffreys_T1": (C2.scaled(n=260, d=256, v=2100, kl_divergence="jeffreys",
+                                   temperature=1.0), 512),
+    "tied_compact": (C2.scaled(n=300, d=512, v=3000, ignore_frac=0.3, compact_valid=True), 768),
+    "separate_T2": (C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=2.0,
+                              ignore_frac=0.1), 512),
+    "dense_teacher_logits": (C6.scaled(n=200, d=256, v=2000), 512),
+    "dense_teacher_logits_staged": (C6.scaled(n=130, d=136, v=1029), 256),
+    "topk": (C4.scaled(n=300, d=512, v=5000), 1024),
+    "topk_staged": (C4.scaled(n=129, d=264, v=1031, k=7), 256),
+    "tied_train_teacher": (C2.scaled(n=300, d=512, v=3000, teacher_ce_weight=0.7), 1024),
+    "separate_train_teacher_compact": (C3.scaled(n=200, d=256, d_t=512, v=2000,
+                                                 teacher_ce_weight=0.5, ignore_frac=0.3,
+                                                 compact_valid=True), 512),
+}
+
+
+def _run(w, x, chunk, keep):
+    r = make_runner(w, x, chunk, keep_last_chunk=keep)
+    r.forward()
+    dh = torch.empty((r.n, r.d), dtype=torch.float32, device="cuda")
+    dw = torch.empty((r.v, r.d), dtype=torch.float32, device="cuda")
+    r.backward(dh, dw)
+    out = {"loss": r.loss, "kl": r.kl, "student_ce": r.student_ce, "teacher_ce": r.teacher_ce,
+           "dh": dh, "dw": dw}
+    if w.teacher_ce_weight > 0 and w.teacher in ("tied", "separate"):
+        dht = torch.empty((r.n, r.dt), dtype=torch.float32, device="cuda")
+        dwt = torch.empty((r.v, r.dt), dtype=torch.float32, device="cuda")
+        r.backward_teacher(dht, dwt)
+        out.update(dht=dht, dwt=dwt)
+    torch.cuda.synchronize()
+    assert r.read_status() == 0
+    return {k: v.clone() for k, v in out.items()}, r.saved.numel()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_keep_last_chunk_is_bit_identical(name):
+    w, chunk = CASES[name]
+    say(f"[keep] {name} n={w.n} d={w.d} d_t={w.d_t} v={w.v} chunk={chunk}")
+    x = make_inputs(w, "cuda", seed=5)
+    ref, small = _run(w, x, chunk, False)
+    got, big = _run(w, x, chunk, True)
+    assert big > small  # the kept products live in `saved`
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), f"{name}: {k} differs with the kept last chunk"
+        assert torch.isfinite(got[k]).all(), f"{name}: {k}"
