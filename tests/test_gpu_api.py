@@ -212,3 +212,29 @@ def test_kdloss_given_logits_autograd():
     g = O.logit_grad(s, t, p, labels, np.arange(w.n), 400.0, grad_loss=0.5)
     assert zl.grad.dtype == zl.dtype and zl.grad.shape == zl.shape
     assert_grad(f64(zl.grad.reshape(w.n, w.v)), g, "bf16", "KDLoss d student logits")
+
+
+def test_distillation_loss_keep_last_chunk_identical_gradients():
+    """keep_last_chunk on (the default with a backward) and off give the same
+    loss and bit-identical gradients through autograd."""
+    w = WORKLOADS["quickstart_tied_bf16"].scaled(n=260, d=256, v=2100)
+    say("[api] keep_last_chunk on / off")
+    x = make_inputs(w, "cuda", seed=12)
+    res = []
+    for keep in (None, False):
+        hs = x["student_hidden"].clone().requires_grad_(True)
+        W = x["weight"].clone().requires_grad_(True)
+        out = api.distillation_loss(hs, W, x["labels"], api.TiedTeacher(x["teacher_hidden"]),
+                                    kl_weight=0.5, kl_temperature=2.0, vocab_chunk=512,
+                                    ignore_index=w.ignore_index, keep_last_chunk=keep)
+        out.loss.backward()
+        torch.cuda.synchronize()
+        res.append((out.loss.detach().clone(), hs.grad.clone(), W.grad.clone()))
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+    # without a backward nothing is kept
+    with torch.no_grad():
+        out = api.distillation_loss(x["student_hidden"], x["weight"], x["labels"],
+                                    api.TiedTeacher(x["teacher_hidden"]), kl_weight=0.5,
+                                    kl_temperature=2.0, vocab_chunk=512, ignore_index=w.ignore_index)
+    assert torch.equal(out.loss, res[0][0])
