@@ -264,13 +264,16 @@ __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t ar
 __device__ __forceinline__ int64_t kept_block(int64_t tile, int waves, int w, int lane) {
   return ((tile * waves + w) * (kMB * kNB)) * 256 + lane * 4;
 }
+// Stores are nontemporal: the backward reads them back only after the rest of
+// the forward and a whole recomputed chunk (equal or 0.3% faster per step).
 __device__ __forceinline__ void kept_store(float* m, int64_t tile, int waves, int w, int lane,
                                            const WaveAcc& x) {
   float* p = m + kept_block(tile, waves, w, lane);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) *reinterpret_cast<f32x4*>(p + (mb * kNB + nb) * 256) = x[mb][nb];
+    for (int nb = 0; nb < kNB; ++nb)
+      __builtin_nontemporal_store(x[mb][nb], reinterpret_cast<f32x4*>(p + (mb * kNB + nb) * 256));
 }
 // Token block nb of that part read back (streaming loads: each byte is read
 // once); a token that is not live reads as zero.
