@@ -210,8 +210,9 @@ kd_status kd_workspace_bytes(const kd_student* s, const kd_teacher* t, const kd_
                              int32_t for_backward, size_t* bytes /* host */);
 
 /* Bytes of the buffer that carries per-row statistics from forward to
- * backward: 20 per row plus a 64-byte header. One backward per forward
- * (orda-kernel, Quickstart: each fused forward supports one backward pass). */
+ * backward: 20 per row plus a 64-byte header, enough whenever keep_last_chunk
+ * is 0 (else see kd_saved_bytes_for). One backward per forward (orda-kernel,
+ * Quickstart: each fused forward supports one backward pass). */
 size_t kd_saved_bytes(int64_t n);
 
 /* Bytes of `saved` for these descriptors and params: kd_saved_bytes(n), plus
