@@ -166,6 +166,11 @@ typedef struct {
                                 0: saved is kd_saved_bytes(n) and the backward recomputes every
                                 chunk (CompactifAI/Full-Chunked-KL-Loss, Full Chunked KL:
                                 logits are recomputed chunk by chunk in the backward). */
+  int64_t saved_bytes;       /* bytes of the `saved` buffer the calls are given; with
+                                keep_last_chunk taking effect, kd_loss_fwd, kd_loss_bwd and
+                                kd_loss_bwd_teacher return KD_ERR_WORKSPACE before enqueuing
+                                anything when it is below kd_saved_bytes_for. Not read
+                                otherwise (0 is fine). */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).

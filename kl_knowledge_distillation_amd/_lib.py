@@ -39,7 +39,7 @@ class KdParams(ctypes.Structure):
                 ("reduction", c_int32), ("normalizer", c_float), ("vocab_chunk", c_int64),
                 ("assume_valid_labels", c_int32), ("kl_divergence", c_int32),
                 ("teacher_temperature", c_float), ("compact_valid", c_int32),
-                ("keep_last_chunk", c_int32)]
+                ("keep_last_chunk", c_int32), ("saved_bytes", c_int64)]
 
 
 class KdOutputs(ctypes.Structure):

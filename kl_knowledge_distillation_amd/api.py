@@ -217,6 +217,7 @@ class Runner:
         L.check(self.lib.kd_saved_bytes_for(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p),
                                             ctypes.byref(nb)), "kd_saved_bytes_for")
         self.saved = torch.empty(int(nb.value), dtype=torch.uint8, device=self.device)
+        p.saved_bytes = self.saved.numel()
         self.ws_fwd = self._workspace(0)
         self.ws_bwd = self._workspace(1) if (want_grads and s.kind == L.KD_STUDENT_PROJECTION) \
             else None

@@ -115,6 +115,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   if (check_labels_ptr && labels && ((uintptr_t)labels & 7u)) return KD_ERR_ALIGN;
   if (p->compact_valid != 0 && p->compact_valid != 1) return KD_ERR_PARAM;
   if (p->keep_last_chunk != 0 && p->keep_last_chunk != 1) return KD_ERR_PARAM;
+  if (p->saved_bytes < 0) return KD_ERR_PARAM;
   if (p->compact_valid && q.mode != kd::MODE_TIED && q.mode != kd::MODE_SEPARATE)
     return KD_ERR_UNSUPPORTED;
 
@@ -278,6 +279,8 @@ kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params*
   if (!workspace) return KD_ERR_NULL;
   if (ws_bytes < q.fwd_bytes) return KD_ERR_WORKSPACE;
   if (!aligned16(workspace) || (saved && !aligned16(saved))) return KD_ERR_ALIGN;
+  // the kept products go past the row statistics: the caller must have said it has the room
+  if (saved && q.keep && (size_t)p->saved_bytes < q.saved_bytes) return KD_ERR_WORKSPACE;
   if (out) {
     const void* ptrs[4] = {out->loss, out->student_ce, out->teacher_ce, out->kl};
     for (const void* ptr : ptrs)
@@ -298,6 +301,7 @@ kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params*
   if (!workspace) return KD_ERR_NULL;
   if (ws_bytes < q.bwd_bytes) return KD_ERR_WORKSPACE;
   if (!aligned16(workspace) || !aligned16(saved)) return KD_ERR_ALIGN;
+  if (q.keep && (size_t)p->saved_bytes < q.saved_bytes) return KD_ERR_WORKSPACE;
   if ((d_hidden && !aligned16(d_hidden)) || (d_weight && !aligned16(d_weight))) return KD_ERR_ALIGN;
   if (grad_loss && ((uintptr_t)grad_loss & 3u)) return KD_ERR_ALIGN;
   if (!d_hidden && !d_weight) return KD_OK;
@@ -334,6 +338,7 @@ kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd
   if (!workspace) return KD_ERR_NULL;
   if (ws_bytes < q.bwd_bytes) return KD_ERR_WORKSPACE;
   if (!aligned16(workspace) || !aligned16(saved)) return KD_ERR_ALIGN;
+  if (q.keep && (size_t)p->saved_bytes < q.saved_bytes) return KD_ERR_WORKSPACE;
   if ((d_teacher_hidden && !aligned16(d_teacher_hidden)) ||
       (d_teacher_weight && !aligned16(d_teacher_weight)))
     return KD_ERR_ALIGN;

@@ -120,6 +120,16 @@ def test_saved_bytes_for_keep_last_chunk():
     p.keep_last_chunk = 2
     assert _saved_for(s, t, p)[0] == L.KD_ERR_PARAM
     assert _fwd(s, t, p) == L.KD_ERR_PARAM
+    # the calls refuse a `saved` declared smaller than the kept products need
+    # (nothing is enqueued; these pointers are never dereferenced)
+    p.keep_last_chunk = 1
+    need = _saved_for(s, t, p)[1]
+    for nbytes in (0, need - 1):
+        p.saved_bytes = nbytes
+        assert _fwd(s, t, p) == L.KD_ERR_WORKSPACE
+        assert _bwd(s, t, p) == L.KD_ERR_WORKSPACE
+    p.saved_bytes = -1
+    assert _fwd(s, t, p) == L.KD_ERR_PARAM
 
 
 def test_status_strings():
