@@ -28,7 +28,8 @@
  * The (n, v) logits are never materialised: the forward streams vocabulary
  * tiles through registers with online (max, rescaled sum) statistics
  * (flash_kd, module description), and the backward recomputes each vocabulary
- * chunk and writes only an (n, chunk) gradient slab.
+ * chunk and writes only an (n, chunk) gradient slab (with keep_last_chunk, the
+ * forward's last chunk is read back from `saved` instead of recomputed).
  *
  * Conventions.
  *   - Every pointer in the structs below is a DEVICE pointer, except the
