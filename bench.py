@@ -1,12 +1,20 @@
 """Benchmark: fused LM-head + CE + KL distillation loss, forward + backward, one GPU.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--vocab-chunk C]
+    python bench.py --matrix [--matrix-only NAME ...]
 
 One step is the whole hot path on one batch of synthetic input already
 resident in HBM: prep, forward tiles, merge, finalize, then per vocabulary
-chunk the backward recompute (dz), the dW GEMM and the dH GEMM. The default
-workload is the quickstart-shaped tied teacher (N=4096, D=2048, V=32000,
-bf16, T=2). Prints one JSON line.
+chunk the backward recompute (dz) and the dW / dH GEMMs. The default workload
+is the largest forward + backward one that fits a GPU: the precomputed sparse
+top-K teacher (B=1, S=32768, hidden 4096, vocab 151936, K=100, bf16; the
+Full-Chunked-KL-Loss benchmark's shape). Prints one JSON line.
+
+--matrix runs every workload (and the scorer's chunk sweep) in a fresh child
+process each, the parent importing neither torch nor the library, and
+records each child's JSON line as OK or its error as FAILED (the
+Full-Chunked-KL-Loss README, What it measures: every experiment isolated in
+a subprocess, status OK / FAILED with the captured error).
 
 Throughput `value` is tokens per second. Besides it the line carries the
 method's MFMA TFLOP/s (including the backward recompute), peak HBM bytes,
@@ -246,12 +254,71 @@ def cpu_baseline(w, target_s: float = 12.0) -> dict:
                       f"({'d logits' if w.student == 'logits' else 'dH, dW'}) in float64, {dt:.1f} s"}
 
 
+# The matrix: every workload of the five configurations, the scorer at each
+# chunk of its sweep (flash_kd, flash_ce_kd_loss: chunk_size is the memory
+# knob). Each entry: (label, bench arguments).
+MATRIX = (
+    ("tiny_tied_fp32", ["--workload", "tiny_tied_fp32"]),
+    ("quickstart_tied_bf16", ["--workload", "quickstart_tied_bf16"]),
+    ("separate_bf16", ["--workload", "separate_bf16"]),
+    ("topk_bf16", ["--workload", "topk_bf16"]),
+    ("scorer_bf16_chunk2048", ["--workload", "scorer_bf16", "--vocab-chunk", "2048"]),
+    ("scorer_bf16_chunk8192", ["--workload", "scorer_bf16", "--vocab-chunk", "8192"]),
+    ("scorer_bf16_chunk16384", ["--workload", "scorer_bf16", "--vocab-chunk", "16384"]),
+)
+
+
+def run_matrix(entries, timeout_s: float = 600.0, log=sys.stderr) -> list:
+    """Run each (label, argv) as its own child process, one after another.
+
+    A child that exits 0 and prints a JSON line is OK (the line is kept); any
+    other end (a non-zero exit, a signal, no JSON line, the time limit) is
+    FAILED with the exit status and the tail of its stderr, and the next
+    entry still runs. The caller's process never touches the GPU."""
+    import subprocess
+    results = []
+    for label, argv in entries:
+        print(f"[matrix] {label}: {' '.join(argv)}", file=log, flush=True)
+        t0 = time.perf_counter()
+        rec = {"label": label, "argv": list(argv)}
+        try:
+            r = subprocess.run(argv, capture_output=True, text=True, timeout=timeout_s)
+            rc, out, err = r.returncode, r.stdout, r.stderr
+        except subprocess.TimeoutExpired as e:
+            rc = "timeout"
+            out = e.stdout.decode() if isinstance(e.stdout, bytes) else (e.stdout or "")
+            err = e.stderr.decode() if isinstance(e.stderr, bytes) else (e.stderr or "")
+        rec["wall_s"] = round(time.perf_counter() - t0, 2)
+        line = None
+        for ln in reversed(out.strip().splitlines()):
+            if ln.startswith("{"):
+                try:
+                    line = json.loads(ln)
+                    break
+                except ValueError:
+                    pass
+        if rc == 0 and line is not None:
+            rec["status"] = "OK"
+            rec["result"] = line
+        else:
+            rec["status"] = "FAILED"
+            rec["exit"] = rc
+            rec["error"] = "\n".join((err or "no output").strip().splitlines()[-12:])
+        print(f"[matrix] {label}: {rec['status']} ({rec['wall_s']} s)", file=log, flush=True)
+        results.append(rec)
+    return results
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="quickstart_tied_bf16")
+    ap.add_argument("--workload", default="topk_bf16")
+    ap.add_argument("--matrix", action="store_true",
+                    help="every workload in a fresh child process; OK / FAILED per entry")
+    ap.add_argument("--matrix-only", nargs="*", default=None,
+                    help="with --matrix: only these entries (labels of MATRIX)")
     ap.add_argument("--vocab-chunk", type=int, default=0)
     ap.add_argument("--n", type=int, default=0, help="override the token count")
     ap.add_argument("--d", type=int, default=0, help="override the student hidden size")
@@ -261,8 +328,9 @@ def main() -> int:
                     help="leave rows with an ignored label out of the projections (compact_valid)")
     ap.add_argument("--kl", choices=("forward", "reverse", "jeffreys"), default=None,
                     help="override the workload's KL direction")
-    ap.add_argument("--recompute-last-chunk", action="store_true",
-                    help="keep_last_chunk off: the backward recomputes every chunk's products")
+    ap.add_argument("--keep-last-chunk", action="store_true",
+                    help="keep_last_chunk on (opt-in): the forward keeps its last chunk's fp32 "
+                         "products and the backward reads them instead of recomputing them")
     ap.add_argument("--train-teacher", action="store_true",
                     help="teacher trained through its CE (weight 1): the step adds its backward")
     ap.add_argument("--ignore-frac", type=float, default=None,
@@ -288,6 +356,21 @@ def main() -> int:
             print(f"{c:10s} {rec['hbm_bytes_per_launch'] / 1e6:10.1f} MB/launch "
                   f"(fetch {rec['fetch_bytes_per_launch'] / 1e6:.1f}, write "
                   f"{rec['write_bytes_per_launch'] / 1e6:.1f}, {rec['dispatches']} dispatches)")
+        return 0
+
+    if args.matrix:
+        chosen = [e for e in MATRIX if args.matrix_only is None or e[0] in args.matrix_only]
+        common = ["--steps", str(args.steps), "--warmup", str(args.warmup)]
+        if args.no_cpu_baseline:
+            common.append("--no-cpu-baseline")
+        entries = [(label, [sys.executable, "-u", os.path.abspath(__file__), *a, *common])
+                   for label, a in chosen]
+        results = run_matrix(entries)
+        for rec in results:
+            print(json.dumps(rec), flush=True)
+        ok = sum(r["status"] == "OK" for r in results)
+        print(json.dumps({"matrix": len(results), "ok": ok, "failed": len(results) - ok}),
+              flush=True)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -328,7 +411,8 @@ def main() -> int:
               vocab_chunk=args.vocab_chunk, want_grads=not w.forward_only,
               kl_divergence=w.kl_divergence, teacher_temperature=w.teacher_temperature,
               compact_valid=w.compact_valid,
-              keep_last_chunk=False if args.recompute_last_chunk else None)
+              keep_last_chunk=bool(args.keep_last_chunk) and not w.forward_only
+              and w.student != "logits")
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:
@@ -414,7 +498,17 @@ def main() -> int:
     # the backward chunk the library used (same rule as the C ABI's default)
     chunk = args.vocab_chunk if args.vocab_chunk > 0 else 16384
     chunk = min(-(-chunk // 128) * 128, -(-w.v // 128) * 128)
-    kept = kept_columns(w, chunk, not args.recompute_last_chunk)
+    kept = kept_columns(w, chunk, args.keep_last_chunk)
+    # what the opt-in keep_last_chunk would add to `saved` (or adds, when on)
+    keep_extra = 0
+    if not w.forward_only and w.student != "logits":
+        import ctypes
+        p2 = L.KdParams.from_buffer_copy(r.p)
+        p2.keep_last_chunk = 1
+        nb = ctypes.c_size_t(0)
+        L.check(r.lib.kd_saved_bytes_for(ctypes.byref(r.s), ctypes.byref(r.t), ctypes.byref(p2),
+                                         ctypes.byref(nb)), "kd_saved_bytes_for")
+        keep_extra = int(nb.value) - int(r.lib.kd_saved_bytes(r.n))
     fl = method_flops(w, args.train_teacher, n_rows, kept)
     peak_tflops = PEAK_FP32_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
@@ -447,10 +541,14 @@ def main() -> int:
         "useful_tflops": round(fl["useful"] / (ms_per_step / 1e3) / 1e12, 1),
         "peak_hbm_bytes": int(peak),
         "peak_extra_hbm_bytes": int(peak - base_alloc - output_bytes),
+        "keep_last_chunk_extra_bytes": keep_extra,
         "input_bytes": int(input_bytes),
         "wall_s": round(wall, 3),
         "device_status": status,
-        "kernel_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
+        # per-class kernel times of the last warm-up step, traced with events
+        # around every launch (not the timed region, which traces only the
+        # dominant class)
+        "warmup_kernel_ms_per_step": {k: round(v, 4) for k, v in per_kernel.items()},
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",

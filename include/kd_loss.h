@@ -72,7 +72,9 @@ enum {
   KD_ERR_WORKSPACE = 6,    /* workspace smaller than kd_workspace_bytes, or saved missing */
   KD_ERR_UNSUPPORTED = 7,  /* valid but not provided (backward of the logits scorer, a non-forward KL with a TOPK teacher) */
   KD_ERR_LABEL_RANGE = 8,  /* device flag: a label or top-K index was out of range */
-  KD_ERR_HIP = 9           /* a HIP launch or runtime call failed */
+  KD_ERR_HIP = 9,          /* a HIP launch or runtime call failed */
+  KD_ERR_SAVED = 10        /* device flag: a backward that reads kept products found `saved`
+                              without kept products of its layout (see keep_last_chunk) */
 };
 
 /* Element type of hidden / weight / logits. Accumulation is always fp32. */
@@ -143,7 +145,10 @@ typedef struct {
                                 backward's dz slab holds n x chunk; the forward runs one tile
                                 launch per chunk and keeps one chunk's tile records (40 bytes
                                 per token and 256 columns). */
-  int32_t assume_valid_labels; /* accepted for compatibility; labels are always range-checked */
+  int32_t assume_valid_labels; /* accepted and ignored (orda-kernel, Parameters: the flag lets a
+                                caller skip label validation). Labels are always range-checked:
+                                the check is one compare per row, and an unchecked label would
+                                become a memory address (z[y] reads row y of the weight). */
   int32_t kl_divergence;     /* KD_KL_* */
   float teacher_temperature; /* T_t > 0, finite: the teacher's own temperature (orda-kernel,
                                 Parameters: kl_teacher_temperature); 0 = T. TOPK: 0 or 1 */
@@ -172,6 +177,11 @@ typedef struct {
                                 kd_loss_bwd_teacher return KD_ERR_WORKSPACE before enqueuing
                                 anything when it is below kd_saved_bytes_for. Not read
                                 otherwise (0 is fine). */
+  int32_t kl_output_unscaled; /* 1: the per-token `kl` output is the divergence without the
+                                T^2 factor (flash_kd, flash_ce_kd_loss Returns: the KD term is
+                                not multiplied by T^2); the loss and the gradients keep it.
+                                0: the per-token kl includes T^2 (nemo kd_loss, KDLoss
+                                temperature; orda-kernel, KL variants). */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).
@@ -196,7 +206,7 @@ enum {
   KD_KERNEL_MERGE = 2,     /* per-token merge of the vocabulary-tile records */
   KD_KERNEL_FINALIZE = 3,  /* loss reduction */
   KD_KERNEL_BWD_DZ = 4,    /* backward recompute tiles + logit-gradient epilogue */
-  KD_KERNEL_SCATTER = 5,   /* top-K: subtract p at the cached indices */
+  KD_KERNEL_SCATTER = 5,   /* reserved (the top-K p is subtracted inside the dz epilogue) */
   KD_KERNEL_GEMM_DW = 6,   /* dW[chunk] = dZ_chunk^T H */
   KD_KERNEL_GEMM_DH = 7,   /* dH += dZ_chunk W[chunk] */
   KD_KERNEL_GEMM_DWDH = 8, /* both GEMMs of a chunk in one launch */
@@ -272,8 +282,14 @@ kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd
                               void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
 
 /* Synchronises `stream`, then reads the device flags left in `workspace` by
- * the last kd_loss_fwd that used it: *flags (host, nullable) receives them;
- * returns KD_ERR_LABEL_RANGE if a label or top-K index was out of range. */
+ * the last call that used it (a backward that computes no logit gradient,
+ * as with a zero teacher-CE weight, leaves them as they were): *flags (host,
+ * nullable) receives them. Bit 0, set by
+ * kd_loss_fwd: a label or top-K index was out of range (returns
+ * KD_ERR_LABEL_RANGE). Bit 1, set by kd_loss_bwd / kd_loss_bwd_teacher with
+ * keep_last_chunk: `saved` was not written by a forward that kept its last
+ * chunk with the same vocab_chunk and n; the gradients are then NaN rather
+ * than silently wrong (returns KD_ERR_SAVED). */
 kd_status kd_read_status(const void* workspace, void* stream, int32_t* flags);
 
 /* Static description of a status code. */

@@ -12,6 +12,7 @@ LIB_PATH = os.environ.get("KD_LIBRARY") or os.path.join(os.path.dirname(os.path.
 # Status codes and enums (values fixed by include/kd_loss.h).
 KD_OK, KD_ERR_NULL, KD_ERR_SHAPE, KD_ERR_DTYPE, KD_ERR_PARAM = 0, 1, 2, 3, 4
 KD_ERR_ALIGN, KD_ERR_WORKSPACE, KD_ERR_UNSUPPORTED, KD_ERR_LABEL_RANGE, KD_ERR_HIP = 5, 6, 7, 8, 9
+KD_ERR_SAVED = 10
 KD_F32, KD_BF16 = 0, 1
 KD_STUDENT_PROJECTION, KD_STUDENT_LOGITS = 0, 1
 KD_TEACHER_TIED, KD_TEACHER_SEPARATE, KD_TEACHER_TOPK, KD_TEACHER_LOGITS = 1, 2, 3, 4
@@ -39,7 +40,8 @@ class KdParams(ctypes.Structure):
                 ("reduction", c_int32), ("normalizer", c_float), ("vocab_chunk", c_int64),
                 ("assume_valid_labels", c_int32), ("kl_divergence", c_int32),
                 ("teacher_temperature", c_float), ("compact_valid", c_int32),
-                ("keep_last_chunk", c_int32), ("saved_bytes", c_int64)]
+                ("keep_last_chunk", c_int32), ("saved_bytes", c_int64),
+                ("kl_output_unscaled", c_int32)]
 
 
 class KdOutputs(ctypes.Structure):

@@ -125,7 +125,7 @@ class Runner:
                  teacher_ce_weight=0.0, kl_weight=0.0, temperature=1.0, ignore_index=-100,
                  reduction="mean", normalizer=0.0, vocab_chunk=0, want_grads=True,
                  want_teacher_ce=None, kl_divergence="forward", teacher_temperature=None,
-                 compact_valid=False, keep_last_chunk=None):
+                 compact_valid=False, keep_last_chunk=False, kl_output_unscaled=False):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -191,12 +191,12 @@ class Runner:
         p.kl_divergence = _KL_DIVERGENCES[kl_divergence]
         p.teacher_temperature = 0.0 if teacher_temperature is None else float(teacher_temperature)
         p.compact_valid = 1 if compact_valid else 0
-        # By default the forward keeps its last chunk's products when a
-        # backward through the projections follows (identical results, one
-        # chunk's products fewer to recompute).
-        if keep_last_chunk is None:
-            keep_last_chunk = want_grads and s.kind == L.KD_STUDENT_PROJECTION
+        # Opt-in: the forward keeps its last chunk's fp32 products for the
+        # backward (identical results, one chunk fewer to recompute, at 4-8 B
+        # per token and column of that chunk); off, peak memory stays at the
+        # one-chunk slab.
         p.keep_last_chunk = 1 if keep_last_chunk else 0
+        p.kl_output_unscaled = 1 if kl_output_unscaled else 0
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
         self.teacher_kind = teacher_kind
@@ -287,9 +287,13 @@ class Runner:
             ctypes.byref(trace) if trace is not None else None)
         L.check(st, "kd_loss_bwd_teacher")
 
-    def read_status(self) -> int:
+    def read_status(self, backward: bool = False) -> int:
+        """Device flags of the last forward (or, with backward=True, the last
+        backward): 1 = a label / top-K index out of range, 2 = `saved` without
+        kept products of this layout."""
+        ws = self.ws_bwd if backward else self.ws_fwd
         flags = ctypes.c_int32(0)
-        self.lib.kd_read_status(self.ws_fwd.data_ptr(), self._stream(), ctypes.byref(flags))
+        self.lib.kd_read_status(ws.data_ptr(), self._stream(), ctypes.byref(flags))
         return int(flags.value)
 
 
@@ -342,6 +346,9 @@ class _FusedLoss(torch.autograd.Function):
         # teacher_hidden / teacher_weight are given only for a teacher trained
         # through its CE; otherwise None (the teacher is detached).
         runner.forward()
+        # The backward recomputes from these tensors: saving them lets autograd's
+        # version counters reject an in-place change between forward and backward.
+        ctx.save_for_backward(student_hidden, weight, teacher_hidden, teacher_weight)
         ctx.runner = runner
         ctx.train_teacher = getattr(runner, "train_teacher", False)
         ctx.used = False
@@ -355,6 +362,7 @@ class _FusedLoss(torch.autograd.Function):
         if ctx.used:
             raise RuntimeError("each fused forward supports one backward pass")
         ctx.used = True
+        ctx.saved_tensors  # raises if a saved input was modified in place since the forward
         r: Runner = ctx.runner
         need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         need_ht, need_wt = ctx.needs_input_grad[2], ctx.needs_input_grad[3]
@@ -383,7 +391,7 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
                       kl_teacher_temperature=None, kl_divergence="forward", ignore_index=-100,
                       reduction="mean", num_batch_labels=None, vocab_chunk=0,
                       return_teacher_ce=True, compact_valid=False,
-                      keep_last_chunk=None) -> DistillationLossOutput:
+                      keep_last_chunk=False) -> DistillationLossOutput:
     """Fused LM-head + CE + KL loss; differentiable in student_hidden and weight.
 
     The teacher is always detached. Returns the loss and the unweighted per-token
@@ -393,10 +401,11 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
     reported as zeros. compact_valid=True leaves the rows whose label is
     ignored out of every projection (tied and projected teachers): their
     per-token terms are reported as 0, the loss and gradients are unchanged.
-    keep_last_chunk (default: when a backward can follow) keeps the forward's
-    last vocabulary chunk of fp32 products for the backward, which then does
-    not recompute it: identical results for 8 B per token and column of that
-    chunk (4 B without a projected teacher); False keeps memory at the minimum.
+    keep_last_chunk=True (opt-in) keeps the forward's last vocabulary chunk of
+    fp32 products for the backward, which then does not recompute it:
+    identical results for 8 B per token and column of that chunk (4 B without
+    a projected teacher). Off by default, so the extra memory stays at the
+    one-chunk gradient slab.
     """
     if kl_divergence not in _KL_DIVERGENCES:
         raise ValueError(f"kl_divergence={kl_divergence!r}; one of {tuple(_KL_DIVERGENCES)}")
@@ -451,11 +460,9 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
     if compact_valid and (labels is None or kw["teacher_kind"] not in ("tied", "separate")):
         raise NotImplementedError("compact_valid needs labels and a tied or projected teacher")
     kw["compact_valid"] = bool(compact_valid)
-    if keep_last_chunk is None:
-        # keep the last chunk's products only when a backward can follow
-        keep_last_chunk = torch.is_grad_enabled() and any(
-            x is not None and x.requires_grad for x in (student_hidden, weight, t_hidden, t_weight))
-    kw["keep_last_chunk"] = bool(keep_last_chunk)
+    # the kept products only pay off when a backward follows
+    kw["keep_last_chunk"] = bool(keep_last_chunk) and torch.is_grad_enabled() and any(
+        x is not None and x.requires_grad for x in (student_hidden, weight, t_hidden, t_weight))
     if labels is not None:
         kw["labels"] = labels.to(torch.int64).contiguous()
     runner = Runner(**kw)
@@ -520,9 +527,13 @@ class KDLoss(torch.nn.Module):
         v = student_logits.shape[-1]
         if teacher_logits.shape != student_logits.shape:
             raise ValueError("teacher_logits must have the student logits' shape")
+        if teacher_logits.dtype != student_logits.dtype:
+            # no silent cast: an fp32 teacher rounded to bf16 would lose precision
+            raise TypeError(f"teacher_logits dtype {teacher_logits.dtype} differs from the student "
+                            f"logits' {student_logits.dtype}; convert one of them explicitly")
         z = student_logits.reshape(-1, v)
         runner = Runner(student_logits=z.detach().contiguous(), teacher_kind="logits",
-                        teacher_logits=teacher_logits.detach().reshape(-1, v).to(z.dtype).contiguous(),
+                        teacher_logits=teacher_logits.detach().reshape(-1, v).contiguous(),
                         labels=labels.reshape(-1).to(torch.int64).contiguous(),
                         student_ce_weight=0.0, teacher_ce_weight=0.0, kl_weight=1.0,
                         temperature=self.temperature, ignore_index=self.ignore_index,
@@ -545,7 +556,7 @@ def flash_ce_kd_loss(student_logits, teacher_hidden, teacher_lm_head_weight, lab
                    teacher_hidden=teacher_hidden.contiguous(),
                    teacher_weight=teacher_lm_head_weight.contiguous(), student_ce_weight=1.0,
                    kl_weight=1.0, temperature=temperature, ignore_index=ignore_index,
-                   reduction="none", vocab_chunk=chunk_size, want_grads=False)
+                   reduction="none", vocab_chunk=chunk_size, want_grads=False,
+                   kl_output_unscaled=True)
         r.forward()
-        kd = r.kl / (temperature * temperature)
-        return r.student_ce.clone(), kd
+        return r.student_ce.clone(), r.kl.clone()

@@ -116,6 +116,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   if (p->compact_valid != 0 && p->compact_valid != 1) return KD_ERR_PARAM;
   if (p->keep_last_chunk != 0 && p->keep_last_chunk != 1) return KD_ERR_PARAM;
   if (p->saved_bytes < 0) return KD_ERR_PARAM;
+  if (p->kl_output_unscaled != 0 && p->kl_output_unscaled != 1) return KD_ERR_PARAM;
   if (p->compact_valid && q.mode != kd::MODE_TIED && q.mode != kd::MODE_SEPARATE)
     return KD_ERR_UNSUPPORTED;
 
@@ -128,6 +129,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.reduction = p->reduction;
   q.normalizer = p->normalizer;
   q.kl = p->kl_divergence;
+  q.kl_unscaled = p->kl_output_unscaled;
   // Student statistics at z/T: needed for the KL at T != 1, and always for the
   // reverse direction, whose weights are the student's softmax(z/T).
   q.need_zT = (q.T != 1.f || q.kl != KD_KL_FORWARD) ? 1 : 0;
@@ -204,7 +206,14 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   }
   q.fwd_bytes = off;
   q.off_dz = off_common;
-  q.bwd_bytes = align_up(q.off_dz + (size_t)q.dz_rows * (size_t)q.chunk * elem, 256);
+  off = align_up(q.off_dz + (size_t)q.dz_rows * (size_t)q.chunk * elem, 256);
+  if (q.mode == kd::MODE_TOPK) {
+    q.off_btks = off;
+    off = align_up(off + 8 * (size_t)q.n * (size_t)q.k, 256);
+    q.off_btko = off;
+    off = align_up(off + 4 * (size_t)q.n * (size_t)(q.chunk / vt + 1), 256);
+  }
+  q.bwd_bytes = off;
   // The last chunk's products, kept in `saved` for the backward: columns of
   // that chunk rounded up to whole tiles, every row of the token tiles.
   q.saved_bytes = 20 * (size_t)q.n + kd::kSavedHeaderBytes;
@@ -355,7 +364,8 @@ kd_status kd_read_status(const void* workspace, void* stream, int32_t* flags) {
   int32_t f = 0;
   if (hipMemcpy(&f, workspace, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess) return KD_ERR_HIP;
   if (flags) *flags = f;
-  return f ? KD_ERR_LABEL_RANGE : KD_OK;
+  if (f & kd::kFlagSaved) return KD_ERR_SAVED;
+  return (f & kd::kFlagRange) ? KD_ERR_LABEL_RANGE : KD_OK;
 }
 
 const char* kd_status_string(kd_status st) {
@@ -370,6 +380,7 @@ const char* kd_status_string(kd_status st) {
     case KD_ERR_UNSUPPORTED: return "unsupported combination";
     case KD_ERR_LABEL_RANGE: return "a label or top-K index was out of range";
     case KD_ERR_HIP: return "HIP runtime error";
+    case KD_ERR_SAVED: return "saved holds no kept products of this layout (forward/backward mismatch)";
     default: return "unknown status";
   }
 }

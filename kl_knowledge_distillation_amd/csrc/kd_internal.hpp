@@ -29,6 +29,14 @@ constexpr size_t kNvOffset = 8;
 // `saved`: [n] x 16 bytes of row statistics, a 64-byte header at 16 n, then
 // [n] fp32 lse(t) at T = 1 (the teacher-CE backward) at 16 n + 64.
 constexpr size_t kSavedHeaderBytes = 64;
+// Header words (4 bytes each, from 16 n): 0 den, 1 n_valid, 2 n_bad (fp32);
+// 4..8 the layout of the kept products (int32): kKeepMagic or 0, chunk,
+// keep_ld, keep_ops, n. A backward that reads kept products checks them.
+constexpr int kHdrKeep = 4;
+constexpr int32_t kKeepMagic = 0x4b454550;
+// Device flag bits of the workspace's first word (kd_read_status).
+constexpr int32_t kFlagRange = 1;  // forward: a label or top-K index out of range
+constexpr int32_t kFlagSaved = 2;  // backward: `saved` holds no kept products of this layout
 // Given-logits row kernels: one wave per (row, slice of the row); each lane
 // takes kRowUnroll 16-byte chunks of each matrix per step, and a launch aims
 // at about kRowWaves waves (8 per SIMD over 256 CUs, twice over).
@@ -54,6 +62,7 @@ struct Plan {
   int reduction = KD_REDUCE_MEAN;
   float normalizer = 0.f;
   int kl = KD_KL_FORWARD;  // KD_KL_*
+  int kl_unscaled = 0;     // the per-token kl output without the T^2 factor
   int need_zT = 0;    // statistics at z/T kept apart from z (T != 1, or a reverse-direction KL)
   int need_t1 = 0;    // teacher statistics at t kept apart from t/T_t (T_t != 1)
   int has_labels = 0;
@@ -76,8 +85,11 @@ struct Plan {
   // fp32 prob [n][k]) and where each vocabulary tile of one forward launch
   // starts its run of them (int32 [n][fwd_slices + 1])
   size_t off_tks = 0, off_tko = 0;
-  // backward workspace layout
+  // backward workspace layout; top-K: the row entries sorted again (off_btks,
+  // as off_tks) and where each tile of one chunk starts its run (off_btko,
+  // int32 [n][chunk / vt_rows + 1]), so the dz epilogue subtracts p itself
   size_t off_dz = 0, bwd_bytes = 0;
+  size_t off_btks = 0, off_btko = 0;
   // Kept products of the last chunk in `saved` (keep_last_chunk): keep_ops
   // fp32 [dz_rows][keep_ld] matrices (student, then teacher) from byte keep_off.
   int keep = 0, keep_ops = 0;

@@ -18,8 +18,8 @@
 // Backward (kd_loss_bwd), per vocabulary chunk (CompactifAI/Full-Chunked-KL-
 // Loss, Full Chunked KL: recompute each chunk, apply the closed-form gradient):
 //   bwd_dz    recompute the chunk's logit tiles, form dz in registers from the
-//             saved lse values, round and store the (n x chunk) slab.
-//   scatter   top-K only: subtract (g/den) w_kl p at the cached indices.
+//             saved lse values (top-K: minus (g/den) w_kl p at the row's cached
+//             indices in the tile), round once and store the (n x chunk) slab.
 //   gemm_dw   dW[chunk] = dz^T H_s       (K = n)
 //   gemm_dh   dH += dz W[chunk]          (K = chunk)
 #include <limits.h>
@@ -675,7 +675,7 @@ struct PrepArgs {
   int64_t n, d, dt, v, ignore;
   int k;
   int want_teacher;  // teacher label logit needed (teacher CE weight or output)
-  float* prep;       // [4][n]: z[y] | S, t[y] | E, M, flag
+  float* prep;       // [4][n]: z[y] | S, t[y] | E, M, flag; null: not written
   // top-K: the row's entries sorted by index (an index outside [0, v) as v,
   // last)
   int32_t* sidx;
@@ -764,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrepArgs a) {
       }
     }
   }
-  if (lane == 0) {
+  if (lane == 0 && a.prep) {  // (the backward only wants the sorted entries)
     a.prep[i] = f0;
     a.prep[a.n + i] = f1;
     a.prep[2 * a.n + i] = f2;
@@ -1179,6 +1179,7 @@ struct MergeArgs {
   float T;
   int need_zT, need_t1, teacher_ce;
   int kl;             // KD_KL_*
+  int kl_unscaled;    // the per-token kl output without T^2
   float ws, wt, wkl;
   float* out_sce;
   float* out_tce;
@@ -1243,12 +1244,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       const float lzT = a.need_zT ? kLn2 * (s.mzT + log2f(s.szT)) : lz1;
       const float f0 = a.prep[i], f1 = a.prep[a.n + i], f2 = a.prep[2 * a.n + i];
       const float flag = a.prep[3 * a.n + i];
-      float sce = 0.f, tce = 0.f, kl, ltT = 0.f, mass = 0.f, lt1 = 0.f;
+      float sce = 0.f, tce = 0.f, kl, kl_raw, ltT = 0.f, mass = 0.f, lt1 = 0.f;
       bool valid;
       if (a.mode == MODE_TOPK) {
         // sum p log p - sum p z[idx] + M lse(z); the cross term is the sum of
         // the tiles' record field 6
         kl = f1 - s.a + f2 * lz1;
+        kl_raw = kl;  // T = 1
         mass = f2;
         valid = true;
       } else {
@@ -1259,7 +1261,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
         // (orda-kernel, KL variants: forward, reverse, jeffreys = their sum).
         const float kl_f = s.a / (s.stT * a.T) - ltT + lzT;
         const float kl_r = (a.kl != KD_KL_FORWARD) ? s.ar / (s.szT * a.T) - lzT + ltT : 0.f;
-        kl = a.T * a.T * ((a.kl != KD_KL_REVERSE ? kl_f : 0.f) + kl_r);
+        kl_raw = (a.kl != KD_KL_REVERSE ? kl_f : 0.f) + kl_r;
+        kl = a.T * a.T * kl_raw;
         mass = kl_r;  // the reverse-direction gradient needs this row's KL(P_S || P_T)
         valid = flag == 1.f;
         sce = valid ? lz1 - f0 : 0.f;
@@ -1276,7 +1279,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       }
       if (a.out_sce) a.out_sce[i] = sce;
       if (a.out_tce) a.out_tce[i] = tce;
-      if (a.out_kl) a.out_kl[i] = kl;
+      if (a.out_kl) a.out_kl[i] = a.kl_unscaled ? kl_raw : kl;
       if (a.saved) {
         float4 sv = make_float4(lz1, lzT, ltT, mass);
         reinterpret_cast<float4*>(a.saved)[i] = sv;
@@ -1345,8 +1348,9 @@ struct FinalArgs {
   float normalizer;
   int reduction;
   float* loss;       // nullable
-  float* saved_hdr;  // nullable: [den, n_valid, n_bad, 0]
+  float* saved_hdr;  // nullable: [den, n_valid, n_bad, 0], then the kept layout
   int32_t* status;   // workspace flag word
+  int32_t keep_tag[5];  // kKeepMagic (or 0 when nothing was kept), chunk, keep_ld, keep_ops, n
 };
 
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
@@ -1382,8 +1386,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
       a.saved_hdr[1] = (float)n_valid;
       a.saved_hdr[2] = (float)n_bad;
       a.saved_hdr[3] = 0.f;
+      int32_t* tag = reinterpret_cast<int32_t*>(a.saved_hdr) + kHdrKeep;
+      for (int j = 0; j < 5; ++j) tag[j] = a.keep_tag[j];
     }
-    a.status[0] = n_bad > 0.0 ? 1 : 0;
+    a.status[0] = n_bad > 0.0 ? kFlagRange : 0;
   }
 }
 
@@ -1420,6 +1426,18 @@ struct BwdArgs {
   // teacher's keep_t elements after the student's
   const float* keep;
   int64_t keep_t;
+  // the layout the kept products must have (header words kHdrKeep.. of saved)
+  int32_t keep_tag[5];
+  // top-K: each row's entries sorted by index and where each tile of this
+  // chunk starts its run of them ([n][n_vt + 1]); the epilogue subtracts p
+  const int32_t* tk_sidx;
+  const float* tk_sprob;
+  const int32_t* tk_off;
+  int k;
+  // workspace flag word: the chunk's first launch and the kept launch set it
+  // (kFlagSaved when the kept products are not of the expected layout)
+  int32_t* status;
+  int set_status;
 };
 
 template <typename T>
@@ -1463,6 +1481,16 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   const T* W = static_cast<const T*>(a.w);
   const T* ht = static_cast<const T*>(a.ht);
   const T* Wt = static_cast<const T*>(a.wt);
+  // Kept products are read only if the forward that wrote `saved` kept them
+  // in this layout (its header says so); otherwise every dz of the chunk is
+  // NaN and the flag is raised, so the gradients cannot be silently wrong.
+  bool kept_ok = true;
+  if constexpr (kKept) {
+    const int32_t* tag = reinterpret_cast<const int32_t*>(a.saved + 4 * a.n) + kHdrKeep;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) kept_ok = kept_ok && tag[j] == a.keep_tag[j];
+  }
+  if (a.set_status && blockIdx.x == 0 && tid == 0) a.status[0] = kept_ok ? 0 : kFlagSaved;
 
   f32x4 acc[NB][kMB][kNB];
   f32x4 tacc[1][kMB][kNB];
@@ -1559,6 +1587,21 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     const float rev0 = sv.z - sv.y - mass;   // lse(t/T) - lse(z/T) - KL(P_S || P_T)
     const float invT = 1.f / a.T;
     T* row = dz + tok * a.ldz + (v0 - a.c0);
+    // top-K: this token's run of index-sorted entries in this tile, whose p is
+    // subtracted before the one rounding of dz (each index is distinct)
+    int j0 = 0, j1 = 0;
+    const int32_t* tix = nullptr;
+    const float* tpr = nullptr;
+    if constexpr (MODE == MODE_TOPK) {
+      if (live) {
+        const int32_t* off = a.tk_off + tok * (int64_t)(a.n_vt + 1) + vt;
+        j0 = off[0];
+        j1 = off[1];
+        tix = a.tk_sidx + tok * (int64_t)a.k;
+        tpr = a.tk_sprob + tok * (int64_t)a.k;
+      }
+    }
+    const float cp = coef * a.wkl;           // top-K: the p term
     // kept products of this token block: the student's (MODE_TCE: the
     // teacher's) and, for a TIED or SEPARATE teacher, the teacher's
     f32x4 zk[kMB], tk[kMB];
@@ -1603,6 +1646,19 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
         }
         o[r] = (k < lim) ? dv : 0.f;
       }
+      if constexpr (MODE == MODE_TOPK) {
+        // entries at this lane's four rows of block mb: v0 + rb + 16 mb + r
+        const int base = (int)(v0 + rb) + 16 * mb;
+        for (int j = j0; j < j1; ++j) {
+          const int d = tix[j] - base;
+          const float q = cp * tpr[j];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] -= (d == r) ? q : 0.f;
+        }
+      }
+      if constexpr (kKept) {
+        if (!kept_ok) o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
+      }
       store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
     }
   }
@@ -1615,37 +1671,6 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     if (kStudentKl && a.kl != KD_KL_FORWARD) epilogue(std::true_type{}, std::false_type{});
     else epilogue(std::false_type{}, std::false_type{});
   }
-}
-
-// Top-K: dz[i, idx - c0] -= (g/den) w_kl p for the entries of this chunk.
-// Indices are distinct per row, so every element has a single writer.
-struct ScatterArgs {
-  const int32_t* idx;
-  const float* prob;
-  int k;
-  int64_t n, v, c0, cw;
-  const float* saved;
-  const float* grad;
-  float wkl;
-  void* dz;
-  int64_t ldz;
-};
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void scatter_kernel(ScatterArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (e >= a.n * a.k) return;
-  const int32_t ix = a.idx[e];
-  if (ix < 0 || (int64_t)ix >= a.v) return;
-  const int64_t off = (int64_t)ix - a.c0;
-  if (off < 0 || off >= a.cw) return;
-  const int64_t i = e / a.k;
-  const float den = a.saved[4 * a.n];
-  const float g = a.grad ? *a.grad : 1.f;
-  T* p = static_cast<T*>(a.dz) + i * a.ldz + off;
-  const float nv = to_f32(*p) - (g / den) * a.wkl * a.prob[e];
-  if constexpr (sizeof(T) == 2) *p = bf16_rne(nv);
-  else *p = nv;
 }
 
 // ---------------------------------------------------------------------------
@@ -2113,7 +2138,7 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   }
 
   MergeArgs ma{rec, prep, last_slices, folded ? run : nullptr, p.n, p.mode, p.T, p.need_zT, need_t1,
-               (p.mode != MODE_TOPK) ? 1 : 0, p.kl, p.ws, p.wt, p.wkl,
+               (p.mode != MODE_TOPK) ? 1 : 0, p.kl, p.kl_unscaled, p.ws, p.wt, p.wkl,
                out ? out->student_ce : nullptr, out ? out->teacher_ce : nullptr,
                out ? out->kl : nullptr, static_cast<float*>(saved), part, cp.pos};
   ma.teacher_ce = pa.want_teacher;
@@ -2122,7 +2147,9 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
   }));
 
   FinalArgs fin{part, p.merge_blocks, p.normalizer, p.reduction, out ? out->loss : nullptr,
-                saved ? static_cast<float*>(saved) + 4 * p.n : nullptr, status};
+                saved ? static_cast<float*>(saved) + 4 * p.n : nullptr, status,
+                {p.keep ? kKeepMagic : 0, (int32_t)p.chunk, (int32_t)p.keep_ld, p.keep_ops,
+                 (int32_t)p.n}};
   KD_TRY(L.run(KD_KERNEL_FINALIZE, [&] { finalize_kernel<<<1, kThreads, 0, stream>>>(fin); }));
   return KD_OK;
 }
@@ -2166,6 +2193,18 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
   const T* hs = static_cast<const T*>(teacher ? cp.ht : cp.hs);
   const T* wmat = static_cast<const T*>(teacher ? x.wt : x.w);
   const int mode = teacher ? (int)MODE_TCE : p.mode;
+  // Top-K: each row's entries sorted by index, as the forward sorted them, so
+  // the dz epilogue finds the entries of each tile as one run.
+  int32_t* tk_idx = reinterpret_cast<int32_t*>(base + p.off_btks);
+  float* tk_prob = reinterpret_cast<float*>(base + p.off_btks + 4 * (size_t)p.n * (size_t)p.k);
+  int32_t* tk_off = reinterpret_cast<int32_t*>(base + p.off_btko);
+  if (mode == MODE_TOPK) {
+    PrepArgs pa{x.hs, x.w, x.ht, x.wt, x.logits, x.tlogits, x.labels, x.topk_idx, x.topk_prob,
+                p.n, p.d, p.dt, p.v, p.ignore, p.k, 0, nullptr, tk_idx, tk_prob};
+    KD_TRY(L.run(KD_KERNEL_PREP, [&] {
+      prep_kernel<T, MODE_TOPK><<<dim3((unsigned)((p.n + 3) / 4)), kThreads, 0, stream>>>(pa);
+    }));
+  }
   for (int c = 0; c < p.n_chunks; ++c) {
     const int64_t c0 = (int64_t)c * p.chunk;
     const int64_t cw = (p.v - c0 < p.chunk) ? (p.v - c0) : p.chunk;  // valid columns
@@ -2181,6 +2220,22 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     if (kept) {
       ba.keep = reinterpret_cast<const float*>(static_cast<const uint8_t*>(saved) + p.keep_off);
       ba.keep_t = (p.keep_ops == 2) ? p.dz_rows * p.keep_ld : 0;
+      const int32_t tag[5] = {kKeepMagic, (int32_t)p.chunk, (int32_t)p.keep_ld, p.keep_ops, (int32_t)p.n};
+      for (int j = 0; j < 5; ++j) ba.keep_tag[j] = tag[j];
+    }
+    ba.status = reinterpret_cast<int32_t*>(base);
+    ba.set_status = (c == 0 || kept) ? 1 : 0;
+    if (mode == MODE_TOPK) {
+      ba.tk_sidx = tk_idx;
+      ba.tk_sprob = tk_prob;
+      ba.tk_off = tk_off;
+      ba.k = p.k;
+      const TileStartArgs ts{tk_idx, p.n, p.v, p.k, G::kVT, (int)(c0 / G::kVT), n_vt, tk_off};
+      const int64_t cnt = p.n * (int64_t)(n_vt + 1);
+      KD_TRY(L.run(KD_KERNEL_PREP, [&] {
+        topk_tile_starts_kernel<<<dim3((unsigned)((cnt + kThreads - 1) / kThreads)), kThreads, 0,
+                                  stream>>>(ts);
+      }));
     }
     const dim3 grid((unsigned)((int64_t)n_vt * p.n_ttiles));
     auto launch = [&](auto kept_tag) {
@@ -2197,14 +2252,6 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       if (kept) launch(std::true_type{});
       else launch(std::false_type{});
     }));
-    if (mode == MODE_TOPK) {
-      ScatterArgs sa{x.topk_idx, x.topk_prob, p.k, p.n, p.v, c0, cw,
-                     static_cast<const float*>(saved), grad, p.wkl, dz, ldz};
-      const int64_t ne = p.n * p.k;
-      KD_TRY(L.run(KD_KERNEL_SCATTER, [&] {
-        scatter_kernel<T><<<dim3((unsigned)((ne + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(sa);
-      }));
-    }
     const int64_t cpad = (int64_t)n_vt * G::kVT;  // columns written by bwd_dz
     const int n_gemm_mt = (int)((cw + kTile - 1) / kTile);
     if constexpr (G::kPipe) {

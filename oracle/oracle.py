@@ -495,6 +495,28 @@ def backward_rows(student: Student, teacher: Teacher, p: Params, labels, rows,
     return out
 
 
+def weight_grad_rows(student: Student, teacher: Teacher, p: Params, labels, vrows, den: float,
+                     grad_loss: float = 1.0, progress=None) -> np.ndarray:
+    """dW restricted to the vocabulary rows `vrows`: dW[v, :] = sum_i dz[i, v] H[i, :].
+
+    Each dz[i, v] needs that token's normalisers over all V columns, so every
+    row block's full-vocabulary logits are formed (logit_grad) and only the
+    columns `vrows` of its gradient are kept (CompactifAI/Full-Chunked-KL-Loss,
+    Full Chunked KL: the weight gradient from the closed-form logit gradient).
+    `progress(done_rows, n)` is called after each row block. float64 (len(vrows), D).
+    """
+    vrows = np.asarray(vrows, dtype=np.int64)
+    n = student.n
+    out = np.zeros((len(vrows), student.hidden.shape[1]), F64)
+    for b in range(0, n, ROW_BLOCK):
+        r = np.arange(b, min(b + ROW_BLOCK, n))
+        g = logit_grad(student, teacher, p, labels, r, den, grad_loss)
+        out += g[:, vrows].T @ as_f64(student.hidden[r])
+        if progress is not None:
+            progress(int(r[-1]) + 1, n)
+    return out
+
+
 def teacher_logit_grad(student: Student, teacher: Teacher, p: Params, labels, rows: np.ndarray,
                        den: float, grad_loss: float = 1.0) -> np.ndarray:
     """d loss / d t for the given rows of a teacher trained through its CE.

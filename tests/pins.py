@@ -725,4 +725,33 @@ def check_backward_rows_consistent(O):
         _close(O.backward_rows(s, t, p, y, rows, out["den"]), dH[rows], what=f"rows {name}")
 
 
+def check_weight_grad_rows_finite_differences(O):
+    """dW on a subset of vocabulary rows matches central differences of the
+    reduced loss in those rows of W (float64, h = 1e-6, 1e-6 relative), for
+    every teacher kind; rows given out of order and with the last row."""
+    cases, Hs, W = _fd_cases(O)
+    h = 1e-6
+    vrows = np.array([7, 0, 8, 3])
+    for name, t, y, p in cases:
+        g_up = 0.6
+        t_fixed = O.Teacher("separate", hidden=t.hidden, weight=W.copy()) if t.kind == "tied" else t
+
+        def loss(W_):
+            return O.forward(O.Student(hidden=Hs, weight=W_), t_fixed, p, y)["loss"] * g_up
+
+        s = O.Student(hidden=Hs, weight=W)
+        den = O.forward(s, t, p, y)["den"]
+        got = O.weight_grad_rows(s, t, p, y, vrows, den, grad_loss=g_up)
+        num = np.zeros_like(got)
+        for a, v in enumerate(vrows):
+            for j in range(W.shape[1]):
+                Wp = W.copy()
+                Wm = W.copy()
+                Wp[v, j] += h
+                Wm[v, j] -= h
+                num[a, j] = (loss(Wp) - loss(Wm)) / (2 * h)
+        err = np.max(np.abs(num - got)) / max(np.max(np.abs(got)), 1e-30)
+        assert err < 1e-6, f"weight_grad_rows finite differences {name}: {err:.2e}"
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -134,8 +134,10 @@ def test_saved_bytes_for_keep_last_chunk():
 
 def test_status_strings():
     lib = L.load()
-    for code in range(10):
+    for code in range(11):
         assert lib.kd_status_string(code)
+        assert lib.kd_status_string(code) != b"unknown status"
+    assert lib.kd_status_string(L.KD_ERR_SAVED) != lib.kd_status_string(L.KD_ERR_LABEL_RANGE)
     assert lib.kd_status_string(L.KD_OK) == b"ok"
 
 
@@ -169,16 +171,22 @@ def test_forward_workspace_is_O_n_chunk_not_n_vocab():
 
 
 def test_backward_workspace_is_O_n_chunk_not_n_vocab():
-    # topk-sized problem: the dz slab is n * chunk * 2 bytes, far below n * v * 4
-    s, t, p = _desc("topk", n=32768, d=4096, v=151936, k=100)
-    p.vocab_chunk = 8192
+    # topk-sized problem: the dz slab is n * chunk * 2 bytes, far below n * v * 4,
+    # plus the row entries sorted by index (8 n k) and where each tile of a
+    # chunk starts its run of them (4 n (chunk / 256 + 1))
+    n, k = 32768, 100
+    s, t, p = _desc("topk", n=n, d=4096, v=151936, k=k)
+    for chunk in (8192, 16384):
+        p.vocab_chunk = chunk if chunk != 16384 else 0  # 0: the default chunk
+        st, bwd = _ws(s, t, p, 1)
+        assert st == L.KD_OK
+        want = n * chunk * 2 + 8 * n * k + 4 * n * (chunk // 256 + 1)
+        assert want <= bwd <= want + (1 << 16)
+        assert bwd < n * 151936 * 4 / 8
+    # the other teachers need the slab alone
+    s, t, p = _desc("tied", n=4096, d=2048, v=32000)
     st, bwd = _ws(s, t, p, 1)
-    assert st == L.KD_OK
-    assert bwd <= 32768 * 8192 * 2 + (1 << 16)
-    assert bwd < 32768 * 151936 * 4 / 8
-    p.vocab_chunk = 0  # the default chunk: 16384 columns
-    st, bwd = _ws(s, t, p, 1)
-    assert st == L.KD_OK and 32768 * 16384 * 2 <= bwd <= 32768 * 16384 * 2 + (1 << 16)
+    assert st == L.KD_OK and 4096 * 16384 * 2 <= bwd <= 4096 * 16384 * 2 + (1 << 16)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -196,6 +204,7 @@ def test_backward_workspace_is_O_n_chunk_not_n_vocab():
     ("tT_neg", L.KD_ERR_PARAM), ("tT_nan", L.KD_ERR_PARAM), ("topk_tT", L.KD_ERR_UNSUPPORTED),
     ("tlog_null", L.KD_ERR_NULL), ("tlog_misaligned", L.KD_ERR_ALIGN),
     ("topk_compact", L.KD_ERR_UNSUPPORTED), ("compact_bad", L.KD_ERR_PARAM),
+    ("unscaled_bad", L.KD_ERR_PARAM),
 ])
 def test_forward_rejects_invalid_arguments(case, expect):
     kind = "topk" if case.startswith("topk") else ("separate" if case.startswith("sep") else "tied")
@@ -265,6 +274,8 @@ def test_forward_rejects_invalid_arguments(case, expect):
         p.compact_valid = 1
     elif case == "compact_bad":
         p.compact_valid = 2
+    elif case == "unscaled_bad":
+        p.kl_output_unscaled = 2
     elif case == "tlog_null":
         t.kind = L.KD_TEACHER_LOGITS
         t.logits = None

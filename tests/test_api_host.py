@@ -73,3 +73,11 @@ def test_precomputed_teacher_must_not_require_grad():
     t = api.PrecomputedTeacher(logits=torch.zeros(4, 16, requires_grad=True))
     with pytest.raises(ValueError, match="require grad"):
         api.distillation_loss(h, w, y, t)
+
+
+def test_kdloss_rejects_mixed_dtypes_instead_of_casting():
+    """An fp32 teacher with a bf16 student is an error, not a silent rounding."""
+    z = torch.zeros(4, 16, dtype=torch.bfloat16)
+    t = torch.zeros(4, 16, dtype=torch.float32)
+    with pytest.raises(TypeError, match="dtype"):
+        api.KDLoss()(z, t, torch.zeros(4, dtype=torch.int64))

@@ -63,3 +63,64 @@ def test_kept_last_chunk_flops():
     assert abs(tt["total"] - f["total"] - (2 * n * d * chunk + 4 * n * d * v)) <= 1e-6 * tt["total"]
     # nothing is kept without a backward through projections
     assert bench.kept_columns(WORKLOADS["scorer_bf16"], chunk, True) == 0
+
+
+def test_matrix_records_a_failing_child_and_goes_on(tmp_path):
+    """The matrix parent keeps going past a child that fails: the failed entry
+    carries its exit status and stderr, the next entry's JSON line is kept."""
+    import io
+    import sys
+    ok_py = tmp_path / "ok.py"
+    ok_py.write_text('import json\nprint("progress")\nprint(json.dumps({"value": 1.5}))\n')
+    bad_py = tmp_path / "bad.py"
+    bad_py.write_text('import sys\nsys.stderr.write("kernel launch failed\\n")\nsys.exit(3)\n')
+    silent_py = tmp_path / "silent.py"
+    silent_py.write_text('print("no json here")\n')
+    log = io.StringIO()
+    res = bench.run_matrix([("bad", [sys.executable, str(bad_py)]),
+                            ("ok", [sys.executable, str(ok_py)]),
+                            ("silent", [sys.executable, str(silent_py)])], log=log)
+    assert [r["status"] for r in res] == ["FAILED", "OK", "FAILED"]
+    assert res[0]["exit"] == 3 and "kernel launch failed" in res[0]["error"]
+    assert res[1]["result"] == {"value": 1.5}
+    assert res[2]["exit"] == 0  # exited cleanly but printed no result line
+    assert "bad: FAILED" in log.getvalue() and "ok: OK" in log.getvalue()
+
+
+def test_matrix_times_out_a_hung_child(tmp_path):
+    import io
+    import sys
+    hang = tmp_path / "hang.py"
+    hang.write_text("import time\ntime.sleep(60)\n")
+    res = bench.run_matrix([("hang", [sys.executable, str(hang)])], timeout_s=1.0, log=io.StringIO())
+    assert res[0]["status"] == "FAILED" and res[0]["exit"] == "timeout"
+
+
+def test_matrix_entries_cover_the_workloads_and_the_scorer_sweep():
+    labels = [e[0] for e in bench.MATRIX]
+    for w in ("tiny_tied_fp32", "quickstart_tied_bf16", "separate_bf16", "topk_bf16"):
+        assert w in labels
+    chunks = sorted(int(a[a.index("--vocab-chunk") + 1]) for _, a in bench.MATRIX
+                    if "scorer_bf16" in a)
+    assert chunks == [2048, 8192, 16384]
+
+
+def test_bench_matrix_on_a_machine_without_the_gpu_path():
+    """End to end on the CPU: `bench.py --matrix` runs the real child, which
+    cannot reach a GPU here and fails; the parent records FAILED and exits 0."""
+    import json
+    import os
+    import subprocess
+    import sys
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: the child would run")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--matrix",
+                        "--matrix-only", "tiny_tied_fp32", "--steps", "1", "--warmup", "1",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    lines = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+    assert lines[0]["label"] == "tiny_tied_fp32" and lines[0]["status"] == "FAILED"
+    assert lines[0]["error"]
+    assert lines[-1] == {"matrix": 1, "ok": 0, "failed": 1}

@@ -215,13 +215,13 @@ def test_kdloss_given_logits_autograd():
 
 
 def test_distillation_loss_keep_last_chunk_identical_gradients():
-    """keep_last_chunk on (the default with a backward) and off give the same
-    loss and bit-identical gradients through autograd."""
+    """keep_last_chunk on (opt-in) and off (the default) give the same loss and
+    bit-identical gradients through autograd."""
     w = WORKLOADS["quickstart_tied_bf16"].scaled(n=260, d=256, v=2100)
     say("[api] keep_last_chunk on / off")
     x = make_inputs(w, "cuda", seed=12)
     res = []
-    for keep in (None, False):
+    for keep in (True, False):
         hs = x["student_hidden"].clone().requires_grad_(True)
         W = x["weight"].clone().requires_grad_(True)
         out = api.distillation_loss(hs, W, x["labels"], api.TiedTeacher(x["teacher_hidden"]),
@@ -238,3 +238,20 @@ def test_distillation_loss_keep_last_chunk_identical_gradients():
                                     api.TiedTeacher(x["teacher_hidden"]), kl_weight=0.5,
                                     kl_temperature=2.0, vocab_chunk=512, ignore_index=w.ignore_index)
     assert torch.equal(out.loss, res[0][0])
+
+
+def test_in_place_change_between_forward_and_backward_is_an_error():
+    """The backward recomputes from the inputs, so autograd must reject a
+    student hidden state or weight changed in place after the forward."""
+    w = WORKLOADS["quickstart_tied_bf16"].scaled(n=130, d=128, v=1000)
+    x = make_inputs(w, "cuda", seed=15)
+    for which in ("hidden", "weight"):
+        hs = x["student_hidden"].clone().requires_grad_(True)
+        W = x["weight"].clone().requires_grad_(True)
+        out = api.distillation_loss(hs, W, x["labels"], api.TiedTeacher(x["teacher_hidden"]),
+                                    kl_weight=0.5, kl_temperature=2.0, ignore_index=w.ignore_index)
+        with torch.no_grad():
+            (hs if which == "hidden" else W).mul_(2.0)
+        with pytest.raises(RuntimeError, match="modified by an inplace operation"):
+            out.loss.backward()
+    torch.cuda.synchronize()

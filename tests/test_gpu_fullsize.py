@@ -17,11 +17,21 @@ the rest:
   * the loss equals the masked, weighted sum of the per-token outputs over the
     labels' denominator.
 
+  * dW itself, element by element, on 1024 seeded vocabulary rows (the first
+    and last, both sides of a 256-row tile edge and of the chunk edges, and
+    random rows): the oracle forms every token's full-vocabulary logits in
+    float64 (its own lse over all V columns, never the GPU's saved values) and
+    keeps those columns of the gradient.
+
+The scorer is checked at each chunk of its sweep (2048, 8192, 16384) on the
+same inputs.
+
 Sizes: separate teacher N=8192, D=2048, D_t=4096, V=128256; top-K N=32768,
 D=4096, V=151936, K=100; scorer N=65536, D_t=4096, V=248320 (32.5 GB of
 student logits), all bf16.
 """
 import gc
+import time
 
 import numpy as np
 import pytest
@@ -99,12 +109,58 @@ def check_loss_consistency(r, w, labels_np, out_sce, out_tce, out_kl):
     return den
 
 
-def run_fullsize(name: str, grads: bool):
+def vocab_sample(v: int, chunk: int = 16384, count: int = 1024, seed: int = 0) -> np.ndarray:
+    """Seeded vocabulary rows for the element-by-element dW check: the edges of
+    the vocabulary, of a 256-row tile and of every chunk, then random rows."""
+    rows = {0, 1, 255, 256, v - 1, v - 2}
+    for c in range(chunk, v, chunk):
+        rows.update((c - 1, c))
+    rows = {r for r in rows if 0 <= r < v}
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.setdiff1d(np.arange(v), sorted(rows)), count - len(rows), replace=False)
+    return np.array(sorted(rows | set(rest.tolist())), dtype=np.int64)
+
+
+def check_dw_rows(w, x, dw, labels_np, den):
+    """dW on seeded vocabulary rows against the oracle's, element by element."""
+    vrows = vocab_sample(w.v)
+    s = O.Student(hidden=f64_all(x["student_hidden"]), weight=f64_all(x["weight"]))
+    if w.teacher == "separate":
+        t = O.Teacher("separate", hidden=f64_all(x["teacher_hidden"]),
+                      weight=f64_all(x["teacher_weight"]))
+    else:
+        t = O.Teacher("topk", idx=to_np(x["topk_idx"]).astype(np.int64), prob=f64_all(x["topk_prob"]))
+    p = params_of(w)
+    t0 = time.perf_counter()
+    last = [t0]
+
+    def progress(done, n):
+        if time.perf_counter() - last[0] > 20 or done == n:
+            last[0] = time.perf_counter()
+            say(f"  oracle dW rows: {done}/{n} tokens, {last[0] - t0:.0f} s")
+
+    ref = O.weight_grad_rows(s, t, p, labels_np, vrows, den, progress=progress)
+    got = to_np(dw[torch.as_tensor(vrows, device=dw.device)]).astype(np.float64)
+    assert_grad(got, ref, w.dtype, f"{w.name} dW on {len(vrows)} vocabulary rows")
+    say(f"  dW on {len(vrows)} vocabulary rows matches")
+
+
+def run_fullsize(name: str, grads: bool, dw_rows: bool = False, chunks=(0,)):
     w = WORKLOADS[name]
     say(f"[fullsize] {name}: n={w.n} d={w.d} d_t={w.d_t} v={w.v} k={w.k} grads={grads}")
     x = make_inputs(w, "cuda", seed=0)
     torch.cuda.synchronize()
-    r = make_runner(w, x, want_teacher_ce=w.teacher_ce_weight > 0)
+    for chunk in chunks:
+        run_fullsize_once(w, x, grads, dw_rows, chunk)
+    del x
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def run_fullsize_once(w, x, grads: bool, dw_rows: bool, chunk: int):
+    name = w.name
+    say(f"  vocab chunk {chunk or 'default'}")
+    r = make_runner(w, x, vocab_chunk=chunk, want_teacher_ce=w.teacher_ce_weight > 0)
     r.forward()
     dh = dw = None
     if grads:
@@ -139,21 +195,27 @@ def run_fullsize(name: str, grads: bool):
         assert_grad(f64_rows(dh, rows), ref_dh, w.dtype, f"{name} dH (sampled rows)")
         say("  dH rows match")
         check_dw_identities(r, x, dh, dw, w.dtype)
-    del r, x, dh, dw
+        if dw_rows:
+            check_dw_rows(w, x, dw, labels_np, den)
+    del r, dh, dw
     gc.collect()
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(1200)
 def test_fullsize_separate_teacher():
-    run_fullsize("separate_bf16", grads=True)
+    run_fullsize("separate_bf16", grads=True, dw_rows=True)
 
 
+@pytest.mark.timeout(1200)
 def test_fullsize_topk():
-    run_fullsize("topk_bf16", grads=True)
+    run_fullsize("topk_bf16", grads=True, dw_rows=True)
 
 
-def test_fullsize_scorer():
-    run_fullsize("scorer_bf16", grads=False)
+@pytest.mark.timeout(1200)
+def test_fullsize_scorer_chunk_sweep():
+    """The scorer at each chunk of its sweep on the same 32.5 GB of logits."""
+    run_fullsize("scorer_bf16", grads=False, chunks=(2048, 8192, 16384))
 
 
 def test_fullsize_quickstart_dw_identities():

@@ -69,3 +69,38 @@ def test_keep_last_chunk_is_bit_identical(name):
     for k in ref:
         assert torch.equal(got[k], ref[k]), f"{name}: {k} differs with the kept last chunk"
         assert torch.isfinite(got[k]).all(), f"{name}: {k}"
+
+
+def test_backward_refuses_kept_products_of_another_layout():
+    """A backward that reads kept products checks the layout the forward wrote
+    into the saved header: with nothing kept, or kept for another chunk, it
+    raises the device flag and its gradients are NaN, never silently wrong; the
+    matching pair leaves the flag clear."""
+    w = C2.scaled(n=300, d=512, v=3000)
+    x = make_inputs(w, "cuda", seed=7)
+    r = make_runner(w, x, 1024, keep_last_chunk=True)  # saved sized for the kept chunk
+    dh = torch.empty((r.n, r.d), dtype=torch.float32, device="cuda")
+    dw = torch.empty((r.v, r.d), dtype=torch.float32, device="cuda")
+
+    def step(fwd_keep, fwd_chunk, bwd_keep, bwd_chunk):
+        r.p.keep_last_chunk, r.p.vocab_chunk = fwd_keep, fwd_chunk
+        r.forward()
+        r.p.keep_last_chunk, r.p.vocab_chunk = bwd_keep, bwd_chunk
+        r.backward(dh, dw)
+        torch.cuda.synchronize()
+        return r.read_status(backward=True)
+
+    say("[keep] forward and backward agree")
+    assert step(1, 1024, 1, 1024) == 0
+    assert torch.isfinite(dh).all() and torch.isfinite(dw).all()
+    say("[keep] forward kept nothing, backward expects kept products")
+    assert step(0, 1024, 1, 1024) == 2
+    assert torch.isnan(dw[2048:]).all() and torch.isnan(dh).any()
+    say("[keep] forward kept another chunk size")
+    assert step(1, 1024, 1, 512) == 2
+    assert torch.isnan(dw[2560:]).all()
+    say("[keep] a backward that recomputes everything ignores what was kept")
+    assert step(1, 1024, 0, 1024) == 0
+    assert torch.isfinite(dh).all() and torch.isfinite(dw).all()
+    # and the flag clears again on the next matching pair
+    assert step(1, 512, 1, 512) == 0

@@ -49,7 +49,7 @@ def test_chunk_and_slice_sizes(chunk):
     full_parity(C2.scaled(n=260, d=256, v=2100, name=f"quickstart_chunk{chunk}"), vocab_chunk=chunk)
 
 
-@pytest.mark.parametrize("chunk", [256, 2048, 16384])
+@pytest.mark.parametrize("chunk", [256, 2048, 8192, 16384])
 def test_scorer_chunk_sweep(chunk):
     full_parity(C5.scaled(n=256, d_t=256, v=9000), vocab_chunk=chunk)
 
@@ -455,3 +455,54 @@ def test_wide_gemm_tiles(shape):
     """Shapes where the dH (first) or dW (second) GEMM has enough 256x256 tiles to
     use them, so both GEMM tile widths are checked against the oracle."""
     full_parity(C2.scaled(name="quickstart_" + "_".join(f"{k}{v}" for k, v in shape.items()), **shape))
+
+
+def test_topk_zero_subnormal_and_cancelling_entries():
+    """Planted top-K entries (readings R7, R8): p = 0 and fp32-subnormal p in
+    some rows, and in every row one entry at a shared column v* whose p equals
+    M softmax(z)[v*] (M = sum of the row's stored p), so that its logit gradient
+    M softmax(z) - p cancels. Everything matches the oracle, and dW[v*], a sum
+    of cancelled gradients, stays within what one rounding of each dz allows:
+    subtracting p after rounding M softmax(z) to bf16 would leave ~2^-9 p per
+    entry there."""
+    w = C4.scaled(n=200, d=256, v=3000, k=20)
+    x = make_inputs(w, "cuda", seed=21)
+    idx = x["topk_idx"].cpu().numpy().copy()
+    prob = x["topk_prob"].cpu().numpy().astype(np.float32).copy()
+    vstar = 1500
+    prob[:50, 1:5] = 0.0
+    prob[50:100, 1:5] = np.array([1e-41, 3e-40, 1e-39, 1.4e-45], np.float32)
+    assert (prob[50:100, 1:5] > 0).all() and (prob[50:100, 1:5] < np.finfo(np.float32).tiny).all()
+    H = to_np(x["student_hidden"]).astype(np.float64)
+    W = to_np(x["weight"]).astype(np.float64)
+    z = H @ W.T
+    sm = np.exp(z - z.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    for i in range(w.n):
+        hit = np.flatnonzero(idx[i] == vstar)
+        j = int(hit[0]) if hit.size else 0
+        if not hit.size:
+            idx[i, j] = vstar
+        others = float(prob[i].astype(np.float64).sum() - prob[i, j])
+        s_ = sm[i, vstar]
+        prob[i, j] = np.float32(others * s_ / (1.0 - s_))  # p_j = (others + p_j) s
+    assert all(len(set(r)) == w.k for r in idx.tolist())
+    x["topk_idx"] = torch.from_numpy(idx).to("cuda")
+    x["topk_prob"] = torch.from_numpy(prob).to("cuda")
+    say(f"[planted top-K] n={w.n} d={w.d} v={w.v} k={w.k} v*={vstar}")
+    r, dh, dw = run_gpu(w, x, vocab_chunk=1024)
+    s, t, labels = oracle_problem(w, x)
+    p = params_of(w)
+    ref = O.forward(s, t, p, None)
+    assert r.read_status() == 0
+    assert_tokens(to_np(r.kl), ref["kl"], w.dtype, "planted top-K objective")
+    assert_scalar(float(r.loss), ref["loss"], w.dtype, "planted top-K loss")
+    dH, dW = O.backward(s, t, p, None)
+    assert_grad(to_np(dh), dH, w.dtype, "planted top-K dH")
+    assert_grad(to_np(dw), dW, w.dtype, "planted top-K dW")
+    # the cancelled column
+    pj = prob[np.arange(w.n), np.argmax(idx == vstar, axis=1)].astype(np.float64)
+    scale = np.sqrt(((pj[:, None] * H) ** 2).sum(0)).max() / ref["den"]
+    err = np.abs(to_np(dw)[vstar].astype(np.float64) - dW[vstar]).max()
+    say(f"  dW[v*]: |gpu - oracle| = {err:.3e}, scale {scale:.3e}, ratio {err / scale:.2e}")
+    assert err <= 2e-4 * scale, f"dW[v*] error {err / scale:.2e} of the p-term scale"

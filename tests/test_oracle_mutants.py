@@ -18,6 +18,10 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
                    "oracle.py")
 
 MUTANTS = {
+    "weight_rows_reversed": ("out += g[:, vrows].T @ as_f64(student.hidden[r])",
+                             "out += g[:, vrows[::-1]].T @ as_f64(student.hidden[r])"),
+    "weight_rows_teacher_hidden": ("out += g[:, vrows].T @ as_f64(student.hidden[r])",
+                                   "out += g[:, vrows].T @ as_f64(student.hidden[r][::-1])"),
     "reverse_as_forward": ("return (T * T) * (np.exp(lp_s) * (lp_s - lp_t)).sum(axis=-1)",
                            "return (T * T) * (np.exp(lp_t) * (lp_t - lp_s)).sum(axis=-1)"),
     "reverse_grad_missing_kl": ("return T * p * (lp_s - lp_t - kl)", "return T * p * (lp_s - lp_t)"),
