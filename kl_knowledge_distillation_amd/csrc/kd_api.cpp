@@ -13,7 +13,6 @@ namespace {
 
 using kd::Plan;
 
-constexpr int64_t kTile = 128;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 // Default backward chunk: flash_kd's chunk_size default (flash_ce_kd_loss). A
 // 16384-column slab is n x 32 KB of bf16 (134 MB at 4096 tokens), and half as
@@ -150,7 +149,8 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   // Forward grid: (vocabulary tile) x (128-token tile), one tile per workgroup,
   // so the per-token statistics are only live after the main loop; each
   // vocabulary tile leaves one record per token for the merge.
-  q.n_ttiles = (int)ceil_div(q.n, kTile);
+  q.tt_rows = kd::fused_token_rows(q.mode, q.pipe);
+  q.n_ttiles = (int)ceil_div(q.n, q.tt_rows);
   q.n_vtiles = (int)ceil_div(q.v, vt);
   if (q.mode == kd::MODE_BOTH) {
     // Row kernels: each row split into slices of whole steps, enough of them
@@ -174,7 +174,7 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.merge_blocks = (int)ceil_div(q.n, kd::kMergeTok);
 
   const size_t elem = (q.dtype == KD_BF16) ? 2 : 4;
-  q.dz_rows = (int64_t)q.n_ttiles * kTile;
+  q.dz_rows = (int64_t)q.n_ttiles * q.tt_rows;
   // Compaction buffers first, at the same offsets in both workspaces.
   size_t off = kd::kStatusBytes;
   if (q.compact) {

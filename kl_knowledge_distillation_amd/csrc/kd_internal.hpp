@@ -75,6 +75,7 @@ struct Plan {
   // with several launches each chunk's records are folded into a running record
   int fwd_slices = 0;
   int64_t chunk = 0;  // backward vocabulary chunk (multiple of the fused tile rows)
+  int tt_rows = 128;     // token rows per fused tile
   int64_t dz_rows = 0;  // rows of the logit-gradient slab: n rounded up to the token tile
   int n_chunks = 0;
   int merge_blocks = 0;
@@ -114,6 +115,8 @@ struct Tensors {
 
 // Vocabulary rows per tile of the pipelined bf16 geometry compiled in.
 int pipe_vocab_rows();
+// Token rows per fused tile for a mode (pipe: the pipelined bf16 geometry).
+int fused_token_rows(int mode, int pipe);
 // Contraction lengths of the pipelined path are multiples of this (one K step).
 constexpr int kPipeK = 64;
 

@@ -93,8 +93,8 @@ __device__ __forceinline__ void rec_store(float* r, int64_t stride, const RowSta
 __device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int r) { return (ok >> (mb * 4 + r)) & 1u; }
 
 // Largest of the 16 values a lane holds for token block nb (masked rows skipped).
-template <bool TAIL>
-__device__ __forceinline__ float tile_max(const WaveAcc& x, int nb, uint32_t ok) {
+template <bool TAIL, int NBT>
+__device__ __forceinline__ float tile_max(const f32x4 (&x)[kMB][NBT], int nb, uint32_t ok) {
   float m = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
@@ -106,8 +106,8 @@ __device__ __forceinline__ float tile_max(const WaveAcc& x, int nb, uint32_t ok)
 
 // sum over the lane's 16 values of 2^(x c - mc); mc = c * (token max), so every
 // term is at most 1 and all partial sums of a token share one reference.
-template <bool TAIL>
-__device__ __forceinline__ float tile_sum(const WaveAcc& x, int nb, float c, float mc, uint32_t ok) {
+template <bool TAIL, int NBT>
+__device__ __forceinline__ float tile_sum(const f32x4 (&x)[kMB][NBT], int nb, float c, float mc, uint32_t ok) {
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
@@ -130,8 +130,9 @@ __device__ __forceinline__ float tile_sum(const WaveAcc& x, int nb, float c, flo
 // x = z, y = t, a = sum e (z - t rho); rho = T_s / T_t, so a / T_s is the
 // weighted sum of t / T_t - z / T_s (or its negative). ZERO_SAFE: an e of 0
 // adds 0 even where the difference is infinite (a teacher logit of -inf).
-template <bool TAIL, bool TEACHER_W, bool ZERO_SAFE = false>
-__device__ __forceinline__ void tile_sum_cross(const WaveAcc& x, const WaveAcc& y, int nb, float c, float mc,
+template <bool TAIL, bool TEACHER_W, bool ZERO_SAFE = false, int NBT = kNB>
+__device__ __forceinline__ void tile_sum_cross(const f32x4 (&x)[kMB][NBT], const f32x4 (&y)[kMB][NBT], int nb,
+                                               float c, float mc,
                                                float rho, uint32_t ok, float& s, float& a) {
   float s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -170,8 +171,9 @@ __device__ __forceinline__ void tile_sum_cross(const WaveAcc& x, const WaveAcc& 
 // element serves both temperatures (the square rounds once more, well inside
 // fp32). STUDENT_W: the student-weighted cross term (e of z, d = z - t rho);
 // CROSS = false: no cross term (a is left alone).
-template <bool TAIL, bool CROSS, bool TEACHER_W, bool ZERO_SAFE = false>
-__device__ __forceinline__ void tile_sums_sq(const WaveAcc& x, const WaveAcc& y, int nb, float c, float mc,
+template <bool TAIL, bool CROSS, bool TEACHER_W, bool ZERO_SAFE = false, int NBT = kNB>
+__device__ __forceinline__ void tile_sums_sq(const f32x4 (&x)[kMB][NBT], const f32x4 (&y)[kMB][NBT], int nb,
+                                             float c, float mc,
                                              float rho, uint32_t ok, float& s, float& q, float& a) {
   float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -216,20 +218,31 @@ __device__ __forceinline__ void tile_sums_sq(const WaveAcc& x, const WaveAcc& y,
 
 // Staged: 128 vocabulary rows x 128 tokens, 4 waves (2 x 2), registers carry
 // the copies; any element type, any hidden size that is a multiple of 8.
+// Every geometry: a wave holds kMB x kNB blocks of 16 x 16 (vocabulary rows x
+// tokens); col() is the token column (within the tile) of block nb.
 struct GeoStaged {
   static constexpr bool kPipe = false;
-  static constexpr int kThreads = 256, kVT = 128, kTT = 128, kWM = 2;
+  static constexpr int kThreads = 256, kVT = 128, kTT = 128, kWM = 2, kNB = 4;
   template <int NB> static constexpr int lds_bytes() { return 2 * (1 + NB) * kTileBytes; }
+  __device__ static int col(int wn, int nb, int lane) { return acc_col(wn, nb, lane); }
 };
-// Pipelined: 256 vocabulary rows x 128 tokens, 8 waves (4 x 2, two ping-pong
-// groups), two slots of buffer-load copies; bf16 with hidden sizes multiple of 64.
-struct GeoPipe {
+// Pipelined: 256 vocabulary rows x TT tokens, 8 waves (4 x 2, two ping-pong
+// groups), two slots of buffer-load copies; bf16 with hidden sizes multiple of
+// 64. TT = 128 for two B operands (tied teacher) and for the tiles that hold a
+// given logits tile in registers; TT = 256 for one B operand (top-K), which
+// halves the operand bytes copied per MFMA against 256 x 128.
+template <int TT>
+struct GeoPipeT {
   static constexpr bool kPipe = true;
-  static constexpr int kThreads = 512, kVT = 256, kTT = 128, kWM = 4;
-  template <int NB> using Cfg = PipeCfg<256, 128, NB>;
+  static constexpr int kThreads = 512, kVT = 256, kTT = TT, kWM = 4, kNB = TT / 32;
+  template <int NB> using Cfg = PipeCfg<256, TT, NB>;
   template <int NB> static constexpr int lds_bytes() { return Cfg<NB>::kLdsBytes; }
+  __device__ static int col(int wn, int nb, int lane) { return wn * (TT / 2) + nb * 16 + (lane & 15); }
 };
+using GeoPipe = GeoPipeT<128>;
+using GeoWide = GeoPipeT<256>;
 using GeoFused = GeoPipe;
+static_assert(GeoPipe::kNB == kNB, "the 128-token tiles keep the staged block layout");
 
 // acc[g] = A[a_row0 : +VT, 0:K] * B_g[b_row0 : +TT, 0:K]^T for K-contiguous operands.
 // pf: the cooperative prefetch share of this tile (pipelined, two B operands).
@@ -237,7 +250,7 @@ template <typename T, class G, int NB>
 __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t arows,
                                              const T* const (&b)[NB], int64_t ldb, int64_t brows,
                                              int64_t a_row0, int64_t b_row0, int64_t K,
-                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][kNB], int tid,
+                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][G::kNB], int tid,
                                              PipePrefetch pf = PipePrefetch{0, 0, 0, nullptr}) {
   if constexpr (G::kPipe) {
     static_assert(sizeof(T) == 2, "the pipelined geometry is bf16 only");
@@ -261,28 +274,31 @@ __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t ar
 // store and load of a wave is one contiguous 1 KB and a tile one contiguous
 // [kVT x kTT] block. Only the library reads the layout back, with the same
 // tile geometry.
+template <int NBT>
 __device__ __forceinline__ int64_t kept_block(int64_t tile, int waves, int w, int lane) {
-  return ((tile * waves + w) * (kMB * kNB)) * 256 + lane * 4;
+  return ((tile * waves + w) * (kMB * NBT)) * 256 + lane * 4;
 }
 // Stores are nontemporal: the backward reads them back only after the rest of
 // the forward and a whole recomputed chunk (equal or 0.3% faster per step).
+template <int NBT>
 __device__ __forceinline__ void kept_store(float* m, int64_t tile, int waves, int w, int lane,
-                                           const WaveAcc& x) {
-  float* p = m + kept_block(tile, waves, w, lane);
+                                           const f32x4 (&x)[kMB][NBT]) {
+  float* p = m + kept_block<NBT>(tile, waves, w, lane);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-      __builtin_nontemporal_store(x[mb][nb], reinterpret_cast<f32x4*>(p + (mb * kNB + nb) * 256));
+    for (int nb = 0; nb < NBT; ++nb)
+      __builtin_nontemporal_store(x[mb][nb], reinterpret_cast<f32x4*>(p + (mb * NBT + nb) * 256));
 }
 // Token block nb of that part read back (streaming loads: each byte is read
 // once); a token that is not live reads as zero.
+template <int NBT>
 __device__ __forceinline__ void kept_load(const float* m, int64_t tile, int waves, int w, int lane, int nb,
                                           bool live, f32x4 (&x)[kMB]) {
-  const float* p = m + kept_block(tile, waves, w, lane);
+  const float* p = m + kept_block<NBT>(tile, waves, w, lane);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
-    const uint4 u = load_stream(p + (mb * kNB + nb) * 256);
+    const uint4 u = load_stream(p + (mb * NBT + nb) * 256);
     x[mb] = live ? f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)}
                  : f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -414,25 +430,19 @@ struct FwdArgs {
   int64_t keep_t;
 };
 
-// Top-K: floats per token row of the z tile staged in LDS (the padding spreads
-// the rows of a 16-token block over the banks).
-template <class G>
-constexpr int topk_zstride() { return G::kVT + 4; }
-
 template <typename T, int MODE, class G>
 __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
+  constexpr int NBT = G::kNB;  // token blocks of 16 per wave
+  using Acc = f32x4[kMB][NBT];
   constexpr bool kGiven = MODE == MODE_TLOGITS || MODE == MODE_LOGITS;  // one logits tile is given
   constexpr int kMainBytes = G::template lds_bytes<NB>();
-  // top-K: the fp32 z tile [kTT][zstride] after the main loop, then the tile's
-  // cross terms [kTT] past the epilogue's exchange area
-  constexpr int kTopkBytes = (MODE == MODE_TOPK) ? G::kTT * topk_zstride<G>() * 4 : 0;
   // pipelined tiles: 1 KB past the slots where the prefetch reads land; a
   // given logits tile is held in registers
   constexpr bool kGivenRegs = kGiven && G::kPipe;
   constexpr bool kPf = G::kPipe && kPipeAhead > 0;
   constexpr int kLdsMain = kMainBytes + (kPf ? 1024 : 0);
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsMain > kTopkBytes ? kLdsMain : kTopkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsMain];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: only the token tiles below nv have work; they are mapped
   // onto the first blocks of every XCD and the rest of the grid exits.
@@ -449,9 +459,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   const T* ht = static_cast<const T*>(a.ht);
   const T* Wt = static_cast<const T*>(a.wt);
 
-  f32x4 acc[NB][kMB][kNB];
-  f32x4 tacc[1][kMB][kNB];  // teacher accumulator of the separate / logits modes
-  WaveAcc zl;               // student logits loaded in LOGITS mode
+  f32x4 acc[NB][kMB][NBT];
+  f32x4 tacc[1][kMB][NBT];  // teacher accumulator of the separate / logits modes
+  Acc zl;                   // student logits loaded in LOGITS mode
 
   // the tile's share of the cooperative prefetch (grouped order: token tiles
   // tt % 8 and vocabulary tiles slice % 4 run side by side)
@@ -498,9 +508,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     if (a.keep) {
       const int64_t tile = (int64_t)tt * a.n_slices + slice;
       constexpr int kWaves = G::kThreads / 64;
-      kept_store(a.keep, tile, kWaves, w, lane, acc[0]);
+      kept_store<NBT>(a.keep, tile, kWaves, w, lane, acc[0]);
       if constexpr (MODE == MODE_TIED || MODE == MODE_SEPARATE)
-        kept_store(a.keep + a.keep_t, tile, kWaves, w, lane, MODE == MODE_TIED ? acc[NB - 1] : tacc[0]);
+        kept_store<NBT>(a.keep + a.keep_t, tile, kWaves, w, lane, MODE == MODE_TIED ? acc[NB - 1] : tacc[0]);
     }
   }
 
@@ -520,49 +530,20 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       for (int r = 0; r < 4; ++r)
         if (v0 + acc_row(wm, mb, r, lane) < a.v) ok |= 1u << (mb * 4 + r);
   }
-  const WaveAcc& z = (MODE == MODE_LOGITS) ? zl : acc[0];
-  const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const Acc& z = (MODE == MODE_LOGITS) ? zl : acc[0];
+  const Acc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
   constexpr bool kTeacher = MODE != MODE_TOPK;
   constexpr bool kInfT = MODE == MODE_TLOGITS;  // given teacher logits may be -inf
-  constexpr int kSums = 6;  // sz1, szT, stT, a, st1, ar
-  float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNB][2][16]
-  float* xsum = xmax + G::kWM * 2 * kNB * 2 * 16;                 // [kWM][2][kNB][kSums][16]
-  float* xcross = xsum + G::kWM * 2 * kNB * kSums * 16;           // [kTT] (top-K)
-  if constexpr (MODE == MODE_TOPK) {
-    // Sum over a token's entries whose index falls in this tile of p z[idx]
-    // (orda-kernel, Teacher descriptors: TopKTeacher), z read back from the
-    // tile itself, so the cross term and the statistics share every value.
-    // The tile goes through LDS ([token][vocabulary row], free after the main
-    // loop); the token's entries of this tile are a run of its sorted entries,
-    // added in index order by the first of its kTpt threads.
-    constexpr int kZs = topk_zstride<G>();
-    float* zt = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb)
-        *reinterpret_cast<f32x4*>(zt + acc_col(wn, nb, lane) * kZs + acc_row(wm, mb, 0, lane)) = z[mb][nb];
-    __syncthreads();
-    constexpr int kTpt = G::kThreads / G::kTT;  // threads per token (adjacent lanes)
-    static_assert(kTpt >= 1 && (kTpt & (kTpt - 1)) == 0 && kTpt <= 64, "threads per token");
-    const int tq = tid / kTpt, part = tid % kTpt;
-    const int64_t tok = t0 + tq;
-    float cross = 0.f;
-    if (tok < a.n && part == 0) {
-      const int32_t* off = a.topk_off + tok * (a.n_slices + 1) + slice;
-      const int j0 = off[0], j1 = off[1];  // sorted entries with index in [v0, v0 + kVT) and < v
-      const int32_t* ix = a.topk_sidx + tok * a.k;
-      const float* pr = a.topk_sprob + tok * a.k;
-      for (int j = j0; j < j1; ++j) cross = fmaf(pr[j], zt[tq * kZs + (ix[j] - v0)], cross);
-    }
-    __syncthreads();  // every read of the z tile done: the epilogue reuses the LDS
-    if (part == 0) xcross[tq] = cross;
-  }
+  constexpr int kSums = 6;  // sz1, szT, stT, a (top-K: sum p z[idx]), st1, ar
+  static_assert(G::kWM * 2 * NBT * (2 + kSums) * 16 * 4 <= kLdsMain, "epilogue exchange fits the LDS");
+  float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][NBT][2][16]
+  float* xsum = xmax + G::kWM * 2 * NBT * 2 * 16;                 // [kWM][2][NBT][kSums][16]
+  const int rb = acc_row(wm, 0, 0, lane);  // this lane's rows: v0 + rb + 16 mb + r
   const int l16 = lane & 15;
 
-  float mz[kNB], mt[kNB];
+  float mz[NBT], mt[NBT];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NBT; ++nb) {
     mz[nb] = tail ? tile_max<true>(z, nb, ok) : tile_max<false>(z, nb, ok);
     mt[nb] = !kTeacher ? 0.f : (tail ? tile_max<true>(tl, nb, ok) : tile_max<false>(tl, nb, ok));
 #pragma unroll
@@ -571,19 +552,19 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       if (kTeacher) mt[nb] = fmaxf(mt[nb], __shfl_xor(mt[nb], off));
     }
     if (lane < 16) {
-      float* p = xmax + (((wm * 2 + wn) * kNB + nb) * 2) * 16 + l16;
+      float* p = xmax + (((wm * 2 + wn) * NBT + nb) * 2) * 16 + l16;
       p[0] = mz[nb];
       p[16] = mt[nb];
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NBT; ++nb) {
     // every wave reads the same kWM values (fmax is exact, so the order is free)
     float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int src = 0; src < G::kWM; ++src) {
-      const float* p = xmax + (((src * 2 + wn) * kNB + nb) * 2) * 16 + l16;
+      const float* p = xmax + (((src * 2 + wn) * NBT + nb) * 2) * 16 + l16;
       m0 = fmaxf(m0, p[0]);
       m1 = fmaxf(m1, p[16]);
     }
@@ -591,9 +572,34 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     mt[nb] = m1;
   }
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
+  for (int nb = 0; nb < NBT; ++nb) {
     float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const bool rev = a.kl != KD_KL_FORWARD;
+    if constexpr (MODE == MODE_TOPK) {
+      // sum of p z[idx] over the token's cached entries in this tile (orda-kernel,
+      // Teacher descriptors: TopKTeacher), from the tile's own z values: the
+      // token's run of index-sorted entries, each added by the lane that holds
+      // its row; the lane and wave partials add up like the sums below.
+      const int64_t tok = t0 + G::col(wn, nb, lane);
+      float cr = 0.f;
+      if (tok < a.n) {
+        const int32_t* off = a.topk_off + tok * (a.n_slices + 1) + slice;
+        const int j0 = off[0], j1 = off[1];  // sorted entries with index in [v0, v0 + kVT) and < v
+        const int32_t* ix = a.topk_sidx + tok * a.k;
+        const float* pr = a.topk_sprob + tok * a.k;
+        const int base = (int)(v0 + rb);
+        for (int j = j0; j < j1; ++j) {
+          const int d = ix[j] - base;
+          float zz = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) zz = (d == 16 * mb + r) ? z[mb][nb][r] : zz;
+          cr = fmaf(pr[j], zz, cr);
+        }
+      }
+      v[3] = cr;
+    }
     const float mz1 = mz[nb] * kLog2e, mzT = mz[nb] * a.cT;
     // A teacher tile with no finite logit (all -inf) sums 2^-inf = 0 against a
     // finite reference; its record keeps the -inf maximum, which the merge
@@ -626,7 +632,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       v[j] += __shfl_xor(v[j], 32);
     }
     if (lane < 16) {
-      float* p = xsum + (((wm * 2 + wn) * kNB + nb) * kSums) * 16 + l16;
+      float* p = xsum + (((wm * 2 + wn) * NBT + nb) * kSums) * 16 + l16;
 #pragma unroll
       for (int j = 0; j < kSums; ++j) p[j * 16] = v[j];
     }
@@ -634,15 +640,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   __syncthreads();
   if (wm == 0 && lane < 16) {
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
+    for (int nb = 0; nb < NBT; ++nb) {
       float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int src = 0; src < G::kWM; ++src) {  // fixed order
-        const float* p = xsum + (((src * 2 + wn) * kNB + nb) * kSums) * 16 + l16;
+        const float* p = xsum + (((src * 2 + wn) * NBT + nb) * kSums) * 16 + l16;
 #pragma unroll
         for (int j = 0; j < kSums; ++j) v[j] += p[j * 16];
       }
-      const int64_t tok = t0 + acc_col(wn, nb, lane);
+      const int64_t tok = t0 + G::col(wn, nb, lane);
       if (tok < a.n) {
         const int64_t stride = (int64_t)a.n_slices * a.n;
         float* r = a.rec + (int64_t)slice * a.n + tok;
@@ -650,7 +656,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
         r[2 * stride] = mz[nb] * a.cT;   r[3 * stride] = v[1];
         r[4 * stride] = mt[nb] * a.cTt;  r[5 * stride] = v[2];
         // top-K: field 6 carries the tile's cross term sum p z[idx]
-        r[6 * stride] = (MODE == MODE_TOPK) ? xcross[acc_col(wn, nb, lane)] : v[3];
+        r[6 * stride] = v[3];
         r[7 * stride] = mt[nb] * kLog2e; r[8 * stride] = v[4];
         r[9 * stride] = v[5];
       }
@@ -1459,6 +1465,8 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float x0, float x1, fl
 template <typename T, int MODE, class G, bool kKept>
 __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdArgs a) {
   constexpr int NB = (MODE == MODE_TIED) ? 2 : 1;
+  constexpr int NBT = G::kNB;  // token blocks of 16 per wave
+  using Acc = f32x4[kMB][NBT];
   constexpr bool kGiven = MODE == MODE_TLOGITS;
   constexpr int kMainBytes = G::template lds_bytes<NB>();
   constexpr bool kGivenRegs = kGiven && G::kPipe;  // a given logits tile in registers
@@ -1492,8 +1500,8 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   }
   if (a.set_status && blockIdx.x == 0 && tid == 0) a.status[0] = kept_ok ? 0 : kFlagSaved;
 
-  f32x4 acc[NB][kMB][kNB];
-  f32x4 tacc[1][kMB][kNB];
+  f32x4 acc[NB][kMB][NBT];
+  f32x4 tacc[1][kMB][NBT];
   // the tile's share of the cooperative prefetch (grouped order)
   const PipePrefetch pf{kPf ? 1 : 0, tt % 8, vt % 4, lds + (kKept ? 0 : kMainBytes)};
   if constexpr (kKept) {
@@ -1536,8 +1544,8 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     const T* const b[1] = {hs};
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   }
-  const WaveAcc& z = acc[0];  // MODE_TCE: the teacher logits
-  const WaveAcc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const Acc& z = acc[0];  // MODE_TCE: the teacher logits
+  const Acc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
 
   const float* hdr = a.saved + 4 * a.n;
   const float den = hdr[0];
@@ -1556,8 +1564,8 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   constexpr bool kRev = decltype(rev_tag)::value;
   constexpr bool kSq = decltype(sq_tag)::value;
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int64_t tok = t0 + acc_col(wn, nb, lane);
+  for (int nb = 0; nb < NBT; ++nb) {
+    const int64_t tok = t0 + G::col(wn, nb, lane);
     if (tok >= a.dz_rows) continue;
     const bool live = tok < n_live;  // rows past n (or nv) are zero padding of the slab
     const int64_t orig = (live && a.idx) ? a.idx[tok] : tok;  // original row
@@ -1608,8 +1616,8 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     if constexpr (kKept) {
       const int64_t tile = (int64_t)tt * a.n_vt + vt;
       constexpr int kWaves = G::kThreads / 64;
-      kept_load(a.keep + (MODE == MODE_TCE ? a.keep_t : 0), tile, kWaves, w, lane, nb, live, zk);
-      if constexpr (kKeptT) kept_load(a.keep + a.keep_t, tile, kWaves, w, lane, nb, live, tk);
+      kept_load<NBT>(a.keep + (MODE == MODE_TCE ? a.keep_t : 0), tile, kWaves, w, lane, nb, live, zk);
+      if constexpr (kKeptT) kept_load<NBT>(a.keep + a.keep_t, tile, kWaves, w, lane, nb, live, tk);
     }
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
@@ -2122,7 +2130,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
         switch (p.mode) {
           case MODE_TIED: fwd_tiles_kernel<T, MODE_TIED, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
           case MODE_SEPARATE: fwd_tiles_kernel<T, MODE_SEPARATE, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
-          case MODE_TOPK: fwd_tiles_kernel<T, MODE_TOPK, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          case MODE_TOPK:  // one B operand: the 256-token tiles in the pipelined geometry
+            fwd_tiles_kernel<T, MODE_TOPK, std::conditional_t<G::kPipe, GeoWide, G>>
+                <<<fgrid, G::kThreads, 0, stream>>>(fa);
+            break;
           case MODE_TLOGITS: fwd_tiles_kernel<T, MODE_TLOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
           default: fwd_tiles_kernel<T, MODE_LOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
         }
@@ -2245,7 +2256,10 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_TLOGITS: bwd_dz_kernel<T, MODE_TLOGITS, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
-        default: bwd_dz_kernel<T, MODE_TOPK, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        default:
+          bwd_dz_kernel<T, MODE_TOPK, std::conditional_t<G::kPipe, GeoWide, G>, K>
+              <<<grid, G::kThreads, 0, stream>>>(ba);
+          break;
       }
     };
     KD_TRY(L.run(kept ? KD_KERNEL_BWD_KEPT : KD_KERNEL_BWD_DZ, [&] {
@@ -2375,7 +2389,11 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
 }  // namespace
 
 static_assert(kPipeK == kPipeBK, "K step of the pipelined path");
+static_assert(GeoWide::kVT == GeoFused::kVT, "one vocabulary tile for every pipelined mode");
 int pipe_vocab_rows() { return GeoFused::kVT; }
+int fused_token_rows(int mode, int pipe) {
+  return (pipe && mode == MODE_TOPK) ? GeoWide::kTT : GeoFused::kTT;
+}
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
                       void* workspace, hipStream_t stream, kd_trace* trace) {
