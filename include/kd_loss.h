@@ -245,6 +245,25 @@ kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params*
                       const int64_t* labels, const kd_outputs* out, void* saved,
                       void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
 
+/* kd_loss_fwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). The forward's workspace is a library-owned scratch
+ * array of 64 MiB per device (allocated with the library's device code on
+ * each device it runs on and held until the process ends); the call itself
+ * allocates and frees nothing. Same arguments and results as kd_loss_fwd
+ * (the outputs and `saved` are bit-identical), with the current device the
+ * one `stream` runs on. Returns KD_ERR_WORKSPACE, before enqueuing
+ * anything, when kd_workspace_bytes(..., 0) for these descriptors exceeds
+ * 64 MiB (about 2.5 KB per token at the default vocab_chunk of 16384 with a
+ * 256-column tile; a smaller vocab_chunk shrinks it). device_flags (device
+ * int32, nullable) receives the flag word kd_read_status would report (bit 0:
+ * a label or top-K index out of range). Every call on a device shares that
+ * device's scratch and leaves its contents behind: calls that overlap in time
+ * on one device race and must be serialised (one stream, or events). */
+kd_status kd_loss_fwd_noalloc(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                              const int64_t* labels, const kd_outputs* out, void* saved,
+                              int32_t* device_flags, void* stream, kd_trace* trace);
+
 /* Backward of the reduced loss to the student hidden states and weight.
  * saved: written by the matching kd_loss_fwd with the same inputs and params.
  * grad_loss: device fp32 scalar (upstream gradient of loss), NULL = 1.

@@ -63,6 +63,9 @@ EXPORTS = {
     "kd_loss_fwd": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                               c_void_p, POINTER(KdOutputs), c_void_p, c_void_p, c_size_t,
                               c_void_p, POINTER(KdTrace)]),
+    "kd_loss_fwd_noalloc": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
+                                      c_void_p, POINTER(KdOutputs), c_void_p, c_void_p, c_void_p,
+                                      POINTER(KdTrace)]),
     "kd_loss_bwd": (c_int32, [POINTER(KdStudent), POINTER(KdTeacher), POINTER(KdParams),
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                               c_void_p, c_size_t, c_void_p, POINTER(KdTrace)]),

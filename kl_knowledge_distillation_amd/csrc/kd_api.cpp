@@ -299,6 +299,28 @@ kd_status kd_loss_fwd(const kd_student* s, const kd_teacher* t, const kd_params*
                          static_cast<hipStream_t>(stream), trace);
 }
 
+kd_status kd_loss_fwd_noalloc(const kd_student* s, const kd_teacher* t, const kd_params* p,
+                              const int64_t* labels, const kd_outputs* out, void* saved,
+                              int32_t* device_flags, void* stream, kd_trace* trace) {
+  Plan q;
+  kd_status st = plan_call(s, t, p, labels, true, false, &q);
+  if (st != KD_OK) return st;
+  // the forward workspace must fit the library's per-device scratch
+  if (q.fwd_bytes > kd::kScratchBytes) return KD_ERR_WORKSPACE;
+  if (saved && !aligned16(saved)) return KD_ERR_ALIGN;
+  if (saved && q.keep && (size_t)p->saved_bytes < q.saved_bytes) return KD_ERR_WORKSPACE;
+  if (device_flags && ((uintptr_t)device_flags & 3u)) return KD_ERR_ALIGN;
+  if (out) {
+    const void* ptrs[4] = {out->loss, out->student_ce, out->teacher_ce, out->kl};
+    for (const void* ptr : ptrs)
+      if (ptr && ((uintptr_t)ptr & 3u)) return KD_ERR_ALIGN;
+  }
+  void* ws = kd::scratch_address(&st);
+  if (ws == nullptr) return st;
+  return kd::run_forward(q, tensors_of(s, t, labels), out, saved, ws,
+                         static_cast<hipStream_t>(stream), trace, device_flags);
+}
+
 kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
                       const int64_t* labels, const void* saved, const float* grad_loss,
                       float* d_hidden, float* d_weight, int32_t accumulate, void* workspace,

@@ -120,8 +120,15 @@ int fused_token_rows(int mode, int pipe);
 // Contraction lengths of the pipelined path are multiples of this (one K step).
 constexpr int kPipeK = 64;
 
+// status_out: where the forward's device flags go (null: the workspace's first word).
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
-                      void* workspace, hipStream_t stream, kd_trace* trace);
+                      void* workspace, hipStream_t stream, kd_trace* trace,
+                      int32_t* status_out = nullptr);
+// The no-allocation forward's scratch: kScratchBytes of device memory per
+// device; scratch_address gives the current device's address (looked up once
+// per device), or null with *st set.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+void* scratch_address(kd_status* st);
 kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
                        float* d_hidden, float* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace);

@@ -25,6 +25,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include <type_traits>
 
 #include "kd_device.hpp"
@@ -2052,13 +2054,13 @@ kd_status compact_rows(const Plan& p, const Tensors& x, uint8_t* base, Launch& L
 
 template <typename T, class G>
 kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved, void* ws,
-                    hipStream_t stream, kd_trace* trace) {
+                    hipStream_t stream, kd_trace* trace, int32_t* status_out) {
   Launch L{stream, trace};
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* prep = reinterpret_cast<float*>(base + p.off_prep);
   float* rec = reinterpret_cast<float*>(base + p.off_rec);
   double* part = reinterpret_cast<double*>(base + p.off_part);
-  int32_t* status = reinterpret_cast<int32_t*>(base);
+  int32_t* status = status_out ? status_out : reinterpret_cast<int32_t*>(base);
 
   int32_t* tk_idx = reinterpret_cast<int32_t*>(base + p.off_tks);
   float* tk_prob = reinterpret_cast<float*>(base + p.off_tks + 4 * (size_t)p.n * (size_t)p.k);
@@ -2396,12 +2398,46 @@ int fused_token_rows(int mode, int pipe) {
 }
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
-                      void* workspace, hipStream_t stream, kd_trace* trace) {
+                      void* workspace, hipStream_t stream, kd_trace* trace, int32_t* status_out) {
   if (p.dtype == KD_BF16) {
-    if (p.pipe) return forward_t<bf16_t, GeoFused>(p, x, out, saved, workspace, stream, trace);
-    return forward_t<bf16_t, GeoStaged>(p, x, out, saved, workspace, stream, trace);
+    if (p.pipe) return forward_t<bf16_t, GeoFused>(p, x, out, saved, workspace, stream, trace, status_out);
+    return forward_t<bf16_t, GeoStaged>(p, x, out, saved, workspace, stream, trace, status_out);
   }
-  return forward_t<float, GeoStaged>(p, x, out, saved, workspace, stream, trace);
+  return forward_t<float, GeoStaged>(p, x, out, saved, workspace, stream, trace, status_out);
+}
+
+}  // namespace kd
+
+// Scratch of the forward that allocates nothing (kd_loss_fwd_noalloc): the
+// forward workspace of every such call on a device, a file-scope device array
+// that each device holds until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): it takes the address hipGetSymbolAddress gives for the current
+// device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[kd::kScratchBytes];
+
+namespace kd {
+
+void* scratch_address(kd_status* st) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = KD_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      *st = KD_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  *st = KD_OK;
+  return addr[dev];
 }
 
 namespace {

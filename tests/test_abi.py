@@ -94,17 +94,18 @@ def _saved_for(s, t, p):
 def test_saved_bytes_for_keep_last_chunk():
     lib = L.load()
     align = lambda x: -(-x // 256) * 256  # noqa: E731
-    # bf16, hidden sizes multiple of 32: 256-column tiles; n = 300 -> 384 token rows
-    for kind, ops in (("tied", 2), ("separate", 2), ("topk", 1)):
+    # bf16, hidden sizes multiple of 64: 256-column tiles of 128 tokens (two B
+    # operands) or 256 tokens (top-K); n = 300 -> 384 or 512 token rows
+    for kind, ops, rows in (("tied", 2, 384), ("separate", 2, 384), ("topk", 1, 512)):
         s, t, p = _desc(kind)
         assert _saved_for(s, t, p) == (L.KD_OK, lib.kd_saved_bytes(300))
         p.keep_last_chunk = 1
         p.vocab_chunk = 1024  # chunks of 1024 columns: the last one holds 3000 - 2048 = 952
         st, nb = _saved_for(s, t, p)
         assert st == L.KD_OK
-        assert nb == align(lib.kd_saved_bytes(300)) + ops * 384 * 1024 * 4, kind
+        assert nb == align(lib.kd_saved_bytes(300)) + ops * rows * 1024 * 4, kind
         p.vocab_chunk = 0  # one chunk covers the vocabulary: 3000 -> 3072 columns
-        assert _saved_for(s, t, p)[1] == align(lib.kd_saved_bytes(300)) + ops * 384 * 3072 * 4
+        assert _saved_for(s, t, p)[1] == align(lib.kd_saved_bytes(300)) + ops * rows * 3072 * 4
     # fp32 inputs run 128-column tiles: the last of the 1024-column chunks rounds 952 up to 1024
     s, t, p = _desc("tied", dtype=L.KD_F32)
     p.keep_last_chunk, p.vocab_chunk = 1, 1000
@@ -381,3 +382,24 @@ def test_teacher_backward_rejections():
     st = lib.kd_loss_bwd_teacher(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), FAKE, FAKE, None,
                                  FAKE + 4, None, 0, FAKE, 1 << 30, None, None)
     assert st == L.KD_ERR_ALIGN
+
+
+def test_no_alloc_forward_checks_on_the_host():
+    """kd_loss_fwd_noalloc validates like kd_loss_fwd and refuses, before any
+    HIP call, a forward workspace larger than its 64 MiB scratch."""
+    lib = L.load()
+    out = L.KdOutputs(FAKE, FAKE, FAKE, FAKE)
+
+    def call(s, t, p, labels=FAKE, flags=None):
+        return lib.kd_loss_fwd_noalloc(ctypes.byref(s), ctypes.byref(t), ctypes.byref(p), labels,
+                                       ctypes.byref(out), FAKE, flags, None, None)
+    s, t, p = _desc("tied", n=40000, d=256, v=20000)
+    st, fwd = _ws(s, t, p, 0)
+    assert st == L.KD_OK and fwd > 64 << 20
+    assert call(s, t, p) == L.KD_ERR_WORKSPACE
+    s, t, p = _desc()
+    p.temperature = 0.0
+    assert call(s, t, p) == L.KD_ERR_PARAM
+    s, t, p = _desc()
+    assert call(s, t, p, flags=FAKE + 2) == L.KD_ERR_ALIGN
+    assert call(s, t, p, labels=None) == L.KD_ERR_NULL
