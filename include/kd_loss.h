@@ -182,6 +182,16 @@ typedef struct {
                                 not multiplied by T^2); the loss and the gradients keep it.
                                 0: the per-token kl includes T^2 (nemo kd_loss, KDLoss
                                 temperature; orda-kernel, KL variants). */
+  int32_t dh_dtype;          /* element type of the d_hidden output of kd_loss_bwd and
+                                kd_loss_bwd_teacher: KD_F32 (0) or KD_BF16 (1). bf16 is the fp32
+                                result rounded once to nearest even: dH sums its vocabulary
+                                chunks in an fp32 buffer of the workspace (n x max(d, d_t) x 4
+                                bytes more when there are several chunks) and rounds at the
+                                last one; with accumulate = 1 the old bf16 value is added in
+                                fp32 before that rounding. */
+  int32_t dw_dtype;          /* element type of the d_weight output, as dh_dtype: each
+                                vocabulary row is written once per call, rounded once (with
+                                accumulate = 1, old value + new in fp32, then rounded). */
 } kd_params;
 
 /* Forward outputs, all device pointers, each nullable (NULL = not written).
@@ -267,13 +277,15 @@ kd_status kd_loss_fwd_noalloc(const kd_student* s, const kd_teacher* t, const kd
 /* Backward of the reduced loss to the student hidden states and weight.
  * saved: written by the matching kd_loss_fwd with the same inputs and params.
  * grad_loss: device fp32 scalar (upstream gradient of loss), NULL = 1.
- * d_hidden: fp32 [n, d], d_weight: fp32 [v, d], each nullable (NULL = skip).
+ * d_hidden: [n, d], d_weight: [v, d], row-major, of the element types
+ * kd_params.dh_dtype / dw_dtype (fp32 by default), 16-byte aligned, each
+ * nullable (NULL = skip).
  * accumulate = 1 adds into d_hidden / d_weight (orda-kernel, Parameters:
  * KernelConfig weight-gradient accumulation); 0 overwrites.
  * Not available for LOGITS students or REDUCE_NONE (KD_ERR_UNSUPPORTED). */
 kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
                       const int64_t* labels, const void* saved, const float* grad_loss,
-                      float* d_hidden, float* d_weight, int32_t accumulate,
+                      void* d_hidden, void* d_weight, int32_t accumulate,
                       void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
 
 /* Backward to given student logits (nemo kd_loss, KDLoss: the loss is
@@ -290,14 +302,14 @@ kd_status kd_loss_bwd_logits(const kd_student* s, const kd_teacher* t, const kd_
  * descriptors: with teacher_ce_weight > 0 the teacher trains via CE; the KL
  * variants here detach the teacher, so only w_t CE(t) at T = 1 reaches it).
  * TIED or SEPARATE teacher, PROJECTION student, same arguments as kd_loss_bwd
- * (the same workspace size serves). d_teacher_hidden: fp32 [n, d_t];
- * d_teacher_weight: fp32 [v, d_t] (TIED: d_t = d and this is the teacher
+ * (the same workspace size serves). d_teacher_hidden: [n, d_t];
+ * d_teacher_weight: [v, d_t], of the types dh_dtype / dw_dtype (TIED: d_t = d and this is the teacher
  * half of the shared weight's gradient: pass d_weight with accumulate = 1
  * after kd_loss_bwd to sum the halves). Each nullable; accumulate as above.
  * With teacher_ce_weight = 0 the gradients are 0. */
 kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd_params* p,
                               const int64_t* labels, const void* saved, const float* grad_loss,
-                              float* d_teacher_hidden, float* d_teacher_weight, int32_t accumulate,
+                              void* d_teacher_hidden, void* d_teacher_weight, int32_t accumulate,
                               void* workspace, size_t ws_bytes, void* stream, kd_trace* trace);
 
 /* Synchronises `stream`, then reads the device flags left in `workspace` by

@@ -41,7 +41,7 @@ class KdParams(ctypes.Structure):
                 ("assume_valid_labels", c_int32), ("kl_divergence", c_int32),
                 ("teacher_temperature", c_float), ("compact_valid", c_int32),
                 ("keep_last_chunk", c_int32), ("saved_bytes", c_int64),
-                ("kl_output_unscaled", c_int32)]
+                ("kl_output_unscaled", c_int32), ("dh_dtype", c_int32), ("dw_dtype", c_int32)]
 
 
 class KdOutputs(ctypes.Structure):

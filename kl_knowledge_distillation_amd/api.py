@@ -125,7 +125,8 @@ class Runner:
                  teacher_ce_weight=0.0, kl_weight=0.0, temperature=1.0, ignore_index=-100,
                  reduction="mean", normalizer=0.0, vocab_chunk=0, want_grads=True,
                  want_teacher_ce=None, kl_divergence="forward", teacher_temperature=None,
-                 compact_valid=False, keep_last_chunk=False, kl_output_unscaled=False):
+                 compact_valid=False, keep_last_chunk=False, kl_output_unscaled=False,
+                 grad_dtype=torch.float32):
         self.lib = L.load()
         ref = student_hidden if student_hidden is not None else student_logits
         if ref is None:
@@ -197,6 +198,11 @@ class Runner:
         # one-chunk slab.
         p.keep_last_chunk = 1 if keep_last_chunk else 0
         p.kl_output_unscaled = 1 if kl_output_unscaled else 0
+        # dH / dW (and a trained teacher's) element type: fp32, or bf16 rounded once
+        if grad_dtype not in _DTYPES:
+            raise ValueError(f"unsupported gradient dtype {grad_dtype}")
+        self.grad_dtype = grad_dtype
+        p.dh_dtype = p.dw_dtype = _DTYPES[grad_dtype]
         self.s, self.t, self.p = s, t, p
         self.n, self.v, self.d = int(s.n), int(s.v), int(s.d)
         self.teacher_kind = teacher_kind
@@ -246,9 +252,9 @@ class Runner:
                  grad_loss: Optional[torch.Tensor] = None, accumulate: bool = False,
                  trace: Optional[L.KdTrace] = None) -> None:
         for g, shape in ((d_hidden, (self.n, self.d)), (d_weight, (self.v, self.d))):
-            if g is not None and (g.dtype != torch.float32 or tuple(g.shape) != shape
+            if g is not None and (g.dtype != self.grad_dtype or tuple(g.shape) != shape
                                   or not g.is_contiguous()):
-                raise ValueError(f"gradient buffers must be contiguous fp32 {shape}")
+                raise ValueError(f"gradient buffers must be contiguous {self.grad_dtype} {shape}")
         st = self.lib.kd_loss_bwd(ctypes.byref(self.s), ctypes.byref(self.t), ctypes.byref(self.p),
                                   self.labels_ptr, self.saved.data_ptr(), _ptr(grad_loss),
                                   _ptr(d_hidden), _ptr(d_weight), int(accumulate),
@@ -277,9 +283,9 @@ class Runner:
         """Gradient of w_t CE(t) to a tied or separate teacher (the KL detaches it).
         Tied: d_teacher_weight is the teacher half of the shared weight's gradient."""
         for g, shape in ((d_teacher_hidden, (self.n, self.dt)), (d_teacher_weight, (self.v, self.dt))):
-            if g is not None and (g.dtype != torch.float32 or tuple(g.shape) != shape
+            if g is not None and (g.dtype != self.grad_dtype or tuple(g.shape) != shape
                                   or not g.is_contiguous()):
-                raise ValueError(f"gradient buffers must be contiguous fp32 {shape}")
+                raise ValueError(f"gradient buffers must be contiguous {self.grad_dtype} {shape}")
         st = self.lib.kd_loss_bwd_teacher(
             ctypes.byref(self.s), ctypes.byref(self.t), ctypes.byref(self.p), self.labels_ptr,
             self.saved.data_ptr(), _ptr(grad_loss), _ptr(d_teacher_hidden), _ptr(d_teacher_weight),
@@ -366,7 +372,9 @@ class _FusedLoss(torch.autograd.Function):
         r: Runner = ctx.runner
         need_h, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         need_ht, need_wt = ctx.needs_input_grad[2], ctx.needs_input_grad[3]
-        f32 = dict(dtype=torch.float32, device=r.device)
+        # gradients come out of the library in r.grad_dtype (the inputs' dtype,
+        # rounded once from fp32 for bf16)
+        f32 = dict(dtype=r.grad_dtype, device=r.device)
         dh = torch.empty((r.n, r.d), **f32) if need_h else None
         dw = torch.empty((r.v, r.d), **f32) if need_w else None
         g = (g_loss if g_loss is not None else torch.ones((), device=r.device))
@@ -435,7 +443,14 @@ def distillation_loss(student_hidden, weight, labels, teacher, *, student_ce_wei
             raise NotImplementedError("co-trained teachers (mutual / cojeffreys) are not provided")
         if teacher.mode != role:
             raise ValueError(f"TiedTeacher(mode={teacher.mode!r}) but the weights make it {role}")
+    # Gradients in the inputs' dtype straight from the library (bf16: the fp32
+    # result rounded once, as a cast would). A trained tied teacher sums two
+    # halves into the shared weight's gradient, which stays fp32 for that sum.
+    grad_dtype = student_hidden.dtype
+    if isinstance(teacher, TiedTeacher) and train_teacher:
+        grad_dtype = torch.float32
     kw = dict(kl_divergence=kl_divergence, teacher_temperature=kl_teacher_temperature,
+              grad_dtype=grad_dtype,
               student_hidden=student_hidden.detach().contiguous(),
               weight=weight.detach().contiguous(), student_ce_weight=student_ce_weight,
               teacher_ce_weight=teacher_ce_weight, kl_weight=kl_weight,

@@ -116,6 +116,9 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   if (p->keep_last_chunk != 0 && p->keep_last_chunk != 1) return KD_ERR_PARAM;
   if (p->saved_bytes < 0) return KD_ERR_PARAM;
   if (p->kl_output_unscaled != 0 && p->kl_output_unscaled != 1) return KD_ERR_PARAM;
+  if ((p->dh_dtype != KD_F32 && p->dh_dtype != KD_BF16) ||
+      (p->dw_dtype != KD_F32 && p->dw_dtype != KD_BF16))
+    return KD_ERR_DTYPE;
   if (p->compact_valid && q.mode != kd::MODE_TIED && q.mode != kd::MODE_SEPARATE)
     return KD_ERR_UNSUPPORTED;
 
@@ -129,6 +132,8 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
   q.normalizer = p->normalizer;
   q.kl = p->kl_divergence;
   q.kl_unscaled = p->kl_output_unscaled;
+  q.dh_bf16 = p->dh_dtype == KD_BF16;
+  q.dw_bf16 = p->dw_dtype == KD_BF16;
   // Student statistics at z/T: needed for the KL at T != 1, and always for the
   // reverse direction, whose weights are the student's softmax(z/T).
   q.need_zT = (q.T != 1.f || q.kl != KD_KL_FORWARD) ? 1 : 0;
@@ -212,6 +217,10 @@ kd_status plan_call(const kd_student* s, const kd_teacher* t, const kd_params* p
     off = align_up(off + 8 * (size_t)q.n * (size_t)q.k, 256);
     q.off_btko = off;
     off = align_up(off + 4 * (size_t)q.n * (size_t)(q.chunk / vt + 1), 256);
+  }
+  if (q.dh_bf16 && q.n_chunks > 1) {
+    q.off_dhacc = off;
+    off = align_up(off + 4 * (size_t)q.n * (size_t)std::max(q.d, q.dt), 256);
   }
   q.bwd_bytes = off;
   // The last chunk's products, kept in `saved` for the backward: columns of
@@ -323,7 +332,7 @@ kd_status kd_loss_fwd_noalloc(const kd_student* s, const kd_teacher* t, const kd
 
 kd_status kd_loss_bwd(const kd_student* s, const kd_teacher* t, const kd_params* p,
                       const int64_t* labels, const void* saved, const float* grad_loss,
-                      float* d_hidden, float* d_weight, int32_t accumulate, void* workspace,
+                      void* d_hidden, void* d_weight, int32_t accumulate, void* workspace,
                       size_t ws_bytes, void* stream, kd_trace* trace) {
   Plan q;
   const kd_status st = plan_call(s, t, p, labels, true, true, &q);
@@ -358,7 +367,7 @@ kd_status kd_loss_bwd_logits(const kd_student* s, const kd_teacher* t, const kd_
 
 kd_status kd_loss_bwd_teacher(const kd_student* s, const kd_teacher* t, const kd_params* p,
                               const int64_t* labels, const void* saved, const float* grad_loss,
-                              float* d_teacher_hidden, float* d_teacher_weight, int32_t accumulate,
+                              void* d_teacher_hidden, void* d_teacher_weight, int32_t accumulate,
                               void* workspace, size_t ws_bytes, void* stream, kd_trace* trace) {
   Plan q;
   const kd_status st = plan_call(s, t, p, labels, true, true, &q);

@@ -63,6 +63,7 @@ struct Plan {
   float normalizer = 0.f;
   int kl = KD_KL_FORWARD;  // KD_KL_*
   int kl_unscaled = 0;     // the per-token kl output without the T^2 factor
+  int dh_bf16 = 0, dw_bf16 = 0;  // gradient outputs in bf16 (else fp32)
   int need_zT = 0;    // statistics at z/T kept apart from z (T != 1, or a reverse-direction KL)
   int need_t1 = 0;    // teacher statistics at t kept apart from t/T_t (T_t != 1)
   int has_labels = 0;
@@ -91,6 +92,8 @@ struct Plan {
   // int32 [n][chunk / vt_rows + 1]), so the dz epilogue subtracts p itself
   size_t off_dz = 0, bwd_bytes = 0;
   size_t off_btks = 0, off_btko = 0;
+  // bf16 dH with several chunks: the chunks' fp32 sum [n][max(d, dt)] (off_dhacc)
+  size_t off_dhacc = 0;
   // Kept products of the last chunk in `saved` (keep_last_chunk): keep_ops
   // fp32 [dz_rows][keep_ld] matrices (student, then teacher) from byte keep_off.
   int keep = 0, keep_ops = 0;
@@ -130,7 +133,7 @@ kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, vo
 constexpr size_t kScratchBytes = (size_t)64 << 20;
 void* scratch_address(kd_status* st);
 kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
-                       float* d_hidden, float* d_weight, int accumulate, void* workspace,
+                       void* d_hidden, void* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace);
 // The backward to given student logits (student and teacher logits given).
 kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved,
@@ -138,7 +141,7 @@ kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved
                               hipStream_t stream, kd_trace* trace);
 // The teacher-CE backward: d_hidden / d_weight are the teacher's.
 kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,
-                               const float* grad_loss, float* d_hidden, float* d_weight,
+                               const float* grad_loss, void* d_hidden, void* d_weight,
                                int accumulate, void* workspace, hipStream_t stream, kd_trace* trace);
 
 }  // namespace kd

@@ -1766,14 +1766,32 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* m, int64_t c
   if (i < cnt) m[i] = 0.f;
 }
 
-// Rows i with pos[i] < 0 (left out by the compaction) of an fp32 [n x d] matrix
-// set to zero; one wave per row.
-__global__ __launch_bounds__(kThreads) void zero_rows_kernel(float* m, const int32_t* pos, int64_t n,
-                                                              int64_t d) {
+// Rows i with pos[i] < 0 (left out by the compaction) of a [n x d] matrix of
+// `elem`-byte elements set to zero (d elem a multiple of 4); one wave per row.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(void* m, const int32_t* pos, int64_t n,
+                                                              int64_t d, int elem) {
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (i >= n || pos[i] >= 0) return;
-  for (int64_t j = lane; j < d; j += 64) m[i * d + j] = 0.f;
+  const int64_t words = d * elem / 4;
+  float* row = static_cast<float*>(m) + i * words;
+  for (int64_t j = lane; j < words; j += 64) row[j] = 0.f;
+}
+
+// One element of a gradient output: the tile's value v, plus the fp32 partial
+// of the earlier chunks (cadd, nullable), plus the old output (accumulate),
+// stored as fp32 or rounded once to bf16.
+__device__ __forceinline__ void store_grad(void* C, int out_bf16, const float* cadd, int accumulate,
+                                           int64_t off, float v) {
+  if (cadd) v += cadd[off];
+  if (out_bf16) {
+    bf16_t* p = static_cast<bf16_t*>(C) + off;
+    if (accumulate) v += to_f32(*p);
+    *p = bf16_rne(v);
+  } else {
+    float* p = static_cast<float*>(C) + off;
+    *p = accumulate ? *p + v : v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1784,7 +1802,9 @@ template <typename T, bool AKC, bool BKC>
 struct GemmArgs {
   Operand<T, AKC> A;
   Operand<T, BKC> B;
-  float* C;
+  void* C;             // fp32, or bf16 (out_bf16)
+  int out_bf16;
+  const float* cadd;   // nullable: an fp32 partial added to every element (same layout as C)
   int64_t ldc, M, N, K;
   int accumulate;
   int n_mt, n_nt;
@@ -1817,9 +1837,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
       for (int r = 0; r < 4; ++r) {
         const int64_t row = m0 + acc_row(wm, mb, r, lane);
         if (row < M) {
-          float* p = a.C + (a.rowmap ? (int64_t)a.rowmap[row] : row) * a.ldc + col;
-          const float vv = acc[0][mb][nb][r];
-          *p = a.accumulate ? *p + vv : vv;
+          const int64_t off = (a.rowmap ? (int64_t)a.rowmap[row] : row) * a.ldc + col;
+          store_grad(a.C, a.out_bf16, a.cadd, a.accumulate, off, acc[0][mb][nb][r]);
         }
       }
     }
@@ -1833,7 +1852,9 @@ template <bool AKC, bool BKC, int BN>
 struct GemmPipeArgs {
   std::conditional_t<AKC, PipeOperand, PipeOperandMN> A;
   std::conditional_t<BKC, PipeOperand, PipeOperandMN> B;
-  float* C;
+  void* C;             // fp32, or bf16 (out_bf16)
+  int out_bf16;
+  const float* cadd;   // nullable: an fp32 partial added to every element (same layout as C)
   int64_t ldc, M, N, K;
   int accumulate;
   int n_mt, n_nt;
@@ -1878,11 +1899,8 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>&
       if (col >= a.N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (orow[mb][r] >= 0) {
-          float* p = a.C + orow[mb][r] * a.ldc + col;
-          const float vv = acc[0][mb][nb][r];
-          *p = a.accumulate ? *p + vv : vv;
-        }
+        if (orow[mb][r] >= 0)
+          store_grad(a.C, a.out_bf16, a.cadd, a.accumulate, orow[mb][r] * a.ldc + col, acc[0][mb][nb][r]);
       }
     }
 }
@@ -2172,25 +2190,43 @@ template <typename T, class G>
 // teacher = true: the teacher's from its CE gradient (dh / dw are then the
 // teacher's hidden and weight gradients, of width d_t).
 kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const float* grad,
-                     float* dh, float* dw, int accumulate, void* ws, hipStream_t stream,
+                     void* dh, void* dw, int accumulate, void* ws, hipStream_t stream,
                      kd_trace* trace, bool teacher) {
   Launch L{stream, trace};
   uint8_t* base = static_cast<uint8_t*>(ws);
   T* dz = reinterpret_cast<T*>(base + p.off_dz);
   const int64_t ldz = p.chunk;
   const int64_t gd = teacher ? p.dt : p.d;  // width of the gradients
+  const int eh = p.dh_bf16 ? 2 : 4, ew = p.dw_bf16 ? 2 : 4;  // gradient element bytes
   if (teacher && p.wt == 0.f) {  // no teacher CE: nothing reaches the teacher
     if (!accumulate) {
-      for (float* m : {dh, dw}) {
+      for (void* m : {dh, dw}) {
         if (!m) continue;
-        const int64_t cnt = (m == dh ? p.n : p.v) * gd;
+        const int64_t cnt = (m == dh ? p.n * eh : p.v * ew) * gd / 4;  // fp32 words (gd % 8 == 0)
         KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
-          fill_zero_kernel<<<dim3((unsigned)((cnt + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(m, cnt);
+          fill_zero_kernel<<<dim3((unsigned)((cnt + kThreads - 1) / kThreads)), kThreads, 0, stream>>>(
+              static_cast<float*>(m), cnt);
         }));
       }
     }
     return KD_OK;
   }
+  // bf16 dH over several chunks: the chunks before the last sum into an fp32
+  // buffer, which the last chunk's launch adds before its one rounding
+  float* dh_acc = (p.dh_bf16 && p.n_chunks > 1) ? reinterpret_cast<float*>(base + p.off_dhacc) : nullptr;
+  struct DhTarget {
+    void* C;
+    int out_bf16;
+    const float* cadd;
+    int accumulate;
+  };
+  auto dh_target = [&](int c) -> DhTarget {
+    const bool last = c == p.n_chunks - 1;
+    if (dh_acc && !last) return DhTarget{dh_acc, 0, nullptr, c > 0 ? 1 : 0};
+    if (dh_acc) return DhTarget{dh, 1, dh_acc, accumulate};
+    return DhTarget{dh, p.dh_bf16, nullptr, (accumulate || c > 0) ? 1 : 0};
+  };
+  void* const dw_base = dw;
   Compacted cp{nullptr, nullptr, nullptr, x.hs, x.ht};
   if (p.compact) {
     KD_TRY(compact_rows<T>(p, x, base, L, stream, &cp));
@@ -2198,7 +2234,7 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
     if (dh && !accumulate) {
       KD_TRY(L.run(KD_KERNEL_GEMM_DH, [&] {
         zero_rows_kernel<<<dim3((unsigned)((p.n + kThreads / 64 - 1) / (kThreads / 64))), kThreads, 0,
-                           stream>>>(dh, cp.pos, p.n, gd);
+                           stream>>>(dh, cp.pos, p.n, gd, eh);
       }));
     }
   }
@@ -2278,7 +2314,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         GemmPipeArgs<false, false, BN> ga;
         ga.A = PipeOperandMN{dz, ldz, cpad, p.dz_rows};
         ga.B = PipeOperandMN{hs, gd, gd, p.n};
-        ga.C = dw + c0 * gd;
+        ga.C = static_cast<uint8_t*>(dw_base) + c0 * gd * ew;
+        ga.out_bf16 = p.dw_bf16;
+        ga.cadd = nullptr;
         ga.ldc = gd;
         ga.M = cw;
         ga.N = gd;
@@ -2298,12 +2336,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         GemmPipeArgs<true, false, BN> gb;
         gb.A = PipeOperand{dz, ldz, p.n};
         gb.B = PipeOperandMN{wmat + c0 * gd, gd, gd, cw};
-        gb.C = dh;
+        const DhTarget tg = dh_target(c);
+        gb.C = tg.C;
+        gb.out_bf16 = tg.out_bf16;
+        gb.cadd = tg.cadd;
         gb.ldc = gd;
         gb.M = p.n;
         gb.N = gd;
         gb.K = cpad;
-        gb.accumulate = (accumulate || c > 0) ? 1 : 0;
+        gb.accumulate = tg.accumulate;
         gb.n_mt = (int)((p.n + 255) / 256);
         gb.n_nt = (int)((gd + BN - 1) / BN);
         gb.kdev = nullptr;
@@ -2346,7 +2387,9 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       GemmArgs<T, false, false> ga;
       ga.A = Operand<T, false>{dz, ldz, cpad, p.n};
       ga.B = Operand<T, false>{hs, gd, gd, p.n};
-      ga.C = dw + c0 * gd;
+      ga.C = static_cast<uint8_t*>(dw_base) + c0 * gd * ew;
+      ga.out_bf16 = p.dw_bf16;
+      ga.cadd = nullptr;
       ga.ldc = gd;
       ga.M = cw;
       ga.N = gd;
@@ -2367,12 +2410,15 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
       GemmArgs<T, true, false> gb;
       gb.A = Operand<T, true>{dz, ldz, p.n, cpad};
       gb.B = Operand<T, false>{wmat + c0 * gd, gd, gd, cw};
-      gb.C = dh;
+      const DhTarget tg = dh_target(c);
+      gb.C = tg.C;
+      gb.out_bf16 = tg.out_bf16;
+      gb.cadd = tg.cadd;
       gb.ldc = gd;
       gb.M = p.n;
       gb.N = gd;
       gb.K = cw;
-      gb.accumulate = (accumulate || c > 0) ? 1 : 0;
+      gb.accumulate = tg.accumulate;
       gb.n_mt = p.n_ttiles;
       gb.n_nt = (int)((gd + kTile - 1) / kTile);
       gb.kdev = nullptr;
@@ -2442,7 +2488,7 @@ void* scratch_address(kd_status* st) {
 
 namespace {
 kd_status backward_any(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
-                       float* d_hidden, float* d_weight, int accumulate, void* workspace,
+                       void* d_hidden, void* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace, bool teacher) {
   if (p.dtype == KD_BF16) {
     if (p.pipe)
@@ -2457,7 +2503,7 @@ kd_status backward_any(const Plan& p, const Tensors& x, const void* saved, const
 }  // namespace
 
 kd_status run_backward(const Plan& p, const Tensors& x, const void* saved, const float* grad_loss,
-                       float* d_hidden, float* d_weight, int accumulate, void* workspace,
+                       void* d_hidden, void* d_weight, int accumulate, void* workspace,
                        hipStream_t stream, kd_trace* trace) {
   return backward_any(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace, stream,
                       trace, false);
@@ -2499,7 +2545,7 @@ kd_status run_backward_logits(const Plan& p, const Tensors& x, const void* saved
 }
 
 kd_status run_backward_teacher(const Plan& p, const Tensors& x, const void* saved,
-                               const float* grad_loss, float* d_hidden, float* d_weight,
+                               const float* grad_loss, void* d_hidden, void* d_weight,
                                int accumulate, void* workspace, hipStream_t stream, kd_trace* trace) {
   return backward_any(p, x, saved, grad_loss, d_hidden, d_weight, accumulate, workspace, stream,
                       trace, true);

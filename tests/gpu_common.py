@@ -74,7 +74,7 @@ def oracle_problem(w: Workload, x: dict, rows=None):
 def make_runner(w: Workload, x: dict, vocab_chunk: int = 0, reduction: str = "mean",
                 want_grads: Optional[bool] = None,
                 want_teacher_ce: Optional[bool] = None,
-                keep_last_chunk: Optional[bool] = None) -> Runner:
+                keep_last_chunk: Optional[bool] = None, grad_dtype=torch.float32) -> Runner:
     kw = dict(labels=x["labels"], student_ce_weight=w.student_ce_weight,
               teacher_ce_weight=w.teacher_ce_weight, kl_weight=w.kl_weight,
               temperature=w.temperature, ignore_index=w.ignore_index, reduction=reduction,
@@ -82,7 +82,7 @@ def make_runner(w: Workload, x: dict, vocab_chunk: int = 0, reduction: str = "me
               want_grads=(not w.forward_only) if want_grads is None else want_grads,
               want_teacher_ce=want_teacher_ce, kl_divergence=w.kl_divergence,
               teacher_temperature=w.teacher_temperature, compact_valid=w.compact_valid,
-              keep_last_chunk=keep_last_chunk)
+              keep_last_chunk=keep_last_chunk, grad_dtype=grad_dtype)
     if w.student == "logits":
         kw["student_logits"] = x["student_logits"]
     else:

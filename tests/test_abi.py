@@ -205,7 +205,8 @@ def test_backward_workspace_is_O_n_chunk_not_n_vocab():
     ("tT_neg", L.KD_ERR_PARAM), ("tT_nan", L.KD_ERR_PARAM), ("topk_tT", L.KD_ERR_UNSUPPORTED),
     ("tlog_null", L.KD_ERR_NULL), ("tlog_misaligned", L.KD_ERR_ALIGN),
     ("topk_compact", L.KD_ERR_UNSUPPORTED), ("compact_bad", L.KD_ERR_PARAM),
-    ("unscaled_bad", L.KD_ERR_PARAM),
+    ("unscaled_bad", L.KD_ERR_PARAM), ("dh_dtype_bad", L.KD_ERR_DTYPE),
+    ("dw_dtype_bad", L.KD_ERR_DTYPE),
 ])
 def test_forward_rejects_invalid_arguments(case, expect):
     kind = "topk" if case.startswith("topk") else ("separate" if case.startswith("sep") else "tied")
@@ -277,6 +278,10 @@ def test_forward_rejects_invalid_arguments(case, expect):
         p.compact_valid = 2
     elif case == "unscaled_bad":
         p.kl_output_unscaled = 2
+    elif case == "dh_dtype_bad":
+        p.dh_dtype = 2
+    elif case == "dw_dtype_bad":
+        p.dw_dtype = -1
     elif case == "tlog_null":
         t.kind = L.KD_TEACHER_LOGITS
         t.logits = None
@@ -403,3 +408,21 @@ def test_no_alloc_forward_checks_on_the_host():
     s, t, p = _desc()
     assert call(s, t, p, flags=FAKE + 2) == L.KD_ERR_ALIGN
     assert call(s, t, p, labels=None) == L.KD_ERR_NULL
+
+
+def test_bf16_hidden_gradient_workspace():
+    """A bf16 dH over several chunks adds an fp32 [n, max(d, d_t)] buffer to the
+    backward workspace; fp32 dH, bf16 dW or a single chunk do not."""
+    s, t, p = _desc("separate", n=300, d=512, d_t=256)
+    p.vocab_chunk = 1024  # 3 chunks of the 3000 columns
+    base = _ws(s, t, p, 1)[1]
+    p.dw_dtype = L.KD_BF16
+    assert _ws(s, t, p, 1)[1] == base
+    p.dh_dtype = L.KD_BF16
+    extra = _ws(s, t, p, 1)[1] - base
+    assert 4 * 300 * 512 <= extra <= 4 * 300 * 512 + 256
+    p.vocab_chunk = 0  # one chunk: dH is rounded directly
+    p.dh_dtype = L.KD_F32
+    one = _ws(s, t, p, 1)[1]
+    p.dh_dtype = L.KD_BF16
+    assert _ws(s, t, p, 1)[1] == one

@@ -506,3 +506,52 @@ def test_topk_zero_subnormal_and_cancelling_entries():
     err = np.abs(to_np(dw)[vstar].astype(np.float64) - dW[vstar]).max()
     say(f"  dW[v*]: |gpu - oracle| = {err:.3e}, scale {scale:.3e}, ratio {err / scale:.2e}")
     assert err <= 2e-4 * scale, f"dW[v*] error {err / scale:.2e} of the p-term scale"
+
+
+# bf16 gradient outputs: (workload, vocab chunk); several chunks unless noted
+BF16_GRAD_CASES = {
+    "tied": (C2.scaled(n=300, d=512, v=3000), 1024),
+    "tied_one_chunk": (C2.scaled(n=300, d=512, v=3000), 0),
+    "tied_compact": (C2.scaled(n=300, d=512, v=3000, ignore_frac=0.3, compact_valid=True), 768),
+    "separate_train_teacher": (C3.scaled(n=200, d=256, d_t=512, v=2000, teacher_ce_weight=0.5), 512),
+    "topk": (C4.scaled(n=300, d=512, v=5000), 1024),
+    "fp32_inputs": (C1.scaled(n=70, v=1000, ignore_frac=0.2), 256),
+}
+
+
+@pytest.mark.parametrize("name", list(BF16_GRAD_CASES))
+def test_bf16_gradient_outputs(name):
+    """dH / dW (and a CE-trained teacher's) written as bf16 equal the fp32
+    gradients rounded to nearest even, bit for bit: one rounding of the same
+    fp32 sums (dH sums its chunks in an fp32 buffer first). With accumulate
+    the old bf16 value is added in fp32 before that one rounding."""
+    w, chunk = BF16_GRAD_CASES[name]
+    say(f"[bf16 grads] {name} n={w.n} d={w.d} v={w.v} chunk={chunk}")
+    x = make_inputs(w, "cuda", seed=9)
+    trained = w.teacher_ce_weight > 0
+    res = {}
+    for gdt in (torch.float32, torch.bfloat16):
+        r = make_runner(w, x, chunk, grad_dtype=gdt)
+        r.forward()
+        g = {"dh": torch.empty((r.n, r.d), dtype=gdt, device="cuda"),
+             "dw": torch.empty((r.v, r.d), dtype=gdt, device="cuda")}
+        r.backward(g["dh"], g["dw"])
+        if trained:
+            g["dht"] = torch.empty((r.n, r.dt), dtype=gdt, device="cuda")
+            g["dwt"] = torch.empty((r.v, r.dt), dtype=gdt, device="cuda")
+            r.backward_teacher(g["dht"], g["dwt"])
+        torch.cuda.synchronize()
+        res[gdt] = (r, g)
+    r16, g16 = res[torch.bfloat16]
+    g32 = res[torch.float32][1]
+    for k in g16:
+        assert torch.equal(g16[k], g32[k].to(torch.bfloat16)), f"{name}: bf16 {k} is not the rounded fp32 {k}"
+    # accumulate: old + new in fp32, rounded once
+    old = {k: v.clone() for k, v in g16.items()}
+    r16.forward()
+    r16.backward(g16["dh"], g16["dw"], accumulate=True)
+    torch.cuda.synchronize()
+    for k in ("dh", "dw"):
+        want = old[k].float() + g32[k]
+        err = (g16[k].float() - want).abs()
+        assert (err <= 2.0 ** -8 * want.abs() + 1e-30).all(), f"{name}: accumulated bf16 {k}"
