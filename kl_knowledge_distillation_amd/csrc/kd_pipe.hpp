@@ -70,6 +70,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer descriptor over [base, base + bytes); sizes of 4 GiB and more are
@@ -356,6 +357,7 @@ __device__ __forceinline__ void pipe_copy(const SA& sa, const SB (&sb)[NB], int6
 #define KD_PIPE_AHEAD 4
 #endif
 constexpr int kPipeAhead = KD_PIPE_AHEAD;
+
 struct PipePrefetch {
   int on;         // 0: no prefetch
   int a_share;    // 0..7
@@ -420,19 +422,22 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     bool pf_on = false;
     rsrc_t pf_r = make_rsrc(nullptr, 0);  // no records: reads nothing
     uint32_t pf_voff = 0;
-    if constexpr (C::kAKC && C::kBKC && NB <= 2 && C::kBBytes / 128 == 128) {
+    constexpr int kRowsB = C::kBBytes / 128;  // rows of one B operand
+    if constexpr (C::kAKC && C::kBKC && NB * kRowsB == 256) {
+      // 256 B rows in all (two operands of 128, or one of 256): each of the 4
+      // vocabulary tiles of the group prefetches a quarter of them, 32 per wave
       if (pf.on) {
         pf_on = true;
         pf_r = sa.rsrc;
         if (gw < 2) {
           pf_voff = (uint32_t)(pf.a_share * 32 + gw * 16 + (lane & 15)) * sa.stride;
         } else {
-          constexpr int kHalf = NB * 16;  // B rows per wave
-          const int first = pf.b_share * 2 * kHalf + (gw - 2) * kHalf;  // of the NB x 128 B rows
+          constexpr int kHalf = NB * kRowsB / 8;  // B rows per wave
+          const int first = pf.b_share * 2 * kHalf + (gw - 2) * kHalf;  // of the NB x kRowsB B rows
           // (a branch, not an index: an indexed sb would live in scratch)
-          const TileSrc<C::kBKC, C::kBBytes / 128>& src = (first >= 128) ? sb[NB - 1] : sb[0];
+          const TileSrc<C::kBKC, kRowsB>& src = (first >= kRowsB) ? sb[NB - 1] : sb[0];
           pf_r = src.rsrc;
-          pf_voff = (uint32_t)((first & 127) + (lane & (kHalf - 1))) * src.stride;
+          pf_voff = (uint32_t)((first % kRowsB) + (lane & (kHalf - 1))) * src.stride;
         }
       }
     }
