@@ -70,7 +70,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer descriptor over [base, base + bytes); sizes of 4 GiB and more are
@@ -357,7 +356,6 @@ __device__ __forceinline__ void pipe_copy(const SA& sa, const SB (&sb)[NB], int6
 #define KD_PIPE_AHEAD 4
 #endif
 constexpr int kPipeAhead = KD_PIPE_AHEAD;
-
 struct PipePrefetch {
   int on;         // 0: no prefetch
   int a_share;    // 0..7
