@@ -91,32 +91,54 @@ __device__ __forceinline__ void rec_store(float* r, int64_t stride, const RowSta
   r[9 * stride] = o.ar;
 }
 
+// Read access to a wave's tile values, value (mb, nb, r) = register r of
+// block (mb, nb): fp32 accumulators, or given bf16 logits still packed two to
+// a register (bf16 -> fp32 is exact, so unpacking at each use loses nothing
+// and halves the registers the tile holds).
+template <int NBT>
+struct AccView {
+  const f32x4 (&x)[kMB][NBT];
+  __device__ __forceinline__ float operator()(int mb, int nb, int r) const { return x[mb][nb][r]; }
+};
+template <int NBT>
+struct PackedView {
+  const uint2 (&u)[kMB][NBT];
+  __device__ __forceinline__ float operator()(int mb, int nb, int r) const {
+    const uint32_t w = (r < 2) ? u[mb][nb].x : u[mb][nb].y;
+    return __uint_as_float((r & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <int NBT>
+__device__ __forceinline__ AccView<NBT> view(const f32x4 (&x)[kMB][NBT]) { return AccView<NBT>{x}; }
+template <int NBT>
+__device__ __forceinline__ PackedView<NBT> view(const uint2 (&u)[kMB][NBT]) { return PackedView<NBT>{u}; }
+
 // Bit 4 mb + r of `ok`: register r of row block mb is a real vocabulary row.
 __device__ __forceinline__ bool ok_bit(uint32_t ok, int mb, int r) { return (ok >> (mb * 4 + r)) & 1u; }
 
 // Largest of the 16 values a lane holds for token block nb (masked rows skipped).
-template <bool TAIL, int NBT>
-__device__ __forceinline__ float tile_max(const f32x4 (&x)[kMB][NBT], int nb, uint32_t ok) {
+template <bool TAIL, class XV>
+__device__ __forceinline__ float tile_max(const XV& x, int nb, uint32_t ok) {
   float m = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (!TAIL || ok_bit(ok, mb, r)) m = fmaxf(m, x[mb][nb][r]);
+      if (!TAIL || ok_bit(ok, mb, r)) m = fmaxf(m, x(mb, nb, r));
   return m;
 }
 
 // sum over the lane's 16 values of 2^(x c - mc); mc = c * (token max), so every
 // term is at most 1 and all partial sums of a token share one reference.
-template <bool TAIL, int NBT>
-__device__ __forceinline__ float tile_sum(const f32x4 (&x)[kMB][NBT], int nb, float c, float mc, uint32_t ok) {
+template <bool TAIL, class XV>
+__device__ __forceinline__ float tile_sum(const XV& x, int nb, float c, float mc, uint32_t ok) {
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mc));
-      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mc));
+      float e0 = exp2_fast(fmaf(x(mb, nb, r), c, -mc));
+      float e1 = exp2_fast(fmaf(x(mb + 1, nb, r), c, -mc));
       if (TAIL) {
         e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
         e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
@@ -132,17 +154,16 @@ __device__ __forceinline__ float tile_sum(const f32x4 (&x)[kMB][NBT], int nb, fl
 // x = z, y = t, a = sum e (z - t rho); rho = T_s / T_t, so a / T_s is the
 // weighted sum of t / T_t - z / T_s (or its negative). ZERO_SAFE: an e of 0
 // adds 0 even where the difference is infinite (a teacher logit of -inf).
-template <bool TAIL, bool TEACHER_W, bool ZERO_SAFE = false, int NBT = kNB>
-__device__ __forceinline__ void tile_sum_cross(const f32x4 (&x)[kMB][NBT], const f32x4 (&y)[kMB][NBT], int nb,
-                                               float c, float mc,
+template <bool TAIL, bool TEACHER_W, bool ZERO_SAFE = false, class XV, class YV>
+__device__ __forceinline__ void tile_sum_cross(const XV& x, const YV& y, int nb, float c, float mc,
                                                float rho, uint32_t ok, float& s, float& a) {
   float s0 = 0.f, s1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mc));
-      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mc));
+      float e0 = exp2_fast(fmaf(x(mb, nb, r), c, -mc));
+      float e1 = exp2_fast(fmaf(x(mb + 1, nb, r), c, -mc));
       if (TAIL) {
         e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
         e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
@@ -151,11 +172,11 @@ __device__ __forceinline__ void tile_sum_cross(const f32x4 (&x)[kMB][NBT], const
       s1 += e1;
       float d0, d1;
       if constexpr (TEACHER_W) {
-        d0 = fmaf(x[mb][nb][r], rho, -y[mb][nb][r]);
-        d1 = fmaf(x[mb + 1][nb][r], rho, -y[mb + 1][nb][r]);
+        d0 = fmaf(x(mb, nb, r), rho, -y(mb, nb, r));
+        d1 = fmaf(x(mb + 1, nb, r), rho, -y(mb + 1, nb, r));
       } else {
-        d0 = fmaf(y[mb][nb][r], -rho, x[mb][nb][r]);
-        d1 = fmaf(y[mb + 1][nb][r], -rho, x[mb + 1][nb][r]);
+        d0 = fmaf(y(mb, nb, r), -rho, x(mb, nb, r));
+        d1 = fmaf(y(mb + 1, nb, r), -rho, x(mb + 1, nb, r));
       }
       if constexpr (ZERO_SAFE) {
         d0 = (e0 > 0.f) ? d0 : 0.f;
@@ -173,17 +194,16 @@ __device__ __forceinline__ void tile_sum_cross(const f32x4 (&x)[kMB][NBT], const
 // element serves both temperatures (the square rounds once more, well inside
 // fp32). STUDENT_W: the student-weighted cross term (e of z, d = z - t rho);
 // CROSS = false: no cross term (a is left alone).
-template <bool TAIL, bool CROSS, bool TEACHER_W, bool ZERO_SAFE = false, int NBT = kNB>
-__device__ __forceinline__ void tile_sums_sq(const f32x4 (&x)[kMB][NBT], const f32x4 (&y)[kMB][NBT], int nb,
-                                             float c, float mc,
+template <bool TAIL, bool CROSS, bool TEACHER_W, bool ZERO_SAFE = false, class XV, class YV>
+__device__ __forceinline__ void tile_sums_sq(const XV& x, const YV& y, int nb, float c, float mc,
                                              float rho, uint32_t ok, float& s, float& q, float& a) {
   float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < kMB; mb += 2)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e0 = exp2_fast(fmaf(x[mb][nb][r], c, -mc));
-      float e1 = exp2_fast(fmaf(x[mb + 1][nb][r], c, -mc));
+      float e0 = exp2_fast(fmaf(x(mb, nb, r), c, -mc));
+      float e1 = exp2_fast(fmaf(x(mb + 1, nb, r), c, -mc));
       if (TAIL) {
         e0 = ok_bit(ok, mb, r) ? e0 : 0.f;
         e1 = ok_bit(ok, mb + 1, r) ? e1 : 0.f;
@@ -195,11 +215,11 @@ __device__ __forceinline__ void tile_sums_sq(const f32x4 (&x)[kMB][NBT], const f
       if constexpr (CROSS) {
         float d0, d1;
         if constexpr (TEACHER_W) {
-          d0 = fmaf(x[mb][nb][r], rho, -y[mb][nb][r]);
-          d1 = fmaf(x[mb + 1][nb][r], rho, -y[mb + 1][nb][r]);
+          d0 = fmaf(x(mb, nb, r), rho, -y(mb, nb, r));
+          d1 = fmaf(x(mb + 1, nb, r), rho, -y(mb + 1, nb, r));
         } else {
-          d0 = fmaf(y[mb][nb][r], -rho, x[mb][nb][r]);
-          d1 = fmaf(y[mb + 1][nb][r], -rho, x[mb + 1][nb][r]);
+          d0 = fmaf(y(mb, nb, r), -rho, x(mb, nb, r));
+          d1 = fmaf(y(mb + 1, nb, r), -rho, x(mb + 1, nb, r));
         }
         if constexpr (ZERO_SAFE) {
           d0 = (e0 > 0.f) ? d0 : 0.f;
@@ -354,13 +374,18 @@ __device__ __forceinline__ void load_logits_tile(const T* L, int64_t n, int64_t 
 // block); otherwise element loads. Tokens past n and rows past v read 0.
 // (Staging the tile through LDS with buffer loads instead left no LDS for the
 // cooperative prefetch and measured 2-4% slower.)
-typedef uint2 GivenRaw[kMB][kNB];
+template <int NBT>
+using GivenRawT = uint2[kMB][NBT];
+typedef GivenRawT<kNB> GivenRaw;
+// G: the tile geometry (its token column map and token blocks per wave);
+// token blocks nb0 .. nb0 + count - 1 (default: all of them).
+template <class G>
 __device__ __forceinline__ void given_raw_load(const bf16_t* L, int64_t n, int64_t v, int64_t t0,
                                                int64_t v0, int wm, int wn, int lane, bool vec,
-                                               GivenRaw& raw) {
+                                               GivenRawT<G::kNB>& raw, int nb0 = 0, int count = G::kNB) {
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) {
-    const int64_t tok = t0 + acc_col(wn, nb, lane);
+  for (int nb = nb0; nb < nb0 + count; ++nb) {
+    const int64_t tok = t0 + G::col(wn, nb, lane);
     const bool live = tok < n;
     const int64_t base = live ? tok * v : 0;
 #pragma unroll
@@ -378,11 +403,12 @@ __device__ __forceinline__ void given_raw_load(const bf16_t* L, int64_t n, int64
   }
 }
 
-__device__ __forceinline__ void given_raw_unpack(const GivenRaw& raw, WaveAcc& out) {
+template <int NBT>
+__device__ __forceinline__ void given_raw_unpack(const GivenRawT<NBT>& raw, f32x4 (&out)[kMB][NBT]) {
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
+    for (int nb = 0; nb < NBT; ++nb) {
       const uint2 u = raw[mb][nb];
       out[mb][nb][0] = __uint_as_float(u.x << 16);
       out[mb][nb][1] = __uint_as_float(u.x & 0xffff0000u);
@@ -463,7 +489,12 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
 
   f32x4 acc[NB][kMB][NBT];
   f32x4 tacc[1][kMB][NBT];  // teacher accumulator of the separate / logits modes
-  Acc zl;                   // student logits loaded in LOGITS mode
+  // student logits given (LOGITS): unpacked to fp32 (128-token tiles), or kept
+  // packed and unpacked at each use (256-token tiles, beside 128 registers of
+  // teacher accumulators)
+  constexpr bool kPackedZ = MODE == MODE_LOGITS && kGivenRegs && G::kTT > 128;
+  Acc zl;
+  GivenRawT<NBT> zraw;
 
   // the tile's share of the cooperative prefetch (grouped order: token tiles
   // tt % 8 and vocabulary tiles slice % 4 run side by side)
@@ -483,10 +514,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
     if constexpr (kGivenRegs) {
-      GivenRaw raw;
-      given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+      GivenRawT<NBT> raw;
+      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
-      given_raw_unpack(raw, tacc[0]);
+      given_raw_unpack<NBT>(raw, tacc[0]);
     } else {
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
@@ -494,11 +525,16 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   } else {  // MODE_LOGITS
     const T* L = static_cast<const T*>(a.logits);
     const T* const bt[1] = {ht};
-    if constexpr (kGivenRegs) {
-      GivenRaw raw;
-      given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+    if constexpr (kGivenRegs && G::kTT > 128) {
+      // 256-token tiles: the given tile (64 registers) would not fit beside the
+      // main loop's; it is loaded once the loop is done (its latency is a few
+      // percent of the tile's)
       tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
-      given_raw_unpack(raw, zl);
+    } else if constexpr (kGivenRegs) {
+      GivenRawT<NBT> raw;
+      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
+      given_raw_unpack<NBT>(raw, zl);
     } else {
       tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, zl);
@@ -532,49 +568,69 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       for (int r = 0; r < 4; ++r)
         if (v0 + acc_row(wm, mb, r, lane) < a.v) ok |= 1u << (mb * 4 + r);
   }
-  const Acc& z = (MODE == MODE_LOGITS) ? zl : acc[0];
-  const Acc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const Acc& z_acc = (MODE == MODE_LOGITS) ? zl : acc[0];
+  const Acc& tl_acc = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const auto z = [&]() {
+    if constexpr (kPackedZ) return view(zraw);
+    else return view(z_acc);
+  }();
+  const auto tl = view(tl_acc);
   constexpr bool kTeacher = MODE != MODE_TOPK;
   constexpr bool kInfT = MODE == MODE_TLOGITS;  // given teacher logits may be -inf
   constexpr int kSums = 6;  // sz1, szT, stT, a (top-K: sum p z[idx]), st1, ar
   static_assert(G::kWM * 2 * NBT * (2 + kSums) * 16 * 4 <= kLdsMain, "epilogue exchange fits the LDS");
-  float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][NBT][2][16]
-  float* xsum = xmax + G::kWM * 2 * NBT * 2 * 16;                 // [kWM][2][NBT][kSums][16]
+  constexpr int kNBX = kPackedZ ? NBT / 2 : NBT;                  // token blocks per exchange
+  float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNBX][2][16]
+  float* xsum = xmax + G::kWM * 2 * kNBX * 2 * 16;                // [kWM][2][kNBX][kSums][16]
   const int rb = acc_row(wm, 0, 0, lane);  // this lane's rows: v0 + rb + 16 mb + r
   const int l16 = lane & 15;
 
-  float mz[NBT], mt[NBT];
+  // 256-token tiles with packed given logits run the epilogue in two halves of
+  // token blocks, each loading its half of the given tile just before it, so
+  // only half of it is held beside the teacher accumulators.
+  constexpr int kHalves = kPackedZ ? 2 : 1;
+  constexpr int NBH = NBT / kHalves;
+  auto half = [&](auto h_tag) {
+  constexpr int h = decltype(h_tag)::value;  // compile-time, so every register index is too
+  if constexpr (kPackedZ) {
+    const T* L = static_cast<const T*>(a.logits);
+    given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, zraw,
+                      h * NBH, NBH);
+  }
+  float mz[NBH], mt[NBH];
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb) {
-    mz[nb] = tail ? tile_max<true>(z, nb, ok) : tile_max<false>(z, nb, ok);
-    mt[nb] = !kTeacher ? 0.f : (tail ? tile_max<true>(tl, nb, ok) : tile_max<false>(tl, nb, ok));
+  for (int jb = 0; jb < NBH; ++jb) {
+    const int nb = h * NBH + jb;
+    mz[jb] = tail ? tile_max<true>(z, nb, ok) : tile_max<false>(z, nb, ok);
+    mt[jb] = !kTeacher ? 0.f : (tail ? tile_max<true>(tl, nb, ok) : tile_max<false>(tl, nb, ok));
 #pragma unroll
     for (int off = 16; off <= 32; off *= 2) {
-      mz[nb] = fmaxf(mz[nb], __shfl_xor(mz[nb], off));
-      if (kTeacher) mt[nb] = fmaxf(mt[nb], __shfl_xor(mt[nb], off));
+      mz[jb] = fmaxf(mz[jb], __shfl_xor(mz[jb], off));
+      if (kTeacher) mt[jb] = fmaxf(mt[jb], __shfl_xor(mt[jb], off));
     }
     if (lane < 16) {
-      float* p = xmax + (((wm * 2 + wn) * NBT + nb) * 2) * 16 + l16;
-      p[0] = mz[nb];
-      p[16] = mt[nb];
+      float* p = xmax + (((wm * 2 + wn) * NBH + jb) * 2) * 16 + l16;
+      p[0] = mz[jb];
+      p[16] = mt[jb];
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb) {
+  for (int jb = 0; jb < NBH; ++jb) {
     // every wave reads the same kWM values (fmax is exact, so the order is free)
     float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int src = 0; src < G::kWM; ++src) {
-      const float* p = xmax + (((src * 2 + wn) * NBT + nb) * 2) * 16 + l16;
+      const float* p = xmax + (((src * 2 + wn) * NBH + jb) * 2) * 16 + l16;
       m0 = fmaxf(m0, p[0]);
       m1 = fmaxf(m1, p[16]);
     }
-    mz[nb] = m0;
-    mt[nb] = m1;
+    mz[jb] = m0;
+    mt[jb] = m1;
   }
 #pragma unroll
-  for (int nb = 0; nb < NBT; ++nb) {
+  for (int jb = 0; jb < NBH; ++jb) {
+    const int nb = h * NBH + jb;
     float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const bool rev = a.kl != KD_KL_FORWARD;
     if constexpr (MODE == MODE_TOPK) {
@@ -596,17 +652,17 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) zz = (d == 16 * mb + r) ? z[mb][nb][r] : zz;
+            for (int r = 0; r < 4; ++r) zz = (d == 16 * mb + r) ? z(mb, nb, r) : zz;
           cr = fmaf(pr[j], zz, cr);
         }
       }
       v[3] = cr;
     }
-    const float mz1 = mz[nb] * kLog2e, mzT = mz[nb] * a.cT;
+    const float mz1 = mz[jb] * kLog2e, mzT = mz[jb] * a.cT;
     // A teacher tile with no finite logit (all -inf) sums 2^-inf = 0 against a
     // finite reference; its record keeps the -inf maximum, which the merge
     // treats as empty.
-    const float mtb = (kInfT && mt[nb] == -INFINITY) ? 0.f : mt[nb];
+    const float mtb = (kInfT && mt[jb] == -INFINITY) ? 0.f : mt[jb];
     const float mtT = mtb * a.cTt, mt1 = mtb * kLog2e;
     auto sums = [&](auto tail_tag) {
       constexpr bool TL = decltype(tail_tag)::value;
@@ -634,7 +690,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       v[j] += __shfl_xor(v[j], 32);
     }
     if (lane < 16) {
-      float* p = xsum + (((wm * 2 + wn) * NBT + nb) * kSums) * 16 + l16;
+      float* p = xsum + (((wm * 2 + wn) * NBH + jb) * kSums) * 16 + l16;
 #pragma unroll
       for (int j = 0; j < kSums; ++j) p[j * 16] = v[j];
     }
@@ -642,11 +698,12 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   __syncthreads();
   if (wm == 0 && lane < 16) {
 #pragma unroll
-    for (int nb = 0; nb < NBT; ++nb) {
+    for (int jb = 0; jb < NBH; ++jb) {
+      const int nb = h * NBH + jb;
       float v[kSums] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int src = 0; src < G::kWM; ++src) {  // fixed order
-        const float* p = xsum + (((src * 2 + wn) * NBT + nb) * kSums) * 16 + l16;
+        const float* p = xsum + (((src * 2 + wn) * NBH + jb) * kSums) * 16 + l16;
 #pragma unroll
         for (int j = 0; j < kSums; ++j) v[j] += p[j * 16];
       }
@@ -654,16 +711,19 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       if (tok < a.n) {
         const int64_t stride = (int64_t)a.n_slices * a.n;
         float* r = a.rec + (int64_t)slice * a.n + tok;
-        r[0 * stride] = mz[nb] * kLog2e; r[1 * stride] = v[0];
-        r[2 * stride] = mz[nb] * a.cT;   r[3 * stride] = v[1];
-        r[4 * stride] = mt[nb] * a.cTt;  r[5 * stride] = v[2];
+        r[0 * stride] = mz[jb] * kLog2e; r[1 * stride] = v[0];
+        r[2 * stride] = mz[jb] * a.cT;   r[3 * stride] = v[1];
+        r[4 * stride] = mt[jb] * a.cTt;  r[5 * stride] = v[2];
         // top-K: field 6 carries the tile's cross term sum p z[idx]
         r[6 * stride] = v[3];
-        r[7 * stride] = mt[nb] * kLog2e; r[8 * stride] = v[4];
+        r[7 * stride] = mt[jb] * kLog2e; r[8 * stride] = v[4];
         r[9 * stride] = v[5];
       }
     }
   }
+  };
+  half(std::integral_constant<int, 0>{});
+  if constexpr (kHalves == 2) half(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1512,9 +1572,9 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     if constexpr (MODE == MODE_TLOGITS) {
       const T* L = static_cast<const T*>(a.tlogits);
       if constexpr (kGivenRegs) {
-        GivenRaw raw;
-        given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-        given_raw_unpack(raw, tacc[0]);
+        GivenRawT<NBT> raw;
+        given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+        given_raw_unpack<NBT>(raw, tacc[0]);
       } else {
         given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
       }
@@ -1531,10 +1591,10 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
     if constexpr (kGivenRegs) {
-      GivenRaw raw;
-      given_raw_load(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
+      GivenRawT<NBT> raw;
+      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
-      given_raw_unpack(raw, tacc[0]);
+      given_raw_unpack<NBT>(raw, tacc[0]);
     } else {
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
@@ -2155,7 +2215,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
                 <<<fgrid, G::kThreads, 0, stream>>>(fa);
             break;
           case MODE_TLOGITS: fwd_tiles_kernel<T, MODE_TLOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
-          default: fwd_tiles_kernel<T, MODE_LOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          default:  // one B operand: the 256-token tiles in the pipelined geometry
+            fwd_tiles_kernel<T, MODE_LOGITS, std::conditional_t<G::kPipe, GeoWide, G>>
+                <<<fgrid, G::kThreads, 0, stream>>>(fa);
+            break;
         }
       }));
       last_slices = fa.n_slices;
@@ -2440,7 +2503,7 @@ static_assert(kPipeK == kPipeBK, "K step of the pipelined path");
 static_assert(GeoWide::kVT == GeoFused::kVT, "one vocabulary tile for every pipelined mode");
 int pipe_vocab_rows() { return GeoFused::kVT; }
 int fused_token_rows(int mode, int pipe) {
-  return (pipe && mode == MODE_TOPK) ? GeoWide::kTT : GeoFused::kTT;
+  return (pipe && (mode == MODE_TOPK || mode == MODE_LOGITS)) ? GeoWide::kTT : GeoFused::kTT;
 }
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,

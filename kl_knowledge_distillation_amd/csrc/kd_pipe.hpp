@@ -421,9 +421,10 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     rsrc_t pf_r = make_rsrc(nullptr, 0);  // no records: reads nothing
     uint32_t pf_voff = 0;
     constexpr int kRowsB = C::kBBytes / 128;  // rows of one B operand
-    if constexpr (C::kAKC && C::kBKC && NB * kRowsB == 256) {
-      // 256 B rows in all (two operands of 128, or one of 256): each of the 4
-      // vocabulary tiles of the group prefetches a quarter of them, 32 per wave
+    if constexpr (C::kAKC && C::kBKC && (NB * kRowsB == 128 || NB * kRowsB == 256)) {
+      // NB x kRowsB B rows in all (one operand of 128 or 256, or two of 128):
+      // each of the 4 vocabulary tiles of the group prefetches a quarter of
+      // them, half per wave
       if (pf.on) {
         pf_on = true;
         pf_r = sa.rsrc;
