@@ -489,12 +489,14 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
 
   f32x4 acc[NB][kMB][NBT];
   f32x4 tacc[1][kMB][NBT];  // teacher accumulator of the separate / logits modes
-  // student logits given (LOGITS): unpacked to fp32 (128-token tiles), or kept
-  // packed and unpacked at each use (256-token tiles, beside 128 registers of
-  // teacher accumulators)
-  constexpr bool kPackedZ = MODE == MODE_LOGITS && kGivenRegs && G::kTT > 128;
+  // a given logits tile (the scorer's student logits, LOGITS; a cached dense
+  // teacher, TLOGITS): unpacked to fp32 (128-token tiles), or kept packed and
+  // unpacked at each use (256-token tiles, beside 128 accumulator registers)
+  constexpr bool kPacked = kGiven && kGivenRegs && G::kTT > 128;
+  constexpr bool kPackedZ = kPacked && MODE == MODE_LOGITS;
+  constexpr bool kPackedT = kPacked && MODE == MODE_TLOGITS;
   Acc zl;
-  GivenRawT<NBT> zraw;
+  GivenRawT<NBT> zraw;  // the packed given tile (student or teacher)
 
   // the tile's share of the cooperative prefetch (grouped order: token tiles
   // tt % 8 and vocabulary tiles slice % 4 run side by side)
@@ -513,7 +515,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
-    if constexpr (kGivenRegs) {
+    if constexpr (kPackedT) {  // the teacher tile is loaded in the epilogue, half at a time
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    } else if constexpr (kGivenRegs) {
       GivenRawT<NBT> raw;
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
@@ -574,12 +578,15 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     if constexpr (kPackedZ) return view(zraw);
     else return view(z_acc);
   }();
-  const auto tl = view(tl_acc);
+  const auto tl = [&]() {
+    if constexpr (kPackedT) return view(zraw);
+    else return view(tl_acc);
+  }();
   constexpr bool kTeacher = MODE != MODE_TOPK;
   constexpr bool kInfT = MODE == MODE_TLOGITS;  // given teacher logits may be -inf
   constexpr int kSums = 6;  // sz1, szT, stT, a (top-K: sum p z[idx]), st1, ar
   static_assert(G::kWM * 2 * NBT * (2 + kSums) * 16 * 4 <= kLdsMain, "epilogue exchange fits the LDS");
-  constexpr int kNBX = kPackedZ ? NBT / 2 : NBT;                  // token blocks per exchange
+  constexpr int kNBX = kPacked ? NBT / 2 : NBT;                   // token blocks per exchange
   float* xmax = reinterpret_cast<float*>(lds);                    // [kWM][2][kNBX][2][16]
   float* xsum = xmax + G::kWM * 2 * kNBX * 2 * 16;                // [kWM][2][kNBX][kSums][16]
   const int rb = acc_row(wm, 0, 0, lane);  // this lane's rows: v0 + rb + 16 mb + r
@@ -588,12 +595,12 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   // 256-token tiles with packed given logits run the epilogue in two halves of
   // token blocks, each loading its half of the given tile just before it, so
   // only half of it is held beside the teacher accumulators.
-  constexpr int kHalves = kPackedZ ? 2 : 1;
+  constexpr int kHalves = kPacked ? 2 : 1;
   constexpr int NBH = NBT / kHalves;
   auto half = [&](auto h_tag) {
   constexpr int h = decltype(h_tag)::value;  // compile-time, so every register index is too
-  if constexpr (kPackedZ) {
-    const T* L = static_cast<const T*>(a.logits);
+  if constexpr (kPacked) {
+    const T* L = static_cast<const T*>(kPackedZ ? a.logits : a.tlogits);
     given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, zraw,
                       h * NBH, NBH);
   }
@@ -1564,6 +1571,9 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
 
   f32x4 acc[NB][kMB][NBT];
   f32x4 tacc[1][kMB][NBT];
+  // a given teacher tile on 256-token tiles: kept packed (unpacked at each use)
+  constexpr bool kPackedT = kGivenRegs && G::kTT > 128;
+  GivenRawT<NBT> traw;
   // the tile's share of the cooperative prefetch (grouped order)
   const PipePrefetch pf{kPf ? 1 : 0, tt % 8, vt % 4, lds + (kKept ? 0 : kMainBytes)};
   if constexpr (kKept) {
@@ -1571,7 +1581,9 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     // teacher tile is loaded here as in the recomputing tiles
     if constexpr (MODE == MODE_TLOGITS) {
       const T* L = static_cast<const T*>(a.tlogits);
-      if constexpr (kGivenRegs) {
+      if constexpr (kPackedT) {
+        given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, traw);
+      } else if constexpr (kGivenRegs) {
         GivenRawT<NBT> raw;
         given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
         given_raw_unpack<NBT>(raw, tacc[0]);
@@ -1590,7 +1602,11 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
-    if constexpr (kGivenRegs) {
+    if constexpr (kPackedT) {
+      // 256-token tiles: the teacher tile, still packed, after the main loop
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, traw);
+    } else if constexpr (kGivenRegs) {
       GivenRawT<NBT> raw;
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
@@ -1607,7 +1623,11 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
   }
   const Acc& z = acc[0];  // MODE_TCE: the teacher logits
-  const Acc& tl = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const Acc& tl_acc = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
+  const auto tl = [&]() {
+    if constexpr (kPackedT) return view(traw);
+    else return view(tl_acc);
+  }();
 
   const float* hdr = a.saved + 4 * a.n;
   const float den = hdr[0];
@@ -1709,7 +1729,7 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
           dv = cs * (p1 - (yl == k ? 1.f : 0.f));
           float tt;
           if constexpr (kKeptT) tt = tk[mb][r];
-          else tt = tl[mb][nb][r];
+          else tt = tl(mb, nb, r);
           const float pt = exp2_fast(fmaf(tt, a.cTt, -LtT));
           dv = fmaf(ckf, pz - pt, dv);
           if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(fmaf(tt, -a.rho, zz), invT, rev0), dv);
@@ -2214,7 +2234,10 @@ kd_status forward_t(const Plan& p, const Tensors& x, const kd_outputs* out, void
             fwd_tiles_kernel<T, MODE_TOPK, std::conditional_t<G::kPipe, GeoWide, G>>
                 <<<fgrid, G::kThreads, 0, stream>>>(fa);
             break;
-          case MODE_TLOGITS: fwd_tiles_kernel<T, MODE_TLOGITS, G><<<fgrid, G::kThreads, 0, stream>>>(fa); break;
+          case MODE_TLOGITS:
+            fwd_tiles_kernel<T, MODE_TLOGITS, std::conditional_t<G::kPipe, GeoWide, G>>
+                <<<fgrid, G::kThreads, 0, stream>>>(fa);
+            break;
           default:  // one B operand: the 256-token tiles in the pipelined geometry
             fwd_tiles_kernel<T, MODE_LOGITS, std::conditional_t<G::kPipe, GeoWide, G>>
                 <<<fgrid, G::kThreads, 0, stream>>>(fa);
@@ -2356,7 +2379,10 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         case MODE_TCE: bwd_dz_kernel<T, MODE_TCE, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_TIED: bwd_dz_kernel<T, MODE_TIED, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
         case MODE_SEPARATE: bwd_dz_kernel<T, MODE_SEPARATE, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
-        case MODE_TLOGITS: bwd_dz_kernel<T, MODE_TLOGITS, G, K><<<grid, G::kThreads, 0, stream>>>(ba); break;
+        case MODE_TLOGITS:
+          bwd_dz_kernel<T, MODE_TLOGITS, std::conditional_t<G::kPipe, GeoWide, G>, K>
+              <<<grid, G::kThreads, 0, stream>>>(ba);
+          break;
         default:
           bwd_dz_kernel<T, MODE_TOPK, std::conditional_t<G::kPipe, GeoWide, G>, K>
               <<<grid, G::kThreads, 0, stream>>>(ba);
@@ -2503,7 +2529,8 @@ static_assert(kPipeK == kPipeBK, "K step of the pipelined path");
 static_assert(GeoWide::kVT == GeoFused::kVT, "one vocabulary tile for every pipelined mode");
 int pipe_vocab_rows() { return GeoFused::kVT; }
 int fused_token_rows(int mode, int pipe) {
-  return (pipe && (mode == MODE_TOPK || mode == MODE_LOGITS)) ? GeoWide::kTT : GeoFused::kTT;
+  const bool one_b = mode == MODE_TOPK || mode == MODE_LOGITS || mode == MODE_TLOGITS;
+  return (pipe && one_b) ? GeoWide::kTT : GeoFused::kTT;
 }
 
 kd_status run_forward(const Plan& p, const Tensors& x, const kd_outputs* out, void* saved,
