@@ -1924,6 +1924,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
     }
 }
 
+// Tiles of one kind a GEMM launch needs before its tiles prefetch: 32 per XCD,
+// so that each XCD runs 4 x 8 of them side by side.
+constexpr int kGemmPfTiles = 32 * kXcds;
+
 // Pipelined bf16 GEMM: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output, tile
 // 256 x BN, 8 waves, two slots. A / B are K-contiguous or row-contiguous; K is
 // a multiple of 64 and both operands are zero (or read as zero) past their
@@ -1954,14 +1958,21 @@ __device__ __forceinline__ void gemm_pipe_bounds(const GemmPipeArgs<AKC, BKC, BN
 }
 
 // Output tile (mt, nt) of the pipelined GEMM.
-template <bool AKC, bool BKC, int BN>
+// PF: cooperative L2 prefetch. Launches with at least 32 tiles of a kind per
+// XCD run 4 row tiles x 8 column tiles of it side by side (grouped order), so
+// the tile takes prefetch shares nt % 8 of its A lines and mt % 4 of its B
+// lines, with 1 KB of LDS past the slots for the reads to land in. (With fewer
+// tiles the shares would not match what runs together; those launches do not
+// prefetch.)
+template <bool AKC, bool BKC, int BN, bool PF>
 __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>& a, int mt, int nt,
                                                int64_t M, int64_t K, uint8_t* lds, int tid) {
   using C = PipeCfg<256, BN, 1, AKC, BKC>;
   const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
   f32x4 acc[1][C::MB][C::NBK];
-  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid);
+  const PipePrefetch pf{PF ? 1 : 0, nt % 8, mt % 4, lds + C::kLdsBytes};
+  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid, pf);
   // output row of each of this lane's MB x 4 accumulator rows
   int64_t orow[C::MB][4];
 #pragma unroll
@@ -1985,10 +1996,10 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>&
     }
 }
 
-template <bool AKC, bool BKC, int BN>
+template <bool AKC, bool BKC, int BN, bool PF>
 __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC, BN> a) {
   using C = PipeCfg<256, BN, 1, AKC, BKC>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes + (PF ? 1024 : 0)];
   int64_t M, K;
   int n_mt;
   gemm_pipe_bounds(a, M, K, n_mt);
@@ -1996,7 +2007,7 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
   if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
   int mt, nt;
   grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
-  gemm_pipe_tile(a, mt, nt, M, K, lds, threadIdx.x);
+  gemm_pipe_tile<AKC, BKC, BN, PF>(a, mt, nt, M, K, lds, threadIdx.x);
 }
 
 // dH and dW of one chunk in one launch, both from the dz slab with 256 x 256
@@ -2005,13 +2016,13 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
 // tiles it needs no second wave: each XCD takes its share of dH tiles first
 // (the longer ones, K = chunk) and then its share of dW tiles (K = N), so while
 // half of an XCD's CUs run one dH tile the other half run two dW tiles.
-template <int BN>
+template <int BN, bool PF>
 __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, false, BN> h,
                                                            GemmPipeArgs<false, false, BN> g) {
   using CH = PipeCfg<256, BN, 1, true, false>;
   using CW = PipeCfg<256, BN, 1, false, false>;
   static_assert(CH::kLdsBytes == CW::kLdsBytes, "one LDS image serves both");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[CH::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CH::kLdsBytes + (PF ? 1024 : 0)];
   int64_t mh, kh, mw, kw;
   int nmt_h, nmt_w;
   gemm_pipe_bounds(h, mh, kh, nmt_h);
@@ -2023,10 +2034,10 @@ __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, fa
   int mt, nt;
   if (local < qa) {
     grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + local, nmt_h, h.n_nt, 8, mt, nt);
-    gemm_pipe_tile(h, mt, nt, mh, kh, lds, threadIdx.x);
+    gemm_pipe_tile<true, false, BN, PF>(h, mt, nt, mh, kh, lds, threadIdx.x);
   } else if (local - qa < qb) {
     grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + (local - qa), nmt_w, g.n_nt, 8, mt, nt);
-    gemm_pipe_tile(g, mt, nt, mw, kw, lds, threadIdx.x);
+    gemm_pipe_tile<false, false, BN, PF>(g, mt, nt, mw, kw, lds, threadIdx.x);
   }
 }
 
@@ -2452,22 +2463,32 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         int most = 0;
         for (int xc = 0; xc < kXcds; ++xc)
           most = std::max(most, na / kXcds + (xc < na % kXcds) + nb / kXcds + (xc < nb % kXcds));
+        const bool pf = std::min(na, nb) >= kGemmPfTiles;
         KD_TRY(L.run(KD_KERNEL_GEMM_DWDH, [&] {
-          gemm_dual_kernel<256><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
+          if (pf) gemm_dual_kernel<256, true><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
+          else gemm_dual_kernel<256, false><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
         }));
       } else {
         // 256-wide tiles when they still give every CU a tile, else 128-wide.
         auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((gd + 255) / 256) >= 256; };
-        auto run = [&](int kind, auto args, auto kern) {
-          return L.run(kind, [&] { kern<<<dim3((unsigned)(args.n_mt * args.n_nt)), 512, 0, stream>>>(args); });
+        auto run = [&](int kind, auto args, auto kern, auto kern_pf) {
+          const unsigned tiles = (unsigned)(args.n_mt * args.n_nt);
+          return L.run(kind, [&] {
+            if (tiles >= (unsigned)kGemmPfTiles) kern_pf<<<dim3(tiles), 512, 0, stream>>>(args);
+            else kern<<<dim3(tiles), 512, 0, stream>>>(args);
+          });
         };
         if (dw) {
-          KD_TRY(wide(cw) ? run(KD_KERNEL_GEMM_DW, dw_args(W256{}), gemm_pipe_kernel<false, false, 256>)
-                          : run(KD_KERNEL_GEMM_DW, dw_args(W128{}), gemm_pipe_kernel<false, false, 128>));
+          KD_TRY(wide(cw) ? run(KD_KERNEL_GEMM_DW, dw_args(W256{}), gemm_pipe_kernel<false, false, 256, false>,
+                                gemm_pipe_kernel<false, false, 256, true>)
+                          : run(KD_KERNEL_GEMM_DW, dw_args(W128{}), gemm_pipe_kernel<false, false, 128, false>,
+                                gemm_pipe_kernel<false, false, 128, true>));
         }
         if (dh) {
-          KD_TRY(wide(p.n) ? run(KD_KERNEL_GEMM_DH, dh_args(W256{}), gemm_pipe_kernel<true, false, 256>)
-                           : run(KD_KERNEL_GEMM_DH, dh_args(W128{}), gemm_pipe_kernel<true, false, 128>));
+          KD_TRY(wide(p.n) ? run(KD_KERNEL_GEMM_DH, dh_args(W256{}), gemm_pipe_kernel<true, false, 256, false>,
+                                 gemm_pipe_kernel<true, false, 256, true>)
+                           : run(KD_KERNEL_GEMM_DH, dh_args(W128{}), gemm_pipe_kernel<true, false, 128, false>,
+                                 gemm_pipe_kernel<true, false, 128, true>));
         }
       }
     } else {

@@ -363,6 +363,25 @@ struct PipePrefetch {
   uint8_t* dump;  // 1 KB of LDS that the prefetch reads land in (never read)
 };
 
+// Prefetch lines of a row-contiguous tile (R columns, R / 64 lines per k-row)
+// read by `sharers` tiles side by side: share s takes 64 / sharers of the 64
+// k-rows of every K step, half per wave (`half` 0 or 1); the other lanes repeat
+// those lines. Left off (on stays false) when the operand spans 4 GiB or more,
+// where the per-step offsets would not fit 32 bits.
+template <int R>
+__device__ __forceinline__ void mn_prefetch_lines(const TileSrc<false, R>& s, int sharers, int share, int half,
+                                                  int lane, rsrc_t& r, uint32_t& voff, uint32_t& step_bytes,
+                                                  bool& on) {
+  constexpr int kLines = R / 64;
+  const int kper = 64 / sharers / 2;  // k-rows per wave
+  if (s.kdim * s.ld * 2 >= 0xffffffffll) return;
+  r = make_rsrc(s.base, (s.kdim * s.ld - s.row0) * 2);
+  const int kr = share * 2 * kper + half * kper + (lane / kLines) % kper;
+  voff = (uint32_t)kr * (uint32_t)(s.ld * 2) + (uint32_t)(lane % kLines) * 128u;
+  step_bytes = (uint32_t)(kPipeBK * s.ld * 2);
+  on = true;
+}
+
 // acc[g] = A[a_row0 : +BM, 0:K] * B[g][b_row0 : +BN, 0:K]^T, K a multiple of 64.
 // Ends with a full barrier, so the caller may reuse `lds` right after. With a
 // prefetch share (K-contiguous operands, two B operands of 128 rows) group B
@@ -413,37 +432,45 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     sa.init(A, a_row0, lane);
 #pragma unroll
     for (int g = 0; g < NB; ++g) sb[g].init(B[g], b_row0, lane);
-    // This wave's prefetch lines: waves 0-1 16 A rows each, waves 2-3 NB 16 B
-    // rows each (within one B operand); the other lanes repeat those lines (a
-    // repeated line in one read costs nothing more). Rows past the operand
+    // This wave's prefetch lines: waves 0-1 take the A operand's share (read by
+    // the 8 tiles along B), waves 2-3 the B operands' share (read by the 4
+    // tiles along A), half each. K-contiguous rows are one line per K step;
+    // row-contiguous tiles are k-rows of R / 64 lines. Lines past the operand
     // read out of range (nothing).
     bool pf_on = false;
     rsrc_t pf_r = make_rsrc(nullptr, 0);  // no records: reads nothing
-    uint32_t pf_voff = 0;
+    uint32_t pf_voff = 0, pf_step = kPipeBK * 2;
     constexpr int kRowsB = C::kBBytes / 128;  // rows of one B operand
-    if constexpr (C::kAKC && C::kBKC && (NB * kRowsB == 128 || NB * kRowsB == 256)) {
-      // NB x kRowsB B rows in all (one operand of 128 or 256, or two of 128):
-      // each of the 4 vocabulary tiles of the group prefetches a quarter of
-      // them, half per wave
+    constexpr bool kPfB = C::kBKC ? (NB * kRowsB == 128 || NB * kRowsB == 256) : NB == 1;
+    if constexpr (kPfB) {
       if (pf.on) {
-        pf_on = true;
-        pf_r = sa.rsrc;
         if (gw < 2) {
-          pf_voff = (uint32_t)(pf.a_share * 32 + gw * 16 + (lane & 15)) * sa.stride;
-        } else {
+          if constexpr (C::kAKC) {
+            pf_on = true;
+            pf_r = sa.rsrc;
+            pf_voff = (uint32_t)(pf.a_share * 32 + gw * 16 + (lane & 15)) * sa.stride;
+          } else {
+            mn_prefetch_lines(sa, 8, pf.a_share, gw, lane, pf_r, pf_voff, pf_step, pf_on);
+          }
+        } else if constexpr (C::kBKC) {
+          // NB x kRowsB B rows in all (one operand of 128 or 256, or two of
+          // 128): each of the 4 tiles along A prefetches a quarter of them
+          pf_on = true;
           constexpr int kHalf = NB * kRowsB / 8;  // B rows per wave
           const int first = pf.b_share * 2 * kHalf + (gw - 2) * kHalf;  // of the NB x kRowsB B rows
           // (a branch, not an index: an indexed sb would live in scratch)
           const TileSrc<C::kBKC, kRowsB>& src = (first >= kRowsB) ? sb[NB - 1] : sb[0];
           pf_r = src.rsrc;
           pf_voff = (uint32_t)((first % kRowsB) + (lane & (kHalf - 1))) * src.stride;
+        } else {
+          mn_prefetch_lines(sb[0], 4, pf.b_share, gw - 2, lane, pf_r, pf_voff, pf_step, pf_on);
         }
       }
     }
     // the lines of K step `step` if it exists; true if a read was issued
     auto prefetch = [&](int step) -> bool {
       if (!pf_on || step >= nk) return false;
-      buffer_copy(pf_r, pf.dump, pf_voff, (uint32_t)step * (uint32_t)(kPipeBK * 2));
+      buffer_copy(pf_r, pf.dump, pf_voff, (uint32_t)step * pf_step);
       return true;
     };
     bool pf_last = false;  // the youngest vector memory operation is a prefetch

@@ -29,7 +29,7 @@ CASES = {
     "tied_compact": (C2.scaled(n=300, d=512, v=3000, ignore_frac=0.3, compact_valid=True), 768),
     "separate_T2": (C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=2.0,
                               ignore_frac=0.1), 512),
-    "dense_teacher_logits": (C6.scaled(n=200, d=256, v=2000), 512),
+    "dense_teacher_logits": (C6.scaled(n=300, d=256, v=2000), 512),
     "dense_teacher_logits_staged": (C6.scaled(n=130, d=136, v=1029), 256),
     "topk": (C4.scaled(n=300, d=512, v=5000), 1024),
     "topk_staged": (C4.scaled(n=129, d=264, v=1031, k=7), 256),

@@ -62,7 +62,7 @@ CHUNKED_FORWARD = {
     "separate_T2": (C3.scaled(n=200, d=256, d_t=512, v=2000, temperature=2.0), 512),
     "tied_compact": (C2.scaled(n=300, d=512, v=3000, ignore_frac=0.3, compact_valid=True), 768),
     "tied_jeffreys": (C2.scaled(n=260, d=256, v=2100, kl_divergence="jeffreys"), 512),
-    "dense_teacher_logits": (C6.scaled(n=200, d=256, v=2000), 512),
+    "dense_teacher_logits": (C6.scaled(n=300, d=256, v=2000), 512),
 }
 
 
