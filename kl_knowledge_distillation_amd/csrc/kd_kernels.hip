@@ -1971,7 +1971,7 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>&
   const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
   f32x4 acc[1][C::MB][C::NBK];
-  const PipePrefetch pf{PF ? 1 : 0, nt % 8, mt % 4, lds + C::kLdsBytes};
+  const PipePrefetch pf{(PF && kPipeAhead > 0) ? 1 : 0, nt % 8, mt % 4, lds + C::kLdsBytes};
   pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid, pf);
   // output row of each of this lane's MB x 4 accumulator rows
   int64_t orow[C::MB][4];

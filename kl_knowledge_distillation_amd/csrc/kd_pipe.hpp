@@ -198,7 +198,11 @@ struct PipeCfg {
   static constexpr int kAPer = kABytes / 1024 / 4, kBPer = kBBytes / 1024 / 4;
   static constexpr int kCopies = kAPer + NB * kBPer;
   static constexpr int kMfma = 2 * NB * MB * NBK;  // per wave per step
-  static constexpr int kIL = (kMfma / 2) / kCopies > 0 ? (kMfma / 2) / kCopies : 1;
+  // MFMAs per copy: the copies spread evenly over the whole MFMA phase. Four
+  // waves each issuing 1 KB per kIL MFMAs (16 cycles each) ask for 64 B/clk
+  // per CU at kIL = 4, the rate the L2 delivers to a CU; issued faster, they
+  // queue and stall the MFMAs behind them.
+  static constexpr int kIL = kMfma / kCopies > 0 ? kMfma / kCopies : 1;
   static_assert(BM % 256 == 0 && BN % 128 == 0, "copies must split evenly over 4 waves");
   static_assert(kCopies * kIL <= kMfma, "copies must fit between the MFMAs");
   static_assert(kCopies < 64, "vmcnt range");
