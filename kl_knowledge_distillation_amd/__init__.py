@@ -10,7 +10,7 @@ from __future__ import annotations
 __all__ = [
     "distillation_loss", "flash_ce_kd_loss", "DistillationLossOutput", "Runner", "Tracer",
     "TiedTeacher", "SeparateTeacher", "PrecomputedTeacher", "TopKTeacher",
-    "DistillationLoss", "is_available", "lib",
+    "DistillationLoss", "KDLoss", "is_available", "lib",
 ]
 
 
