@@ -1629,6 +1629,9 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     else return view(tl_acc);
   }();
 
+  // Pipelined bf16 tiles stage the dz tile in the (free) LDS and write whole
+  // token rows of it (512 contiguous bytes) instead of 32-byte pieces.
+  constexpr bool kStage = G::kPipe && !kKept && std::is_same<T, bf16_t>::value;
   const float* hdr = a.saved + 4 * a.n;
   const float den = hdr[0];
   const float g = a.grad ? *a.grad : 1.f;
@@ -1749,7 +1752,18 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
       if constexpr (kKept) {
         if (!kept_ok) o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
       }
-      store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
+      if constexpr (kStage) {
+        // into the LDS image of the tile: token-major rows of 256 bf16, the
+        // 16-byte chunk index XOR-ed with the token's low bits
+        const int tl = (int)(tok - t0);
+        const int vl = rb + 16 * mb;
+        uint2 u;
+        u.x = bf16x2_rne(o[0], o[1]);
+        u.y = bf16x2_rne(o[2], o[3]);
+        *reinterpret_cast<uint2*>(lds + tl * 512 + (((vl >> 3) ^ (tl & 31)) << 4) + (vl & 7) * 2) = u;
+      } else {
+        store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
+      }
     }
   }
   };
@@ -1760,6 +1774,19 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   } else {
     if (kStudentKl && a.kl != KD_KL_FORWARD) epilogue(std::true_type{}, std::false_type{});
     else epilogue(std::false_type{}, std::false_type{});
+  }
+  if constexpr (kStage) {
+    static_assert(G::kTT * 512 <= kMainBytes, "the dz tile fits the main loop's LDS");
+    __syncthreads();
+    // two token rows per instruction: lanes 0-31 row tl, lanes 32-63 row tl + 1
+    const int c = lane & 31;
+#pragma unroll 4
+    for (int pr = 2 * w; pr < G::kTT; pr += 2 * (G::kThreads / 64)) {
+      const int tl = pr + (lane >> 5);
+      const int64_t tok = t0 + tl;
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + tl * 512 + ((c ^ (tl & 31)) << 4));
+      if (tok < a.dz_rows) *reinterpret_cast<uint4*>(dz + tok * a.ldz + (v0 - a.c0) + c * 8) = v;
+    }
   }
 }
 
