@@ -249,7 +249,7 @@ struct GeoStaged {
   __device__ static int col(int wn, int nb, int lane) { return acc_col(wn, nb, lane); }
 };
 // Pipelined: 256 vocabulary rows x TT tokens, 8 waves (4 x 2, two ping-pong
-// groups), two slots of buffer-load copies; bf16 with hidden sizes multiple of
+// groups), buffer-load copies into 3 + 2 LDS slots; bf16 with hidden sizes multiple of
 // 64. TT = 128 for two B operands (tied teacher) and for the tiles that hold a
 // given logits tile in registers; TT = 256 for one B operand (top-K), which
 // halves the operand bytes copied per MFMA against 256 x 128.
@@ -267,20 +267,18 @@ using GeoFused = GeoPipe;
 static_assert(GeoPipe::kNB == kNB, "the 128-token tiles keep the staged block layout");
 
 // acc[g] = A[a_row0 : +VT, 0:K] * B_g[b_row0 : +TT, 0:K]^T for K-contiguous operands.
-// pf: the cooperative prefetch share of this tile (pipelined, two B operands).
 template <typename T, class G, int NB>
 __device__ __forceinline__ void tile_product(const T* a, int64_t lda, int64_t arows,
                                              const T* const (&b)[NB], int64_t ldb, int64_t brows,
                                              int64_t a_row0, int64_t b_row0, int64_t K,
-                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][G::kNB], int tid,
-                                             PipePrefetch pf = PipePrefetch{0, 0, 0, nullptr}) {
+                                             uint8_t* lds, f32x4 (&acc)[NB][kMB][G::kNB], int tid) {
   if constexpr (G::kPipe) {
     static_assert(sizeof(T) == 2, "the pipelined geometry is bf16 only");
     const PipeOperand A{a, lda, arows};
     PipeOperand B[NB];
 #pragma unroll
     for (int g = 0; g < NB; ++g) B[g] = PipeOperand{b[g], ldb, brows};
-    pipe_mainloop<typename G::template Cfg<NB>, NB>(A, B, a_row0, b_row0, K, lds, acc, tid, pf);
+    pipe_mainloop<typename G::template Cfg<NB>, NB>(A, B, a_row0, b_row0, K, lds, acc, tid);
   } else {
     const Operand<T, true> A{a, lda, arows, K};
     Operand<T, true> B[NB];
@@ -369,11 +367,10 @@ __device__ __forceinline__ void load_logits_tile(const T* L, int64_t n, int64_t 
 // Given bf16 logits kept in registers across the main loop (pipelined
 // geometry): every wave loads its own part of the tile, still packed (two
 // bf16 per register), before the main loop, so the loads land under the
-// MFMAs and the LDS stays free for the copy slots and the prefetch. `vec`: v a
-// multiple of 4 and the matrix 8-byte aligned (one 8-byte load per lane and
-// block); otherwise element loads. Tokens past n and rows past v read 0.
-// (Staging the tile through LDS with buffer loads instead left no LDS for the
-// cooperative prefetch and measured 2-4% slower.)
+// MFMAs and the LDS stays free for the copy slots. `vec`: v a multiple of 4
+// and the matrix 8-byte aligned (one 8-byte load per lane and block);
+// otherwise element loads. Tokens past n and rows past v read 0. (Staging the
+// tile through LDS with buffer loads instead measured 2-4% slower.)
 template <int NBT>
 using GivenRawT = uint2[kMB][NBT];
 typedef GivenRawT<kNB> GivenRaw;
@@ -465,11 +462,9 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   using Acc = f32x4[kMB][NBT];
   constexpr bool kGiven = MODE == MODE_TLOGITS || MODE == MODE_LOGITS;  // one logits tile is given
   constexpr int kMainBytes = G::template lds_bytes<NB>();
-  // pipelined tiles: 1 KB past the slots where the prefetch reads land; a
-  // given logits tile is held in registers
+  // pipelined tiles hold a given logits tile in registers
   constexpr bool kGivenRegs = kGiven && G::kPipe;
-  constexpr bool kPf = G::kPipe && kPipeAhead > 0;
-  constexpr int kLdsMain = kMainBytes + (kPf ? 1024 : 0);
+  constexpr int kLdsMain = kMainBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsMain];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: only the token tiles below nv have work; they are mapped
@@ -498,29 +493,26 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   Acc zl;
   GivenRawT<NBT> zraw;  // the packed given tile (student or teacher)
 
-  // the tile's share of the cooperative prefetch (grouped order: token tiles
-  // tt % 8 and vocabulary tiles slice % 4 run side by side)
-  const PipePrefetch pf{kPf ? 1 : 0, tt % 8, slice % 4, lds + kMainBytes};
   if constexpr (MODE == MODE_TIED) {
     const T* const b[2] = {hs, ht};
-    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   } else if constexpr (MODE == MODE_SEPARATE) {
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
   } else if constexpr (MODE == MODE_TOPK) {
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
     if constexpr (kPackedT) {  // the teacher tile is loaded in the epilogue, half at a time
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     } else if constexpr (kGivenRegs) {
       GivenRawT<NBT> raw;
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_raw_unpack<NBT>(raw, tacc[0]);
     } else {
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
@@ -533,11 +525,11 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       // 256-token tiles: the given tile (64 registers) would not fit beside the
       // main loop's; it is loaded once the loop is done (its latency is a few
       // percent of the tile's)
-      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
     } else if constexpr (kGivenRegs) {
       GivenRawT<NBT> raw;
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
+      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
       given_raw_unpack<NBT>(raw, zl);
     } else {
       tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
@@ -1539,9 +1531,8 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   constexpr bool kGiven = MODE == MODE_TLOGITS;
   constexpr int kMainBytes = G::template lds_bytes<NB>();
   constexpr bool kGivenRegs = kGiven && G::kPipe;  // a given logits tile in registers
-  constexpr bool kPf = G::kPipe && kPipeAhead > 0 && !kKept;  // prefetch reads: 1 KB
   constexpr bool kKeptT = kKept && (MODE == MODE_TIED || MODE == MODE_SEPARATE);  // teacher's kept too
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kKept ? 16 : kMainBytes + (kPf ? 1024 : 0)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kKept ? 16 : kMainBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   // Compacted rows: token tiles from round_up(nv, 128) on would hold only zero
   // rows, which no GEMM reads (their K and M stop at nv); only the tiles below
@@ -1574,8 +1565,6 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   // a given teacher tile on 256-token tiles: kept packed (unpacked at each use)
   constexpr bool kPackedT = kGivenRegs && G::kTT > 128;
   GivenRawT<NBT> traw;
-  // the tile's share of the cooperative prefetch (grouped order)
-  const PipePrefetch pf{kPf ? 1 : 0, tt % 8, vt % 4, lds + (kKept ? 0 : kMainBytes)};
   if constexpr (kKept) {
     // the kept products are read per token block in the epilogue; a given
     // teacher tile is loaded here as in the recomputing tiles
@@ -1593,23 +1582,23 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     }
   } else if constexpr (MODE == MODE_TIED) {
     const T* const b[2] = {hs, ht};
-    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    tile_product<T, G, 2>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   } else if constexpr (MODE == MODE_SEPARATE) {
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid, pf);
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
   } else if constexpr (MODE == MODE_TLOGITS) {
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
     if constexpr (kPackedT) {
       // 256-token tiles: the teacher tile, still packed, after the main loop
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, traw);
     } else if constexpr (kGivenRegs) {
       GivenRawT<NBT> raw;
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_raw_unpack<NBT>(raw, tacc[0]);
     } else {
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
@@ -1617,10 +1606,10 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     }
   } else if constexpr (MODE == MODE_TCE) {  // the teacher tile alone
     const T* const bt[1] = {ht};
-    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, acc, tid, pf);
+    tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, acc, tid);
   } else {  // MODE_TOPK
     const T* const b[1] = {hs};
-    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid, pf);
+    tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
   }
   const Acc& z = acc[0];  // MODE_TCE: the teacher logits
   const Acc& tl_acc = (MODE == MODE_TIED) ? acc[NB - 1] : tacc[0];
@@ -1951,12 +1940,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
     }
 }
 
-// Tiles of one kind a GEMM launch needs before its tiles prefetch: 32 per XCD,
-// so that each XCD runs 4 x 8 of them side by side.
-constexpr int kGemmPfTiles = 32 * kXcds;
-
 // Pipelined bf16 GEMM: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output, tile
-// 256 x BN, 8 waves, two slots. A / B are K-contiguous or row-contiguous; K is
+// 256 x BN, 8 waves, 3 + 2 slots. A / B are K-contiguous or row-contiguous; K is
 // a multiple of 64 and both operands are zero (or read as zero) past their
 // own K extent.
 template <bool AKC, bool BKC, int BN>
@@ -1985,21 +1970,14 @@ __device__ __forceinline__ void gemm_pipe_bounds(const GemmPipeArgs<AKC, BKC, BN
 }
 
 // Output tile (mt, nt) of the pipelined GEMM.
-// PF: cooperative L2 prefetch. Launches with at least 32 tiles of a kind per
-// XCD run 4 row tiles x 8 column tiles of it side by side (grouped order), so
-// the tile takes prefetch shares nt % 8 of its A lines and mt % 4 of its B
-// lines, with 1 KB of LDS past the slots for the reads to land in. (With fewer
-// tiles the shares would not match what runs together; those launches do not
-// prefetch.)
-template <bool AKC, bool BKC, int BN, bool PF>
+template <bool AKC, bool BKC, int BN>
 __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>& a, int mt, int nt,
                                                int64_t M, int64_t K, uint8_t* lds, int tid) {
   using C = PipeCfg<256, BN, 1, AKC, BKC>;
   const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int64_t m0 = (int64_t)mt * 256, n0 = (int64_t)nt * BN;
   f32x4 acc[1][C::MB][C::NBK];
-  const PipePrefetch pf{(PF && kPipeAhead > 0) ? 1 : 0, nt % 8, mt % 4, lds + C::kLdsBytes};
-  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid, pf);
+  pipe_mainloop<C, 1>(a.A, &a.B, m0, n0, K, lds, acc, tid);
   // output row of each of this lane's MB x 4 accumulator rows
   int64_t orow[C::MB][4];
 #pragma unroll
@@ -2023,10 +2001,10 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>&
     }
 }
 
-template <bool AKC, bool BKC, int BN, bool PF>
+template <bool AKC, bool BKC, int BN>
 __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC, BN> a) {
   using C = PipeCfg<256, BN, 1, AKC, BKC>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes + (PF ? 1024 : 0)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
   int64_t M, K;
   int n_mt;
   gemm_pipe_bounds(a, M, K, n_mt);
@@ -2034,7 +2012,7 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
   if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
   int mt, nt;
   grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
-  gemm_pipe_tile<AKC, BKC, BN, PF>(a, mt, nt, M, K, lds, threadIdx.x);
+  gemm_pipe_tile<AKC, BKC, BN>(a, mt, nt, M, K, lds, threadIdx.x);
 }
 
 // dH and dW of one chunk in one launch, both from the dz slab with 256 x 256
@@ -2043,13 +2021,13 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
 // tiles it needs no second wave: each XCD takes its share of dH tiles first
 // (the longer ones, K = chunk) and then its share of dW tiles (K = N), so while
 // half of an XCD's CUs run one dH tile the other half run two dW tiles.
-template <int BN, bool PF>
+template <int BN>
 __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, false, BN> h,
                                                            GemmPipeArgs<false, false, BN> g) {
   using CH = PipeCfg<256, BN, 1, true, false>;
   using CW = PipeCfg<256, BN, 1, false, false>;
   static_assert(CH::kLdsBytes == CW::kLdsBytes, "one LDS image serves both");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[CH::kLdsBytes + (PF ? 1024 : 0)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CH::kLdsBytes];
   int64_t mh, kh, mw, kw;
   int nmt_h, nmt_w;
   gemm_pipe_bounds(h, mh, kh, nmt_h);
@@ -2061,10 +2039,10 @@ __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, fa
   int mt, nt;
   if (local < qa) {
     grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + local, nmt_h, h.n_nt, 8, mt, nt);
-    gemm_pipe_tile<true, false, BN, PF>(h, mt, nt, mh, kh, lds, threadIdx.x);
+    gemm_pipe_tile<true, false, BN>(h, mt, nt, mh, kh, lds, threadIdx.x);
   } else if (local - qa < qb) {
     grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + (local - qa), nmt_w, g.n_nt, 8, mt, nt);
-    gemm_pipe_tile<false, false, BN, PF>(g, mt, nt, mw, kw, lds, threadIdx.x);
+    gemm_pipe_tile<false, false, BN>(g, mt, nt, mw, kw, lds, threadIdx.x);
   }
 }
 
@@ -2490,32 +2468,22 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         int most = 0;
         for (int xc = 0; xc < kXcds; ++xc)
           most = std::max(most, na / kXcds + (xc < na % kXcds) + nb / kXcds + (xc < nb % kXcds));
-        const bool pf = std::min(na, nb) >= kGemmPfTiles;
         KD_TRY(L.run(KD_KERNEL_GEMM_DWDH, [&] {
-          if (pf) gemm_dual_kernel<256, true><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
-          else gemm_dual_kernel<256, false><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
+          gemm_dual_kernel<256><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
         }));
       } else {
         // 256-wide tiles when they still give every CU a tile, else 128-wide.
         auto wide = [&](int64_t m) { return ((m + 255) / 256) * ((gd + 255) / 256) >= 256; };
-        auto run = [&](int kind, auto args, auto kern, auto kern_pf) {
-          const unsigned tiles = (unsigned)(args.n_mt * args.n_nt);
-          return L.run(kind, [&] {
-            if (tiles >= (unsigned)kGemmPfTiles) kern_pf<<<dim3(tiles), 512, 0, stream>>>(args);
-            else kern<<<dim3(tiles), 512, 0, stream>>>(args);
-          });
+        auto run = [&](int kind, auto args, auto kern) {
+          return L.run(kind, [&] { kern<<<dim3((unsigned)(args.n_mt * args.n_nt)), 512, 0, stream>>>(args); });
         };
         if (dw) {
-          KD_TRY(wide(cw) ? run(KD_KERNEL_GEMM_DW, dw_args(W256{}), gemm_pipe_kernel<false, false, 256, false>,
-                                gemm_pipe_kernel<false, false, 256, true>)
-                          : run(KD_KERNEL_GEMM_DW, dw_args(W128{}), gemm_pipe_kernel<false, false, 128, false>,
-                                gemm_pipe_kernel<false, false, 128, true>));
+          KD_TRY(wide(cw) ? run(KD_KERNEL_GEMM_DW, dw_args(W256{}), gemm_pipe_kernel<false, false, 256>)
+                          : run(KD_KERNEL_GEMM_DW, dw_args(W128{}), gemm_pipe_kernel<false, false, 128>));
         }
         if (dh) {
-          KD_TRY(wide(p.n) ? run(KD_KERNEL_GEMM_DH, dh_args(W256{}), gemm_pipe_kernel<true, false, 256, false>,
-                                 gemm_pipe_kernel<true, false, 256, true>)
-                           : run(KD_KERNEL_GEMM_DH, dh_args(W128{}), gemm_pipe_kernel<true, false, 128, false>,
-                                 gemm_pipe_kernel<true, false, 128, true>));
+          KD_TRY(wide(p.n) ? run(KD_KERNEL_GEMM_DH, dh_args(W256{}), gemm_pipe_kernel<true, false, 256>)
+                           : run(KD_KERNEL_GEMM_DH, dh_args(W128{}), gemm_pipe_kernel<true, false, 128>));
         }
       }
     } else {

@@ -1,5 +1,6 @@
-// bf16 main loop with buffer loads straight into LDS, two slots, ping-pong
-// scheduling and v_mfma_f32_16x16x32_bf16 (gfx950).
+// bf16 main loop with buffer loads straight into LDS (three A-operand slots,
+// two B-operand slots), ping-pong scheduling and v_mfma_f32_16x16x32_bf16
+// (gfx950).
 //
 // Workgroup: 512 threads = 8 wave64 as 4 (A rows) x 2 (B rows). Output tile
 // BM x BN (A rows x B rows); each wave owns TM x TN = (BM/4) x (BN/2), made of
@@ -31,18 +32,21 @@
 // Row-contiguous tiles (the dW / dH operands) are 64 k-rows of R bf16; their
 // fragments are read with ds_read_b64_tr_b16 (see mn_offset).
 //
-// Schedule (two slots). Waves 0..3 (group A) and 4..7 (group B), one of each
-// per SIMD, run half a step apart:
-//   part 1:  A: MFMAs of step i            B: read fragments of step i
-//   barrier 1 (step i+1 has landed: group B waited for its copies)
-//   part 2:  A: read fragments of step i+1 B: MFMAs of step i, issuing the
-//                                             copies of step i+2 into the slot
-//                                             of step i between them
+// Schedule. Waves 0..3 (group A) and 4..7 (group B), one of each per SIMD, run
+// half a step apart:
+//   part 1:  A: MFMAs of step i, copying    B: read fragments of step i
+//               the A operand of step i+2
+//   barrier 1 (step i+1 has landed: each group waited for its own copies)
+//   part 2:  A: read fragments of step i+1  B: MFMAs of step i, copying the
+//                                              B operands of step i+2
 //   barrier 2
 // While one wave of a SIMD issues MFMAs the other does its LDS reads, so the
-// matrix pipe keeps running across the barriers. The slot of step i is free at
-// barrier 1: group B read it in part 1, group A in part 2 of step i-1. Copies
-// of step i+2 have the rest of part 2 and part 1 of step i+1 to land.
+// matrix pipe keeps running across the barriers. The copies are spread over
+// both parts, each half of them between one group's MFMAs: the rate at which
+// a CU's copies can be served (~64 B/clk) is the loop's limit, and copies
+// bunched in one part stall the MFMAs behind them. Step s has its A operand in
+// A-slot s % 3 and its B operands in B-slot s % 2; the A-slot of step i-1 and
+// the B-slot of step i are free after barrier 1 of those steps.
 #pragma once
 
 #include "kd_device.hpp"
@@ -192,20 +196,17 @@ struct PipeCfg {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int MB = TM / 16, NBK = TN / 16;
   static constexpr int kABytes = BM * 128, kBBytes = BN * 128;
-  static constexpr int kStageBytes = kABytes + NB * kBBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
-  // copy instructions per group-B wave per step: A blocks first, then each B
+  // LDS: three A-operand slots, then two slots of the NB B operands
+  static constexpr int kBBase = 3 * kABytes;
+  static constexpr int kLdsBytes = 3 * kABytes + 2 * NB * kBBytes;
+  // copy instructions per wave and step: group A copies the A operand, group
+  // B the B operands, a quarter each per wave
   static constexpr int kAPer = kABytes / 1024 / 4, kBPer = kBBytes / 1024 / 4;
-  static constexpr int kCopies = kAPer + NB * kBPer;
+  static constexpr int kACopies = kAPer, kBCopies = NB * kBPer;
   static constexpr int kMfma = 2 * NB * MB * NBK;  // per wave per step
-  // MFMAs per copy: the copies spread evenly over the whole MFMA phase. Four
-  // waves each issuing 1 KB per kIL MFMAs (16 cycles each) ask for 64 B/clk
-  // per CU at kIL = 4, the rate the L2 delivers to a CU; issued faster, they
-  // queue and stall the MFMAs behind them.
-  static constexpr int kIL = kMfma / kCopies > 0 ? kMfma / kCopies : 1;
   static_assert(BM % 256 == 0 && BN % 128 == 0, "copies must split evenly over 4 waves");
-  static_assert(kCopies * kIL <= kMfma, "copies must fit between the MFMAs");
-  static_assert(kCopies < 64, "vmcnt range");
+  static_assert(kACopies <= kMfma && kBCopies <= kMfma, "copies must fit between the MFMAs");
+  static_assert(kACopies < 32 && kBCopies < 32, "vmcnt range");
   static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
@@ -274,21 +275,23 @@ struct PipeLanes {
   }
 };
 
+// Fragments of one K step from its A-operand slot and its B-operand slot (the
+// NB B operands one after another).
 template <class C, int NB>
-__device__ __forceinline__ void pipe_read(const uint8_t* stage, PipeFrags<C, NB>& f, const PipeLanes<C>& pl,
-                                          int wm, int wn, int lane) {
+__device__ __forceinline__ void pipe_read(const uint8_t* aslot, const uint8_t* bslot, PipeFrags<C, NB>& f,
+                                          const PipeLanes<C>& pl, int wm, int wn, int lane) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb) {
-      if constexpr (C::kAKC) f.a[kk][mb] = kc_frag(stage, wm * C::TM + mb * 16, kk, lane);
-      else f.a[kk][mb] = mn_frag(stage, pl.a, mb, kk);
+      if constexpr (C::kAKC) f.a[kk][mb] = kc_frag(aslot, wm * C::TM + mb * 16, kk, lane);
+      else f.a[kk][mb] = mn_frag(aslot, pl.a, mb, kk);
     }
 #pragma unroll
     for (int g = 0; g < NB; ++g)
 #pragma unroll
       for (int nb = 0; nb < C::NBK; ++nb) {
-        const uint8_t* tile = stage + C::kABytes + g * C::kBBytes;
+        const uint8_t* tile = bslot + g * C::kBBytes;
         if constexpr (C::kBKC) f.b[kk][g][nb] = kc_frag(tile, wn * C::TN + nb * 16, kk, lane);
         else f.b[kk][g][nb] = mn_frag(tile, pl.b, nb, kk);
       }
@@ -309,11 +312,16 @@ __device__ __forceinline__ void pipe_mma(const PipeFrags<C, NB>& f, f32x4 (&acc)
                                                                    acc[g][mb][nb], 0, 0, 0);
 }
 
-// The same MFMAs with copy(j), j = 0 .. C::kCopies-1, issued after MFMA
-// kIL (j + 1) - 1, in that order (sched_group_barrier keeps the interleave).
-template <class C, int NB, class F>
+// The same MFMAs with copy(j), j = 0 .. N-1, spread evenly: copy j after MFMA
+// IL (j + 1) - 1, IL = kMfma / N (sched_group_barrier keeps the interleave).
+// Four waves each issuing 1 KB per 4 MFMAs (16 cycles each) ask for 64 B/clk
+// per CU, the rate the L2 delivers to a CU; issued faster, copies queue and
+// stall the MFMAs behind them.
+template <class C, int NB, int N, class F>
 __device__ __forceinline__ void pipe_mma_copies(const PipeFrags<C, NB>& f,
                                                 f32x4 (&acc)[NB][C::MB][C::NBK], F&& copy) {
+  constexpr int IL = C::kMfma / N;
+  static_assert(IL >= 1 && N * IL <= C::kMfma, "copies fit between the MFMAs");
   int m = 0;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
@@ -325,78 +333,33 @@ __device__ __forceinline__ void pipe_mma_copies(const PipeFrags<C, NB>& f,
         for (int nb = 0; nb < C::NBK; ++nb) {
           acc[g][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[kk][mb], f.b[kk][g][nb],
                                                                    acc[g][mb][nb], 0, 0, 0);
-          if (m % C::kIL == C::kIL - 1 && m / C::kIL < C::kCopies) copy(m / C::kIL);
+          if (m % IL == IL - 1 && m / IL < N) copy(m / IL);
           ++m;
         }
 #pragma unroll
-  for (int j = 0; j < C::kCopies; ++j) {
-    __builtin_amdgcn_sched_group_barrier(0x008, C::kIL, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // VMEM read
+  for (int j = 0; j < N; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, IL, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, C::kMfma - C::kCopies * C::kIL, 0);
-}
-
-// Copy j of group-B wave gw for the K step at k0 into `stage`: the wave takes a
-// quarter of the A blocks, then a quarter of each B operand's blocks.
-template <class C, int NB, class SA, class SB>
-__device__ __forceinline__ void pipe_copy(const SA& sa, const SB (&sb)[NB], int64_t k0, uint8_t* stage,
-                                          int gw, int j) {
-  if (j < C::kAPer) {
-    sa.issue(k0, stage, gw * C::kAPer + j);
-  } else {
-    const int g = (j - C::kAPer) / C::kBPer, jj = (j - C::kAPer) % C::kBPer;
-    sb[g].issue(k0, stage + C::kABytes + g * C::kBBytes, gw * C::kBPer + jj);
-  }
-}
-
-// Cooperative L2 prefetch of the fused tiles. The 32 tiles an XCD runs at
-// once are 4 vocabulary tiles x 8 token tiles in the grouped order, so each A
-// row (256 per tile) is read by 8 of them and each B row (NB x 128) by 4. Tile
-// (a, b) reads, kPipeAhead K steps early, one 16-byte piece of each 128-byte
-// line of its share: A rows 32 (b % 8) .. + 31 and B rows NB 32 (a % 4) ..
-// + NB 32 - 1, so each line of the group comes into L2 once, before the tiles
-// copy it (measured: fused kernels 3-5% faster at the quickstart shape).
-#ifndef KD_PIPE_AHEAD
-#define KD_PIPE_AHEAD 4
-#endif
-constexpr int kPipeAhead = KD_PIPE_AHEAD;
-struct PipePrefetch {
-  int on;         // 0: no prefetch
-  int a_share;    // 0..7
-  int b_share;    // 0..3
-  uint8_t* dump;  // 1 KB of LDS that the prefetch reads land in (never read)
-};
-
-// Prefetch lines of a row-contiguous tile (R columns, R / 64 lines per k-row)
-// read by `sharers` tiles side by side: share s takes 64 / sharers of the 64
-// k-rows of every K step, half per wave (`half` 0 or 1); the other lanes repeat
-// those lines. Left off (on stays false) when the operand spans 4 GiB or more,
-// where the per-step offsets would not fit 32 bits.
-template <int R>
-__device__ __forceinline__ void mn_prefetch_lines(const TileSrc<false, R>& s, int sharers, int share, int half,
-                                                  int lane, rsrc_t& r, uint32_t& voff, uint32_t& step_bytes,
-                                                  bool& on) {
-  constexpr int kLines = R / 64;
-  const int kper = 64 / sharers / 2;  // k-rows per wave
-  if (s.kdim * s.ld * 2 >= 0xffffffffll) return;
-  r = make_rsrc(s.base, (s.kdim * s.ld - s.row0) * 2);
-  const int kr = share * 2 * kper + half * kper + (lane / kLines) % kper;
-  voff = (uint32_t)kr * (uint32_t)(s.ld * 2) + (uint32_t)(lane % kLines) * 128u;
-  step_bytes = (uint32_t)(kPipeBK * s.ld * 2);
-  on = true;
+  if constexpr (C::kMfma - N * IL > 0) __builtin_amdgcn_sched_group_barrier(0x008, C::kMfma - N * IL, 0);
 }
 
 // acc[g] = A[a_row0 : +BM, 0:K] * B[g][b_row0 : +BN, 0:K]^T, K a multiple of 64.
-// Ends with a full barrier, so the caller may reuse `lds` right after. With a
-// prefetch share (K-contiguous operands, two B operands of 128 rows) group B
-// also reads its share of the lines kPipeAhead steps ahead: one buffer read
-// per wave after a batch of copies (while that step exists); a wait for the
-// copies then leaves that one younger read outstanding.
+// Ends with a full barrier, so the caller may reuse `lds` right after.
+//
+// Step s (64 of K) has its A operand in A-slot s % 3 and its B operands in
+// B-slot s % 2. Group A (waves 0-3) runs its MFMAs of step i while group B
+// reads its fragments of step i; after barrier 1 group B runs its MFMAs while
+// group A reads step i+1; barrier 2 ends the step. Each group copies its own
+// operand, between its own MFMAs of step i, for step i+2: group A into the
+// A-slot of step i-1 (both groups read it before barrier 1 of step i-1), group
+// B into the B-slot of step i (read before barrier 1 of step i). The A operand
+// so leads by 1.5-2 steps, the B operands by 1. Each group waits for its own
+// copies of step i+1 before barrier 1 of step i.
 template <class C, int NB, class OA, class OB>
 __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t a_row0, int64_t b_row0,
                                               int64_t K, uint8_t* lds,
-                                              f32x4 (&acc)[NB][C::MB][C::NBK], int tid,
-                                              PipePrefetch pf = PipePrefetch{0, 0, 0, nullptr}) {
+                                              f32x4 (&acc)[NB][C::MB][C::NBK], int tid) {
   static_assert(C::kWaves == 8, "two groups of four waves");
   // The wave index is the same for all lanes of a wave; readfirstlane makes that
   // visible to the compiler, so the group branches below are scalar branches.
@@ -418,103 +381,85 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
   PipeFrags<C, NB> f;
   PipeLanes<C> pl;
   pl.init(wm, wn, lane);
+  auto aslot = [&](int st) { return lds + (st % 3) * C::kABytes; };
+  auto bslot = [&](int st) { return lds + C::kBBase + (st & 1) * (NB * C::kBBytes); };
+  constexpr int kNA = C::kACopies, kNB = C::kBCopies;
+  // (copy-and-MFMA steps and the last two steps are separate loops: one loop
+  // with a branch between the two MFMA bodies made the compiler spill)
   if (!grp_b) {
-    pipe_barrier();  // pairs with the prologue barrier of group B: step 0 visible
-    pipe_read<C, NB>(lds, f, pl, wm, wn, lane);
-    for (int i = 0; i < nk; ++i) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments of step i ready
-      __builtin_amdgcn_s_setprio(1);
-      pipe_mma<C, NB>(f, acc);
-      __builtin_amdgcn_s_setprio(0);
-      pipe_barrier();  // 1: step i+1 has landed
-      if (i + 1 < nk) pipe_read<C, NB>(lds + ((i + 1) & 1) * C::kStageBytes, f, pl, wm, wn, lane);
-      pipe_barrier();  // 2
-    }
-  } else {
     TileSrc<C::kAKC, C::kABytes / 128> sa;
-    TileSrc<C::kBKC, C::kBBytes / 128> sb[NB];
     sa.init(A, a_row0, lane);
+    auto copy_a = [&](int st, int j) { sa.issue((int64_t)st * kPipeBK, aslot(st), gw * kNA + j); };
+    // Prologue: the A operand of steps 0 and 1; step 0 visible at the first barrier.
 #pragma unroll
-    for (int g = 0; g < NB; ++g) sb[g].init(B[g], b_row0, lane);
-    // This wave's prefetch lines: waves 0-1 take the A operand's share (read by
-    // the 8 tiles along B), waves 2-3 the B operands' share (read by the 4
-    // tiles along A), half each. K-contiguous rows are one line per K step;
-    // row-contiguous tiles are k-rows of R / 64 lines. Lines past the operand
-    // read out of range (nothing).
-    bool pf_on = false;
-    rsrc_t pf_r = make_rsrc(nullptr, 0);  // no records: reads nothing
-    uint32_t pf_voff = 0, pf_step = kPipeBK * 2;
-    constexpr int kRowsB = C::kBBytes / 128;  // rows of one B operand
-    constexpr bool kPfB = C::kBKC ? (NB * kRowsB == 128 || NB * kRowsB == 256) : NB == 1;
-    if constexpr (kPfB) {
-      if (pf.on) {
-        if (gw < 2) {
-          if constexpr (C::kAKC) {
-            pf_on = true;
-            pf_r = sa.rsrc;
-            pf_voff = (uint32_t)(pf.a_share * 32 + gw * 16 + (lane & 15)) * sa.stride;
-          } else {
-            mn_prefetch_lines(sa, 8, pf.a_share, gw, lane, pf_r, pf_voff, pf_step, pf_on);
-          }
-        } else if constexpr (C::kBKC) {
-          // NB x kRowsB B rows in all (one operand of 128 or 256, or two of
-          // 128): each of the 4 tiles along A prefetches a quarter of them
-          pf_on = true;
-          constexpr int kHalf = NB * kRowsB / 8;  // B rows per wave
-          const int first = pf.b_share * 2 * kHalf + (gw - 2) * kHalf;  // of the NB x kRowsB B rows
-          // (a branch, not an index: an indexed sb would live in scratch)
-          const TileSrc<C::kBKC, kRowsB>& src = (first >= kRowsB) ? sb[NB - 1] : sb[0];
-          pf_r = src.rsrc;
-          pf_voff = (uint32_t)((first % kRowsB) + (lane & (kHalf - 1))) * src.stride;
-        } else {
-          mn_prefetch_lines(sb[0], 4, pf.b_share, gw - 2, lane, pf_r, pf_voff, pf_step, pf_on);
-        }
-      }
-    }
-    // the lines of K step `step` if it exists; true if a read was issued
-    auto prefetch = [&](int step) -> bool {
-      if (!pf_on || step >= nk) return false;
-      buffer_copy(pf_r, pf.dump, pf_voff, (uint32_t)step * pf_step);
-      return true;
-    };
-    bool pf_last = false;  // the youngest vector memory operation is a prefetch
-    // Prologue: steps 0 and 1; step 0 visible at the first barrier.
-#pragma unroll
-    for (int j = 0; j < C::kCopies; ++j) pipe_copy<C, NB>(sa, sb, 0, lds, gw, j);
+    for (int j = 0; j < kNA; ++j) copy_a(0, j);
     if (nk > 1) {
 #pragma unroll
-      for (int j = 0; j < C::kCopies; ++j)
-        pipe_copy<C, NB>(sa, sb, kPipeBK, lds + C::kStageBytes, gw, j);
-      pf_last = prefetch(kPipeAhead - 1);
-      if (pf_last) wait_vmcnt<C::kCopies + 1>();
-      else wait_vmcnt<C::kCopies>();
+      for (int j = 0; j < kNA; ++j) copy_a(1, j);
+      wait_vmcnt<kNA>();
     } else {
       wait_vmcnt<0>();
     }
     pipe_barrier();
-    // Steps that still copy step i+2, then the last two without copies: two
-    // branch-free loop bodies.
+    pipe_read<C, NB>(aslot(0), bslot(0), f, pl, wm, wn, lane);
     int i = 0;
     for (; i + 2 < nk; ++i) {
-      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, pl, wm, wn, lane);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments of step i ready
+      __builtin_amdgcn_s_setprio(1);
+      pipe_mma_copies<C, NB, kNA>(f, acc, [&](int j) { copy_a(i + 2, j); });
+      __builtin_amdgcn_s_setprio(0);
+      wait_vmcnt<kNA>();  // the A operand of step i+1 has landed
+      pipe_barrier();     // 1
+      pipe_read<C, NB>(aslot(i + 1), bslot(i + 1), f, pl, wm, wn, lane);
+      pipe_barrier();  // 2
+    }
+    for (; i < nk; ++i) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_setprio(1);
+      pipe_mma<C, NB>(f, acc);
+      __builtin_amdgcn_s_setprio(0);
+      wait_vmcnt<0>();
+      pipe_barrier();  // 1
+      if (i + 1 < nk) pipe_read<C, NB>(aslot(i + 1), bslot(i + 1), f, pl, wm, wn, lane);
+      pipe_barrier();  // 2
+    }
+  } else {
+    TileSrc<C::kBKC, C::kBBytes / 128> sb[NB];
+#pragma unroll
+    for (int g = 0; g < NB; ++g) sb[g].init(B[g], b_row0, lane);
+    auto copy_b = [&](int st, int j) {
+      const int g = j / C::kBPer, jj = j % C::kBPer;
+      uint8_t* dst = bslot(st) + g * C::kBBytes;
+      // (a branch, not an index: an indexed sb would live in scratch)
+      if (g == 0) sb[0].issue((int64_t)st * kPipeBK, dst, gw * C::kBPer + jj);
+      else sb[NB - 1].issue((int64_t)st * kPipeBK, dst, gw * C::kBPer + jj);
+    };
+    // Prologue: the B operands of steps 0 and 1.
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) copy_b(0, j);
+    if (nk > 1) {
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) copy_b(1, j);
+      wait_vmcnt<kNB>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    pipe_barrier();
+    int i = 0;
+    for (; i + 2 < nk; ++i) {
+      pipe_read<C, NB>(aslot(i), bslot(i), f, pl, wm, wn, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step i done
-      if (pf_last) wait_vmcnt<1>();                          // step i+1 has landed
-      else wait_vmcnt<0>();
+      wait_vmcnt<0>();                                       // the B operands of step i+1 have landed
       pipe_barrier();  // 1
       __builtin_amdgcn_s_setprio(1);
-      uint8_t* stage = lds + (i & 1) * C::kStageBytes;
-      const int64_t k0 = (int64_t)(i + 2) * kPipeBK;
-      pipe_mma_copies<C, NB>(f, acc, [&](int j) { pipe_copy<C, NB>(sa, sb, k0, stage, gw, j); });
-      pf_last = prefetch(i + kPipeAhead);
+      pipe_mma_copies<C, NB, kNB>(f, acc, [&](int j) { copy_b(i + 2, j); });
       __builtin_amdgcn_s_setprio(0);
       pipe_barrier();  // 2
     }
     for (; i < nk; ++i) {
-      pipe_read<C, NB>(lds + (i & 1) * C::kStageBytes, f, pl, wm, wn, lane);
+      pipe_read<C, NB>(aslot(i), bslot(i), f, pl, wm, wn, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (pf_last) wait_vmcnt<1>();
-      else wait_vmcnt<0>();
-      pf_last = false;
+      wait_vmcnt<0>();
       pipe_barrier();  // 1
       __builtin_amdgcn_s_setprio(1);
       pipe_mma<C, NB>(f, acc);
