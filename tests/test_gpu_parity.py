@@ -44,6 +44,29 @@ def test_small_parity(name):
     full_parity(SMALL[name])
 
 
+# Contractions of 1, 2 and 3 K steps of 64 on the pipelined bf16 path: the
+# main loop's prologue alone, its last-two-steps loop alone, and one step of
+# its copy loop (hidden sizes 64 / 128 / 192; token counts whose dW
+# contraction, rounded up to 64, is 1, 2 or 3 steps too).
+SHORT_K = {
+    "tied_d64_n60": C2.scaled(n=60, d=64, v=1000),
+    "tied_d128_n100": C2.scaled(n=100, d=128, v=1300),
+    "tied_d192_n170": C2.scaled(n=170, d=192, v=900),
+    "topk_d64_n100": C4.scaled(n=100, d=64, v=1500, k=8),
+    "topk_d192_n170": C4.scaled(n=170, d=192, v=1500, k=8),
+    "separate_d64_dt192": C3.scaled(n=130, d=64, d_t=192, v=1100),
+    "separate_d192_dt64": C3.scaled(n=60, d=192, d_t=64, v=1100),
+    "dense_teacher_d64": C6.scaled(n=90, d=64, v=1024),
+    "scorer_dt64": C5.scaled(n=100, d_t=64, v=2000),
+    "scorer_dt128": C5.scaled(n=170, d_t=128, v=1300),
+}
+
+
+@pytest.mark.parametrize("name", list(SHORT_K))
+def test_short_contractions(name):
+    full_parity(SHORT_K[name].scaled(name=f"short_{name}"), vocab_chunk=512)
+
+
 @pytest.mark.parametrize("chunk", [128, 384, 1024])
 def test_chunk_and_slice_sizes(chunk):
     full_parity(C2.scaled(n=260, d=256, v=2100, name=f"quickstart_chunk{chunk}"), vocab_chunk=chunk)
