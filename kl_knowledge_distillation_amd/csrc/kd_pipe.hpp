@@ -361,6 +361,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
                                               int64_t K, uint8_t* lds,
                                               f32x4 (&acc)[NB][C::MB][C::NBK], int tid) {
   static_assert(C::kWaves == 8, "two groups of four waves");
+  static_assert(NB == 1 || NB == 2, "one or two B operands (copy_b picks between the first and the last)");
   // The wave index is the same for all lanes of a wave; readfirstlane makes that
   // visible to the compiler, so the group branches below are scalar branches.
   const int lane = tid & 63;
