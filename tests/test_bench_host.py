@@ -124,3 +124,13 @@ def test_bench_matrix_on_a_machine_without_the_gpu_path():
     assert lines[0]["label"] == "tiny_tied_fp32" and lines[0]["status"] == "FAILED"
     assert lines[0]["error"]
     assert lines[-1] == {"matrix": 1, "ok": 0, "failed": 1}
+
+
+def test_cpu_baseline_reports_the_oracle_on_a_row_sample():
+    """The oracle's own rate on a bounded row sample (the tiny workload caps it
+    at its 64 rows), with the threads it used and what the sample was."""
+    w = WORKLOADS["tiny_tied_fp32"]
+    cb = bench.cpu_baseline(w, target_s=0.05)
+    assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s"
+    assert cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["sample"].startswith(f"64 of {w.n} rows of {w.name}")
