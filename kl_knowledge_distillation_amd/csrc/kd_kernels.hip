@@ -364,13 +364,13 @@ __device__ __forceinline__ void load_logits_tile(const T* L, int64_t n, int64_t 
   }
 }
 
-// Given bf16 logits kept in registers across the main loop (pipelined
-// geometry): every wave loads its own part of the tile, still packed (two
-// bf16 per register), before the main loop, so the loads land under the
-// MFMAs and the LDS stays free for the copy slots. `vec`: v a multiple of 4
-// and the matrix 8-byte aligned (one 8-byte load per lane and block);
-// otherwise element loads. Tokens past n and rows past v read 0. (Staging the
-// tile through LDS with buffer loads instead measured 2-4% slower.)
+// Given bf16 logits in registers (pipelined geometry, 256-token tiles): every
+// wave loads its own part of the tile, still packed (two bf16 per register,
+// unpacked at each use; bf16 -> fp32 is exact), after the main loop, whose
+// registers it would not fit beside. `vec`: v a multiple of 4 and the matrix
+// 8-byte aligned (one 8-byte load per lane and block); otherwise element
+// loads. Tokens past n and rows past v read 0. (Staging the tile through LDS
+// with buffer loads instead measured 2-4% slower.)
 template <int NBT>
 using GivenRawT = uint2[kMB][NBT];
 typedef GivenRawT<kNB> GivenRaw;
@@ -398,20 +398,6 @@ __device__ __forceinline__ void given_raw_load(const bf16_t* L, int64_t n, int64
       }
     }
   }
-}
-
-template <int NBT>
-__device__ __forceinline__ void given_raw_unpack(const GivenRawT<NBT>& raw, f32x4 (&out)[kMB][NBT]) {
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NBT; ++nb) {
-      const uint2 u = raw[mb][nb];
-      out[mb][nb][0] = __uint_as_float(u.x << 16);
-      out[mb][nb][1] = __uint_as_float(u.x & 0xffff0000u);
-      out[mb][nb][2] = __uint_as_float(u.y << 16);
-      out[mb][nb][3] = __uint_as_float(u.y & 0xffff0000u);
-    }
 }
 
 // Given logits of this tile in the staged geometry, loaded after the main
@@ -485,9 +471,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   f32x4 acc[NB][kMB][NBT];
   f32x4 tacc[1][kMB][NBT];  // teacher accumulator of the separate / logits modes
   // a given logits tile (the scorer's student logits, LOGITS; a cached dense
-  // teacher, TLOGITS): unpacked to fp32 (128-token tiles), or kept packed and
-  // unpacked at each use (256-token tiles, beside 128 accumulator registers)
-  constexpr bool kPacked = kGiven && kGivenRegs && G::kTT > 128;
+  // teacher, TLOGITS): on the pipelined path always a 256-token tile, kept
+  // packed beside the 128 accumulator registers and unpacked at each use
+  static_assert(!kGivenRegs || G::kTT > 128, "pipelined given tiles are 256-token tiles");
+  constexpr bool kPacked = kGiven && kGivenRegs;
   constexpr bool kPackedZ = kPacked && MODE == MODE_LOGITS;
   constexpr bool kPackedT = kPacked && MODE == MODE_TLOGITS;
   Acc zl;
@@ -509,11 +496,6 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
     const T* const b[1] = {hs};
     if constexpr (kPackedT) {  // the teacher tile is loaded in the epilogue, half at a time
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-    } else if constexpr (kGivenRegs) {
-      GivenRawT<NBT> raw;
-      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-      given_raw_unpack<NBT>(raw, tacc[0]);
     } else {
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
@@ -521,16 +503,10 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   } else {  // MODE_LOGITS
     const T* L = static_cast<const T*>(a.logits);
     const T* const bt[1] = {ht};
-    if constexpr (kGivenRegs && G::kTT > 128) {
-      // 256-token tiles: the given tile (64 registers) would not fit beside the
-      // main loop's; it is loaded once the loop is done (its latency is a few
-      // percent of the tile's)
+    if constexpr (kPackedZ) {
+      // the given tile (64 registers) would not fit beside the main loop's; it
+      // is loaded in the epilogue (its latency is a few percent of the tile's)
       tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-    } else if constexpr (kGivenRegs) {
-      GivenRawT<NBT> raw;
-      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-      tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
-      given_raw_unpack<NBT>(raw, zl);
     } else {
       tile_product<T, G, 1>(Wt, a.dt, a.v, bt, a.dt, a.n, v0, t0, a.dt, lds, tacc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, zl);
@@ -1562,8 +1538,10 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
 
   f32x4 acc[NB][kMB][NBT];
   f32x4 tacc[1][kMB][NBT];
-  // a given teacher tile on 256-token tiles: kept packed (unpacked at each use)
-  constexpr bool kPackedT = kGivenRegs && G::kTT > 128;
+  // a given teacher tile (pipelined: 256-token tiles) is kept packed and
+  // unpacked at each use
+  static_assert(!kGivenRegs || G::kTT > 128, "pipelined given tiles are 256-token tiles");
+  constexpr bool kPackedT = kGivenRegs;
   GivenRawT<NBT> traw;
   if constexpr (kKept) {
     // the kept products are read per token block in the epilogue; a given
@@ -1572,10 +1550,6 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
       const T* L = static_cast<const T*>(a.tlogits);
       if constexpr (kPackedT) {
         given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, traw);
-      } else if constexpr (kGivenRegs) {
-        GivenRawT<NBT> raw;
-        given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-        given_raw_unpack<NBT>(raw, tacc[0]);
       } else {
         given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
       }
@@ -1592,14 +1566,9 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     const T* L = static_cast<const T*>(a.tlogits);
     const T* const b[1] = {hs};
     if constexpr (kPackedT) {
-      // 256-token tiles: the teacher tile, still packed, after the main loop
+      // the teacher tile, still packed, after the main loop
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, traw);
-    } else if constexpr (kGivenRegs) {
-      GivenRawT<NBT> raw;
-      given_raw_load<G>(reinterpret_cast<const bf16_t*>(L), a.n, a.v, t0, v0, wm, wn, lane, a.vec == 3, raw);
-      tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
-      given_raw_unpack<NBT>(raw, tacc[0]);
     } else {
       tile_product<T, G, 1>(W, a.d, a.v, b, a.d, a.n, v0, t0, a.d, lds, acc, tid);
       given_tile<T>(L, a.n, a.v, t0, v0, a.vec, wm, wn, lane, tacc[0]);
