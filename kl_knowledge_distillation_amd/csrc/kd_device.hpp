@@ -30,6 +30,7 @@ constexpr int kTile = 128;
 constexpr int kRowBytes = 80;
 constexpr int kTileBytes = kTile * kRowBytes;  // 10240
 constexpr int kXcds = 8;                       // MI355X: 8 XCDs, each with its own L2
+constexpr int kCusPerXcd = 32;                 // 256 CUs in all
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

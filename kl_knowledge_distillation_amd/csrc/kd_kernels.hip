@@ -25,9 +25,10 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
-
 #include <type_traits>
+#include <vector>
 
 #include "kd_device.hpp"
 #include "kd_internal.hpp"
@@ -1987,12 +1988,13 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
 // dH and dW of one chunk in one launch, both from the dz slab with 256 x 256
 // tiles. dH alone has too few 256 x 256 tiles to fill the chip (N/256 x D/256)
 // and its 256 x 128 form moves twice the operand bytes per MFMA; next to the dW
-// tiles it needs no second wave: each XCD takes its share of dH tiles first
-// (the longer ones, K = chunk) and then its share of dW tiles (K = N), so while
-// half of an XCD's CUs run one dH tile the other half run two dW tiles.
+// tiles it needs no second wave: each XCD takes its share of one kind first
+// and then its share of the other, so while some of an XCD's CUs run the long
+// tiles of one kind the others run the shorter ones. dw_first: the dW tiles
+// take the XCD's first places (the host picks the order that finishes first).
 template <int BN>
 __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, false, BN> h,
-                                                           GemmPipeArgs<false, false, BN> g) {
+                                                           GemmPipeArgs<false, false, BN> g, int dw_first) {
   using CH = PipeCfg<256, BN, 1, true, false>;
   using CW = PipeCfg<256, BN, 1, false, false>;
   static_assert(CH::kLdsBytes == CW::kLdsBytes, "one LDS image serves both");
@@ -2005,12 +2007,18 @@ __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, fa
   const int x = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
   const int qa = na / kXcds + (x < na % kXcds ? 1 : 0);
   const int qb = nb / kXcds + (x < nb % kXcds ? 1 : 0);
+  // this block's kind and its place among the XCD's tiles of that kind
+  const int q1 = dw_first ? qb : qa;
+  const bool is_w = (local < q1) == (dw_first != 0);
+  const int j = local < q1 ? local : local - q1;
   int mt, nt;
-  if (local < qa) {
-    grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + local, nmt_h, h.n_nt, 8, mt, nt);
+  if (!is_w) {
+    if (j >= qa) return;
+    grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + j, nmt_h, h.n_nt, 8, mt, nt);
     gemm_pipe_tile<true, false, BN>(h, mt, nt, mh, kh, lds, threadIdx.x);
-  } else if (local - qa < qb) {
-    grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + (local - qa), nmt_w, g.n_nt, 8, mt, nt);
+  } else {
+    if (j >= qb) return;
+    grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + j, nmt_w, g.n_nt, 8, mt, nt);
     gemm_pipe_tile<false, false, BN>(g, mt, nt, mw, kw, lds, threadIdx.x);
   }
 }
@@ -2437,8 +2445,24 @@ kd_status backward_t(const Plan& p, const Tensors& x, const void* saved, const f
         int most = 0;
         for (int xc = 0; xc < kXcds; ++xc)
           most = std::max(most, na / kXcds + (xc < na % kXcds) + nb / kXcds + (xc < nb % kXcds));
+        // Order of the two kinds on an XCD: a greedy schedule of its tiles (one
+        // per CU at a time, in dispatch order) on its CUs, in K steps, for each
+        // order; dH first unless dW first finishes sooner (a short last chunk:
+        // few long dW tiles left over after the short dH tiles would run alone).
+        auto makespan = [](int n1, int64_t k1, int n2, int64_t k2) {
+          std::vector<int64_t> cu(kCusPerXcd, 0);
+          auto take = [&](int cnt, int64_t k) {
+            for (int j = 0; j < cnt; ++j) *std::min_element(cu.begin(), cu.end()) += k;
+          };
+          take(n1, k1);
+          take(n2, k2);
+          return *std::max_element(cu.begin(), cu.end());
+        };
+        const int qa = (na + kXcds - 1) / kXcds, qb = (nb + kXcds - 1) / kXcds;
+        const int64_t sh = (gb.K + kPipeBK - 1) / kPipeBK, sw = (ga.K + kPipeBK - 1) / kPipeBK;
+        const int dw_first = makespan(qb, sw, qa, sh) < makespan(qa, sh, qb, sw) ? 1 : 0;
         KD_TRY(L.run(KD_KERNEL_GEMM_DWDH, [&] {
-          gemm_dual_kernel<256><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga);
+          gemm_dual_kernel<256><<<dim3((unsigned)(kXcds * most)), 512, 0, stream>>>(gb, ga, dw_first);
         }));
       } else {
         // 256-wide tiles when they still give every CU a tile, else 128-wide.
