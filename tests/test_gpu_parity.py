@@ -95,6 +95,15 @@ def test_chunked_forward(name):
     full_parity(w.scaled(name=f"{w.name}_{name}"), vocab_chunk=chunk)
 
 
+# dW and dH of a chunk share one launch, in which each XCD runs its tiles of one
+# kind before the other's. With 8192 tokens, hidden 2048 and 1024-column chunks
+# the dW tiles are few and long (K = 8192) next to many short dH tiles (K = the
+# chunk), so the host puts the dW tiles first on both chunks (the full one and
+# the 256-column last one); every element of dH and dW is compared.
+def test_dual_launch_dw_tiles_first():
+    full_parity(C4.scaled(n=8192, d=2048, v=1280, k=8, name="topk_dual_dw_first"), vocab_chunk=1024)
+
+
 def test_reductions_and_normalizer():
     w = C2.scaled(n=200, d=256, v=1500)
     x = make_inputs(w, "cuda", seed=3)
