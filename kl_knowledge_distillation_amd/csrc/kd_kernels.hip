@@ -460,7 +460,7 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   int t;
   if (!xcd_live_tile(blockIdx.x, a.n_slices * n_tt, t)) return;
   int slice, tt;  // slice = the vocabulary tile of this workgroup
-  grouped_tile(t, a.n_slices, n_tt, 8, slice, tt);
+  grouped_tile(t, a.n_slices, n_tt, tile_group(G::kVT, G::kTT), slice, tt);
   const int64_t t0 = (int64_t)tt * G::kTT;
   const int64_t v0 = (int64_t)(a.slice0 + slice) * G::kVT;
 
@@ -1519,7 +1519,7 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   int t;
   if (!xcd_live_tile(blockIdx.x, a.n_vt * n_tt, t)) return;
   int vt, tt;
-  grouped_tile(t, a.n_vt, n_tt, 8, vt, tt);
+  grouped_tile(t, a.n_vt, n_tt, tile_group(G::kVT, G::kTT), vt, tt);
   const int64_t v0 = a.c0 + (int64_t)vt * G::kVT;
   const int64_t t0 = (int64_t)tt * G::kTT;
   const T* hs = static_cast<const T*>(a.hs);
@@ -1981,7 +1981,7 @@ __global__ __launch_bounds__(512, 2) void gemm_pipe_kernel(GemmPipeArgs<AKC, BKC
   int t;
   if (!xcd_live_tile(blockIdx.x, n_mt * a.n_nt, t)) return;
   int mt, nt;
-  grouped_tile(t, n_mt, a.n_nt, 8, mt, nt);
+  grouped_tile(t, n_mt, a.n_nt, tile_group(256, BN), mt, nt);
   gemm_pipe_tile<AKC, BKC, BN>(a, mt, nt, M, K, lds, threadIdx.x);
 }
 
@@ -2014,11 +2014,11 @@ __global__ __launch_bounds__(512, 2) void gemm_dual_kernel(GemmPipeArgs<true, fa
   int mt, nt;
   if (!is_w) {
     if (j >= qa) return;
-    grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + j, nmt_h, h.n_nt, 8, mt, nt);
+    grouped_tile(x * (na / kXcds) + min(x, na % kXcds) + j, nmt_h, h.n_nt, tile_group(256, BN), mt, nt);
     gemm_pipe_tile<true, false, BN>(h, mt, nt, mh, kh, lds, threadIdx.x);
   } else {
     if (j >= qb) return;
-    grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + j, nmt_w, g.n_nt, 8, mt, nt);
+    grouped_tile(x * (nb / kXcds) + min(x, nb % kXcds) + j, nmt_w, g.n_nt, tile_group(256, BN), mt, nt);
     gemm_pipe_tile<false, false, BN>(g, mt, nt, mw, kw, lds, threadIdx.x);
   }
 }
