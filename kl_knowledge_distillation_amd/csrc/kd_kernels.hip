@@ -250,10 +250,11 @@ struct GeoStaged {
   __device__ static int col(int wn, int nb, int lane) { return acc_col(wn, nb, lane); }
 };
 // Pipelined: 256 vocabulary rows x TT tokens, 8 waves (4 x 2, two ping-pong
-// groups), buffer-load copies into 3 + 2 LDS slots; bf16 with hidden sizes multiple of
-// 64. TT = 128 for two B operands (tied teacher) and for the tiles that hold a
-// given logits tile in registers; TT = 256 for one B operand (top-K), which
-// halves the operand bytes copied per MFMA against 256 x 128.
+// groups), buffer-load copies into 3 A slots and 2 or 4 B slots; bf16 with hidden sizes multiple of
+// 64. TT = 128 for two B operands (tied teacher) and for the separate teacher's
+// two products in turn; TT = 256 for one B operand (top-K, and the tiles that
+// hold a given logits tile in registers), which halves the operand bytes
+// copied per MFMA against 256 x 128.
 template <int TT>
 struct GeoPipeT {
   static constexpr bool kPipe = true;

@@ -196,9 +196,12 @@ struct PipeCfg {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int MB = TM / 16, NBK = TN / 16;
   static constexpr int kABytes = BM * 128, kBBytes = BN * 128;
-  // LDS: three A-operand slots, then two slots of the NB B operands
+  // LDS: three A-operand slots, then slots of the NB B operands: four where
+  // the rest of the LDS holds them (one 128-row B operand), else two
+  static constexpr int kBFit = (160 * 1024 - 3 * kABytes) / (NB * kBBytes);
+  static constexpr int kBSlots = kBFit >= 4 ? 4 : 2;
   static constexpr int kBBase = 3 * kABytes;
-  static constexpr int kLdsBytes = 3 * kABytes + 2 * NB * kBBytes;
+  static constexpr int kLdsBytes = 3 * kABytes + kBSlots * NB * kBBytes;
   // copy instructions per wave and step: group A copies the A operand, group
   // B the B operands, a quarter each per wave
   static constexpr int kAPer = kABytes / 1024 / 4, kBPer = kBBytes / 1024 / 4;
@@ -348,20 +351,22 @@ __device__ __forceinline__ void pipe_mma_copies(const PipeFrags<C, NB>& f,
 // Ends with a full barrier, so the caller may reuse `lds` right after.
 //
 // Step s (64 of K) has its A operand in A-slot s % 3 and its B operands in
-// B-slot s % 2. Group A (waves 0-3) runs its MFMAs of step i while group B
-// reads its fragments of step i; after barrier 1 group B runs its MFMAs while
-// group A reads step i+1; barrier 2 ends the step. Each group copies its own
-// operand, between its own MFMAs of step i, for step i+2: group A into the
-// A-slot of step i-1 (both groups read it before barrier 1 of step i-1), group
-// B into the B-slot of step i (read before barrier 1 of step i). The A operand
-// so leads by 1.5-2 steps, the B operands by 1. Each group waits for its own
-// copies of step i+1 before barrier 1 of step i.
+// B-slot s % SB (SB = C::kBSlots, 2 or 4). Group A (waves 0-3) runs its MFMAs
+// of step i while group B reads its fragments of step i; after barrier 1 group
+// B runs its MFMAs while group A reads step i+1; barrier 2 ends the step. Each
+// group copies its own operand between its own MFMAs of step i: group A the A
+// operand of step i+2 into the A-slot of step i-1 (both groups read it before
+// barrier 1 of step i-1), group B the B operands of step i+SB into the B-slot
+// of step i (read before barrier 1 of step i). The A operand so leads by
+// 1.5-2 steps, the B operands by SB-1. Each group waits for its own copies of
+// step i+1 before barrier 1 of step i.
 template <class C, int NB, class OA, class OB>
 __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t a_row0, int64_t b_row0,
                                               int64_t K, uint8_t* lds,
                                               f32x4 (&acc)[NB][C::MB][C::NBK], int tid) {
   static_assert(C::kWaves == 8, "two groups of four waves");
   static_assert(NB == 1 || NB == 2, "one or two B operands (copy_b picks between the first and the last)");
+  static_assert(C::kBSlots == 2 || C::kBSlots == 4, "B-slot index by mask; the tail's waits cover up to four");
   // The wave index is the same for all lanes of a wave; readfirstlane makes that
   // visible to the compiler, so the group branches below are scalar branches.
   const int lane = tid & 63;
@@ -383,7 +388,8 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
   PipeLanes<C> pl;
   pl.init(wm, wn, lane);
   auto aslot = [&](int st) { return lds + (st % 3) * C::kABytes; };
-  auto bslot = [&](int st) { return lds + C::kBBase + (st & 1) * (NB * C::kBBytes); };
+  constexpr int SB = C::kBSlots;
+  auto bslot = [&](int st) { return lds + C::kBBase + (st & (SB - 1)) * (NB * C::kBBytes); };
   constexpr int kNA = C::kACopies, kNB = C::kBCopies;
   // (copy-and-MFMA steps and the last two steps are separate loops: one loop
   // with a branch between the two MFMA bodies made the compiler spill)
@@ -435,32 +441,39 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
       if (g == 0) sb[0].issue((int64_t)st * kPipeBK, dst, gw * C::kBPer + jj);
       else sb[NB - 1].issue((int64_t)st * kPipeBK, dst, gw * C::kBPer + jj);
     };
-    // Prologue: the B operands of steps 0 and 1.
+    // Prologue: the B operands of steps 0 .. SB-1; step 0 visible at the first barrier.
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) copy_b(0, j);
-    if (nk > 1) {
+    for (int st = 0; st < SB; ++st)
+      if (st < nk) {
 #pragma unroll
-      for (int j = 0; j < kNB; ++j) copy_b(1, j);
-      wait_vmcnt<kNB>();
-    } else {
-      wait_vmcnt<0>();
-    }
+        for (int j = 0; j < kNB; ++j) copy_b(st, j);
+      }
+    if (nk >= SB) wait_vmcnt<(SB - 1) * kNB>();
+    else wait_vmcnt<0>();
     pipe_barrier();
     int i = 0;
-    for (; i + 2 < nk; ++i) {
+    for (; i + SB < nk; ++i) {
       pipe_read<C, NB>(aslot(i), bslot(i), f, pl, wm, wn, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step i done
-      wait_vmcnt<0>();                                       // the B operands of step i+1 have landed
+      wait_vmcnt<(SB - 2) * kNB>();  // the B operands of step i+1 have landed (those of i+2 .. i+SB-1 may not)
       pipe_barrier();  // 1
       __builtin_amdgcn_s_setprio(1);
-      pipe_mma_copies<C, NB, kNB>(f, acc, [&](int j) { copy_b(i + 2, j); });
+      pipe_mma_copies<C, NB, kNB>(f, acc, [&](int j) { copy_b(i + SB, j); });
       __builtin_amdgcn_s_setprio(0);
       pipe_barrier();  // 2
     }
     for (; i < nk; ++i) {
       pipe_read<C, NB>(aslot(i), bslot(i), f, pl, wm, wn, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      wait_vmcnt<0>();
+      // step i+1 landed; the copies of steps i+2 .. nk-1 may still be in flight
+      if constexpr (SB == 4) {
+        const int later = nk - 2 - i;
+        if (later >= 2) wait_vmcnt<2 * kNB>();
+        else if (later == 1) wait_vmcnt<kNB>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
       pipe_barrier();  // 1
       __builtin_amdgcn_s_setprio(1);
       pipe_mma<C, NB>(f, acc);
