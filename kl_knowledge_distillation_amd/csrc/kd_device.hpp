@@ -96,17 +96,6 @@ __device__ __forceinline__ bool xcd_live_tile(int bid, int live, int& t) {
 // Grouped order over an (na x nb) grid of tiles: runs of `group` consecutive
 // b values for each a, so a window of consecutive tiles covers a near-square
 // block and both operands are re-read from L2 rather than HBM.
-__device__ __forceinline__ void grouped_tile(int t, int na, int nb, int group, int& a, int& b);
-
-// The group of an XCD's 32 concurrent tiles (a x b = 32 / group x group): the
-// shape that touches the fewest distinct operand bytes per K step, and, where
-// two shapes tie (square tiles), the one in which each b-side (B operand) block
-// serves more tiles, since the pipelined loop copies that operand with less
-// lead and its L2 misses cost more. 256-row A and 128-row B tiles: 4 x 8
-// (256 KB per step against 320 KB for 8 x 4); 256 x 256: 8 x 4. (The
-// register-staged 128 x 128 tiles keep 4 x 8.)
-constexpr int tile_group(int a_rows, int b_rows) { return a_rows == 256 && b_rows == 256 ? 4 : 8; }
-
 __device__ __forceinline__ void grouped_tile(int t, int na, int nb, int group, int& a, int& b) {
   const int width = group * na;
   const int g = t / width;
@@ -116,6 +105,15 @@ __device__ __forceinline__ void grouped_tile(int t, int na, int nb, int group, i
   a = r / gsz;
   b = first + r % gsz;
 }
+
+// The group of an XCD's 32 concurrent tiles (a x b = 32 / group x group): the
+// shape that touches the fewest distinct operand bytes per K step, and, where
+// two shapes tie (square tiles), the one in which each b-side (B operand) block
+// serves more tiles, since the pipelined loop copies that operand with less
+// lead and its L2 misses cost more. 256-row A and 128-row B tiles: 4 x 8
+// (256 KB per step against 320 KB for 8 x 4); 256 x 256: 8 x 4. (The
+// register-staged 128 x 128 tiles keep 4 x 8.)
+constexpr int tile_group(int a_rows, int b_rows) { return a_rows == 256 && b_rows == 256 ? 4 : 8; }
 
 // An operand of C = A B^T-style contractions, seen as (row, k) elements.
 // KC  (K-contiguous):  element (row, k) at ptr[row * ld + k]; rows < `rows`, k < `kdim`.
