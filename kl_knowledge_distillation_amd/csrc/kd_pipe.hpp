@@ -1,6 +1,6 @@
 // bf16 main loop with buffer loads straight into LDS (three A-operand slots,
-// two B-operand slots), ping-pong scheduling and v_mfma_f32_16x16x32_bf16
-// (gfx950).
+// two or four B-operand slots), ping-pong scheduling and
+// v_mfma_f32_16x16x32_bf16 (gfx950).
 //
 // Workgroup: 512 threads = 8 wave64 as 4 (A rows) x 2 (B rows). Output tile
 // BM x BN (A rows x B rows); each wave owns TM x TN = (BM/4) x (BN/2), made of
@@ -38,15 +38,16 @@
 //               the A operand of step i+2
 //   barrier 1 (step i+1 has landed: each group waited for its own copies)
 //   part 2:  A: read fragments of step i+1  B: MFMAs of step i, copying the
-//                                              B operands of step i+2
+//                                              B operands of step i+SB
 //   barrier 2
 // While one wave of a SIMD issues MFMAs the other does its LDS reads, so the
 // matrix pipe keeps running across the barriers. The copies are spread over
 // both parts, each half of them between one group's MFMAs: the rate at which
 // a CU's copies can be served (~64 B/clk) is the loop's limit, and copies
 // bunched in one part stall the MFMAs behind them. Step s has its A operand in
-// A-slot s % 3 and its B operands in B-slot s % 2; the A-slot of step i-1 and
-// the B-slot of step i are free after barrier 1 of those steps.
+// A-slot s % 3 and its B operands in B-slot s % SB (SB = 4 where the LDS holds
+// four, one 128-row B operand; else 2); the A-slot of step i-1 and the B-slot
+// of step i are free after barrier 1 of those steps.
 #pragma once
 
 #include "kd_device.hpp"
