@@ -224,8 +224,8 @@ __device__ __forceinline__ bf16x8 kc_frag(const uint8_t* tile, int row0, int kk,
 // ds_read_b64_tr_b16 through inline asm: issued this way the compiler does not
 // add a wait for every in-flight LDS copy in front of it (it cannot tell the
 // intrinsic form apart from the slots those copies fill). Its results are only
-// ready after an lgkmcnt wait, which the main loop issues explicitly before the
-// fragments are used.
+// ready after an lgkmcnt wait, which the main loop issues explicitly, and
+// pipe_frags_ready ties every use to that wait.
 __device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* p) {
   uint2 v;
   const uint32_t addr = (uint32_t)(uintptr_t)p;
@@ -266,6 +266,30 @@ struct PipeFrags {
   bf16x8 a[2][C::MB];
   bf16x8 b[2][NB][C::NBK];
 };
+
+// Waits for this wave's LDS reads, then makes every fragment register that a
+// transposed read (inline asm, whose latency the compiler does not see) filled
+// the result of an asm statement placed after the wait. Volatile asm keeps its
+// order, so no MFMA using such a fragment can be scheduled above the wait; the
+// compiler itself waits for the K-contiguous fragments (ordinary LDS loads).
+template <class C, int NB>
+__device__ __forceinline__ void pipe_frags_ready(PipeFrags<C, NB>& f) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if constexpr (!C::kAKC) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) asm volatile("" : "+v"(f.a[kk][mb]));
+  }
+  if constexpr (!C::kBKC) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int g = 0; g < NB; ++g)
+#pragma unroll
+        for (int nb = 0; nb < C::NBK; ++nb) asm volatile("" : "+v"(f.b[kk][g][nb]));
+  }
+}
 
 // Transposed-read lane bases of this wave's A and B fragments (unused for
 // K-contiguous operands).
@@ -412,7 +436,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     pipe_read<C, NB>(aslot(0), bslot(0), f, pl, wm, wn, lane);
     int i = 0;
     for (; i + 2 < nk; ++i) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // fragments of step i ready
+      pipe_frags_ready<C, NB>(f);  // fragments of step i ready
       __builtin_amdgcn_s_setprio(1);
       pipe_mma_copies<C, NB, kNA>(f, acc, [&](int j) { copy_a(i + 2, j); });
       __builtin_amdgcn_s_setprio(0);
@@ -422,7 +446,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
       pipe_barrier();  // 2
     }
     for (; i < nk; ++i) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      pipe_frags_ready<C, NB>(f);
       __builtin_amdgcn_s_setprio(1);
       pipe_mma<C, NB>(f, acc);
       __builtin_amdgcn_s_setprio(0);
@@ -455,7 +479,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     int i = 0;
     for (; i + SB < nk; ++i) {
       pipe_read<C, NB>(aslot(i), bslot(i), f, pl, wm, wn, lane);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of step i done
+      pipe_frags_ready<C, NB>(f);  // reads of step i done
       wait_vmcnt<(SB - 2) * kNB>();  // the B operands of step i+1 have landed (those of i+2 .. i+SB-1 may not)
       pipe_barrier();  // 1
       __builtin_amdgcn_s_setprio(1);
@@ -465,7 +489,7 @@ __device__ __forceinline__ void pipe_mainloop(const OA& A, const OB* B, int64_t 
     }
     for (; i < nk; ++i) {
       pipe_read<C, NB>(aslot(i), bslot(i), f, pl, wm, wn, lane);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      pipe_frags_ready<C, NB>(f);
       // step i+1 landed; the copies of steps i+2 .. nk-1 may still be in flight
       if constexpr (SB == 4) {
         const int later = nk - 2 - i;
