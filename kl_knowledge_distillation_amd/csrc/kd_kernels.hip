@@ -1605,7 +1605,59 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
   // and the vocabulary bound become 32-bit compares against constants.
   const int rb = acc_row(wm, 0, 0, lane);
   const int lim = (int)min(a.v - v0 - rb, (int64_t)1 << 30);  // rows k >= lim are past v
+  // One token's inputs, read from indices that are always valid (a row that is
+  // not live reads row 0, then reads as zero), so that no load is conditional.
+  struct TokIn {
+    float4 sv;   // saved statistics
+    float l1;    // MODE_TCE: the teacher's log-normaliser at T = 1
+    int64_t y;   // label, -1 without labels
+    int j0, j1;  // top-K: this token's run of entries in the tile
+  };
+  auto tok_inputs = [&](int nb) {
+    TokIn r;
+    const int64_t tok = t0 + G::col(wn, nb, lane);
+    const bool live = tok < n_live;
+    const int64_t tc = live ? tok : 0;
+    // (idx[0] may be unwritten when no row is usable: only a live row's entry is used)
+    const int64_t ix = a.idx ? (int64_t)a.idx[tc] : tc;
+    const int64_t orig = live ? ix : 0;  // original row
+    const float4 s4 = reinterpret_cast<const float4*>(a.saved)[orig];
+    r.sv = live ? s4 : make_float4(0.f, 0.f, 0.f, 0.f);
+    r.l1 = 0.f;
+    r.y = -1;
+    r.j0 = r.j1 = 0;
+    if constexpr (MODE == MODE_TCE) {
+      const float x = a.saved[4 * a.n + kSavedHeaderBytes / 4 + orig];
+      r.l1 = live ? x : 0.f;
+    }
+    if constexpr (MODE != MODE_TOPK) {
+      const int64_t yy = a.labels ? a.labels[orig] : -1;
+      r.y = live ? yy : -1;
+    }
+    if constexpr (MODE == MODE_TOPK) {
+      const int32_t* off = a.tk_off + tc * (int64_t)(a.n_vt + 1) + vt;
+      const int o0 = off[0], o1 = off[1];
+      r.j0 = live ? o0 : 0;
+      r.j1 = live ? o1 : 0;
+    }
+    return r;
+  };
+  // All token blocks' inputs are loaded before any is used, so that their
+  // latencies overlap instead of adding up block by block. The tiles that hold
+  // a packed teacher tile, and the kept-product tiles (four waves per SIMD),
+  // have no registers to spare and load per block.
+  constexpr bool kPreload = !kPackedT && !kKept;
+  TokIn pre[kPreload ? NBT : 1];
+  if constexpr (kPreload) {
+#pragma unroll
+    for (int nb = 0; nb < NBT; ++nb) pre[nb] = tok_inputs(nb);
+  }
   auto epilogue = [&](auto rev_tag, auto sq_tag) {
+  // No implicit multiply-add contraction here: which products the compiler
+  // fuses depends on the surrounding code, and the kept-product and recompute
+  // instantiations must round every value alike (every fusion meant is an
+  // explicit fmaf).
+#pragma clang fp contract(off)
   constexpr bool kRev = decltype(rev_tag)::value;
   constexpr bool kSq = decltype(sq_tag)::value;
 #pragma unroll
@@ -1613,18 +1665,17 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     const int64_t tok = t0 + G::col(wn, nb, lane);
     if (tok >= a.dz_rows) continue;
     const bool live = tok < n_live;  // rows past n (or nv) are zero padding of the slab
-    const int64_t orig = (live && a.idx) ? a.idx[tok] : tok;  // original row
-    const float4 sv = live ? reinterpret_cast<const float4*>(a.saved)[orig] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const TokIn ti = kPreload ? pre[kPreload ? nb : 0] : tok_inputs(nb);
+    const float4 sv = ti.sv;
     // MODE_TCE: the softmax at T = 1 is the teacher's
-    const float L1 = (MODE == MODE_TCE ? (live ? a.saved[4 * a.n + kSavedHeaderBytes / 4 + orig] : 0.f)
-                                       : sv.x) * kLog2e;
+    const float L1 = (MODE == MODE_TCE ? ti.l1 : sv.x) * kLog2e;
     const float LzT = sv.y * kLog2e, LtT = sv.z * kLog2e, mass = sv.w;
     const float L1h = 0.5f * L1;
     const float kz = kSq ? exp2_fast(L1h - LzT) : 0.f;
     int64_t y = -1;
     bool valid = live;
     if (live && MODE != MODE_TOPK && a.labels) {
-      y = a.labels[orig];
+      y = ti.y;
       valid = y != a.ignore && y >= 0 && y < a.v;
     }
     // coef = 0 zeroes every term of a row that is not valid (all are finite)
@@ -1647,9 +1698,8 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
     const float* tpr = nullptr;
     if constexpr (MODE == MODE_TOPK) {
       if (live) {
-        const int32_t* off = a.tk_off + tok * (int64_t)(a.n_vt + 1) + vt;
-        j0 = off[0];
-        j1 = off[1];
+        j0 = ti.j0;
+        j1 = ti.j1;
         tix = a.tk_sidx + tok * (int64_t)a.k;
         tpr = a.tk_sprob + tok * (int64_t)a.k;
       }
@@ -1664,10 +1714,11 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
       kept_load<NBT>(a.keep + (MODE == MODE_TCE ? a.keep_t : 0), tile, kWaves, w, lane, nb, live, zk);
       if constexpr (kKeptT) kept_load<NBT>(a.keep + a.keep_t, tile, kWaves, w, lane, nb, live, tk);
     }
+    // o[mb][r]: this token's dz at vocabulary row v0 + rb + 16 mb + r
+    float o[kMB][4];
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       // registers r = 0..3 are four consecutive vocabulary rows
-      float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int k = mb * 16 + r;
@@ -1697,20 +1748,26 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
           dv = fmaf(ckf, pz - pt, dv);
           if constexpr (kRev) dv = fmaf(ckr * pz, fmaf(fmaf(tt, -a.rho, zz), invT, rev0), dv);
         }
-        o[r] = (k < lim) ? dv : 0.f;
+        o[mb][r] = (k < lim) ? dv : 0.f;
       }
-      if constexpr (MODE == MODE_TOPK) {
-        // entries at this lane's four rows of block mb: v0 + rb + 16 mb + r
-        const int base = (int)(v0 + rb) + 16 * mb;
-        for (int j = j0; j < j1; ++j) {
-          const int d = tix[j] - base;
-          const float q = cp * tpr[j];
+    }
+    if constexpr (MODE == MODE_TOPK) {
+      // the token's entries in this tile, each read once: the one at row
+      // v0 + rb + 16 mb + r (if this lane holds it) subtracts its p term
+      const int base = (int)(v0 + rb);
+      for (int j = j0; j < j1; ++j) {
+        const int d = tix[j] - base;
+        const float q = cp * tpr[j];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] -= (d == r) ? q : 0.f;
-        }
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[mb][r] -= (d == 16 * mb + r) ? q : 0.f;
       }
+    }
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
       if constexpr (kKept) {
-        if (!kept_ok) o[0] = o[1] = o[2] = o[3] = __builtin_nanf("");
+        if (!kept_ok) o[mb][0] = o[mb][1] = o[mb][2] = o[mb][3] = __builtin_nanf("");
       }
       if constexpr (kStage) {
         // into the LDS image of the tile: token-major rows of 256 bf16, the
@@ -1718,11 +1775,11 @@ __global__ __launch_bounds__(G::kThreads, kKept ? 4 : 2) void bwd_dz_kernel(BwdA
         const int tl = (int)(tok - t0);
         const int vl = rb + 16 * mb;
         uint2 u;
-        u.x = bf16x2_rne(o[0], o[1]);
-        u.y = bf16x2_rne(o[2], o[3]);
+        u.x = bf16x2_rne(o[mb][0], o[mb][1]);
+        u.y = bf16x2_rne(o[mb][2], o[mb][3]);
         *reinterpret_cast<uint2*>(lds + tl * 512 + (((vl >> 3) ^ (tl & 31)) << 4) + (vl & 7) * 2) = u;
       } else {
-        store4<T>(row + acc_row(wm, mb, 0, lane), o[0], o[1], o[2], o[3]);
+        store4<T>(row + acc_row(wm, mb, 0, lane), o[mb][0], o[mb][1], o[mb][2], o[mb][3]);
       }
     }
   }
