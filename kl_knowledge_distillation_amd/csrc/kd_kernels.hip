@@ -562,6 +562,21 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
   const int rb = acc_row(wm, 0, 0, lane);  // this lane's rows: v0 + rb + 16 mb + r
   const int l16 = lane & 15;
 
+  // Top-K: each token block's run of index-sorted entries in this tile, read
+  // for all token blocks before any is used (a row past n reads row 0's bounds
+  // and gets an empty run), so that the loads' latencies overlap.
+  int kj0[MODE == MODE_TOPK ? NBT : 1], kj1[MODE == MODE_TOPK ? NBT : 1];
+  if constexpr (MODE == MODE_TOPK) {
+#pragma unroll
+    for (int nb = 0; nb < NBT; ++nb) {
+      const int64_t tok = t0 + G::col(wn, nb, lane);
+      const bool live = tok < a.n;
+      const int32_t* off = a.topk_off + (live ? tok : 0) * (a.n_slices + 1) + slice;
+      const int o0 = off[0], o1 = off[1];
+      kj0[nb] = live ? o0 : 0;
+      kj1[nb] = live ? o1 : 0;
+    }
+  }
   // 256-token tiles with packed given logits run the epilogue in two halves of
   // token blocks, each loading its half of the given tile just before it, so
   // only half of it is held beside the teacher accumulators.
@@ -617,9 +632,8 @@ __global__ __launch_bounds__(G::kThreads, 2) void fwd_tiles_kernel(FwdArgs a) {
       // its row; the lane and wave partials add up like the sums below.
       const int64_t tok = t0 + G::col(wn, nb, lane);
       float cr = 0.f;
-      if (tok < a.n) {
-        const int32_t* off = a.topk_off + tok * (a.n_slices + 1) + slice;
-        const int j0 = off[0], j1 = off[1];  // sorted entries with index in [v0, v0 + kVT) and < v
+      {
+        const int j0 = kj0[nb], j1 = kj1[nb];  // sorted entries with index in [v0, v0 + kVT) and < v
         const int32_t* ix = a.topk_sidx + tok * a.k;
         const float* pr = a.topk_sprob + tok * a.k;
         const int base = (int)(v0 + rb);
