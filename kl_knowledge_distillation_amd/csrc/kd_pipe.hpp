@@ -42,9 +42,10 @@
 //   barrier 2
 // While one wave of a SIMD issues MFMAs the other does its LDS reads, so the
 // matrix pipe keeps running across the barriers. The copies are spread over
-// both parts, each half of them between one group's MFMAs: the rate at which
-// a CU's copies can be served (~64 B/clk) is the loop's limit, and copies
-// bunched in one part stall the MFMAs behind them. Step s has its A operand in
+// both parts, each half of them between one group's MFMAs; bunched in one
+// part they stall the MFMAs behind them. (The copies set the loop's pace, but
+// not by the rate a CU can be served: with every copy hitting L2 the loop is
+// only a few percent faster.) Step s has its A operand in
 // A-slot s % 3 and its B operands in B-slot s % SB (SB = 4 where the LDS holds
 // four, one 128-row B operand; else 2); the A-slot of step i-1 and the B-slot
 // of step i are free after barrier 1 of those steps.
