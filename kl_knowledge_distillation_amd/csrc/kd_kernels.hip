@@ -2029,18 +2029,62 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmPipeArgs<AKC, BKC, BN>&
       const int64_t row = m0 + pipe_row<C>(wm, mb, r, lane);
       orow[mb][r] = (row >= M) ? -1 : (a.rowmap ? (int64_t)a.rowmap[row] : row);
     }
+  // One 16-row block at a time: the values added to it (the fp32 partial cadd,
+  // the output being accumulated) are all loaded before any of the block is
+  // stored, from offsets that are always valid (an element past M or N reads
+  // element 0 and is not stored), so that their latencies overlap; per element,
+  // the loads would wait one after another behind the stores before them. The
+  // three options are compile-time in each variant, so no load is conditional.
+  // The sum keeps store_grad's order: (acc + cadd) + old.
+  auto finish = [&](auto c_tag, auto o_tag, auto b_tag) {
+    constexpr bool kAddC = decltype(c_tag)::value, kAddOld = decltype(o_tag)::value;
+    constexpr bool kBf16 = decltype(b_tag)::value;
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb) {
+      float xc[C::NBK][4], xo[C::NBK][4];
 #pragma unroll
-    for (int nb = 0; nb < C::NBK; ++nb) {
-      const int64_t col = n0 + pipe_col<C>(wn, nb, lane);
-      if (col >= a.N) continue;
+      for (int nb = 0; nb < C::NBK; ++nb) {
+        const int64_t col = n0 + pipe_col<C>(wn, nb, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (orow[mb][r] >= 0)
-          store_grad(a.C, a.out_bf16, a.cadd, a.accumulate, orow[mb][r] * a.ldc + col, acc[0][mb][nb][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int64_t o = (col < a.N && orow[mb][r] >= 0) ? orow[mb][r] * a.ldc + col : 0;
+          if constexpr (kAddC) xc[nb][r] = a.cadd[o];
+          if constexpr (kAddOld) {
+            if constexpr (kBf16) xo[nb][r] = to_f32(static_cast<const bf16_t*>(a.C)[o]);
+            else xo[nb][r] = static_cast<const float*>(a.C)[o];
+          }
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < C::NBK; ++nb) {
+        const int64_t col = n0 + pipe_col<C>(wn, nb, lane);
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (orow[mb][r] < 0) continue;
+          const int64_t o = orow[mb][r] * a.ldc + col;
+          float v = acc[0][mb][nb][r];
+          if constexpr (kAddC) v += xc[nb][r];
+          if constexpr (kAddOld) v = xo[nb][r] + v;
+          if constexpr (kBf16) static_cast<bf16_t*>(a.C)[o] = bf16_rne(v);
+          else static_cast<float*>(a.C)[o] = v;
+        }
       }
     }
+  };
+  using Y = std::true_type;
+  using N_ = std::false_type;
+  const int sel = (a.cadd ? 4 : 0) | (a.accumulate ? 2 : 0) | (a.out_bf16 ? 1 : 0);
+  switch (sel) {
+    case 0: finish(N_{}, N_{}, N_{}); break;
+    case 1: finish(N_{}, N_{}, Y{}); break;
+    case 2: finish(N_{}, Y{}, N_{}); break;
+    case 3: finish(N_{}, Y{}, Y{}); break;
+    case 4: finish(Y{}, N_{}, N_{}); break;
+    case 5: finish(Y{}, N_{}, Y{}); break;
+    case 6: finish(Y{}, Y{}, N_{}); break;
+    default: finish(Y{}, Y{}, Y{}); break;
+  }
 }
 
 template <bool AKC, bool BKC, int BN>
