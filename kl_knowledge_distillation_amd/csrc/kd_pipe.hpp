@@ -343,9 +343,9 @@ __device__ __forceinline__ void pipe_mma(const PipeFrags<C, NB>& f, f32x4 (&acc)
 
 // The same MFMAs with copy(j), j = 0 .. N-1, spread evenly: copy j after MFMA
 // IL (j + 1) - 1, IL = kMfma / N (sched_group_barrier keeps the interleave).
-// Four waves each issuing 1 KB per 4 MFMAs (16 cycles each) ask for 64 B/clk
-// per CU, the rate the L2 delivers to a CU; issued faster, copies queue and
-// stall the MFMAs behind them.
+// With 256-row operands IL is 8: four waves each issuing 1 KB per 8 MFMAs (16
+// cycles each) ask for ~32 B/clk per CU, about half of what the L2 delivers to
+// a CU; issued faster, copies queue and stall the MFMAs behind them.
 template <class C, int NB, int N, class F>
 __device__ __forceinline__ void pipe_mma_copies(const PipeFrags<C, NB>& f,
                                                 f32x4 (&acc)[NB][C::MB][C::NBK], F&& copy) {
