@@ -1983,9 +1983,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs<T, AKC, BKC>
 }
 
 // Pipelined bf16 GEMM: C[M x N] (+)= sum_k A(m, k) B(n, k), fp32 output, tile
-// 256 x BN, 8 waves, 3 + 2 slots. A / B are K-contiguous or row-contiguous; K is
-// a multiple of 64 and both operands are zero (or read as zero) past their
-// own K extent.
+// 256 x BN, 8 waves, three A slots and two B slots (four for BN = 128). A / B
+// are K-contiguous or row-contiguous; K is a multiple of 64 and both operands
+// are zero (or read as zero) past their own K extent.
 template <bool AKC, bool BKC, int BN>
 struct GemmPipeArgs {
   std::conditional_t<AKC, PipeOperand, PipeOperandMN> A;
