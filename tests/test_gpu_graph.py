@@ -86,3 +86,58 @@ def test_captured_step_replays_bit_identical(name):
         for a, b in zip(_outputs(r, grads), ref):
             assert torch.equal(a, b), f"{name}: replay {rep} differs from the eager step"
     assert r.read_status() == 0
+
+
+def test_captured_no_alloc_forward():
+    """kd_loss_fwd_noalloc is meant for callers that cannot allocate, such as
+    code under graph capture: its workspace is the library's per-device scratch
+    (set up by an eager call before the capture). Every replay equals the
+    workspace forward bit for bit."""
+    import ctypes
+
+    from kl_knowledge_distillation_amd import _lib as L
+
+    w, chunk = CASES["tied"]
+    say(f"[graph] no-alloc forward n={w.n} d={w.d} v={w.v} chunk={chunk}")
+    x = make_inputs(w, "cuda", seed=7)
+    r = make_runner(w, x, vocab_chunk=chunk)
+    r.saved.zero_()
+    r.forward()
+    torch.cuda.synchronize()
+    ref = [r.loss.clone(), r.student_ce.clone(), r.kl.clone(), r.saved.clone()]
+
+    lib = L.load()
+    f32 = dict(dtype=torch.float32, device="cuda")
+    loss, sce, kl = torch.empty((), **f32), torch.empty(r.n, **f32), torch.empty(r.n, **f32)
+    saved = torch.zeros_like(r.saved)
+    flags = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    out = L.KdOutputs(loss.data_ptr(), sce.data_ptr(), None, kl.data_ptr())
+
+    def call():
+        st = lib.kd_loss_fwd_noalloc(ctypes.byref(r.s), ctypes.byref(r.t), ctypes.byref(r.p), r.labels_ptr,
+                                     ctypes.byref(out), saved.data_ptr(), flags.data_ptr(),
+                                     torch.cuda.current_stream().cuda_stream, None)
+        assert st == L.KD_OK, lib.kd_status_string(st)
+
+    call()  # eager: sets up the scratch of this device
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (loss, sce, kl):
+            t.fill_(SENTINEL)
+        flags.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((loss, sce, kl, saved), ref):
+            assert torch.equal(a, b), f"no-alloc replay {rep} differs from the workspace forward"
+        assert int(flags.item()) == 0
